@@ -1,0 +1,198 @@
+"""Fixed-point solvers for the stacked trajectory, written as plain loops.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+The article [PN §1.2] recasts the evaluation of s_t = f_t(s_{t-1}), t = 1..T,
+as a root-finding problem F(s) = 0 over the whole trajectory and applies the
+update s <- s - J~^{-1}(s) F(s), where the four methods differ only in J~.
+With F_t(s) = s_t - f_t(s_{t-1}) (s_0 given), the exact Jacobian of F is the
+block lower-bidiagonal matrix with identity blocks on the diagonal and
+-A_t = -df_t/ds_{t-1} below it.  Replacing A_t by an approximation A~_t and
+solving J~ d = -F by forward substitution gives the update used here:
+
+    p_t  = s_{t-1}                (p_1 = s_0)
+    v_t  = f_t(p_t)
+    s^_t = v_t + A~_t (s^_{t-1} - p_t),   s^_0 = s_0
+
+with A~_t = 0 (Jacobi, J~ = I), A~_t = I (Picard, identity dynamics
+[PN §2.2.3]), A~_t = diag(A_t) (quasi-Newton, diagonal approximation
+[PN §2.2.1]) and A~_t = A_t (Newton).  The forward substitution is a
+first-order linear recurrence — the object a parallel scan evaluates
+[PN §2.1] — and here it is a deliberately sequential loop.
+
+Readings where the article is silent (documented alongside the build):
+  * initial guess s^(0)_t = s_0 for every t;
+  * residual r = max over (b, t, d) of |F|, one stop rule per solve;
+  * stop when r is not finite (NONFINITE), else when r <= tol (OK), else when
+    the number of applied updates reaches max_iter (NOT_CONVERGED);
+  * damping is step damping, s <- s + lam (s^ - s) [PN §4.3, §5.3];
+  * windows are consecutive, non-overlapping blocks of W steps, each solved
+    from its own initial state, which is the last state of the previous
+    window [PN §1.3.1, §2.3].
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .cells import make_cell
+
+JACOBI, PICARD, QUASI_NEWTON, NEWTON = 0, 1, 2, 3
+OK, NOT_CONVERGED, NONFINITE = 0, 1, 2
+
+
+def sequential(cell, x, s0):
+    """Ground truth s_t = f_t(s_{t-1}) by the plain time loop [PN §1.1].
+
+    x: [B, T, m], s0: [B, D]  ->  [B, T, D] holding s_1..s_T.
+    """
+    B, T = x.shape[0], x.shape[1]
+    out = np.empty((B, T, cell.D), dtype=cell.dtype)
+    prev = np.asarray(s0, dtype=cell.dtype)
+    for t in range(T):
+        prev = cell.f(prev, x[:, t])
+        out[:, t] = prev
+    return out
+
+
+def shift(s, s0):
+    """p_t = s_{t-1} with p_1 = s_0: [B, T, D] -> [B, T, D]."""
+    return np.concatenate([np.asarray(s0, dtype=s.dtype)[:, None, :], s[:, :-1]], axis=1)
+
+
+def residual_inf(cell, x, s0, s):
+    """max over (b, t, d) of |s_t - f_t(s_{t-1})|; NaN/Inf propagate; 0 if empty."""
+    if s.size == 0:
+        return 0.0
+    v = cell.f(shift(s, s0), x)
+    return float(np.max(np.abs(s - v)))
+
+
+def jacobian_approx(mode, cell, p, x):
+    """A~_t for every (b, t): [B, T, D] for the diagonal modes, [B, T, D, D] for Newton."""
+    if mode == JACOBI:
+        return np.zeros(p.shape, dtype=cell.dtype)
+    if mode == PICARD:
+        return np.ones(p.shape, dtype=cell.dtype)
+    if mode == QUASI_NEWTON:
+        return cell.jac_diag(p, x)
+    if mode == NEWTON:
+        return cell.jac(p, x)
+    raise ValueError(f"unknown mode {mode}")
+
+
+def affine_recurrence(v, p, A, s0):
+    """s^_t = v_t + A_t (s^_{t-1} - p_t), s^_0 = s0, by a sequential loop over t.
+
+    A is [B, T, D] (diagonal) or [B, T, D, D] (dense).  This is the forward
+    substitution of J~ d = -F; the GPU evaluates the same recurrence with an
+    associative scan over the affine maps y -> A_t y + (v_t - A_t p_t).
+    """
+    B, T, D = v.shape
+    out = np.empty_like(v)
+    prev = np.asarray(s0, dtype=v.dtype)
+    dense = A.ndim == 4
+    for t in range(T):
+        d = prev - p[:, t]
+        if dense:
+            step = np.einsum("bij,bj->bi", A[:, t], d)
+        else:
+            step = A[:, t] * d
+        prev = v[:, t] + step
+        out[:, t] = prev
+    return out
+
+
+def newton_step(cell, x, s0, s, mode):
+    """One undamped update s -> s^ of the chosen method [PN §1.2]."""
+    p = shift(s, s0)
+    v = cell.f(p, x)
+    A = jacobian_approx(mode, cell, p, x)
+    return affine_recurrence(v, p, A, s0)
+
+
+@dataclass
+class SolveResult:
+    s: np.ndarray                 # [B, T, D] final iterate (NaN where never reached)
+    iters: int                    # total updates over all windows
+    status: int                   # OK / NOT_CONVERGED / NONFINITE
+    window_iters: list = field(default_factory=list)   # K per window solved
+    window_status: list = field(default_factory=list)
+    hist: list = field(default_factory=list)           # per window: [r_0, ..., r_K]
+
+
+def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force):
+    B, T = x.shape[0], x.shape[1]
+    s = np.broadcast_to(np.asarray(s0, dtype=cell.dtype)[:, None, :], (B, T, cell.D)).copy()
+    hist = []
+    i = 0
+    while True:
+        p = shift(s, s0)
+        v = cell.f(p, x)
+        r = float(np.max(np.abs(s - v))) if s.size else 0.0
+        hist.append(r)
+        if force is None:
+            if not np.isfinite(r):
+                return s, i, NONFINITE, hist
+            if r <= tol:
+                return s, i, OK, hist
+            if i == max_iter:
+                return s, i, NOT_CONVERGED, hist
+        elif i == force:
+            status = NONFINITE if not np.isfinite(r) else (OK if r <= tol else NOT_CONVERGED)
+            return s, i, status, hist
+        A = jacobian_approx(mode, cell, p, x)
+        s_hat = affine_recurrence(v, p, A, s0)
+        if damping == 1.0:
+            s = s_hat
+        else:
+            s = s + damping * (s_hat - s)
+        i += 1
+
+
+def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
+          dtype=np.float64, force_iters=None):
+    """Parallel-in-time fixed-point solve, evaluated sequentially.
+
+    kind/params follow the flat layout of ``make_cell``; x: [B, T, m];
+    s0: [B, D].  ``window`` = 0 solves the whole horizon at once; W > 0 solves
+    windows of W steps in order (the last may be shorter).  ``force_iters``
+    (one count per window) replaces the stop rule by a fixed number of
+    updates; it is used to follow a run whose stopping decision landed inside
+    the floating-point ambiguity band of the tolerance.
+    """
+    x = np.asarray(x)
+    s0 = np.asarray(s0)
+    B, T = x.shape[0], x.shape[1]
+    D = s0.shape[1]
+    m = x.shape[2]
+    cell = make_cell(kind, params, D, m, dtype)
+    xc = x.astype(dtype)
+    s_init = s0.astype(dtype)
+    out = np.full((B, T, D), np.nan, dtype=dtype)
+    W = T if window <= 0 else int(window)
+    res = SolveResult(out, 0, OK)
+    w0 = 0
+    wi = 0
+    while w0 < T or (T == 0 and wi == 0):
+        w1 = min(T, w0 + W)
+        force = None if force_iters is None else int(force_iters[wi])
+        s, K, st, hist = _solve_window(cell, xc[:, w0:w1], s_init, mode, tol, max_iter,
+                                       damping, force)
+        out[:, w0:w1] = s
+        res.iters += K
+        res.window_iters.append(K)
+        res.window_status.append(st)
+        res.hist.append(hist)
+        if st == NONFINITE:
+            res.status = NONFINITE
+            break
+        if st == NOT_CONVERGED:
+            res.status = NOT_CONVERGED
+        if w1 > w0:
+            s_init = s[:, -1]
+        w0 = w1
+        wi += 1
+        if T == 0:
+            break
+    return res

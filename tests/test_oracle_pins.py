@@ -1,0 +1,436 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one oracle function to a library routine, a closed form, an
+invariant stated in the article "并行牛顿方法：加速非线性序列评估的计算革命" [PN], or
+brute force on tiny inputs, chosen so that a dropped term, a wrong sign, a
+shifted index or a transposed operand in the oracle fails at least one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import cells as oc
+from oracle import solver as osv
+import workloads
+
+RNG = np.random.default_rng(1234)
+
+
+def _rnn_params(D, m, rng, scale=1.0):
+    return workloads.random_cell_params(oracle.CELL_TANH_RNN, D, m, rng, scale).astype(np.float64)
+
+
+def _gru_params(D, m, rng, scale=1.0):
+    return workloads.random_cell_params(oracle.CELL_GRU, D, m, rng, scale).astype(np.float64)
+
+
+# ---------------------------------------------------------------- sequential
+
+def test_sequential_tanh_rnn_matches_torch_rnn():
+    D, m, B, T = 5, 3, 3, 17
+    rng = np.random.default_rng(1)
+    params = _rnn_params(D, m, rng, 1.5)
+    cell = oracle.make_cell(oracle.CELL_TANH_RNN, params, D, m)
+    x = rng.standard_normal((B, T, m))
+    s0 = rng.standard_normal((B, D))
+    ref = torch.nn.RNN(m, D, nonlinearity="tanh", batch_first=True).double()
+    with torch.no_grad():
+        ref.weight_hh_l0.copy_(torch.from_numpy(cell.W))
+        ref.weight_ih_l0.copy_(torch.from_numpy(cell.U))
+        ref.bias_ih_l0.copy_(torch.from_numpy(cell.b))
+        ref.bias_hh_l0.zero_()
+        out, _ = ref(torch.from_numpy(x), torch.from_numpy(s0)[None])
+    got = oracle.sequential(cell, x, s0)
+    np.testing.assert_allclose(got, out.numpy(), rtol=0, atol=1e-12)
+
+
+def test_sequential_gru_matches_torch_gru():
+    D, m, B, T = 6, 4, 3, 19
+    rng = np.random.default_rng(2)
+    params = _gru_params(D, m, rng, 2.0)
+    cell = oracle.make_cell(oracle.CELL_GRU, params, D, m)
+    x = rng.standard_normal((B, T, m))
+    s0 = rng.standard_normal((B, D)) * 0.5
+    ref = torch.nn.GRU(m, D, batch_first=True).double()
+    with torch.no_grad():
+        ref.weight_ih_l0.copy_(torch.from_numpy(cell.W_ih))
+        ref.weight_hh_l0.copy_(torch.from_numpy(cell.W_hh))
+        ref.bias_ih_l0.copy_(torch.from_numpy(cell.b_ih))
+        ref.bias_hh_l0.copy_(torch.from_numpy(cell.b_hh))
+        out, _ = ref(torch.from_numpy(x), torch.from_numpy(s0)[None])
+    got = oracle.sequential(cell, x, s0)
+    np.testing.assert_allclose(got, out.numpy(), rtol=0, atol=1e-12)
+
+
+def test_sequential_diag_tanh_is_an_rnn_with_diagonal_weights():
+    # tanh(a*s + x) is torch's Elman RNN with W_hh = diag(a), W_ih = I, no bias.
+    D, B, T = 7, 2, 23
+    rng = np.random.default_rng(3)
+    a = rng.uniform(-0.95, 0.95, D)
+    cell = oracle.make_cell(oracle.CELL_DIAG_TANH, a, D, D)
+    x = rng.standard_normal((B, T, D))
+    s0 = rng.standard_normal((B, D))
+    ref = torch.nn.RNN(D, D, nonlinearity="tanh", batch_first=True).double()
+    with torch.no_grad():
+        ref.weight_hh_l0.copy_(torch.diag(torch.from_numpy(a)))
+        ref.weight_ih_l0.copy_(torch.eye(D, dtype=torch.float64))
+        ref.bias_ih_l0.zero_()
+        ref.bias_hh_l0.zero_()
+        out, _ = ref(torch.from_numpy(x), torch.from_numpy(s0)[None])
+    np.testing.assert_allclose(oracle.sequential(cell, x, s0), out.numpy(), rtol=0, atol=1e-12)
+
+
+def test_sequential_scalar_closed_form():
+    # Two hand-evaluated steps of the scalar cell: s1 = tanh(x1), s2 = tanh(a s1 + x2).
+    cell = oracle.make_cell(oracle.CELL_DIAG_TANH, np.array([0.5]), 1, 1)
+    x = np.array([[[0.25], [-1.0]]])
+    s = oracle.sequential(cell, x, np.zeros((1, 1)))
+    s1 = np.tanh(0.25)
+    assert s[0, 0, 0] == pytest.approx(s1, abs=1e-15)
+    assert s[0, 1, 0] == pytest.approx(np.tanh(0.5 * s1 - 1.0), abs=1e-15)
+
+
+# ---------------------------------------------------------------- Jacobians
+
+def _torch_cell_jacobian(torch_cell, p, x):
+    """Per-row Jacobian of a torch RNNCell/GRUCell w.r.t. its hidden state."""
+    out = []
+    for b in range(p.shape[0]):
+        xb = torch.from_numpy(x[b:b + 1])
+        J = torch.autograd.functional.jacobian(
+            lambda h: torch_cell(xb, h[None])[0], torch.from_numpy(p[b]))
+        out.append(J.numpy())
+    return np.stack(out)
+
+
+def test_gru_jacobian_matches_autograd_and_fd():
+    D, m, B = 6, 3, 4
+    rng = np.random.default_rng(4)
+    params = _gru_params(D, m, rng, 2.5)
+    cell = oracle.make_cell(oracle.CELL_GRU, params, D, m)
+    p = rng.standard_normal((B, D))
+    x = rng.standard_normal((B, m))
+    tc = torch.nn.GRUCell(m, D).double()
+    with torch.no_grad():
+        tc.weight_ih.copy_(torch.from_numpy(cell.W_ih))
+        tc.weight_hh.copy_(torch.from_numpy(cell.W_hh))
+        tc.bias_ih.copy_(torch.from_numpy(cell.b_ih))
+        tc.bias_hh.copy_(torch.from_numpy(cell.b_hh))
+    ref = _torch_cell_jacobian(tc, p, x)
+    J = cell.jac(p, x)
+    np.testing.assert_allclose(J, ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(cell.jac_diag(p, x), np.diagonal(ref, axis1=-2, axis2=-1),
+                               rtol=0, atol=1e-13)
+    # central finite differences, column by column
+    h = 1e-6
+    fd = np.empty_like(J)
+    for k in range(D):
+        e = np.zeros(D)
+        e[k] = h
+        fd[..., k] = (cell.f(p + e, x) - cell.f(p - e, x)) / (2 * h)
+    np.testing.assert_allclose(J, fd, rtol=0, atol=1e-8)
+
+
+def test_tanh_rnn_jacobian_matches_autograd():
+    D, m, B = 5, 2, 3
+    rng = np.random.default_rng(5)
+    params = _rnn_params(D, m, rng, 1.3)
+    cell = oracle.make_cell(oracle.CELL_TANH_RNN, params, D, m)
+    p = rng.standard_normal((B, D))
+    x = rng.standard_normal((B, m))
+    tc = torch.nn.RNNCell(m, D, nonlinearity="tanh").double()
+    with torch.no_grad():
+        tc.weight_hh.copy_(torch.from_numpy(cell.W))
+        tc.weight_ih.copy_(torch.from_numpy(cell.U))
+        tc.bias_ih.copy_(torch.from_numpy(cell.b))
+        tc.bias_hh.zero_()
+    ref = _torch_cell_jacobian(tc, p, x)
+    np.testing.assert_allclose(cell.jac(p, x), ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(cell.jac_diag(p, x), np.diagonal(ref, axis1=-2, axis2=-1),
+                               rtol=0, atol=1e-13)
+
+
+def test_diag_tanh_jacobian_fd():
+    D, B = 9, 3
+    rng = np.random.default_rng(6)
+    cell = oracle.make_cell(oracle.CELL_DIAG_TANH, rng.uniform(-1, 1, D), D, D)
+    p = rng.standard_normal((B, D))
+    x = rng.standard_normal((B, D))
+    h = 1e-6
+    fd = (cell.f(p + h, x) - cell.f(p - h, x)) / (2 * h)   # channels are independent
+    np.testing.assert_allclose(cell.jac_diag(p, x), fd, rtol=0, atol=1e-9)
+    J = cell.jac(p, x)
+    assert np.all(J - np.einsum("bi,ij->bij", cell.jac_diag(p, x), np.eye(D)) == 0)
+
+
+# ---------------------------------------------------------------- linear recurrence
+
+def _brute_force_affine(v, p, A, s0):
+    """s^_t = sum_{tau<=t} (A_t..A_{tau+1}) c_tau + (A_t..A_1) s0, c = v - A p."""
+    B, T, D = v.shape
+    dense = A.ndim == 4
+    Am = A if dense else np.einsum("btd,de->btde", A, np.eye(D))
+    c = v - np.einsum("btij,btj->bti", Am, p)
+    out = np.zeros_like(v)
+    for b in range(B):
+        for t in range(T):
+            acc = np.zeros(D)
+            for tau in range(-1, t + 1):
+                M = np.eye(D)
+                for u in range(tau + 1, t + 1):
+                    M = Am[b, u] @ M
+                acc += M @ (s0[b] if tau == -1 else c[b, tau])
+            out[b, t] = acc
+    return out
+
+
+@pytest.mark.parametrize("dense", [False, True])
+def test_affine_recurrence_brute_force(dense):
+    B, T, D = 2, 7, 3
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((B, T, D))
+    p = rng.standard_normal((B, T, D))
+    A = rng.standard_normal((B, T, D, D) if dense else (B, T, D)) * 0.8
+    s0 = rng.standard_normal((B, D))
+    np.testing.assert_allclose(oracle.affine_recurrence(v, p, A, s0),
+                               _brute_force_affine(v, p, A, s0), rtol=0, atol=1e-12)
+
+
+def test_affine_combine_is_associative():
+    # The scan element is the affine map y -> A y + c; composing "later after
+    # earlier" is (A_l A_e, A_l c_e + c_l) [PN §2.1].  Check associativity and
+    # that folding the elements reproduces the recurrence.
+    rng = np.random.default_rng(8)
+    D = 4
+
+    def comb(e, l):
+        return (l[0] @ e[0], l[0] @ e[1] + l[1])
+
+    els = [(rng.standard_normal((D, D)), rng.standard_normal(D)) for _ in range(3)]
+    a = comb(comb(els[0], els[1]), els[2])
+    b = comb(els[0], comb(els[1], els[2]))
+    np.testing.assert_allclose(a[0], b[0], atol=1e-13)
+    np.testing.assert_allclose(a[1], b[1], atol=1e-13)
+    y0 = rng.standard_normal(D)
+    y = y0
+    for A, c in els:
+        y = A @ y + c
+    np.testing.assert_allclose(a[0] @ y0 + a[1], y, atol=1e-13)
+
+
+def test_picard_recurrence_is_a_cumulative_sum():
+    # A~ = I turns the recurrence into s0 + cumsum(v - p) [PN §2.2.3, §4.1].
+    B, T, D = 3, 50, 4
+    rng = np.random.default_rng(9)
+    v, p = rng.standard_normal((2, B, T, D))
+    s0 = rng.standard_normal((B, D))
+    ref = s0[:, None] + torch.cumsum(torch.from_numpy(v - p), dim=1).numpy()
+    np.testing.assert_allclose(oracle.affine_recurrence(v, p, np.ones((B, T, D)), s0), ref,
+                               rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- the update itself
+
+def _dense_update(cell, x, s0, s, mode):
+    """s - J~^{-1} F(s) with J~ assembled as a (T*D)x(T*D) matrix per batch row
+    and solved by numpy.linalg.solve, straight from the update equation [PN §1.2]."""
+    B, T, D = s.shape
+    p = osv.shift(s, s0)
+    F = s - cell.f(p, x)
+    A = osv.jacobian_approx(mode, cell, p, x)
+    if A.ndim == 3:
+        A = np.einsum("btd,de->btde", A, np.eye(D))
+    out = np.empty_like(s)
+    for b in range(B):
+        J = np.eye(T * D)
+        for t in range(1, T):
+            J[t * D:(t + 1) * D, (t - 1) * D:t * D] = -A[b, t]
+        out[b] = (s[b].ravel() - np.linalg.solve(J, F[b].ravel())).reshape(T, D)
+    return out
+
+
+@pytest.mark.parametrize("kind", [oracle.CELL_TANH_RNN, oracle.CELL_GRU, oracle.CELL_DIAG_TANH])
+@pytest.mark.parametrize("mode", [oracle.JACOBI, oracle.PICARD, oracle.QUASI_NEWTON, oracle.NEWTON])
+def test_update_equals_linear_solve_of_the_stacked_system(kind, mode):
+    D, m, B, T = 4, 3, 2, 9
+    if kind == oracle.CELL_DIAG_TANH:
+        m = D
+    rng = np.random.default_rng(10 + kind * 4 + mode)
+    params = workloads.random_cell_params(kind, D, m, rng, 1.5).astype(np.float64)
+    cell = oracle.make_cell(kind, params, D, m)
+    x = rng.standard_normal((B, T, m))
+    s0 = rng.standard_normal((B, D)) * 0.3
+    s = rng.standard_normal((B, T, D)) * 0.5
+    np.testing.assert_allclose(oracle.newton_step(cell, x, s0, s, mode),
+                               _dense_update(cell, x, s0, s, mode), rtol=0, atol=1e-11)
+
+
+# ---------------------------------------------------------------- invariants from [PN §3.1]
+
+@pytest.mark.parametrize("kind", [oracle.CELL_TANH_RNN, oracle.CELL_GRU, oracle.CELL_DIAG_TANH])
+@pytest.mark.parametrize("mode", [oracle.JACOBI, oracle.PICARD, oracle.QUASI_NEWTON, oracle.NEWTON])
+def test_causality_prefix_exact_and_T_step_convergence(kind, mode):
+    # After i undamped updates the first i states equal the sequential ones,
+    # so every method has converged after at most T updates.
+    D, m, B, T = 3, 2, 2, 8
+    if kind == oracle.CELL_DIAG_TANH:
+        m = D
+    rng = np.random.default_rng(30 + kind * 4 + mode)
+    params = workloads.random_cell_params(kind, D, m, rng, 2.0).astype(np.float64)
+    cell = oracle.make_cell(kind, params, D, m)
+    x = rng.standard_normal((B, T, m))
+    s0 = rng.standard_normal((B, D)) * 0.3
+    seq = oracle.sequential(cell, x, s0)
+    s = np.broadcast_to(s0[:, None], (B, T, D)).copy()
+    for i in range(1, T + 1):
+        s = oracle.newton_step(cell, x, s0, s, mode)
+        if mode == oracle.JACOBI:
+            assert np.array_equal(s[:, :i], seq[:, :i])
+        else:
+            np.testing.assert_allclose(s[:, :i], seq[:, :i], rtol=0, atol=1e-12)
+    res = oracle.solve(kind, params, x, s0, mode, 1e-12, T)
+    assert res.status == oracle.OK and res.iters <= T
+    assert oracle.residual_inf(cell, x, s0, res.s) <= 1e-12
+
+
+def test_picard_exact_jacobian_case():
+    # f_t(s) = s + c_t has A_t = I exactly, so one Picard update is exact.
+    class Shift:
+        D, m, dtype = 3, 3, np.float64
+
+        def f(self, p, x):
+            return p + x
+
+        def jac_diag(self, p, x):
+            return np.ones_like(p)
+
+        def jac(self, p, x):
+            return np.broadcast_to(np.eye(3), p.shape + (3,)).copy()
+
+    cell = Shift()
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((2, 12, 3))
+    s0 = rng.standard_normal((2, 3))
+    s = np.broadcast_to(s0[:, None], (2, 12, 3)).copy()
+    s1 = oracle.newton_step(cell, x, s0, s, oracle.PICARD)
+    np.testing.assert_allclose(s1, oracle.sequential(cell, x, s0), atol=1e-13)
+
+
+def test_newton_on_affine_maps_converges_in_one_update_and_jacobi_on_constants():
+    D, T, B = 3, 10, 2
+    rng = np.random.default_rng(12)
+    A = rng.standard_normal((D, D)) * 0.9
+
+    class Affine:
+        dtype = np.float64
+
+        def __init__(self, A):
+            self.A, self.D, self.m = A, A.shape[0], A.shape[0]
+
+        def f(self, p, x):
+            return p @ self.A.T + x
+
+        def jac(self, p, x):
+            return np.broadcast_to(self.A, p.shape + (self.D,)).copy()
+
+        def jac_diag(self, p, x):
+            return np.broadcast_to(np.diagonal(self.A), p.shape).copy()
+
+    x = rng.standard_normal((B, T, D))
+    s0 = rng.standard_normal((B, D))
+    s = np.broadcast_to(s0[:, None], (B, T, D)).copy()
+    cell = Affine(A)
+    seq = oracle.sequential(cell, x, s0)
+    np.testing.assert_allclose(oracle.newton_step(cell, x, s0, s, oracle.NEWTON), seq, atol=1e-12)
+    const = Affine(np.zeros((D, D)))     # f_t = c_t
+    np.testing.assert_array_equal(oracle.newton_step(const, x, s0, s, oracle.JACOBI),
+                                  oracle.sequential(const, x, s0))
+
+
+def test_quasi_newton_equals_newton_for_channelwise_cell():
+    wl = workloads.make(3, B=2, T=512)
+    a = [oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], md, 1e-10, 512)
+         for md in (oracle.QUASI_NEWTON, oracle.NEWTON)]
+    assert a[0].iters == a[1].iters and a[0].status == a[1].status == oracle.OK
+    np.testing.assert_array_equal(a[0].s, a[1].s)
+
+
+def test_newton_converges_quadratically_quasi_newton_linearly():
+    wl = workloads.make(2, B=4, T=256)
+    rn = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], oracle.NEWTON, 1e-13, 256)
+    rq = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], oracle.QUASI_NEWTON, 1e-11, 256)
+    h = rn.hist[0]
+    # consecutive residuals above the float64 floor
+    pairs = [(h[i], h[i + 1]) for i in range(len(h) - 1) if h[i + 1] > 1e-13 and h[i] < 0.5]
+    assert pairs, h
+    for r0, r1 in pairs:
+        assert r1 <= 5.0 * r0 * r0, h
+    hq = np.array(rq.hist[0])
+    ratios = hq[3:-1][1:] / hq[3:-1][:-1]
+    assert ratios.max() < 0.9 and ratios.min() > 1e-3, hq   # linear, not quadratic
+    assert len(hq) > len(h)
+
+
+def test_damping_scales_the_step_and_keeps_the_fixed_point():
+    D, m, B, T = 4, 3, 2, 12
+    rng = np.random.default_rng(13)
+    params = workloads.random_cell_params(oracle.CELL_GRU, D, m, rng, 1.5).astype(np.float64)
+    cell = oracle.make_cell(oracle.CELL_GRU, params, D, m)
+    x = rng.standard_normal((B, T, m))
+    s0 = np.zeros((B, D))
+    lam = 0.5
+    r1 = oracle.solve(oracle.CELL_GRU, params, x, s0, oracle.QUASI_NEWTON, 0, 1, damping=lam)
+    s_init = np.zeros((B, T, D))
+    step = oracle.newton_step(cell, x, s0, s_init, oracle.QUASI_NEWTON) - s_init
+    np.testing.assert_allclose(r1.s - s_init, lam * step, rtol=0, atol=1e-15)
+    r = oracle.solve(oracle.CELL_GRU, params, x, s0, oracle.QUASI_NEWTON, 1e-12, 400, damping=lam)
+    assert r.status == oracle.OK
+    np.testing.assert_allclose(r.s, oracle.sequential(cell, x, s0), atol=1e-11)
+
+
+def test_windows_chain_and_full_window_is_identical():
+    wl = workloads.make(2, B=3, T=300)
+    args = (wl["cell"], wl["params"], wl["x"], wl["s0"], oracle.QUASI_NEWTON, 1e-7, 300)
+    full = oracle.solve(*args)
+    same = oracle.solve(*args, window=300)
+    np.testing.assert_array_equal(full.s, same.s)
+    assert full.iters == same.iters
+    win = oracle.solve(*args, window=64)
+    assert len(win.window_iters) == 5 and win.iters == sum(win.window_iters)
+    cell = oracle.make_cell(wl["cell"], wl["params"], wl["D"], wl["m"])
+    assert oracle.residual_inf(cell, wl["x"].astype(np.float64), wl["s0"].astype(np.float64),
+                               win.s) <= 1e-7
+
+
+def test_residual_of_a_perturbed_trajectory():
+    D, m, B, T = 3, 2, 2, 6
+    rng = np.random.default_rng(14)
+    params = _rnn_params(D, m, rng)
+    cell = oracle.make_cell(oracle.CELL_TANH_RNN, params, D, m)
+    x = rng.standard_normal((B, T, m))
+    s0 = rng.standard_normal((B, D))
+    seq = oracle.sequential(cell, x, s0)
+    assert oracle.residual_inf(cell, x, s0, seq) <= 1e-15
+    pert = seq.copy()
+    pert[1, T - 1, 2] += 0.125        # last step: no downstream effect
+    assert oracle.residual_inf(cell, x, s0, pert) == pytest.approx(0.125, abs=1e-15)
+
+
+def test_stop_rule_edges():
+    wl = workloads.make(2, B=2, T=40)
+    a = (wl["cell"], wl["params"], wl["x"], wl["s0"], oracle.QUASI_NEWTON)
+    r0 = oracle.solve(*a, 1e-5, 0)
+    assert r0.status == oracle.NOT_CONVERGED and r0.iters == 0
+    assert np.all(r0.s == 0)
+    rbig = oracle.solve(*a, 1e9, 10)
+    assert rbig.status == oracle.OK and rbig.iters == 0
+    r1 = oracle.solve(*a, 0.0, 3)
+    assert r1.status == oracle.NOT_CONVERGED and r1.iters == 3
+    x = wl["x"].copy()
+    x[1, 7, 0] = np.nan
+    rn = oracle.solve(wl["cell"], wl["params"], x, wl["s0"], oracle.QUASI_NEWTON, 1e-5, 10)
+    assert rn.status == oracle.NONFINITE and rn.iters == 0
+    empty = oracle.solve(wl["cell"], wl["params"], wl["x"][:, :0], wl["s0"], oracle.NEWTON, 1e-5, 5)
+    assert empty.status == oracle.OK and empty.iters == 0 and empty.s.shape == (2, 0, 16)
