@@ -1,0 +1,164 @@
+"""Benchmark: converged state-updates/s of one parallel-in-time solve on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--mode qn]
+
+A step is one complete solve (all iterations, all windows) of a seeded
+synthetic workload with inputs resident in HBM.  Default workload: the
+channel-wise tanh recurrence s_t = tanh(a*s_{t-1} + x_t), B=8, T=65536, D=256,
+float32, quasi-Newton (diagonal Jacobian) to residual 1e-5.
+
+Prints one JSON line.  Besides the throughput it reports the roofline of the
+dominant kernel (the fused apply kernel; algorithmic bytes = x and s^(i) read,
+s^(i+1) written, per launch, over its HIP-event-timed duration) and the CPU
+oracle timed on a bounded sample of the same workload on this host.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "converged state-updates/s (B*T*D) per Newton solve; achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+FP32_PEAK_TFLOPS = 157.3
+MODES = {"jacobi": 0, "picard": 1, "qn": 2, "quasi_newton": 2, "newton": 3}
+KERNEL_SOURCES = {  # source file of the dominant kernel per cell kind
+    0: "newton_evaluation_nonlinear_amd/csrc/pn_diag.hip",
+    1: "newton_evaluation_nonlinear_amd/csrc/pn_cell.hip",
+    2: "newton_evaluation_nonlinear_amd/csrc/pn_cell.hip",
+}
+
+
+def _src_hash(path):
+    with open(os.path.join(ROOT, path), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def _traffic(name, src, launch_bytes_alg):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    they were taken on another revision of the kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_sha256_16") != _src_hash(src):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, mode):
+    """The float64 oracle on a bounded sample of the workload, one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    import workloads
+
+    samples = {3: dict(B=2, T=16384), 2: dict(B=8, T=2048), 4: dict(B=4, T=4096),
+               1: dict(B=None, T=None), 5: dict(B=1, T=4096)}
+    sm = samples.get(cfg, dict(B=1, T=4096))
+    wl = workloads.make(cfg, **sm)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        r = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], mode, wl["tol"],
+                         wl["max_iter"], wl["damping"], wl["window"])
+        el = time.perf_counter() - t0
+    n = wl["B"] * wl["T"] * wl["D"]
+    return {"value": n / el, "unit": "state-updates/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 oracle solve of the same workload cut to B={wl['B']}, "
+                      f"T={wl['T']} (D={wl['D']}): {r.iters} updates, status {r.status}, "
+                      f"{el:.2f} s on one host thread",
+            "seconds": el}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--mode", default=None)
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is described, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads
+    import newton_evaluation_nonlinear_amd as pn
+
+    wl = workloads.make(args.config)
+    mode = MODES[args.mode] if args.mode else wl["modes"][0]
+    dev = torch.device("cuda:0")
+    params, x, s0 = (torch.from_numpy(wl[k]).to(dev) for k in ("params", "x", "s0"))
+    out = torch.empty((wl["B"], wl["T"], wl["D"]), dtype=torch.float32, device=dev)
+    nbytes = pn.workspace_bytes(wl["cell"], wl["m"], wl["B"], wl["T"], wl["D"], mode,
+                                wl["damping"], wl["window"], args.chunk)
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+
+    def solve(profile):
+        return pn.eval(wl["cell"], params, x, s0, mode=mode, tol=wl["tol"],
+                       max_iter=wl["max_iter"], damping=wl["damping"], window=wl["window"],
+                       chunk=args.chunk, out=out, workspace=ws, profile=profile)
+
+    for _ in range(args.warmup):
+        solve(False)
+    torch.cuda.synchronize()
+    results = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        results.append(solve(True))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) / args.steps * 1e3
+    n_upd = wl["B"] * wl["T"] * wl["D"]
+    value = n_upd / (ms / 1e3)
+    last = results[-1]
+    apply_ms = sum(r.profile["apply_ms"] for r in results)
+    apply_launches = sum(r.profile["apply_launches"] for r in results)
+    apply_bytes = sum(r.profile["apply_bytes"] for r in results)
+    apply_flops = sum(r.profile["apply_flops"] for r in results)
+    carry_ms = sum(r.profile["carry_ms"] for r in results)
+    avg_launch_ms = apply_ms / max(apply_launches, 1)
+    bytes_per_launch = apply_bytes / max(apply_launches, 1)
+    gbs = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9 if avg_launch_ms > 0 else 0.0
+    name = f"{wl['name']}_{workloads.MODE_NAMES[mode]}"
+    src = KERNEL_SOURCES[wl["cell"]]
+    if mode == 3 and wl["cell"] != 0:
+        tf = apply_flops / max(apply_launches, 1) / (avg_launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": tf, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tf / FP32_PEAK_TFLOPS, "traffic": _traffic(name, src, bytes_per_launch)}
+    else:
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS, "traffic": _traffic(name, src, bytes_per_launch)}
+    roof.update(kernel="apply (fused cell + scan replay + residual + next chunk maps)",
+                avg_launch_ms=avg_launch_ms, launches_per_step=apply_launches / args.steps,
+                alg_bytes_per_launch=bytes_per_launch, carry_ms_per_step=carry_ms / args.steps)
+    line = {
+        "metric": METRIC, "value": value, "unit": "state-updates/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded PCG64 draws, no dataset)",
+        "config": {"workload": name, "cell": wl["cell"], "B": wl["B"], "T": wl["T"],
+                   "D": wl["D"], "m": wl["m"], "mode": workloads.MODE_NAMES[mode],
+                   "tol": wl["tol"], "damping": wl["damping"], "window": wl["window"],
+                   "iters": last.iters, "window_iters_first": last.window_iters[:4],
+                   "status": last.status, "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(args.config, mode)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * pn.h -- C interface of libpn, a GPU engine that evaluates nonlinear
+ * recurrences s_t = f_t(s_{t-1}), t = 1..T, in parallel over time.
+ *
+ * Method: the web article "并行牛顿方法：加速非线性序列评估的计算革命" (a survey of
+ * parallel Newton methods for nonlinear sequence evaluation; cited below as
+ * [PN §x]).  The whole trajectory s = (s_1..s_T) is the unknown of a
+ * fixed-point problem F(s) = 0 [PN §1.2] with
+ *     F_t(s) = s_t - f_t(s_{t-1}),   s_0 given,
+ * and is improved by s <- s - J~^{-1}(s) F(s), where J~ is I minus the
+ * sub-diagonal of approximated state Jacobians A~_t ~ df_t/ds_{t-1}:
+ *     Jacobi        A~_t = 0                      [PN §1.2]
+ *     Picard        A~_t = I                      [PN §1.2, §2.2.3]
+ *     quasi-Newton  A~_t = diag(df_t/ds_{t-1})    [PN §2.2.1]
+ *     Newton        A~_t = df_t/ds_{t-1} (dense)  [PN §1.2]
+ * Applying J~^{-1} is the first-order linear recurrence
+ *     s^_t = v_t + A~_t (s^_{t-1} - p_t),  p_t = s_{t-1},  v_t = f_t(p_t),
+ * evaluated by an associative scan over affine maps [PN §2.1].
+ *
+ * Readings fixed by this library where the article is silent:
+ *   - initial iterate s_t = s_0 for every t;
+ *   - residual r = max over (b, t, d) of |F|, one stop rule for the batch;
+ *   - stop at the first check with r non-finite (PN_NONFINITE), else with
+ *     r <= tol (PN_OK), else when max_iter updates have been applied
+ *     (PN_NOT_CONVERGED); the count reported is the number of updates;
+ *   - damping lam in (0, 1] is step damping, s <- s + lam (s^ - s)
+ *     [PN §4.3 suggests more damping when iterations stall];
+ *   - windows [PN §1.3.1, §2.3]: consecutive blocks of W steps solved in
+ *     order, window w starting from the last state of window w-1.
+ *
+ * Memory conventions (all functions):
+ *   - float pointers named params, x, s0, out, A, b are DEVICE pointers to
+ *     C-contiguous float32 arrays owned by the caller; the library never
+ *     frees them.  out must not alias any input.
+ *   - x is [B, T, m]; s0 is [B, D]; out is [B, T, D] and receives s_1..s_T.
+ *   - pointers named *_hist, *_iters, iters_out, profile are HOST pointers.
+ *   - calls block until the result is complete on the device.
+ *   - on a negative (error) status nothing is written to out; the message
+ *     is available from pn_last_error() on the calling thread.
+ *   - thread-safe when concurrent calls use distinct streams and workspaces.
+ */
+#ifndef PN_H
+#define PN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Transition maps f(p, x) (p = previous state, x = input at this step).
+ *  PN_CELL_DIAG_TANH  f = tanh(a * p + x), channel-wise; params a[D];
+ *                     input_dim must equal D.  Any D >= 1.
+ *  PN_CELL_TANH_RNN   f = tanh(W p + U x + b); params W[D*D] | U[D*m] | b[D]
+ *                     (row-major, W[i*D+k] multiplies p_k into output i).
+ *                     1 <= D <= 64.
+ *  PN_CELL_GRU        gated recurrent unit with torch.nn.GRU's equations and
+ *                     gate order (r, z, n); params W_ih[3D*m] | W_hh[3D*D] |
+ *                     b_ih[3D] | b_hh[3D].  1 <= D <= 64.
+ * The RNN cell is the application the article names [PN §1.3.2]. */
+enum { PN_CELL_DIAG_TANH = 0, PN_CELL_TANH_RNN = 1, PN_CELL_GRU = 2 };
+
+/* Jacobian approximations (see above).  Every cell supports every mode. */
+enum { PN_JACOBI = 0, PN_PICARD = 1, PN_QUASI_NEWTON = 2, PN_NEWTON = 3 };
+
+/* Status codes. */
+enum {
+    PN_OK = 0,              /* converged: final r <= tol                       */
+    PN_NOT_CONVERGED = 1,   /* max_iter updates applied; out = last iterate     */
+    PN_NONFINITE = 2,       /* r became NaN/Inf; out = the offending iterate     */
+    PN_EINVAL = -1,         /* bad argument (null pointer, negative size, ...)  */
+    PN_EUNSUPPORTED = -2,   /* valid but unsupported shape (e.g. D > 64 RNN)    */
+    PN_EHIP = -3,           /* a HIP runtime call failed                         */
+    PN_EWORKSPACE = -4      /* workspace missing, misaligned or too small        */
+};
+
+typedef struct pn_cell {
+    int32_t kind;        /* PN_CELL_*                                        */
+    int32_t input_dim;   /* m, the width of x (>= 1; == D for DIAG_TANH)      */
+} pn_cell;
+
+/* Optional per-call measurements of the library's own kernels, taken with
+ * HIP events on the call's stream.  "apply" is the fused per-iteration
+ * kernel (cell + Jacobian + scan replay + damping + residual + next
+ * aggregate); its algorithmic bytes are what the iteration must move:
+ * read x and s^(i), write s^(i+1). */
+typedef struct pn_profile {
+    double apply_ms;          /* summed device time of apply launches       */
+    int32_t apply_launches;   /* launches, including early-exit ones          */
+    double apply_bytes;       /* summed algorithmic bytes of those launches   */
+    double apply_flops;       /* summed algorithmic flops (dense compose etc.)*/
+    double carry_ms;          /* summed device time of the carry kernel       */
+    int32_t carry_launches;
+    double total_ms;          /* first launch to last completion              */
+} pn_profile;
+
+typedef struct pn_opts {
+    float damping;            /* (0, 1]; 1 = plain update                      */
+    int32_t chunk;            /* timesteps per tile; 0 = library choice         */
+    int64_t window;           /* 0 = whole horizon, else W >= 1                 */
+    void* stream;             /* hipStream_t; NULL = the null stream            */
+    void* workspace;          /* device memory, 256-byte aligned; NULL = the
+                                 library allocates (stream-ordered) per call   */
+    size_t workspace_bytes;
+    float* resid_hist;        /* host; receives r_0..r_K of each window in
+                                 order (truncated to resid_hist_len)           */
+    int32_t resid_hist_len;
+    int32_t* window_iters;    /* host; updates per window (truncated)          */
+    int64_t window_iters_len;
+    pn_profile* profile;      /* host; NULL = no event timing                   */
+} pn_opts;
+
+/* Fill *o with the defaults: damping 1, chunk 0, window 0, everything else
+ * NULL / 0. */
+void pn_opts_init(pn_opts* o);
+
+/* Solve the recurrence for all B sequences [PN §1.1, §1.2].
+ *   cell      host struct, read during the call only.
+ *   params    device, float32, layout per cell kind (above).
+ *   x         device [B, T, m];  s0 device [B, D].
+ *   mode      PN_JACOBI .. PN_NEWTON.
+ *   tol       stop when r <= tol (tol >= 0; 0 runs to max_iter unless r == 0).
+ *   max_iter  cap on updates per window (>= 0).
+ *   out       device [B, T, D].  iters_out host int32: total updates applied
+ *             over all windows.
+ * Returns a status code.  B, T or D equal to 0 is an empty problem: PN_OK
+ * with *iters_out = 0 and nothing written. */
+int pn_eval(const pn_cell* cell, const float* params, const float* x, const float* s0,
+            int64_t B, int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter,
+            float* out, int32_t* iters_out);
+
+/* pn_eval with options (opts may be NULL = defaults). */
+int pn_eval_ex(const pn_cell* cell, const float* params, const float* x, const float* s0,
+               int64_t B, int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter,
+               float* out, int32_t* iters_out, const pn_opts* opts);
+
+/* Bytes of workspace pn_eval_ex needs for this problem with these options
+ * (uses opts->window and opts->chunk; opts may be NULL).  Returns 0 and sets
+ * the last error for invalid or unsupported arguments. */
+size_t pn_workspace_bytes(const pn_cell* cell, int64_t B, int64_t T, int64_t D,
+                          int32_t mode, const pn_opts* opts);
+
+/* The scan step alone [PN §2.1]: out_t = A_t out_{t-1} + b_t, out_0 = s0,
+ * for t = 1..T.  A is device [B, T, D] (dense = 0: diagonal A_t) or
+ * [B, T, D, D] (dense = 1, row-major, 1 <= D <= 64); b device [B, T, D];
+ * s0 device [B, D]; out device [B, T, D].  Uses opts->stream, workspace,
+ * chunk; returns PN_OK or an error code. */
+int pn_affine_scan(const float* A, const float* b, const float* s0, int64_t B, int64_t T,
+                   int64_t D, int32_t dense, float* out, const pn_opts* opts);
+
+/* Workspace bytes for pn_affine_scan. */
+size_t pn_affine_scan_workspace_bytes(int64_t B, int64_t T, int64_t D, int32_t dense,
+                                      const pn_opts* opts);
+
+/* Message of the last error on this thread ("" if none).  The pointer stays
+ * valid until the next library call on the same thread. */
+const char* pn_last_error(void);
+
+/* Library version string, e.g. "pn 0.1.0 gfx950". */
+const char* pn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PN_H */

@@ -1,0 +1,219 @@
+"""Python binding of libpn (parallel-in-time evaluation of nonlinear recurrences).
+
+Argument marshalling only: every step of the solve runs in the HIP kernels of
+``libpn.so``; torch is used for device memory and the current stream.  The
+library must have been built (``python -m newton_evaluation_nonlinear_amd._build``);
+there is no fallback of any kind.
+
+    out, iters, status = pn.eval(cell, params, x, s0, mode=pn.QUASI_NEWTON, tol=1e-5)
+
+The method, the stop rule and all layouts are documented in include/pn.h.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpn.so")
+
+CELL_DIAG_TANH, CELL_TANH_RNN, CELL_GRU = 0, 1, 2
+JACOBI, PICARD, QUASI_NEWTON, NEWTON = 0, 1, 2, 3
+OK, NOT_CONVERGED, NONFINITE = 0, 1, 2
+EINVAL, EUNSUPPORTED, EHIP, EWORKSPACE = -1, -2, -3, -4
+
+EXPORTED = ("pn_opts_init", "pn_eval", "pn_eval_ex", "pn_workspace_bytes", "pn_affine_scan",
+            "pn_affine_scan_workspace_bytes", "pn_last_error", "pn_version")
+
+
+class PnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libpn error {code}: {msg}")
+        self.code = code
+
+
+class Cell(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("input_dim", ctypes.c_int32)]
+
+
+class Profile(ctypes.Structure):
+    _fields_ = [("apply_ms", ctypes.c_double), ("apply_launches", ctypes.c_int32),
+                ("apply_bytes", ctypes.c_double), ("apply_flops", ctypes.c_double),
+                ("carry_ms", ctypes.c_double), ("carry_launches", ctypes.c_int32),
+                ("total_ms", ctypes.c_double)]
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("damping", ctypes.c_float), ("chunk", ctypes.c_int32), ("window", ctypes.c_int64),
+                ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t),
+                ("resid_hist", ctypes.POINTER(ctypes.c_float)), ("resid_hist_len", ctypes.c_int32),
+                ("window_iters", ctypes.POINTER(ctypes.c_int32)),
+                ("window_iters_len", ctypes.c_int64),
+                ("profile", ctypes.POINTER(Profile))]
+
+
+_lib = None
+
+
+def lib():
+    """Load libpn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m newton_evaluation_nonlinear_amd._build`")
+        L = ctypes.CDLL(LIB_PATH)
+        f = ctypes.c_float
+        i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        L.pn_opts_init.argtypes = [ctypes.POINTER(Opts)]
+        L.pn_opts_init.restype = None
+        sig = [ctypes.POINTER(Cell), vp, vp, vp, i64, i64, i64, i32, f, i32, vp,
+               ctypes.POINTER(i32)]
+        L.pn_eval.argtypes = sig
+        L.pn_eval.restype = ctypes.c_int
+        L.pn_eval_ex.argtypes = sig + [ctypes.POINTER(Opts)]
+        L.pn_eval_ex.restype = ctypes.c_int
+        L.pn_workspace_bytes.argtypes = [ctypes.POINTER(Cell), i64, i64, i64, i32, ctypes.POINTER(Opts)]
+        L.pn_workspace_bytes.restype = ctypes.c_size_t
+        L.pn_affine_scan.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, ctypes.POINTER(Opts)]
+        L.pn_affine_scan.restype = ctypes.c_int
+        L.pn_affine_scan_workspace_bytes.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Opts)]
+        L.pn_affine_scan_workspace_bytes.restype = ctypes.c_size_t
+        L.pn_last_error.argtypes = []
+        L.pn_last_error.restype = ctypes.c_char_p
+        L.pn_version.argtypes = []
+        L.pn_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def version():
+    return lib().pn_version().decode()
+
+
+def last_error():
+    return lib().pn_last_error().decode()
+
+
+def _dev_f32(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) torch tensor")
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous float32")
+    return t.data_ptr()
+
+
+def _stream_ptr(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def make_opts(damping=1.0, window=0, chunk=0, stream=None):
+    o = Opts()
+    lib().pn_opts_init(ctypes.byref(o))
+    o.damping = float(damping)
+    o.window = int(window)
+    o.chunk = int(chunk)
+    o.stream = stream
+    return o
+
+
+def workspace_bytes(cell_kind, input_dim, B, T, D, mode, damping=1.0, window=0, chunk=0):
+    o = make_opts(damping, window, chunk)
+    c = Cell(cell_kind, input_dim)
+    n = lib().pn_workspace_bytes(ctypes.byref(c), B, T, D, mode, ctypes.byref(o))
+    if n == 0:
+        raise PnError(EINVAL, last_error())
+    return n
+
+
+class Result:
+    """Outcome of one solve: trajectory, total updates, status and diagnostics."""
+
+    def __init__(self, out, iters, status, window_iters, resid_hist, profile):
+        self.out, self.iters, self.status = out, iters, status
+        self.window_iters, self.resid_hist, self.profile = window_iters, resid_hist, profile
+
+    def __iter__(self):
+        return iter((self.out, self.iters, self.status))
+
+
+def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, damping=1.0,
+         window=0, chunk=0, out=None, history=False, profile=False, workspace=None):
+    """Solve s_t = f(s_{t-1}, x_t) for t = 1..T over the batch; see include/pn.h.
+
+    params, x [B,T,m], s0 [B,D] are float32 tensors on one HIP device.
+    Returns a ``Result`` (unpacks as ``out, iters, status``).  Negative
+    library statuses raise ``PnError``.
+    """
+    B, T, m = x.shape
+    D = s0.shape[1]
+    if s0.shape[0] != B:
+        raise ValueError("x and s0 disagree on B")
+    W = T if window in (0, None) else int(window)
+    if max_iter is None:
+        max_iter = W
+    dev = x.device
+    if out is None:
+        out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+    c = Cell(int(cell_kind), int(m))
+    o = make_opts(damping, window or 0, chunk, _stream_ptr(dev))
+    nbytes = lib().pn_workspace_bytes(ctypes.byref(c), B, T, D, int(mode), ctypes.byref(o))
+    if nbytes == 0:
+        raise PnError(EINVAL, last_error())
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    base = workspace.data_ptr()
+    aligned = (base + 255) // 256 * 256
+    o.workspace = aligned
+    o.workspace_bytes = workspace.numel() - (aligned - base)
+    nwin = max(1, -(-T // W)) if T > 0 else 1
+    wit = (ctypes.c_int32 * nwin)()
+    o.window_iters = wit
+    o.window_iters_len = nwin
+    hist = None
+    if history:
+        hlen = min(nwin * (int(max_iter) + 1), 1 << 22)
+        hist = (ctypes.c_float * hlen)()
+        o.resid_hist = hist
+        o.resid_hist_len = hlen
+    prof = Profile() if profile else None
+    if prof is not None:
+        o.profile = ctypes.pointer(prof)
+    iters = ctypes.c_int32(0)
+    rc = lib().pn_eval_ex(ctypes.byref(c), _dev_f32(params, "params"), _dev_f32(x, "x"),
+                          _dev_f32(s0, "s0"), B, T, D, int(mode), float(tol), int(max_iter),
+                          _dev_f32(out, "out"), ctypes.byref(iters), ctypes.byref(o))
+    if rc < 0:
+        raise PnError(rc, last_error())
+    witer = list(wit)
+    rh = None
+    if history:
+        n = sum(k + 1 for k in witer[:nwin])
+        rh = list(hist[:min(n, len(hist))])
+    pd = None
+    if prof is not None:
+        pd = {k: getattr(prof, k) for k, _ in Profile._fields_}
+    return Result(out, int(iters.value), int(rc), witer, rh, pd)
+
+
+def affine_scan(A, b, s0, dense=False, chunk=0, out=None):
+    """out_t = A_t out_{t-1} + b_t (A diagonal [B,T,D] or dense [B,T,D,D])."""
+    B, T, D = b.shape
+    if out is None:
+        out = torch.empty_like(b)
+    o = make_opts(chunk=chunk, stream=_stream_ptr(b.device))
+    nbytes = lib().pn_affine_scan_workspace_bytes(B, T, D, int(dense), ctypes.byref(o))
+    if nbytes == 0:
+        raise PnError(EINVAL, last_error())
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=b.device)
+    base = ws.data_ptr()
+    aligned = (base + 255) // 256 * 256
+    o.workspace = aligned
+    o.workspace_bytes = ws.numel() - (aligned - base)
+    rc = lib().pn_affine_scan(_dev_f32(A, "A"), _dev_f32(b, "b"), _dev_f32(s0, "s0"), B, T, D,
+                              int(dense), _dev_f32(out, "out"), ctypes.byref(o))
+    if rc < 0:
+        raise PnError(rc, last_error())
+    return out

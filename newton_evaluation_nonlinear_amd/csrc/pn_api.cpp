@@ -1,0 +1,533 @@
+// C interface and host-side iteration driver of libpn.
+//
+// One call = one stream.  For every window the driver launches
+//   prologue                      maps of iteration 0 (at s^(0) = s0) + r_0
+//   repeat i = 0, 1, ...:
+//     carry(i)   scan of the chunk maps; block 0 first reduces the residual
+//                of the previous pass and takes the stop decision for i,
+//                publishing it on the device and in pinned host memory
+//     apply(i)   fused update s^(i) -> s^(i+1) (exits at once if stopped)
+// The host reads the decision of carry(i) while apply(i) runs, so the GPU is
+// never idle waiting for the host; after the stop, one apply launch exits
+// immediately.  Stop rule and counting follow include/pn.h.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/pn.h"
+#include "pn_internal.hpp"
+
+namespace {
+
+using namespace pn;
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+#define PN_HIP(call)                                                                    \
+    do {                                                                                \
+        hipError_t e_ = (call);                                                         \
+        if (e_ != hipSuccess)                                                           \
+            return fail(PN_EHIP, "%s failed: %s", #call, hipGetErrorString(e_));        \
+    } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int next_pow2(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+// ---------------------------------------------------------------- planning
+struct Plan {
+    int kind, mode, D, m, B;
+    int64_t T, W;          // horizon, window length
+    int L, NC;             // chunk length, chunks of a full window
+    int DP, cpb;           // padded D (matrix cells), channels per block (diag cell)
+    bool dense, matrix_cell;
+    int nblocks;
+    size_t off_ctrl, off_rpart, off_aggA, off_aggB, off_carry, off_halo, off_w, total;
+};
+
+int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int32_t mode,
+              const pn_opts* o) {
+    p.kind = cell->kind;
+    p.mode = mode;
+    p.D = static_cast<int>(D);
+    p.m = cell->input_dim;
+    p.B = static_cast<int>(B);
+    p.T = T;
+    const int64_t window = o ? o->window : 0;
+    p.W = (window <= 0 || window > T) ? T : window;
+    const int chunk = o ? o->chunk : 0;
+    p.matrix_cell = p.kind != PN_CELL_DIAG_TANH;
+    p.dense = p.matrix_cell && mode == PN_NEWTON;
+    if (!p.matrix_cell) {
+        p.cpb = std::min(256, ((p.D + 63) / 64) * 64);
+        if (chunk > 0) {
+            p.L = chunk;
+        } else {
+            // aim for about 2^20 threads in flight over B x D x chunks
+            int64_t L = 16;
+            while (L < 1024 && static_cast<int64_t>(B) * D * ((p.W + 2 * L - 1) / (2 * L)) >= (1 << 20)) L *= 2;
+            p.L = static_cast<int>(L);
+        }
+        p.L = static_cast<int>(std::min<int64_t>(p.L, p.W));
+        p.NC = static_cast<int>((p.W + p.L - 1) / p.L);
+        DiagArgs a{};
+        a.B = p.B; a.D = p.D; a.NC = p.NC; a.cpb = p.cpb;
+        p.nblocks = diag_tanh_nblocks(a);
+        p.DP = 0;
+    } else {
+        p.DP = std::max(4, next_pow2(p.D));
+        const int Lmax = std::min(64, 16 * (kThreads / p.DP));
+        int L = Lmax;
+        if (chunk > 0) {
+            L = std::min(chunk, Lmax);
+        } else {
+            while (L > 4 && cell_pass_lds_bytes(p.kind, p.DP, p.dense, L, p.m) > 64 * 1024) L /= 2;
+            while (L > 16 && static_cast<int64_t>(B) * ((p.W + L - 1) / L) < 1024) L /= 2;
+        }
+        p.L = static_cast<int>(std::min<int64_t>(L, p.W));
+        p.NC = static_cast<int>((p.W + p.L - 1) / p.L);
+        p.nblocks = p.NC * p.B;
+        if (cell_pass_lds_bytes(p.kind, p.DP, p.dense, p.L, p.m) > 160 * 1024)
+            return fail(PN_EUNSUPPORTED, "chunk of %d steps needs too much LDS for D=%d, m=%d", p.L, p.D, p.m);
+    }
+    const size_t bnd = static_cast<size_t>(p.B) * p.NC * p.D;
+    size_t off = 0;
+    p.off_ctrl = off; off = align_up(off + sizeof(Ctrl));
+    p.off_rpart = off; off = align_up(off + sizeof(uint32_t) * p.nblocks);
+    p.off_aggA = off; off = align_up(off + sizeof(float) * bnd * (p.dense ? p.D : 1));
+    p.off_aggB = off; off = align_up(off + sizeof(float) * bnd);
+    p.off_carry = off; off = align_up(off + sizeof(float) * bnd);
+    p.off_halo = off; off = align_up(off + sizeof(float) * 2 * bnd);
+    p.off_w = off;
+    if (p.matrix_cell) off = align_up(off + sizeof(float) * prepared_weight_floats(p.kind, p.DP, p.m));
+    p.total = off;
+    return PN_OK;
+}
+
+int validate(const pn_cell* cell, const float* params, const float* x, const float* s0, int64_t B,
+             int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter, const float* out,
+             const int32_t* iters_out, const pn_opts* o) {
+    if (!cell) return fail(PN_EINVAL, "cell is NULL");
+    if (!iters_out) return fail(PN_EINVAL, "iters_out is NULL");
+    if (B < 0 || T < 0 || D < 0) return fail(PN_EINVAL, "negative size (B=%lld T=%lld D=%lld)",
+                                             (long long)B, (long long)T, (long long)D);
+    if (cell->kind < PN_CELL_DIAG_TANH || cell->kind > PN_CELL_GRU)
+        return fail(PN_EINVAL, "unknown cell kind %d", cell->kind);
+    if (mode < PN_JACOBI || mode > PN_NEWTON) return fail(PN_EINVAL, "unknown mode %d", mode);
+    if (cell->input_dim < 1) return fail(PN_EINVAL, "input_dim must be >= 1");
+    if (cell->kind == PN_CELL_DIAG_TANH && cell->input_dim != D && D > 0)
+        return fail(PN_EINVAL, "diag-tanh cell needs input_dim == D");
+    if (!(tol >= 0.0f) || std::isinf(tol)) return fail(PN_EINVAL, "tol must be finite and >= 0");
+    if (max_iter < 0) return fail(PN_EINVAL, "max_iter must be >= 0");
+    if (o) {
+        if (!(o->damping > 0.0f && o->damping <= 1.0f)) return fail(PN_EINVAL, "damping must lie in (0, 1]");
+        if (o->window < 0) return fail(PN_EINVAL, "window must be >= 0");
+        if (o->chunk < 0 || o->chunk > (1 << 20)) return fail(PN_EINVAL, "chunk out of range");
+        if (o->resid_hist_len < 0 || o->window_iters_len < 0) return fail(PN_EINVAL, "negative history length");
+        if (o->resid_hist_len > 0 && !o->resid_hist) return fail(PN_EINVAL, "resid_hist is NULL");
+        if (o->window_iters_len > 0 && !o->window_iters) return fail(PN_EINVAL, "window_iters is NULL");
+        if (o->workspace && (reinterpret_cast<uintptr_t>(o->workspace) % kAlign) != 0)
+            return fail(PN_EWORKSPACE, "workspace must be 256-byte aligned");
+    }
+    if (B == 0 || T == 0 || D == 0) return PN_OK;
+    if (!params || !x || !s0 || !out) return fail(PN_EINVAL, "a device pointer is NULL");
+    if (cell->kind != PN_CELL_DIAG_TANH && D > 64)
+        return fail(PN_EUNSUPPORTED, "matrix cells support D <= 64 (got %lld)", (long long)D);
+    if (B > 65535) return fail(PN_EUNSUPPORTED, "B must be <= 65535");
+    if (T >= (int64_t(1) << 31) || D >= (int64_t(1) << 24) || cell->input_dim >= (1 << 24))
+        return fail(PN_EUNSUPPORTED, "size too large");
+    return PN_OK;
+}
+
+// ---------------------------------------------------------------- per-thread resources
+struct ThreadRes {
+    int device = -1;
+    HostRec* host = nullptr;     // pinned
+    HostRec* host_dev = nullptr; // device-usable alias
+    hipEvent_t sync_ev = nullptr;
+    std::vector<hipEvent_t> timing;   // pool of timing events
+};
+thread_local ThreadRes g_res;
+
+int get_res(ThreadRes** out) {
+    int dev = 0;
+    PN_HIP(hipGetDevice(&dev));
+    ThreadRes& r = g_res;
+    if (r.device != dev) {
+        if (!r.host) {
+            void* p = nullptr;
+            PN_HIP(hipHostMalloc(&p, sizeof(HostRec), hipHostMallocMapped | hipHostMallocCoherent));
+            r.host = static_cast<HostRec*>(p);
+        }
+        void* dp = nullptr;
+        PN_HIP(hipHostGetDevicePointer(&dp, r.host, 0));
+        r.host_dev = static_cast<HostRec*>(dp);
+        if (r.sync_ev) (void)hipEventDestroy(r.sync_ev);
+        for (auto e : r.timing) (void)hipEventDestroy(e);
+        r.timing.clear();
+        PN_HIP(hipEventCreateWithFlags(&r.sync_ev, hipEventDisableTiming));
+        r.device = dev;
+    }
+    *out = &r;
+    return PN_OK;
+}
+
+int timing_event(ThreadRes* r, size_t idx, hipEvent_t* ev) {
+    while (r->timing.size() <= idx) {
+        hipEvent_t e;
+        PN_HIP(hipEventCreate(&e));
+        r->timing.push_back(e);
+    }
+    *ev = r->timing[idx];
+    return PN_OK;
+}
+
+// ---------------------------------------------------------------- the solve
+struct Timing {
+    bool on = false;
+    std::vector<std::pair<size_t, size_t>> apply, carry;   // event index pairs
+    std::vector<double> apply_bytes, apply_flops;
+    size_t next = 0;
+};
+
+struct SolveCtx {
+    const Plan* p;
+    hipStream_t st;
+    char* ws;
+    ThreadRes* res;
+    const float* params;
+    float tol, lam;
+    int32_t max_iter;
+    Timing* tm;
+    std::vector<float>* hist;
+};
+
+double apply_bytes(const Plan& p, int Tw, bool first) {
+    // algorithmic bytes of one apply launch: read x, read s^(i) (not for
+    // i = 0, where s^(0) = s0 is implicit), write s^(i+1)
+    const double rows = static_cast<double>(p.B) * Tw;
+    return rows * 4.0 * (p.m + (first ? 1 : 2) * p.D);
+}
+
+double apply_flops(const Plan& p, int Tw) {
+    // dense Newton: one D x D compose per step (2 D^3) dominates
+    if (!p.dense) return 0.0;
+    return static_cast<double>(p.B) * Tw * 2.0 * p.D * p.D * p.D;
+}
+
+int record(SolveCtx& c, size_t* idx) {
+    hipEvent_t e;
+    int rc = timing_event(c.res, c.tm->next, &e);
+    if (rc != PN_OK) return rc;
+    PN_HIP(hipEventRecord(e, c.st));
+    *idx = c.tm->next++;
+    return PN_OK;
+}
+
+// Solve one window.  Writes *K (updates) and *status.
+int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, const float* s0,
+                 int64_t s0s, int Tw, int* K, int* status) {
+    const Plan& p = *c.p;
+    const int NC = (Tw + p.L - 1) / p.L;
+    Ctrl* ctrl = reinterpret_cast<Ctrl*>(c.ws + p.off_ctrl);
+    uint32_t* rpart = reinterpret_cast<uint32_t*>(c.ws + p.off_rpart);
+    float* aggA = reinterpret_cast<float*>(c.ws + p.off_aggA);
+    float* aggB = reinterpret_cast<float*>(c.ws + p.off_aggB);
+    float* carry = reinterpret_cast<float*>(c.ws + p.off_carry);
+    float* halo = reinterpret_cast<float*>(c.ws + p.off_halo);
+    const float* w = reinterpret_cast<const float*>(c.ws + p.off_w);
+
+    DiagArgs da{};
+    CellArgs ca{};
+    int nblocks;
+    if (!p.matrix_cell) {
+        da.a = c.params; da.x = x; da.xs = xs; da.s = s; da.ss = ss; da.s0 = s0; da.s0s = s0s;
+        da.B = p.B; da.Tw = Tw; da.D = p.D; da.L = p.L; da.NC = NC; da.cpb = p.cpb;
+        da.aggA = aggA; da.aggB = aggB; da.carry = carry; da.halo = halo; da.rpart = rpart;
+        da.ctrl = ctrl; da.mode = p.mode; da.lam = c.lam; da.undamped = c.lam == 1.0f;
+        nblocks = diag_tanh_nblocks(da);
+    } else {
+        ca.w = w; ca.x = x; ca.xs = xs; ca.s = s; ca.ss = ss; ca.s0 = s0; ca.s0s = s0s;
+        ca.B = p.B; ca.Tw = Tw; ca.D = p.D; ca.m = p.m; ca.L = p.L; ca.NC = NC;
+        ca.aggA = aggA; ca.aggB = aggB; ca.carry = carry; ca.halo = halo; ca.rpart = rpart;
+        ca.ctrl = ctrl; ca.mode = p.mode; ca.lam = c.lam; ca.undamped = c.lam == 1.0f;
+        nblocks = cell_pass_nblocks(ca);
+    }
+    auto launch_pass = [&](int phase, int iter) -> hipError_t {
+        if (!p.matrix_cell) {
+            da.iter = iter;
+            return launch_diag_tanh_pass(phase, da, c.st);
+        }
+        ca.iter = iter;
+        return launch_cell_pass(p.kind, p.DP, p.dense, phase, ca, c.st);
+    };
+
+    PN_HIP(launch_pass(kPrologue, 0));
+    CarryArgs cy{};
+    cy.aggA = aggA; cy.aggB = aggB; cy.carry = carry; cy.s0 = s0; cy.s0s = s0s;
+    cy.B = p.B; cy.D = p.D; cy.NC = NC; cy.do_check = 1;
+    cy.chk.rpart = rpart; cy.chk.nparts = nblocks; cy.chk.max_iter = c.max_iter; cy.chk.tol = c.tol;
+    cy.chk.ctrl = ctrl; cy.chk.host = c.res->host_dev;
+    volatile HostRec* hr = c.res->host;
+    for (int i = 0;; ++i) {
+        cy.chk.iter = i;
+        size_t e0 = 0, e1 = 0;
+        if (c.tm->on) { int rc = record(c, &e0); if (rc) return rc; }
+        PN_HIP(p.dense ? launch_dense_carry(cy, c.st) : launch_diag_carry(cy, c.st));
+        if (c.tm->on) { int rc = record(c, &e1); if (rc) return rc; c.tm->carry.push_back({e0, e1}); }
+        PN_HIP(hipEventRecord(c.res->sync_ev, c.st));
+        if (c.tm->on) { int rc = record(c, &e0); if (rc) return rc; }
+        PN_HIP(launch_pass(i == 0 ? kFirst : kSteady, i));
+        if (c.tm->on) {
+            int rc = record(c, &e1);
+            if (rc) return rc;
+            c.tm->apply.push_back({e0, e1});
+            c.tm->apply_bytes.push_back(0.0);   // filled below once we know if it ran
+            c.tm->apply_flops.push_back(0.0);
+        }
+        PN_HIP(hipEventSynchronize(c.res->sync_ev));
+        const int stop = hr->stop;
+        const int st = hr->status;
+        const uint32_t rb = hr->r_bits;
+        const int it = hr->iter;
+        if (it != i) return fail(PN_EHIP, "control record out of sequence (%d vs %d)", it, i);
+        float r;
+        std::memcpy(&r, &rb, sizeof(r));
+        if (c.hist) c.hist->push_back(r);
+        if (c.tm->on && !stop) {
+            c.tm->apply_bytes.back() = apply_bytes(p, Tw, i == 0) ;
+            c.tm->apply_flops.back() = apply_flops(p, Tw);
+        }
+        if (stop) {
+            *K = i;
+            *status = st;
+            break;
+        }
+    }
+    if (*K == 0) PN_HIP(launch_fill(s, ss, s0, s0s, p.B, Tw, p.D, c.st));
+    return PN_OK;
+}
+
+int eval_impl(const pn_cell* cell, const float* params, const float* x, const float* s0, int64_t B,
+              int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter, float* out,
+              int32_t* iters_out, const pn_opts* o) {
+    g_err.clear();
+    int rc = validate(cell, params, x, s0, B, T, D, mode, tol, max_iter, out, iters_out, o);
+    if (rc != PN_OK) return rc;
+    if (o && o->profile) std::memset(o->profile, 0, sizeof(pn_profile));
+    if (B == 0 || T == 0 || D == 0) {
+        *iters_out = 0;
+        if (o && o->window_iters_len > 0) o->window_iters[0] = 0;
+        if (o && o->resid_hist_len > 0) o->resid_hist[0] = 0.0f;
+        return PN_OK;
+    }
+    Plan p;
+    rc = make_plan(p, cell, B, T, D, mode, o);
+    if (rc != PN_OK) return rc;
+    if (o && o->workspace && o->workspace_bytes < p.total)
+        return fail(PN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                    o->workspace_bytes, p.total);
+    ThreadRes* res;
+    rc = get_res(&res);
+    if (rc != PN_OK) return rc;
+    hipStream_t st = o ? static_cast<hipStream_t>(o->stream) : nullptr;
+    char* ws = nullptr;
+    bool own_ws = false;
+    if (o && o->workspace) {
+        ws = static_cast<char*>(o->workspace);
+    } else {
+        void* q = nullptr;
+        PN_HIP(hipMallocAsync(&q, p.total, st));
+        ws = static_cast<char*>(q);
+        own_ws = true;
+    }
+    Timing tm;
+    tm.on = o && o->profile;
+    std::vector<float> hist;
+    SolveCtx c{&p, st, ws, res, params, tol, o ? o->damping : 1.0f, max_iter, &tm, &hist};
+    if (p.matrix_cell)
+        PN_HIP(launch_prep_weights(p.kind, params, reinterpret_cast<float*>(ws + p.off_w), p.D, p.DP, p.m, st));
+    size_t ev_first = 0;
+    if (tm.on) { rc = record(c, &ev_first); if (rc) return rc; }
+    int total = 0, overall = PN_OK;
+    std::vector<int> wit;
+    const int64_t m = p.m;
+    for (int64_t w0 = 0; w0 < T; w0 += p.W) {
+        const int Tw = static_cast<int>(std::min<int64_t>(p.W, T - w0));
+        const float* xw = x + w0 * m;
+        float* sw = out + w0 * D;
+        const float* s0w = w0 == 0 ? s0 : out + (w0 - 1) * D;
+        const int64_t s0s = w0 == 0 ? D : T * D;
+        int K = 0, status = PN_OK;
+        rc = solve_window(c, xw, T * m, sw, T * D, s0w, s0s, Tw, &K, &status);
+        if (rc != PN_OK) {
+            if (own_ws) { (void)hipFreeAsync(ws, st); (void)hipStreamSynchronize(st); }
+            return rc;
+        }
+        total += K;
+        wit.push_back(K);
+        if (status == PN_NONFINITE) { overall = PN_NONFINITE; break; }
+        if (status == PN_NOT_CONVERGED) overall = PN_NOT_CONVERGED;
+    }
+    size_t ev_last = 0;
+    if (tm.on) { rc = record(c, &ev_last); if (rc) return rc; }
+    PN_HIP(hipStreamSynchronize(st));
+    if (own_ws) {
+        PN_HIP(hipFreeAsync(ws, st));
+        PN_HIP(hipStreamSynchronize(st));
+    }
+    *iters_out = total;
+    if (o) {
+        for (int64_t k = 0; k < o->window_iters_len && k < static_cast<int64_t>(wit.size()); ++k)
+            o->window_iters[k] = wit[k];
+        for (int32_t k = 0; k < o->resid_hist_len && k < static_cast<int32_t>(hist.size()); ++k)
+            o->resid_hist[k] = hist[k];
+        if (o->profile) {
+            pn_profile* pr = o->profile;
+            for (size_t k = 0; k < tm.apply.size(); ++k) {
+                float ms = 0.0f;
+                PN_HIP(hipEventElapsedTime(&ms, res->timing[tm.apply[k].first], res->timing[tm.apply[k].second]));
+                pr->apply_ms += ms;
+                pr->apply_bytes += tm.apply_bytes[k];
+                pr->apply_flops += tm.apply_flops[k];
+            }
+            pr->apply_launches = static_cast<int32_t>(tm.apply.size());
+            for (auto& pq : tm.carry) {
+                float ms = 0.0f;
+                PN_HIP(hipEventElapsedTime(&ms, res->timing[pq.first], res->timing[pq.second]));
+                pr->carry_ms += ms;
+            }
+            pr->carry_launches = static_cast<int32_t>(tm.carry.size());
+            float ms = 0.0f;
+            PN_HIP(hipEventElapsedTime(&ms, res->timing[ev_first], res->timing[ev_last]));
+            pr->total_ms = ms;
+        }
+    }
+    return overall;
+}
+
+}  // namespace
+
+extern "C" {
+
+void pn_opts_init(pn_opts* o) {
+    if (!o) return;
+    std::memset(o, 0, sizeof(*o));
+    o->damping = 1.0f;
+}
+
+int pn_eval_ex(const pn_cell* cell, const float* params, const float* x, const float* s0, int64_t B,
+               int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter, float* out,
+               int32_t* iters_out, const pn_opts* opts) {
+    return eval_impl(cell, params, x, s0, B, T, D, mode, tol, max_iter, out, iters_out, opts);
+}
+
+int pn_eval(const pn_cell* cell, const float* params, const float* x, const float* s0, int64_t B,
+            int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter, float* out,
+            int32_t* iters_out) {
+    return eval_impl(cell, params, x, s0, B, T, D, mode, tol, max_iter, out, iters_out, nullptr);
+}
+
+size_t pn_workspace_bytes(const pn_cell* cell, int64_t B, int64_t T, int64_t D, int32_t mode,
+                          const pn_opts* opts) {
+    g_err.clear();
+    int32_t dummy = 0;
+    static const float kDummy = 0.0f;
+    int rc = validate(cell, &kDummy, &kDummy, &kDummy, B, T, D, mode, 0.0f, 0, &kDummy, &dummy, opts);
+    if (rc != PN_OK) return 0;
+    if (B == 0 || T == 0 || D == 0) return kAlign;
+    Plan p;
+    if (make_plan(p, cell, B, T, D, mode, opts) != PN_OK) return 0;
+    return p.total;
+}
+
+size_t pn_affine_scan_workspace_bytes(int64_t B, int64_t T, int64_t D, int32_t dense,
+                                      const pn_opts* opts) {
+    g_err.clear();
+    if (B < 0 || T < 0 || D < 0) { fail(PN_EINVAL, "negative size"); return 0; }
+    if (dense && D > 64) { fail(PN_EUNSUPPORTED, "dense scan supports D <= 64"); return 0; }
+    if (B == 0 || T == 0 || D == 0) return kAlign;
+    const int chunk = opts && opts->chunk > 0 ? opts->chunk : (dense ? 32 : 128);
+    const int64_t L = std::min<int64_t>(chunk, T);
+    const int64_t NC = (T + L - 1) / L;
+    const size_t bnd = static_cast<size_t>(B) * NC * D;
+    return align_up(sizeof(float) * bnd * (dense ? D : 1)) + 2 * align_up(sizeof(float) * bnd);
+}
+
+int pn_affine_scan(const float* A, const float* b, const float* s0, int64_t B, int64_t T, int64_t D,
+                   int32_t dense, float* out, const pn_opts* opts) {
+    g_err.clear();
+    if (B < 0 || T < 0 || D < 0) return fail(PN_EINVAL, "negative size");
+    if (dense != 0 && dense != 1) return fail(PN_EINVAL, "dense must be 0 or 1");
+    if (opts && (opts->chunk < 0 || opts->chunk > (1 << 20))) return fail(PN_EINVAL, "chunk out of range");
+    if (opts && opts->workspace && (reinterpret_cast<uintptr_t>(opts->workspace) % kAlign) != 0)
+        return fail(PN_EWORKSPACE, "workspace must be 256-byte aligned");
+    if (B == 0 || T == 0 || D == 0) return PN_OK;
+    if (!A || !b || !s0 || !out) return fail(PN_EINVAL, "a device pointer is NULL");
+    if (dense && D > 64) return fail(PN_EUNSUPPORTED, "dense scan supports D <= 64");
+    if (B > 65535 || T >= (int64_t(1) << 31)) return fail(PN_EUNSUPPORTED, "size too large");
+    const size_t need = pn_affine_scan_workspace_bytes(B, T, D, dense, opts);
+    hipStream_t st = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
+    char* ws = nullptr;
+    bool own = false;
+    if (opts && opts->workspace) {
+        if (opts->workspace_bytes < need)
+            return fail(PN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                        opts->workspace_bytes, need);
+        ws = static_cast<char*>(opts->workspace);
+    } else {
+        void* q = nullptr;
+        PN_HIP(hipMallocAsync(&q, need, st));
+        ws = static_cast<char*>(q);
+        own = true;
+    }
+    const int chunk = opts && opts->chunk > 0 ? opts->chunk : (dense ? 32 : 128);
+    const int L = static_cast<int>(std::min<int64_t>(chunk, T));
+    const int NC = static_cast<int>((T + L - 1) / L);
+    const size_t bnd = static_cast<size_t>(B) * NC * D;
+    ScanArgs a{};
+    a.A = A; a.b = b; a.out = out;
+    a.B = static_cast<int>(B); a.T = static_cast<int>(T); a.D = static_cast<int>(D); a.L = L; a.NC = NC;
+    a.aggA = reinterpret_cast<float*>(ws);
+    a.aggB = reinterpret_cast<float*>(ws + align_up(sizeof(float) * bnd * (dense ? D : 1)));
+    float* carry = reinterpret_cast<float*>(reinterpret_cast<char*>(a.aggB) + align_up(sizeof(float) * bnd));
+    a.carry = carry;
+    const int DP = dense ? std::max(4, next_pow2(static_cast<int>(D))) : 0;
+    PN_HIP(launch_scan_aggregate(dense != 0, DP, a, st));
+    CarryArgs cy{};
+    cy.aggA = a.aggA; cy.aggB = a.aggB; cy.carry = carry; cy.s0 = s0; cy.s0s = D;
+    cy.B = a.B; cy.D = a.D; cy.NC = NC; cy.do_check = 0;
+    PN_HIP(dense ? launch_dense_carry(cy, st) : launch_diag_carry(cy, st));
+    PN_HIP(launch_scan_apply(dense != 0, DP, a, st));
+    if (own) PN_HIP(hipFreeAsync(ws, st));
+    PN_HIP(hipStreamSynchronize(st));
+    return PN_OK;
+}
+
+const char* pn_last_error(void) { return g_err.c_str(); }
+
+const char* pn_version(void) { return "pn 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,519 @@
+// Matrix cells (tanh RNN, GRU): fused iteration kernel for every mode, the
+// dense carry scan, and the weight preparation kernel.
+//
+// Work split per iteration is the same as for the channel-wise cell (see
+// pn_diag.hip): a tiny carry scan over per-chunk affine maps, then one apply
+// sweep per chunk that replays the recurrence of [PN §1.2] from the carry,
+// stores s^(i+1) and, at the new iterate, produces the residual and the chunk
+// maps of iteration i+1.  Differences:
+//   * the cell couples channels (matrix-vector products), so a chunk is one
+//     workgroup holding all D channels of L consecutive steps in LDS;
+//   * the Jacobian of both cells is a diagonal plus row-scaled copies of the
+//     recurrent weight matrices:
+//         tanh RNN: A_t = diag(1 - v^2) W
+//         GRU     : A_t = diag(z) + diag(cz) W_hz + diag(cn) W_hn + diag(cr) W_hr
+//     so only D-vectors of coefficients per step are kept; the diagonal
+//     modes use the diagonal of A_t (quasi-Newton [PN §2.2.1]), 1 (Picard) or
+//     0 (Jacobi), and Newton uses A_t itself;
+//   * for Newton the chunk map is (prod A_t, folded offset), a D x D matrix
+//     chain [PN §2.1], and the replay is a matrix-vector chain.
+// The input projection U x_t (+ bias) does not depend on the iterate and is
+// computed once per sweep.  D is padded to DP (a power of two <= 64) inside
+// LDS; padded rows/columns are kept at zero.
+
+#include "pn_device.hpp"
+
+namespace pn {
+
+constexpr int kCellTanhRnn = 1;
+constexpr int kCellGru = 2;
+constexpr int kRowsPerThread = 16;   // rows of a chunk evaluated by one thread
+
+template <int CELL> struct CellTraits;
+template <> struct CellTraits<kCellTanhRnn> { static constexpr int NG = 1, NCO = 1; };
+template <> struct CellTraits<kCellGru> { static constexpr int NG = 3, NCO = 4; };
+
+size_t prepared_weight_floats(int kind, int DP, int m) {
+    if (kind == kCellTanhRnn) return static_cast<size_t>(DP) * DP + static_cast<size_t>(m) * DP + 2 * DP;
+    return 3ull * DP * DP + 3ull * m * DP + 9ull * DP;
+}
+
+// ---------------------------------------------------------------- weight prep
+// tanh RNN: WT[k][i] = W[i][k] | UT[q][i] = U[i][q] | bias[i] | wdiag[i]
+// GRU     : WhT[g][k][i] = W_hh[gD+i][k] | WiT[g][q][i] = W_ih[gD+i][q] |
+//           bih[g][i] | bhh[g][i] | whdiag[g][i] = W_hh[gD+i][i]
+__global__ __launch_bounds__(kThreads) void prep_weights_kernel(int kind, const float* __restrict__ p,
+                                                                 float* __restrict__ w, int D, int DP,
+                                                                 int m, int n) {
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += gridDim.x * blockDim.x) {
+        float val = 0.0f;
+        if (kind == kCellTanhRnn) {
+            const float* W = p;
+            const float* U = p + D * D;
+            const float* bb = U + D * m;
+            if (e < DP * DP) {
+                const int k = e / DP, i = e % DP;
+                if (i < D && k < D) val = W[i * D + k];
+            } else if (e < DP * DP + m * DP) {
+                const int f = e - DP * DP, q = f / DP, i = f % DP;
+                if (i < D) val = U[i * m + q];
+            } else if (e < DP * DP + m * DP + DP) {
+                const int i = e - DP * DP - m * DP;
+                if (i < D) val = bb[i];
+            } else {
+                const int i = e - DP * DP - m * DP - DP;
+                if (i < D) val = W[i * D + i];
+            }
+        } else {
+            const float* Wih = p;
+            const float* Whh = p + 3 * D * m;
+            const float* bih = Whh + 3 * D * D;
+            const float* bhh = bih + 3 * D;
+            const int s1 = 3 * DP * DP, s2 = s1 + 3 * m * DP, s3 = s2 + 3 * DP, s4 = s3 + 3 * DP;
+            if (e < s1) {
+                const int g = e / (DP * DP), r = e % (DP * DP), k = r / DP, i = r % DP;
+                if (i < D && k < D) val = Whh[(g * D + i) * D + k];
+            } else if (e < s2) {
+                const int f = e - s1, g = f / (m * DP), r = f % (m * DP), q = r / DP, i = r % DP;
+                if (i < D) val = Wih[(g * D + i) * m + q];
+            } else if (e < s3) {
+                const int f = e - s2, g = f / DP, i = f % DP;
+                if (i < D) val = bih[g * D + i];
+            } else if (e < s4) {
+                const int f = e - s3, g = f / DP, i = f % DP;
+                if (i < D) val = bhh[g * D + i];
+            } else {
+                const int f = e - s4, g = f / DP, i = f % DP;
+                if (i < D) val = Whh[(g * D + i) * D + i];
+            }
+        }
+        w[e] = val;
+    }
+}
+
+hipError_t launch_prep_weights(int kind, const float* params, float* w, int D, int DP, int m,
+                               hipStream_t st) {
+    const int n = static_cast<int>(prepared_weight_floats(kind, DP, m));
+    const int blocks = std::min((n + kThreads - 1) / kThreads, 1024);
+    prep_weights_kernel<<<blocks, kThreads, 0, st>>>(kind, params, w, D, DP, m, n);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- LDS plan
+template <int CELL, int DP, bool DENSE>
+struct Lds {
+    static constexpr int NG = CellTraits<CELL>::NG;
+    static constexpr int NCO = DENSE ? CellTraits<CELL>::NCO : 1;
+    static size_t floats(int L, int m) {
+        size_t f = 2ull * (L + 1) * DP          // P, N
+                 + static_cast<size_t>(NG) * L * DP   // XP
+                 + static_cast<size_t>(L) * DP         // V
+                 + static_cast<size_t>(NCO) * L * DP   // CO
+                 + static_cast<size_t>(L) * m          // X
+                 + DP;                                 // DL (replay vector)
+        if (DENSE) f += 2ull * DP * DP + 2ull * DP;    // M ping-pong, offset ping-pong
+        return f;
+    }
+};
+
+// ---------------------------------------------------------------- cell evaluation
+// For rows j < Lc of a chunk with p_t = Pin[j] (the state one step earlier):
+// V[j] = f_t(p_t) and the Jacobian coefficients CO.  If Sres is given, also
+// folds |Sres[j+1] - V[j]| (the residual of the trajectory held in Sres) into rb.
+template <int CELL, int DP, bool DENSE>
+__device__ __forceinline__ void eval_rows(const float* __restrict__ w, const float* Pin,
+                                          const float* XP, float* V, float* CO, int Lc, int L,
+                                          int D, int m, int mode, const float* Sres, uint32_t& rb) {
+    constexpr int NG = CellTraits<CELL>::NG;
+    constexpr int NRG = kThreads / DP;
+    const int i = threadIdx.x % DP;
+    const int rg = threadIdx.x / DP;
+    float acc[kRowsPerThread][NG];
+#pragma unroll
+    for (int r = 0; r < kRowsPerThread; ++r)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) acc[r][g] = 0.0f;
+    for (int k = 0; k < D; ++k) {
+        float wk[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) wk[g] = w[(g * DP + k) * DP + i];
+#pragma unroll
+        for (int r = 0; r < kRowsPerThread; ++r) {
+            const int j = rg + r * NRG;
+            if (j < Lc) {
+                const float pk = Pin[j * DP + k];
+#pragma unroll
+                for (int g = 0; g < NG; ++g) acc[r][g] += wk[g] * pk;
+            }
+        }
+    }
+    const bool live = i < D;
+#pragma unroll
+    for (int r = 0; r < kRowsPerThread; ++r) {
+        const int j = rg + r * NRG;
+        if (j >= Lc) continue;
+        const int o = j * DP + i;
+        if (!live) {
+            V[o] = 0.0f;
+            if constexpr (DENSE) {
+#pragma unroll
+                for (int q = 0; q < CellTraits<CELL>::NCO; ++q) CO[q * L * DP + o] = 0.0f;
+            } else {
+                CO[o] = 0.0f;
+            }
+            continue;
+        }
+        float v;
+        if constexpr (CELL == kCellTanhRnn) {
+            const float* wdiag = w + DP * DP + m * DP + DP;
+            v = tanh_f(acc[r][0] + XP[o]);
+            const float c1 = 1.0f - v * v;
+            if constexpr (DENSE) {
+                CO[o] = c1;
+            } else {
+                CO[o] = mode == kJacobi ? 0.0f : (mode == kPicard ? 1.0f : c1 * wdiag[i]);
+            }
+        } else {
+            const float* bhh = w + 3 * DP * DP + 3 * m * DP + 3 * DP;
+            const float* whd = bhh + 3 * DP;
+            const float rr = sigmoid_f(XP[o] + acc[r][0] + bhh[i]);
+            const float z = sigmoid_f(XP[L * DP + o] + acc[r][1] + bhh[DP + i]);
+            const float gg = acc[r][2] + bhh[2 * DP + i];
+            const float n = tanh_f(XP[2 * L * DP + o] + rr * gg);
+            const float pi = Pin[o];
+            v = (1.0f - z) * n + z * pi;
+            const float dn = (1.0f - z) * (1.0f - n * n);
+            const float cz = (pi - n) * z * (1.0f - z);
+            const float cn = dn * rr;
+            const float cr = dn * gg * rr * (1.0f - rr);
+            if constexpr (DENSE) {
+                CO[o] = z;
+                CO[L * DP + o] = cz;
+                CO[2 * L * DP + o] = cn;
+                CO[3 * L * DP + o] = cr;
+            } else {
+                const float jd = z + cz * whd[DP + i] + cn * whd[2 * DP + i] + cr * whd[i];
+                CO[o] = mode == kJacobi ? 0.0f : (mode == kPicard ? 1.0f : jd);
+            }
+        }
+        V[o] = v;
+        if (Sres) rb = max(rb, abs_bits(Sres[o + DP] - v));
+    }
+}
+
+// (A_t y)[i] for the dense Jacobian, with y in LDS; row i only.
+template <int CELL, int DP>
+__device__ __forceinline__ float jac_row_apply(const float* __restrict__ w, const float* CO, int o,
+                                               int L, int i, int D, const float* y) {
+    constexpr int NG = CellTraits<CELL>::NG;
+    float acc[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[g] = 0.0f;
+    for (int k = 0; k < D; ++k) {
+        const float yk = y[k];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) acc[g] += w[(g * DP + k) * DP + i] * yk;
+    }
+    if constexpr (CELL == kCellTanhRnn) {
+        return CO[o] * acc[0];
+    } else {
+        return CO[o] * y[i] + CO[L * DP + o] * acc[1] + CO[2 * L * DP + o] * acc[2] +
+               CO[3 * L * DP + o] * acc[0];
+    }
+}
+
+// ---------------------------------------------------------------- the fused pass
+template <int CELL, int DP, bool DENSE, int PHASE>
+__global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
+    if constexpr (PHASE != kPrologue) {
+        if (g.ctrl->stop) return;
+    }
+    extern __shared__ float lds[];
+    constexpr int NG = CellTraits<CELL>::NG;
+    constexpr int NCO = DENSE ? CellTraits<CELL>::NCO : 1;
+    const int L = g.L, m = g.m, D = g.D;
+    const int c = blockIdx.x, b = blockIdx.y;
+    const int t0 = c * L;
+    const int Lc = min(L, g.Tw - t0);
+    const int tid = threadIdx.x;
+    float* P = lds;
+    float* N = P + (L + 1) * DP;
+    float* XP = N + (L + 1) * DP;
+    float* V = XP + NG * L * DP;
+    float* CO = V + L * DP;
+    float* X = CO + NCO * L * DP;
+    float* DL = X + L * m;
+    const float* w = g.w;
+    const size_t ci = static_cast<size_t>(b) * g.NC + c;        // chunk index
+    const float* s0 = g.s0 + b * g.s0s;
+
+    // ---- stage inputs: X rows, then the input projection XP (iterate-free)
+    const float* xg = g.x + b * g.xs + static_cast<int64_t>(t0) * m;
+    for (int e = tid; e < Lc * m; e += kThreads) X[e] = xg[e];
+    __syncthreads();
+    {
+        const float* UT = (CELL == kCellTanhRnn) ? w + DP * DP : w + 3 * DP * DP;
+        const float* bi = (CELL == kCellTanhRnn) ? w + DP * DP + m * DP : w + 3 * DP * DP + 3 * m * DP;
+        for (int e = tid; e < NG * Lc * DP; e += kThreads) {
+            const int gte = e / (Lc * DP), r = e % (Lc * DP), j = r / DP, i = r % DP;
+            float a = bi[gte * DP + i];
+            for (int q = 0; q < m; ++q) a += UT[(gte * m + q) * DP + i] * X[j * m + q];
+            XP[gte * L * DP + j * DP + i] = a;
+        }
+    }
+    uint32_t rb = 0;
+    const size_t HS = static_cast<size_t>(g.B) * g.NC * D;
+
+    if constexpr (PHASE == kPrologue) {
+        // s^(0) = s0 everywhere: N holds rows t0-1 .. t1-1 of s^(0).
+        for (int e = tid; e < (Lc + 1) * DP; e += kThreads) {
+            const int i = e % DP;
+            N[e] = i < D ? s0[i] : 0.0f;
+        }
+        __syncthreads();
+    } else {
+        // ---- P: rows t0-1 .. t1-1 of s^(i)
+        float* sg = g.s + b * g.ss + static_cast<int64_t>(t0) * D;
+        for (int e = tid; e < (Lc + 1) * DP; e += kThreads) {
+            const int j = e / DP, i = e % DP;
+            float val = 0.0f;
+            if (i < D) {
+                if (PHASE == kFirst) val = s0[i];
+                else if (j == 0) val = (c == 0) ? s0[i] : g.halo[(g.iter & 1) * HS + (ci - 1) * D + i];
+                else val = sg[(j - 1) * D + i];
+            }
+            P[e] = val;
+        }
+        __syncthreads();
+        // ---- maps of iteration i at p_t = P[j]
+        eval_rows<CELL, DP, DENSE>(w, P, XP, V, CO, Lc, L, D, m, g.mode, nullptr, rb);
+        __syncthreads();
+        // ---- replay from the carry, damping, N = rows t0-1 .. t1-1 of s^(i+1)
+        const bool has_next = c + 1 < g.NC;
+        const float* cr = g.carry + ci * D;
+        const float lam = g.lam;
+        const bool und = g.undamped != 0;
+        if constexpr (!DENSE) {
+            if (tid < D) {
+                float shat = cr[tid];
+                N[tid] = und ? shat : P[tid] + lam * (shat - P[tid]);
+                for (int j = 0; j < Lc; ++j) {
+                    const int o = j * DP + tid;
+                    shat = V[o] + CO[o] * (shat - P[o]);
+                    if (j == Lc - 1 && has_next) shat = cr[D + tid];
+                    const float so = P[o + DP];
+                    N[o + DP] = und ? shat : so + lam * (shat - so);
+                }
+            } else if (tid < DP) {
+                for (int j = 0; j <= Lc; ++j) N[j * DP + tid] = 0.0f;
+            }
+        } else {
+            float shat = 0.0f;
+            if (tid < D) {
+                shat = cr[tid];
+                N[tid] = und ? shat : P[tid] + lam * (shat - P[tid]);
+            } else if (tid < DP) {
+                for (int j = 0; j <= Lc; ++j) N[j * DP + tid] = 0.0f;
+                DL[tid] = 0.0f;
+            }
+            for (int j = 0; j < Lc; ++j) {
+                const int o = j * DP + tid;
+                if (tid < D) DL[tid] = shat - P[o];
+                __syncthreads();
+                if (tid < D) {
+                    shat = V[o] + jac_row_apply<CELL, DP>(w, CO, o, L, tid, D, DL);
+                    if (j == Lc - 1 && has_next) shat = cr[D + tid];
+                    const float so = P[o + DP];
+                    N[o + DP] = und ? shat : so + lam * (shat - so);
+                }
+                __syncthreads();
+            }
+        }
+        __syncthreads();
+        // ---- store s^(i+1) rows t0 .. t1-1 and the halo for the next chunk
+        for (int e = tid; e < Lc * D; e += kThreads) {
+            const int j = e / D, i = e % D;
+            sg[e] = N[(j + 1) * DP + i];
+        }
+        if (tid < D) g.halo[((g.iter + 1) & 1) * HS + ci * D + tid] = N[Lc * DP + tid];
+    }
+    // ---- maps of iteration i+1 at the new iterate, and its residual
+    eval_rows<CELL, DP, DENSE>(w, N, XP, V, CO, Lc, L, D, m, g.mode, N, rb);
+    __syncthreads();
+    if constexpr (!DENSE) {
+        if (tid < D) {
+            float A = 1.0f, Bc = 0.0f;
+            for (int j = 0; j < Lc; ++j) {
+                const int o = j * DP + tid;
+                const float at = CO[o];
+                const float bt = V[o] - at * N[o];
+                Bc = at * Bc + bt;
+                A = at * A;
+            }
+            g.aggA[ci * D + tid] = A;
+            g.aggB[ci * D + tid] = Bc;
+        }
+    } else {
+        // chunk map y -> M y + bg, built step by step: M <- A_j M, bg <- A_j (bg - p_j) + v_j
+        float* M0 = DL + DP;
+        float* M1 = M0 + DP * DP;
+        float* B0 = M1 + DP * DP;
+        float* B1 = B0 + DP;
+        for (int e = tid; e < DP * DP; e += kThreads) {
+            const int i = e / DP, k = e % DP;
+            M0[e] = (i == k && i < D) ? 1.0f : 0.0f;
+            M1[e] = 0.0f;
+        }
+        if (tid < DP) {
+            B0[tid] = 0.0f;
+            B1[tid] = 0.0f;
+        }
+        __syncthreads();
+        constexpr int NCG = kThreads / DP;
+        const int i = tid % DP;
+        const int cg = tid / DP;
+        for (int j = 0; j < Lc; ++j) {
+            const int o = j * DP + i;
+            if (i < D) {
+                for (int col = cg; col < D; col += NCG) {
+                    float acc[NG];
+#pragma unroll
+                    for (int q = 0; q < NG; ++q) acc[q] = 0.0f;
+                    for (int k = 0; k < D; ++k) {
+                        const float mk = M0[k * DP + col];
+#pragma unroll
+                        for (int q = 0; q < NG; ++q) acc[q] += w[(q * DP + k) * DP + i] * mk;
+                    }
+                    float val;
+                    if constexpr (CELL == kCellTanhRnn) {
+                        val = CO[o] * acc[0];
+                    } else {
+                        val = CO[o] * M0[i * DP + col] + CO[L * DP + o] * acc[1] +
+                              CO[2 * L * DP + o] * acc[2] + CO[3 * L * DP + o] * acc[0];
+                    }
+                    M1[i * DP + col] = val;
+                }
+                if (cg == 0) {
+                    // offset: A_j (bg - p_j) + v_j, p_j = N[j]
+                    float acc[NG];
+#pragma unroll
+                    for (int q = 0; q < NG; ++q) acc[q] = 0.0f;
+                    for (int k = 0; k < D; ++k) {
+                        const float yk = B0[k] - N[j * DP + k];
+#pragma unroll
+                        for (int q = 0; q < NG; ++q) acc[q] += w[(q * DP + k) * DP + i] * yk;
+                    }
+                    float val;
+                    if constexpr (CELL == kCellTanhRnn) {
+                        val = CO[o] * acc[0];
+                    } else {
+                        val = CO[o] * (B0[i] - N[o]) + CO[L * DP + o] * acc[1] +
+                              CO[2 * L * DP + o] * acc[2] + CO[3 * L * DP + o] * acc[0];
+                    }
+                    B1[i] = V[o] + val;
+                }
+            }
+            __syncthreads();
+            float* t = M0; M0 = M1; M1 = t;
+            t = B0; B0 = B1; B1 = t;
+        }
+        float* aA = g.aggA + ci * D * D;
+        for (int e = tid; e < D * D; e += kThreads) aA[e] = M0[(e / D) * DP + (e % D)];
+        if (tid < D) g.aggB[ci * D + tid] = B0[tid];
+    }
+    rb = block_max_u32(rb);
+    if (tid == 0) g.rpart[ci] = rb;
+}
+
+template <int CELL, int DP, bool DENSE, int PHASE>
+static hipError_t launch_one(const CellArgs& a, size_t lds, hipStream_t st) {
+    auto k = cell_pass<CELL, DP, DENSE, PHASE>;
+    if (lds > 64 * 1024) {   // opt in to a larger LDS allocation
+        const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (attr != hipSuccess) return attr;
+    }
+    k<<<dim3(a.NC, a.B), kThreads, lds, st>>>(a);
+    return hipGetLastError();
+}
+
+template <int CELL, int DP, bool DENSE>
+static hipError_t launch_phase(int phase, const CellArgs& a, hipStream_t st) {
+    const size_t lds = Lds<CELL, DP, DENSE>::floats(a.L, a.m) * sizeof(float);
+    if (phase == kPrologue) return launch_one<CELL, DP, DENSE, kPrologue>(a, lds, st);
+    if (phase == kFirst) return launch_one<CELL, DP, DENSE, kFirst>(a, lds, st);
+    return launch_one<CELL, DP, DENSE, kSteady>(a, lds, st);
+}
+
+template <int CELL, bool DENSE>
+static hipError_t launch_dp(int DP, int phase, const CellArgs& a, hipStream_t st) {
+    switch (DP) {
+        case 4: return launch_phase<CELL, 4, DENSE>(phase, a, st);
+        case 8: return launch_phase<CELL, 8, DENSE>(phase, a, st);
+        case 16: return launch_phase<CELL, 16, DENSE>(phase, a, st);
+        case 32: return launch_phase<CELL, 32, DENSE>(phase, a, st);
+        case 64: return launch_phase<CELL, 64, DENSE>(phase, a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_cell_pass(int kind, int DP, bool dense, int phase, const CellArgs& a,
+                            hipStream_t st) {
+    if (kind == kCellTanhRnn) {
+        return dense ? launch_dp<kCellTanhRnn, true>(DP, phase, a, st)
+                     : launch_dp<kCellTanhRnn, false>(DP, phase, a, st);
+    }
+    return dense ? launch_dp<kCellGru, true>(DP, phase, a, st)
+                 : launch_dp<kCellGru, false>(DP, phase, a, st);
+}
+
+size_t cell_pass_lds_bytes(int kind, int DP, bool dense, int L, int m) {
+    const size_t NG = kind == kCellTanhRnn ? 1 : 3;
+    const size_t NCO = dense ? (kind == kCellTanhRnn ? 1 : 4) : 1;
+    size_t f = 2ull * (L + 1) * DP + NG * L * DP + static_cast<size_t>(L) * DP + NCO * L * DP +
+               static_cast<size_t>(L) * m + DP;
+    if (dense) f += 2ull * DP * DP + 2ull * DP;
+    return f * sizeof(float);
+}
+
+int cell_pass_nblocks(const CellArgs& a) { return a.NC * a.B; }
+
+// ---------------------------------------------------------------- dense carry scan
+// carry[b][0] = s0[b]; carry[b][c+1] = M[b][c] carry[b][c] + bg[b][c].
+// One wave per batch row; the chunk count per call is modest (T / L).
+__global__ __launch_bounds__(64) void dense_carry_kernel(CarryArgs g) {
+    if (g.do_check && blockIdx.x == 0) run_check(g.chk);
+    __shared__ float y[64];
+    const int b = blockIdx.x;
+    const int i = threadIdx.x;
+    const int D = g.D;
+    const size_t cb = static_cast<size_t>(b) * g.NC;
+    float yi = 0.0f;
+    if (i < D) {
+        yi = g.s0[b * g.s0s + i];
+        y[i] = yi;
+        g.carry[cb * D + i] = yi;
+    }
+    __syncthreads();
+    for (int c = 0; c + 1 < g.NC; ++c) {
+        float acc = 0.0f;
+        if (i < D) {
+            const float* M = g.aggA + (cb + c) * D * D + static_cast<size_t>(i) * D;
+            acc = g.aggB[(cb + c) * D + i];
+            for (int k = 0; k < D; ++k) acc += M[k] * y[k];
+        }
+        __syncthreads();
+        if (i < D) {
+            y[i] = acc;
+            g.carry[(cb + c + 1) * D + i] = acc;
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_dense_carry(const CarryArgs& a, hipStream_t st) {
+    dense_carry_kernel<<<a.B, 64, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace pn

@@ -1,0 +1,93 @@
+// Device helpers: transcendental functions, residual bit-max reductions and
+// the convergence check shared by the carry kernels.
+#pragma once
+
+#include "pn_internal.hpp"
+
+namespace pn {
+
+enum { kJacobi = 0, kPicard = 1, kQuasiNewton = 2, kNewton = 3 };
+enum { kStOk = 0, kStNotConverged = 1, kStNonFinite = 2 };
+
+// tanh u = 1 - 2 / (e^{2u} + 1).  e^{2u} is the hardware base-2 exponential
+// of 2u*log2(e); the reciprocal is the hardware one.  Saturates correctly
+// (e -> inf gives 1, e -> 0 gives -1) and propagates NaN.  Absolute error is
+// a few 1e-8 plus the final rounding (tested against float64 tanh).
+__device__ __forceinline__ float tanh_f(float u) {
+    const float e = __builtin_amdgcn_exp2f(u * 2.88539008177792681472f);
+    return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+}
+
+// logistic sigmoid 1 / (1 + e^{-u}), same building blocks.
+__device__ __forceinline__ float sigmoid_f(float u) {
+    const float e = __builtin_amdgcn_exp2f(u * -1.44269504088896340736f);
+    return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// |v| as an unsigned bit pattern.  For non-negative floats the unsigned order
+// is the numeric order, and every NaN/Inf pattern is >= 0x7f800000, so an
+// integer max is an exact, order-independent, NaN-preserving max of |v|.
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7fffffffu; }
+
+// Diagonal coefficient of the affine map for the diagonal modes.
+template <int MODE>
+__device__ __forceinline__ float mode_coef(float jac_diag) {
+    if constexpr (MODE == kJacobi) return 0.0f;
+    else if constexpr (MODE == kPicard) return 1.0f;
+    else return jac_diag;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64));
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+// Max over the workgroup (blockDim.x a multiple of 64, <= 1024); every thread
+// must call it.  Returns the result in all threads.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
+    __shared__ uint32_t red[16];
+    v = wave_max_u32(v);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    if (lane == 0) red[wid] = v;
+    __syncthreads();
+    const int nw = blockDim.x >> 6;
+    uint32_t r = 0;
+    for (int k = 0; k < nw; ++k) r = r > red[k] ? r : red[k];
+    __syncthreads();
+    return r;
+}
+
+// Convergence decision for iteration i, taken by one workgroup: reduce the
+// per-block maxima of the previous pass, apply the stop rule (non-finite,
+// then r <= tol, then i == max_iter) and publish it to the device control
+// word and to the pinned host record.
+__device__ __forceinline__ void run_check(const CheckArgs& c) {
+    uint32_t m = 0;
+    for (int k = threadIdx.x; k < c.nparts; k += blockDim.x) {
+        const uint32_t v = c.rpart[k];
+        m = m > v ? m : v;
+    }
+    m = block_max_u32(m);
+    if (threadIdx.x == 0) {
+        int st = -1;
+        if (m >= kNonFiniteBits) st = kStNonFinite;
+        else if (__uint_as_float(m) <= c.tol) st = kStOk;
+        else if (c.iter >= c.max_iter) st = kStNotConverged;
+        const int stop = st >= 0 ? 1 : 0;
+        c.ctrl->stop = stop;
+        c.ctrl->status = st;
+        c.ctrl->iter = c.iter;
+        c.ctrl->r_bits = m;
+        c.host->r_bits = m;
+        c.host->iter = c.iter;
+        c.host->status = st;
+        c.host->stop = stop;
+        __threadfence_system();
+    }
+}
+
+}  // namespace pn

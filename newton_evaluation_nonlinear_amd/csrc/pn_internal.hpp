@@ -1,0 +1,126 @@
+// Internal declarations shared by the host driver (pn_api.cpp) and the HIP
+// kernel files.  Not part of the public interface (include/pn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pn {
+
+constexpr int kThreads = 256;          // threads per workgroup of every tile kernel
+constexpr uint32_t kNonFiniteBits = 0x7f800000u;
+
+// Device-side control word of one solve, written by the check (block 0 of the
+// carry kernel) and read by the next apply launch.
+struct Ctrl {
+    int32_t stop;      // 1: the iteration loop is over, apply launches exit at once
+    int32_t status;    // PN_OK / PN_NOT_CONVERGED / PN_NONFINITE, or -1 (running)
+    int32_t iter;      // iteration index i of the last check
+    uint32_t r_bits;   // bit pattern of r_i = max |F| (non-negative float)
+};
+
+// Host-visible copy (pinned, mapped) of the same record.
+struct HostRec {
+    int32_t stop;
+    int32_t status;
+    int32_t iter;
+    uint32_t r_bits;
+};
+
+// Arguments of the per-check decision, evaluated on the device.
+struct CheckArgs {
+    const uint32_t* rpart;   // per-block residual maxima of the previous pass
+    int32_t nparts;
+    int32_t iter;            // i: number of updates applied so far
+    int32_t max_iter;
+    float tol;
+    Ctrl* ctrl;
+    HostRec* host;           // device-usable pointer to pinned host memory
+};
+
+// ---------------------------------------------------------------- elementwise cell
+struct DiagArgs {
+    const float* a;          // [D]
+    const float* x;          // window base; row stride D (m == D), batch stride xs
+    int64_t xs;
+    float* s;                // window base of out; row stride D, batch stride ss
+    int64_t ss;
+    const float* s0;         // initial state of the window; batch stride s0s
+    int64_t s0s;
+    int32_t B, Tw, D, L, NC, cpb;
+    float* aggA;             // [B][NC][D]
+    float* aggB;             // [B][NC][D]
+    const float* carry;      // [B][NC][D]
+    float* halo;             // [2][B][NC][D]
+    uint32_t* rpart;         // one slot per workgroup
+    const Ctrl* ctrl;
+    int32_t mode, iter, undamped;
+    float lam;
+};
+
+// ---------------------------------------------------------------- matrix cells
+// Prepared (transposed, zero-padded) weights live in the workspace:
+//   tanh RNN: WT[DP][DP] | UT[m][DP] | bias[DP] | wdiag[DP]
+//   GRU     : WhT[3][DP][DP] | WiT[3][m][DP] | bih[3][DP] | bhh[3][DP] | whdiag[3][DP]
+struct CellArgs {
+    const float* w;          // prepared weights
+    const float* x;          // window base; row stride m, batch stride xs
+    int64_t xs;
+    float* s;                // window base of out; row stride D, batch stride ss
+    int64_t ss;
+    const float* s0;
+    int64_t s0s;
+    int32_t B, Tw, D, m, L, NC;
+    float* aggA;             // diag: [B][NC][D]; dense: [B][NC][D][D] (row-major M)
+    float* aggB;             // [B][NC][D]
+    const float* carry;      // [B][NC][D]
+    float* halo;             // [2][B][NC][D]
+    uint32_t* rpart;
+    const Ctrl* ctrl;
+    int32_t mode, iter, undamped;
+    float lam;
+};
+
+struct CarryArgs {
+    const float* aggA;
+    const float* aggB;
+    float* carry;
+    const float* s0;
+    int64_t s0s;
+    int32_t B, D, NC;
+    int32_t do_check;
+    CheckArgs chk;
+};
+
+enum Phase { kPrologue = 0, kFirst = 1, kSteady = 2 };
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_diag_tanh_pass(int phase, const DiagArgs& a, hipStream_t st);
+int diag_tanh_nblocks(const DiagArgs& a);
+hipError_t launch_diag_carry(const CarryArgs& a, hipStream_t st);
+hipError_t launch_dense_carry(const CarryArgs& a, hipStream_t st);
+hipError_t launch_fill(float* out, int64_t ss, const float* s0, int64_t s0s, int B, int Tw, int D,
+                       hipStream_t st);
+
+hipError_t launch_prep_weights(int kind, const float* params, float* w, int D, int DP, int m,
+                               hipStream_t st);
+size_t prepared_weight_floats(int kind, int DP, int m);
+hipError_t launch_cell_pass(int kind, int DP, bool dense, int phase, const CellArgs& a,
+                            hipStream_t st);
+size_t cell_pass_lds_bytes(int kind, int DP, bool dense, int L, int m);
+int cell_pass_nblocks(const CellArgs& a);
+
+// Standalone affine scan.
+struct ScanArgs {
+    const float* A;          // diag [B][T][D] or dense [B][T][D][D]
+    const float* b;          // [B][T][D]
+    float* out;              // [B][T][D]
+    int32_t B, T, D, L, NC;
+    float* aggA;
+    float* aggB;
+    const float* carry;
+};
+hipError_t launch_scan_aggregate(bool dense, int DP, const ScanArgs& a, hipStream_t st);
+hipError_t launch_scan_apply(bool dense, int DP, const ScanArgs& a, hipStream_t st);
+
+}  // namespace pn

@@ -1,0 +1,152 @@
+"""Helpers for the GPU-vs-oracle parity tests.
+
+Acceptance for one solve (status, counts, trajectory, residual):
+  1. status equals the oracle's (float64 oracle; for a non-finite outcome the
+     float32 oracle, whose arithmetic is the library's);
+  2. updates per window equal the oracle's.  The count is an integer decided
+     by a floating-point comparison r <= tol; where the oracle's residual at
+     the deciding iteration lies within COUNT_BAND (relative) of tol, the
+     float32 decision may legitimately land on the other side, so a count one
+     off is accepted there.  Where the float64 count differs by more, the
+     decision is taken in the library's precision: the counts must then match
+     the float32 oracle (same band).  This happens only on runs with huge
+     transients (Picard on the GRU reaches 1e20+), where the precision itself
+     moves the count.  The trajectory is then compared with the float64 oracle
+     run for exactly the library's counts (both are valid stopping points; the
+     trajectory at the chosen count is what stays unique);
+  3. max |s_gpu - s_oracle| <= 1e-4 * max(1, max |s_oracle|);
+  4. the float64 residual of s_gpu, recomputed by the oracle, is <= tol + 1e-6
+     for converged runs, and the library's own reported residual is <= tol.
+"""
+
+import numpy as np
+import torch
+
+import oracle
+import newton_evaluation_nonlinear_amd as pn
+
+TRAJ_TOL = 1e-4
+RESID_SLACK = 1e-6
+COUNT_BAND = 0.02
+
+_oracle_cache = {}
+
+
+def to_dev(wl):
+    dev = torch.device("cuda:0")
+    return (torch.from_numpy(wl["params"]).to(dev), torch.from_numpy(wl["x"]).to(dev),
+            torch.from_numpy(wl["s0"]).to(dev))
+
+
+def run_gpu(wl, mode, tol=None, max_iter=None, damping=None, window=None, chunk=0, history=True,
+            profile=False):
+    params, x, s0 = to_dev(wl)
+    res = pn.eval(wl["cell"], params, x, s0, mode=mode,
+                  tol=wl["tol"] if tol is None else tol,
+                  max_iter=wl["max_iter"] if max_iter is None else max_iter,
+                  damping=wl["damping"] if damping is None else damping,
+                  window=wl["window"] if window is None else window,
+                  chunk=chunk, history=history, profile=profile)
+    torch.cuda.synchronize()
+    res.out_np = res.out.cpu().numpy()
+    return res
+
+
+def run_oracle(wl, mode, tol=None, max_iter=None, damping=None, window=None, dtype=np.float64,
+               force_iters=None, key=None):
+    args = dict(tol=wl["tol"] if tol is None else tol,
+                max_iter=wl["max_iter"] if max_iter is None else max_iter,
+                damping=wl["damping"] if damping is None else damping,
+                window=wl["window"] if window is None else window)
+    ck = None
+    if key is not None and force_iters is None:
+        ck = (key, mode, dtype, tuple(sorted(args.items())))
+        if ck in _oracle_cache:
+            return _oracle_cache[ck]
+    r = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], mode, args["tol"],
+                     args["max_iter"], args["damping"], args["window"], dtype=dtype,
+                     force_iters=force_iters)
+    if ck is not None:
+        _oracle_cache[ck] = r
+    return r
+
+
+def residual64(wl, s):
+    cell = oracle.make_cell(wl["cell"], wl["params"], wl["D"], wl["m"])
+    return oracle.residual_inf(cell, wl["x"].astype(np.float64), wl["s0"].astype(np.float64),
+                               np.asarray(s, dtype=np.float64))
+
+
+def _windows(T, W):
+    W = T if not W else W
+    return [(w0, min(T, w0 + W)) for w0 in range(0, T, W)]
+
+
+def _counts_within_band(gw, ref, tol):
+    """Counts equal, or one off where ref's residual at the deciding iteration
+    lies within COUNT_BAND of tol."""
+    if len(gw) != len(ref.window_iters):
+        return False
+    for w, (kg, ko) in enumerate(zip(gw, ref.window_iters)):
+        if kg == ko:
+            continue
+        if abs(kg - ko) != 1:
+            return False
+        h = ref.hist[w]
+        k = min(kg, ko)
+        r = h[k] if k < len(h) else None
+        if r is None:
+            return False
+        if kg > ko and not r >= tol * (1 - COUNT_BAND):
+            return False
+        if kg < ko and not r <= tol * (1 + COUNT_BAND):
+            return False
+    return True
+
+
+def check_parity(wl, mode, gpu, ref, tol=None, window=None, damping=None, max_iter=None,
+                 label=""):
+    """Apply the acceptance rules; returns the oracle result the trajectory was compared with."""
+    tol = wl["tol"] if tol is None else tol
+    window = wl["window"] if window is None else window
+    damping = wl["damping"] if damping is None else damping
+    max_iter = wl["max_iter"] if max_iter is None else max_iter
+    msg = f"{label} mode={mode} gpu(status={gpu.status}, iters={gpu.iters}, win={gpu.window_iters[:8]}) " \
+          f"oracle(status={ref.status}, iters={ref.iters}, win={ref.window_iters[:8]})"
+    assert gpu.status == ref.status, msg
+    nw = len(ref.window_iters)
+    gw = list(gpu.window_iters[:nw])
+    cmp_ref = ref
+    if gw != list(ref.window_iters):
+        assert len(gw) == nw, msg
+        if not _counts_within_band(gw, ref, tol):
+            # The count differs beyond the tolerance band: take the decision in
+            # the library's precision (float32 oracle) as the count reference.
+            ref32 = run_oracle(wl, mode, tol=tol, max_iter=max_iter, damping=damping,
+                               window=window, dtype=np.float32)
+            msg += f" float32-oracle(status={ref32.status}, win={ref32.window_iters[:8]})"
+            assert ref32.status == gpu.status, msg
+            assert _counts_within_band(gw, ref32, tol), msg
+        cmp_ref = run_oracle(wl, mode, tol=tol, max_iter=max_iter, damping=damping, window=window,
+                             force_iters=gw)
+    s_ref = cmp_ref.s
+    s_gpu = gpu.out_np
+    T = wl["x"].shape[1]
+    # compare the windows that were solved
+    solved = _windows(T, window)[:nw]
+    hi = solved[-1][1] if solved else 0
+    scale = max(1.0, float(np.nanmax(np.abs(s_ref[:, :hi])))) if hi else 1.0
+    if ref.status != oracle.NONFINITE:
+        err = float(np.max(np.abs(s_gpu[:, :hi].astype(np.float64) - s_ref[:, :hi]))) if hi else 0.0
+        assert err <= TRAJ_TOL * scale, f"{msg}: max abs error {err:.3e}"
+    if ref.status == oracle.OK:
+        r64 = residual64(wl, s_gpu)
+        assert r64 <= tol + RESID_SLACK, f"{msg}: float64 residual of the GPU result {r64:.3e}"
+        if gpu.resid_hist:
+            last = [None]
+            pos = 0
+            for k in gw:
+                pos += k + 1
+                last = gpu.resid_hist[pos - 1]
+                assert last <= tol, f"{msg}: reported residual {last:.3e} > tol"
+    return cmp_ref

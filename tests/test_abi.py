@@ -1,0 +1,127 @@
+"""The C-ABI library: it loads, exports every function include/pn.h declares,
+and rejects bad arguments on the host before touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import newton_evaluation_nonlinear_amd as pn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert _declared_functions() == sorted(pn.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pn.lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_last_error():
+    assert pn.version().startswith("pn ")
+    assert "gfx950" in pn.version()
+    assert pn.last_error() == ""
+
+
+def _eval_raw(kind=pn.CELL_TANH_RNN, m=3, B=2, T=5, D=4, mode=pn.NEWTON, tol=1e-5, max_iter=5,
+              ptr=1, opts=None, iters=True):
+    c = pn.Cell(kind, m)
+    it = ctypes.c_int32(-7)
+    p = ctypes.c_void_p(ptr) if ptr else None
+    rc = pn.lib().pn_eval_ex(ctypes.byref(c), p, p, p, B, T, D, mode, tol, max_iter, p,
+                             ctypes.byref(it) if iters else None,
+                             ctypes.byref(opts) if opts is not None else None)
+    return rc, it.value
+
+
+@pytest.mark.parametrize("kw, code", [
+    (dict(B=-1), pn.EINVAL),
+    (dict(T=-3), pn.EINVAL),
+    (dict(D=-2), pn.EINVAL),
+    (dict(mode=7), pn.EINVAL),
+    (dict(kind=9), pn.EINVAL),
+    (dict(m=0), pn.EINVAL),
+    (dict(tol=float("nan")), pn.EINVAL),
+    (dict(tol=-1.0), pn.EINVAL),
+    (dict(tol=float("inf")), pn.EINVAL),
+    (dict(max_iter=-1), pn.EINVAL),
+    (dict(ptr=0), pn.EINVAL),
+    (dict(iters=False), pn.EINVAL),
+    (dict(kind=pn.CELL_DIAG_TANH, m=3, D=4), pn.EINVAL),
+    (dict(kind=pn.CELL_GRU, D=65), pn.EUNSUPPORTED),
+    (dict(kind=pn.CELL_TANH_RNN, D=100), pn.EUNSUPPORTED),
+    (dict(B=70000), pn.EUNSUPPORTED),
+])
+def test_invalid_arguments_are_rejected_on_the_host(kw, code):
+    rc, _ = _eval_raw(**kw)
+    assert rc == code
+    assert pn.last_error() != ""
+
+
+def test_invalid_options():
+    for field, value in [("damping", 0.0), ("damping", 1.5), ("window", -1), ("chunk", -4)]:
+        o = pn.make_opts()
+        setattr(o, field, value)
+        rc, _ = _eval_raw(opts=o)
+        assert rc == pn.EINVAL, field
+    o = pn.make_opts()
+    o.workspace = 0x1001            # misaligned
+    o.workspace_bytes = 1 << 20
+    rc, _ = _eval_raw(opts=o)
+    assert rc == pn.EWORKSPACE
+    o = pn.make_opts()
+    o.resid_hist_len = 4            # length without a buffer
+    rc, _ = _eval_raw(opts=o)
+    assert rc == pn.EINVAL
+
+
+def test_empty_problems_succeed_without_work():
+    for B, T, D in [(0, 5, 4), (2, 0, 4), (2, 5, 0)]:
+        rc, it = _eval_raw(B=B, T=T, D=D, ptr=0)
+        assert rc == pn.OK and it == 0
+
+
+def test_workspace_bytes_is_host_only_and_monotone():
+    n1 = pn.workspace_bytes(pn.CELL_DIAG_TANH, 256, 8, 65536, 256, pn.QUASI_NEWTON, chunk=128)
+    n2 = pn.workspace_bytes(pn.CELL_DIAG_TANH, 256, 8, 131072, 256, pn.QUASI_NEWTON, chunk=128)
+    assert 0 < n1 < n2 and n1 % 256 == 0
+    g = pn.Cell(pn.CELL_GRU, 8)
+    nq = pn.workspace_bytes(pn.CELL_GRU, 8, 64, 2048, 16, pn.QUASI_NEWTON)
+    nn = pn.workspace_bytes(pn.CELL_GRU, 8, 64, 2048, 16, pn.NEWTON)
+    assert nn > nq > 0          # dense chunk maps hold D x D per chunk
+    assert pn.lib().pn_workspace_bytes(ctypes.byref(g), 1, 10, 65, pn.NEWTON, None) == 0
+    # a window bounds the workspace
+    nw = pn.workspace_bytes(pn.CELL_GRU, 32, 4, 32768, 64, pn.QUASI_NEWTON, window=1024)
+    nf = pn.workspace_bytes(pn.CELL_GRU, 32, 4, 32768, 64, pn.QUASI_NEWTON)
+    assert nw < nf
+
+
+def test_affine_scan_argument_checks():
+    L = pn.lib()
+    p = ctypes.c_void_p(1)
+    assert L.pn_affine_scan(p, p, p, -1, 4, 4, 0, p, None) == pn.EINVAL
+    assert L.pn_affine_scan(p, p, p, 1, 4, 4, 2, p, None) == pn.EINVAL
+    assert L.pn_affine_scan(p, p, p, 1, 4, 65, 1, p, None) == pn.EUNSUPPORTED
+    assert L.pn_affine_scan(None, p, p, 1, 4, 4, 0, p, None) == pn.EINVAL
+    assert L.pn_affine_scan(None, None, None, 0, 4, 4, 0, None, None) == pn.OK
+    assert L.pn_affine_scan_workspace_bytes(2, 100, 3, 1, None) > 0
+
+
+def test_undersized_workspace_is_rejected_before_any_device_work():
+    o = pn.make_opts()
+    o.workspace = 0x10000
+    o.workspace_bytes = 1024
+    rc, _ = _eval_raw(kind=pn.CELL_GRU, m=8, B=64, T=2048, D=16, mode=pn.QUASI_NEWTON, opts=o)
+    assert rc == pn.EWORKSPACE
+    assert "smaller" in pn.last_error()

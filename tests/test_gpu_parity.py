@@ -1,0 +1,238 @@
+"""GPU parity: the HIP library against the CPU oracle on the seeded workloads.
+
+Reduced sizes (same weights, fewer batch rows / steps) span several chunks and
+a ragged last chunk; the full-size cases (marked slow) run the shapes and the
+launch configuration the benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import newton_evaluation_nonlinear_amd as pn
+from _parity import run_gpu, run_oracle, check_parity, residual64
+
+pytestmark = pytest.mark.gpu
+
+J, P, Q, N = pn.JACOBI, pn.PICARD, pn.QUASI_NEWTON, pn.NEWTON
+
+
+def _case(cfg, B=None, T=None):
+    return workloads.make(cfg, B=B, T=T)
+
+
+def _label(wl):
+    return f"cfg{wl['cfg']} B={wl['B']} T={wl['T']}"
+
+
+def _report_residual_agreement(gpu, ref):
+    """Print how far the library's float32 residuals sit from the oracle's
+    (relative), over iterations where both are below 1e-3."""
+    if not gpu.resid_hist:
+        return
+    pos, worst = 0, 0.0
+    for w, k in enumerate(gpu.window_iters[:len(ref.hist)]):
+        g = gpu.resid_hist[pos:pos + k + 1]
+        pos += k + 1
+        for a, b in zip(g, ref.hist[w]):
+            if 1e-7 < b < 1e-3:
+                worst = max(worst, abs(a - b) / b)
+    print(f"   residual agreement: max relative |r_gpu - r_oracle| / r_oracle = {worst:.2e}", flush=True)
+
+
+def _parity(wl, mode, **kw):
+    print(f"[parity] {_label(wl)} mode={mode} {kw}", flush=True)
+    okw = {k: v for k, v in kw.items() if k != "chunk"}
+    ref = run_oracle(wl, mode, **okw)
+    gpu = run_gpu(wl, mode, **kw)
+    print(f"   gpu iters={gpu.iters} win={gpu.window_iters[:6]} status={gpu.status} "
+          f"oracle iters={ref.iters} win={ref.window_iters[:6]} status={ref.status}", flush=True)
+    _report_residual_agreement(gpu, ref)
+    if ref.status == oracle.NONFINITE or gpu.status == pn.NONFINITE:
+        # a divergent run: its outcome is judged against the float32 oracle
+        ref32 = run_oracle(wl, mode, dtype=np.float32, **okw)
+        print(f"   float32 oracle iters={ref32.iters} status={ref32.status} "
+              f"hist tail={[f'{v:.2e}' for v in ref32.hist[-1][-4:]]}", flush=True)
+        assert gpu.status == ref32.status == oracle.NONFINITE
+        assert gpu.iters == ref32.iters
+        return ref32
+    return check_parity(wl, mode, gpu, ref, label=_label(wl),
+                        **{k: v for k, v in kw.items() if k in ("tol", "window", "damping", "max_iter")})
+
+
+# ---------------------------------------------------------------- small sizes
+
+def test_device_tanh_accuracy_through_one_jacobi_update():
+    # One Jacobi update from s0 = 0 on the channel-wise cell gives tanh(x_t) exactly.
+    wl = _case(3, B=2, T=1000)
+    gpu = run_gpu(wl, J, max_iter=1, tol=0.0)
+    assert gpu.status == pn.NOT_CONVERGED and gpu.iters == 1
+    err = np.max(np.abs(gpu.out_np.astype(np.float64) - np.tanh(wl["x"].astype(np.float64))))
+    print("device tanh max abs error", err)
+    assert err <= 3e-7
+
+
+@pytest.mark.parametrize("mode", [J, P, Q, N])
+def test_diag_tanh_small(mode):
+    wl = _case(3, B=2, T=3001)
+    _parity(wl, mode, tol=1e-5 if mode != P else 1e-4)
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 64, 3001, 5000])
+def test_diag_tanh_chunk_sizes(chunk):
+    wl = _case(3, B=2, T=3001)
+    _parity(wl, Q, chunk=chunk)
+
+
+def test_diag_tanh_odd_width_and_damping():
+    rng = np.random.default_rng(5)
+    D, B, T = 77, 3, 517
+    wl = dict(cfg=0, cell=pn.CELL_DIAG_TANH, D=D, m=D, B=B, T=T, tol=1e-6, damping=0.7, window=0,
+              max_iter=T, params=rng.uniform(-0.9, 0.9, D).astype(np.float32),
+              x=rng.standard_normal((B, T, D)).astype(np.float32),
+              s0=(0.3 * rng.standard_normal((B, D))).astype(np.float32))
+    _parity(wl, Q)
+    _parity(wl, J)
+
+
+def test_cfg1_newton_full():
+    wl = _case(1)
+    ref = _parity(wl, N)
+    assert ref.iters == 4
+
+
+@pytest.mark.parametrize("mode", [Q, N, J])
+def test_cfg2_gru_small(mode):
+    wl = _case(2, B=4, T=300)
+    _parity(wl, mode)
+
+
+def test_cfg2_gru_picard_small():
+    # T=300 is short enough for Picard to converge, after transients near 1e27
+    wl = _case(2, B=4, T=300)
+    _parity(wl, P)
+
+
+@pytest.mark.parametrize("mode", [N, Q])
+def test_cfg4_tanh_rnn_small(mode):
+    wl = _case(4, B=3, T=700)
+    _parity(wl, mode)
+
+
+def test_cfg5_gru_damped_windows_small():
+    wl = _case(5, B=2, T=2500)
+    _parity(wl, Q)
+
+
+@pytest.mark.parametrize("D", [1, 3, 5, 16, 33, 64])
+@pytest.mark.parametrize("kind", [pn.CELL_TANH_RNN, pn.CELL_GRU])
+def test_matrix_cells_other_widths(kind, D):
+    rng = np.random.default_rng(100 + D)
+    m, B, T = 3, 2, 150
+    params = workloads.random_cell_params(kind, D, m, rng, 1.0)
+    wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-6, damping=1.0, window=0,
+              max_iter=T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32))
+    for mode in (N, Q):
+        _parity(wl, mode)
+
+
+# ---------------------------------------------------------------- the scan alone
+
+@pytest.mark.parametrize("dense", [False, True])
+@pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 1000])
+def test_affine_scan(dense, T):
+    rng = np.random.default_rng(T + 10 * dense)
+    B, D = 3, (5 if dense else 70)
+    A = rng.uniform(-1, 1, (B, T, D, D) if dense else (B, T, D)).astype(np.float32)
+    if dense:
+        A /= np.sqrt(D)
+    A[:, ::7] = 0.0
+    if not dense:
+        A[:, 3::11] = 1.0
+    b = rng.standard_normal((B, T, D)).astype(np.float32)
+    s0 = rng.standard_normal((B, D)).astype(np.float32)
+    dev = torch.device("cuda:0")
+    out = pn.affine_scan(torch.from_numpy(A).to(dev), torch.from_numpy(b).to(dev),
+                         torch.from_numpy(s0).to(dev), dense=dense).cpu().numpy()
+    ref = oracle.affine_recurrence(b.astype(np.float64), np.zeros((B, T, D)), A.astype(np.float64),
+                                   s0.astype(np.float64))
+    scale = max(1.0, np.abs(ref).max())
+    assert np.max(np.abs(out - ref)) <= 2e-5 * scale * max(1.0, np.sqrt(T) / 4)
+
+
+# ---------------------------------------------------------------- outcomes and edge cases
+
+def test_max_iter_and_zero_tolerance():
+    wl = _case(2, B=2, T=200)
+    for mi in (0, 1, 2):
+        gpu = run_gpu(wl, Q, max_iter=mi, tol=0.0)
+        ref = run_oracle(wl, Q, max_iter=mi, tol=0.0)
+        assert gpu.status == ref.status == oracle.NOT_CONVERGED
+        assert gpu.iters == ref.iters == mi
+        assert np.max(np.abs(gpu.out_np - ref.s)) <= 1e-4
+
+
+def test_nonfinite_input_is_reported_at_the_oracle_iteration():
+    wl = _case(2, B=2, T=200)
+    wl["x"] = wl["x"].copy()
+    wl["x"][1, 150, 3] = np.nan
+    gpu = run_gpu(wl, Q)
+    ref = run_oracle(wl, Q)
+    assert gpu.status == ref.status == oracle.NONFINITE
+    assert gpu.iters == ref.iters == 0
+
+
+def test_huge_tolerance_returns_the_initial_iterate():
+    wl = _case(4, B=2, T=100)
+    gpu = run_gpu(wl, N, tol=1e6)
+    assert gpu.status == pn.OK and gpu.iters == 0
+    assert np.all(gpu.out_np == 0.0)
+
+
+def test_deterministic_bitwise():
+    wl = _case(3, B=2, T=4000)
+    a = run_gpu(wl, Q)
+    b = run_gpu(wl, Q)
+    assert a.iters == b.iters and np.array_equal(a.out_np, b.out_np)
+    wl = _case(4, B=2, T=400)
+    a = run_gpu(wl, N)
+    b = run_gpu(wl, N)
+    assert a.iters == b.iters and np.array_equal(a.out_np, b.out_np)
+
+
+# ---------------------------------------------------------------- full sizes
+
+@pytest.mark.slow
+def test_cfg3_full_quasi_newton():
+    wl = _case(3)
+    ref = _parity(wl, Q)
+    assert ref.status == oracle.OK
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("mode", [Q, N, J])
+def test_cfg2_full(mode):
+    _parity(_case(2), mode)
+
+
+@pytest.mark.slow
+def test_cfg2_full_picard_outcome():
+    wl = _case(2)
+    ref32 = run_oracle(wl, P, dtype=np.float32)
+    gpu = run_gpu(wl, P)
+    print("picard full", gpu.status, gpu.iters, ref32.status, ref32.iters)
+    assert ref32.status == oracle.NONFINITE
+    assert gpu.status == pn.NONFINITE and gpu.iters == ref32.iters
+
+
+@pytest.mark.slow
+def test_cfg4_full_newton():
+    _parity(_case(4), N)
+
+
+@pytest.mark.slow
+def test_cfg5_full_damped_windows():
+    _parity(_case(5), Q)
