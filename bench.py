@@ -8,8 +8,10 @@ channel-wise tanh recurrence s_t = tanh(a*s_{t-1} + x_t), B=8, T=65536, D=256,
 float32, quasi-Newton (diagonal Jacobian) to residual 1e-5.
 
 Prints one JSON line.  Besides the throughput it reports the roofline of the
-dominant kernel (the fused apply kernel; algorithmic bytes = x and s^(i) read,
-s^(i+1) written, per launch, over its HIP-event-timed duration) and the CPU
+dominant kernel (the steady-state launches of the fused apply kernel, i >= 1,
+including the final launch that exits at once; algorithmic bytes = x and s^(i)
+read, s^(i+1) written, averaged per launch, over the HIP-event-timed average
+launch duration) and the CPU
 oracle timed on a bounded sample of the same workload on this host.
 """
 
@@ -59,8 +61,8 @@ def cpu_baseline(cfg, mode):
     import oracle
     import workloads
 
-    samples = {3: dict(B=2, T=16384), 2: dict(B=8, T=2048), 4: dict(B=4, T=4096),
-               1: dict(B=None, T=None), 5: dict(B=1, T=4096)}
+    samples = {3: dict(B=8, T=32768), 2: dict(B=16, T=2048), 4: dict(B=8, T=4096),
+               1: dict(B=None, T=None), 5: dict(B=4, T=4096)}
     sm = samples.get(cfg, dict(B=1, T=4096))
     wl = workloads.make(cfg, **sm)
     with threadpool_limits(1):
@@ -76,6 +78,67 @@ def cpu_baseline(cfg, mode):
             "seconds": el}
 
 
+COPY_PROBE_BYTES = 64 * 1024 * 1024 * 4   # read once and written once by the probe copy
+
+
+def _read_counters(d, counter):
+    """{dispatch_id: (kernel_name, value)} from a rocprofv3 counter_collection csv."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                did = int(row["Dispatch_Id"])
+                name, val = out.get(did, (row["Kernel_Name"], 0.0))
+                out[did] = (name, val + float(row["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(args, fetch_dir, write_dir):
+    """Per-launch HBM bytes of the dominant kernel from two counter runs.
+
+    FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch; both are scaled
+    by the ratio of the known bytes of the probe copy to what the same counter
+    reads for it."""
+    import workloads
+    wl = workloads.make(args.config, B=1, T=1)   # names only
+    mode = MODES[args.mode] if args.mode else wl["modes"][0]
+    name = f"{wl['name']}_{workloads.MODE_NAMES[mode]}"
+    res = {}
+    for label, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _read_counters(d, counter)
+        copies = [v for n, v in rows.values() if "copyBuffer" in n]   # the device-to-device probe
+        if not copies:
+            raise SystemExit(f"no copy-probe dispatch found in {d}")
+        scale = COPY_PROBE_BYTES / (max(copies) * 1024.0)
+        steady = [v for n, v in rows.values()
+                  if ("diag_tanh_pass<" in n and ", 2>" in n) or ("cell_pass<" in n and ", 2>" in n)]
+        if not steady:
+            raise SystemExit(f"no steady apply dispatch found in {d}")
+        per = sum(steady) / len(steady) * 1024.0
+        res[label] = dict(counter=counter, copy_probe_kib=max(copies), scale=scale,
+                          launches=len(steady), raw_bytes_per_launch=per,
+                          bytes_per_launch=per * scale)
+    src = KERNEL_SOURCES[wl["cell"]]
+    bargs = f"--config {args.config}" + (f" --mode {args.mode}" if args.mode else "")
+    cmds = [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- "
+            f"python3 bench.py {bargs} --steps 2 --warmup 0 --no-cpu --copy-probe",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- "
+            f"python3 bench.py {bargs} --steps 2 --warmup 0 --no-cpu --copy-probe",
+            f"python3 bench.py {bargs} --pmc-summary {fetch_dir} {write_dir}"]
+    out = dict(workload=name, commands=cmds, kernel="steady apply launches", source=src,
+               source_sha256_16=_src_hash(src),
+               bytes_per_launch=res["fetch"]["bytes_per_launch"] + res["write"]["bytes_per_launch"],
+               fetch=res["fetch"], write=res["write"])
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,7 +148,15 @@ def main():
     ap.add_argument("--mode", default=None)
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one plain 256 MiB device copy first (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --copy-probe` into profiles/<workload>_traffic.json")
     args = ap.parse_args()
+    if args.pmc_summary:
+        summarize_pmc(args, *args.pmc_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is described, not built).", file=sys.stderr)
@@ -110,6 +181,13 @@ def main():
                        max_iter=wl["max_iter"], damping=wl["damping"], window=wl["window"],
                        chunk=args.chunk, out=out, workspace=ws, profile=profile)
 
+    if args.copy_probe:
+        n = 64 * 1024 * 1024
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         solve(False)
     torch.cuda.synchronize()
@@ -127,7 +205,6 @@ def main():
     apply_launches = sum(r.profile["apply_launches"] for r in results)
     apply_bytes = sum(r.profile["apply_bytes"] for r in results)
     apply_flops = sum(r.profile["apply_flops"] for r in results)
-    carry_ms = sum(r.profile["carry_ms"] for r in results)
     avg_launch_ms = apply_ms / max(apply_launches, 1)
     bytes_per_launch = apply_bytes / max(apply_launches, 1)
     gbs = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9 if avg_launch_ms > 0 else 0.0
@@ -142,7 +219,7 @@ def main():
                 "frac": gbs / HBM_PEAK_GBS, "traffic": _traffic(name, src, bytes_per_launch)}
     roof.update(kernel="apply (fused cell + scan replay + residual + next chunk maps)",
                 avg_launch_ms=avg_launch_ms, launches_per_step=apply_launches / args.steps,
-                alg_bytes_per_launch=bytes_per_launch, carry_ms_per_step=carry_ms / args.steps)
+                alg_bytes_per_launch=bytes_per_launch)
     line = {
         "metric": METRIC, "value": value, "unit": "state-updates/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,

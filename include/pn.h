@@ -81,17 +81,17 @@ typedef struct pn_cell {
 } pn_cell;
 
 /* Optional per-call measurements of the library's own kernels, taken with
- * HIP events on the call's stream.  "apply" is the fused per-iteration
- * kernel (cell + Jacobian + scan replay + damping + residual + next
- * aggregate); its algorithmic bytes are what the iteration must move:
- * read x and s^(i), write s^(i+1). */
+ * HIP events on the call's stream.  They cover the steady-state launches of
+ * the fused per-iteration "apply" kernel (cell + Jacobian + scan replay +
+ * damping + residual + next chunk maps) for iterations i >= 1, including the
+ * last launch, which finds the loop stopped and exits at once.  Algorithmic
+ * bytes of a launch that runs: read x and s^(i), write s^(i+1); 0 for the
+ * launch that exits. */
 typedef struct pn_profile {
     double apply_ms;          /* summed device time of apply launches       */
     int32_t apply_launches;   /* launches, including early-exit ones          */
     double apply_bytes;       /* summed algorithmic bytes of those launches   */
     double apply_flops;       /* summed algorithmic flops (dense compose etc.)*/
-    double carry_ms;          /* summed device time of the carry kernel       */
-    int32_t carry_launches;
     double total_ms;          /* first launch to last completion              */
 } pn_profile;
 

@@ -40,7 +40,6 @@ class Cell(ctypes.Structure):
 class Profile(ctypes.Structure):
     _fields_ = [("apply_ms", ctypes.c_double), ("apply_launches", ctypes.c_int32),
                 ("apply_bytes", ctypes.c_double), ("apply_flops", ctypes.c_double),
-                ("carry_ms", ctypes.c_double), ("carry_launches", ctypes.c_int32),
                 ("total_ms", ctypes.c_double)]
 
 

@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -85,9 +87,11 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
         if (chunk > 0) {
             p.L = chunk;
         } else {
-            // aim for about 2^20 threads in flight over B x D x chunks
+            // Longest chunk that still leaves about 2^18 threads (B x D x chunks):
+            // the per-iteration carry scan shrinks with the chunk count, while
+            // the apply sweep keeps 2^18 threads x 16 loads in flight.
             int64_t L = 16;
-            while (L < 1024 && static_cast<int64_t>(B) * D * ((p.W + 2 * L - 1) / (2 * L)) >= (1 << 20)) L *= 2;
+            while (L < 1024 && static_cast<int64_t>(B) * D * ((p.W + 2 * L - 1) / (2 * L)) >= (1 << 18)) L *= 2;
             p.L = static_cast<int>(L);
         }
         p.L = static_cast<int>(std::min<int64_t>(p.L, p.W));
@@ -166,7 +170,7 @@ struct ThreadRes {
     int device = -1;
     HostRec* host = nullptr;     // pinned
     HostRec* host_dev = nullptr; // device-usable alias
-    hipEvent_t sync_ev = nullptr;
+    int32_t epoch = 0;           // per-thread call counter
     std::vector<hipEvent_t> timing;   // pool of timing events
 };
 thread_local ThreadRes g_res;
@@ -184,10 +188,8 @@ int get_res(ThreadRes** out) {
         void* dp = nullptr;
         PN_HIP(hipHostGetDevicePointer(&dp, r.host, 0));
         r.host_dev = static_cast<HostRec*>(dp);
-        if (r.sync_ev) (void)hipEventDestroy(r.sync_ev);
         for (auto e : r.timing) (void)hipEventDestroy(e);
         r.timing.clear();
-        PN_HIP(hipEventCreateWithFlags(&r.sync_ev, hipEventDisableTiming));
         r.device = dev;
     }
     *out = &r;
@@ -204,10 +206,33 @@ int timing_event(ThreadRes* r, size_t idx, hipEvent_t* ev) {
     return PN_OK;
 }
 
+// Wait until the check of iteration `iter` (call `epoch`) has published its
+// record in pinned host memory.  Polls the record; every few thousand polls
+// asks the runtime whether the stream failed or drained without writing it.
+int wait_record(volatile HostRec* hr, hipStream_t st, int32_t epoch, int32_t iter) {
+    using clk = std::chrono::steady_clock;
+    const auto t0 = clk::now();
+    for (uint64_t n = 1;; ++n) {
+        if (hr->iter == iter && hr->epoch == epoch) {
+            std::atomic_thread_fence(std::memory_order_acquire);
+            return PN_OK;
+        }
+        if ((n & 4095) == 0) {
+            const hipError_t q = hipStreamQuery(st);
+            if (q != hipSuccess && q != hipErrorNotReady)
+                return fail(PN_EHIP, "stream failed while solving: %s", hipGetErrorString(q));
+            if (q == hipSuccess && !(hr->iter == iter && hr->epoch == epoch))
+                return fail(PN_EHIP, "stream drained without publishing iteration %d", iter);
+            if (clk::now() - t0 > std::chrono::seconds(600))
+                return fail(PN_EHIP, "timed out waiting for iteration %d", iter);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- the solve
 struct Timing {
     bool on = false;
-    std::vector<std::pair<size_t, size_t>> apply, carry;   // event index pairs
+    std::vector<std::pair<size_t, size_t>> apply;   // event index pairs
     std::vector<double> apply_bytes, apply_flops;
     size_t next = 0;
 };
@@ -291,23 +316,29 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
     cy.chk.rpart = rpart; cy.chk.nparts = nblocks; cy.chk.max_iter = c.max_iter; cy.chk.tol = c.tol;
     cy.chk.ctrl = ctrl; cy.chk.host = c.res->host_dev;
     volatile HostRec* hr = c.res->host;
+    const int32_t epoch = ++c.res->epoch;
+    cy.chk.epoch = epoch;
+    hr->iter = -1;
     for (int i = 0;; ++i) {
         cy.chk.iter = i;
         size_t e0 = 0, e1 = 0;
-        if (c.tm->on) { int rc = record(c, &e0); if (rc) return rc; }
         PN_HIP(p.dense ? launch_dense_carry(cy, c.st) : launch_diag_carry(cy, c.st));
-        if (c.tm->on) { int rc = record(c, &e1); if (rc) return rc; c.tm->carry.push_back({e0, e1}); }
-        PN_HIP(hipEventRecord(c.res->sync_ev, c.st));
-        if (c.tm->on) { int rc = record(c, &e0); if (rc) return rc; }
+        // timing covers the steady-state apply launches (i >= 1), including
+        // the final one that exits at once
+        const bool timed = c.tm->on && i > 0;
+        if (timed) { int rc = record(c, &e0); if (rc) return rc; }
         PN_HIP(launch_pass(i == 0 ? kFirst : kSteady, i));
-        if (c.tm->on) {
+        if (timed) {
             int rc = record(c, &e1);
             if (rc) return rc;
             c.tm->apply.push_back({e0, e1});
             c.tm->apply_bytes.push_back(0.0);   // filled below once we know if it ran
             c.tm->apply_flops.push_back(0.0);
         }
-        PN_HIP(hipEventSynchronize(c.res->sync_ev));
+        {
+            int rc = wait_record(hr, c.st, epoch, i);
+            if (rc != PN_OK) return rc;
+        }
         const int stop = hr->stop;
         const int st = hr->status;
         const uint32_t rb = hr->r_bits;
@@ -316,8 +347,8 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
         float r;
         std::memcpy(&r, &rb, sizeof(r));
         if (c.hist) c.hist->push_back(r);
-        if (c.tm->on && !stop) {
-            c.tm->apply_bytes.back() = apply_bytes(p, Tw, i == 0) ;
+        if (timed && !stop) {
+            c.tm->apply_bytes.back() = apply_bytes(p, Tw, false);
             c.tm->apply_flops.back() = apply_flops(p, Tw);
         }
         if (stop) {
@@ -414,12 +445,6 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
                 pr->apply_flops += tm.apply_flops[k];
             }
             pr->apply_launches = static_cast<int32_t>(tm.apply.size());
-            for (auto& pq : tm.carry) {
-                float ms = 0.0f;
-                PN_HIP(hipEventElapsedTime(&ms, res->timing[pq.first], res->timing[pq.second]));
-                pr->carry_ms += ms;
-            }
-            pr->carry_launches = static_cast<int32_t>(tm.carry.size());
             float ms = 0.0f;
             PN_HIP(hipEventElapsedTime(&ms, res->timing[ev_first], res->timing[ev_last]));
             pr->total_ms = ms;

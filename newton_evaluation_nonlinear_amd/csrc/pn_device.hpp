@@ -83,9 +83,12 @@ __device__ __forceinline__ void run_check(const CheckArgs& c) {
         c.ctrl->iter = c.iter;
         c.ctrl->r_bits = m;
         c.host->r_bits = m;
-        c.host->iter = c.iter;
         c.host->status = st;
         c.host->stop = stop;
+        __threadfence_system();
+        __hip_atomic_store(&c.host->epoch, c.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __threadfence_system();
+        __hip_atomic_store(&c.host->iter, c.iter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         __threadfence_system();
     }
 }

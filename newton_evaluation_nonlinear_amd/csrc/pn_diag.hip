@@ -21,6 +21,11 @@
 
 namespace pn {
 
+// Steps per prefetch group: the loads of group g+1 are issued before group g
+// is computed, so every thread keeps 2*U loads in flight.
+constexpr int kU = 8;
+constexpr int kUP = 16;   // the prologue only reads x, so it prefetches twice as far
+
 template <int MODE, int PHASE>
 __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
     if constexpr (PHASE != kPrologue) {
@@ -36,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
     if (c < g.NC && d < g.D) {
         const int D = g.D;
         const int t0 = c * g.L;
-        const int t1 = min(t0 + g.L, g.Tw);
+        const int n = min(g.L, g.Tw - t0);          // steps in this chunk
         const float a = g.a[d];
         const float s0v = g.s0[b * g.s0s + d];
         const float* xp = g.x + b * g.xs + static_cast<int64_t>(t0) * D + d;
@@ -44,15 +49,27 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
         float A = 1.0f, Bc = 0.0f;
         if constexpr (PHASE == kPrologue) {
             // Iteration 0: s^(0)_t = s0 for every t, so p_t = s0 throughout.
-            for (int t = t0; t < t1; ++t) {
-                const float xt = *xp;
-                xp += D;
-                const float v = tanh_f(a * s0v + xt);
-                rb = max(rb, abs_bits(s0v - v));
-                const float at = mode_coef<MODE>(a * (1.0f - v * v));
-                const float bt = v - at * s0v;
-                A = at * A;
-                Bc = at * Bc + bt;
+            float xb[kUP];
+#pragma unroll
+            for (int u = 0; u < kUP; ++u) xb[u] = u < n ? xp[u * D] : 0.0f;
+            for (int j = 0; j < n; j += kUP) {
+                const float* xq = xp + static_cast<int64_t>(j) * D;   // row j of the chunk
+                float xn[kUP];
+#pragma unroll
+                for (int u = 0; u < kUP; ++u) xn[u] = (j + kUP + u < n) ? xq[(kUP + u) * D] : 0.0f;
+#pragma unroll
+                for (int u = 0; u < kUP; ++u) {
+                    if (j + u < n) {
+                        const float v = tanh_f(a * s0v + xb[u]);
+                        rb = max(rb, abs_bits(s0v - v));
+                        const float at = mode_coef<MODE>(a * (1.0f - v * v));
+                        const float bt = v - at * s0v;
+                        A = at * A;
+                        Bc = at * Bc + bt;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kUP; ++u) xb[u] = xn[u];
             }
         } else {
             const size_t HS = static_cast<size_t>(g.B) * g.NC * D;
@@ -62,30 +79,57 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
             float shat = g.carry[ai];
             const bool has_next = (c + 1 < g.NC);
             const float shat_end = has_next ? g.carry[ai + D] : 0.0f;
+            const bool und = g.undamped != 0;
+            const float lam = g.lam;
             // s^(i+1) at t0-1, exactly as the previous chunk stores it.
-            float snp = g.undamped ? shat : p_old + g.lam * (shat - p_old);
-            for (int t = t0; t < t1; ++t) {
-                const float xt = *xp;
-                xp += D;
-                const float so = (PHASE == kFirst) ? s0v : *sp;
-                // iteration i: map at p_t = s^(i)_{t-1}
-                const float v = tanh_f(a * p_old + xt);
-                const float at = mode_coef<MODE>(a * (1.0f - v * v));
-                shat = v + at * (shat - p_old);
-                // the chunk's last value is the one the scan hands to the next chunk
-                if (t == t1 - 1 && has_next) shat = shat_end;
-                const float sn = g.undamped ? shat : so + g.lam * (shat - so);
-                *sp = sn;
-                sp += D;
-                // iteration i+1: residual and affine map at p_t = s^(i+1)_{t-1}
-                const float v2 = tanh_f(a * snp + xt);
-                rb = max(rb, abs_bits(sn - v2));
-                const float a2 = mode_coef<MODE>(a * (1.0f - v2 * v2));
-                const float b2 = v2 - a2 * snp;
-                A = a2 * A;
-                Bc = a2 * Bc + b2;
-                p_old = so;
-                snp = sn;
+            float snp = und ? shat : p_old + lam * (shat - p_old);
+            float xb[kU], sb[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                xb[u] = u < n ? xp[u * D] : 0.0f;
+                if constexpr (PHASE == kFirst) sb[u] = s0v;
+                else sb[u] = u < n ? sp[u * D] : 0.0f;
+            }
+            for (int j = 0; j < n; j += kU) {
+                const float* xq = xp + static_cast<int64_t>(j) * D;   // row j of the chunk
+                float* sq = sp + static_cast<int64_t>(j) * D;
+                float xn[kU], sn_[kU];
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const bool in = j + kU + u < n;
+                    xn[u] = in ? xq[(kU + u) * D] : 0.0f;
+                    if constexpr (PHASE == kFirst) sn_[u] = s0v;
+                    else sn_[u] = in ? sq[(kU + u) * D] : 0.0f;
+                }
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    if (j + u < n) {
+                        const float xt = xb[u];
+                        const float so = sb[u];
+                        // iteration i: map at p_t = s^(i)_{t-1}
+                        const float v = tanh_f(a * p_old + xt);
+                        const float at = mode_coef<MODE>(a * (1.0f - v * v));
+                        shat = v + at * (shat - p_old);
+                        // the chunk's last value is the one the scan hands to the next chunk
+                        if (j + u == n - 1 && has_next) shat = shat_end;
+                        const float sn = und ? shat : so + lam * (shat - so);
+                        sq[u * D] = sn;
+                        // iteration i+1: residual and affine map at p_t = s^(i+1)_{t-1}
+                        const float v2 = tanh_f(a * snp + xt);
+                        rb = max(rb, abs_bits(sn - v2));
+                        const float a2 = mode_coef<MODE>(a * (1.0f - v2 * v2));
+                        const float b2 = v2 - a2 * snp;
+                        A = a2 * A;
+                        Bc = a2 * Bc + b2;
+                        p_old = so;
+                        snp = sn;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    xb[u] = xn[u];
+                    sb[u] = sn_[u];
+                }
             }
             g.halo[((g.iter + 1) & 1) * HS + ai] = snp;
         }
@@ -130,9 +174,11 @@ hipError_t launch_diag_tanh_pass(int phase, const DiagArgs& a, hipStream_t st) {
 // carry[b][0] = s0[b]; carry[b][c+1] = aggA[b][c] * carry[b][c] + aggB[b][c].
 // Thread = (b, d, segment); each of kSeg threads of a channel composes a
 // contiguous run of chunks, the runs are combined in LDS, and every thread
-// replays its run from the combined carry.
+// replays its run from the combined carry.  Runs of up to kPer chunks are held
+// in registers, so each thread issues all of its loads at once.
 constexpr int kSeg = 16;          // segments per channel
 constexpr int kChan = 64;         // channels per workgroup (one wave wide)
+constexpr int kPer = 16;          // chunks per segment held in registers
 
 __global__ __launch_bounds__(kSeg * kChan) void diag_carry_kernel(CarryArgs g) {
     if (g.do_check && blockIdx.x == 0 && blockIdx.y == 0) run_check(g.chk);
@@ -143,18 +189,34 @@ __global__ __launch_bounds__(kSeg * kChan) void diag_carry_kernel(CarryArgs g) {
     const int d = blockIdx.x * kChan + dl;
     const int b = blockIdx.y;
     const int NC = g.NC;
+    const int D = g.D;
     const int per = (NC + kSeg - 1) / kSeg;
-    const int c0 = sg * per;
+    const int c0 = min(NC, sg * per);
     const int c1 = min(NC, c0 + per);
-    const bool act = d < g.D;
-    const size_t base = static_cast<size_t>(b) * NC * g.D + d;
+    const bool act = d < D;
+    const size_t base = static_cast<size_t>(b) * NC * D + d;
     float A = 1.0f, Bc = 0.0f;
+    float ra[kPer], rbv[kPer];
     if (act) {
-        for (int c = c0; c < c1; ++c) {
-            const float ac = g.aggA[base + static_cast<size_t>(c) * g.D];
-            const float bc = g.aggB[base + static_cast<size_t>(c) * g.D];
-            Bc = ac * Bc + bc;
-            A = ac * A;
+        if (c1 - c0 <= kPer) {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                const bool in = c0 + k < c1;
+                ra[k] = in ? g.aggA[base + static_cast<size_t>(c0 + k) * D] : 1.0f;
+                rbv[k] = in ? g.aggB[base + static_cast<size_t>(c0 + k) * D] : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                Bc = ra[k] * Bc + rbv[k];
+                A = ra[k] * A;
+            }
+        } else {
+            for (int c = c0; c < c1; ++c) {
+                const float ac = g.aggA[base + static_cast<size_t>(c) * D];
+                const float bc = g.aggB[base + static_cast<size_t>(c) * D];
+                Bc = ac * Bc + bc;
+                A = ac * A;
+            }
         }
     }
     segA[sg][dl] = A;
@@ -163,9 +225,19 @@ __global__ __launch_bounds__(kSeg * kChan) void diag_carry_kernel(CarryArgs g) {
     if (act) {
         float y = g.s0[b * g.s0s + d];
         for (int k = 0; k < sg; ++k) y = segA[k][dl] * y + segB[k][dl];
-        for (int c = c0; c < c1; ++c) {
-            g.carry[base + static_cast<size_t>(c) * g.D] = y;
-            y = g.aggA[base + static_cast<size_t>(c) * g.D] * y + g.aggB[base + static_cast<size_t>(c) * g.D];
+        if (c1 - c0 <= kPer) {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                if (c0 + k < c1) {
+                    g.carry[base + static_cast<size_t>(c0 + k) * D] = y;
+                    y = ra[k] * y + rbv[k];
+                }
+            }
+        } else {
+            for (int c = c0; c < c1; ++c) {
+                g.carry[base + static_cast<size_t>(c) * D] = y;
+                y = g.aggA[base + static_cast<size_t>(c) * D] * y + g.aggB[base + static_cast<size_t>(c) * D];
+            }
         }
     }
 }

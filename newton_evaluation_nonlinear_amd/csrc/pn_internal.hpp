@@ -19,12 +19,14 @@ struct Ctrl {
     uint32_t r_bits;   // bit pattern of r_i = max |F| (non-negative float)
 };
 
-// Host-visible copy (pinned, mapped) of the same record.
+// Host-visible copy (pinned, mapped) of the same record.  The device writes
+// the payload, then epoch, then iter; the host polls (epoch, iter).
 struct HostRec {
     int32_t stop;
     int32_t status;
-    int32_t iter;
     uint32_t r_bits;
+    int32_t epoch;
+    int32_t iter;
 };
 
 // Arguments of the per-check decision, evaluated on the device.
@@ -36,6 +38,7 @@ struct CheckArgs {
     float tol;
     Ctrl* ctrl;
     HostRec* host;           // device-usable pointer to pinned host memory
+    int32_t epoch;           // call sequence number, echoed to the host record
 };
 
 // ---------------------------------------------------------------- elementwise cell
