@@ -1,25 +1,29 @@
 """Compile libpn.so in-tree for gfx950 with hipcc.
 
     python -m newton_evaluation_nonlinear_amd._build
+
+Each source is compiled to an object in parallel (the device code of every
+file is self-contained), then the objects are linked into one shared library.
 """
 
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpn.so")
 
-SOURCES = ["pn_api.cpp", "pn_diag.hip", "pn_cell.hip", "pn_scan.hip"]
+SOURCES = ["pn_api.cpp", "pn_diag.hip", "pn_cell.hip", "pn_dense.hip", "pn_scan.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed fp32 ALU forms stay off: keep every FP32 op scalar
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
@@ -32,18 +36,34 @@ def hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose=False):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-o", tmp] + srcs
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
+        sys.stderr.write(" ".join(cmd) + "\n" + r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building libpn.so")
-    if verbose and r.stderr.strip():
-        sys.stderr.write(r.stderr)
+    return r.stderr
+
+
+def build(verbose=False):
+    with tempfile.TemporaryDirectory(prefix="pn_build_") as tmpd:
+        objs, cmds = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpd, src + ".o")
+            objs.append(obj)
+            cmds.append([hipcc()] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-c",
+                                             os.path.join(CSRC, src), "-o", obj])
+        workers = min(len(cmds), max(1, (os.cpu_count() or 1)))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            logs = list(ex.map(_run, cmds))
+        tmp = LIB + ".tmp"
+        logs.append(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs))
+    if verbose:
+        for cmd in cmds:
+            print(" ".join(cmd), flush=True)
+        for lg in logs:
+            lines = [ln for ln in lg.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+            if lines:
+                sys.stderr.write("\n".join(lines) + "\n")
     os.replace(tmp, LIB)
     return LIB
 

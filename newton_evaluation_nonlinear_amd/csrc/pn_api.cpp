@@ -64,7 +64,7 @@ struct Plan {
     int64_t T, W;          // horizon, window length
     int L, NC;             // chunk length, chunks of a full window
     int DP, cpb;           // padded D (matrix cells), channels per block (diag cell)
-    bool dense, matrix_cell;
+    bool dense, matrix_cell, mfma;
     int nblocks;
     size_t off_ctrl, off_rpart, off_aggA, off_aggB, off_carry, off_halo, off_w, total;
 };
@@ -82,6 +82,7 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
     const int chunk = o ? o->chunk : 0;
     p.matrix_cell = p.kind != PN_CELL_DIAG_TANH;
     p.dense = p.matrix_cell && mode == PN_NEWTON;
+    p.mfma = false;
     if (!p.matrix_cell) {
         p.cpb = std::min(256, ((p.D + 63) / 64) * 64);
         if (chunk > 0) {
@@ -100,14 +101,35 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
         a.B = p.B; a.D = p.D; a.NC = p.NC; a.cpb = p.cpb;
         p.nblocks = diag_tanh_nblocks(a);
         p.DP = 0;
+    } else if (p.dense && (next_pow2(p.D) == 16 || next_pow2(p.D) == 32) &&
+               dense_mfma_supported(p.kind, next_pow2(p.D), p.m)) {
+        // Newton on the matrix cores: one wavefront per chunk; chunks long
+        // enough to keep the serial carry short, with ~2048 chunks in flight
+        // (about two wavefronts per SIMD).
+        p.mfma = true;
+        p.DP = next_pow2(p.D);
+        int64_t L = 64;
+        if (chunk > 0) {
+            L = chunk;
+        } else {
+            while (L < 512 && static_cast<int64_t>(B) * ((p.W + 2 * L - 1) / (2 * L)) >= 2048) L *= 2;
+        }
+        p.L = static_cast<int>(std::min<int64_t>(L, p.W));
+        p.NC = static_cast<int>((p.W + p.L - 1) / p.L);
+        p.nblocks = p.NC * p.B;
     } else {
         p.DP = std::max(4, next_pow2(p.D));
-        const int Lmax = std::min(64, 16 * (kThreads / p.DP));
+        const int Lmax = 64;
         int L = Lmax;
         if (chunk > 0) {
             L = std::min(chunk, Lmax);
         } else {
-            while (L > 4 && cell_pass_lds_bytes(p.kind, p.DP, p.dense, L, p.m) > 64 * 1024) L /= 2;
+            // prefer a chunk whose arrays and staged weights fit the LDS budget
+            while (L > 4 && !cell_pass_stages_weights(p.kind, p.DP, p.dense, L, p.m)) L /= 2;
+            if (!cell_pass_stages_weights(p.kind, p.DP, p.dense, L, p.m)) {
+                L = Lmax;   // weights stay in global memory
+                while (L > 4 && cell_pass_lds_bytes(p.kind, p.DP, p.dense, L, p.m) > 64 * 1024) L /= 2;
+            }
             while (L > 16 && static_cast<int64_t>(B) * ((p.W + L - 1) / L) < 1024) L /= 2;
         }
         p.L = static_cast<int>(std::min<int64_t>(L, p.W));
@@ -306,6 +328,7 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
             return launch_diag_tanh_pass(phase, da, c.st);
         }
         ca.iter = iter;
+        if (p.mfma) return launch_dense_mfma_pass(p.kind, p.DP, phase, ca, c.st);
         return launch_cell_pass(p.kind, p.DP, p.dense, phase, ca, c.st);
     };
 

@@ -27,13 +27,12 @@ namespace pn {
 
 constexpr int kCellTanhRnn = 1;
 constexpr int kCellGru = 2;
-constexpr int kRowsPerThread = 16;   // rows of a chunk evaluated by one thread
 
 template <int CELL> struct CellTraits;
 template <> struct CellTraits<kCellTanhRnn> { static constexpr int NG = 1, NCO = 1; };
 template <> struct CellTraits<kCellGru> { static constexpr int NG = 3, NCO = 4; };
 
-size_t prepared_weight_floats(int kind, int DP, int m) {
+__host__ __device__ size_t prepared_weight_floats(int kind, int DP, int m) {
     if (kind == kCellTanhRnn) return static_cast<size_t>(DP) * DP + static_cast<size_t>(m) * DP + 2 * DP;
     return 3ull * DP * DP + 3ull * m * DP + 9ull * DP;
 }
@@ -99,59 +98,84 @@ hipError_t launch_prep_weights(int kind, const float* params, float* w, int D, i
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- LDS plan
-template <int CELL, int DP, bool DENSE>
-struct Lds {
-    static constexpr int NG = CellTraits<CELL>::NG;
-    static constexpr int NCO = DENSE ? CellTraits<CELL>::NCO : 1;
-    static size_t floats(int L, int m) {
-        size_t f = 2ull * (L + 1) * DP          // P, N
-                 + static_cast<size_t>(NG) * L * DP   // XP
-                 + static_cast<size_t>(L) * DP         // V
-                 + static_cast<size_t>(NCO) * L * DP   // CO
-                 + static_cast<size_t>(L) * m          // X
-                 + DP;                                 // DL (replay vector)
-        if (DENSE) f += 2ull * DP * DP + 2ull * DP;    // M ping-pong, offset ping-pong
-        return f;
-    }
-};
-
 // ---------------------------------------------------------------- cell evaluation
-// For rows j < Lc of a chunk with p_t = Pin[j] (the state one step earlier):
-// V[j] = f_t(p_t) and the Jacobian coefficients CO.  If Sres is given, also
-// folds |Sres[j+1] - V[j]| (the residual of the trajectory held in Sres) into rb.
-template <int CELL, int DP, bool DENSE>
-__device__ __forceinline__ void eval_rows(const float* __restrict__ w, const float* Pin,
-                                          const float* XP, float* V, float* CO, int Lc, int L,
-                                          int D, int m, int mode, const float* Sres, uint32_t& rb) {
-    constexpr int NG = CellTraits<CELL>::NG;
-    constexpr int NRG = kThreads / DP;
-    const int i = threadIdx.x % DP;
-    const int rg = threadIdx.x / DP;
-    float acc[kRowsPerThread][NG];
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// C[j][o] = sum_{k<K} A[j][k] * bval(k, o) for rows j < nrows and columns
+// o < NO (a multiple of 16), on the matrix cores: 16 x 16 output tiles of
+// 16x16x4 FP32 MFMA steps, tiles spread over the workgroup's wavefronts.
+// A is an LDS array of row stride lda, zero-padded to K (a multiple of 4).
+// Lane layout of one step: A[l % 16][l / 16], B[l / 16][l % 16];
+// the accumulator holds C[4 (l / 16) + r][l % 16], r < 4.
+template <int KC, typename BFun>
+__device__ __forceinline__ void rows_gemm(const float* A, int lda, int nrows, int K, int NO, BFun bval,
+                                          float* C, int ldc) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int c16 = lane & 15, kq = lane >> 4;
+    const int RT = (nrows + 15) >> 4, CT = NO >> 4;
+    const int KK = KC > 0 ? KC : K;
+    for (int t = wave; t < RT * CT; t += kThreads / 64) {
+        const int rt = t / CT, ct = t - rt * CT;
+        const int row = rt * 16 + c16;
+        const int col = ct * 16 + c16;
+        const float* Ar = A + (row < nrows ? row : 0) * lda + kq;
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+        for (int k0 = 0; k0 < KK; k0 += 4) {
+            const float a = row < nrows ? Ar[k0] : 0.0f;
+            const float b = bval(k0 + kq, col);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+        }
 #pragma unroll
-    for (int r = 0; r < kRowsPerThread; ++r)
-#pragma unroll
-        for (int g = 0; g < NG; ++g) acc[r][g] = 0.0f;
-    for (int k = 0; k < D; ++k) {
-        float wk[NG];
-#pragma unroll
-        for (int g = 0; g < NG; ++g) wk[g] = w[(g * DP + k) * DP + i];
-#pragma unroll
-        for (int r = 0; r < kRowsPerThread; ++r) {
-            const int j = rg + r * NRG;
-            if (j < Lc) {
-                const float pk = Pin[j * DP + k];
-#pragma unroll
-                for (int g = 0; g < NG; ++g) acc[r][g] += wk[g] * pk;
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int orow = rt * 16 + kq * 4 + r;
+            if (orow < nrows) C[orow * ldc + col] = acc[r];
         }
     }
+}
+
+// Columns of the gate pre-activation tables: NG gates of DP rows, padded to 16.
+template <int CELL, int DP>
+struct Gates {
+    static constexpr int NG = CellTraits<CELL>::NG;
+    static constexpr int NO = (NG * DP + 15) & ~15;
+};
+
+// Input projection XI[j][g*DP + i] = sum_q W_ig[i][q] x_j[q] (no bias), for the
+// staged x rows X (row stride mp = m rounded up to 4, zero-padded).
+template <int CELL, int DP>
+__device__ __forceinline__ void input_projection(const float* __restrict__ w, const float* X, int mp,
+                                                 int Lc, int m, float* XI) {
+    constexpr int NG = CellTraits<CELL>::NG, NO = Gates<CELL, DP>::NO;
+    const float* UT = w + NG * DP * DP;
+    rows_gemm<0>(X, mp, Lc, mp, NO, [&](int q, int o) {
+        const int gte = o / DP, i = o - gte * DP;
+        return (gte < NG && q < m) ? UT[(gte * m + q) * DP + i] : 0.0f;
+    }, XI, NO);
+}
+
+// For rows j < Lc of a chunk with p_t = Pin[j] (the state one step earlier):
+// V[j] = f_t(p_t) and the Jacobian coefficients CO.  The recurrent products
+// W_g p_t go through the matrix cores into H (LDS); the gate nonlinearities
+// are per element.  If Sres is given, also folds |Sres[j+1] - V[j]| (the
+// residual of the trajectory held in Sres) into rb.  Callers synchronise the
+// workgroup before and after.
+template <int CELL, int DP, bool DENSE>
+__device__ __forceinline__ void eval_rows(const float* __restrict__ w, const float* Pin,
+                                          const float* XI, float* H, float* V, float* CO, int Lc,
+                                          int L, int D, int m, int mode, const float* Sres,
+                                          uint32_t& rb) {
+    constexpr int NG = CellTraits<CELL>::NG, NO = Gates<CELL, DP>::NO;
+    constexpr int NRG = kThreads / DP;
+    rows_gemm<DP>(Pin, DP, Lc, DP, NO, [&](int k, int o) {
+        const int gte = o / DP, i = o - gte * DP;
+        return gte < NG ? w[(gte * DP + k) * DP + i] : 0.0f;
+    }, H, NO);
+    __syncthreads();
+    const int i = threadIdx.x % DP;
     const bool live = i < D;
-#pragma unroll
-    for (int r = 0; r < kRowsPerThread; ++r) {
-        const int j = rg + r * NRG;
-        if (j >= Lc) continue;
+    const float* bi = w + NG * DP * DP + NG * m * DP;     // input biases
+    for (int j = threadIdx.x / DP; j < Lc; j += NRG) {
         const int o = j * DP + i;
         if (!live) {
             V[o] = 0.0f;
@@ -163,10 +187,12 @@ __device__ __forceinline__ void eval_rows(const float* __restrict__ w, const flo
             }
             continue;
         }
+        const float* hj = H + j * NO;
+        const float* xj = XI + j * NO;
         float v;
         if constexpr (CELL == kCellTanhRnn) {
-            const float* wdiag = w + DP * DP + m * DP + DP;
-            v = tanh_f(acc[r][0] + XP[o]);
+            const float* wdiag = bi + DP;
+            v = tanh_f(hj[i] + xj[i] + bi[i]);
             const float c1 = 1.0f - v * v;
             if constexpr (DENSE) {
                 CO[o] = c1;
@@ -174,12 +200,12 @@ __device__ __forceinline__ void eval_rows(const float* __restrict__ w, const flo
                 CO[o] = mode == kJacobi ? 0.0f : (mode == kPicard ? 1.0f : c1 * wdiag[i]);
             }
         } else {
-            const float* bhh = w + 3 * DP * DP + 3 * m * DP + 3 * DP;
+            const float* bhh = bi + 3 * DP;
             const float* whd = bhh + 3 * DP;
-            const float rr = sigmoid_f(XP[o] + acc[r][0] + bhh[i]);
-            const float z = sigmoid_f(XP[L * DP + o] + acc[r][1] + bhh[DP + i]);
-            const float gg = acc[r][2] + bhh[2 * DP + i];
-            const float n = tanh_f(XP[2 * L * DP + o] + rr * gg);
+            const float rr = sigmoid_f(xj[i] + bi[i] + hj[i] + bhh[i]);
+            const float z = sigmoid_f(xj[DP + i] + bi[DP + i] + hj[DP + i] + bhh[DP + i]);
+            const float gg = hj[2 * DP + i] + bhh[2 * DP + i];
+            const float n = tanh_f(xj[2 * DP + i] + bi[2 * DP + i] + rr * gg);
             const float pi = Pin[o];
             v = (1.0f - z) * n + z * pi;
             const float dn = (1.0f - z) * (1.0f - n * n);
@@ -223,7 +249,7 @@ __device__ __forceinline__ float jac_row_apply(const float* __restrict__ w, cons
 }
 
 // ---------------------------------------------------------------- the fused pass
-template <int CELL, int DP, bool DENSE, int PHASE>
+template <int CELL, int DP, bool DENSE, int PHASE, bool STAGE>
 __global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
     if constexpr (PHASE != kPrologue) {
         if (g.ctrl->stop) return;
@@ -236,31 +262,29 @@ __global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
     const int t0 = c * L;
     const int Lc = min(L, g.Tw - t0);
     const int tid = threadIdx.x;
-    float* P = lds;
+    // the prepared weights are staged once per workgroup in LDS when they fit
+    const int nw = STAGE ? static_cast<int>(prepared_weight_floats(CELL, DP, m)) : 0;
+    float* WL = lds;
+    copy_to_lds<kThreads>(WL, g.w, nw);
+    constexpr int NO = Gates<CELL, DP>::NO;
+    const int mp = (m + 3) & ~3;
+    float* P = WL + ((nw + 3) & ~3);
     float* N = P + (L + 1) * DP;
-    float* XP = N + (L + 1) * DP;
-    float* V = XP + NG * L * DP;
+    float* XI = N + (L + 1) * DP;            // [L][NO] input projections
+    float* H = XI + L * NO;                  // [L][NO] recurrent pre-activations
+    float* V = H + L * NO;
     float* CO = V + L * DP;
-    float* X = CO + NCO * L * DP;
-    float* DL = X + L * m;
-    const float* w = g.w;
+    float* X = CO + NCO * L * DP;            // [L][mp]
+    float* DL = X + L * mp;
+    const float* w = STAGE ? WL : g.w;
     const size_t ci = static_cast<size_t>(b) * g.NC + c;        // chunk index
     const float* s0 = g.s0 + b * g.s0s;
 
-    // ---- stage inputs: X rows, then the input projection XP (iterate-free)
+    // ---- stage inputs: X rows, then the input projection (iterate-free)
     const float* xg = g.x + b * g.xs + static_cast<int64_t>(t0) * m;
-    for (int e = tid; e < Lc * m; e += kThreads) X[e] = xg[e];
+    copy_rows_to_lds<kThreads>(X, mp, xg, m, Lc, m);
     __syncthreads();
-    {
-        const float* UT = (CELL == kCellTanhRnn) ? w + DP * DP : w + 3 * DP * DP;
-        const float* bi = (CELL == kCellTanhRnn) ? w + DP * DP + m * DP : w + 3 * DP * DP + 3 * m * DP;
-        for (int e = tid; e < NG * Lc * DP; e += kThreads) {
-            const int gte = e / (Lc * DP), r = e % (Lc * DP), j = r / DP, i = r % DP;
-            float a = bi[gte * DP + i];
-            for (int q = 0; q < m; ++q) a += UT[(gte * m + q) * DP + i] * X[j * m + q];
-            XP[gte * L * DP + j * DP + i] = a;
-        }
-    }
+    input_projection<CELL, DP>(w, X, mp, Lc, m, XI);
     uint32_t rb = 0;
     const size_t HS = static_cast<size_t>(g.B) * g.NC * D;
 
@@ -274,19 +298,20 @@ __global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
     } else {
         // ---- P: rows t0-1 .. t1-1 of s^(i)
         float* sg = g.s + b * g.ss + static_cast<int64_t>(t0) * D;
-        for (int e = tid; e < (Lc + 1) * DP; e += kThreads) {
-            const int j = e / DP, i = e % DP;
-            float val = 0.0f;
-            if (i < D) {
-                if (PHASE == kFirst) val = s0[i];
-                else if (j == 0) val = (c == 0) ? s0[i] : g.halo[(g.iter & 1) * HS + (ci - 1) * D + i];
-                else val = sg[(j - 1) * D + i];
+        if constexpr (PHASE == kFirst) {
+            for (int e = tid; e < (Lc + 1) * DP; e += kThreads) {
+                const int i = e % DP;
+                P[e] = i < D ? s0[i] : 0.0f;
             }
-            P[e] = val;
+        } else {
+            if (tid < DP) {
+                P[tid] = tid < D ? ((c == 0) ? s0[tid] : g.halo[(g.iter & 1) * HS + (ci - 1) * D + tid]) : 0.0f;
+            }
+            copy_rows_to_lds<kThreads>(P + DP, DP, sg, D, Lc, D);
         }
         __syncthreads();
         // ---- maps of iteration i at p_t = P[j]
-        eval_rows<CELL, DP, DENSE>(w, P, XP, V, CO, Lc, L, D, m, g.mode, nullptr, rb);
+        eval_rows<CELL, DP, DENSE>(w, P, XI, H, V, CO, Lc, L, D, m, g.mode, nullptr, rb);
         __syncthreads();
         // ---- replay from the carry, damping, N = rows t0-1 .. t1-1 of s^(i+1)
         const bool has_next = c + 1 < g.NC;
@@ -338,7 +363,7 @@ __global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
         if (tid < D) g.halo[((g.iter + 1) & 1) * HS + ci * D + tid] = N[Lc * DP + tid];
     }
     // ---- maps of iteration i+1 at the new iterate, and its residual
-    eval_rows<CELL, DP, DENSE>(w, N, XP, V, CO, Lc, L, D, m, g.mode, N, rb);
+    eval_rows<CELL, DP, DENSE>(w, N, XI, H, V, CO, Lc, L, D, m, g.mode, N, rb);
     __syncthreads();
     if constexpr (!DENSE) {
         if (tid < D) {
@@ -425,9 +450,9 @@ __global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
     if (tid == 0) g.rpart[ci] = rb;
 }
 
-template <int CELL, int DP, bool DENSE, int PHASE>
+template <int CELL, int DP, bool DENSE, int PHASE, bool STAGE>
 static hipError_t launch_one(const CellArgs& a, size_t lds, hipStream_t st) {
-    auto k = cell_pass<CELL, DP, DENSE, PHASE>;
+    auto k = cell_pass<CELL, DP, DENSE, PHASE, STAGE>;
     if (lds > 64 * 1024) {   // opt in to a larger LDS allocation
         const hipError_t attr = hipFuncSetAttribute(
             reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -439,10 +464,16 @@ static hipError_t launch_one(const CellArgs& a, size_t lds, hipStream_t st) {
 
 template <int CELL, int DP, bool DENSE>
 static hipError_t launch_phase(int phase, const CellArgs& a, hipStream_t st) {
-    const size_t lds = Lds<CELL, DP, DENSE>::floats(a.L, a.m) * sizeof(float);
-    if (phase == kPrologue) return launch_one<CELL, DP, DENSE, kPrologue>(a, lds, st);
-    if (phase == kFirst) return launch_one<CELL, DP, DENSE, kFirst>(a, lds, st);
-    return launch_one<CELL, DP, DENSE, kSteady>(a, lds, st);
+    const bool stage = cell_pass_stages_weights(CELL, DP, DENSE, a.L, a.m);
+    const size_t lds = cell_pass_lds_bytes(CELL, DP, DENSE, a.L, a.m);
+    if (stage) {
+        if (phase == kPrologue) return launch_one<CELL, DP, DENSE, kPrologue, true>(a, lds, st);
+        if (phase == kFirst) return launch_one<CELL, DP, DENSE, kFirst, true>(a, lds, st);
+        return launch_one<CELL, DP, DENSE, kSteady, true>(a, lds, st);
+    }
+    if (phase == kPrologue) return launch_one<CELL, DP, DENSE, kPrologue, false>(a, lds, st);
+    if (phase == kFirst) return launch_one<CELL, DP, DENSE, kFirst, false>(a, lds, st);
+    return launch_one<CELL, DP, DENSE, kSteady, false>(a, lds, st);
 }
 
 template <int CELL, bool DENSE>
@@ -467,12 +498,28 @@ hipError_t launch_cell_pass(int kind, int DP, bool dense, int phase, const CellA
                  : launch_dp<kCellGru, false>(DP, phase, a, st);
 }
 
-size_t cell_pass_lds_bytes(int kind, int DP, bool dense, int L, int m) {
+static size_t cell_pass_array_floats(int kind, int DP, bool dense, int L, int m) {
     const size_t NG = kind == kCellTanhRnn ? 1 : 3;
     const size_t NCO = dense ? (kind == kCellTanhRnn ? 1 : 4) : 1;
-    size_t f = 2ull * (L + 1) * DP + NG * L * DP + static_cast<size_t>(L) * DP + NCO * L * DP +
-               static_cast<size_t>(L) * m + DP;
+    const size_t NO = (NG * DP + 15) & ~size_t(15);
+    const size_t mp = (m + 3) & ~3;
+    size_t f = 2ull * (L + 1) * DP + 2ull * L * NO + static_cast<size_t>(L) * DP + NCO * L * DP +
+               static_cast<size_t>(L) * mp + DP;
     if (dense) f += 2ull * DP * DP + 2ull * DP;
+    return f;
+}
+
+// Weights go to LDS when the whole workgroup footprint stays within 150 KB
+// (of the 160 KB per compute unit).
+bool cell_pass_stages_weights(int kind, int DP, bool dense, int L, int m) {
+    const size_t w = (prepared_weight_floats(kind, DP, m) + 3) & ~size_t(3);
+    return (w + cell_pass_array_floats(kind, DP, dense, L, m)) * sizeof(float) <= 150 * 1024;
+}
+
+size_t cell_pass_lds_bytes(int kind, int DP, bool dense, int L, int m) {
+    size_t f = cell_pass_array_floats(kind, DP, dense, L, m);
+    if (cell_pass_stages_weights(kind, DP, dense, L, m))
+        f += (prepared_weight_floats(kind, DP, m) + 3) & ~size_t(3);
     return f * sizeof(float);
 }
 
@@ -480,39 +527,58 @@ int cell_pass_nblocks(const CellArgs& a) { return a.NC * a.B; }
 
 // ---------------------------------------------------------------- dense carry scan
 // carry[b][0] = s0[b]; carry[b][c+1] = M[b][c] carry[b][c] + bg[b][c].
-// One wave per batch row; the chunk count per call is modest (T / L).
+// One wavefront per batch row; lane i owns row i of every chunk map and the
+// i-th entry of the running carry.  The carry entries are broadcast with
+// readlane (no LDS, no barrier), and each lane prefetches the next chunk's row
+// into registers while it applies the current one.
+__device__ __forceinline__ float bcast_lane(float v, int k) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
+}
+
+template <int DP>
 __global__ __launch_bounds__(64) void dense_carry_kernel(CarryArgs g) {
     if (g.do_check && blockIdx.x == 0) run_check(g.chk);
-    __shared__ float y[64];
     const int b = blockIdx.x;
     const int i = threadIdx.x;
     const int D = g.D;
+    const bool live = i < D;
     const size_t cb = static_cast<size_t>(b) * g.NC;
-    float yi = 0.0f;
-    if (i < D) {
-        yi = g.s0[b * g.s0s + i];
-        y[i] = yi;
-        g.carry[cb * D + i] = yi;
+    float y = 0.0f;
+    if (live) {
+        y = g.s0[b * g.s0s + i];
+        g.carry[cb * D + i] = y;
     }
-    __syncthreads();
+    float cur[DP] = {}, nxt[DP] = {};
+    float bc = 0.0f, bn = 0.0f;
+    auto load = [&](int c, float (&row)[DP], float& off) {
+        const float* M = g.aggA + (cb + c) * D * D + static_cast<size_t>(i) * D;
+#pragma unroll
+        for (int k = 0; k < DP; ++k) row[k] = (live && k < D) ? M[k] : 0.0f;
+        off = live ? g.aggB[(cb + c) * D + i] : 0.0f;
+    };
+    if (g.NC > 1) load(0, cur, bc);
     for (int c = 0; c + 1 < g.NC; ++c) {
-        float acc = 0.0f;
-        if (i < D) {
-            const float* M = g.aggA + (cb + c) * D * D + static_cast<size_t>(i) * D;
-            acc = g.aggB[(cb + c) * D + i];
-            for (int k = 0; k < D; ++k) acc += M[k] * y[k];
-        }
-        __syncthreads();
-        if (i < D) {
-            y[i] = acc;
-            g.carry[(cb + c + 1) * D + i] = acc;
-        }
-        __syncthreads();
+        if (c + 2 < g.NC) load(c + 1, nxt, bn);
+        float acc = bc;
+#pragma unroll
+        for (int k = 0; k < DP; ++k) acc += cur[k] * bcast_lane(y, k);
+        y = live ? acc : 0.0f;
+        if (live) g.carry[(cb + c + 1) * D + i] = acc;
+#pragma unroll
+        for (int k = 0; k < DP; ++k) cur[k] = nxt[k];
+        bc = bn;
     }
 }
 
 hipError_t launch_dense_carry(const CarryArgs& a, hipStream_t st) {
-    dense_carry_kernel<<<a.B, 64, 0, st>>>(a);
+    const int DP = a.D <= 4 ? 4 : a.D <= 8 ? 8 : a.D <= 16 ? 16 : a.D <= 32 ? 32 : 64;
+    switch (DP) {
+        case 4: dense_carry_kernel<4><<<a.B, 64, 0, st>>>(a); break;
+        case 8: dense_carry_kernel<8><<<a.B, 64, 0, st>>>(a); break;
+        case 16: dense_carry_kernel<16><<<a.B, 64, 0, st>>>(a); break;
+        case 32: dense_carry_kernel<32><<<a.B, 64, 0, st>>>(a); break;
+        default: dense_carry_kernel<64><<<a.B, 64, 0, st>>>(a); break;
+    }
     return hipGetLastError();
 }
 

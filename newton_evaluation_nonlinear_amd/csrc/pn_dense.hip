@@ -1,0 +1,421 @@
+// Newton (dense Jacobian) iteration for the matrix cells with D padded to 16
+// or 32, on the FP32 matrix cores.
+//
+// One wavefront owns one chunk of L steps and walks it in sub-chunks of 32
+// steps staged through LDS.  Per sub-chunk it
+//   1. computes the input projection U x_t + b once;
+//   2. evaluates the cell at the old iterate (v_t and the Jacobian row
+//      scalings) and replays s^_t = v_t + A_t (s^_{t-1} - p_t) from the carry,
+//      damps, and stores s^(i+1) [the update of PN §1.2];
+//   3. evaluates the cell at the new iterate (residual and the maps of
+//      iteration i+1) and extends the chunk map
+//          M <- A_t M,   bg <- A_t (bg - p_t) + v_t
+//      [the affine-map composition of PN §2.1] with A_t = diag(z) +
+//      sum_g diag(c_g) W_g (tanh RNN: A_t = diag(1 - v^2) W).
+// W_g M is a DP x DP x DP product done as MFMA k-steps: the accumulator of
+// one step holds M in the instruction's output layout, whose rows per lane
+// group are exactly the k indices that lane group supplies as the B operand
+// of the next step, so the chain never leaves registers.  The A operand
+// (W_g restricted to that k subset) is loaded once into registers and also
+// serves the matrix-vector products of the replay and the offset chain.
+//
+// Lane roles (64 lanes): i = lane % DP is a state row, h = lane / DP picks the
+// k subset K_h = {krow(h, s), s < KS}.  Row-vector dot products are partial
+// sums over K_h combined across the NH = 64 / DP lane groups.
+
+#include "pn_device.hpp"
+
+namespace pn {
+
+constexpr int kCellTanhRnnD = 1;
+constexpr int kCellGruD = 2;
+constexpr int kSub = 16;          // steps per LDS sub-chunk
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+template <int DP> struct MfmaTile;
+template <> struct MfmaTile<32> {
+    static constexpr int NH = 2, KS = 16;
+    typedef v16f acc_t;
+    // k index (= output row) of slot s for lane group h
+    __device__ static int krow(int h, int s) { return 8 * (s >> 2) + 4 * h + (s & 3); }
+    __device__ static acc_t step(float a, float b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct MfmaTile<16> {
+    static constexpr int NH = 4, KS = 4;
+    typedef v4f acc_t;
+    __device__ static int krow(int h, int s) { return 4 * h + s; }
+    __device__ static acc_t step(float a, float b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// The lane's k subset of a DP-vector in LDS, as KS/4 aligned 16-byte reads:
+// for DP = 32 the subset is {8g + 4h + t}, for DP = 16 it is {4h + t}.
+template <int DP>
+__device__ __forceinline__ float4 kgroup(const float* v, int h, int g) {
+    if constexpr (DP == 32) return *reinterpret_cast<const float4*>(v + 8 * g + 4 * h);
+    else return *reinterpret_cast<const float4*>(v + 4 * h);
+}
+
+// sum of v over the NH lane groups that share a row (lanes i, i+DP, ...)
+template <int DP>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (DP == 32) {
+        v += __shfl_xor(v, 32, 64);
+    } else {
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+    }
+    return v;
+}
+
+template <int CELL> struct DTraits;
+template <> struct DTraits<kCellTanhRnnD> { static constexpr int NG = 1, NCO = 1; };
+template <> struct DTraits<kCellGruD> { static constexpr int NG = 3, NCO = 4; };
+
+// LDS layout (floats) for one wave / one chunk.
+template <int CELL, int DP>
+struct DLds {
+    static constexpr int NG = DTraits<CELL>::NG, NCO = DTraits<CELL>::NCO;
+    static __host__ __device__ size_t floats(int m) {
+        return 2ull * (kSub + 1) * DP        // P, N rows
+             + static_cast<size_t>(kSub) * m  // x rows
+             + static_cast<size_t>(NG) * kSub * DP   // input projection
+             + static_cast<size_t>(kSub) * DP        // v
+             + static_cast<size_t>(NCO) * kSub * DP  // Jacobian coefficients
+             + static_cast<size_t>(NG) * m * DP      // U^T (all gates)
+             + 2 * DP;                               // vector exchange
+    }
+};
+
+// Cell evaluation for row p (LDS, DP floats) with the lane's partial weights
+// wr[g][s] = W_g[i][krow(h,s)].  Returns v and writes the coefficient values
+// for row i into co[q] (q < NCO).
+template <int CELL, int DP>
+__device__ __forceinline__ float cell_eval_row(const float (&wr)[DTraits<CELL>::NG][MfmaTile<DP>::KS],
+                                               const float* p, const float* xp, int i, int h,
+                                               const float (&bhh)[3], float (&co)[DTraits<CELL>::NCO]) {
+    using Tl = MfmaTile<DP>;
+    constexpr int NG = DTraits<CELL>::NG;
+    float acc[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[g] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < Tl::KS / 4; ++q) {
+        const float4 p4 = kgroup<DP>(p, h, q);
+        const float pk[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) acc[g] += wr[g][4 * q + t] * pk[t];
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[g] = group_sum<DP>(acc[g]);
+    if constexpr (CELL == kCellTanhRnnD) {
+        const float v = tanh_f(acc[0] + xp[0]);
+        co[0] = 1.0f - v * v;
+        return v;
+    } else {
+        const float r = sigmoid_f(xp[0] + acc[0] + bhh[0]);
+        const float z = sigmoid_f(xp[kSub * DP] + acc[1] + bhh[1]);
+        const float gg = acc[2] + bhh[2];
+        const float n = tanh_f(xp[2 * kSub * DP] + r * gg);
+        const float pi = p[i];
+        const float dn = (1.0f - z) * (1.0f - n * n);
+        co[0] = z;
+        co[1] = (pi - n) * z * (1.0f - z);
+        co[2] = dn * r;
+        co[3] = dn * gg * r * (1.0f - r);
+        return (1.0f - z) * n + z * pi;
+    }
+}
+
+// (A_t d)[i] for the difference vector d in LDS (only the lane's k subset is
+// read; d_i is passed for the diagonal GRU term).
+template <int CELL, int DP>
+__device__ __forceinline__ float jac_apply_row(const float (&wr)[DTraits<CELL>::NG][MfmaTile<DP>::KS],
+                                               const float* d, int h,
+                                               const float (&co)[DTraits<CELL>::NCO], float di) {
+    using Tl = MfmaTile<DP>;
+    constexpr int NG = DTraits<CELL>::NG;
+    float acc[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[g] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < Tl::KS / 4; ++q) {
+        const float4 d4 = kgroup<DP>(d, h, q);
+        const float dk[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) acc[g] += wr[g][4 * q + t] * dk[t];
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[g] = group_sum<DP>(acc[g]);
+    if constexpr (CELL == kCellTanhRnnD) {
+        return co[0] * acc[0];
+    } else {
+        // gates are stored (r, z, n); coefficients (z, cz, cn, cr)
+        return co[0] * di + co[1] * acc[1] + co[2] * acc[2] + co[3] * acc[0];
+    }
+}
+
+template <int CELL, int DP, int PHASE>
+__global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
+    if constexpr (PHASE != kPrologue) {
+        if (g.ctrl->stop) return;
+    }
+    using Tl = MfmaTile<DP>;
+    using acc_t = typename Tl::acc_t;
+    constexpr int NG = DTraits<CELL>::NG;
+    constexpr int NCO = DTraits<CELL>::NCO;
+    constexpr int KS = Tl::KS;
+    extern __shared__ float lds[];
+    const int D = g.D, m = g.m;
+    const int lane = threadIdx.x;
+    const int i = lane % DP, h = lane / DP;
+    const bool live = i < D;
+    const int c = blockIdx.x, b = blockIdx.y;
+    const int t0 = c * g.L;
+    const int Lc = min(g.L, g.Tw - t0);
+    const size_t ci = static_cast<size_t>(b) * g.NC + c;
+    const size_t HS = static_cast<size_t>(g.B) * g.NC * D;
+    const float* s0 = g.s0 + b * g.s0s;
+
+    float* P = lds;                          // [kSub+1][DP]
+    float* N = P + (kSub + 1) * DP;          // [kSub+1][DP]
+    float* X = N + (kSub + 1) * DP;          // [kSub][m]
+    float* XP = X + kSub * m;                // [NG][kSub][DP]
+    float* V = XP + NG * kSub * DP;          // [kSub][DP]
+    float* CO = V + kSub * DP;               // [NCO][kSub][DP]
+    float* UT = CO + NCO * kSub * DP;        // [NG][m][DP]
+    float* YV = UT + NG * m * DP;            // [2][DP]
+
+    const float* w = g.w;
+    // prepared layout: tanh RNN WT | UT | bias | wdiag;  GRU WhT | WiT | bih | bhh | whdiag
+    const float* wUT = w + NG * DP * DP;
+    const float* wbi = wUT + NG * m * DP;
+    const float* wbh = wbi + NG * DP;         // GRU only
+    float wr[NG][KS];
+#pragma unroll
+    for (int gt = 0; gt < NG; ++gt)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) wr[gt][s] = w[(gt * DP + Tl::krow(h, s)) * DP + i];
+    copy_to_lds<64>(UT, wUT, NG * m * DP);
+    const float bias_i[3] = {wbi[i], NG > 1 ? wbi[DP + i] : 0.0f, NG > 2 ? wbi[2 * DP + i] : 0.0f};
+    float bhh_l[3] = {0.0f, 0.0f, 0.0f};
+    if constexpr (CELL == kCellGruD) {
+        bhh_l[0] = wbh[i];
+        bhh_l[1] = wbh[DP + i];
+        bhh_l[2] = wbh[2 * DP + i];
+    }
+
+    // chunk map: M in accumulator layout (column lane%DP, rows krow(h, r)), offset bg[i]
+    acc_t M;
+#pragma unroll
+    for (int r = 0; r < KS; ++r) M[r] = (Tl::krow(h, r) == i && live) ? 1.0f : 0.0f;
+    float bg = 0.0f;
+    uint32_t rb = 0;
+
+    const bool has_next = c + 1 < g.NC;
+    const float* cr = g.carry + ci * D;
+    float shat = 0.0f;                       // s^ at the row before the current one (lane row i)
+    float* sg = g.s + b * g.ss + static_cast<int64_t>(t0) * D;
+    const float* xg = g.x + b * g.xs + static_cast<int64_t>(t0) * m;
+
+    // row t0-1 of the old and the new iterate
+    {
+        float po = 0.0f, pn = 0.0f;
+        if (live) {
+            if constexpr (PHASE == kPrologue) {
+                po = pn = s0[i];
+            } else {
+                po = (PHASE == kFirst || c == 0) ? s0[i] : g.halo[(g.iter & 1) * HS + (ci - 1) * D + i];
+                shat = cr[i];
+                pn = g.undamped ? shat : po + g.lam * (shat - po);
+            }
+        }
+        if (h == 0) {
+            P[i] = po;
+            N[i] = pn;
+        }
+    }
+
+    for (int j0 = 0; j0 < Lc; j0 += kSub) {
+        const int Sc = min(kSub, Lc - j0);
+        // ---- stage x rows and the old iterate rows j0 .. j0+Sc-1 (P[1..Sc])
+        copy_to_lds<64>(X, xg + static_cast<int64_t>(j0) * m, Sc * m);
+        if constexpr (PHASE == kPrologue || PHASE == kFirst) {
+            for (int e = lane; e < Sc * DP; e += 64) {
+                const int q = e % DP;
+                P[DP + e] = q < D ? s0[q] : 0.0f;
+            }
+        } else {
+            copy_rows_to_lds<64>(P + DP, DP, sg + static_cast<int64_t>(j0) * D, D, Sc, D);
+        }
+        __syncthreads();
+        // ---- input projection U x + b_ih for every row and gate
+        for (int j = 0; j < Sc; ++j) {
+#pragma unroll
+            for (int gt = 0; gt < NG; ++gt) {
+                float a = 0.0f;
+                for (int q = h; q < m; q += Tl::NH) a += UT[(gt * m + q) * DP + i] * X[j * m + q];
+                a = group_sum<DP>(a);
+                if (h == 0) XP[(gt * kSub + j) * DP + i] = a + bias_i[gt];
+            }
+        }
+        __syncthreads();
+
+        if constexpr (PHASE != kPrologue) {
+            // ---- maps of iteration i at the old iterate, then the replay
+            for (int j = 0; j < Sc; ++j) {
+                float co[NCO];
+                const float v = cell_eval_row<CELL, DP>(wr, P + j * DP, XP + j * DP + i, i, h, bhh_l, co);
+                if (h == 0) {
+                    V[j * DP + i] = live ? v : 0.0f;
+#pragma unroll
+                    for (int q = 0; q < NCO; ++q) CO[(q * kSub + j) * DP + i] = live ? co[q] : 0.0f;
+                }
+            }
+            __syncthreads();
+            for (int j = 0; j < Sc; ++j) {
+                const float di = live ? shat - P[j * DP + i] : 0.0f;
+                if (h == 0) YV[i] = di;
+                __syncthreads();
+                float co[NCO];
+#pragma unroll
+                for (int q = 0; q < NCO; ++q) co[q] = CO[(q * kSub + j) * DP + i];
+                const float ad = jac_apply_row<CELL, DP>(wr, YV, h, co, di);
+                shat = V[j * DP + i] + ad;
+                if (j0 + j == Lc - 1 && has_next && live) shat = cr[D + i];
+                const float so = P[(j + 1) * DP + i];
+                const float sn = g.undamped ? shat : so + g.lam * (shat - so);
+                if (h == 0) N[(j + 1) * DP + i] = live ? sn : 0.0f;
+                __syncthreads();
+            }
+            for (int e = lane; e < Sc * D; e += 64) {
+                const int j = e / D, q = e % D;
+                sg[static_cast<int64_t>(j0 + j) * D + q] = N[(j + 1) * DP + q];
+            }
+        } else {
+            for (int e = lane; e < Sc * DP; e += 64) N[DP + e] = P[DP + e];
+        }
+        __syncthreads();
+
+        // ---- maps of iteration i+1 at the new iterate; residual
+        for (int j = 0; j < Sc; ++j) {
+            float co[NCO];
+            const float v = cell_eval_row<CELL, DP>(wr, N + j * DP, XP + j * DP + i, i, h, bhh_l, co);
+            if (live) rb = max(rb, abs_bits(N[(j + 1) * DP + i] - v));
+            if (h == 0) {
+                V[j * DP + i] = live ? v : 0.0f;
+#pragma unroll
+                for (int q = 0; q < NCO; ++q) CO[(q * kSub + j) * DP + i] = live ? co[q] : 0.0f;
+            }
+        }
+        __syncthreads();
+
+        // ---- extend the chunk map over the sub-chunk
+        for (int j = 0; j < Sc; ++j) {
+            // W_g M for each gate, then row-scale and combine
+            acc_t C[NG];
+#pragma unroll
+            for (int gt = 0; gt < NG; ++gt) {
+#pragma unroll
+                for (int r = 0; r < KS; ++r) C[gt][r] = 0.0f;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) C[gt] = Tl::step(wr[gt][s], M[s], C[gt]);
+            }
+            // offset: bg <- A_j (bg - p_j) + v_j  (p_j = N[j])
+            const float dbi = live ? bg - N[j * DP + i] : 0.0f;
+            if (h == 0) YV[DP + i] = dbi;
+            __syncthreads();
+            {
+                float co[NCO];
+#pragma unroll
+                for (int q = 0; q < NCO; ++q) co[q] = CO[(q * kSub + j) * DP + i];
+                bg = V[j * DP + i] + jac_apply_row<CELL, DP>(wr, YV + DP, h, co, dbi);
+            }
+            // row scalings of the lane's accumulator rows
+            float rs[NCO][KS];
+#pragma unroll
+            for (int q = 0; q < NCO; ++q)
+#pragma unroll
+                for (int u = 0; u < KS / 4; ++u) {
+                    const float4 c4 = kgroup<DP>(CO + (q * kSub + j) * DP, h, u);
+                    rs[q][4 * u] = c4.x;
+                    rs[q][4 * u + 1] = c4.y;
+                    rs[q][4 * u + 2] = c4.z;
+                    rs[q][4 * u + 3] = c4.w;
+                }
+#pragma unroll
+            for (int r = 0; r < KS; ++r) {
+                if constexpr (CELL == kCellTanhRnnD) {
+                    M[r] = rs[0][r] * C[0][r];
+                } else {
+                    M[r] = rs[0][r] * M[r] + rs[1][r] * C[1][r] + rs[2][r] * C[2][r] + rs[3][r] * C[0][r];
+                }
+            }
+            __syncthreads();
+        }
+        // ---- carry the last rows into the next sub-chunk
+        const float plast = P[Sc * DP + i];
+        const float nlast = N[Sc * DP + i];
+        __syncthreads();
+        if (h == 0) {
+            P[i] = plast;
+            N[i] = nlast;
+        }
+        __syncthreads();
+    }
+
+    if constexpr (PHASE != kPrologue) {
+        if (h == 0 && live) g.halo[((g.iter + 1) & 1) * HS + ci * D + i] = N[i];
+    }
+    // chunk map out: M[row][col] row-major, col = i
+    float* aA = g.aggA + ci * D * D;
+#pragma unroll
+    for (int r = 0; r < KS; ++r) {
+        const int row = Tl::krow(h, r);
+        if (row < D && live) aA[row * D + i] = M[r];
+    }
+    if (h == 0 && live) g.aggB[ci * D + i] = bg;
+    rb = wave_max_u32(rb);
+    if (lane == 0) g.rpart[ci] = rb;
+}
+
+template <int CELL, int DP>
+static hipError_t launch_dense_phase(int phase, const CellArgs& a, hipStream_t st) {
+    const size_t lds = DLds<CELL, DP>::floats(a.m) * sizeof(float);
+    const dim3 grid(a.NC, a.B);
+    if (phase == kPrologue) dense_pass<CELL, DP, kPrologue><<<grid, 64, lds, st>>>(a);
+    else if (phase == kFirst) dense_pass<CELL, DP, kFirst><<<grid, 64, lds, st>>>(a);
+    else dense_pass<CELL, DP, kSteady><<<grid, 64, lds, st>>>(a);
+    return hipGetLastError();
+}
+
+bool dense_mfma_supported(int kind, int DP, int m) {
+    if (DP != 16 && DP != 32) return false;
+    const size_t f = kind == kCellTanhRnnD ? DLds<kCellTanhRnnD, 32>::floats(m) : DLds<kCellGruD, 32>::floats(m);
+    return f * sizeof(float) <= 64 * 1024;
+}
+
+size_t dense_mfma_lds_bytes(int kind, int DP, int m) {
+    if (kind == kCellTanhRnnD) return (DP == 16 ? DLds<kCellTanhRnnD, 16>::floats(m) : DLds<kCellTanhRnnD, 32>::floats(m)) * sizeof(float);
+    return (DP == 16 ? DLds<kCellGruD, 16>::floats(m) : DLds<kCellGruD, 32>::floats(m)) * sizeof(float);
+}
+
+hipError_t launch_dense_mfma_pass(int kind, int DP, int phase, const CellArgs& a, hipStream_t st) {
+    if (kind == kCellTanhRnnD) {
+        return DP == 16 ? launch_dense_phase<kCellTanhRnnD, 16>(phase, a, st)
+                        : launch_dense_phase<kCellTanhRnnD, 32>(phase, a, st);
+    }
+    return DP == 16 ? launch_dense_phase<kCellGruD, 16>(phase, a, st)
+                    : launch_dense_phase<kCellGruD, 32>(phase, a, st);
+}
+
+}  // namespace pn

@@ -29,6 +29,74 @@ __device__ __forceinline__ float sigmoid_f(float u) {
 // integer max is an exact, order-independent, NaN-preserving max of |v|.
 __device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7fffffffu; }
 
+// ---------------------------------------------------------------- staging
+// Global -> LDS copies by all NT threads of a workgroup.  Each thread issues
+// KB loads before the matching LDS stores, so KB loads per thread are in
+// flight instead of one (a plain copy loop waits for every load).
+
+// dst[e] = src[e], e < n.  Uses 16-byte accesses when both sides allow it.
+template <int NT, int KB = 8>
+__device__ __forceinline__ void copy_to_lds(float* dst, const float* __restrict__ src, int n) {
+    const int t = threadIdx.x;
+    const bool v4 = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
+    int done = 0;
+    if (v4) {
+        const int n4 = n >> 2;
+        const float4* s4 = reinterpret_cast<const float4*>(src);
+        float4* d4 = reinterpret_cast<float4*>(dst);
+        for (int base = 0; base < n4; base += NT * KB) {
+            float4 v[KB];
+#pragma unroll
+            for (int u = 0; u < KB; ++u) {
+                const int e = base + u * NT + t;
+                v[u] = e < n4 ? s4[e] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int u = 0; u < KB; ++u) {
+                const int e = base + u * NT + t;
+                if (e < n4) d4[e] = v[u];
+            }
+        }
+        done = n4 << 2;
+    }
+    for (int base = done; base < n; base += NT * KB) {
+        float v[KB];
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            const int e = base + u * NT + t;
+            v[u] = e < n ? src[e] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            const int e = base + u * NT + t;
+            if (e < n) dst[e] = v[u];
+        }
+    }
+}
+
+// rows x cols block of a row-major global array (row stride src_stride) into
+// LDS rows of dst_stride >= cols floats; columns [cols, dst_stride) are zeroed.
+template <int NT, int KB = 8>
+__device__ __forceinline__ void copy_rows_to_lds(float* dst, int dst_stride, const float* __restrict__ src,
+                                                 int64_t src_stride, int rows, int cols) {
+    const int t = threadIdx.x;
+    const int n = rows * dst_stride;
+    for (int base = 0; base < n; base += NT * KB) {
+        float v[KB];
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            const int e = base + u * NT + t;
+            const int r = e / dst_stride, q = e - r * dst_stride;
+            v[u] = (e < n && q < cols) ? src[r * src_stride + q] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            const int e = base + u * NT + t;
+            if (e < n) dst[e] = v[u];
+        }
+    }
+}
+
 // Diagonal coefficient of the affine map for the diagonal modes.
 template <int MODE>
 __device__ __forceinline__ float mode_coef(float jac_diag) {

@@ -107,11 +107,16 @@ hipError_t launch_fill(float* out, int64_t ss, const float* s0, int64_t s0s, int
 
 hipError_t launch_prep_weights(int kind, const float* params, float* w, int D, int DP, int m,
                                hipStream_t st);
-size_t prepared_weight_floats(int kind, int DP, int m);
+__host__ __device__ size_t prepared_weight_floats(int kind, int DP, int m);
 hipError_t launch_cell_pass(int kind, int DP, bool dense, int phase, const CellArgs& a,
                             hipStream_t st);
 size_t cell_pass_lds_bytes(int kind, int DP, bool dense, int L, int m);
+bool cell_pass_stages_weights(int kind, int DP, bool dense, int L, int m);
 int cell_pass_nblocks(const CellArgs& a);
+// Newton on the matrix cores (D padded to 16 or 32): one wavefront per chunk.
+bool dense_mfma_supported(int kind, int DP, int m);
+size_t dense_mfma_lds_bytes(int kind, int DP, int m);
+hipError_t launch_dense_mfma_pass(int kind, int DP, int phase, const CellArgs& a, hipStream_t st);
 
 // Standalone affine scan.
 struct ScanArgs {

@@ -5,9 +5,10 @@ Acceptance for one solve (status, counts, trajectory, residual):
      float32 oracle, whose arithmetic is the library's);
   2. updates per window equal the oracle's.  The count is an integer decided
      by a floating-point comparison r <= tol; where the oracle's residual at
-     the deciding iteration lies within COUNT_BAND (relative) of tol, the
-     float32 decision may legitimately land on the other side, so a count one
-     off is accepted there.  Where the float64 count differs by more, the
+     the deciding iteration lies within the ambiguity band of tol (2% of tol
+     plus two float32 ulps of the state scale), the float32 decision may
+     legitimately land on the other side, so a count one off is accepted
+     there.  Where the float64 count differs by more, the
      decision is taken in the library's precision: the counts must then match
      the float32 oracle (same band).  This happens only on runs with huge
      transients (Picard on the GRU reaches 1e20+), where the precision itself
@@ -27,7 +28,8 @@ import newton_evaluation_nonlinear_amd as pn
 
 TRAJ_TOL = 1e-4
 RESID_SLACK = 1e-6
-COUNT_BAND = 0.02
+COUNT_BAND = 0.02          # relative part of the ambiguity band around tol
+ULP1 = 2.0 ** -23          # float32 spacing at 1.0
 
 _oracle_cache = {}
 
@@ -84,9 +86,14 @@ def _windows(T, W):
 
 def _counts_within_band(gw, ref, tol):
     """Counts equal, or one off where ref's residual at the deciding iteration
-    lies within COUNT_BAND of tol."""
+    lies within the ambiguity band of tol: COUNT_BAND relative, plus two float32
+    ulps of the state scale, the resolution at which a float32 residual
+    |s_t - f_t(s_{t-1})| of states of that size can be computed at all."""
     if len(gw) != len(ref.window_iters):
         return False
+    finite = ref.s[np.isfinite(ref.s)]
+    scale = max(1.0, float(np.max(np.abs(finite)))) if finite.size else 1.0
+    band = COUNT_BAND * tol + 2 * ULP1 * scale
     for w, (kg, ko) in enumerate(zip(gw, ref.window_iters)):
         if kg == ko:
             continue
@@ -97,9 +104,9 @@ def _counts_within_band(gw, ref, tol):
         r = h[k] if k < len(h) else None
         if r is None:
             return False
-        if kg > ko and not r >= tol * (1 - COUNT_BAND):
+        if kg > ko and not r >= tol - band:
             return False
-        if kg < ko and not r <= tol * (1 + COUNT_BAND):
+        if kg < ko and not r <= tol + band:
             return False
     return True
 

@@ -126,7 +126,7 @@ def test_cfg5_gru_damped_windows_small():
     _parity(wl, Q)
 
 
-@pytest.mark.parametrize("D", [1, 3, 5, 16, 33, 64])
+@pytest.mark.parametrize("D", [1, 3, 5, 12, 16, 20, 32, 33, 64])
 @pytest.mark.parametrize("kind", [pn.CELL_TANH_RNN, pn.CELL_GRU])
 def test_matrix_cells_other_widths(kind, D):
     rng = np.random.default_rng(100 + D)
@@ -135,6 +135,19 @@ def test_matrix_cells_other_widths(kind, D):
     wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-6, damping=1.0, window=0,
               max_iter=T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
               s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32))
+    for mode in (N, Q):
+        _parity(wl, mode)
+
+
+@pytest.mark.parametrize("kind", [pn.CELL_TANH_RNN, pn.CELL_GRU])
+def test_matrix_cells_wide_input(kind):
+    # weights too large to stage in LDS: the kernels read them from global memory
+    rng = np.random.default_rng(7)
+    D, m, B, T = 64, 300, 2, 90
+    params = workloads.random_cell_params(kind, D, m, rng, 1.0)
+    wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-5, damping=1.0, window=0,
+              max_iter=T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=np.zeros((B, D), dtype=np.float32))
     for mode in (N, Q):
         _parity(wl, mode)
 
