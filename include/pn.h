@@ -91,7 +91,10 @@ typedef struct pn_profile {
     double apply_ms;          /* summed device time of apply launches       */
     int32_t apply_launches;   /* launches, including early-exit ones          */
     double apply_bytes;       /* summed algorithmic bytes of those launches   */
-    double apply_flops;       /* summed algorithmic flops (dense compose etc.)*/
+    double apply_flops;       /* summed algorithmic flops: matrix-cell
+                                 evaluations and, for Newton, the D x D
+                                 chunk-map compose (0 for the channel-wise
+                                 cell)                                        */
     double total_ms;          /* first launch to last completion              */
 } pn_profile;
 

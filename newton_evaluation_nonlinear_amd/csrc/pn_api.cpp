@@ -279,9 +279,15 @@ double apply_bytes(const Plan& p, int Tw, bool first) {
 }
 
 double apply_flops(const Plan& p, int Tw) {
-    // dense Newton: one D x D compose per step (2 D^3) dominates
-    if (!p.dense) return 0.0;
-    return static_cast<double>(p.B) * Tw * 2.0 * p.D * p.D * p.D;
+    // algorithmic flops of one apply launch per (b, t): two cell evaluations
+    // (recurrent products 2*NG*D^2 each) and one input projection (2*NG*D*m);
+    // Newton adds one D x D chunk-map compose (2 D^3) and two matrix-vector
+    // chains through the Jacobian (2*NG*D^2 each)
+    if (!p.matrix_cell) return 0.0;
+    const double D = p.D, m = p.m, NG = p.kind == PN_CELL_GRU ? 3.0 : 1.0;
+    double per = 2.0 * (2.0 * NG * D * D) + 2.0 * NG * D * m;
+    if (p.dense) per += 2.0 * D * D * D + 2.0 * (2.0 * NG * D * D);
+    return static_cast<double>(p.B) * Tw * per;
 }
 
 int record(SolveCtx& c, size_t* idx) {
