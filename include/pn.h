@@ -112,7 +112,17 @@ typedef struct pn_opts {
     int32_t* window_iters;    /* host; updates per window (truncated)          */
     int64_t window_iters_len;
     pn_profile* profile;      /* host; NULL = no event timing                   */
+    int32_t flags;            /* PN_FLAG_* bits, 0 = defaults                    */
 } pn_opts;
+
+/* pn_opts.flags.  PN_FLAG_PERSISTENT runs a solve of a matrix cell in a
+ * diagonal mode as one cooperative launch (all windows and iterations, with
+ * grid-wide barriers between the carry and apply phases), when the device
+ * supports cooperative launches and the weights fit in LDS; otherwise, and by
+ * default, each phase is its own launch.  Results meet the same bar; on
+ * MI355X a grid barrier costs more than a launch boundary, so the default is
+ * the faster one for the shapes measured here. */
+enum { PN_FLAG_PERSISTENT = 1 };
 
 /* Fill *o with the defaults: damping 1, chunk 0, window 0, everything else
  * NULL / 0. */

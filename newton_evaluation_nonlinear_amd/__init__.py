@@ -22,6 +22,7 @@ CELL_DIAG_TANH, CELL_TANH_RNN, CELL_GRU = 0, 1, 2
 JACOBI, PICARD, QUASI_NEWTON, NEWTON = 0, 1, 2, 3
 OK, NOT_CONVERGED, NONFINITE = 0, 1, 2
 EINVAL, EUNSUPPORTED, EHIP, EWORKSPACE = -1, -2, -3, -4
+FLAG_PERSISTENT = 1
 
 EXPORTED = ("pn_opts_init", "pn_eval", "pn_eval_ex", "pn_workspace_bytes", "pn_affine_scan",
             "pn_affine_scan_workspace_bytes", "pn_last_error", "pn_version")
@@ -50,7 +51,8 @@ class Opts(ctypes.Structure):
                 ("resid_hist", ctypes.POINTER(ctypes.c_float)), ("resid_hist_len", ctypes.c_int32),
                 ("window_iters", ctypes.POINTER(ctypes.c_int32)),
                 ("window_iters_len", ctypes.c_int64),
-                ("profile", ctypes.POINTER(Profile))]
+                ("profile", ctypes.POINTER(Profile)),
+                ("flags", ctypes.c_int32)]
 
 
 _lib = None
@@ -108,13 +110,14 @@ def _stream_ptr(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def make_opts(damping=1.0, window=0, chunk=0, stream=None):
+def make_opts(damping=1.0, window=0, chunk=0, stream=None, flags=0):
     o = Opts()
     lib().pn_opts_init(ctypes.byref(o))
     o.damping = float(damping)
     o.window = int(window)
     o.chunk = int(chunk)
     o.stream = stream
+    o.flags = int(flags)
     return o
 
 
@@ -139,7 +142,7 @@ class Result:
 
 
 def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, damping=1.0,
-         window=0, chunk=0, out=None, history=False, profile=False, workspace=None):
+         window=0, chunk=0, out=None, history=False, profile=False, workspace=None, flags=0):
     """Solve s_t = f(s_{t-1}, x_t) for t = 1..T over the batch; see include/pn.h.
 
     params, x [B,T,m], s0 [B,D] are float32 tensors on one HIP device.
@@ -157,7 +160,7 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     if out is None:
         out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
     c = Cell(int(cell_kind), int(m))
-    o = make_opts(damping, window or 0, chunk, _stream_ptr(dev))
+    o = make_opts(damping, window or 0, chunk, _stream_ptr(dev), flags)
     nbytes = lib().pn_workspace_bytes(ctypes.byref(c), B, T, D, int(mode), ctypes.byref(o))
     if nbytes == 0:
         raise PnError(EINVAL, last_error())

@@ -65,8 +65,10 @@ struct Plan {
     int L, NC;             // chunk length, chunks of a full window
     int DP, cpb;           // padded D (matrix cells), channels per block (diag cell)
     bool dense, matrix_cell, mfma;
-    int nblocks;
+    bool persist_ok;       // shape allows the one-launch persistent solver
+    int nblocks, nwin, hist_cap;
     size_t off_ctrl, off_rpart, off_aggA, off_aggB, off_carry, off_halo, off_w, total;
+    size_t off_sync, off_winfo, off_hist;
 };
 
 int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int32_t mode,
@@ -138,6 +140,9 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
         if (cell_pass_lds_bytes(p.kind, p.DP, p.dense, p.L, p.m) > 160 * 1024)
             return fail(PN_EUNSUPPORTED, "chunk of %d steps needs too much LDS for D=%d, m=%d", p.L, p.D, p.m);
     }
+    p.nwin = static_cast<int>((T + p.W - 1) / p.W);
+    p.persist_ok = p.matrix_cell && !p.dense && cell_persist_eligible(p.kind, p.DP, p.L, p.m);
+    p.hist_cap = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(p.nwin) * (p.W + 1), 1 << 16));
     const size_t bnd = static_cast<size_t>(p.B) * p.NC * p.D;
     size_t off = 0;
     p.off_ctrl = off; off = align_up(off + sizeof(Ctrl));
@@ -148,6 +153,12 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
     p.off_halo = off; off = align_up(off + sizeof(float) * 2 * bnd);
     p.off_w = off;
     if (p.matrix_cell) off = align_up(off + sizeof(float) * prepared_weight_floats(p.kind, p.DP, p.m));
+    p.off_sync = p.off_winfo = p.off_hist = off;
+    if (p.persist_ok) {
+        p.off_sync = off; off = align_up(off + 256);
+        p.off_winfo = off; off = align_up(off + sizeof(int32_t) * 2 * p.nwin);
+        p.off_hist = off; off = align_up(off + sizeof(float) * p.hist_cap);
+    }
     p.total = off;
     return PN_OK;
 }
@@ -390,6 +401,89 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
     return PN_OK;
 }
 
+// The whole solve as one cooperative launch (matrix cells, diagonal modes).
+// Returns PN_EUNSUPPORTED (no launch made) when the device cannot run it, so
+// the caller falls back to the multi-launch driver.
+int solve_persistent(SolveCtx& c, const float* x, const float* s0, float* out, int64_t T,
+                     std::vector<int>* wit, int* total, int* overall) {
+    const Plan& p = *c.p;
+    int dev = 0, coop = 0;
+    PN_HIP(hipGetDevice(&dev));
+    PN_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
+    if (!coop) return PN_EUNSUPPORTED;
+    int nb_max = 0;
+    PN_HIP(cell_persist_max_blocks(p.kind, p.DP, p.L, p.m, &nb_max));
+    if (nb_max < 1) return PN_EUNSUPPORTED;
+    const int nblocks = static_cast<int>(std::min<int64_t>(nb_max, static_cast<int64_t>(p.B) * p.NC));
+    char* ws = c.ws;
+    unsigned* bar = reinterpret_cast<unsigned*>(ws + p.off_sync);
+    int32_t* winfo = reinterpret_cast<int32_t*>(ws + p.off_winfo);
+    PN_HIP(hipMemsetAsync(ws + p.off_sync, 0, 256, c.st));
+    PN_HIP(hipMemsetAsync(winfo, 0xff, sizeof(int32_t) * 2 * p.nwin, c.st));
+    PersistArgs a{};
+    CellArgs& g = a.g;
+    g.w = reinterpret_cast<const float*>(ws + p.off_w);
+    g.xs = T * p.m;
+    g.ss = T * p.D;
+    g.B = p.B; g.D = p.D; g.m = p.m; g.L = p.L;
+    g.aggA = reinterpret_cast<float*>(ws + p.off_aggA);
+    g.aggB = reinterpret_cast<float*>(ws + p.off_aggB);
+    g.carry = reinterpret_cast<float*>(ws + p.off_carry);
+    g.halo = reinterpret_cast<float*>(ws + p.off_halo);
+    g.rpart = reinterpret_cast<uint32_t*>(ws + p.off_rpart);
+    g.ctrl = nullptr;
+    g.mode = p.mode; g.lam = c.lam; g.undamped = c.lam == 1.0f;
+    a.x0 = x; a.s_base = out; a.s0_user = s0;
+    a.T = T; a.W = static_cast<int32_t>(p.W); a.nwin = p.nwin;
+    a.tol = c.tol; a.max_iter = c.max_iter;
+    a.bar = bar; a.err = bar + 1;
+    a.hist_len = reinterpret_cast<int32_t*>(bar + 2);
+    a.win_iters = winfo; a.win_status = winfo + p.nwin;
+    a.hist = reinterpret_cast<float*>(ws + p.off_hist);
+    a.hist_cap = p.hist_cap;
+    size_t e0 = 0, e1 = 0;
+    if (c.tm->on) { int rc = record(c, &e0); if (rc) return rc; }
+    {
+        const hipError_t le = launch_cell_persist(p.kind, p.DP, nblocks, a, c.st);
+        if (le == hipErrorCooperativeLaunchTooLarge) {
+            (void)hipGetLastError();
+            return PN_EUNSUPPORTED;
+        }
+        if (le != hipSuccess) return fail(PN_EHIP, "cooperative launch failed: %s", hipGetErrorString(le));
+    }
+    if (c.tm->on) { int rc = record(c, &e1); if (rc) return rc; }
+    PN_HIP(hipStreamSynchronize(c.st));
+    std::vector<int32_t> info(64 + 2 * p.nwin);
+    PN_HIP(hipMemcpy(info.data(), bar, 256, hipMemcpyDeviceToHost));
+    PN_HIP(hipMemcpy(info.data() + 64, winfo, sizeof(int32_t) * 2 * p.nwin, hipMemcpyDeviceToHost));
+    if (info[1] != 0) return fail(PN_EHIP, "grid barrier of the persistent solver timed out");
+    const int hlen = std::min(info[2], p.hist_cap);
+    if (c.hist && hlen > 0) {
+        c.hist->resize(hlen);
+        PN_HIP(hipMemcpy(c.hist->data(), a.hist, sizeof(float) * hlen, hipMemcpyDeviceToHost));
+    }
+    *total = 0;
+    *overall = PN_OK;
+    double bytes = 0.0, flops = 0.0;
+    for (int w = 0; w < p.nwin; ++w) {
+        const int K = info[64 + w], st = info[64 + p.nwin + w];
+        if (K < 0) break;
+        const int Tw = static_cast<int>(std::min<int64_t>(p.W, T - static_cast<int64_t>(w) * p.W));
+        wit->push_back(K);
+        *total += K;
+        if (K > 0) bytes += apply_bytes(p, Tw, true) + (K - 1) * apply_bytes(p, Tw, false);
+        flops += K * apply_flops(p, Tw);
+        if (st == PN_NONFINITE) { *overall = PN_NONFINITE; break; }
+        if (st == PN_NOT_CONVERGED) *overall = PN_NOT_CONVERGED;
+    }
+    if (c.tm->on) {
+        c.tm->apply.push_back({e0, e1});
+        c.tm->apply_bytes.push_back(bytes);
+        c.tm->apply_flops.push_back(flops);
+    }
+    return PN_OK;
+}
+
 int eval_impl(const pn_cell* cell, const float* params, const float* x, const float* s0, int64_t B,
               int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter, float* out,
               int32_t* iters_out, const pn_opts* o) {
@@ -434,7 +528,13 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     int total = 0, overall = PN_OK;
     std::vector<int> wit;
     const int64_t m = p.m;
-    for (int64_t w0 = 0; w0 < T; w0 += p.W) {
+    bool persisted = false;
+    if (p.persist_ok && o && (o->flags & PN_FLAG_PERSISTENT)) {
+        rc = solve_persistent(c, x, s0, out, T, &wit, &total, &overall);
+        if (rc == PN_OK) persisted = true;
+        else if (rc != PN_EUNSUPPORTED) return rc;
+    }
+    for (int64_t w0 = 0; !persisted && w0 < T; w0 += p.W) {
         const int Tw = static_cast<int>(std::min<int64_t>(p.W, T - w0));
         const float* xw = x + w0 * m;
         float* sw = out + w0 * D;

@@ -249,26 +249,21 @@ __device__ __forceinline__ float jac_row_apply(const float* __restrict__ w, cons
 }
 
 // ---------------------------------------------------------------- the fused pass
-template <int CELL, int DP, bool DENSE, int PHASE, bool STAGE>
-__global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
-    if constexpr (PHASE != kPrologue) {
-        if (g.ctrl->stop) return;
-    }
-    extern __shared__ float lds[];
+// One tile (batch row b, chunk c) of one sweep.  `arr` is the LDS array
+// region, `w` the prepared weights (LDS or global).  Returns the tile's
+// residual bit-max through rb (the caller reduces it over the workgroup).
+template <int CELL, int DP, bool DENSE, int PHASE>
+__device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float* arr,
+                                          const float* w, uint32_t& rb) {
     constexpr int NG = CellTraits<CELL>::NG;
     constexpr int NCO = DENSE ? CellTraits<CELL>::NCO : 1;
     const int L = g.L, m = g.m, D = g.D;
-    const int c = blockIdx.x, b = blockIdx.y;
     const int t0 = c * L;
     const int Lc = min(L, g.Tw - t0);
     const int tid = threadIdx.x;
-    // the prepared weights are staged once per workgroup in LDS when they fit
-    const int nw = STAGE ? static_cast<int>(prepared_weight_floats(CELL, DP, m)) : 0;
-    float* WL = lds;
-    copy_to_lds<kThreads>(WL, g.w, nw);
     constexpr int NO = Gates<CELL, DP>::NO;
     const int mp = (m + 3) & ~3;
-    float* P = WL + ((nw + 3) & ~3);
+    float* P = arr;
     float* N = P + (L + 1) * DP;
     float* XI = N + (L + 1) * DP;            // [L][NO] input projections
     float* H = XI + L * NO;                  // [L][NO] recurrent pre-activations
@@ -276,7 +271,6 @@ __global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
     float* CO = V + L * DP;
     float* X = CO + NCO * L * DP;            // [L][mp]
     float* DL = X + L * mp;
-    const float* w = STAGE ? WL : g.w;
     const size_t ci = static_cast<size_t>(b) * g.NC + c;        // chunk index
     const float* s0 = g.s0 + b * g.s0s;
 
@@ -285,7 +279,6 @@ __global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
     copy_rows_to_lds<kThreads>(X, mp, xg, m, Lc, m);
     __syncthreads();
     input_projection<CELL, DP>(w, X, mp, Lc, m, XI);
-    uint32_t rb = 0;
     const size_t HS = static_cast<size_t>(g.B) * g.NC * D;
 
     if constexpr (PHASE == kPrologue) {
@@ -446,8 +439,22 @@ __global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
         for (int e = tid; e < D * D; e += kThreads) aA[e] = M0[(e / D) * DP + (e % D)];
         if (tid < D) g.aggB[ci * D + tid] = B0[tid];
     }
+}
+
+template <int CELL, int DP, bool DENSE, int PHASE, bool STAGE>
+__global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
+    if constexpr (PHASE != kPrologue) {
+        if (g.ctrl->stop) return;
+    }
+    extern __shared__ float lds[];
+    // the prepared weights are staged once per workgroup in LDS when they fit
+    const int nw = STAGE ? static_cast<int>(prepared_weight_floats(CELL, DP, g.m)) : 0;
+    copy_to_lds<kThreads>(lds, g.w, nw);
+    const float* w = STAGE ? lds : g.w;
+    uint32_t rb = 0;
+    cell_tile<CELL, DP, DENSE, PHASE>(g, blockIdx.x, blockIdx.y, lds + ((nw + 3) & ~3), w, rb);
     rb = block_max_u32(rb);
-    if (tid == 0) g.rpart[ci] = rb;
+    if (threadIdx.x == 0) g.rpart[static_cast<size_t>(blockIdx.y) * g.NC + blockIdx.x] = rb;
 }
 
 template <int CELL, int DP, bool DENSE, int PHASE, bool STAGE>
@@ -524,6 +531,261 @@ size_t cell_pass_lds_bytes(int kind, int DP, bool dense, int L, int m) {
 }
 
 int cell_pass_nblocks(const CellArgs& a) { return a.NC * a.B; }
+
+// ---------------------------------------------------------------- persistent solver
+// Grid-wide barrier over co-resident workgroups (cooperative launch): every
+// block adds one arrival to a monotonically increasing counter and waits for
+// epoch * nblocks arrivals.  Agent-scope fences before the arrival and after
+// the wait publish this block's writes and make the others' visible.  The
+// wait is bounded: on timeout, or when another block has timed out, the
+// block sets the error flag and returns false, and every block then leaves
+// the kernel, so a broken barrier cannot hang the device.
+__device__ __forceinline__ bool grid_sync(const PersistArgs& a, unsigned& epoch) {
+    __shared__ int ok;
+    __syncthreads();
+    ++epoch;
+    if (threadIdx.x == 0) {
+        ok = 1;
+        __threadfence();
+        atomicAdd(a.bar, 1u);
+        const unsigned target = epoch * gridDim.x;
+        unsigned spins = 0;
+        while (__hip_atomic_load(a.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(1);
+            if (__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
+                ++spins > (1u << 24)) {
+                atomicExch(a.err, 1u);
+                ok = 0;
+                break;
+            }
+        }
+        __threadfence();
+    }
+    __syncthreads();
+    return ok != 0;
+}
+
+// Carries of one batch row for the diagonal modes (same recurrence as
+// diag_carry_kernel): NSEG threads per channel compose contiguous runs of
+// chunk maps, the runs are combined through LDS, each thread replays its run.
+template <int DP>
+__device__ __forceinline__ void carry_row(const CellArgs& g, int b, float* segA, float* segB) {
+    constexpr int NSEG = kThreads / DP;
+    constexpr int kPerR = 16;
+    const int dl = threadIdx.x % DP, sg = threadIdx.x / DP;
+    const int NC = g.NC, D = g.D;
+    const int per = (NC + NSEG - 1) / NSEG;
+    const int c0 = min(NC, sg * per), c1 = min(NC, c0 + per);
+    const bool act = dl < D;
+    const size_t base = static_cast<size_t>(b) * NC * D + dl;
+    float A = 1.0f, Bc = 0.0f;
+    float ra[kPerR], rbv[kPerR];
+    const bool inreg = c1 - c0 <= kPerR;
+    if (act) {
+        if (inreg) {
+#pragma unroll
+            for (int k = 0; k < kPerR; ++k) {
+                const bool in = c0 + k < c1;
+                ra[k] = in ? g.aggA[base + static_cast<size_t>(c0 + k) * D] : 1.0f;
+                rbv[k] = in ? g.aggB[base + static_cast<size_t>(c0 + k) * D] : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < kPerR; ++k) {
+                Bc = ra[k] * Bc + rbv[k];
+                A = ra[k] * A;
+            }
+        } else {
+            for (int cc = c0; cc < c1; ++cc) {
+                const float ac = g.aggA[base + static_cast<size_t>(cc) * D];
+                const float bc = g.aggB[base + static_cast<size_t>(cc) * D];
+                Bc = ac * Bc + bc;
+                A = ac * A;
+            }
+        }
+    }
+    segA[sg * DP + dl] = A;
+    segB[sg * DP + dl] = Bc;
+    __syncthreads();
+    if (act) {
+        float y = g.s0[b * g.s0s + dl];
+        for (int k = 0; k < sg; ++k) y = segA[k * DP + dl] * y + segB[k * DP + dl];
+        float* cr = const_cast<float*>(g.carry);
+        if (inreg) {
+#pragma unroll
+            for (int k = 0; k < kPerR; ++k) {
+                if (c0 + k < c1) {
+                    cr[base + static_cast<size_t>(c0 + k) * D] = y;
+                    y = ra[k] * y + rbv[k];
+                }
+            }
+        } else {
+            for (int cc = c0; cc < c1; ++cc) {
+                cr[base + static_cast<size_t>(cc) * D] = y;
+                y = g.aggA[base + static_cast<size_t>(cc) * D] * y + g.aggB[base + static_cast<size_t>(cc) * D];
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// One launch for the whole solve: per window, the iteration-0 chunk maps,
+// then per iteration (identical stop decision in every block, from the same
+// residual partials) a carry phase and an apply phase, each followed by a
+// grid barrier.  The weights are staged in LDS once.
+template <int CELL, int DP>
+__global__ __launch_bounds__(kThreads) void cell_persist(PersistArgs a) {
+    extern __shared__ float lds[];
+    __shared__ float segA[kThreads], segB[kThreads];
+    CellArgs g = a.g;
+    const int nw = static_cast<int>(prepared_weight_floats(CELL, DP, g.m));
+    copy_to_lds<kThreads>(lds, g.w, nw);
+    const float* w = lds;
+    float* arr = lds + ((nw + 3) & ~3);
+    unsigned epoch = 0;
+    int hist_pos = 0;
+    const int B = g.B;
+    for (int wi = 0; wi < a.nwin; ++wi) {
+        const int64_t w0 = static_cast<int64_t>(wi) * a.W;
+        const int Tw = static_cast<int>(a.T - w0 < a.W ? a.T - w0 : a.W);
+        g.Tw = Tw;
+        g.NC = (Tw + g.L - 1) / g.L;
+        g.x = a.x0 + w0 * g.m;
+        g.s = a.s_base + w0 * g.D;
+        if (wi == 0) {
+            g.s0 = a.s0_user;
+            g.s0s = g.D;
+        } else {
+            g.s0 = a.s_base + (w0 - 1) * g.D;
+            g.s0s = a.T * g.D;
+        }
+        const int ntiles = B * g.NC;
+        for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+            uint32_t rb = 0;
+            cell_tile<CELL, DP, false, kPrologue>(g, t % g.NC, t / g.NC, arr, w, rb);
+            rb = block_max_u32(rb);
+            if (threadIdx.x == 0) g.rpart[t] = rb;
+        }
+        if (!grid_sync(a, epoch)) return;
+        int K = 0, status = -1;
+        for (int i = 0;; ++i) {
+            uint32_t mx = 0;
+            for (int k = threadIdx.x; k < ntiles; k += kThreads) mx = max(mx, g.rpart[k]);
+            mx = block_max_u32(mx);
+            int st = -1;
+            if (mx >= kNonFiniteBits) st = kStNonFinite;
+            else if (__uint_as_float(mx) <= a.tol) st = kStOk;
+            else if (i >= a.max_iter) st = kStNotConverged;
+            if (blockIdx.x == 0 && threadIdx.x == 0 && hist_pos < a.hist_cap) a.hist[hist_pos] = __uint_as_float(mx);
+            ++hist_pos;
+            if (st >= 0) {
+                K = i;
+                status = st;
+                break;
+            }
+            for (int bb = blockIdx.x; bb < B; bb += gridDim.x) carry_row<DP>(g, bb, segA, segB);
+            if (!grid_sync(a, epoch)) return;
+            g.iter = i;
+            for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+                uint32_t rb = 0;
+                if (i == 0) cell_tile<CELL, DP, false, kFirst>(g, t % g.NC, t / g.NC, arr, w, rb);
+                else cell_tile<CELL, DP, false, kSteady>(g, t % g.NC, t / g.NC, arr, w, rb);
+                rb = block_max_u32(rb);
+                if (threadIdx.x == 0) g.rpart[t] = rb;
+            }
+            if (!grid_sync(a, epoch)) return;
+        }
+        if (K == 0) {
+            // no update applied: the window's result is s0 repeated
+            for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+                const int c = t % g.NC, b = t / g.NC;
+                const int t0 = c * g.L, Lc = min(g.L, Tw - t0);
+                float* sg = g.s + b * g.ss + static_cast<int64_t>(t0) * g.D;
+                const float* s0 = g.s0 + b * g.s0s;
+                for (int e = threadIdx.x; e < Lc * g.D; e += kThreads) sg[e] = s0[e % g.D];
+            }
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            a.win_iters[wi] = K;
+            a.win_status[wi] = status;
+            *a.hist_len = hist_pos;
+        }
+        if (status == kStNonFinite) break;
+        if (!grid_sync(a, epoch)) return;
+    }
+}
+
+bool cell_persist_eligible(int kind, int DP, int L, int m) {
+    return cell_pass_stages_weights(kind, DP, false, L, m);
+}
+
+template <int CELL, int DP>
+static hipError_t persist_max_blocks_t(size_t lds, int* nb) {
+    int per_cu = 0, dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (lds > 64 * 1024) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(cell_persist<CELL, DP>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cell_persist<CELL, DP>, kThreads, lds);
+    if (e != hipSuccess) return e;
+    *nb = per_cu * ncu;
+    return hipSuccess;
+}
+
+static size_t persist_lds(int kind, int DP, int L, int m) {
+    return cell_pass_lds_bytes(kind, DP, false, L, m);
+}
+
+hipError_t cell_persist_max_blocks(int kind, int DP, int L, int m, int* nb) {
+    const size_t lds = persist_lds(kind, DP, L, m);
+    if (kind == kCellTanhRnn) {
+        switch (DP) {
+            case 4: return persist_max_blocks_t<kCellTanhRnn, 4>(lds, nb);
+            case 8: return persist_max_blocks_t<kCellTanhRnn, 8>(lds, nb);
+            case 16: return persist_max_blocks_t<kCellTanhRnn, 16>(lds, nb);
+            case 32: return persist_max_blocks_t<kCellTanhRnn, 32>(lds, nb);
+            default: return persist_max_blocks_t<kCellTanhRnn, 64>(lds, nb);
+        }
+    }
+    switch (DP) {
+        case 4: return persist_max_blocks_t<kCellGru, 4>(lds, nb);
+        case 8: return persist_max_blocks_t<kCellGru, 8>(lds, nb);
+        case 16: return persist_max_blocks_t<kCellGru, 16>(lds, nb);
+        case 32: return persist_max_blocks_t<kCellGru, 32>(lds, nb);
+        default: return persist_max_blocks_t<kCellGru, 64>(lds, nb);
+    }
+}
+
+template <int CELL, int DP>
+static hipError_t launch_persist_t(int nblocks, const PersistArgs& a, size_t lds, hipStream_t st) {
+    void* args[] = {const_cast<PersistArgs*>(&a)};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(cell_persist<CELL, DP>), dim3(nblocks),
+                                      dim3(kThreads), args, static_cast<unsigned>(lds), st);
+}
+
+hipError_t launch_cell_persist(int kind, int DP, int nblocks, const PersistArgs& a, hipStream_t st) {
+    const size_t lds = persist_lds(kind, DP, a.g.L, a.g.m);
+    if (kind == kCellTanhRnn) {
+        switch (DP) {
+            case 4: return launch_persist_t<kCellTanhRnn, 4>(nblocks, a, lds, st);
+            case 8: return launch_persist_t<kCellTanhRnn, 8>(nblocks, a, lds, st);
+            case 16: return launch_persist_t<kCellTanhRnn, 16>(nblocks, a, lds, st);
+            case 32: return launch_persist_t<kCellTanhRnn, 32>(nblocks, a, lds, st);
+            default: return launch_persist_t<kCellTanhRnn, 64>(nblocks, a, lds, st);
+        }
+    }
+    switch (DP) {
+        case 4: return launch_persist_t<kCellGru, 4>(nblocks, a, lds, st);
+        case 8: return launch_persist_t<kCellGru, 8>(nblocks, a, lds, st);
+        case 16: return launch_persist_t<kCellGru, 16>(nblocks, a, lds, st);
+        case 32: return launch_persist_t<kCellGru, 32>(nblocks, a, lds, st);
+        default: return launch_persist_t<kCellGru, 64>(nblocks, a, lds, st);
+    }
+}
 
 // ---------------------------------------------------------------- dense carry scan
 // carry[b][0] = s0[b]; carry[b][c+1] = M[b][c] carry[b][c] + bg[b][c].

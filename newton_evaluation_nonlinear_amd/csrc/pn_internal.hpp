@@ -118,6 +118,29 @@ bool dense_mfma_supported(int kind, int DP, int m);
 size_t dense_mfma_lds_bytes(int kind, int DP, int m);
 hipError_t launch_dense_mfma_pass(int kind, int DP, int phase, const CellArgs& a, hipStream_t st);
 
+// Persistent solver (matrix cells, diagonal modes): one cooperative launch runs
+// every window and iteration with grid-wide barriers between phases.
+struct PersistArgs {
+    CellArgs g;              // per-window fields are filled in by the kernel
+    const float* x0;         // x at t = 0
+    float* s_base;           // out at t = 0
+    const float* s0_user;    // s0 of the first window (batch stride D)
+    int64_t T;
+    int32_t W, nwin;
+    float tol;
+    int32_t max_iter;
+    unsigned* bar;           // grid barrier arrival counter (zeroed before launch)
+    unsigned* err;           // set when a barrier times out; every block then exits
+    int32_t* win_iters;      // [nwin] updates per window (-1 = not reached)
+    int32_t* win_status;     // [nwin]
+    float* hist;             // residual history r_0..r_K of each window, appended
+    int32_t hist_cap;
+    int32_t* hist_len;
+};
+bool cell_persist_eligible(int kind, int DP, int L, int m);
+hipError_t cell_persist_max_blocks(int kind, int DP, int L, int m, int* nblocks);
+hipError_t launch_cell_persist(int kind, int DP, int nblocks, const PersistArgs& a, hipStream_t st);
+
 // Standalone affine scan.
 struct ScanArgs {
     const float* A;          // diag [B][T][D] or dense [B][T][D][D]

@@ -12,7 +12,16 @@ import torch
 import oracle
 import workloads
 import newton_evaluation_nonlinear_amd as pn
-from _parity import run_gpu, run_oracle, check_parity, residual64
+from _parity import run_gpu, run_oracle, check_parity, residual64, to_dev
+
+
+def run_gpu_flags(wl, mode, flags):
+    params, x, s0 = to_dev(wl)
+    res = pn.eval(wl["cell"], params, x, s0, mode=mode, tol=wl["tol"], max_iter=wl["max_iter"],
+                  damping=wl["damping"], window=wl["window"], history=True, flags=flags)
+    torch.cuda.synchronize()
+    res.out_np = res.out.cpu().numpy()
+    return res
 
 pytestmark = pytest.mark.gpu
 
@@ -150,6 +159,22 @@ def test_matrix_cells_wide_input(kind):
               s0=np.zeros((B, D), dtype=np.float32))
     for mode in (N, Q):
         _parity(wl, mode)
+
+
+@pytest.mark.parametrize("cfg, B, T, mode", [(5, 2, 2500, Q), (2, 4, 300, Q), (2, 4, 300, J),
+                                            (2, 4, 300, P)])
+def test_persistent_and_multilaunch_paths_agree(cfg, B, T, mode):
+    # the one-launch cooperative solver and the launch-per-phase driver run the
+    # same tile arithmetic; both must meet the oracle bar and agree on counts
+    wl = _case(cfg, B=B, T=T)
+    a = run_gpu_flags(wl, mode, pn.FLAG_PERSISTENT)
+    b = run_gpu(wl, mode)
+    assert a.status == b.status and a.window_iters == b.window_iters
+    assert np.max(np.abs(a.out_np - b.out_np)) <= 1e-5
+    assert len(a.resid_hist) == len(b.resid_hist)
+    if mode != P:
+        ref = run_oracle(wl, mode)
+        check_parity(wl, mode, a, ref, label=_label(wl) + " persistent")
 
 
 # ---------------------------------------------------------------- the scan alone
