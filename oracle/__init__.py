@@ -20,17 +20,17 @@ Pins (what each function is checked against) live in
 
 from .cells import DiagTanh, TanhRNN, GRU, make_cell, CELL_DIAG_TANH, CELL_TANH_RNN, CELL_GRU
 from .solver import (
-    JACOBI, PICARD, QUASI_NEWTON, NEWTON,
+    JACOBI, PICARD, QUASI_NEWTON, NEWTON, BANDED,
     OK, NOT_CONVERGED, NONFINITE,
-    sequential, shift, residual_inf, jacobian_approx, affine_recurrence,
+    sequential, shift, residual_inf, band, jacobian_approx, affine_recurrence,
     newton_step, solve, SolveResult,
 )
 
 __all__ = [
     "DiagTanh", "TanhRNN", "GRU", "make_cell",
     "CELL_DIAG_TANH", "CELL_TANH_RNN", "CELL_GRU",
-    "JACOBI", "PICARD", "QUASI_NEWTON", "NEWTON",
+    "JACOBI", "PICARD", "QUASI_NEWTON", "NEWTON", "BANDED",
     "OK", "NOT_CONVERGED", "NONFINITE",
-    "sequential", "shift", "residual_inf", "jacobian_approx",
+    "sequential", "shift", "residual_inf", "band", "jacobian_approx",
     "affine_recurrence", "newton_step", "solve", "SolveResult",
 ]

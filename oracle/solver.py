@@ -16,7 +16,9 @@ solving J~ d = -F by forward substitution gives the update used here:
 
 with A~_t = 0 (Jacobi, J~ = I), A~_t = I (Picard, identity dynamics
 [PN §2.2.3]), A~_t = diag(A_t) (quasi-Newton, diagonal approximation
-[PN §2.2.1]) and A~_t = A_t (Newton).  The forward substitution is a
+[PN §2.2.1]), A~_t = band_k(A_t), the entries with |i - j| <= k (banded
+approximation for locally coupled systems [PN §2.2.2]), and A~_t = A_t
+(Newton).  The forward substitution is a
 first-order linear recurrence — the object a parallel scan evaluates
 [PN §2.1] — and here it is a deliberately sequential loop.
 
@@ -37,7 +39,7 @@ import numpy as np
 
 from .cells import make_cell
 
-JACOBI, PICARD, QUASI_NEWTON, NEWTON = 0, 1, 2, 3
+JACOBI, PICARD, QUASI_NEWTON, NEWTON, BANDED = 0, 1, 2, 3, 4
 OK, NOT_CONVERGED, NONFINITE = 0, 1, 2
 
 
@@ -68,8 +70,17 @@ def residual_inf(cell, x, s0, s):
     return float(np.max(np.abs(s - v)))
 
 
-def jacobian_approx(mode, cell, p, x):
-    """A~_t for every (b, t): [B, T, D] for the diagonal modes, [B, T, D, D] for Newton."""
+def band(J, k):
+    """Entries of J (..., D, D) with |i - j| <= k; the rest set to zero."""
+    D = J.shape[-1]
+    i = np.arange(D)
+    mask = np.abs(i[:, None] - i[None, :]) <= k
+    return np.where(mask, J, 0.0).astype(J.dtype)
+
+
+def jacobian_approx(mode, cell, p, x, bandwidth=1):
+    """A~_t for every (b, t): [B, T, D] for the diagonal modes, [B, T, D, D]
+    for Newton and the banded mode (half-bandwidth ``bandwidth``)."""
     if mode == JACOBI:
         return np.zeros(p.shape, dtype=cell.dtype)
     if mode == PICARD:
@@ -78,6 +89,8 @@ def jacobian_approx(mode, cell, p, x):
         return cell.jac_diag(p, x)
     if mode == NEWTON:
         return cell.jac(p, x)
+    if mode == BANDED:
+        return band(cell.jac(p, x), bandwidth)
     raise ValueError(f"unknown mode {mode}")
 
 
@@ -103,11 +116,11 @@ def affine_recurrence(v, p, A, s0):
     return out
 
 
-def newton_step(cell, x, s0, s, mode):
+def newton_step(cell, x, s0, s, mode, bandwidth=1):
     """One undamped update s -> s^ of the chosen method [PN §1.2]."""
     p = shift(s, s0)
     v = cell.f(p, x)
-    A = jacobian_approx(mode, cell, p, x)
+    A = jacobian_approx(mode, cell, p, x, bandwidth)
     return affine_recurrence(v, p, A, s0)
 
 
@@ -121,7 +134,7 @@ class SolveResult:
     hist: list = field(default_factory=list)           # per window: [r_0, ..., r_K]
 
 
-def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force):
+def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force, bandwidth):
     B, T = x.shape[0], x.shape[1]
     s = np.broadcast_to(np.asarray(s0, dtype=cell.dtype)[:, None, :], (B, T, cell.D)).copy()
     hist = []
@@ -141,7 +154,7 @@ def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force):
         elif i == force:
             status = NONFINITE if not np.isfinite(r) else (OK if r <= tol else NOT_CONVERGED)
             return s, i, status, hist
-        A = jacobian_approx(mode, cell, p, x)
+        A = jacobian_approx(mode, cell, p, x, bandwidth)
         s_hat = affine_recurrence(v, p, A, s0)
         if damping == 1.0:
             s = s_hat
@@ -151,7 +164,7 @@ def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force):
 
 
 def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
-          dtype=np.float64, force_iters=None):
+          dtype=np.float64, force_iters=None, bandwidth=1):
     """Parallel-in-time fixed-point solve, evaluated sequentially.
 
     kind/params follow the flat layout of ``make_cell``; x: [B, T, m];
@@ -159,7 +172,8 @@ def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
     windows of W steps in order (the last may be shorter).  ``force_iters``
     (one count per window) replaces the stop rule by a fixed number of
     updates; it is used to follow a run whose stopping decision landed inside
-    the floating-point ambiguity band of the tolerance.
+    the floating-point ambiguity band of the tolerance.  ``bandwidth`` is the
+    half-bandwidth k of the banded mode.
     """
     x = np.asarray(x)
     s0 = np.asarray(s0)
@@ -178,7 +192,7 @@ def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
         w1 = min(T, w0 + W)
         force = None if force_iters is None else int(force_iters[wi])
         s, K, st, hist = _solve_window(cell, xc[:, w0:w1], s_init, mode, tol, max_iter,
-                                       damping, force)
+                                       damping, force, bandwidth)
         out[:, w0:w1] = s
         res.iters += K
         res.window_iters.append(K)

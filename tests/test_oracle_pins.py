@@ -233,13 +233,13 @@ def test_picard_recurrence_is_a_cumulative_sum():
 
 # ---------------------------------------------------------------- the update itself
 
-def _dense_update(cell, x, s0, s, mode):
+def _dense_update(cell, x, s0, s, mode, bandwidth=1):
     """s - J~^{-1} F(s) with J~ assembled as a (T*D)x(T*D) matrix per batch row
     and solved by numpy.linalg.solve, straight from the update equation [PN §1.2]."""
     B, T, D = s.shape
     p = osv.shift(s, s0)
     F = s - cell.f(p, x)
-    A = osv.jacobian_approx(mode, cell, p, x)
+    A = osv.jacobian_approx(mode, cell, p, x, bandwidth)
     if A.ndim == 3:
         A = np.einsum("btd,de->btde", A, np.eye(D))
     out = np.empty_like(s)
@@ -267,10 +267,71 @@ def test_update_equals_linear_solve_of_the_stacked_system(kind, mode):
                                _dense_update(cell, x, s0, s, mode), rtol=0, atol=1e-11)
 
 
+@pytest.mark.parametrize("kind", [oracle.CELL_TANH_RNN, oracle.CELL_GRU])
+@pytest.mark.parametrize("k", [0, 1, 2])
+def test_banded_update_equals_linear_solve(kind, k):
+    D, m, B, T = 5, 3, 2, 8
+    rng = np.random.default_rng(50 + kind * 3 + k)
+    params = workloads.random_cell_params(kind, D, m, rng, 1.5).astype(np.float64)
+    cell = oracle.make_cell(kind, params, D, m)
+    x = rng.standard_normal((B, T, m))
+    s0 = rng.standard_normal((B, D)) * 0.3
+    s = rng.standard_normal((B, T, D)) * 0.5
+    np.testing.assert_allclose(oracle.newton_step(cell, x, s0, s, oracle.BANDED, k),
+                               _dense_update(cell, x, s0, s, oracle.BANDED, k), rtol=0, atol=1e-11)
+
+
+def test_band_limits_reduce_to_quasi_newton_and_newton():
+    # [PN §2.2.2] sits between the diagonal approximation and the full Jacobian
+    D, m, B, T = 6, 3, 2, 30
+    rng = np.random.default_rng(60)
+    params = workloads.random_cell_params(oracle.CELL_GRU, D, m, rng, 2.0).astype(np.float64)
+    cell = oracle.make_cell(oracle.CELL_GRU, params, D, m)
+    x = rng.standard_normal((B, T, m))
+    s0 = np.zeros((B, D))
+    s = rng.standard_normal((B, T, D)) * 0.4
+    np.testing.assert_array_equal(oracle.newton_step(cell, x, s0, s, oracle.BANDED, 0),
+                                  oracle.newton_step(cell, x, s0, s, oracle.QUASI_NEWTON))
+    np.testing.assert_array_equal(oracle.newton_step(cell, x, s0, s, oracle.BANDED, D - 1),
+                                  oracle.newton_step(cell, x, s0, s, oracle.NEWTON))
+    J = rng.standard_normal((3, D, D))
+    Bk = oracle.band(J, 1)
+    for i in range(D):
+        for j in range(D):
+            assert Bk[0, i, j] == (J[0, i, j] if abs(i - j) <= 1 else 0.0)
+    # more band, fewer updates (on this locally coupled example)
+    its = [oracle.solve(oracle.CELL_GRU, params, x, s0, oracle.BANDED, 1e-9, T, bandwidth=k).iters
+           for k in (0, 2, D - 1)]
+    assert its[0] >= its[1] >= its[2]
+
+
+def test_banded_is_exact_newton_on_a_banded_lattice():
+    # A tanh RNN whose W couples only units within distance k has a Jacobian
+    # diag(c) W inside the band, so the banded update is the Newton update and
+    # converges as fast.
+    D, m, B, T, k = 7, 2, 2, 40, 2
+    rng = np.random.default_rng(70)
+    i = np.arange(D)
+    W = np.where(np.abs(i[:, None] - i[None, :]) <= k, rng.standard_normal((D, D)), 0.0) * 0.4
+    U = rng.standard_normal((D, m))
+    params = np.concatenate([W.ravel(), U.ravel(), np.zeros(D)])
+    cell = oracle.make_cell(oracle.CELL_TANH_RNN, params, D, m)
+    x = rng.standard_normal((B, T, m))
+    s0 = np.zeros((B, D))
+    s = rng.standard_normal((B, T, D)) * 0.3
+    np.testing.assert_array_equal(oracle.newton_step(cell, x, s0, s, oracle.BANDED, k),
+                                  oracle.newton_step(cell, x, s0, s, oracle.NEWTON))
+    nb = oracle.solve(oracle.CELL_TANH_RNN, params, x, s0, oracle.BANDED, 1e-10, T, bandwidth=k)
+    nn = oracle.solve(oracle.CELL_TANH_RNN, params, x, s0, oracle.NEWTON, 1e-10, T)
+    assert nb.iters == nn.iters
+    np.testing.assert_allclose(nb.s, oracle.sequential(cell, x, s0), rtol=0, atol=1e-10)
+
+
 # ---------------------------------------------------------------- invariants from [PN §3.1]
 
 @pytest.mark.parametrize("kind", [oracle.CELL_TANH_RNN, oracle.CELL_GRU, oracle.CELL_DIAG_TANH])
-@pytest.mark.parametrize("mode", [oracle.JACOBI, oracle.PICARD, oracle.QUASI_NEWTON, oracle.NEWTON])
+@pytest.mark.parametrize("mode", [oracle.JACOBI, oracle.PICARD, oracle.QUASI_NEWTON, oracle.NEWTON,
+                                  oracle.BANDED])
 def test_causality_prefix_exact_and_T_step_convergence(kind, mode):
     # After i undamped updates the first i states equal the sequential ones,
     # so every method has converged after at most T updates.
