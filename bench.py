@@ -28,12 +28,19 @@ sys.path.insert(0, ROOT)
 METRIC = "converged state-updates/s (B*T*D) per Newton solve; achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 FP32_PEAK_TFLOPS = 157.3
-MODES = {"jacobi": 0, "picard": 1, "qn": 2, "quasi_newton": 2, "newton": 3}
+MODES = {"jacobi": 0, "picard": 1, "qn": 2, "quasi_newton": 2, "newton": 3, "banded": 4}
 KERNEL_SOURCES = {  # source file of the dominant kernel per cell kind
     0: "newton_evaluation_nonlinear_amd/csrc/pn_diag.hip",
     1: "newton_evaluation_nonlinear_amd/csrc/pn_cell.hip",
     2: "newton_evaluation_nonlinear_amd/csrc/pn_cell.hip",
 }
+
+
+def _kernel_source(wl, mode):
+    if wl["cell"] != 0 and 8 < wl["D"] <= 32 and (
+            mode == 3 or (mode == 4 and 0 < wl["bandwidth"] < wl["D"] - 1)):
+        return "newton_evaluation_nonlinear_amd/csrc/pn_dense.hip"   # dense modes on the matrix cores
+    return KERNEL_SOURCES[wl["cell"]]
 
 
 def _src_hash(path):
@@ -62,7 +69,7 @@ def cpu_baseline(cfg, mode):
     import workloads
 
     samples = {3: dict(B=8, T=32768), 2: dict(B=16, T=2048), 4: dict(B=8, T=4096),
-               1: dict(B=None, T=None), 5: dict(B=4, T=4096)}
+               1: dict(B=None, T=None), 5: dict(B=4, T=4096), 6: dict(B=8, T=4096)}
     sm = samples.get(cfg, dict(B=1, T=4096))
     if cfg == 2 and mode == 1:
         # float64 Picard on this GRU needs ~T updates (it converges only
@@ -72,7 +79,7 @@ def cpu_baseline(cfg, mode):
     with threadpool_limits(1):
         t0 = time.perf_counter()
         r = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], mode, wl["tol"],
-                         wl["max_iter"], wl["damping"], wl["window"])
+                         wl["max_iter"], wl["damping"], wl["window"], bandwidth=wl["bandwidth"])
         el = time.perf_counter() - t0
     n = wl["B"] * wl["T"] * wl["D"]
     return {"value": n / el, "unit": "state-updates/s", "cores": 1, "kind": "oracle",
@@ -101,6 +108,17 @@ def _read_counters(d, counter):
     return out
 
 
+def _steady_apply(kernel_name):
+    """True for a steady-state apply launch (phase template argument 2)."""
+    import re
+    m = re.search(r"\b(diag_tanh_pass|cell_pass|dense_pass)<([^>]*)>", kernel_name)
+    if not m:
+        return False
+    targs = [a.strip() for a in m.group(2).split(",")]
+    pos = {"diag_tanh_pass": 1, "cell_pass": 3, "dense_pass": 2}[m.group(1)]
+    return len(targs) > pos and targs[pos] == "2"
+
+
 def summarize_pmc(args, fetch_dir, write_dir):
     """Per-launch HBM bytes of the dominant kernel from two counter runs.
 
@@ -118,17 +136,14 @@ def summarize_pmc(args, fetch_dir, write_dir):
         if not copies:
             raise SystemExit(f"no copy-probe dispatch found in {d}")
         scale = COPY_PROBE_BYTES / (max(copies) * 1024.0)
-        steady = [v for n, v in rows.values()
-                  if ("diag_tanh_pass<" in n and ", 2>" in n) or ("cell_pass<" in n and ", 2>" in n)]
+        steady = [v for n, v in rows.values() if _steady_apply(n)]
         if not steady:
             raise SystemExit(f"no steady apply dispatch found in {d}")
         per = sum(steady) / len(steady) * 1024.0
         res[label] = dict(counter=counter, copy_probe_kib=max(copies), scale=scale,
                           launches=len(steady), raw_bytes_per_launch=per,
                           bytes_per_launch=per * scale)
-    src = KERNEL_SOURCES[wl["cell"]]
-    if wl["cell"] != 0 and mode == 3 and 8 < wl["D"] <= 32:
-        src = "newton_evaluation_nonlinear_amd/csrc/pn_dense.hip"   # Newton on the matrix cores
+    src = _kernel_source(wl, mode)
     bargs = f"--config {args.config}" + (f" --mode {args.mode}" if args.mode else "")
     cmds = [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- "
             f"python3 bench.py {bargs} --steps 2 --warmup 0 --no-cpu --copy-probe",
@@ -179,13 +194,14 @@ def main():
     params, x, s0 = (torch.from_numpy(wl[k]).to(dev) for k in ("params", "x", "s0"))
     out = torch.empty((wl["B"], wl["T"], wl["D"]), dtype=torch.float32, device=dev)
     nbytes = pn.workspace_bytes(wl["cell"], wl["m"], wl["B"], wl["T"], wl["D"], mode,
-                                wl["damping"], wl["window"], args.chunk)
+                                wl["damping"], wl["window"], args.chunk, wl["bandwidth"])
     ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
 
     def solve(profile):
         return pn.eval(wl["cell"], params, x, s0, mode=mode, tol=wl["tol"],
                        max_iter=wl["max_iter"], damping=wl["damping"], window=wl["window"],
-                       chunk=args.chunk, out=out, workspace=ws, profile=profile)
+                       chunk=args.chunk, out=out, workspace=ws, profile=profile,
+                       bandwidth=wl["bandwidth"])
 
     if args.copy_probe:
         n = 64 * 1024 * 1024
@@ -215,14 +231,16 @@ def main():
     bytes_per_launch = apply_bytes / max(apply_launches, 1)
     gbs = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9 if avg_launch_ms > 0 else 0.0
     name = f"{wl['name']}_{workloads.MODE_NAMES[mode]}"
-    src = KERNEL_SOURCES[wl["cell"]]
-    if wl["cell"] != 0 and mode == 3 and 8 < wl["D"] <= 32:
-        src = "newton_evaluation_nonlinear_amd/csrc/pn_dense.hip"   # Newton on the matrix cores
+    src = _kernel_source(wl, mode)
     # bound by arithmetic intensity of the kernel against the FP32 ridge point
     flops_per_launch = apply_flops / max(apply_launches, 1)
     if flops_per_launch > bytes_per_launch * (FP32_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9):
         tf = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": tf, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+        # the dense modes outside the matrix-core kernel compose on the vector
+        # ALUs (FP32 vector and matrix peaks are both 157.3 TFLOP/s on MI355X)
+        dense = mode == 3 or (mode == 4 and 0 < wl["bandwidth"] < wl["D"] - 1)
+        unit = "alu" if dense and src == KERNEL_SOURCES[wl["cell"]] else "mfma"
+        roof = {"bound": unit, "achieved": tf, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": tf / FP32_PEAK_TFLOPS, "traffic": _traffic(name, src, bytes_per_launch)}
     else:
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -238,6 +256,7 @@ def main():
         "config": {"workload": name, "cell": wl["cell"], "B": wl["B"], "T": wl["T"],
                    "D": wl["D"], "m": wl["m"], "mode": workloads.MODE_NAMES[mode],
                    "tol": wl["tol"], "damping": wl["damping"], "window": wl["window"],
+                   **({"bandwidth": wl["bandwidth"]} if mode == 4 else {}),
                    "iters": last.iters, "window_iters_first": last.window_iters[:4],
                    "status": last.status, "parallelism": "single GPU"},
         "roofline": roof,

@@ -12,6 +12,8 @@
  *     Jacobi        A~_t = 0                      [PN §1.2]
  *     Picard        A~_t = I                      [PN §1.2, §2.2.3]
  *     quasi-Newton  A~_t = diag(df_t/ds_{t-1})    [PN §2.2.1]
+ *     banded        A~_t = band_k(df_t/ds_{t-1})  [PN §2.2.2]
+ *                   (entries with |i - j| <= k kept, the rest zero)
  *     Newton        A~_t = df_t/ds_{t-1} (dense)  [PN §1.2]
  * Applying J~^{-1} is the first-order linear recurrence
  *     s^_t = v_t + A~_t (s^_{t-1} - p_t),  p_t = s_{t-1},  v_t = f_t(p_t),
@@ -61,8 +63,12 @@ extern "C" {
  * The RNN cell is the application the article names [PN §1.3.2]. */
 enum { PN_CELL_DIAG_TANH = 0, PN_CELL_TANH_RNN = 1, PN_CELL_GRU = 2 };
 
-/* Jacobian approximations (see above).  Every cell supports every mode. */
-enum { PN_JACOBI = 0, PN_PICARD = 1, PN_QUASI_NEWTON = 2, PN_NEWTON = 3 };
+/* Jacobian approximations (see above).  Every cell supports every mode.
+ * PN_BANDED takes its half-bandwidth k from pn_opts.bandwidth; band_0 is the
+ * diagonal and band_{D-1} the whole matrix, so k = 0 runs as PN_QUASI_NEWTON
+ * and k >= D-1 as PN_NEWTON (for the channel-wise cell every k runs as
+ * PN_QUASI_NEWTON: its Jacobian is diagonal). */
+enum { PN_JACOBI = 0, PN_PICARD = 1, PN_QUASI_NEWTON = 2, PN_NEWTON = 3, PN_BANDED = 4 };
 
 /* Status codes. */
 enum {
@@ -92,9 +98,11 @@ typedef struct pn_profile {
     int32_t apply_launches;   /* launches, including early-exit ones          */
     double apply_bytes;       /* summed algorithmic bytes of those launches   */
     double apply_flops;       /* summed algorithmic flops: matrix-cell
-                                 evaluations and, for Newton, the D x D
-                                 chunk-map compose (0 for the channel-wise
-                                 cell)                                        */
+                                 evaluations and, for Newton and the banded
+                                 mode, the chunk-map compose with A~_t (a
+                                 band of 2k+1 diagonals costs that fraction
+                                 of the dense product; 0 for the
+                                 channel-wise cell)                           */
     double total_ms;          /* first launch to last completion              */
 } pn_profile;
 
@@ -113,6 +121,7 @@ typedef struct pn_opts {
     int64_t window_iters_len;
     pn_profile* profile;      /* host; NULL = no event timing                   */
     int32_t flags;            /* PN_FLAG_* bits, 0 = defaults                    */
+    int32_t bandwidth;        /* PN_BANDED half-bandwidth k >= 0 (default 1)    */
 } pn_opts;
 
 /* pn_opts.flags.  PN_FLAG_PERSISTENT runs a solve of a matrix cell in a
@@ -124,15 +133,16 @@ typedef struct pn_opts {
  * the faster one for the shapes measured here. */
 enum { PN_FLAG_PERSISTENT = 1 };
 
-/* Fill *o with the defaults: damping 1, chunk 0, window 0, everything else
- * NULL / 0. */
+/* Fill *o with the defaults: damping 1, chunk 0, window 0, bandwidth 1,
+ * everything else NULL / 0. */
 void pn_opts_init(pn_opts* o);
 
 /* Solve the recurrence for all B sequences [PN §1.1, §1.2].
  *   cell      host struct, read during the call only.
  *   params    device, float32, layout per cell kind (above).
  *   x         device [B, T, m];  s0 device [B, D].
- *   mode      PN_JACOBI .. PN_NEWTON.
+ *   mode      PN_JACOBI .. PN_BANDED (PN_BANDED needs opts->bandwidth >= 0;
+ *             pn_eval without options uses k = 1).
  *   tol       stop when r <= tol (tol >= 0; 0 runs to max_iter unless r == 0).
  *   max_iter  cap on updates per window (>= 0).
  *   out       device [B, T, D].  iters_out host int32: total updates applied

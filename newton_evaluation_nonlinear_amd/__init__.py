@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpn.so")
 
 CELL_DIAG_TANH, CELL_TANH_RNN, CELL_GRU = 0, 1, 2
-JACOBI, PICARD, QUASI_NEWTON, NEWTON = 0, 1, 2, 3
+JACOBI, PICARD, QUASI_NEWTON, NEWTON, BANDED = 0, 1, 2, 3, 4
 OK, NOT_CONVERGED, NONFINITE = 0, 1, 2
 EINVAL, EUNSUPPORTED, EHIP, EWORKSPACE = -1, -2, -3, -4
 FLAG_PERSISTENT = 1
@@ -52,7 +52,7 @@ class Opts(ctypes.Structure):
                 ("window_iters", ctypes.POINTER(ctypes.c_int32)),
                 ("window_iters_len", ctypes.c_int64),
                 ("profile", ctypes.POINTER(Profile)),
-                ("flags", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("bandwidth", ctypes.c_int32)]
 
 
 _lib = None
@@ -110,7 +110,7 @@ def _stream_ptr(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def make_opts(damping=1.0, window=0, chunk=0, stream=None, flags=0):
+def make_opts(damping=1.0, window=0, chunk=0, stream=None, flags=0, bandwidth=1):
     o = Opts()
     lib().pn_opts_init(ctypes.byref(o))
     o.damping = float(damping)
@@ -118,11 +118,13 @@ def make_opts(damping=1.0, window=0, chunk=0, stream=None, flags=0):
     o.chunk = int(chunk)
     o.stream = stream
     o.flags = int(flags)
+    o.bandwidth = int(bandwidth)
     return o
 
 
-def workspace_bytes(cell_kind, input_dim, B, T, D, mode, damping=1.0, window=0, chunk=0):
-    o = make_opts(damping, window, chunk)
+def workspace_bytes(cell_kind, input_dim, B, T, D, mode, damping=1.0, window=0, chunk=0,
+                    bandwidth=1):
+    o = make_opts(damping, window, chunk, bandwidth=bandwidth)
     c = Cell(cell_kind, input_dim)
     n = lib().pn_workspace_bytes(ctypes.byref(c), B, T, D, mode, ctypes.byref(o))
     if n == 0:
@@ -142,10 +144,12 @@ class Result:
 
 
 def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, damping=1.0,
-         window=0, chunk=0, out=None, history=False, profile=False, workspace=None, flags=0):
+         window=0, chunk=0, out=None, history=False, profile=False, workspace=None, flags=0,
+         bandwidth=1):
     """Solve s_t = f(s_{t-1}, x_t) for t = 1..T over the batch; see include/pn.h.
 
     params, x [B,T,m], s0 [B,D] are float32 tensors on one HIP device.
+    ``bandwidth`` is the half-bandwidth k of the BANDED mode.
     Returns a ``Result`` (unpacks as ``out, iters, status``).  Negative
     library statuses raise ``PnError``.
     """
@@ -160,7 +164,7 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     if out is None:
         out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
     c = Cell(int(cell_kind), int(m))
-    o = make_opts(damping, window or 0, chunk, _stream_ptr(dev), flags)
+    o = make_opts(damping, window or 0, chunk, _stream_ptr(dev), flags, bandwidth)
     nbytes = lib().pn_workspace_bytes(ctypes.byref(c), B, T, D, int(mode), ctypes.byref(o))
     if nbytes == 0:
         raise PnError(EINVAL, last_error())

@@ -61,6 +61,7 @@ int next_pow2(int v) {
 // ---------------------------------------------------------------- planning
 struct Plan {
     int kind, mode, D, m, B;
+    int band;              // half-bandwidth of A~_t in the dense modes (Newton: D)
     int64_t T, W;          // horizon, window length
     int L, NC;             // chunk length, chunks of a full window
     int DP, cpb;           // padded D (matrix cells), channels per block (diag cell)
@@ -74,16 +75,24 @@ struct Plan {
 int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int32_t mode,
               const pn_opts* o) {
     p.kind = cell->kind;
-    p.mode = mode;
     p.D = static_cast<int>(D);
     p.m = cell->input_dim;
+    p.matrix_cell = p.kind != PN_CELL_DIAG_TANH;
+    // band_0(A) = diag(A) and band_{D-1}(A) = A; a diagonal Jacobian is its
+    // own band
+    const int k = o ? o->bandwidth : 1;
+    if (mode == PN_BANDED) {
+        if (!p.matrix_cell || k == 0) mode = PN_QUASI_NEWTON;
+        else if (k >= p.D - 1) mode = PN_NEWTON;
+    }
+    p.mode = mode;
+    p.band = mode == PN_BANDED ? k : p.D;
     p.B = static_cast<int>(B);
     p.T = T;
     const int64_t window = o ? o->window : 0;
     p.W = (window <= 0 || window > T) ? T : window;
     const int chunk = o ? o->chunk : 0;
-    p.matrix_cell = p.kind != PN_CELL_DIAG_TANH;
-    p.dense = p.matrix_cell && mode == PN_NEWTON;
+    p.dense = p.matrix_cell && (mode == PN_NEWTON || mode == PN_BANDED);
     p.mfma = false;
     if (!p.matrix_cell) {
         p.cpb = std::min(256, ((p.D + 63) / 64) * 64);
@@ -172,7 +181,8 @@ int validate(const pn_cell* cell, const float* params, const float* x, const flo
                                              (long long)B, (long long)T, (long long)D);
     if (cell->kind < PN_CELL_DIAG_TANH || cell->kind > PN_CELL_GRU)
         return fail(PN_EINVAL, "unknown cell kind %d", cell->kind);
-    if (mode < PN_JACOBI || mode > PN_NEWTON) return fail(PN_EINVAL, "unknown mode %d", mode);
+    if (mode < PN_JACOBI || mode > PN_BANDED) return fail(PN_EINVAL, "unknown mode %d", mode);
+    if (mode == PN_BANDED && o && o->bandwidth < 0) return fail(PN_EINVAL, "bandwidth must be >= 0");
     if (cell->input_dim < 1) return fail(PN_EINVAL, "input_dim must be >= 1");
     if (cell->kind == PN_CELL_DIAG_TANH && cell->input_dim != D && D > 0)
         return fail(PN_EINVAL, "diag-tanh cell needs input_dim == D");
@@ -293,11 +303,17 @@ double apply_flops(const Plan& p, int Tw) {
     // algorithmic flops of one apply launch per (b, t): two cell evaluations
     // (recurrent products 2*NG*D^2 each) and one input projection (2*NG*D*m);
     // Newton adds one D x D chunk-map compose (2 D^3) and two matrix-vector
-    // chains through the Jacobian (2*NG*D^2 each)
+    // chains through the Jacobian (2*NG*D^2 each); the banded mode does the
+    // same with nz (mean entries per row of the band) in place of one D
     if (!p.matrix_cell) return 0.0;
     const double D = p.D, m = p.m, NG = p.kind == PN_CELL_GRU ? 3.0 : 1.0;
     double per = 2.0 * (2.0 * NG * D * D) + 2.0 * NG * D * m;
-    if (p.dense) per += 2.0 * D * D * D + 2.0 * (2.0 * NG * D * D);
+    if (p.dense) {
+        double nz = 0.0;
+        for (int i = 0; i < p.D; ++i) nz += std::min(p.D - 1, i + p.band) - std::max(0, i - p.band) + 1;
+        nz /= D;
+        per += 2.0 * D * D * nz + 2.0 * (2.0 * NG * D * nz);
+    }
     return static_cast<double>(p.B) * Tw * per;
 }
 
@@ -337,6 +353,7 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
         ca.B = p.B; ca.Tw = Tw; ca.D = p.D; ca.m = p.m; ca.L = p.L; ca.NC = NC;
         ca.aggA = aggA; ca.aggB = aggB; ca.carry = carry; ca.halo = halo; ca.rpart = rpart;
         ca.ctrl = ctrl; ca.mode = p.mode; ca.lam = c.lam; ca.undamped = c.lam == 1.0f;
+        ca.band = p.band;
         nblocks = cell_pass_nblocks(ca);
     }
     auto launch_pass = [&](int phase, int iter) -> hipError_t {
@@ -590,6 +607,7 @@ void pn_opts_init(pn_opts* o) {
     if (!o) return;
     std::memset(o, 0, sizeof(*o));
     o->damping = 1.0f;
+    o->bandwidth = 1;
 }
 
 int pn_eval_ex(const pn_cell* cell, const float* params, const float* x, const float* s0, int64_t B,

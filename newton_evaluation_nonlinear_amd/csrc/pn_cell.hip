@@ -15,8 +15,14 @@
 //     so only D-vectors of coefficients per step are kept; the diagonal
 //     modes use the diagonal of A_t (quasi-Newton [PN §2.2.1]), 1 (Picard) or
 //     0 (Jacobi), and Newton uses A_t itself;
-//   * for Newton the chunk map is (prod A_t, folded offset), a D x D matrix
-//     chain [PN §2.1], and the replay is a matrix-vector chain.
+//   * the banded mode [PN §2.2.2] keeps the entries |i - k| <= band of A_t.
+//     Row scaling keeps a band in place, so band(A_t) is the same sum with
+//     every W restricted to the band: each product below only runs over the
+//     2 band + 1 columns k of row i (Newton is band >= D);
+//   * for Newton and the banded mode the chunk map is (prod A~_t, folded
+//     offset), a D x D matrix chain [PN §2.1] (a product of banded factors
+//     fills in, so the map itself is kept dense), and the replay is a
+//     matrix-vector chain.
 // The input projection U x_t (+ bias) does not depend on the iterate and is
 // computed once per sweep.  D is padded to DP (a power of two <= 64) inside
 // LDS; padded rows/columns are kept at zero.
@@ -227,15 +233,16 @@ __device__ __forceinline__ void eval_rows(const float* __restrict__ w, const flo
     }
 }
 
-// (A_t y)[i] for the dense Jacobian, with y in LDS; row i only.
+// (A~_t y)[i] for the dense or banded Jacobian, with y in LDS; row i only.
 template <int CELL, int DP>
 __device__ __forceinline__ float jac_row_apply(const float* __restrict__ w, const float* CO, int o,
-                                               int L, int i, int D, const float* y) {
+                                               int L, int i, int D, int band, const float* y) {
     constexpr int NG = CellTraits<CELL>::NG;
     float acc[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) acc[g] = 0.0f;
-    for (int k = 0; k < D; ++k) {
+    const int k1 = min(D, i + band + 1);
+    for (int k = max(0, i - band); k < k1; ++k) {
         const float yk = y[k];
 #pragma unroll
         for (int g = 0; g < NG; ++g) acc[g] += w[(g * DP + k) * DP + i] * yk;
@@ -339,7 +346,7 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
                 if (tid < D) DL[tid] = shat - P[o];
                 __syncthreads();
                 if (tid < D) {
-                    shat = V[o] + jac_row_apply<CELL, DP>(w, CO, o, L, tid, D, DL);
+                    shat = V[o] + jac_row_apply<CELL, DP>(w, CO, o, L, tid, D, g.band, DL);
                     if (j == Lc - 1 && has_next) shat = cr[D + tid];
                     const float so = P[o + DP];
                     N[o + DP] = und ? shat : so + lam * (shat - so);
@@ -372,13 +379,16 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
             g.aggB[ci * D + tid] = Bc;
         }
     } else {
-        // chunk map y -> M y + bg, built step by step: M <- A_j M, bg <- A_j (bg - p_j) + v_j
+        // chunk map y -> M y + bg, built step by step: M <- A~_j M, bg <- A~_j (bg - p_j) + v_j.
+        // M rows are padded to MS = DP + 1 floats: in the banded mode the
+        // lanes of a wave read M at rows k that follow their own row i.
+        constexpr int MS = DP + 1;
         float* M0 = DL + DP;
-        float* M1 = M0 + DP * DP;
-        float* B0 = M1 + DP * DP;
+        float* M1 = M0 + DP * MS;
+        float* B0 = M1 + DP * MS;
         float* B1 = B0 + DP;
-        for (int e = tid; e < DP * DP; e += kThreads) {
-            const int i = e / DP, k = e % DP;
+        for (int e = tid; e < DP * MS; e += kThreads) {
+            const int i = e / MS, k = e % MS;
             M0[e] = (i == k && i < D) ? 1.0f : 0.0f;
             M1[e] = 0.0f;
         }
@@ -390,6 +400,7 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
         constexpr int NCG = kThreads / DP;
         const int i = tid % DP;
         const int cg = tid / DP;
+        const int k0 = max(0, i - g.band), k1 = min(D, i + g.band + 1);
         for (int j = 0; j < Lc; ++j) {
             const int o = j * DP + i;
             if (i < D) {
@@ -397,8 +408,8 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
                     float acc[NG];
 #pragma unroll
                     for (int q = 0; q < NG; ++q) acc[q] = 0.0f;
-                    for (int k = 0; k < D; ++k) {
-                        const float mk = M0[k * DP + col];
+                    for (int k = k0; k < k1; ++k) {
+                        const float mk = M0[k * MS + col];
 #pragma unroll
                         for (int q = 0; q < NG; ++q) acc[q] += w[(q * DP + k) * DP + i] * mk;
                     }
@@ -406,17 +417,17 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
                     if constexpr (CELL == kCellTanhRnn) {
                         val = CO[o] * acc[0];
                     } else {
-                        val = CO[o] * M0[i * DP + col] + CO[L * DP + o] * acc[1] +
+                        val = CO[o] * M0[i * MS + col] + CO[L * DP + o] * acc[1] +
                               CO[2 * L * DP + o] * acc[2] + CO[3 * L * DP + o] * acc[0];
                     }
-                    M1[i * DP + col] = val;
+                    M1[i * MS + col] = val;
                 }
                 if (cg == 0) {
-                    // offset: A_j (bg - p_j) + v_j, p_j = N[j]
+                    // offset: A~_j (bg - p_j) + v_j, p_j = N[j]
                     float acc[NG];
 #pragma unroll
                     for (int q = 0; q < NG; ++q) acc[q] = 0.0f;
-                    for (int k = 0; k < D; ++k) {
+                    for (int k = k0; k < k1; ++k) {
                         const float yk = B0[k] - N[j * DP + k];
 #pragma unroll
                         for (int q = 0; q < NG; ++q) acc[q] += w[(q * DP + k) * DP + i] * yk;
@@ -436,7 +447,7 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
             t = B0; B0 = B1; B1 = t;
         }
         float* aA = g.aggA + ci * D * D;
-        for (int e = tid; e < D * D; e += kThreads) aA[e] = M0[(e / D) * DP + (e % D)];
+        for (int e = tid; e < D * D; e += kThreads) aA[e] = M0[(e / D) * MS + (e % D)];
         if (tid < D) g.aggB[ci * D + tid] = B0[tid];
     }
 }
@@ -512,7 +523,7 @@ static size_t cell_pass_array_floats(int kind, int DP, bool dense, int L, int m)
     const size_t mp = (m + 3) & ~3;
     size_t f = 2ull * (L + 1) * DP + 2ull * L * NO + static_cast<size_t>(L) * DP + NCO * L * DP +
                static_cast<size_t>(L) * mp + DP;
-    if (dense) f += 2ull * DP * DP + 2ull * DP;
+    if (dense) f += 2ull * DP * (DP + 1) + 2ull * DP;
     return f;
 }
 

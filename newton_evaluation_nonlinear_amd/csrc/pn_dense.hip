@@ -12,6 +12,11 @@
 //          M <- A_t M,   bg <- A_t (bg - p_t) + v_t
 //      [the affine-map composition of PN §2.1] with A_t = diag(z) +
 //      sum_g diag(c_g) W_g (tanh RNN: A_t = diag(1 - v^2) W).
+// The banded mode [PN §2.2.2] replaces A_t by its band |i - k| <= band, which
+// is the same sum over the band-restricted W_g (row scaling keeps the band):
+// the lane's weights for the Jacobian products are masked once at start, the
+// cell itself keeps the full weights.  The chunk map of banded factors fills
+// in, so it stays a dense DP x DP product.
 // W_g M is a DP x DP x DP product done as MFMA k-steps: the accumulator of
 // one step holds M in the instruction's output layout, whose rows per lane
 // group are exactly the k indices that lane group supplies as the B operand
@@ -164,7 +169,7 @@ __device__ __forceinline__ float jac_apply_row(const float (&wr)[DTraits<CELL>::
     }
 }
 
-template <int CELL, int DP, int PHASE>
+template <int CELL, int DP, int PHASE, bool BANDED>
 __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
     if constexpr (PHASE != kPrologue) {
         if (g.ctrl->stop) return;
@@ -205,6 +210,13 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
     for (int gt = 0; gt < NG; ++gt)
 #pragma unroll
         for (int s = 0; s < KS; ++s) wr[gt][s] = w[(gt * DP + Tl::krow(h, s)) * DP + i];
+    // weights of the Jacobian products: wr itself, or its band
+    float wj[NG][KS];
+#pragma unroll
+    for (int gt = 0; gt < NG; ++gt)
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            wj[gt][s] = (!BANDED || abs(Tl::krow(h, s) - i) <= g.band) ? wr[gt][s] : 0.0f;
     copy_to_lds<64>(UT, wUT, NG * m * DP);
     const float bias_i[3] = {wbi[i], NG > 1 ? wbi[DP + i] : 0.0f, NG > 2 ? wbi[2 * DP + i] : 0.0f};
     float bhh_l[3] = {0.0f, 0.0f, 0.0f};
@@ -289,7 +301,7 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
                 float co[NCO];
 #pragma unroll
                 for (int q = 0; q < NCO; ++q) co[q] = CO[(q * kSub + j) * DP + i];
-                const float ad = jac_apply_row<CELL, DP>(wr, YV, h, co, di);
+                const float ad = jac_apply_row<CELL, DP>(wj, YV, h, co, di);
                 shat = V[j * DP + i] + ad;
                 if (j0 + j == Lc - 1 && has_next && live) shat = cr[D + i];
                 const float so = P[(j + 1) * DP + i];
@@ -328,7 +340,7 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
 #pragma unroll
                 for (int r = 0; r < KS; ++r) C[gt][r] = 0.0f;
 #pragma unroll
-                for (int s = 0; s < KS; ++s) C[gt] = Tl::step(wr[gt][s], M[s], C[gt]);
+                for (int s = 0; s < KS; ++s) C[gt] = Tl::step(wj[gt][s], M[s], C[gt]);
             }
             // offset: bg <- A_j (bg - p_j) + v_j  (p_j = N[j])
             const float dbi = live ? bg - N[j * DP + i] : 0.0f;
@@ -338,7 +350,7 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
                 float co[NCO];
 #pragma unroll
                 for (int q = 0; q < NCO; ++q) co[q] = CO[(q * kSub + j) * DP + i];
-                bg = V[j * DP + i] + jac_apply_row<CELL, DP>(wr, YV + DP, h, co, dbi);
+                bg = V[j * DP + i] + jac_apply_row<CELL, DP>(wj, YV + DP, h, co, dbi);
             }
             // row scalings of the lane's accumulator rows
             float rs[NCO][KS];
@@ -388,14 +400,21 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
     if (lane == 0) g.rpart[ci] = rb;
 }
 
-template <int CELL, int DP>
-static hipError_t launch_dense_phase(int phase, const CellArgs& a, hipStream_t st) {
+template <int CELL, int DP, bool BANDED>
+static hipError_t launch_dense_phase_b(int phase, const CellArgs& a, hipStream_t st) {
     const size_t lds = DLds<CELL, DP>::floats(a.m) * sizeof(float);
     const dim3 grid(a.NC, a.B);
-    if (phase == kPrologue) dense_pass<CELL, DP, kPrologue><<<grid, 64, lds, st>>>(a);
-    else if (phase == kFirst) dense_pass<CELL, DP, kFirst><<<grid, 64, lds, st>>>(a);
-    else dense_pass<CELL, DP, kSteady><<<grid, 64, lds, st>>>(a);
+    if (phase == kPrologue) dense_pass<CELL, DP, kPrologue, BANDED><<<grid, 64, lds, st>>>(a);
+    else if (phase == kFirst) dense_pass<CELL, DP, kFirst, BANDED><<<grid, 64, lds, st>>>(a);
+    else dense_pass<CELL, DP, kSteady, BANDED><<<grid, 64, lds, st>>>(a);
     return hipGetLastError();
+}
+
+// band < D - 1 selects the masked Jacobian weights; Newton passes band = D.
+template <int CELL, int DP>
+static hipError_t launch_dense_phase(int phase, const CellArgs& a, hipStream_t st) {
+    return a.band < a.D - 1 ? launch_dense_phase_b<CELL, DP, true>(phase, a, st)
+                            : launch_dense_phase_b<CELL, DP, false>(phase, a, st);
 }
 
 bool dense_mfma_supported(int kind, int DP, int m) {

@@ -82,6 +82,7 @@ struct CellArgs {
     const Ctrl* ctrl;
     int32_t mode, iter, undamped;
     float lam;
+    int32_t band;            // Jacobian half-bandwidth (dense modes; Newton: D)
 };
 
 struct CarryArgs {

@@ -48,7 +48,8 @@ def run_gpu(wl, mode, tol=None, max_iter=None, damping=None, window=None, chunk=
                   max_iter=wl["max_iter"] if max_iter is None else max_iter,
                   damping=wl["damping"] if damping is None else damping,
                   window=wl["window"] if window is None else window,
-                  chunk=chunk, history=history, profile=profile)
+                  chunk=chunk, history=history, profile=profile,
+                  bandwidth=wl.get("bandwidth", 1))
     torch.cuda.synchronize()
     res.out_np = res.out.cpu().numpy()
     return res
@@ -59,7 +60,8 @@ def run_oracle(wl, mode, tol=None, max_iter=None, damping=None, window=None, dty
     args = dict(tol=wl["tol"] if tol is None else tol,
                 max_iter=wl["max_iter"] if max_iter is None else max_iter,
                 damping=wl["damping"] if damping is None else damping,
-                window=wl["window"] if window is None else window)
+                window=wl["window"] if window is None else window,
+                bandwidth=wl.get("bandwidth", 1))
     ck = None
     if key is not None and force_iters is None:
         ck = (key, mode, dtype, tuple(sorted(args.items())))
@@ -67,7 +69,7 @@ def run_oracle(wl, mode, tol=None, max_iter=None, damping=None, window=None, dty
             return _oracle_cache[ck]
     r = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], mode, args["tol"],
                      args["max_iter"], args["damping"], args["window"], dtype=dtype,
-                     force_iters=force_iters)
+                     force_iters=force_iters, bandwidth=args["bandwidth"])
     if ck is not None:
         _oracle_cache[ck] = r
     return r

@@ -50,6 +50,7 @@ def _eval_raw(kind=pn.CELL_TANH_RNN, m=3, B=2, T=5, D=4, mode=pn.NEWTON, tol=1e-
     (dict(T=-3), pn.EINVAL),
     (dict(D=-2), pn.EINVAL),
     (dict(mode=7), pn.EINVAL),
+    (dict(mode=5), pn.EINVAL),
     (dict(kind=9), pn.EINVAL),
     (dict(m=0), pn.EINVAL),
     (dict(tol=float("nan")), pn.EINVAL),
@@ -84,6 +85,17 @@ def test_invalid_options():
     o.resid_hist_len = 4            # length without a buffer
     rc, _ = _eval_raw(opts=o)
     assert rc == pn.EINVAL
+    o = pn.make_opts(bandwidth=-1)  # the banded mode needs k >= 0
+    rc, _ = _eval_raw(mode=pn.BANDED, opts=o)
+    assert rc == pn.EINVAL and "bandwidth" in pn.last_error()
+    rc, _ = _eval_raw(mode=pn.NEWTON, opts=o)   # ignored by the other modes
+    assert rc != pn.EINVAL or "bandwidth" not in pn.last_error()
+
+
+def test_options_defaults():
+    o = pn.make_opts()
+    assert o.damping == 1.0 and o.chunk == 0 and o.window == 0 and o.flags == 0
+    assert o.bandwidth == 1
 
 
 def test_empty_problems_succeed_without_work():
@@ -101,6 +113,14 @@ def test_workspace_bytes_is_host_only_and_monotone():
     nn = pn.workspace_bytes(pn.CELL_GRU, 8, 64, 2048, 16, pn.NEWTON)
     assert nn > nq > 0          # dense chunk maps hold D x D per chunk
     assert pn.lib().pn_workspace_bytes(ctypes.byref(g), 1, 10, 65, pn.NEWTON, None) == 0
+    # the banded mode keeps dense chunk maps, except where it reduces to the
+    # diagonal (k = 0) or the full Jacobian (k >= D - 1)
+    nb = pn.workspace_bytes(pn.CELL_GRU, 8, 64, 2048, 16, pn.BANDED, bandwidth=2)
+    nb0 = pn.workspace_bytes(pn.CELL_GRU, 8, 64, 2048, 16, pn.BANDED, bandwidth=0)
+    nbf = pn.workspace_bytes(pn.CELL_GRU, 8, 64, 2048, 16, pn.BANDED, bandwidth=40)
+    assert nb == nn and nb0 == nq and nbf == nn
+    assert pn.workspace_bytes(pn.CELL_DIAG_TANH, 256, 8, 4096, 256, pn.BANDED, bandwidth=3) == \
+        pn.workspace_bytes(pn.CELL_DIAG_TANH, 256, 8, 4096, 256, pn.QUASI_NEWTON)
     # a window bounds the workspace
     nw = pn.workspace_bytes(pn.CELL_GRU, 32, 4, 32768, 64, pn.QUASI_NEWTON, window=1024)
     nf = pn.workspace_bytes(pn.CELL_GRU, 32, 4, 32768, 64, pn.QUASI_NEWTON)

@@ -148,6 +148,63 @@ def test_matrix_cells_other_widths(kind, D):
         _parity(wl, mode)
 
 
+@pytest.mark.parametrize("k", [1, 2, 3])
+@pytest.mark.parametrize("D", [5, 12, 20, 33, 64])
+@pytest.mark.parametrize("kind", [pn.CELL_TANH_RNN, pn.CELL_GRU])
+def test_banded_matches_oracle(kind, D, k):
+    # widths on both dense paths: the matrix cores (D padded to 16 / 32) and
+    # the LDS kernel (D padded to 8 / 64); a ragged last chunk.  Locally
+    # coupled weights (band 2 plus a weak dense part): k = 1 cuts into the
+    # coupling, k = 2 holds it, k = 3 holds more.
+    rng = np.random.default_rng(300 + D + 7 * k)
+    m, B, T = 3, 2, 150
+    params = workloads.lattice_cell_params(kind, D, m, rng)
+    wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-6, damping=1.0, window=0,
+              max_iter=T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32), bandwidth=k)
+    _parity(wl, pn.BANDED)
+
+
+@pytest.mark.parametrize("kind", [pn.CELL_TANH_RNN, pn.CELL_GRU])
+@pytest.mark.parametrize("D", [12, 33])
+def test_banded_limits_run_as_quasi_newton_and_newton(kind, D):
+    # band_0 is the diagonal and band_{D-1} the whole Jacobian: the library
+    # runs those as the quasi-Newton and Newton solves, bit for bit
+    rng = np.random.default_rng(400 + D)
+    m, B, T = 4, 2, 200
+    params = workloads.random_cell_params(kind, D, m, rng, 1.2)
+    wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-6, damping=1.0, window=0,
+              max_iter=T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=np.zeros((B, D), dtype=np.float32))
+    q = run_gpu(wl, Q)
+    n = run_gpu(wl, N)
+    for k, same in [(0, q), (D - 1, n), (D + 9, n)]:
+        wl["bandwidth"] = k
+        b = run_gpu(wl, pn.BANDED)
+        assert b.iters == same.iters and b.status == same.status
+        np.testing.assert_array_equal(b.out_np, same.out_np)
+
+
+def test_banded_on_the_channel_wise_cell_is_quasi_newton():
+    wl = _case(3, B=2, T=1000)
+    q = run_gpu(wl, Q)
+    wl["bandwidth"] = 5
+    b = run_gpu(wl, pn.BANDED)
+    assert b.iters == q.iters
+    np.testing.assert_array_equal(b.out_np, q.out_np)
+    _parity(wl, pn.BANDED)
+
+
+@pytest.mark.parametrize("mode", [pn.BANDED, Q, N])
+def test_cfg6_lattice_small(mode):
+    wl = _case(6, B=2, T=700)
+    ref = _parity(wl, mode)
+    if mode == pn.BANDED:
+        # the band holds the lattice coupling: far fewer updates than the diagonal
+        qn = run_oracle(wl, Q)
+        assert ref.iters * 2 <= qn.iters
+
+
 @pytest.mark.parametrize("kind", [pn.CELL_TANH_RNN, pn.CELL_GRU])
 def test_matrix_cells_wide_input(kind):
     # weights too large to stage in LDS: the kernels read them from global memory
@@ -156,8 +213,8 @@ def test_matrix_cells_wide_input(kind):
     params = workloads.random_cell_params(kind, D, m, rng, 1.0)
     wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-5, damping=1.0, window=0,
               max_iter=T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
-              s0=np.zeros((B, D), dtype=np.float32))
-    for mode in (N, Q):
+              s0=np.zeros((B, D), dtype=np.float32), bandwidth=3)
+    for mode in (N, Q, pn.BANDED):
         _parity(wl, mode)
 
 
@@ -269,6 +326,12 @@ def test_cfg2_full_picard_outcome():
 @pytest.mark.slow
 def test_cfg4_full_newton():
     _parity(_case(4), N)
+
+
+@pytest.mark.slow
+def test_cfg6_full_banded():
+    wl = _case(6)
+    _parity(wl, pn.BANDED)
 
 
 @pytest.mark.slow

@@ -27,8 +27,9 @@ import os
 import numpy as np
 
 CELL_DIAG_TANH, CELL_TANH_RNN, CELL_GRU = 0, 1, 2
-JACOBI, PICARD, QUASI_NEWTON, NEWTON = 0, 1, 2, 3
-MODE_NAMES = {JACOBI: "jacobi", PICARD: "picard", QUASI_NEWTON: "quasi_newton", NEWTON: "newton"}
+JACOBI, PICARD, QUASI_NEWTON, NEWTON, BANDED = 0, 1, 2, 3, 4
+MODE_NAMES = {JACOBI: "jacobi", PICARD: "picard", QUASI_NEWTON: "quasi_newton", NEWTON: "newton",
+              BANDED: "banded"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -46,6 +47,13 @@ CONFIGS = {
             modes=(NEWTON,), tol=1e-5, damping=1.0, window=0, rho=0.9),
     5: dict(name="gru_d64_near_critical", cell=CELL_GRU, B=4, T=32768, D=64, m=32,
             modes=(QUASI_NEWTON,), tol=1e-5, damping=0.5, window=1024),
+    # A locally coupled system, the case the banded Jacobian approximation is
+    # meant for [PN §2.2.2]: a tanh RNN on a ring-free 1-D lattice whose
+    # recurrent matrix couples each unit to its neighbours within distance
+    # ``lattice_band``, plus a weak dense coupling of relative size ``eps``.
+    6: dict(name="lattice_tanh_d64", cell=CELL_TANH_RNN, B=16, T=4096, D=64, m=16,
+            modes=(BANDED, QUASI_NEWTON, NEWTON), tol=1e-5, damping=1.0, window=0, rho=0.9,
+            lattice_band=2, eps=0.05, bandwidth=2),
 }
 
 
@@ -76,14 +84,25 @@ def make(cfg, B=None, T=None, scale=None):
     """Return a dict with the float32 arrays and settings of workload ``cfg``.
 
     Keys: cfg, name, cell, D, m, B, T, params (flat float32), x [B,T,m],
-    s0 [B,D] (zeros), modes, tol, damping, window, max_iter.
+    s0 [B,D] (zeros), modes, tol, damping, window, max_iter, bandwidth (the
+    half-bandwidth the banded mode runs with; 1 where unset).
     """
     c = dict(CONFIGS[cfg])
     B = c["B"] if B is None else int(B)
     T = c["T"] if T is None else int(T)
     D, m = c["D"], c["m"]
     rng = np.random.Generator(np.random.PCG64(cfg))
-    if c["cell"] == CELL_TANH_RNN:
+    if c["cell"] == CELL_TANH_RNN and "lattice_band" in c:
+        i = np.arange(D)
+        near = np.abs(i[:, None] - i[None, :]) <= c["lattice_band"]
+        S = np.where(near, rng.standard_normal((D, D)), 0.0)
+        R = rng.standard_normal((D, D)) / np.sqrt(D)
+        W = _rescale_spectral_radius(S + c["eps"] * R, c["rho"])
+        U = rng.standard_normal((D, m)) / np.sqrt(m)
+        b = np.zeros(D)
+        x = rng.standard_normal((B, T, m))
+        params = np.concatenate([W.ravel(), U.ravel(), b])
+    elif c["cell"] == CELL_TANH_RNN:
         W = _rescale_spectral_radius(rng.standard_normal((D, D)), c["rho"])
         U = rng.standard_normal((D, m))
         b = np.zeros(D)
@@ -113,7 +132,32 @@ def make(cfg, B=None, T=None, scale=None):
              s0=np.zeros((B, D), dtype=np.float32))
     W = c["window"] if c["window"] else T
     c["max_iter"] = int(W)
+    c.setdefault("bandwidth", 1)
     return c
+
+
+def lattice_cell_params(kind, D, m, rng, band=2, eps=0.05, rho=0.9):
+    """Locally coupled recurrent weights for tests (float32, flat C layout):
+    every recurrent matrix couples units within distance ``band``, plus a
+    dense part of relative size ``eps``.  tanh RNN: W rescaled to spectral
+    radius ``rho``; GRU: each W_hh gate block rescaled likewise."""
+    i = np.arange(D)
+    near = np.abs(i[:, None] - i[None, :]) <= band
+
+    def lattice():
+        S = np.where(near, rng.standard_normal((D, D)), 0.0)
+        return _rescale_spectral_radius(S + eps * rng.standard_normal((D, D)) / np.sqrt(D), rho)
+
+    if kind == CELL_TANH_RNN:
+        W = lattice()
+        U = rng.standard_normal((D, m)) / np.sqrt(m)
+        b = rng.standard_normal(D) * 0.1
+        return np.concatenate([W.ravel(), U.ravel(), b]).astype(np.float32)
+    if kind == CELL_GRU:
+        W_ih, _, b_ih, b_hh = _gru_weights(rng, D, m)
+        W_hh = np.concatenate([lattice() for _ in range(3)], axis=0)
+        return np.concatenate([W_ih.ravel(), W_hh.ravel(), b_ih, b_hh]).astype(np.float32)
+    raise ValueError(kind)
 
 
 def random_cell_params(kind, D, m, rng, scale=1.0):
