@@ -18,19 +18,20 @@ Pins (what each function is checked against) live in
 ``tests/test_oracle_pins.py``; every public function here has at least one.
 """
 
-from .cells import DiagTanh, TanhRNN, GRU, make_cell, CELL_DIAG_TANH, CELL_TANH_RNN, CELL_GRU
+from .cells import (DiagTanh, TanhRNN, GRU, EulerTanh, make_cell, CELL_DIAG_TANH, CELL_TANH_RNN,
+                    CELL_GRU, CELL_EULER_TANH)
 from .solver import (
     JACOBI, PICARD, QUASI_NEWTON, NEWTON, BANDED,
     OK, NOT_CONVERGED, NONFINITE,
     sequential, shift, residual_inf, band, jacobian_approx, affine_recurrence,
-    newton_step, solve, SolveResult,
+    newton_step, solve, solve_advancing, SolveResult,
 )
 
 __all__ = [
-    "DiagTanh", "TanhRNN", "GRU", "make_cell",
-    "CELL_DIAG_TANH", "CELL_TANH_RNN", "CELL_GRU",
+    "DiagTanh", "TanhRNN", "GRU", "EulerTanh", "make_cell",
+    "CELL_DIAG_TANH", "CELL_TANH_RNN", "CELL_GRU", "CELL_EULER_TANH",
     "JACOBI", "PICARD", "QUASI_NEWTON", "NEWTON", "BANDED",
     "OK", "NOT_CONVERGED", "NONFINITE",
     "sequential", "shift", "residual_inf", "band", "jacobian_approx",
-    "affine_recurrence", "newton_step", "solve", "SolveResult",
+    "affine_recurrence", "newton_step", "solve", "solve_advancing", "SolveResult",
 ]

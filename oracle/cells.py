@@ -11,6 +11,11 @@ applications section [PN §1.3.2] names RNNs.  Three concrete cells are used:
 * ``GRU``       the gated recurrent unit in the convention of torch.nn.GRU,
   gate order (r, z, n), with the hidden bias of the candidate inside the reset
   product (params: W_ih[3D,m] | W_hh[3D,D] | b_ih[3D] | b_hh[3D]).
+* ``EulerTanh`` f(p, x) = p + h * (tanh(W p + U x + b) - p): one explicit
+  Euler step, per-channel step sizes h, of the continuous-time RNN
+  ds/dt = -s + tanh(W s + U x(t) + b).  For small h the dynamics Jacobian is
+  close to the identity, the regime of Picard's identity approximation
+  [PN §1.3.1, §2.2.3] (params: W[D,D] | U[D,m] | b[D] | h[D]).
 
 Every method is vectorised over any leading axes: ``p`` has shape [..., D] and
 ``x`` shape [..., m].  Jacobians are with respect to the previous state p,
@@ -26,6 +31,7 @@ import numpy as np
 CELL_DIAG_TANH = 0
 CELL_TANH_RNN = 1
 CELL_GRU = 2
+CELL_EULER_TANH = 3
 
 
 def _sigmoid(u):
@@ -156,6 +162,37 @@ class GRU:
                 + cr * np.diagonal(self.W_hr))
 
 
+class EulerTanh:
+    """s_t = s_{t-1} + h * (tanh(W s_{t-1} + U x_t + b) - s_{t-1})."""
+
+    kind = CELL_EULER_TANH
+
+    def __init__(self, W, U, b, h, dtype=np.float64):
+        self.W = np.asarray(W, dtype=dtype)
+        self.U = np.asarray(U, dtype=dtype)
+        self.b = np.asarray(b, dtype=dtype)
+        self.h = np.asarray(h, dtype=dtype)
+        self.D = self.W.shape[0]
+        self.m = self.U.shape[1]
+        self.dtype = dtype
+
+    def _g(self, p, x):
+        return np.tanh(p @ self.W.T + x @ self.U.T + self.b)
+
+    def f(self, p, x):
+        return p + self.h * (self._g(p, x) - p)
+
+    def jac(self, p, x):
+        # A[i, k] = (1 - h_i) [i == k] + h_i (1 - g_i^2) W[i, k]
+        g = self._g(p, x)
+        return (_diag_embed(np.broadcast_to(1.0 - self.h, g.shape))
+                + (self.h * (1.0 - g * g))[..., :, None] * self.W)
+
+    def jac_diag(self, p, x):
+        g = self._g(p, x)
+        return 1.0 - self.h + self.h * (1.0 - g * g) * np.diagonal(self.W)
+
+
 def make_cell(kind, params, D, m, dtype=np.float64):
     """Build a cell from the flat parameter vector of the C interface.
 
@@ -163,6 +200,7 @@ def make_cell(kind, params, D, m, dtype=np.float64):
       diag-tanh: a[D]                                   (m must equal D)
       tanh RNN : W[D*D] | U[D*m] | b[D]
       GRU      : W_ih[3D*m] | W_hh[3D*D] | b_ih[3D] | b_hh[3D]
+      Euler    : W[D*D] | U[D*m] | b[D] | h[D]
     """
     w = np.asarray(params, dtype=np.float64).ravel()
     if kind == CELL_DIAG_TANH:
@@ -187,4 +225,12 @@ def make_cell(kind, params, D, m, dtype=np.float64):
         b_ih = w[n_ih + n_hh:n_ih + n_hh + 3 * D]
         b_hh = w[n_ih + n_hh + 3 * D:]
         return GRU(W_ih, W_hh, b_ih, b_hh, dtype)
+    if kind == CELL_EULER_TANH:
+        if w.size != D * D + D * m + 2 * D:
+            raise ValueError("Euler params must hold D*D + D*m + 2D values")
+        W = w[:D * D].reshape(D, D)
+        U = w[D * D:D * D + D * m].reshape(D, m)
+        b = w[D * D + D * m:D * D + D * m + D]
+        h = w[D * D + D * m + D:]
+        return EulerTanh(W, U, b, h, dtype)
     raise ValueError(f"unknown cell kind {kind}")

@@ -30,7 +30,12 @@ Readings where the article is silent (documented alongside the build):
   * damping is step damping, s <- s + lam (s^ - s) [PN §4.3, §5.3];
   * windows are consecutive, non-overlapping blocks of W steps, each solved
     from its own initial state, which is the last state of the previous
-    window [PN §1.3.1, §2.3].
+    window [PN §1.3.1, §2.3];
+  * the advancing window (``solve_advancing``) is the sliding window of
+    [PN §1.3.1] read as: a window of W steps starts at the first step not yet
+    accepted; after each check the leading steps of the window whose residual
+    is <= tol are accepted and the window slides past them, taking in new
+    steps that start from the last state of the current iterate.
 """
 
 from dataclasses import dataclass, field
@@ -209,4 +214,70 @@ def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
         wi += 1
         if T == 0:
             break
+    return res
+
+
+def solve_advancing(cell, x, s0, mode, tol, max_iter, W, damping=1.0, bandwidth=1):
+    """Advancing-window solve: the window slides past its converged prefix.
+
+    ``cell`` is a cell object (``make_cell``); x: [B, T, m]; s0: [B, D].
+    Steps [0, a) are accepted and never change again; the window is [a, e),
+    e = min(T, a + W).  Each round:
+      1. check: r_t = max over (b, d) of |s_t - f_t(s_{t-1})| for t in [a, e)
+         at the current iterate (s_{a-1} accepted, or s0); r = max_t r_t is
+         the round's residual.  Non-finite r stops with NONFINITE;
+      2. accept: a moves to the first t with r_t > tol (to e if none); a = T
+         stops with OK; after max_iter updates the solve stops with
+         NOT_CONVERGED;
+      3. slide: e = min(T, a + W); steps that enter the window start from the
+         last state of the current iterate;
+      4. update the window [a, e) once with the chosen method [PN §1.2], from
+         the accepted state s_{a-1}, with step damping.
+    The count is the number of updates; ``window_iters`` = [count].  On
+    exit, steps the window never reached hold its last state.
+    """
+    x = np.asarray(x, dtype=cell.dtype)
+    s0 = np.asarray(s0, dtype=cell.dtype)
+    B, T = x.shape[0], x.shape[1]
+    D = cell.D
+    W = T if W <= 0 else int(W)
+    s = np.full((B, T, D), np.nan, dtype=cell.dtype)
+    a, e = 0, min(T, W)
+    s[:, :e] = s0[:, None, :]
+    hist = []
+    i = 0
+    res = SolveResult(s, 0, OK)
+    while T > 0:
+        prev = s0 if a == 0 else s[:, a - 1]
+        win = s[:, a:e]
+        v = cell.f(shift(win, prev), x[:, a:e])
+        r_t = np.max(np.abs(win - v), axis=(0, 2))
+        r = float(np.max(r_t))
+        hist.append(r)
+        if not np.isfinite(r):
+            res.status = NONFINITE
+            break
+        bad = np.nonzero(~(r_t <= tol))[0]
+        a = a + int(bad[0]) if bad.size else e
+        if a >= T:
+            break
+        if i == max_iter:
+            res.status = NOT_CONVERGED
+            break
+        e_new = min(T, a + W)
+        s[:, e:e_new] = s[:, e - 1:e]
+        e = e_new
+        prev = s0 if a == 0 else s[:, a - 1]
+        win = s[:, a:e]
+        s_hat = newton_step(cell, x[:, a:e], prev, win, mode, bandwidth)
+        s[:, a:e] = s_hat if damping == 1.0 else win + damping * (s_hat - win)
+        i += 1
+    if T == 0:
+        hist.append(0.0)
+    elif e < T:
+        s[:, e:] = s[:, e - 1:e]      # steps never reached: the window's last state
+    res.iters = i
+    res.window_iters = [i]
+    res.window_status = [res.status]
+    res.hist = [hist]
     return res

@@ -152,6 +152,52 @@ def test_tanh_rnn_jacobian_matches_autograd():
                                rtol=0, atol=1e-13)
 
 
+def test_euler_cell_jacobian_matches_autograd_and_fd():
+    D, m, B = 6, 3, 4
+    rng = np.random.default_rng(15)
+    params = workloads.random_cell_params(oracle.CELL_EULER_TANH, D, m, rng, 1.5).astype(np.float64)
+    cell = oracle.make_cell(oracle.CELL_EULER_TANH, params, D, m)
+    p = rng.standard_normal((B, D))
+    x = rng.standard_normal((B, m))
+    W, U, b, h = (torch.from_numpy(a) for a in (cell.W, cell.U, cell.b, cell.h))
+
+    def step(pb, xb):   # one explicit Euler step of ds/dt = -s + tanh(W s + U x + b)
+        return pb + h * (torch.tanh(W @ pb + U @ xb + b) - pb)
+
+    ref = np.stack([torch.autograd.functional.jacobian(
+        lambda q: step(q, torch.from_numpy(x[i])), torch.from_numpy(p[i])).numpy() for i in range(B)])
+    np.testing.assert_allclose(cell.jac(p, x), ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(cell.jac_diag(p, x), np.diagonal(ref, axis1=-2, axis2=-1),
+                               rtol=0, atol=1e-13)
+    np.testing.assert_allclose(cell.f(p, x),
+                               np.stack([step(torch.from_numpy(p[i]), torch.from_numpy(x[i])).numpy()
+                                         for i in range(B)]), rtol=0, atol=1e-14)
+    eps = 1e-6
+    for k in range(D):
+        e = np.zeros(D)
+        e[k] = eps
+        fd = (cell.f(p + e, x) - cell.f(p - e, x)) / (2 * eps)
+        np.testing.assert_allclose(cell.jac(p, x)[..., k], fd, rtol=0, atol=1e-8)
+
+
+def test_euler_cell_sequential_leaky_integrator_closed_form():
+    # W = 0 and a constant input: s_t = g + (1 - h)^t (s_0 - g), g = tanh(U x + b)
+    D, m, B, T = 4, 2, 2, 50
+    rng = np.random.default_rng(16)
+    U = rng.standard_normal((D, m))
+    b = rng.standard_normal(D) * 0.3
+    h = rng.uniform(0.01, 0.2, D)
+    params = np.concatenate([np.zeros(D * D), U.ravel(), b, h])
+    cell = oracle.make_cell(oracle.CELL_EULER_TANH, params, D, m)
+    xc = rng.standard_normal((B, m))
+    x = np.broadcast_to(xc[:, None], (B, T, m)).copy()
+    s0 = rng.standard_normal((B, D))
+    g = np.tanh(xc @ U.T + b)
+    t = np.arange(1, T + 1)[None, :, None]
+    ref = g[:, None] + (1.0 - h) ** t * (s0 - g)[:, None]
+    np.testing.assert_allclose(oracle.sequential(cell, x, s0), ref, rtol=0, atol=1e-13)
+
+
 def test_diag_tanh_jacobian_fd():
     D, B = 9, 3
     rng = np.random.default_rng(6)
@@ -463,6 +509,86 @@ def test_windows_chain_and_full_window_is_identical():
     cell = oracle.make_cell(wl["cell"], wl["params"], wl["D"], wl["m"])
     assert oracle.residual_inf(cell, wl["x"].astype(np.float64), wl["s0"].astype(np.float64),
                                win.s) <= 1e-7
+
+
+# ---------------------------------------------------------------- advancing window [PN §1.3.1]
+
+class _Affine:
+    """f_t(p) = A p + x_t (m = D)."""
+    dtype = np.float64
+
+    def __init__(self, A):
+        self.A, self.D, self.m = A, A.shape[0], A.shape[0]
+
+    def f(self, p, x):
+        return p @ self.A.T + x
+
+    def jac(self, p, x):
+        return np.broadcast_to(self.A, p.shape + (self.D,)).copy()
+
+    def jac_diag(self, p, x):
+        return np.broadcast_to(np.diagonal(self.A), p.shape).copy()
+
+
+def test_advancing_window_hand_traced_jacobi_case():
+    # f_t(p) = p/2 + 1, s0 = 0, T = 3, W = 2, tol = 0, traced by hand:
+    #   round 0: window [0,2) = (0, 0), r_t = (1, 1), nothing accepted; Jacobi -> (1, 1)
+    #   round 1: r = (0, 0.5): accept t=0; window [1,3), new step 2 starts at 1;
+    #            update from s_0 = 1 -> (1.5, 1.5)
+    #   round 2: r = (0, 0.25): accept t=1; window [2,3); update from 1.5 -> 1.75
+    #   round 3: r = (0,): accept t=2 -> done after 3 updates
+    cell = _Affine(np.array([[0.5]]))
+    x = np.ones((1, 3, 1))
+    r = oracle.solve_advancing(cell, x, np.zeros((1, 1)), oracle.JACOBI, 0.0, 100, 2)
+    assert r.status == oracle.OK and r.iters == 3 and r.window_iters == [3]
+    np.testing.assert_array_equal(r.s[0, :, 0], [1.0, 1.5, 1.75])
+    np.testing.assert_array_equal(r.hist[0], [1.0, 0.5, 0.25, 0.0])
+
+
+@pytest.mark.parametrize("T, W", [(10, 3), (12, 4), (7, 7), (5, 9)])
+def test_advancing_window_exact_methods_take_one_update_per_window(T, W):
+    # Newton on affine maps and Picard on s + c_t solve a whole window per
+    # update, so the window jumps by W every round: ceil(T / W) updates.
+    rng = np.random.default_rng(17)
+    D = 3
+    x = rng.standard_normal((2, T, D))
+    s0 = rng.standard_normal((2, D))
+    for cell, mode in ((_Affine(rng.standard_normal((D, D)) * 0.5), oracle.NEWTON),
+                       (_Affine(np.eye(D)), oracle.PICARD)):
+        r = oracle.solve_advancing(cell, x, s0, mode, 1e-10, 100, W)
+        assert r.status == oracle.OK and r.iters == -(-T // W), (mode, r.iters)
+        np.testing.assert_allclose(r.s, oracle.sequential(cell, x, s0), rtol=0, atol=1e-10)
+
+
+def test_advancing_window_accepts_only_converged_steps():
+    wl = workloads.make(2, B=2, T=200)
+    cell = oracle.make_cell(wl["cell"], wl["params"], wl["D"], wl["m"])
+    x, s0 = wl["x"].astype(np.float64), wl["s0"].astype(np.float64)
+    tol = 1e-7
+    for mode in (oracle.QUASI_NEWTON, oracle.JACOBI, oracle.NEWTON):
+        r = oracle.solve_advancing(cell, x, s0, mode, tol, 1000, 48)
+        assert r.status == oracle.OK
+        # every step of the result meets the tolerance, checked step by step
+        prev = s0
+        for t in range(x.shape[1]):
+            assert np.max(np.abs(r.s[:, t] - cell.f(prev, x[:, t]))) <= tol
+            prev = r.s[:, t]
+        np.testing.assert_allclose(r.s, oracle.sequential(cell, x, s0), rtol=0, atol=1e-5)
+    # Jacobi accepts at least one exact step per update: at most T updates
+    rj = oracle.solve_advancing(cell, x, s0, oracle.JACOBI, 0.0, 1000, 48)
+    assert rj.status == oracle.OK and rj.iters <= 200
+    np.testing.assert_allclose(rj.s, oracle.sequential(cell, x, s0), rtol=0, atol=1e-12)
+
+
+def test_advancing_window_cap_and_nonfinite():
+    cell = _Affine(np.array([[0.5]]))
+    x = np.ones((1, 6, 1))
+    r = oracle.solve_advancing(cell, x, np.zeros((1, 1)), oracle.JACOBI, 0.0, 2, 4)
+    assert r.status == oracle.NOT_CONVERGED and r.iters == 2 and len(r.hist[0]) == 3
+    assert np.all(np.isfinite(r.s))          # steps never reached hold the window's last state
+    x[0, 2, 0] = np.nan
+    r = oracle.solve_advancing(cell, x, np.zeros((1, 1)), oracle.JACOBI, 1e-6, 10, 4)
+    assert r.status == oracle.NONFINITE and r.iters == 0
 
 
 def test_residual_of_a_perturbed_trajectory():

@@ -19,6 +19,7 @@ Parameter layouts are the flat layouts of the C interface:
   diag-tanh: a[D]
   tanh RNN : W[D*D] | U[D*m] | b[D]
   GRU      : W_ih[3D*m] | W_hh[3D*D] | b_ih[3D] | b_hh[3D]  (gates r, z, n)
+  Euler    : W[D*D] | U[D*m] | b[D] | h[D]
 """
 
 import json
@@ -26,7 +27,7 @@ import os
 
 import numpy as np
 
-CELL_DIAG_TANH, CELL_TANH_RNN, CELL_GRU = 0, 1, 2
+CELL_DIAG_TANH, CELL_TANH_RNN, CELL_GRU, CELL_EULER_TANH = 0, 1, 2, 3
 JACOBI, PICARD, QUASI_NEWTON, NEWTON, BANDED = 0, 1, 2, 3, 4
 MODE_NAMES = {JACOBI: "jacobi", PICARD: "picard", QUASI_NEWTON: "quasi_newton", NEWTON: "newton",
               BANDED: "banded"}
@@ -54,6 +55,13 @@ CONFIGS = {
     6: dict(name="lattice_tanh_d64", cell=CELL_TANH_RNN, B=16, T=4096, D=64, m=16,
             modes=(BANDED, QUASI_NEWTON, NEWTON), tol=1e-5, damping=1.0, window=0, rho=0.9,
             lattice_band=2, eps=0.05, bandwidth=2),
+    # A small-step ODE, the regime of Picard's identity approximation and of
+    # the sliding window of [PN §1.3.1]: explicit Euler steps h of the
+    # continuous-time RNN ds/dt = -s + tanh(W s + U x(t) + b), solved with a
+    # window of W = 256 steps that advances past its converged prefix.
+    7: dict(name="ode_ctrnn_d32", cell=CELL_EULER_TANH, B=64, T=8192, D=32, m=8,
+            modes=(PICARD, QUASI_NEWTON, NEWTON), tol=1e-5, damping=1.0, window=256,
+            window_mode="advancing", rho=0.9, h=0.005),
 }
 
 
@@ -85,7 +93,8 @@ def make(cfg, B=None, T=None, scale=None):
 
     Keys: cfg, name, cell, D, m, B, T, params (flat float32), x [B,T,m],
     s0 [B,D] (zeros), modes, tol, damping, window, max_iter, bandwidth (the
-    half-bandwidth the banded mode runs with; 1 where unset).
+    half-bandwidth the banded mode runs with; 1 where unset), window_mode
+    ("consecutive" or "advancing").
     """
     c = dict(CONFIGS[cfg])
     B = c["B"] if B is None else int(B)
@@ -102,6 +111,13 @@ def make(cfg, B=None, T=None, scale=None):
         b = np.zeros(D)
         x = rng.standard_normal((B, T, m))
         params = np.concatenate([W.ravel(), U.ravel(), b])
+    elif c["cell"] == CELL_EULER_TANH:
+        W = _rescale_spectral_radius(rng.standard_normal((D, D)), c["rho"])
+        U = rng.standard_normal((D, m)) / np.sqrt(m)
+        b = rng.standard_normal(D) * 0.1
+        h = np.full(D, c["h"])
+        x = rng.standard_normal((B, T, m))
+        params = np.concatenate([W.ravel(), U.ravel(), b, h])
     elif c["cell"] == CELL_TANH_RNN:
         W = _rescale_spectral_radius(rng.standard_normal((D, D)), c["rho"])
         U = rng.standard_normal((D, m))
@@ -131,8 +147,11 @@ def make(cfg, B=None, T=None, scale=None):
              x=np.ascontiguousarray(x, dtype=np.float32),
              s0=np.zeros((B, D), dtype=np.float32))
     W = c["window"] if c["window"] else T
-    c["max_iter"] = int(W)
     c.setdefault("bandwidth", 1)
+    c.setdefault("window_mode", "consecutive")
+    # the causality bound of [PN §3.1]: W updates per consecutive window; an
+    # advancing window accepts at least one step per undamped update
+    c["max_iter"] = int(T if c["window_mode"] == "advancing" else W)
     return c
 
 
@@ -172,4 +191,10 @@ def random_cell_params(kind, D, m, rng, scale=1.0):
     if kind == CELL_GRU:
         W_ih, W_hh, b_ih, b_hh = _gru_weights(rng, D, m)
         return np.concatenate([W_ih.ravel(), (W_hh * scale).ravel(), b_ih, b_hh]).astype(np.float32)
+    if kind == CELL_EULER_TANH:
+        W = rng.standard_normal((D, D)) / np.sqrt(D) * scale
+        U = rng.standard_normal((D, m)) / np.sqrt(max(m, 1))
+        b = rng.standard_normal(D) * 0.1
+        h = rng.uniform(0.01, 0.1, D)
+        return np.concatenate([W.ravel(), U.ravel(), b, h]).astype(np.float32)
     raise ValueError(kind)
