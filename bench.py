@@ -33,6 +33,7 @@ KERNEL_SOURCES = {  # source file of the dominant kernel per cell kind
     0: "newton_evaluation_nonlinear_amd/csrc/pn_diag.hip",
     1: "newton_evaluation_nonlinear_amd/csrc/pn_cell.hip",
     2: "newton_evaluation_nonlinear_amd/csrc/pn_cell.hip",
+    3: "newton_evaluation_nonlinear_amd/csrc/pn_cell.hip",
 }
 
 
@@ -69,7 +70,8 @@ def cpu_baseline(cfg, mode):
     import workloads
 
     samples = {3: dict(B=8, T=32768), 2: dict(B=16, T=2048), 4: dict(B=8, T=4096),
-               1: dict(B=None, T=None), 5: dict(B=4, T=4096), 6: dict(B=8, T=4096)}
+               1: dict(B=None, T=None), 5: dict(B=4, T=4096), 6: dict(B=8, T=4096),
+               7: dict(B=None, T=None)}
     sm = samples.get(cfg, dict(B=1, T=4096))
     if cfg == 2 and mode == 1:
         # float64 Picard on this GRU needs ~T updates (it converges only
@@ -78,8 +80,13 @@ def cpu_baseline(cfg, mode):
     wl = workloads.make(cfg, **sm)
     with threadpool_limits(1):
         t0 = time.perf_counter()
-        r = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], mode, wl["tol"],
-                         wl["max_iter"], wl["damping"], wl["window"], bandwidth=wl["bandwidth"])
+        if wl["window_mode"] == "advancing":
+            cell = oracle.make_cell(wl["cell"], wl["params"], wl["D"], wl["m"])
+            r = oracle.solve_advancing(cell, wl["x"], wl["s0"], mode, wl["tol"], wl["max_iter"],
+                                       wl["window"], wl["damping"], wl["bandwidth"])
+        else:
+            r = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], mode, wl["tol"],
+                             wl["max_iter"], wl["damping"], wl["window"], bandwidth=wl["bandwidth"])
         el = time.perf_counter() - t0
     n = wl["B"] * wl["T"] * wl["D"]
     return {"value": n / el, "unit": "state-updates/s", "cores": 1, "kind": "oracle",
@@ -193,15 +200,16 @@ def main():
     dev = torch.device("cuda:0")
     params, x, s0 = (torch.from_numpy(wl[k]).to(dev) for k in ("params", "x", "s0"))
     out = torch.empty((wl["B"], wl["T"], wl["D"]), dtype=torch.float32, device=dev)
+    wmode = pn.WINDOW_ADVANCING if wl["window_mode"] == "advancing" else pn.WINDOW_CONSECUTIVE
     nbytes = pn.workspace_bytes(wl["cell"], wl["m"], wl["B"], wl["T"], wl["D"], mode,
-                                wl["damping"], wl["window"], args.chunk, wl["bandwidth"])
+                                wl["damping"], wl["window"], args.chunk, wl["bandwidth"], wmode)
     ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
 
     def solve(profile):
         return pn.eval(wl["cell"], params, x, s0, mode=mode, tol=wl["tol"],
                        max_iter=wl["max_iter"], damping=wl["damping"], window=wl["window"],
                        chunk=args.chunk, out=out, workspace=ws, profile=profile,
-                       bandwidth=wl["bandwidth"])
+                       bandwidth=wl["bandwidth"], window_mode=wmode)
 
     if args.copy_probe:
         n = 64 * 1024 * 1024
@@ -256,6 +264,7 @@ def main():
         "config": {"workload": name, "cell": wl["cell"], "B": wl["B"], "T": wl["T"],
                    "D": wl["D"], "m": wl["m"], "mode": workloads.MODE_NAMES[mode],
                    "tol": wl["tol"], "damping": wl["damping"], "window": wl["window"],
+                   **({"window_mode": "advancing"} if wmode else {}),
                    **({"bandwidth": wl["bandwidth"]} if mode == 4 else {}),
                    "iters": last.iters, "window_iters_first": last.window_iters[:4],
                    "status": last.status, "parallelism": "single GPU"},

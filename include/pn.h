@@ -28,7 +28,9 @@
  *   - damping lam in (0, 1] is step damping, s <- s + lam (s^ - s)
  *     [PN §4.3 suggests more damping when iterations stall];
  *   - windows [PN §1.3.1, §2.3]: consecutive blocks of W steps solved in
- *     order, window w starting from the last state of window w-1.
+ *     order, window w starting from the last state of window w-1; or, with
+ *     PN_WINDOW_ADVANCING, one window of W steps that slides past its
+ *     converged prefix (below).
  *
  * Memory conventions (all functions):
  *   - float pointers named params, x, s0, out, A, b are DEVICE pointers to
@@ -60,8 +62,14 @@ extern "C" {
  *  PN_CELL_GRU        gated recurrent unit with torch.nn.GRU's equations and
  *                     gate order (r, z, n); params W_ih[3D*m] | W_hh[3D*D] |
  *                     b_ih[3D] | b_hh[3D].  1 <= D <= 64.
- * The RNN cell is the application the article names [PN §1.3.2]. */
-enum { PN_CELL_DIAG_TANH = 0, PN_CELL_TANH_RNN = 1, PN_CELL_GRU = 2 };
+ *  PN_CELL_EULER_TANH f = p + h * (tanh(W p + U x + b) - p): one explicit
+ *                     Euler step (per-channel step sizes h) of the
+ *                     continuous-time RNN ds/dt = -s + tanh(W s + U x + b);
+ *                     params W[D*D] | U[D*m] | b[D] | h[D].  1 <= D <= 64.
+ * The RNN cells are the application the article names [PN §1.3.2]; the
+ * Euler cell is the small-step regime of [PN §1.3.1, §2.2.3], where the
+ * dynamics Jacobian is close to the identity. */
+enum { PN_CELL_DIAG_TANH = 0, PN_CELL_TANH_RNN = 1, PN_CELL_GRU = 2, PN_CELL_EULER_TANH = 3 };
 
 /* Jacobian approximations (see above).  Every cell supports every mode.
  * PN_BANDED takes its half-bandwidth k from pn_opts.bandwidth; band_0 is the
@@ -122,7 +130,31 @@ typedef struct pn_opts {
     pn_profile* profile;      /* host; NULL = no event timing                   */
     int32_t flags;            /* PN_FLAG_* bits, 0 = defaults                    */
     int32_t bandwidth;        /* PN_BANDED half-bandwidth k >= 0 (default 1)    */
+    int32_t window_mode;      /* PN_WINDOW_CONSECUTIVE (default) or
+                                 PN_WINDOW_ADVANCING                            */
+    int32_t* accepted;        /* host; advancing window: steps accepted at each
+                                 check with a finite residual, in order
+                                 (truncated to accepted_len)                   */
+    int64_t accepted_len;
 } pn_opts;
+
+/* pn_opts.window_mode.
+ * PN_WINDOW_CONSECUTIVE: windows of W steps solved one after another, each
+ *   to tol; max_iter caps the updates of each window; window_iters and
+ *   resid_hist hold one entry / one run per window.
+ * PN_WINDOW_ADVANCING (matrix cells only; the sliding window of
+ *   [PN §1.3.1]): steps [0, a) are accepted and never change again; the
+ *   window is [a, min(T, a + W)).  Each round checks the current iterate on
+ *   the window, r_t = max over (b, d) of |F_t|, and r = max_t r_t (stored in
+ *   resid_hist); r not finite stops with PN_NONFINITE; otherwise a moves to
+ *   the first t with r_t > tol (past the window if none), a = T stops with
+ *   PN_OK, and after max_iter updates in total the solve stops with
+ *   PN_NOT_CONVERGED.  The window then slides to [a, min(T, a + W)), steps
+ *   entering it start from its last state, and one update of the chosen mode
+ *   is applied to it.  *iters_out and window_iters[0] count the updates; on
+ *   exit, steps the window never reached hold its last state.  Damping and
+ *   every mode apply; PN_FLAG_PERSISTENT is ignored. */
+enum { PN_WINDOW_CONSECUTIVE = 0, PN_WINDOW_ADVANCING = 1 };
 
 /* pn_opts.flags.  PN_FLAG_PERSISTENT runs a solve of a matrix cell in a
  * diagonal mode as one cooperative launch (all windows and iterations, with

@@ -18,11 +18,12 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpn.so")
 
-CELL_DIAG_TANH, CELL_TANH_RNN, CELL_GRU = 0, 1, 2
+CELL_DIAG_TANH, CELL_TANH_RNN, CELL_GRU, CELL_EULER_TANH = 0, 1, 2, 3
 JACOBI, PICARD, QUASI_NEWTON, NEWTON, BANDED = 0, 1, 2, 3, 4
 OK, NOT_CONVERGED, NONFINITE = 0, 1, 2
 EINVAL, EUNSUPPORTED, EHIP, EWORKSPACE = -1, -2, -3, -4
 FLAG_PERSISTENT = 1
+WINDOW_CONSECUTIVE, WINDOW_ADVANCING = 0, 1
 
 EXPORTED = ("pn_opts_init", "pn_eval", "pn_eval_ex", "pn_workspace_bytes", "pn_affine_scan",
             "pn_affine_scan_workspace_bytes", "pn_last_error", "pn_version")
@@ -52,7 +53,9 @@ class Opts(ctypes.Structure):
                 ("window_iters", ctypes.POINTER(ctypes.c_int32)),
                 ("window_iters_len", ctypes.c_int64),
                 ("profile", ctypes.POINTER(Profile)),
-                ("flags", ctypes.c_int32), ("bandwidth", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("bandwidth", ctypes.c_int32),
+                ("window_mode", ctypes.c_int32),
+                ("accepted", ctypes.POINTER(ctypes.c_int32)), ("accepted_len", ctypes.c_int64)]
 
 
 _lib = None
@@ -110,7 +113,8 @@ def _stream_ptr(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def make_opts(damping=1.0, window=0, chunk=0, stream=None, flags=0, bandwidth=1):
+def make_opts(damping=1.0, window=0, chunk=0, stream=None, flags=0, bandwidth=1,
+              window_mode=WINDOW_CONSECUTIVE):
     o = Opts()
     lib().pn_opts_init(ctypes.byref(o))
     o.damping = float(damping)
@@ -119,12 +123,13 @@ def make_opts(damping=1.0, window=0, chunk=0, stream=None, flags=0, bandwidth=1)
     o.stream = stream
     o.flags = int(flags)
     o.bandwidth = int(bandwidth)
+    o.window_mode = int(window_mode)
     return o
 
 
 def workspace_bytes(cell_kind, input_dim, B, T, D, mode, damping=1.0, window=0, chunk=0,
-                    bandwidth=1):
-    o = make_opts(damping, window, chunk, bandwidth=bandwidth)
+                    bandwidth=1, window_mode=WINDOW_CONSECUTIVE):
+    o = make_opts(damping, window, chunk, bandwidth=bandwidth, window_mode=window_mode)
     c = Cell(cell_kind, input_dim)
     n = lib().pn_workspace_bytes(ctypes.byref(c), B, T, D, mode, ctypes.byref(o))
     if n == 0:
@@ -135,9 +140,10 @@ def workspace_bytes(cell_kind, input_dim, B, T, D, mode, damping=1.0, window=0, 
 class Result:
     """Outcome of one solve: trajectory, total updates, status and diagnostics."""
 
-    def __init__(self, out, iters, status, window_iters, resid_hist, profile):
+    def __init__(self, out, iters, status, window_iters, resid_hist, profile, accepted=None):
         self.out, self.iters, self.status = out, iters, status
         self.window_iters, self.resid_hist, self.profile = window_iters, resid_hist, profile
+        self.accepted = accepted     # advancing window: steps accepted per check
 
     def __iter__(self):
         return iter((self.out, self.iters, self.status))
@@ -145,11 +151,13 @@ class Result:
 
 def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, damping=1.0,
          window=0, chunk=0, out=None, history=False, profile=False, workspace=None, flags=0,
-         bandwidth=1):
+         bandwidth=1, window_mode=WINDOW_CONSECUTIVE):
     """Solve s_t = f(s_{t-1}, x_t) for t = 1..T over the batch; see include/pn.h.
 
     params, x [B,T,m], s0 [B,D] are float32 tensors on one HIP device.
-    ``bandwidth`` is the half-bandwidth k of the BANDED mode.
+    ``bandwidth`` is the half-bandwidth k of the BANDED mode; ``window_mode``
+    WINDOW_ADVANCING slides one window past its converged prefix (max_iter
+    then defaults to T and caps the updates of the whole solve).
     Returns a ``Result`` (unpacks as ``out, iters, status``).  Negative
     library statuses raise ``PnError``.
     """
@@ -158,13 +166,14 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     if s0.shape[0] != B:
         raise ValueError("x and s0 disagree on B")
     W = T if window in (0, None) else int(window)
+    advancing = int(window_mode) == WINDOW_ADVANCING
     if max_iter is None:
-        max_iter = W
+        max_iter = T if advancing else W
     dev = x.device
     if out is None:
         out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
     c = Cell(int(cell_kind), int(m))
-    o = make_opts(damping, window or 0, chunk, _stream_ptr(dev), flags, bandwidth)
+    o = make_opts(damping, window or 0, chunk, _stream_ptr(dev), flags, bandwidth, window_mode)
     nbytes = lib().pn_workspace_bytes(ctypes.byref(c), B, T, D, int(mode), ctypes.byref(o))
     if nbytes == 0:
         raise PnError(EINVAL, last_error())
@@ -174,7 +183,7 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     aligned = (base + 255) // 256 * 256
     o.workspace = aligned
     o.workspace_bytes = workspace.numel() - (aligned - base)
-    nwin = max(1, -(-T // W)) if T > 0 else 1
+    nwin = 1 if advancing else (max(1, -(-T // W)) if T > 0 else 1)
     wit = (ctypes.c_int32 * nwin)()
     o.window_iters = wit
     o.window_iters_len = nwin
@@ -184,6 +193,12 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
         hist = (ctypes.c_float * hlen)()
         o.resid_hist = hist
         o.resid_hist_len = hlen
+    acc = None
+    if advancing and history:
+        alen = int(max_iter) + 1
+        acc = (ctypes.c_int32 * alen)()
+        o.accepted = acc
+        o.accepted_len = alen
     prof = Profile() if profile else None
     if prof is not None:
         o.profile = ctypes.pointer(prof)
@@ -201,7 +216,12 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     pd = None
     if prof is not None:
         pd = {k: getattr(prof, k) for k, _ in Profile._fields_}
-    return Result(out, int(iters.value), int(rc), witer, rh, pd)
+    accepted = None
+    if acc is not None:
+        accepted = list(acc[:min(len(rh or []), len(acc))])
+        if rc == NONFINITE:
+            accepted = accepted[:-1]
+    return Result(out, int(iters.value), int(rc), witer, rh, pd, accepted)
 
 
 def affine_scan(A, b, s0, dense=False, chunk=0, out=None):

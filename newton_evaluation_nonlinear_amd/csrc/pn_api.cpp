@@ -66,9 +66,10 @@ struct Plan {
     int L, NC;             // chunk length, chunks of a full window
     int DP, cpb;           // padded D (matrix cells), channels per block (diag cell)
     bool dense, matrix_cell, mfma;
+    bool advancing;        // one window sliding past its converged prefix
     bool persist_ok;       // shape allows the one-launch persistent solver
     int nblocks, nwin, hist_cap;
-    size_t off_ctrl, off_rpart, off_aggA, off_aggB, off_carry, off_halo, off_w, total;
+    size_t off_ctrl, off_rpart, off_fpart, off_aggA, off_aggB, off_carry, off_halo, off_w, total;
     size_t off_sync, off_winfo, off_hist;
 };
 
@@ -91,6 +92,7 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
     p.T = T;
     const int64_t window = o ? o->window : 0;
     p.W = (window <= 0 || window > T) ? T : window;
+    p.advancing = o && o->window_mode == PN_WINDOW_ADVANCING;
     const int chunk = o ? o->chunk : 0;
     p.dense = p.matrix_cell && (mode == PN_NEWTON || mode == PN_BANDED);
     p.mfma = false;
@@ -150,12 +152,14 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
             return fail(PN_EUNSUPPORTED, "chunk of %d steps needs too much LDS for D=%d, m=%d", p.L, p.D, p.m);
     }
     p.nwin = static_cast<int>((T + p.W - 1) / p.W);
-    p.persist_ok = p.matrix_cell && !p.dense && cell_persist_eligible(p.kind, p.DP, p.L, p.m);
+    p.persist_ok = p.matrix_cell && !p.dense && !p.advancing &&
+                   cell_persist_eligible(p.kind, p.DP, p.L, p.m);
     p.hist_cap = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(p.nwin) * (p.W + 1), 1 << 16));
     const size_t bnd = static_cast<size_t>(p.B) * p.NC * p.D;
     size_t off = 0;
     p.off_ctrl = off; off = align_up(off + sizeof(Ctrl));
     p.off_rpart = off; off = align_up(off + sizeof(uint32_t) * p.nblocks);
+    p.off_fpart = off; off = align_up(off + sizeof(uint32_t) * p.nblocks);
     p.off_aggA = off; off = align_up(off + sizeof(float) * bnd * (p.dense ? p.D : 1));
     p.off_aggB = off; off = align_up(off + sizeof(float) * bnd);
     p.off_carry = off; off = align_up(off + sizeof(float) * bnd);
@@ -179,7 +183,7 @@ int validate(const pn_cell* cell, const float* params, const float* x, const flo
     if (!iters_out) return fail(PN_EINVAL, "iters_out is NULL");
     if (B < 0 || T < 0 || D < 0) return fail(PN_EINVAL, "negative size (B=%lld T=%lld D=%lld)",
                                              (long long)B, (long long)T, (long long)D);
-    if (cell->kind < PN_CELL_DIAG_TANH || cell->kind > PN_CELL_GRU)
+    if (cell->kind < PN_CELL_DIAG_TANH || cell->kind > PN_CELL_EULER_TANH)
         return fail(PN_EINVAL, "unknown cell kind %d", cell->kind);
     if (mode < PN_JACOBI || mode > PN_BANDED) return fail(PN_EINVAL, "unknown mode %d", mode);
     if (mode == PN_BANDED && o && o->bandwidth < 0) return fail(PN_EINVAL, "bandwidth must be >= 0");
@@ -195,8 +199,14 @@ int validate(const pn_cell* cell, const float* params, const float* x, const flo
         if (o->resid_hist_len < 0 || o->window_iters_len < 0) return fail(PN_EINVAL, "negative history length");
         if (o->resid_hist_len > 0 && !o->resid_hist) return fail(PN_EINVAL, "resid_hist is NULL");
         if (o->window_iters_len > 0 && !o->window_iters) return fail(PN_EINVAL, "window_iters is NULL");
+        if (o->accepted_len < 0 || (o->accepted_len > 0 && !o->accepted))
+            return fail(PN_EINVAL, "accepted is NULL or its length negative");
         if (o->workspace && (reinterpret_cast<uintptr_t>(o->workspace) % kAlign) != 0)
             return fail(PN_EWORKSPACE, "workspace must be 256-byte aligned");
+        if (o->window_mode != PN_WINDOW_CONSECUTIVE && o->window_mode != PN_WINDOW_ADVANCING)
+            return fail(PN_EINVAL, "unknown window_mode %d", o->window_mode);
+        if (o->window_mode == PN_WINDOW_ADVANCING && cell->kind == PN_CELL_DIAG_TANH)
+            return fail(PN_EUNSUPPORTED, "the advancing window supports the matrix cells only");
     }
     if (B == 0 || T == 0 || D == 0) return PN_OK;
     if (!params || !x || !s0 || !out) return fail(PN_EINVAL, "a device pointer is NULL");
@@ -418,6 +428,118 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
     return PN_OK;
 }
 
+// The advancing window [PN §1.3.1] (matrix cells).  Steps [0, a) are
+// accepted; the window is [a, e), e = min(T, a + W).  Each round: the device
+// reduces the residual of the current iterate on the window and the first
+// step over tol (a check launch), the host reads that record, accepts the
+// prefix and slides the window (new steps start from its last state), then
+// enqueues the chunk maps of the moved window, the carry scan and one apply
+// sweep, whose fused residual feeds the next check.  The host waits once per
+// round: the next window depends on the check.
+int solve_advancing(SolveCtx& c, const float* x, const float* s0, float* out, int64_t T, int* K,
+                    int* status, std::vector<int32_t>* accepted) {
+    const Plan& p = *c.p;
+    const int64_t D = p.D, m = p.m, W = p.W;
+    Ctrl* ctrl = reinterpret_cast<Ctrl*>(c.ws + p.off_ctrl);
+    uint32_t* rpart = reinterpret_cast<uint32_t*>(c.ws + p.off_rpart);
+    uint32_t* fpart = reinterpret_cast<uint32_t*>(c.ws + p.off_fpart);
+    float* aggA = reinterpret_cast<float*>(c.ws + p.off_aggA);
+    float* aggB = reinterpret_cast<float*>(c.ws + p.off_aggB);
+    float* carry = reinterpret_cast<float*>(c.ws + p.off_carry);
+    float* halo = reinterpret_cast<float*>(c.ws + p.off_halo);
+
+    CellArgs ca{};
+    ca.w = reinterpret_cast<const float*>(c.ws + p.off_w);
+    ca.xs = T * m; ca.ss = T * D;
+    ca.B = p.B; ca.D = p.D; ca.m = p.m; ca.L = p.L;
+    ca.aggA = aggA; ca.aggB = aggB; ca.carry = carry; ca.halo = halo; ca.rpart = rpart;
+    ca.ctrl = ctrl; ca.mode = p.mode; ca.lam = c.lam; ca.undamped = c.lam == 1.0f;
+    ca.band = p.band; ca.fpart = fpart; ca.tol = c.tol;
+    CarryArgs cy{};
+    cy.aggA = aggA; cy.aggB = aggB; cy.carry = carry; cy.B = p.B; cy.D = p.D; cy.do_check = 0;
+    CheckArgs chk{};
+    chk.rpart = rpart; chk.fpart = fpart; chk.advancing = 1; chk.max_iter = c.max_iter;
+    chk.tol = c.tol; chk.ctrl = ctrl; chk.host = c.res->host_dev;
+    volatile HostRec* hr = c.res->host;
+    const int32_t epoch = ++c.res->epoch;
+    chk.epoch = epoch;
+    hr->iter = -1;
+
+    int64_t a = 0, e = std::min<int64_t>(T, W);
+    int Tw = 0;
+    auto set_window = [&]() {
+        Tw = static_cast<int>(e - a);
+        const int NC = (Tw + p.L - 1) / p.L;
+        ca.x = x + a * m;
+        ca.s = out + a * D;
+        ca.s0 = a == 0 ? s0 : out + (a - 1) * D;
+        ca.s0s = a == 0 ? D : T * D;
+        ca.Tw = Tw;
+        ca.NC = NC;
+        cy.s0 = ca.s0; cy.s0s = ca.s0s; cy.NC = NC;
+        chk.nparts = p.B * NC;
+    };
+    auto launch_pass = [&](int phase, int iter) -> hipError_t {
+        ca.iter = iter;
+        if (p.mfma) return launch_dense_mfma_pass(p.kind, p.DP, phase, ca, c.st);
+        return launch_cell_pass(p.kind, p.DP, p.dense, phase, ca, c.st);
+    };
+
+    // the initial iterate s0 on the first window, its maps and its check
+    PN_HIP(launch_fill(out, T * D, s0, D, p.B, static_cast<int>(e), p.D, c.st));
+    set_window();
+    PN_HIP(launch_pass(kMaps, 0));
+    chk.iter = 0;
+    PN_HIP(launch_check(chk, c.st));
+    int64_t ma = a, me = e;          // the window the chunk maps on the device belong to
+    for (int i = 0;;) {
+        {
+            int rc = wait_record(hr, c.st, epoch, i);
+            if (rc != PN_OK) return rc;
+        }
+        const uint32_t rb = hr->r_bits;
+        const uint32_t first = hr->first;
+        float r;
+        std::memcpy(&r, &rb, sizeof(r));
+        if (c.hist) c.hist->push_back(r);
+        if (rb >= kNonFiniteBits) { *K = i; *status = PN_NONFINITE; break; }
+        const int64_t acc = std::min<int64_t>(first, e - a);
+        accepted->push_back(static_cast<int32_t>(acc));
+        a += acc;
+        if (a >= T) { *K = i; *status = PN_OK; break; }
+        if (i == c.max_iter) { *K = i; *status = PN_NOT_CONVERGED; break; }
+        const int64_t e_new = std::min<int64_t>(T, a + W);
+        if (e_new > e)
+            PN_HIP(launch_fill(out + e * D, T * D, out + (e - 1) * D, T * D, p.B,
+                               static_cast<int>(e_new - e), p.D, c.st));
+        e = e_new;
+        set_window();
+        if (a != ma || e != me) {
+            PN_HIP(launch_pass(kMaps, i));
+            ma = a;
+            me = e;
+        }
+        PN_HIP(p.dense ? launch_dense_carry(cy, c.st) : launch_diag_carry(cy, c.st));
+        size_t e0 = 0, e1 = 0;
+        if (c.tm->on) { int rc = record(c, &e0); if (rc) return rc; }
+        PN_HIP(launch_pass(kSteady, i));
+        if (c.tm->on) {
+            int rc = record(c, &e1);
+            if (rc) return rc;
+            c.tm->apply.push_back({e0, e1});
+            c.tm->apply_bytes.push_back(apply_bytes(p, Tw, false));
+            c.tm->apply_flops.push_back(apply_flops(p, Tw));
+        }
+        ++i;
+        chk.iter = i;
+        PN_HIP(launch_check(chk, c.st));
+    }
+    if (e < T)
+        PN_HIP(launch_fill(out + e * D, T * D, out + (e - 1) * D, T * D, p.B, static_cast<int>(T - e),
+                           p.D, c.st));
+    return PN_OK;
+}
+
 // The whole solve as one cooperative launch (matrix cells, diagonal modes).
 // Returns PN_EUNSUPPORTED (no launch made) when the device cannot run it, so
 // the caller falls back to the multi-launch driver.
@@ -544,12 +666,25 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     if (tm.on) { rc = record(c, &ev_first); if (rc) return rc; }
     int total = 0, overall = PN_OK;
     std::vector<int> wit;
+    std::vector<int32_t> accepted;
     const int64_t m = p.m;
     bool persisted = false;
     if (p.persist_ok && o && (o->flags & PN_FLAG_PERSISTENT)) {
         rc = solve_persistent(c, x, s0, out, T, &wit, &total, &overall);
         if (rc == PN_OK) persisted = true;
         else if (rc != PN_EUNSUPPORTED) return rc;
+    }
+    if (p.advancing) {
+        int K = 0, status = PN_OK;
+        rc = solve_advancing(c, x, s0, out, T, &K, &status, &accepted);
+        if (rc != PN_OK) {
+            if (own_ws) { (void)hipFreeAsync(ws, st); (void)hipStreamSynchronize(st); }
+            return rc;
+        }
+        total = K;
+        wit.push_back(K);
+        overall = status;
+        persisted = true;       // nothing left for the window loop below
     }
     for (int64_t w0 = 0; !persisted && w0 < T; w0 += p.W) {
         const int Tw = static_cast<int>(std::min<int64_t>(p.W, T - w0));
@@ -581,6 +716,8 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
             o->window_iters[k] = wit[k];
         for (int32_t k = 0; k < o->resid_hist_len && k < static_cast<int32_t>(hist.size()); ++k)
             o->resid_hist[k] = hist[k];
+        for (int64_t k = 0; o->accepted && k < o->accepted_len && k < static_cast<int64_t>(accepted.size()); ++k)
+            o->accepted[k] = accepted[k];
         if (o->profile) {
             pn_profile* pr = o->profile;
             for (size_t k = 0; k < tm.apply.size(); ++k) {

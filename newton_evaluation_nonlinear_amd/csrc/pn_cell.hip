@@ -8,10 +8,12 @@
 // maps of iteration i+1.  Differences:
 //   * the cell couples channels (matrix-vector products), so a chunk is one
 //     workgroup holding all D channels of L consecutive steps in LDS;
-//   * the Jacobian of both cells is a diagonal plus row-scaled copies of the
-//     recurrent weight matrices:
+//   * the Jacobian of every matrix cell is a diagonal plus row-scaled copies
+//     of the recurrent weight matrices:
 //         tanh RNN: A_t = diag(1 - v^2) W
 //         GRU     : A_t = diag(z) + diag(cz) W_hz + diag(cn) W_hn + diag(cr) W_hr
+//         Euler   : A_t = diag(1 - h) + diag(h (1 - g^2)) W,  g = tanh(W p + U x + b)
+//       (the explicit Euler step p + h (g - p) of ds/dt = -s + tanh(...))
 //     so only D-vectors of coefficients per step are kept; the diagonal
 //     modes use the diagonal of A_t (quasi-Newton [PN §2.2.1]), 1 (Picard) or
 //     0 (Jacobi), and Newton uses A_t itself;
@@ -33,18 +35,22 @@ namespace pn {
 
 constexpr int kCellTanhRnn = 1;
 constexpr int kCellGru = 2;
+constexpr int kCellEuler = 3;
 
 template <int CELL> struct CellTraits;
 template <> struct CellTraits<kCellTanhRnn> { static constexpr int NG = 1, NCO = 1; };
 template <> struct CellTraits<kCellGru> { static constexpr int NG = 3, NCO = 4; };
+template <> struct CellTraits<kCellEuler> { static constexpr int NG = 1, NCO = 2; };
 
 __host__ __device__ size_t prepared_weight_floats(int kind, int DP, int m) {
     if (kind == kCellTanhRnn) return static_cast<size_t>(DP) * DP + static_cast<size_t>(m) * DP + 2 * DP;
+    if (kind == kCellEuler) return static_cast<size_t>(DP) * DP + static_cast<size_t>(m) * DP + 3 * DP;
     return 3ull * DP * DP + 3ull * m * DP + 9ull * DP;
 }
 
 // ---------------------------------------------------------------- weight prep
 // tanh RNN: WT[k][i] = W[i][k] | UT[q][i] = U[i][q] | bias[i] | wdiag[i]
+// Euler   : the tanh RNN layout, then h[i]
 // GRU     : WhT[g][k][i] = W_hh[gD+i][k] | WiT[g][q][i] = W_ih[gD+i][q] |
 //           bih[g][i] | bhh[g][i] | whdiag[g][i] = W_hh[gD+i][i]
 __global__ __launch_bounds__(kThreads) void prep_weights_kernel(int kind, const float* __restrict__ p,
@@ -52,10 +58,11 @@ __global__ __launch_bounds__(kThreads) void prep_weights_kernel(int kind, const 
                                                                  int m, int n) {
     for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += gridDim.x * blockDim.x) {
         float val = 0.0f;
-        if (kind == kCellTanhRnn) {
+        if (kind == kCellTanhRnn || kind == kCellEuler) {
             const float* W = p;
             const float* U = p + D * D;
             const float* bb = U + D * m;
+            const float* hh = bb + D;
             if (e < DP * DP) {
                 const int k = e / DP, i = e % DP;
                 if (i < D && k < D) val = W[i * D + k];
@@ -65,9 +72,12 @@ __global__ __launch_bounds__(kThreads) void prep_weights_kernel(int kind, const 
             } else if (e < DP * DP + m * DP + DP) {
                 const int i = e - DP * DP - m * DP;
                 if (i < D) val = bb[i];
-            } else {
+            } else if (e < DP * DP + m * DP + 2 * DP) {
                 const int i = e - DP * DP - m * DP - DP;
                 if (i < D) val = W[i * D + i];
+            } else {
+                const int i = e - DP * DP - m * DP - 2 * DP;
+                if (i < D) val = hh[i];
             }
         } else {
             const float* Wih = p;
@@ -164,13 +174,14 @@ __device__ __forceinline__ void input_projection(const float* __restrict__ w, co
 // V[j] = f_t(p_t) and the Jacobian coefficients CO.  The recurrent products
 // W_g p_t go through the matrix cores into H (LDS); the gate nonlinearities
 // are per element.  If Sres is given, also folds |Sres[j+1] - V[j]| (the
-// residual of the trajectory held in Sres) into rb.  Callers synchronise the
-// workgroup before and after.
+// residual of the trajectory held in Sres) into rb and, if fb is given, the
+// first row j whose residual is not <= tol into *fb.  Callers synchronise
+// the workgroup before and after.
 template <int CELL, int DP, bool DENSE>
 __device__ __forceinline__ void eval_rows(const float* __restrict__ w, const float* Pin,
                                           const float* XI, float* H, float* V, float* CO, int Lc,
                                           int L, int D, int m, int mode, const float* Sres,
-                                          uint32_t& rb) {
+                                          uint32_t& rb, uint32_t* fb = nullptr, float tol = 0.0f) {
     constexpr int NG = CellTraits<CELL>::NG, NO = Gates<CELL, DP>::NO;
     constexpr int NRG = kThreads / DP;
     rows_gemm<DP>(Pin, DP, Lc, DP, NO, [&](int k, int o) {
@@ -205,6 +216,19 @@ __device__ __forceinline__ void eval_rows(const float* __restrict__ w, const flo
             } else {
                 CO[o] = mode == kJacobi ? 0.0f : (mode == kPicard ? 1.0f : c1 * wdiag[i]);
             }
+        } else if constexpr (CELL == kCellEuler) {
+            const float* wdiag = bi + DP;
+            const float hi = bi[2 * DP + i];
+            const float gv = tanh_f(hj[i] + xj[i] + bi[i]);
+            const float pi = Pin[o];
+            v = pi + hi * (gv - pi);
+            const float c1 = hi * (1.0f - gv * gv);
+            if constexpr (DENSE) {
+                CO[o] = 1.0f - hi;
+                CO[L * DP + o] = c1;
+            } else {
+                CO[o] = mode == kJacobi ? 0.0f : (mode == kPicard ? 1.0f : (1.0f - hi) + c1 * wdiag[i]);
+            }
         } else {
             const float* bhh = bi + 3 * DP;
             const float* whd = bhh + 3 * DP;
@@ -229,7 +253,11 @@ __device__ __forceinline__ void eval_rows(const float* __restrict__ w, const flo
             }
         }
         V[o] = v;
-        if (Sres) rb = max(rb, abs_bits(Sres[o + DP] - v));
+        if (Sres) {
+            const float d = Sres[o + DP] - v;
+            rb = max(rb, abs_bits(d));
+            if (fb && !(fabsf(d) <= tol)) *fb = min(*fb, static_cast<uint32_t>(j));
+        }
     }
 }
 
@@ -249,6 +277,8 @@ __device__ __forceinline__ float jac_row_apply(const float* __restrict__ w, cons
     }
     if constexpr (CELL == kCellTanhRnn) {
         return CO[o] * acc[0];
+    } else if constexpr (CELL == kCellEuler) {
+        return CO[o] * y[i] + CO[L * DP + o] * acc[0];
     } else {
         return CO[o] * y[i] + CO[L * DP + o] * acc[1] + CO[2 * L * DP + o] * acc[2] +
                CO[3 * L * DP + o] * acc[0];
@@ -261,7 +291,7 @@ __device__ __forceinline__ float jac_row_apply(const float* __restrict__ w, cons
 // residual bit-max through rb (the caller reduces it over the workgroup).
 template <int CELL, int DP, bool DENSE, int PHASE>
 __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float* arr,
-                                          const float* w, uint32_t& rb) {
+                                          const float* w, uint32_t& rb, uint32_t* fb = nullptr) {
     constexpr int NG = CellTraits<CELL>::NG;
     constexpr int NCO = DENSE ? CellTraits<CELL>::NCO : 1;
     const int L = g.L, m = g.m, D = g.D;
@@ -295,6 +325,15 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
             N[e] = i < D ? s0[i] : 0.0f;
         }
         __syncthreads();
+    } else if constexpr (PHASE == kMaps) {
+        // N: rows t0-1 .. t1-1 of the iterate in s (this pass writes no row
+        // of s, so the row before the chunk is read directly); its last row
+        // is the halo the next apply reads
+        const float* sg = g.s + b * g.ss + static_cast<int64_t>(t0) * D;
+        if (tid < DP) N[tid] = tid < D ? (c == 0 ? s0[tid] : sg[tid - D]) : 0.0f;
+        copy_rows_to_lds<kThreads>(N + DP, DP, sg, D, Lc, D);
+        __syncthreads();
+        if (tid < D) g.halo[(g.iter & 1) * HS + ci * D + tid] = N[Lc * DP + tid];
     } else {
         // ---- P: rows t0-1 .. t1-1 of s^(i)
         float* sg = g.s + b * g.ss + static_cast<int64_t>(t0) * D;
@@ -363,7 +402,7 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
         if (tid < D) g.halo[((g.iter + 1) & 1) * HS + ci * D + tid] = N[Lc * DP + tid];
     }
     // ---- maps of iteration i+1 at the new iterate, and its residual
-    eval_rows<CELL, DP, DENSE>(w, N, XI, H, V, CO, Lc, L, D, m, g.mode, N, rb);
+    eval_rows<CELL, DP, DENSE>(w, N, XI, H, V, CO, Lc, L, D, m, g.mode, N, rb, fb, g.tol);
     __syncthreads();
     if constexpr (!DENSE) {
         if (tid < D) {
@@ -416,6 +455,8 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
                     float val;
                     if constexpr (CELL == kCellTanhRnn) {
                         val = CO[o] * acc[0];
+                    } else if constexpr (CELL == kCellEuler) {
+                        val = CO[o] * M0[i * MS + col] + CO[L * DP + o] * acc[0];
                     } else {
                         val = CO[o] * M0[i * MS + col] + CO[L * DP + o] * acc[1] +
                               CO[2 * L * DP + o] * acc[2] + CO[3 * L * DP + o] * acc[0];
@@ -435,6 +476,8 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
                     float val;
                     if constexpr (CELL == kCellTanhRnn) {
                         val = CO[o] * acc[0];
+                    } else if constexpr (CELL == kCellEuler) {
+                        val = CO[o] * (B0[i] - N[o]) + CO[L * DP + o] * acc[0];
                     } else {
                         val = CO[o] * (B0[i] - N[o]) + CO[L * DP + o] * acc[1] +
                               CO[2 * L * DP + o] * acc[2] + CO[3 * L * DP + o] * acc[0];
@@ -454,7 +497,7 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
 
 template <int CELL, int DP, bool DENSE, int PHASE, bool STAGE>
 __global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
-    if constexpr (PHASE != kPrologue) {
+    if constexpr (PHASE != kPrologue && PHASE != kMaps) {   // apply launches enqueued ahead
         if (g.ctrl->stop) return;
     }
     extern __shared__ float lds[];
@@ -462,10 +505,16 @@ __global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
     const int nw = STAGE ? static_cast<int>(prepared_weight_floats(CELL, DP, g.m)) : 0;
     copy_to_lds<kThreads>(lds, g.w, nw);
     const float* w = STAGE ? lds : g.w;
-    uint32_t rb = 0;
-    cell_tile<CELL, DP, DENSE, PHASE>(g, blockIdx.x, blockIdx.y, lds + ((nw + 3) & ~3), w, rb);
+    uint32_t rb = 0, fb = 0xffffffffu;
+    cell_tile<CELL, DP, DENSE, PHASE>(g, blockIdx.x, blockIdx.y, lds + ((nw + 3) & ~3), w, rb,
+                                      g.fpart ? &fb : nullptr);
     rb = block_max_u32(rb);
-    if (threadIdx.x == 0) g.rpart[static_cast<size_t>(blockIdx.y) * g.NC + blockIdx.x] = rb;
+    const size_t blk = static_cast<size_t>(blockIdx.y) * g.NC + blockIdx.x;
+    if (threadIdx.x == 0) g.rpart[blk] = rb;
+    if (g.fpart) {
+        fb = ~block_max_u32(~fb);
+        if (threadIdx.x == 0) g.fpart[blk] = fb == 0xffffffffu ? fb : blockIdx.x * g.L + fb;
+    }
 }
 
 template <int CELL, int DP, bool DENSE, int PHASE, bool STAGE>
@@ -487,10 +536,12 @@ static hipError_t launch_phase(int phase, const CellArgs& a, hipStream_t st) {
     if (stage) {
         if (phase == kPrologue) return launch_one<CELL, DP, DENSE, kPrologue, true>(a, lds, st);
         if (phase == kFirst) return launch_one<CELL, DP, DENSE, kFirst, true>(a, lds, st);
+        if (phase == kMaps) return launch_one<CELL, DP, DENSE, kMaps, true>(a, lds, st);
         return launch_one<CELL, DP, DENSE, kSteady, true>(a, lds, st);
     }
     if (phase == kPrologue) return launch_one<CELL, DP, DENSE, kPrologue, false>(a, lds, st);
     if (phase == kFirst) return launch_one<CELL, DP, DENSE, kFirst, false>(a, lds, st);
+    if (phase == kMaps) return launch_one<CELL, DP, DENSE, kMaps, false>(a, lds, st);
     return launch_one<CELL, DP, DENSE, kSteady, false>(a, lds, st);
 }
 
@@ -512,13 +563,17 @@ hipError_t launch_cell_pass(int kind, int DP, bool dense, int phase, const CellA
         return dense ? launch_dp<kCellTanhRnn, true>(DP, phase, a, st)
                      : launch_dp<kCellTanhRnn, false>(DP, phase, a, st);
     }
+    if (kind == kCellEuler) {
+        return dense ? launch_dp<kCellEuler, true>(DP, phase, a, st)
+                     : launch_dp<kCellEuler, false>(DP, phase, a, st);
+    }
     return dense ? launch_dp<kCellGru, true>(DP, phase, a, st)
                  : launch_dp<kCellGru, false>(DP, phase, a, st);
 }
 
 static size_t cell_pass_array_floats(int kind, int DP, bool dense, int L, int m) {
-    const size_t NG = kind == kCellTanhRnn ? 1 : 3;
-    const size_t NCO = dense ? (kind == kCellTanhRnn ? 1 : 4) : 1;
+    const size_t NG = kind == kCellGru ? 3 : 1;
+    const size_t NCO = dense ? (kind == kCellTanhRnn ? 1 : kind == kCellEuler ? 2 : 4) : 1;
     const size_t NO = (NG * DP + 15) & ~size_t(15);
     const size_t mp = (m + 3) & ~3;
     size_t f = 2ull * (L + 1) * DP + 2ull * L * NO + static_cast<size_t>(L) * DP + NCO * L * DP +
@@ -726,7 +781,7 @@ __global__ __launch_bounds__(kThreads) void cell_persist(PersistArgs a) {
 }
 
 bool cell_persist_eligible(int kind, int DP, int L, int m) {
-    return cell_pass_stages_weights(kind, DP, false, L, m);
+    return (kind == kCellTanhRnn || kind == kCellGru) && cell_pass_stages_weights(kind, DP, false, L, m);
 }
 
 template <int CELL, int DP>
@@ -796,6 +851,14 @@ hipError_t launch_cell_persist(int kind, int DP, int nblocks, const PersistArgs&
         case 32: return launch_persist_t<kCellGru, 32>(nblocks, a, lds, st);
         default: return launch_persist_t<kCellGru, 64>(nblocks, a, lds, st);
     }
+}
+
+// ---------------------------------------------------------------- standalone check
+__global__ __launch_bounds__(kThreads) void check_kernel(CheckArgs c) { run_check(c); }
+
+hipError_t launch_check(const CheckArgs& c, hipStream_t st) {
+    check_kernel<<<1, kThreads, 0, st>>>(c);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- dense carry scan

@@ -11,7 +11,8 @@
 //      iteration i+1) and extends the chunk map
 //          M <- A_t M,   bg <- A_t (bg - p_t) + v_t
 //      [the affine-map composition of PN §2.1] with A_t = diag(z) +
-//      sum_g diag(c_g) W_g (tanh RNN: A_t = diag(1 - v^2) W).
+//      sum_g diag(c_g) W_g (tanh RNN: A_t = diag(1 - v^2) W; Euler step:
+//      A_t = diag(1 - h) + diag(h (1 - g^2)) W).
 // The banded mode [PN §2.2.2] replaces A_t by its band |i - k| <= band, which
 // is the same sum over the band-restricted W_g (row scaling keeps the band):
 // the lane's weights for the Jacobian products are masked once at start, the
@@ -34,6 +35,7 @@ namespace pn {
 
 constexpr int kCellTanhRnnD = 1;
 constexpr int kCellGruD = 2;
+constexpr int kCellEulerD = 3;
 constexpr int kSub = 16;          // steps per LDS sub-chunk
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -81,6 +83,7 @@ __device__ __forceinline__ float group_sum(float v) {
 template <int CELL> struct DTraits;
 template <> struct DTraits<kCellTanhRnnD> { static constexpr int NG = 1, NCO = 1; };
 template <> struct DTraits<kCellGruD> { static constexpr int NG = 3, NCO = 4; };
+template <> struct DTraits<kCellEulerD> { static constexpr int NG = 1, NCO = 2; };
 
 // LDS layout (floats) for one wave / one chunk.
 template <int CELL, int DP>
@@ -99,11 +102,12 @@ struct DLds {
 
 // Cell evaluation for row p (LDS, DP floats) with the lane's partial weights
 // wr[g][s] = W_g[i][krow(h,s)].  Returns v and writes the coefficient values
-// for row i into co[q] (q < NCO).
+// for row i into co[q] (q < NCO).  aux holds the lane row's per-gate hidden
+// biases (GRU) or its step size in aux[0] (Euler).
 template <int CELL, int DP>
 __device__ __forceinline__ float cell_eval_row(const float (&wr)[DTraits<CELL>::NG][MfmaTile<DP>::KS],
                                                const float* p, const float* xp, int i, int h,
-                                               const float (&bhh)[3], float (&co)[DTraits<CELL>::NCO]) {
+                                               const float (&aux)[3], float (&co)[DTraits<CELL>::NCO]) {
     using Tl = MfmaTile<DP>;
     constexpr int NG = DTraits<CELL>::NG;
     float acc[NG];
@@ -124,10 +128,17 @@ __device__ __forceinline__ float cell_eval_row(const float (&wr)[DTraits<CELL>::
         const float v = tanh_f(acc[0] + xp[0]);
         co[0] = 1.0f - v * v;
         return v;
+    } else if constexpr (CELL == kCellEulerD) {
+        const float g = tanh_f(acc[0] + xp[0]);
+        const float pi = p[i];
+        const float hs = aux[0];
+        co[0] = 1.0f - hs;
+        co[1] = hs * (1.0f - g * g);
+        return pi + hs * (g - pi);
     } else {
-        const float r = sigmoid_f(xp[0] + acc[0] + bhh[0]);
-        const float z = sigmoid_f(xp[kSub * DP] + acc[1] + bhh[1]);
-        const float gg = acc[2] + bhh[2];
+        const float r = sigmoid_f(xp[0] + acc[0] + aux[0]);
+        const float z = sigmoid_f(xp[kSub * DP] + acc[1] + aux[1]);
+        const float gg = acc[2] + aux[2];
         const float n = tanh_f(xp[2 * kSub * DP] + r * gg);
         const float pi = p[i];
         const float dn = (1.0f - z) * (1.0f - n * n);
@@ -163,6 +174,8 @@ __device__ __forceinline__ float jac_apply_row(const float (&wr)[DTraits<CELL>::
     for (int g = 0; g < NG; ++g) acc[g] = group_sum<DP>(acc[g]);
     if constexpr (CELL == kCellTanhRnnD) {
         return co[0] * acc[0];
+    } else if constexpr (CELL == kCellEulerD) {
+        return co[0] * di + co[1] * acc[0];
     } else {
         // gates are stored (r, z, n); coefficients (z, cz, cn, cr)
         return co[0] * di + co[1] * acc[1] + co[2] * acc[2] + co[3] * acc[0];
@@ -171,7 +184,7 @@ __device__ __forceinline__ float jac_apply_row(const float (&wr)[DTraits<CELL>::
 
 template <int CELL, int DP, int PHASE, bool BANDED>
 __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
-    if constexpr (PHASE != kPrologue) {
+    if constexpr (PHASE != kPrologue && PHASE != kMaps) {   // apply launches enqueued ahead
         if (g.ctrl->stop) return;
     }
     using Tl = MfmaTile<DP>;
@@ -201,7 +214,8 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
     float* YV = UT + NG * m * DP;            // [2][DP]
 
     const float* w = g.w;
-    // prepared layout: tanh RNN WT | UT | bias | wdiag;  GRU WhT | WiT | bih | bhh | whdiag
+    // prepared layout: tanh RNN WT | UT | bias | wdiag (Euler: | h);
+    // GRU WhT | WiT | bih | bhh | whdiag
     const float* wUT = w + NG * DP * DP;
     const float* wbi = wUT + NG * m * DP;
     const float* wbh = wbi + NG * DP;         // GRU only
@@ -224,6 +238,8 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
         bhh_l[0] = wbh[i];
         bhh_l[1] = wbh[DP + i];
         bhh_l[2] = wbh[2 * DP + i];
+    } else if constexpr (CELL == kCellEulerD) {
+        bhh_l[0] = wbi[2 * DP + i];          // step size h_i
     }
 
     // chunk map: M in accumulator layout (column lane%DP, rows krow(h, r)), offset bg[i]
@@ -232,6 +248,8 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
     for (int r = 0; r < KS; ++r) M[r] = (Tl::krow(h, r) == i && live) ? 1.0f : 0.0f;
     float bg = 0.0f;
     uint32_t rb = 0;
+    const bool track = g.fpart != nullptr;   // first step over tol (advancing window)
+    uint32_t fb = 0xffffffffu;
 
     const bool has_next = c + 1 < g.NC;
     const float* cr = g.carry + ci * D;
@@ -245,6 +263,8 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
         if (live) {
             if constexpr (PHASE == kPrologue) {
                 po = pn = s0[i];
+            } else if constexpr (PHASE == kMaps) {
+                po = pn = c == 0 ? s0[i] : sg[i - D];   // this pass writes no row of s
             } else {
                 po = (PHASE == kFirst || c == 0) ? s0[i] : g.halo[(g.iter & 1) * HS + (ci - 1) * D + i];
                 shat = cr[i];
@@ -282,7 +302,7 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
         }
         __syncthreads();
 
-        if constexpr (PHASE != kPrologue) {
+        if constexpr (PHASE != kPrologue && PHASE != kMaps) {
             // ---- maps of iteration i at the old iterate, then the replay
             for (int j = 0; j < Sc; ++j) {
                 float co[NCO];
@@ -322,7 +342,11 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
         for (int j = 0; j < Sc; ++j) {
             float co[NCO];
             const float v = cell_eval_row<CELL, DP>(wr, N + j * DP, XP + j * DP + i, i, h, bhh_l, co);
-            if (live) rb = max(rb, abs_bits(N[(j + 1) * DP + i] - v));
+            if (live) {
+                const float d = N[(j + 1) * DP + i] - v;
+                rb = max(rb, abs_bits(d));
+                if (track && !(fabsf(d) <= g.tol)) fb = min(fb, static_cast<uint32_t>(j0 + j));
+            }
             if (h == 0) {
                 V[j * DP + i] = live ? v : 0.0f;
 #pragma unroll
@@ -368,6 +392,8 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
             for (int r = 0; r < KS; ++r) {
                 if constexpr (CELL == kCellTanhRnnD) {
                     M[r] = rs[0][r] * C[0][r];
+                } else if constexpr (CELL == kCellEulerD) {
+                    M[r] = rs[0][r] * M[r] + rs[1][r] * C[0][r];
                 } else {
                     M[r] = rs[0][r] * M[r] + rs[1][r] * C[1][r] + rs[2][r] * C[2][r] + rs[3][r] * C[0][r];
                 }
@@ -385,7 +411,10 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
         __syncthreads();
     }
 
-    if constexpr (PHASE != kPrologue) {
+    if constexpr (PHASE == kMaps) {
+        // the current iterate's last row, for the apply launch that follows
+        if (h == 0 && live) g.halo[(g.iter & 1) * HS + ci * D + i] = N[i];
+    } else if constexpr (PHASE != kPrologue) {
         if (h == 0 && live) g.halo[((g.iter + 1) & 1) * HS + ci * D + i] = N[i];
     }
     // chunk map out: M[row][col] row-major, col = i
@@ -398,6 +427,10 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
     if (h == 0 && live) g.aggB[ci * D + i] = bg;
     rb = wave_max_u32(rb);
     if (lane == 0) g.rpart[ci] = rb;
+    if (track) {
+        fb = ~wave_max_u32(~fb);
+        if (lane == 0) g.fpart[ci] = fb == 0xffffffffu ? fb : t0 + fb;
+    }
 }
 
 template <int CELL, int DP, bool BANDED>
@@ -406,6 +439,7 @@ static hipError_t launch_dense_phase_b(int phase, const CellArgs& a, hipStream_t
     const dim3 grid(a.NC, a.B);
     if (phase == kPrologue) dense_pass<CELL, DP, kPrologue, BANDED><<<grid, 64, lds, st>>>(a);
     else if (phase == kFirst) dense_pass<CELL, DP, kFirst, BANDED><<<grid, 64, lds, st>>>(a);
+    else if (phase == kMaps) dense_pass<CELL, DP, kMaps, BANDED><<<grid, 64, lds, st>>>(a);
     else dense_pass<CELL, DP, kSteady, BANDED><<<grid, 64, lds, st>>>(a);
     return hipGetLastError();
 }
@@ -419,12 +453,12 @@ static hipError_t launch_dense_phase(int phase, const CellArgs& a, hipStream_t s
 
 bool dense_mfma_supported(int kind, int DP, int m) {
     if (DP != 16 && DP != 32) return false;
-    const size_t f = kind == kCellTanhRnnD ? DLds<kCellTanhRnnD, 32>::floats(m) : DLds<kCellGruD, 32>::floats(m);
-    return f * sizeof(float) <= 64 * 1024;
+    return dense_mfma_lds_bytes(kind, 32, m) <= 64 * 1024;
 }
 
 size_t dense_mfma_lds_bytes(int kind, int DP, int m) {
     if (kind == kCellTanhRnnD) return (DP == 16 ? DLds<kCellTanhRnnD, 16>::floats(m) : DLds<kCellTanhRnnD, 32>::floats(m)) * sizeof(float);
+    if (kind == kCellEulerD) return (DP == 16 ? DLds<kCellEulerD, 16>::floats(m) : DLds<kCellEulerD, 32>::floats(m)) * sizeof(float);
     return (DP == 16 ? DLds<kCellGruD, 16>::floats(m) : DLds<kCellGruD, 32>::floats(m)) * sizeof(float);
 }
 
@@ -432,6 +466,10 @@ hipError_t launch_dense_mfma_pass(int kind, int DP, int phase, const CellArgs& a
     if (kind == kCellTanhRnnD) {
         return DP == 16 ? launch_dense_phase<kCellTanhRnnD, 16>(phase, a, st)
                         : launch_dense_phase<kCellTanhRnnD, 32>(phase, a, st);
+    }
+    if (kind == kCellEulerD) {
+        return DP == 16 ? launch_dense_phase<kCellEulerD, 16>(phase, a, st)
+                        : launch_dense_phase<kCellEulerD, 32>(phase, a, st);
     }
     return DP == 16 ? launch_dense_phase<kCellGruD, 16>(phase, a, st)
                     : launch_dense_phase<kCellGruD, 32>(phase, a, st);

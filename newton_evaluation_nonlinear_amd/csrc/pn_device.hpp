@@ -133,24 +133,34 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
 // per-block maxima of the previous pass, apply the stop rule (non-finite,
 // then r <= tol, then i == max_iter) and publish it to the device control
 // word and to the pinned host record.
+// With c.advancing the check only reduces (residual max and the first step
+// over tol) and publishes; the host takes the decision and the device loop
+// keeps running.
 __device__ __forceinline__ void run_check(const CheckArgs& c) {
-    uint32_t m = 0;
+    uint32_t m = 0, nf = 0;   // nf: bitwise NOT of the first failing step (max of ~f = min of f)
     for (int k = threadIdx.x; k < c.nparts; k += blockDim.x) {
         const uint32_t v = c.rpart[k];
         m = m > v ? m : v;
+        if (c.fpart) {
+            const uint32_t f = ~c.fpart[k];
+            nf = nf > f ? nf : f;
+        }
     }
     m = block_max_u32(m);
+    if (c.fpart) nf = block_max_u32(nf);
     if (threadIdx.x == 0) {
         int st = -1;
         if (m >= kNonFiniteBits) st = kStNonFinite;
         else if (__uint_as_float(m) <= c.tol) st = kStOk;
         else if (c.iter >= c.max_iter) st = kStNotConverged;
+        if (c.advancing) st = -1;
         const int stop = st >= 0 ? 1 : 0;
         c.ctrl->stop = stop;
         c.ctrl->status = st;
         c.ctrl->iter = c.iter;
         c.ctrl->r_bits = m;
         c.host->r_bits = m;
+        c.host->first = ~nf;
         c.host->status = st;
         c.host->stop = stop;
         __threadfence_system();

@@ -25,6 +25,7 @@ struct HostRec {
     int32_t stop;
     int32_t status;
     uint32_t r_bits;
+    uint32_t first;    // advancing window: first step (window-relative) with r_t > tol
     int32_t epoch;
     int32_t iter;
 };
@@ -32,6 +33,8 @@ struct HostRec {
 // Arguments of the per-check decision, evaluated on the device.
 struct CheckArgs {
     const uint32_t* rpart;   // per-block residual maxima of the previous pass
+    const uint32_t* fpart;   // per-block first step with r_t > tol (advancing window), or null
+    int32_t advancing;       // 1: only reduce and publish; the host takes the decision
     int32_t nparts;
     int32_t iter;            // i: number of updates applied so far
     int32_t max_iter;
@@ -83,6 +86,9 @@ struct CellArgs {
     int32_t mode, iter, undamped;
     float lam;
     int32_t band;            // Jacobian half-bandwidth (dense modes; Newton: D)
+    uint32_t* fpart;         // advancing window: per-block first step with r_t > tol
+                             // (window-relative; 0xffffffff if none), or null
+    float tol;
 };
 
 struct CarryArgs {
@@ -96,13 +102,17 @@ struct CarryArgs {
     CheckArgs chk;
 };
 
-enum Phase { kPrologue = 0, kFirst = 1, kSteady = 2 };
+// kPrologue: iteration-0 chunk maps at s^(0) = s0 (implicit);  kFirst /
+// kSteady: apply for i = 0 / i >= 1;  kMaps: chunk maps, residual and halo
+// of the iterate stored in s (the advancing window, after it slides).
+enum Phase { kPrologue = 0, kFirst = 1, kSteady = 2, kMaps = 3 };
 
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_diag_tanh_pass(int phase, const DiagArgs& a, hipStream_t st);
 int diag_tanh_nblocks(const DiagArgs& a);
 hipError_t launch_diag_carry(const CarryArgs& a, hipStream_t st);
 hipError_t launch_dense_carry(const CarryArgs& a, hipStream_t st);
+hipError_t launch_check(const CheckArgs& c, hipStream_t st);
 hipError_t launch_fill(float* out, int64_t ss, const float* s0, int64_t s0s, int B, int Tw, int D,
                        hipStream_t st);
 

@@ -137,6 +137,8 @@ class SolveResult:
     window_iters: list = field(default_factory=list)   # K per window solved
     window_status: list = field(default_factory=list)
     hist: list = field(default_factory=list)           # per window: [r_0, ..., r_K]
+    accepted: list = field(default_factory=list)       # advancing window: steps accepted per check
+    round_resid: list = field(default_factory=list)    # advancing window: r_t per check, on request
 
 
 def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force, bandwidth):
@@ -217,7 +219,8 @@ def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
     return res
 
 
-def solve_advancing(cell, x, s0, mode, tol, max_iter, W, damping=1.0, bandwidth=1):
+def solve_advancing(cell, x, s0, mode, tol, max_iter, W, damping=1.0, bandwidth=1,
+                    force_accept=None, keep_round_resid=False):
     """Advancing-window solve: the window slides past its converged prefix.
 
     ``cell`` is a cell object (``make_cell``); x: [B, T, m]; s0: [B, D].
@@ -234,7 +237,11 @@ def solve_advancing(cell, x, s0, mode, tol, max_iter, W, damping=1.0, bandwidth=
       4. update the window [a, e) once with the chosen method [PN §1.2], from
          the accepted state s_{a-1}, with step damping.
     The count is the number of updates; ``window_iters`` = [count].  On
-    exit, steps the window never reached hold its last state.
+    exit, steps the window never reached hold its last state.  ``accepted``
+    lists the steps accepted at each check with a finite residual.
+    ``force_accept`` replaces the acceptance decisions by the given counts (to
+    follow a run whose decisions fell inside the floating-point ambiguity band
+    of tol); ``keep_round_resid`` keeps each check's r_t.
     """
     x = np.asarray(x, dtype=cell.dtype)
     s0 = np.asarray(s0, dtype=cell.dtype)
@@ -254,11 +261,17 @@ def solve_advancing(cell, x, s0, mode, tol, max_iter, W, damping=1.0, bandwidth=
         r_t = np.max(np.abs(win - v), axis=(0, 2))
         r = float(np.max(r_t))
         hist.append(r)
+        if keep_round_resid:
+            res.round_resid.append(r_t.astype(np.float64))
         if not np.isfinite(r):
             res.status = NONFINITE
             break
         bad = np.nonzero(~(r_t <= tol))[0]
-        a = a + int(bad[0]) if bad.size else e
+        acc = int(bad[0]) if bad.size else e - a
+        if force_accept is not None:
+            acc = int(force_accept[len(res.accepted)])
+        res.accepted.append(acc)
+        a = a + acc
         if a >= T:
             break
         if i == max_iter:

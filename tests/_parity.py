@@ -18,6 +18,8 @@ Acceptance for one solve (status, counts, trajectory, residual):
   3. max |s_gpu - s_oracle| <= 1e-4 * max(1, max |s_oracle|);
   4. the float64 residual of s_gpu, recomputed by the oracle, is <= tol + 1e-6
      for converged runs, and the library's own reported residual is <= tol.
+The advancing window compares every acceptance decision instead of one count
+per window (``check_parity_advancing``).
 """
 
 import numpy as np
@@ -49,7 +51,8 @@ def run_gpu(wl, mode, tol=None, max_iter=None, damping=None, window=None, chunk=
                   damping=wl["damping"] if damping is None else damping,
                   window=wl["window"] if window is None else window,
                   chunk=chunk, history=history, profile=profile,
-                  bandwidth=wl.get("bandwidth", 1))
+                  bandwidth=wl.get("bandwidth", 1),
+                  window_mode=pn.WINDOW_ADVANCING if advancing(wl) else pn.WINDOW_CONSECUTIVE)
     torch.cuda.synchronize()
     res.out_np = res.out.cpu().numpy()
     return res
@@ -67,12 +70,23 @@ def run_oracle(wl, mode, tol=None, max_iter=None, damping=None, window=None, dty
         ck = (key, mode, dtype, tuple(sorted(args.items())))
         if ck in _oracle_cache:
             return _oracle_cache[ck]
-    r = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], mode, args["tol"],
-                     args["max_iter"], args["damping"], args["window"], dtype=dtype,
-                     force_iters=force_iters, bandwidth=args["bandwidth"])
+    if advancing(wl):
+        if force_iters is not None:
+            raise ValueError("the advancing window has no forced-count variant")
+        cell = oracle.make_cell(wl["cell"], wl["params"], wl["D"], wl["m"], dtype)
+        r = oracle.solve_advancing(cell, wl["x"], wl["s0"], mode, args["tol"], args["max_iter"],
+                                   args["window"], args["damping"], args["bandwidth"])
+    else:
+        r = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], mode, args["tol"],
+                         args["max_iter"], args["damping"], args["window"], dtype=dtype,
+                         force_iters=force_iters, bandwidth=args["bandwidth"])
     if ck is not None:
         _oracle_cache[ck] = r
     return r
+
+
+def advancing(wl):
+    return wl.get("window_mode", "consecutive") == "advancing"
 
 
 def residual64(wl, s):
@@ -158,4 +172,53 @@ def check_parity(wl, mode, gpu, ref, tol=None, window=None, damping=None, max_it
                 pos += k + 1
                 last = gpu.resid_hist[pos - 1]
                 assert last <= tol, f"{msg}: reported residual {last:.3e} > tol"
+    return cmp_ref
+
+
+def check_parity_advancing(wl, mode, gpu, ref, label=""):
+    """Acceptance for the advancing window.  Its count follows from one
+    acceptance decision per check (the first step with r_t > tol), so the
+    decisions are compared, not only the count:
+      * status equal to the float64 oracle's;
+      * the library's accepted counts equal the oracle's; or else the float64
+        oracle, forced to take the library's decisions, shows each of them
+        consistent with its own r_t within the ambiguity band of tol (every
+        accepted step r_t <= tol + band, the first rejected one r_t >=
+        tol - band; band as for the consecutive windows), and ends with the
+        library's status and count;
+      * the trajectory within the 1e-4 bar of that oracle run, and for
+        converged runs the float64 residual of the GPU result <= tol + 1e-6."""
+    tol = wl["tol"]
+    msg = f"{label} mode={mode} gpu(status={gpu.status}, iters={gpu.iters}) " \
+          f"oracle(status={ref.status}, iters={ref.iters})"
+    assert gpu.window_iters[0] == gpu.iters, msg
+    assert gpu.accepted is not None, msg
+    cmp_ref = ref
+    if gpu.accepted != ref.accepted:
+        cell = oracle.make_cell(wl["cell"], wl["params"], wl["D"], wl["m"])
+        forced = oracle.solve_advancing(cell, wl["x"], wl["s0"], mode, tol, wl["max_iter"],
+                                        wl["window"], wl["damping"], wl.get("bandwidth", 1),
+                                        force_accept=gpu.accepted, keep_round_resid=True)
+        finite = forced.s[np.isfinite(forced.s)]
+        scale = max(1.0, float(np.max(np.abs(finite)))) if finite.size else 1.0
+        band = COUNT_BAND * tol + 2 * ULP1 * scale
+        off = [k for k, (g, o) in enumerate(zip(gpu.accepted, ref.accepted)) if g != o]
+        msg += f" first differing decision at check {off[0] if off else len(ref.accepted)}"
+        for k, acc in enumerate(gpu.accepted):
+            r_t = forced.round_resid[k]
+            assert np.all(r_t[:acc] <= tol + band), f"{msg}: check {k} accepted r={r_t[:acc].max():.4e}"
+            if acc < len(r_t):
+                assert r_t[acc] >= tol - band, f"{msg}: check {k} rejected r={r_t[acc]:.4e}"
+        assert forced.status == gpu.status and forced.iters == gpu.iters, msg
+        cmp_ref = forced
+    assert gpu.status == cmp_ref.status, msg
+    s_ref = cmp_ref.s
+    scale = max(1.0, float(np.nanmax(np.abs(s_ref))))
+    if cmp_ref.status != oracle.NONFINITE:
+        err = float(np.max(np.abs(gpu.out_np.astype(np.float64) - s_ref)))
+        assert err <= TRAJ_TOL * scale, f"{msg}: max abs error {err:.3e}"
+    if cmp_ref.status == oracle.OK:
+        r64 = residual64(wl, gpu.out_np)
+        assert r64 <= tol + RESID_SLACK, f"{msg}: float64 residual of the GPU result {r64:.3e}"
+    assert len(gpu.resid_hist) == gpu.iters + 1, msg
     return cmp_ref

@@ -92,10 +92,27 @@ def test_invalid_options():
     assert rc != pn.EINVAL or "bandwidth" not in pn.last_error()
 
 
+def test_window_mode_checks():
+    o = pn.make_opts(window_mode=2)
+    rc, _ = _eval_raw(opts=o)
+    assert rc == pn.EINVAL and "window_mode" in pn.last_error()
+    o = pn.make_opts(window_mode=pn.WINDOW_ADVANCING)
+    rc, _ = _eval_raw(kind=pn.CELL_DIAG_TANH, m=4, D=4, opts=o)
+    assert rc == pn.EUNSUPPORTED
+
+
+def test_euler_cell_sizes():
+    c = pn.Cell(pn.CELL_EULER_TANH, 3)
+    assert pn.lib().pn_workspace_bytes(ctypes.byref(c), 2, 100, 64, pn.NEWTON, None) > 0
+    assert pn.lib().pn_workspace_bytes(ctypes.byref(c), 2, 100, 65, pn.NEWTON, None) == 0
+    rc, _ = _eval_raw(kind=4)
+    assert rc == pn.EINVAL
+
+
 def test_options_defaults():
     o = pn.make_opts()
     assert o.damping == 1.0 and o.chunk == 0 and o.window == 0 and o.flags == 0
-    assert o.bandwidth == 1
+    assert o.bandwidth == 1 and o.window_mode == pn.WINDOW_CONSECUTIVE
 
 
 def test_empty_problems_succeed_without_work():

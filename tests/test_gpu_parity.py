@@ -12,7 +12,8 @@ import torch
 import oracle
 import workloads
 import newton_evaluation_nonlinear_amd as pn
-from _parity import run_gpu, run_oracle, check_parity, residual64, to_dev
+from _parity import (run_gpu, run_oracle, check_parity, check_parity_advancing, residual64, to_dev,
+                     advancing)
 
 
 def run_gpu_flags(wl, mode, flags):
@@ -58,6 +59,9 @@ def _parity(wl, mode, **kw):
     gpu = run_gpu(wl, mode, **kw)
     print(f"   gpu iters={gpu.iters} win={gpu.window_iters[:6]} status={gpu.status} "
           f"oracle iters={ref.iters} win={ref.window_iters[:6]} status={ref.status}", flush=True)
+    if advancing(wl):
+        assert not kw, "the advancing-window cases run with the workload's own settings"
+        return check_parity_advancing(wl, mode, gpu, ref, label=_label(wl))
     _report_residual_agreement(gpu, ref)
     if ref.status == oracle.NONFINITE or gpu.status == pn.NONFINITE:
         # a divergent run: its outcome is judged against the float32 oracle
@@ -205,6 +209,83 @@ def test_cfg6_lattice_small(mode):
         assert ref.iters * 2 <= qn.iters
 
 
+@pytest.mark.parametrize("D", [5, 16, 32, 64])
+def test_euler_cell_every_mode(D):
+    # the explicit-Euler cell on both dense kernels and the LDS kernel
+    rng = np.random.default_rng(500 + D)
+    m, B, T = 4, 2, 300
+    params = workloads.random_cell_params(pn.CELL_EULER_TANH, D, m, rng, 1.0)
+    wl = dict(cfg=0, cell=pn.CELL_EULER_TANH, D=D, m=m, B=B, T=T, tol=1e-5, damping=1.0,
+              window=0, max_iter=T, params=params,
+              x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32), bandwidth=2)
+    for mode in (N, Q, J, pn.BANDED):
+        _parity(wl, mode)
+    # Picard on the whole horizon converges slowly enough here (steps up to
+    # h = 0.1) for float32 rounding to move its count; over 50-step windows,
+    # its regime, the counts are exact
+    _parity(wl, P, window=50, max_iter=50)
+
+
+def _advancing_case(kind, D, m, B, T, W, seed, tol=1e-5, damping=1.0, params=None):
+    rng = np.random.default_rng(seed)
+    if params is None:
+        params = workloads.random_cell_params(kind, D, m, rng, 1.0)
+    return dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=tol, damping=damping, window=W,
+                window_mode="advancing", max_iter=T, params=params,
+                x=rng.standard_normal((B, T, m)).astype(np.float32),
+                s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32), bandwidth=2)
+
+
+@pytest.mark.parametrize("kind, D", [(pn.CELL_EULER_TANH, 32), (pn.CELL_EULER_TANH, 64),
+                                     (pn.CELL_GRU, 16), (pn.CELL_TANH_RNN, 5)])
+@pytest.mark.parametrize("W", [40, 128])
+def test_advancing_window_matches_oracle(kind, D, W):
+    # windows that are not a multiple of the chunk, a ragged end, every mode
+    wl = _advancing_case(kind, D, 4, 2, 333, W, 600 + D + W)
+    # Picard (A~ = I) is the small-step method: not run on the plain tanh RNN,
+    # where it stalls with 1e30 transients
+    for mode in (Q, N, J, pn.BANDED) + ((P,) if kind != pn.CELL_TANH_RNN else ()):
+        _parity(wl, mode)
+
+
+def test_advancing_window_damped():
+    wl = _advancing_case(pn.CELL_EULER_TANH, 16, 3, 3, 400, 96, 610, damping=0.7)
+    for mode in (Q, N):
+        _parity(wl, mode)
+
+
+def test_advancing_window_exact_newton_takes_one_update_per_window():
+    # W = 0 makes the Euler step affine in the state, so Newton solves a whole
+    # window per update and the window jumps by W: ceil(T / W) updates
+    D, m, B, T, W = 8, 3, 2, 300, 64
+    rng = np.random.default_rng(620)
+    U = rng.standard_normal((D, m)) / np.sqrt(m)
+    params = np.concatenate([np.zeros(D * D), U.ravel(), 0.1 * rng.standard_normal(D),
+                             rng.uniform(0.05, 0.2, D)]).astype(np.float32)
+    wl = _advancing_case(pn.CELL_EULER_TANH, D, m, B, T, W, 621, params=params)
+    ref = _parity(wl, N)
+    assert ref.iters == -(-T // W)
+
+
+def test_advancing_window_cap_fills_the_tail():
+    wl = _advancing_case(pn.CELL_EULER_TANH, 16, 3, 2, 500, 64, 630)
+    wl["max_iter"] = 7
+    gpu = run_gpu(wl, Q)
+    ref = run_oracle(wl, Q)
+    assert gpu.status == ref.status == pn.NOT_CONVERGED and gpu.iters == ref.iters == 7
+    assert np.all(np.isfinite(gpu.out_np))
+    np.testing.assert_allclose(gpu.out_np, ref.s, rtol=0, atol=1e-4)
+    assert len(gpu.resid_hist) == 8
+    np.testing.assert_allclose(gpu.resid_hist, ref.hist[0], rtol=2e-2, atol=1e-6)
+
+
+@pytest.mark.parametrize("mode", [P, Q, N])
+def test_cfg7_ode_advancing_small(mode):
+    wl = _case(7, B=4, T=1500)
+    _parity(wl, mode)
+
+
 @pytest.mark.parametrize("kind", [pn.CELL_TANH_RNN, pn.CELL_GRU])
 def test_matrix_cells_wide_input(kind):
     # weights too large to stage in LDS: the kernels read them from global memory
@@ -326,6 +407,12 @@ def test_cfg2_full_picard_outcome():
 @pytest.mark.slow
 def test_cfg4_full_newton():
     _parity(_case(4), N)
+
+
+@pytest.mark.slow
+def test_cfg7_full_picard_advancing():
+    wl = _case(7)
+    _parity(wl, P)
 
 
 @pytest.mark.slow

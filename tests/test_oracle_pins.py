@@ -543,6 +543,17 @@ def test_advancing_window_hand_traced_jacobi_case():
     assert r.status == oracle.OK and r.iters == 3 and r.window_iters == [3]
     np.testing.assert_array_equal(r.s[0, :, 0], [1.0, 1.5, 1.75])
     np.testing.assert_array_equal(r.hist[0], [1.0, 0.5, 0.25, 0.0])
+    assert r.accepted == [0, 1, 1, 1]
+    # forcing the same decisions reproduces the run; forcing fewer acceptances
+    # costs updates but reaches the same trajectory
+    f = oracle.solve_advancing(cell, x, np.zeros((1, 1)), oracle.JACOBI, 0.0, 100, 2,
+                               force_accept=[0, 1, 1, 1], keep_round_resid=True)
+    np.testing.assert_array_equal(f.s, r.s)
+    assert [list(v) for v in f.round_resid] == [[1.0, 1.0], [0.0, 0.5], [0.0, 0.25], [0.0]]
+    g = oracle.solve_advancing(cell, x, np.zeros((1, 1)), oracle.JACOBI, 0.0, 100, 2,
+                               force_accept=[0, 0, 1, 1, 1])
+    assert g.iters == 4 and g.accepted == [0, 0, 1, 1, 1]
+    np.testing.assert_array_equal(g.s, r.s)
 
 
 @pytest.mark.parametrize("T, W", [(10, 3), (12, 4), (7, 7), (5, 9)])
