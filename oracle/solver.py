@@ -31,6 +31,12 @@ Readings where the article is silent (documented alongside the build):
   * windows are consecutive, non-overlapping blocks of W steps, each solved
     from its own initial state, which is the last state of the previous
     window [PN §1.3.1, §2.3];
+  * residual-driven switching [PN §5.3]: a solve may start with a coarse
+    approximation and change to a better one when the residual curve
+    stagnates.  Read as: at each check i >= 1 of a window, while still on the
+    first mode, r_i > rho * r_{i-1} switches the window to the second mode
+    from update i+1 on (update i, which follows check i, keeps the first
+    mode); each window starts on the first mode;
   * the advancing window (``solve_advancing``) is the sliding window of
     [PN §1.3.1] read as: a window of W steps starts at the first step not yet
     accepted; after each check the leading steps of the window whose residual
@@ -138,14 +144,17 @@ class SolveResult:
     window_status: list = field(default_factory=list)
     hist: list = field(default_factory=list)           # per window: [r_0, ..., r_K]
     accepted: list = field(default_factory=list)       # advancing window: steps accepted per check
+    window_switch: list = field(default_factory=list)  # per window: check that switched modes, or -1
     round_resid: list = field(default_factory=list)    # advancing window: r_t per check, on request
 
 
-def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force, bandwidth):
+def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force, bandwidth, switch=None):
+    """One window.  ``switch`` = (second mode, rho, forced check or None)."""
     B, T = x.shape[0], x.shape[1]
     s = np.broadcast_to(np.asarray(s0, dtype=cell.dtype)[:, None, :], (B, T, cell.D)).copy()
     hist = []
     i = 0
+    sw = -1                 # check at which the window switched modes
     while True:
         p = shift(s, s0)
         v = cell.f(p, x)
@@ -153,15 +162,20 @@ def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force, bandwidth):
         hist.append(r)
         if force is None:
             if not np.isfinite(r):
-                return s, i, NONFINITE, hist
+                return s, i, NONFINITE, hist, sw
             if r <= tol:
-                return s, i, OK, hist
+                return s, i, OK, hist, sw
             if i == max_iter:
-                return s, i, NOT_CONVERGED, hist
+                return s, i, NOT_CONVERGED, hist, sw
         elif i == force:
             status = NONFINITE if not np.isfinite(r) else (OK if r <= tol else NOT_CONVERGED)
-            return s, i, status, hist
-        A = jacobian_approx(mode, cell, p, x, bandwidth)
+            return s, i, status, hist, sw
+        if switch is not None and sw < 0 and i >= 1:
+            mode2, rho, forced = switch
+            if (forced == i) if forced is not None else (r > rho * hist[-2]):
+                sw = i
+        use = switch[0] if (switch is not None and 0 <= sw < i) else mode
+        A = jacobian_approx(use, cell, p, x, bandwidth)
         s_hat = affine_recurrence(v, p, A, s0)
         if damping == 1.0:
             s = s_hat
@@ -171,7 +185,8 @@ def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force, bandwidth):
 
 
 def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
-          dtype=np.float64, force_iters=None, bandwidth=1):
+          dtype=np.float64, force_iters=None, bandwidth=1, switch_mode=None, switch_ratio=0.5,
+          force_switch=None):
     """Parallel-in-time fixed-point solve, evaluated sequentially.
 
     kind/params follow the flat layout of ``make_cell``; x: [B, T, m];
@@ -180,7 +195,9 @@ def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
     (one count per window) replaces the stop rule by a fixed number of
     updates; it is used to follow a run whose stopping decision landed inside
     the floating-point ambiguity band of the tolerance.  ``bandwidth`` is the
-    half-bandwidth k of the banded mode.
+    half-bandwidth k of the banded mode.  ``switch_mode`` (with
+    ``switch_ratio`` rho) turns on residual-driven switching; ``force_switch``
+    (one check index or -1 per window) replaces its decisions.
     """
     x = np.asarray(x)
     s0 = np.asarray(s0)
@@ -198,8 +215,13 @@ def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
     while w0 < T or (T == 0 and wi == 0):
         w1 = min(T, w0 + W)
         force = None if force_iters is None else int(force_iters[wi])
-        s, K, st, hist = _solve_window(cell, xc[:, w0:w1], s_init, mode, tol, max_iter,
-                                       damping, force, bandwidth)
+        switch = None
+        if switch_mode is not None:
+            fs = None if force_switch is None else int(force_switch[wi])
+            switch = (switch_mode, switch_ratio, fs if fs is None or fs >= 0 else 10 ** 9)
+        s, K, st, hist, sw = _solve_window(cell, xc[:, w0:w1], s_init, mode, tol, max_iter,
+                                           damping, force, bandwidth, switch)
+        res.window_switch.append(sw)
         out[:, w0:w1] = s
         res.iters += K
         res.window_iters.append(K)

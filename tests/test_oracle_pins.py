@@ -511,6 +511,58 @@ def test_windows_chain_and_full_window_is_identical():
                                win.s) <= 1e-7
 
 
+# ---------------------------------------------------------------- switching [PN §5.3]
+
+def test_switching_replays_the_mode_sequence_by_hand():
+    # rho = 0 switches at check 1: updates 0 and 1 use the first mode, the rest
+    # the second; the run equals those updates applied one by one
+    wl = workloads.make(2, B=2, T=64)
+    cell = oracle.make_cell(wl["cell"], wl["params"], wl["D"], wl["m"])
+    x, s0 = wl["x"].astype(np.float64), wl["s0"].astype(np.float64)
+    r = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], oracle.QUASI_NEWTON, 1e-9, 64,
+                     switch_mode=oracle.NEWTON, switch_ratio=0.0)
+    assert r.status == oracle.OK and r.window_switch == [1]
+    s = np.broadcast_to(s0[:, None], x.shape[:2] + (wl["D"],)).copy()
+    for k in range(r.iters):
+        s = oracle.newton_step(cell, x, s0, s, oracle.QUASI_NEWTON if k <= 1 else oracle.NEWTON)
+    np.testing.assert_array_equal(r.s, s)
+    # rho = inf never switches: the plain first-mode solve
+    q = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], oracle.QUASI_NEWTON, 1e-9, 64)
+    n = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], oracle.QUASI_NEWTON, 1e-9, 64,
+                     switch_mode=oracle.NEWTON, switch_ratio=np.inf)
+    assert n.window_switch == [-1] and n.iters == q.iters
+    np.testing.assert_array_equal(n.s, q.s)
+    # forcing the decision reproduces it; forcing "never" is the plain solve
+    f = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], oracle.QUASI_NEWTON, 1e-9, 64,
+                     switch_mode=oracle.NEWTON, switch_ratio=0.0, force_switch=[1])
+    np.testing.assert_array_equal(f.s, r.s)
+    g = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], oracle.QUASI_NEWTON, 1e-9, 64,
+                     switch_mode=oracle.NEWTON, switch_ratio=0.0, force_switch=[-1])
+    np.testing.assert_array_equal(g.s, q.s)
+
+
+def test_switching_on_stagnation_saves_fine_updates():
+    # the lattice workload: the first diagonal updates stall (r grows), the
+    # switch moves to the band, which then converges like the band alone
+    wl = workloads.make(6, B=2, T=512)
+    args = (wl["cell"], wl["params"], wl["x"], wl["s0"])
+    b = oracle.solve(*args, oracle.BANDED, 1e-6, 512, bandwidth=2)
+    a = oracle.solve(*args, oracle.QUASI_NEWTON, 1e-6, 512, bandwidth=2,
+                     switch_mode=oracle.BANDED, switch_ratio=0.5)
+    assert a.status == b.status == oracle.OK
+    sw = a.window_switch[0]
+    assert sw >= 1 and a.hist[0][sw] > 0.5 * a.hist[0][sw - 1]
+    assert all(a.hist[0][k] <= 0.5 * a.hist[0][k - 1] for k in range(1, sw))
+    assert a.iters - (sw + 1) < b.iters          # fewer updates in the costly mode
+    cell = oracle.make_cell(wl["cell"], wl["params"], wl["D"], wl["m"])
+    np.testing.assert_allclose(a.s, oracle.sequential(cell, wl["x"].astype(np.float64),
+                                                      wl["s0"].astype(np.float64)), atol=1e-5)
+    # every window starts on the first mode
+    w = oracle.solve(*args, oracle.QUASI_NEWTON, 1e-6, 128, window=128, bandwidth=2,
+                     switch_mode=oracle.BANDED, switch_ratio=0.5)
+    assert len(w.window_switch) == 4 and all(k >= 1 for k in w.window_switch)
+
+
 # ---------------------------------------------------------------- advancing window [PN §1.3.1]
 
 class _Affine:
