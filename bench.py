@@ -62,7 +62,7 @@ def _traffic(name, src, launch_bytes_alg):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, mode):
+def cpu_baseline(cfg, mode, switch_mode=-1, switch_ratio=0.5):
     """The float64 oracle on a bounded sample of the workload, one thread."""
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -86,7 +86,9 @@ def cpu_baseline(cfg, mode):
                                        wl["window"], wl["damping"], wl["bandwidth"])
         else:
             r = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], mode, wl["tol"],
-                             wl["max_iter"], wl["damping"], wl["window"], bandwidth=wl["bandwidth"])
+                             wl["max_iter"], wl["damping"], wl["window"], bandwidth=wl["bandwidth"],
+                             switch_mode=switch_mode if switch_mode >= 0 else None,
+                             switch_ratio=switch_ratio)
         el = time.perf_counter() - t0
     n = wl["B"] * wl["T"] * wl["D"]
     return {"value": n / el, "unit": "state-updates/s", "cores": 1, "kind": "oracle",
@@ -175,6 +177,9 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--mode", default=None)
     ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--switch", default=None,
+                    help="residual-driven switching: the mode each window moves to on a stall")
+    ap.add_argument("--switch-ratio", type=float, default=0.5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 256 MiB device copy first (counter calibration)")
@@ -201,15 +206,18 @@ def main():
     params, x, s0 = (torch.from_numpy(wl[k]).to(dev) for k in ("params", "x", "s0"))
     out = torch.empty((wl["B"], wl["T"], wl["D"]), dtype=torch.float32, device=dev)
     wmode = pn.WINDOW_ADVANCING if wl["window_mode"] == "advancing" else pn.WINDOW_CONSECUTIVE
+    smode = MODES[args.switch] if args.switch else -1
     nbytes = pn.workspace_bytes(wl["cell"], wl["m"], wl["B"], wl["T"], wl["D"], mode,
-                                wl["damping"], wl["window"], args.chunk, wl["bandwidth"], wmode)
+                                wl["damping"], wl["window"], args.chunk, wl["bandwidth"], wmode,
+                                smode)
     ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
 
     def solve(profile):
         return pn.eval(wl["cell"], params, x, s0, mode=mode, tol=wl["tol"],
                        max_iter=wl["max_iter"], damping=wl["damping"], window=wl["window"],
                        chunk=args.chunk, out=out, workspace=ws, profile=profile,
-                       bandwidth=wl["bandwidth"], window_mode=wmode)
+                       bandwidth=wl["bandwidth"], window_mode=wmode, switch_mode=smode,
+                       switch_ratio=args.switch_ratio)
 
     if args.copy_probe:
         n = 64 * 1024 * 1024
@@ -239,14 +247,17 @@ def main():
     bytes_per_launch = apply_bytes / max(apply_launches, 1)
     gbs = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9 if avg_launch_ms > 0 else 0.0
     name = f"{wl['name']}_{workloads.MODE_NAMES[mode]}"
-    src = _kernel_source(wl, mode)
+    if smode >= 0:
+        name += f"_to_{workloads.MODE_NAMES[smode]}"
+    src = _kernel_source(wl, smode if smode >= 0 else mode)
     # bound by arithmetic intensity of the kernel against the FP32 ridge point
     flops_per_launch = apply_flops / max(apply_launches, 1)
     if flops_per_launch > bytes_per_launch * (FP32_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9):
         tf = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
         # the dense modes outside the matrix-core kernel compose on the vector
         # ALUs (FP32 vector and matrix peaks are both 157.3 TFLOP/s on MI355X)
-        dense = mode == 3 or (mode == 4 and 0 < wl["bandwidth"] < wl["D"] - 1)
+        fine = smode if smode >= 0 else mode
+        dense = fine == 3 or (fine == 4 and 0 < wl["bandwidth"] < wl["D"] - 1)
         unit = "alu" if dense and src == KERNEL_SOURCES[wl["cell"]] else "mfma"
         roof = {"bound": unit, "achieved": tf, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": tf / FP32_PEAK_TFLOPS, "traffic": _traffic(name, src, bytes_per_launch)}
@@ -265,13 +276,15 @@ def main():
                    "D": wl["D"], "m": wl["m"], "mode": workloads.MODE_NAMES[mode],
                    "tol": wl["tol"], "damping": wl["damping"], "window": wl["window"],
                    **({"window_mode": "advancing"} if wmode else {}),
-                   **({"bandwidth": wl["bandwidth"]} if mode == 4 else {}),
+                   **({"bandwidth": wl["bandwidth"]} if 4 in (mode, smode) else {}),
+                   **({"switch_to": workloads.MODE_NAMES[smode], "switch_ratio": args.switch_ratio,
+                       "window_switch_first": last.window_switch[:4]} if smode >= 0 else {}),
                    "iters": last.iters, "window_iters_first": last.window_iters[:4],
                    "status": last.status, "parallelism": "single GPU"},
         "roofline": roof,
     }
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(args.config, mode)
+        line["cpu_baseline"] = cpu_baseline(args.config, mode, smode, args.switch_ratio)
     print(json.dumps(line), flush=True)
 
 

@@ -136,7 +136,22 @@ typedef struct pn_opts {
                                  check with a finite residual, in order
                                  (truncated to accepted_len)                   */
     int64_t accepted_len;
+    int32_t switch_mode;      /* -1 (default): off; else the mode a window
+                                 moves to when its residual stalls (below)     */
+    float switch_ratio;       /* rho >= 0 of the stall test (default 0.5)      */
+    int32_t* window_switch;   /* host; per window: the check that switched, or
+                                 -1 (truncated to window_switch_len)           */
+    int64_t window_switch_len;
 } pn_opts;
+
+/* Residual-driven switching [PN §5.3]: start each window on the coarse
+ * approximation `mode` and move to `switch_mode` once the residual stalls.
+ * At each check i >= 1 of a window still on `mode`, r_i > switch_ratio *
+ * r_{i-1} switches it: update i (already under way) keeps `mode`, updates
+ * i+1, ... use `switch_mode` (its chunk maps are rebuilt at s^(i+1) by one
+ * extra sweep).  Matrix cells with consecutive windows only (PN_EUNSUPPORTED
+ * otherwise).  A typical use is quasi-Newton first, then the banded or full
+ * Jacobian. */
 
 /* pn_opts.window_mode.
  * PN_WINDOW_CONSECUTIVE: windows of W steps solved one after another, each
@@ -166,7 +181,7 @@ enum { PN_WINDOW_CONSECUTIVE = 0, PN_WINDOW_ADVANCING = 1 };
 enum { PN_FLAG_PERSISTENT = 1 };
 
 /* Fill *o with the defaults: damping 1, chunk 0, window 0, bandwidth 1,
- * everything else NULL / 0. */
+ * switch_mode -1, switch_ratio 0.5, everything else NULL / 0. */
 void pn_opts_init(pn_opts* o);
 
 /* Solve the recurrence for all B sequences [PN §1.1, §1.2].

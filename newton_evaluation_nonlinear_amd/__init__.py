@@ -55,7 +55,10 @@ class Opts(ctypes.Structure):
                 ("profile", ctypes.POINTER(Profile)),
                 ("flags", ctypes.c_int32), ("bandwidth", ctypes.c_int32),
                 ("window_mode", ctypes.c_int32),
-                ("accepted", ctypes.POINTER(ctypes.c_int32)), ("accepted_len", ctypes.c_int64)]
+                ("accepted", ctypes.POINTER(ctypes.c_int32)), ("accepted_len", ctypes.c_int64),
+                ("switch_mode", ctypes.c_int32), ("switch_ratio", ctypes.c_float),
+                ("window_switch", ctypes.POINTER(ctypes.c_int32)),
+                ("window_switch_len", ctypes.c_int64)]
 
 
 _lib = None
@@ -114,7 +117,7 @@ def _stream_ptr(device):
 
 
 def make_opts(damping=1.0, window=0, chunk=0, stream=None, flags=0, bandwidth=1,
-              window_mode=WINDOW_CONSECUTIVE):
+              window_mode=WINDOW_CONSECUTIVE, switch_mode=-1, switch_ratio=0.5):
     o = Opts()
     lib().pn_opts_init(ctypes.byref(o))
     o.damping = float(damping)
@@ -124,12 +127,15 @@ def make_opts(damping=1.0, window=0, chunk=0, stream=None, flags=0, bandwidth=1,
     o.flags = int(flags)
     o.bandwidth = int(bandwidth)
     o.window_mode = int(window_mode)
+    o.switch_mode = int(switch_mode)
+    o.switch_ratio = float(switch_ratio)
     return o
 
 
 def workspace_bytes(cell_kind, input_dim, B, T, D, mode, damping=1.0, window=0, chunk=0,
-                    bandwidth=1, window_mode=WINDOW_CONSECUTIVE):
-    o = make_opts(damping, window, chunk, bandwidth=bandwidth, window_mode=window_mode)
+                    bandwidth=1, window_mode=WINDOW_CONSECUTIVE, switch_mode=-1):
+    o = make_opts(damping, window, chunk, bandwidth=bandwidth, window_mode=window_mode,
+                  switch_mode=switch_mode)
     c = Cell(cell_kind, input_dim)
     n = lib().pn_workspace_bytes(ctypes.byref(c), B, T, D, mode, ctypes.byref(o))
     if n == 0:
@@ -140,10 +146,12 @@ def workspace_bytes(cell_kind, input_dim, B, T, D, mode, damping=1.0, window=0, 
 class Result:
     """Outcome of one solve: trajectory, total updates, status and diagnostics."""
 
-    def __init__(self, out, iters, status, window_iters, resid_hist, profile, accepted=None):
+    def __init__(self, out, iters, status, window_iters, resid_hist, profile, accepted=None,
+                 window_switch=None):
         self.out, self.iters, self.status = out, iters, status
         self.window_iters, self.resid_hist, self.profile = window_iters, resid_hist, profile
         self.accepted = accepted     # advancing window: steps accepted per check
+        self.window_switch = window_switch   # switching: per window, the check that switched
 
     def __iter__(self):
         return iter((self.out, self.iters, self.status))
@@ -151,13 +159,15 @@ class Result:
 
 def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, damping=1.0,
          window=0, chunk=0, out=None, history=False, profile=False, workspace=None, flags=0,
-         bandwidth=1, window_mode=WINDOW_CONSECUTIVE):
+         bandwidth=1, window_mode=WINDOW_CONSECUTIVE, switch_mode=-1, switch_ratio=0.5):
     """Solve s_t = f(s_{t-1}, x_t) for t = 1..T over the batch; see include/pn.h.
 
     params, x [B,T,m], s0 [B,D] are float32 tensors on one HIP device.
     ``bandwidth`` is the half-bandwidth k of the BANDED mode; ``window_mode``
     WINDOW_ADVANCING slides one window past its converged prefix (max_iter
-    then defaults to T and caps the updates of the whole solve).
+    then defaults to T and caps the updates of the whole solve); ``switch_mode``
+    >= 0 moves each window to that mode when its residual stalls
+    (r_i > switch_ratio * r_{i-1}).
     Returns a ``Result`` (unpacks as ``out, iters, status``).  Negative
     library statuses raise ``PnError``.
     """
@@ -173,7 +183,8 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     if out is None:
         out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
     c = Cell(int(cell_kind), int(m))
-    o = make_opts(damping, window or 0, chunk, _stream_ptr(dev), flags, bandwidth, window_mode)
+    o = make_opts(damping, window or 0, chunk, _stream_ptr(dev), flags, bandwidth, window_mode,
+                  switch_mode, switch_ratio)
     nbytes = lib().pn_workspace_bytes(ctypes.byref(c), B, T, D, int(mode), ctypes.byref(o))
     if nbytes == 0:
         raise PnError(EINVAL, last_error())
@@ -187,6 +198,9 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     wit = (ctypes.c_int32 * nwin)()
     o.window_iters = wit
     o.window_iters_len = nwin
+    wsw = (ctypes.c_int32 * nwin)(*([-1] * nwin))
+    o.window_switch = wsw
+    o.window_switch_len = nwin
     hist = None
     if history:
         hlen = min(nwin * (int(max_iter) + 1), 1 << 22)
@@ -221,7 +235,8 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
         accepted = list(acc[:min(len(rh or []), len(acc))])
         if rc == NONFINITE:
             accepted = accepted[:-1]
-    return Result(out, int(iters.value), int(rc), witer, rh, pd, accepted)
+    wswitch = list(wsw)[:len(witer)] if int(switch_mode) >= 0 else None
+    return Result(out, int(iters.value), int(rc), witer, rh, pd, accepted, wswitch)
 
 
 def affine_scan(A, b, s0, dense=False, chunk=0, out=None):

@@ -73,6 +73,8 @@ struct Plan {
     size_t off_sync, off_winfo, off_hist;
 };
 
+void layout(Plan& p, const Plan* other);
+
 int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int32_t mode,
               const pn_opts* o) {
     p.kind = cell->kind;
@@ -155,12 +157,27 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
     p.persist_ok = p.matrix_cell && !p.dense && !p.advancing &&
                    cell_persist_eligible(p.kind, p.DP, p.L, p.m);
     p.hist_cap = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(p.nwin) * (p.W + 1), 1 << 16));
-    const size_t bnd = static_cast<size_t>(p.B) * p.NC * p.D;
+    layout(p, nullptr);
+    return PN_OK;
+}
+
+// Workspace offsets of a plan; with `other`, every shared region is sized for
+// both plans (a solve that switches modes runs both on one workspace).
+void layout(Plan& p, const Plan* other) {
+    size_t nparts = p.nblocks;
+    size_t bnd = static_cast<size_t>(p.B) * p.NC * p.D;
+    size_t nA = bnd * (p.dense ? p.D : 1);
+    if (other) {
+        const size_t ob = static_cast<size_t>(other->B) * other->NC * other->D;
+        nparts = std::max<size_t>(nparts, other->nblocks);
+        nA = std::max(nA, ob * (other->dense ? other->D : 1));
+        bnd = std::max(bnd, ob);
+    }
     size_t off = 0;
     p.off_ctrl = off; off = align_up(off + sizeof(Ctrl));
-    p.off_rpart = off; off = align_up(off + sizeof(uint32_t) * p.nblocks);
-    p.off_fpart = off; off = align_up(off + sizeof(uint32_t) * p.nblocks);
-    p.off_aggA = off; off = align_up(off + sizeof(float) * bnd * (p.dense ? p.D : 1));
+    p.off_rpart = off; off = align_up(off + sizeof(uint32_t) * nparts);
+    p.off_fpart = off; off = align_up(off + sizeof(uint32_t) * nparts);
+    p.off_aggA = off; off = align_up(off + sizeof(float) * nA);
     p.off_aggB = off; off = align_up(off + sizeof(float) * bnd);
     p.off_carry = off; off = align_up(off + sizeof(float) * bnd);
     p.off_halo = off; off = align_up(off + sizeof(float) * 2 * bnd);
@@ -173,6 +190,21 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
         p.off_hist = off; off = align_up(off + sizeof(float) * p.hist_cap);
     }
     p.total = off;
+}
+
+// The plan of the first mode and, when the options ask for residual-driven
+// switching, the plan of the second, laid out on one workspace.
+int make_plans(Plan& p, Plan& p2, bool* has2, const pn_cell* cell, int64_t B, int64_t T, int64_t D,
+               int32_t mode, const pn_opts* o) {
+    int rc = make_plan(p, cell, B, T, D, mode, o);
+    if (rc != PN_OK) return rc;
+    *has2 = o && o->switch_mode >= 0;
+    if (!*has2) return PN_OK;
+    rc = make_plan(p2, cell, B, T, D, o->switch_mode, o);
+    if (rc != PN_OK) return rc;
+    p.persist_ok = p2.persist_ok = false;
+    layout(p, &p2);
+    layout(p2, &p);
     return PN_OK;
 }
 
@@ -207,6 +239,19 @@ int validate(const pn_cell* cell, const float* params, const float* x, const flo
             return fail(PN_EINVAL, "unknown window_mode %d", o->window_mode);
         if (o->window_mode == PN_WINDOW_ADVANCING && cell->kind == PN_CELL_DIAG_TANH)
             return fail(PN_EUNSUPPORTED, "the advancing window supports the matrix cells only");
+        if (o->switch_mode < -1 || o->switch_mode > PN_BANDED)
+            return fail(PN_EINVAL, "unknown switch_mode %d", o->switch_mode);
+        if (o->switch_mode >= 0) {
+            if (!(o->switch_ratio >= 0.0f)) return fail(PN_EINVAL, "switch_ratio must be >= 0");
+            if (o->switch_mode == PN_BANDED && o->bandwidth < 0)
+                return fail(PN_EINVAL, "bandwidth must be >= 0");
+            if (cell->kind == PN_CELL_DIAG_TANH)
+                return fail(PN_EUNSUPPORTED, "mode switching supports the matrix cells only");
+            if (o->window_mode == PN_WINDOW_ADVANCING)
+                return fail(PN_EUNSUPPORTED, "mode switching and the advancing window do not combine");
+        }
+        if (o->window_switch_len < 0 || (o->window_switch_len > 0 && !o->window_switch))
+            return fail(PN_EINVAL, "window_switch is NULL or its length negative");
     }
     if (B == 0 || T == 0 || D == 0) return PN_OK;
     if (!params || !x || !s0 || !out) return fail(PN_EINVAL, "a device pointer is NULL");
@@ -300,6 +345,7 @@ struct SolveCtx {
     int32_t max_iter;
     Timing* tm;
     std::vector<float>* hist;
+    float ratio;             // switch_ratio (residual-driven switching)
 };
 
 double apply_bytes(const Plan& p, int Tw, bool first) {
@@ -336,60 +382,75 @@ int record(SolveCtx& c, size_t* idx) {
     return PN_OK;
 }
 
-// Solve one window.  Writes *K (updates) and *status.
+// Solve one window.  Writes *K (updates) and *status.  With p2 (residual-
+// driven switching [PN §5.3]), the window starts on plan p and, at the first
+// check i >= 1 with r_i > ratio * r_{i-1}, moves to p2 from update i+1 on
+// (apply(i) is already enqueued): the chunk maps of p2's mode are rebuilt at
+// s^(i+1) by a maps pass, then the loop continues on p2.  *sw receives that
+// check, or -1.
 int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, const float* s0,
-                 int64_t s0s, int Tw, int* K, int* status) {
-    const Plan& p = *c.p;
-    const int NC = (Tw + p.L - 1) / p.L;
-    Ctrl* ctrl = reinterpret_cast<Ctrl*>(c.ws + p.off_ctrl);
-    uint32_t* rpart = reinterpret_cast<uint32_t*>(c.ws + p.off_rpart);
-    float* aggA = reinterpret_cast<float*>(c.ws + p.off_aggA);
-    float* aggB = reinterpret_cast<float*>(c.ws + p.off_aggB);
-    float* carry = reinterpret_cast<float*>(c.ws + p.off_carry);
-    float* halo = reinterpret_cast<float*>(c.ws + p.off_halo);
-    const float* w = reinterpret_cast<const float*>(c.ws + p.off_w);
+                 int64_t s0s, int Tw, int* K, int* status, const Plan* p2, int* sw) {
+    const Plan* pp = c.p;
+    Ctrl* ctrl = reinterpret_cast<Ctrl*>(c.ws + pp->off_ctrl);
+    uint32_t* rpart = reinterpret_cast<uint32_t*>(c.ws + pp->off_rpart);
+    float* aggA = reinterpret_cast<float*>(c.ws + pp->off_aggA);
+    float* aggB = reinterpret_cast<float*>(c.ws + pp->off_aggB);
+    float* carry = reinterpret_cast<float*>(c.ws + pp->off_carry);
+    float* halo = reinterpret_cast<float*>(c.ws + pp->off_halo);
+    const float* w = reinterpret_cast<const float*>(c.ws + pp->off_w);
 
     DiagArgs da{};
     CellArgs ca{};
-    int nblocks;
-    if (!p.matrix_cell) {
-        da.a = c.params; da.x = x; da.xs = xs; da.s = s; da.ss = ss; da.s0 = s0; da.s0s = s0s;
-        da.B = p.B; da.Tw = Tw; da.D = p.D; da.L = p.L; da.NC = NC; da.cpb = p.cpb;
-        da.aggA = aggA; da.aggB = aggB; da.carry = carry; da.halo = halo; da.rpart = rpart;
-        da.ctrl = ctrl; da.mode = p.mode; da.lam = c.lam; da.undamped = c.lam == 1.0f;
-        nblocks = diag_tanh_nblocks(da);
-    } else {
-        ca.w = w; ca.x = x; ca.xs = xs; ca.s = s; ca.ss = ss; ca.s0 = s0; ca.s0s = s0s;
-        ca.B = p.B; ca.Tw = Tw; ca.D = p.D; ca.m = p.m; ca.L = p.L; ca.NC = NC;
-        ca.aggA = aggA; ca.aggB = aggB; ca.carry = carry; ca.halo = halo; ca.rpart = rpart;
-        ca.ctrl = ctrl; ca.mode = p.mode; ca.lam = c.lam; ca.undamped = c.lam == 1.0f;
-        ca.band = p.band;
-        nblocks = cell_pass_nblocks(ca);
-    }
-    auto launch_pass = [&](int phase, int iter) -> hipError_t {
+    CarryArgs cy{};
+    cy.aggA = aggA; cy.aggB = aggB; cy.carry = carry; cy.s0 = s0; cy.s0s = s0s;
+    cy.B = pp->B; cy.D = pp->D; cy.do_check = 1;
+    cy.chk.rpart = rpart; cy.chk.max_iter = c.max_iter; cy.chk.tol = c.tol;
+    cy.chk.ctrl = ctrl; cy.chk.host = c.res->host_dev;
+    // kernel arguments of the plan in use
+    auto configure = [&](const Plan& p) {
+        const int NC = (Tw + p.L - 1) / p.L;
+        int nblocks;
         if (!p.matrix_cell) {
+            da = DiagArgs{};
+            da.a = c.params; da.x = x; da.xs = xs; da.s = s; da.ss = ss; da.s0 = s0; da.s0s = s0s;
+            da.B = p.B; da.Tw = Tw; da.D = p.D; da.L = p.L; da.NC = NC; da.cpb = p.cpb;
+            da.aggA = aggA; da.aggB = aggB; da.carry = carry; da.halo = halo; da.rpart = rpart;
+            da.ctrl = ctrl; da.mode = p.mode; da.lam = c.lam; da.undamped = c.lam == 1.0f;
+            nblocks = diag_tanh_nblocks(da);
+        } else {
+            ca = CellArgs{};
+            ca.w = w; ca.x = x; ca.xs = xs; ca.s = s; ca.ss = ss; ca.s0 = s0; ca.s0s = s0s;
+            ca.B = p.B; ca.Tw = Tw; ca.D = p.D; ca.m = p.m; ca.L = p.L; ca.NC = NC;
+            ca.aggA = aggA; ca.aggB = aggB; ca.carry = carry; ca.halo = halo; ca.rpart = rpart;
+            ca.ctrl = ctrl; ca.mode = p.mode; ca.lam = c.lam; ca.undamped = c.lam == 1.0f;
+            ca.band = p.band;
+            nblocks = cell_pass_nblocks(ca);
+        }
+        cy.NC = NC;
+        cy.chk.nparts = nblocks;
+    };
+    auto launch_pass = [&](int phase, int iter) -> hipError_t {
+        if (!pp->matrix_cell) {
             da.iter = iter;
             return launch_diag_tanh_pass(phase, da, c.st);
         }
         ca.iter = iter;
-        if (p.mfma) return launch_dense_mfma_pass(p.kind, p.DP, phase, ca, c.st);
-        return launch_cell_pass(p.kind, p.DP, p.dense, phase, ca, c.st);
+        if (pp->mfma) return launch_dense_mfma_pass(pp->kind, pp->DP, phase, ca, c.st);
+        return launch_cell_pass(pp->kind, pp->DP, pp->dense, phase, ca, c.st);
     };
 
+    configure(*pp);
+    *sw = -1;
     PN_HIP(launch_pass(kPrologue, 0));
-    CarryArgs cy{};
-    cy.aggA = aggA; cy.aggB = aggB; cy.carry = carry; cy.s0 = s0; cy.s0s = s0s;
-    cy.B = p.B; cy.D = p.D; cy.NC = NC; cy.do_check = 1;
-    cy.chk.rpart = rpart; cy.chk.nparts = nblocks; cy.chk.max_iter = c.max_iter; cy.chk.tol = c.tol;
-    cy.chk.ctrl = ctrl; cy.chk.host = c.res->host_dev;
     volatile HostRec* hr = c.res->host;
     const int32_t epoch = ++c.res->epoch;
     cy.chk.epoch = epoch;
     hr->iter = -1;
+    float r_prev = 0.0f;
     for (int i = 0;; ++i) {
         cy.chk.iter = i;
         size_t e0 = 0, e1 = 0;
-        PN_HIP(p.dense ? launch_dense_carry(cy, c.st) : launch_diag_carry(cy, c.st));
+        PN_HIP(pp->dense ? launch_dense_carry(cy, c.st) : launch_diag_carry(cy, c.st));
         // timing covers the steady-state apply launches (i >= 1), including
         // the final one that exits at once
         const bool timed = c.tm->on && i > 0;
@@ -415,16 +476,24 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
         std::memcpy(&r, &rb, sizeof(r));
         if (c.hist) c.hist->push_back(r);
         if (timed && !stop) {
-            c.tm->apply_bytes.back() = apply_bytes(p, Tw, false);
-            c.tm->apply_flops.back() = apply_flops(p, Tw);
+            c.tm->apply_bytes.back() = apply_bytes(*pp, Tw, false);
+            c.tm->apply_flops.back() = apply_flops(*pp, Tw);
         }
         if (stop) {
             *K = i;
             *status = st;
             break;
         }
+        if (p2 && *sw < 0 && i >= 1 && r > c.ratio * r_prev) {
+            // stagnation: update i runs on the first mode; from i+1 on, p2
+            *sw = i;
+            pp = p2;
+            configure(*pp);
+            PN_HIP(launch_pass(kMaps, i + 1));
+        }
+        r_prev = r;
     }
-    if (*K == 0) PN_HIP(launch_fill(s, ss, s0, s0s, p.B, Tw, p.D, c.st));
+    if (*K == 0) PN_HIP(launch_fill(s, ss, s0, s0s, c.p->B, Tw, c.p->D, c.st));
     return PN_OK;
 }
 
@@ -636,8 +705,9 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
         if (o && o->resid_hist_len > 0) o->resid_hist[0] = 0.0f;
         return PN_OK;
     }
-    Plan p;
-    rc = make_plan(p, cell, B, T, D, mode, o);
+    Plan p, p2;
+    bool has2 = false;
+    rc = make_plans(p, p2, &has2, cell, B, T, D, mode, o);
     if (rc != PN_OK) return rc;
     if (o && o->workspace && o->workspace_bytes < p.total)
         return fail(PN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
@@ -659,14 +729,15 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     Timing tm;
     tm.on = o && o->profile;
     std::vector<float> hist;
-    SolveCtx c{&p, st, ws, res, params, tol, o ? o->damping : 1.0f, max_iter, &tm, &hist};
+    SolveCtx c{&p, st, ws, res, params, tol, o ? o->damping : 1.0f, max_iter, &tm, &hist,
+               o ? o->switch_ratio : 0.0f};
     if (p.matrix_cell)
         PN_HIP(launch_prep_weights(p.kind, params, reinterpret_cast<float*>(ws + p.off_w), p.D, p.DP, p.m, st));
     size_t ev_first = 0;
     if (tm.on) { rc = record(c, &ev_first); if (rc) return rc; }
     int total = 0, overall = PN_OK;
     std::vector<int> wit;
-    std::vector<int32_t> accepted;
+    std::vector<int32_t> accepted, wsw;
     const int64_t m = p.m;
     bool persisted = false;
     if (p.persist_ok && o && (o->flags & PN_FLAG_PERSISTENT)) {
@@ -692,14 +763,15 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
         float* sw = out + w0 * D;
         const float* s0w = w0 == 0 ? s0 : out + (w0 - 1) * D;
         const int64_t s0s = w0 == 0 ? D : T * D;
-        int K = 0, status = PN_OK;
-        rc = solve_window(c, xw, T * m, sw, T * D, s0w, s0s, Tw, &K, &status);
+        int K = 0, status = PN_OK, swi = -1;
+        rc = solve_window(c, xw, T * m, sw, T * D, s0w, s0s, Tw, &K, &status, has2 ? &p2 : nullptr, &swi);
         if (rc != PN_OK) {
             if (own_ws) { (void)hipFreeAsync(ws, st); (void)hipStreamSynchronize(st); }
             return rc;
         }
         total += K;
         wit.push_back(K);
+        wsw.push_back(swi);
         if (status == PN_NONFINITE) { overall = PN_NONFINITE; break; }
         if (status == PN_NOT_CONVERGED) overall = PN_NOT_CONVERGED;
     }
@@ -718,6 +790,8 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
             o->resid_hist[k] = hist[k];
         for (int64_t k = 0; o->accepted && k < o->accepted_len && k < static_cast<int64_t>(accepted.size()); ++k)
             o->accepted[k] = accepted[k];
+        for (int64_t k = 0; o->window_switch && k < o->window_switch_len && k < static_cast<int64_t>(wsw.size()); ++k)
+            o->window_switch[k] = wsw[k];
         if (o->profile) {
             pn_profile* pr = o->profile;
             for (size_t k = 0; k < tm.apply.size(); ++k) {
@@ -745,6 +819,8 @@ void pn_opts_init(pn_opts* o) {
     std::memset(o, 0, sizeof(*o));
     o->damping = 1.0f;
     o->bandwidth = 1;
+    o->switch_mode = -1;
+    o->switch_ratio = 0.5f;
 }
 
 int pn_eval_ex(const pn_cell* cell, const float* params, const float* x, const float* s0, int64_t B,
@@ -767,8 +843,9 @@ size_t pn_workspace_bytes(const pn_cell* cell, int64_t B, int64_t T, int64_t D, 
     int rc = validate(cell, &kDummy, &kDummy, &kDummy, B, T, D, mode, 0.0f, 0, &kDummy, &dummy, opts);
     if (rc != PN_OK) return 0;
     if (B == 0 || T == 0 || D == 0) return kAlign;
-    Plan p;
-    if (make_plan(p, cell, B, T, D, mode, opts) != PN_OK) return 0;
+    Plan p, p2;
+    bool has2 = false;
+    if (make_plans(p, p2, &has2, cell, B, T, D, mode, opts) != PN_OK) return 0;
     return p.total;
 }
 

@@ -52,21 +52,22 @@ def run_gpu(wl, mode, tol=None, max_iter=None, damping=None, window=None, chunk=
                   window=wl["window"] if window is None else window,
                   chunk=chunk, history=history, profile=profile,
                   bandwidth=wl.get("bandwidth", 1),
-                  window_mode=pn.WINDOW_ADVANCING if advancing(wl) else pn.WINDOW_CONSECUTIVE)
+                  window_mode=pn.WINDOW_ADVANCING if advancing(wl) else pn.WINDOW_CONSECUTIVE,
+                  switch_mode=wl.get("switch_mode", -1), switch_ratio=wl.get("switch_ratio", 0.5))
     torch.cuda.synchronize()
     res.out_np = res.out.cpu().numpy()
     return res
 
 
 def run_oracle(wl, mode, tol=None, max_iter=None, damping=None, window=None, dtype=np.float64,
-               force_iters=None, key=None):
+               force_iters=None, key=None, force_switch=None):
     args = dict(tol=wl["tol"] if tol is None else tol,
                 max_iter=wl["max_iter"] if max_iter is None else max_iter,
                 damping=wl["damping"] if damping is None else damping,
                 window=wl["window"] if window is None else window,
                 bandwidth=wl.get("bandwidth", 1))
     ck = None
-    if key is not None and force_iters is None:
+    if key is not None and force_iters is None and force_switch is None:
         ck = (key, mode, dtype, tuple(sorted(args.items())))
         if ck in _oracle_cache:
             return _oracle_cache[ck]
@@ -77,9 +78,12 @@ def run_oracle(wl, mode, tol=None, max_iter=None, damping=None, window=None, dty
         r = oracle.solve_advancing(cell, wl["x"], wl["s0"], mode, args["tol"], args["max_iter"],
                                    args["window"], args["damping"], args["bandwidth"])
     else:
+        sm = wl.get("switch_mode", -1)
         r = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], mode, args["tol"],
                          args["max_iter"], args["damping"], args["window"], dtype=dtype,
-                         force_iters=force_iters, bandwidth=args["bandwidth"])
+                         force_iters=force_iters, bandwidth=args["bandwidth"],
+                         switch_mode=sm if sm >= 0 else None,
+                         switch_ratio=wl.get("switch_ratio", 0.5), force_switch=force_switch)
     if ck is not None:
         _oracle_cache[ck] = r
     return r
@@ -127,6 +131,32 @@ def _counts_within_band(gw, ref, tol):
     return True
 
 
+def _follow_switch(wl, mode, gpu, ref, tol, max_iter, damping, window, msg):
+    """Residual-driven switching: where the library switched at other checks
+    than the oracle, each of its decisions must sit inside the ambiguity band
+    of the stall test r_i > rho r_{i-1} as the oracle, forced to the library's
+    decisions, computes it; the parity checks then run against that forced
+    oracle.  Returns (oracle result, forced decisions or None)."""
+    gsw = list(gpu.window_switch[:len(gpu.window_iters)])
+    if gsw[:len(ref.window_switch)] == ref.window_switch:
+        return ref, None
+    rho = wl.get("switch_ratio", 0.5)
+    forced = run_oracle(wl, mode, tol=tol, max_iter=max_iter, damping=damping, window=window,
+                        force_switch=gsw)
+    finite = forced.s[np.isfinite(forced.s)]
+    scale = max(1.0, float(np.max(np.abs(finite)))) if finite.size else 1.0
+    for w, h in enumerate(forced.hist):
+        sw = gsw[w]
+        last = sw if sw >= 0 else len(h) - 1
+        for k in range(1, last + 1):
+            band = COUNT_BAND * rho * h[k - 1] + 2 * ULP1 * scale
+            if k == sw:
+                assert h[k] >= rho * h[k - 1] - band, f"{msg}: window {w} switched at {k} without a stall"
+            else:
+                assert h[k] <= rho * h[k - 1] + band, f"{msg}: window {w} missed a stall at {k}"
+    return forced, gsw
+
+
 def check_parity(wl, mode, gpu, ref, tol=None, window=None, damping=None, max_iter=None,
                  label=""):
     """Apply the acceptance rules; returns the oracle result the trajectory was compared with."""
@@ -136,6 +166,9 @@ def check_parity(wl, mode, gpu, ref, tol=None, window=None, damping=None, max_it
     max_iter = wl["max_iter"] if max_iter is None else max_iter
     msg = f"{label} mode={mode} gpu(status={gpu.status}, iters={gpu.iters}, win={gpu.window_iters[:8]}) " \
           f"oracle(status={ref.status}, iters={ref.iters}, win={ref.window_iters[:8]})"
+    fsw = None
+    if wl.get("switch_mode", -1) >= 0:
+        ref, fsw = _follow_switch(wl, mode, gpu, ref, tol, max_iter, damping, window, msg)
     assert gpu.status == ref.status, msg
     nw = len(ref.window_iters)
     gw = list(gpu.window_iters[:nw])
@@ -146,12 +179,12 @@ def check_parity(wl, mode, gpu, ref, tol=None, window=None, damping=None, max_it
             # The count differs beyond the tolerance band: take the decision in
             # the library's precision (float32 oracle) as the count reference.
             ref32 = run_oracle(wl, mode, tol=tol, max_iter=max_iter, damping=damping,
-                               window=window, dtype=np.float32)
+                               window=window, dtype=np.float32, force_switch=fsw)
             msg += f" float32-oracle(status={ref32.status}, win={ref32.window_iters[:8]})"
             assert ref32.status == gpu.status, msg
             assert _counts_within_band(gw, ref32, tol), msg
         cmp_ref = run_oracle(wl, mode, tol=tol, max_iter=max_iter, damping=damping, window=window,
-                             force_iters=gw)
+                             force_iters=gw, force_switch=fsw)
     s_ref = cmp_ref.s
     s_gpu = gpu.out_np
     T = wl["x"].shape[1]

@@ -101,6 +101,22 @@ def test_window_mode_checks():
     assert rc == pn.EUNSUPPORTED
 
 
+def test_switch_options():
+    for kw, code in [(dict(switch_mode=7), pn.EINVAL), (dict(switch_mode=pn.NEWTON, switch_ratio=-1.0), pn.EINVAL),
+                     (dict(switch_mode=pn.NEWTON, window_mode=pn.WINDOW_ADVANCING), pn.EUNSUPPORTED)]:
+        rc, _ = _eval_raw(opts=pn.make_opts(**kw))
+        assert rc == code, kw
+    rc, _ = _eval_raw(kind=pn.CELL_DIAG_TANH, m=4, D=4, opts=pn.make_opts(switch_mode=pn.NEWTON))
+    assert rc == pn.EUNSUPPORTED
+    # one workspace holds the regions of both modes
+    nq = pn.workspace_bytes(pn.CELL_GRU, 8, 64, 2048, 16, pn.QUASI_NEWTON)
+    nn = pn.workspace_bytes(pn.CELL_GRU, 8, 64, 2048, 16, pn.NEWTON)
+    ns = pn.workspace_bytes(pn.CELL_GRU, 8, 64, 2048, 16, pn.QUASI_NEWTON, switch_mode=pn.NEWTON)
+    assert ns >= max(nq, nn)
+    o = pn.make_opts()
+    assert o.switch_mode == -1 and abs(o.switch_ratio - 0.5) < 1e-7
+
+
 def test_euler_cell_sizes():
     c = pn.Cell(pn.CELL_EULER_TANH, 3)
     assert pn.lib().pn_workspace_bytes(ctypes.byref(c), 2, 100, 64, pn.NEWTON, None) > 0

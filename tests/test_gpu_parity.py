@@ -286,6 +286,46 @@ def test_cfg7_ode_advancing_small(mode):
     _parity(wl, mode)
 
 
+@pytest.mark.parametrize("kind, D, second", [(pn.CELL_TANH_RNN, 12, N), (pn.CELL_TANH_RNN, 33, pn.BANDED),
+                                             (pn.CELL_GRU, 16, N), (pn.CELL_GRU, 64, N),
+                                             (pn.CELL_EULER_TANH, 32, pn.BANDED)])
+def test_switching_matches_oracle(kind, D, second):
+    # two windows (each starts on quasi-Newton), both dense kernels and the
+    # LDS kernel as the second mode, locally coupled weights
+    rng = np.random.default_rng(700 + D)
+    m, B, T = 3, 2, 300
+    params = (workloads.lattice_cell_params(kind, D, m, rng) if kind != pn.CELL_EULER_TANH
+              else workloads.random_cell_params(kind, D, m, rng, 1.0))
+    wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-5, damping=1.0, window=150,
+              max_iter=150, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32), bandwidth=2,
+              switch_mode=second, switch_ratio=0.5)
+    _parity(wl, Q)
+
+
+def test_switching_limits():
+    # rho = 0 switches at the first check that can (check 1); rho = inf never,
+    # which is the plain first-mode solve bit for bit
+    wl = _case(6, B=2, T=600)
+    wl.update(switch_mode=pn.BANDED, switch_ratio=0.0)
+    g0 = run_gpu(wl, Q)
+    assert g0.window_switch == [1]
+    _parity(wl, Q)
+    wl.update(switch_ratio=float("inf"))
+    gi = run_gpu(wl, Q)
+    assert gi.window_switch == [-1]
+    del wl["switch_mode"]
+    q = run_gpu(wl, Q)
+    assert gi.iters == q.iters
+    np.testing.assert_array_equal(gi.out_np, q.out_np)
+
+
+def test_cfg6_lattice_switching_small():
+    wl = _case(6, B=2, T=700)
+    wl.update(switch_mode=pn.BANDED, switch_ratio=0.5)
+    _parity(wl, Q)
+
+
 @pytest.mark.parametrize("kind", [pn.CELL_TANH_RNN, pn.CELL_GRU])
 def test_matrix_cells_wide_input(kind):
     # weights too large to stage in LDS: the kernels read them from global memory
@@ -413,6 +453,13 @@ def test_cfg4_full_newton():
 def test_cfg7_full_picard_advancing():
     wl = _case(7)
     _parity(wl, P)
+
+
+@pytest.mark.slow
+def test_cfg6_full_switching_to_banded():
+    wl = _case(6)
+    wl.update(switch_mode=pn.BANDED, switch_ratio=0.5)
+    _parity(wl, Q)
 
 
 @pytest.mark.slow
