@@ -37,6 +37,9 @@ Readings where the article is silent (documented alongside the build):
     first mode, r_i > rho * r_{i-1} switches the window to the second mode
     from update i+1 on (update i, which follows check i, keeps the first
     mode); each window starts on the first mode;
+  * reduced-precision storage [PN §2.3, §4.2] (``storage="f16"``): every
+    state the update stores is rounded to nearest-even IEEE binary16 and the
+    iteration continues from the stored states; arithmetic is unchanged;
   * the advancing window (``solve_advancing``) is the sliding window of
     [PN §1.3.1] read as: a window of W steps starts at the first step not yet
     accepted; after each check the leading steps of the window whose residual
@@ -148,7 +151,15 @@ class SolveResult:
     round_resid: list = field(default_factory=list)    # advancing window: r_t per check, on request
 
 
-def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force, bandwidth, switch=None):
+def _stored(s, storage):
+    """The state as a binary16 store would hold it (storage "f16"), else s."""
+    if storage == "f16":
+        return s.astype(np.float16).astype(s.dtype)
+    return s
+
+
+def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force, bandwidth, switch=None,
+                  storage=None):
     """One window.  ``switch`` = (second mode, rho, forced check or None)."""
     B, T = x.shape[0], x.shape[1]
     s = np.broadcast_to(np.asarray(s0, dtype=cell.dtype)[:, None, :], (B, T, cell.D)).copy()
@@ -181,12 +192,13 @@ def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force, bandwidth, s
             s = s_hat
         else:
             s = s + damping * (s_hat - s)
+        s = _stored(s, storage)
         i += 1
 
 
 def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
           dtype=np.float64, force_iters=None, bandwidth=1, switch_mode=None, switch_ratio=0.5,
-          force_switch=None):
+          force_switch=None, storage=None):
     """Parallel-in-time fixed-point solve, evaluated sequentially.
 
     kind/params follow the flat layout of ``make_cell``; x: [B, T, m];
@@ -197,7 +209,9 @@ def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
     the floating-point ambiguity band of the tolerance.  ``bandwidth`` is the
     half-bandwidth k of the banded mode.  ``switch_mode`` (with
     ``switch_ratio`` rho) turns on residual-driven switching; ``force_switch``
-    (one check index or -1 per window) replaces its decisions.
+    (one check index or -1 per window) replaces its decisions.  ``storage``
+    "f16" stores the iterate in binary16 (x must already hold binary16
+    values); the returned trajectory is the stored one.
     """
     x = np.asarray(x)
     s0 = np.asarray(s0)
@@ -220,7 +234,8 @@ def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
             fs = None if force_switch is None else int(force_switch[wi])
             switch = (switch_mode, switch_ratio, fs if fs is None or fs >= 0 else 10 ** 9)
         s, K, st, hist, sw = _solve_window(cell, xc[:, w0:w1], s_init, mode, tol, max_iter,
-                                           damping, force, bandwidth, switch)
+                                           damping, force, bandwidth, switch, storage)
+        s = _stored(s, storage)
         res.window_switch.append(sw)
         out[:, w0:w1] = s
         res.iters += K

@@ -511,6 +511,46 @@ def test_windows_chain_and_full_window_is_identical():
                                win.s) <= 1e-7
 
 
+# ---------------------------------------------------------------- binary16 storage [PN §2.3]
+
+def test_f16_storage_jacobi_reaches_the_stored_sequential_trajectory():
+    # T Jacobi updates (causality) reach the fixed point of the stored map: the
+    # sequence s_t = f16(f(s_{t-1})), evaluated here step by step, bit for bit.
+    # The residual |s_t - f(s_{t-1})| keeps the rounding error, so tol 0 is
+    # never met and the cap stops the solve.
+    wl = workloads.make(3, B=2, T=200)
+    x16 = wl["x"].astype(np.float16).astype(np.float32)
+    cell = oracle.make_cell(wl["cell"], wl["params"], wl["D"], wl["m"])
+    prev = wl["s0"].astype(np.float64)
+    ref = np.empty((2, 200, wl["D"]))
+    for t in range(200):
+        prev = cell.f(prev, x16[:, t].astype(np.float64)).astype(np.float16).astype(np.float64)
+        ref[:, t] = prev
+    r = oracle.solve(wl["cell"], wl["params"], x16, wl["s0"], oracle.JACOBI, 0.0, 200,
+                     storage="f16")
+    assert r.status == oracle.NOT_CONVERGED and r.iters == 200
+    np.testing.assert_array_equal(r.s, ref)
+    assert 0 < r.hist[0][-1] <= 2.0 ** -12      # half a binary16 ulp below 1
+
+
+def test_f16_storage_stores_binary16_and_stays_near_the_float_solution():
+    wl = workloads.make(3, B=2, T=2000)
+    x16 = wl["x"].astype(np.float16).astype(np.float32)
+    h = oracle.solve(wl["cell"], wl["params"], x16, wl["s0"], oracle.QUASI_NEWTON, 1e-3, 2000,
+                     storage="f16")
+    f = oracle.solve(wl["cell"], wl["params"], x16, wl["s0"], oracle.QUASI_NEWTON, 1e-9, 2000)
+    assert h.status == oracle.OK
+    np.testing.assert_array_equal(h.s, h.s.astype(np.float16).astype(np.float64))
+    # the stored fixed point differs from the float one by rounding, damped by
+    # the contraction |a| < 1: a few binary16 ulps (2^-11 below 1)
+    assert np.max(np.abs(h.s - f.s)) <= 8 * 2.0 ** -11
+    # K = 0 returns s0 as stored
+    z = oracle.solve(wl["cell"], wl["params"], x16, wl["s0"] + 0.1, oracle.QUASI_NEWTON, 10.0, 2000,
+                     storage="f16")
+    assert z.iters == 0
+    np.testing.assert_array_equal(z.s[0, 0], (wl["s0"][0] + 0.1).astype(np.float16).astype(np.float64))
+
+
 # ---------------------------------------------------------------- switching [PN §5.3]
 
 def test_switching_replays_the_mode_sequence_by_hand():
