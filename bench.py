@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "converged state-updates/s (B*T*D) per Newton solve; achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+F16_TOL = 1e-3            # residual tolerance with binary16 state storage
 FP32_PEAK_TFLOPS = 157.3
 MODES = {"jacobi": 0, "picard": 1, "qn": 2, "quasi_newton": 2, "newton": 3, "banded": 4}
 KERNEL_SOURCES = {  # source file of the dominant kernel per cell kind
@@ -62,7 +63,7 @@ def _traffic(name, src, launch_bytes_alg):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, mode, switch_mode=-1, switch_ratio=0.5):
+def cpu_baseline(cfg, mode, switch_mode=-1, switch_ratio=0.5, storage=None):
     """The float64 oracle on a bounded sample of the workload, one thread."""
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -78,6 +79,9 @@ def cpu_baseline(cfg, mode, switch_mode=-1, switch_ratio=0.5):
         # through its causality bound), so the sample is shorter in time
         sm = dict(B=16, T=256)
     wl = workloads.make(cfg, **sm)
+    if storage == "f16":
+        wl["tol"] = F16_TOL
+        wl["x"] = wl["x"].astype(np.float16).astype(np.float32)
     with threadpool_limits(1):
         t0 = time.perf_counter()
         if wl["window_mode"] == "advancing":
@@ -88,7 +92,7 @@ def cpu_baseline(cfg, mode, switch_mode=-1, switch_ratio=0.5):
             r = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], mode, wl["tol"],
                              wl["max_iter"], wl["damping"], wl["window"], bandwidth=wl["bandwidth"],
                              switch_mode=switch_mode if switch_mode >= 0 else None,
-                             switch_ratio=switch_ratio)
+                             switch_ratio=switch_ratio, storage=storage)
         el = time.perf_counter() - t0
     n = wl["B"] * wl["T"] * wl["D"]
     return {"value": n / el, "unit": "state-updates/s", "cores": 1, "kind": "oracle",
@@ -118,14 +122,21 @@ def _read_counters(d, counter):
 
 
 def _steady_apply(kernel_name):
-    """True for a steady-state apply launch (phase template argument 2)."""
+    """True for a steady-state apply launch (phase template argument 2), from
+    the demangled name or, where the profiler leaves it mangled, from the
+    integer template arguments (Li<n>E) of the mangled one."""
     import re
     m = re.search(r"\b(diag_tanh_pass|cell_pass|dense_pass)<([^>]*)>", kernel_name)
+    if m:
+        targs = [a.strip() for a in m.group(2).split(",")]
+        pos = {"diag_tanh_pass": 1, "cell_pass": 3, "dense_pass": 2}[m.group(1)]
+        return len(targs) > pos and targs[pos] == "2"
+    m = re.search(r"\d+(diag_tanh_pass|cell_pass|dense_pass)I(.*)", kernel_name)
     if not m:
         return False
-    targs = [a.strip() for a in m.group(2).split(",")]
-    pos = {"diag_tanh_pass": 1, "cell_pass": 3, "dense_pass": 2}[m.group(1)]
-    return len(targs) > pos and targs[pos] == "2"
+    ints = re.findall(r"Li(\d+)E", m.group(2))
+    pos = {"diag_tanh_pass": 1, "cell_pass": 2, "dense_pass": 2}[m.group(1)]
+    return len(ints) > pos and ints[pos] == "2"
 
 
 def summarize_pmc(args, fetch_dir, write_dir):
@@ -137,7 +148,7 @@ def summarize_pmc(args, fetch_dir, write_dir):
     import workloads
     wl = workloads.make(args.config, B=1, T=1)   # names only
     mode = MODES[args.mode] if args.mode else wl["modes"][0]
-    name = f"{wl['name']}_{workloads.MODE_NAMES[mode]}"
+    name = f"{wl['name']}_{workloads.MODE_NAMES[mode]}" + ("_f16" if args.storage == "f16" else "")
     res = {}
     for label, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = _read_counters(d, counter)
@@ -153,7 +164,8 @@ def summarize_pmc(args, fetch_dir, write_dir):
                           launches=len(steady), raw_bytes_per_launch=per,
                           bytes_per_launch=per * scale)
     src = _kernel_source(wl, mode)
-    bargs = f"--config {args.config}" + (f" --mode {args.mode}" if args.mode else "")
+    bargs = f"--config {args.config}" + (f" --mode {args.mode}" if args.mode else "") + \
+        (" --storage f16" if args.storage == "f16" else "")
     cmds = [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- "
             f"python3 bench.py {bargs} --steps 2 --warmup 0 --no-cpu --copy-probe",
             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- "
@@ -180,6 +192,9 @@ def main():
     ap.add_argument("--switch", default=None,
                     help="residual-driven switching: the mode each window moves to on a stall")
     ap.add_argument("--switch-ratio", type=float, default=0.5)
+    ap.add_argument("--storage", choices=("f32", "f16"), default="f32",
+                    help="f16: x and the iterate stored in binary16 (channel-wise cell), "
+                         "float32 arithmetic, tol 1e-3")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 256 MiB device copy first (counter calibration)")
@@ -202,9 +217,15 @@ def main():
 
     wl = workloads.make(args.config)
     mode = MODES[args.mode] if args.mode else wl["modes"][0]
+    half = args.storage == "f16"
+    if half:
+        # binary16 states cannot meet 1e-5: their spacing below 1 is 4.9e-4
+        wl["tol"] = F16_TOL
+        wl["x"] = wl["x"].astype(np.float16)
     dev = torch.device("cuda:0")
     params, x, s0 = (torch.from_numpy(wl[k]).to(dev) for k in ("params", "x", "s0"))
-    out = torch.empty((wl["B"], wl["T"], wl["D"]), dtype=torch.float32, device=dev)
+    out = torch.empty((wl["B"], wl["T"], wl["D"]), dtype=torch.float16 if half else torch.float32,
+                      device=dev)
     wmode = pn.WINDOW_ADVANCING if wl["window_mode"] == "advancing" else pn.WINDOW_CONSECUTIVE
     smode = MODES[args.switch] if args.switch else -1
     nbytes = pn.workspace_bytes(wl["cell"], wl["m"], wl["B"], wl["T"], wl["D"], mode,
@@ -246,7 +267,7 @@ def main():
     avg_launch_ms = apply_ms / max(apply_launches, 1)
     bytes_per_launch = apply_bytes / max(apply_launches, 1)
     gbs = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9 if avg_launch_ms > 0 else 0.0
-    name = f"{wl['name']}_{workloads.MODE_NAMES[mode]}"
+    name = f"{wl['name']}_{workloads.MODE_NAMES[mode]}" + ("_f16" if half else "")
     if smode >= 0:
         name += f"_to_{workloads.MODE_NAMES[smode]}"
     src = _kernel_source(wl, smode if smode >= 0 else mode)
@@ -270,7 +291,8 @@ def main():
     line = {
         "metric": METRIC, "value": value, "unit": "state-updates/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 arithmetic, f16 storage" if half else "f32",
         "data": "synthetic (seeded PCG64 draws, no dataset)",
         "config": {"workload": name, "cell": wl["cell"], "B": wl["B"], "T": wl["T"],
                    "D": wl["D"], "m": wl["m"], "mode": workloads.MODE_NAMES[mode],
@@ -284,7 +306,8 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(args.config, mode, smode, args.switch_ratio)
+        line["cpu_baseline"] = cpu_baseline(args.config, mode, smode, args.switch_ratio,
+                                            "f16" if half else None)
     print(json.dumps(line), flush=True)
 
 

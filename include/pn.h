@@ -205,11 +205,25 @@ int pn_eval_ex(const pn_cell* cell, const float* params, const float* x, const f
                int64_t B, int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter,
                float* out, int32_t* iters_out, const pn_opts* opts);
 
-/* Bytes of workspace pn_eval_ex needs for this problem with these options
- * (uses opts->window and opts->chunk; opts may be NULL).  Returns 0 and sets
+/* Bytes of workspace pn_eval_ex (and pn_eval_f16) needs for this problem
+ * with these options (uses opts->window and opts->chunk; opts may be NULL).  Returns 0 and sets
  * the last error for invalid or unsupported arguments. */
 size_t pn_workspace_bytes(const pn_cell* cell, int64_t B, int64_t T, int64_t D,
                           int32_t mode, const pn_opts* opts);
+
+/* pn_eval_ex with reduced-precision storage [PN §2.3, §4.2]: x and out hold
+ * IEEE binary16 values (device, same shapes and layouts as pn_eval); params
+ * and s0 stay float32 and all arithmetic is float32.  Every stored state is
+ * rounded to nearest-even binary16, and the iteration continues from the
+ * stored (rounded) states, so tol must lie above the binary16 resolution of
+ * the states (about 2.4e-4 for |s| < 1).  Supported for PN_CELL_DIAG_TANH,
+ * solved as one window (opts->window 0 or >= T, consecutive mode);
+ * PN_EUNSUPPORTED otherwise.  With D even, x and out must be 4-byte aligned
+ * (two channels move per access).  pn_workspace_bytes covers this entry
+ * too.  It moves 6 bytes per state element and iteration instead of 12. */
+int pn_eval_f16(const pn_cell* cell, const float* params, const uint16_t* x, const float* s0,
+                int64_t B, int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter,
+                uint16_t* out, int32_t* iters_out, const pn_opts* opts);
 
 /* The scan step alone [PN §2.1]: out_t = A_t out_{t-1} + b_t, out_0 = s0,
  * for t = 1..T.  A is device [B, T, D] (dense = 0: diagonal A_t) or

@@ -25,8 +25,8 @@ EINVAL, EUNSUPPORTED, EHIP, EWORKSPACE = -1, -2, -3, -4
 FLAG_PERSISTENT = 1
 WINDOW_CONSECUTIVE, WINDOW_ADVANCING = 0, 1
 
-EXPORTED = ("pn_opts_init", "pn_eval", "pn_eval_ex", "pn_workspace_bytes", "pn_affine_scan",
-            "pn_affine_scan_workspace_bytes", "pn_last_error", "pn_version")
+EXPORTED = ("pn_opts_init", "pn_eval", "pn_eval_ex", "pn_eval_f16", "pn_workspace_bytes",
+            "pn_affine_scan", "pn_affine_scan_workspace_bytes", "pn_last_error", "pn_version")
 
 
 class PnError(RuntimeError):
@@ -82,6 +82,8 @@ def lib():
         L.pn_eval.restype = ctypes.c_int
         L.pn_eval_ex.argtypes = sig + [ctypes.POINTER(Opts)]
         L.pn_eval_ex.restype = ctypes.c_int
+        L.pn_eval_f16.argtypes = sig + [ctypes.POINTER(Opts)]
+        L.pn_eval_f16.restype = ctypes.c_int
         L.pn_workspace_bytes.argtypes = [ctypes.POINTER(Cell), i64, i64, i64, i32, ctypes.POINTER(Opts)]
         L.pn_workspace_bytes.restype = ctypes.c_size_t
         L.pn_affine_scan.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, ctypes.POINTER(Opts)]
@@ -104,11 +106,11 @@ def last_error():
     return lib().pn_last_error().decode()
 
 
-def _dev_f32(t, name):
+def _dev_f32(t, name, dtype=torch.float32):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA (HIP) torch tensor")
-    if t.dtype != torch.float32 or not t.is_contiguous():
-        raise TypeError(f"{name} must be contiguous float32")
+    if t.dtype != dtype or not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous {dtype}")
     return t.data_ptr()
 
 
@@ -162,7 +164,9 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
          bandwidth=1, window_mode=WINDOW_CONSECUTIVE, switch_mode=-1, switch_ratio=0.5):
     """Solve s_t = f(s_{t-1}, x_t) for t = 1..T over the batch; see include/pn.h.
 
-    params, x [B,T,m], s0 [B,D] are float32 tensors on one HIP device.
+    params, x [B,T,m], s0 [B,D] are float32 tensors on one HIP device; with
+    x in float16 the solve stores x and the iterate in binary16 (pn_eval_f16,
+    channel-wise cell; ``out`` float16).
     ``bandwidth`` is the half-bandwidth k of the BANDED mode; ``window_mode``
     WINDOW_ADVANCING slides one window past its converged prefix (max_iter
     then defaults to T and caps the updates of the whole solve); ``switch_mode``
@@ -180,8 +184,10 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     if max_iter is None:
         max_iter = T if advancing else W
     dev = x.device
+    half = x.dtype == torch.float16
+    sdt = torch.float16 if half else torch.float32
     if out is None:
-        out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+        out = torch.empty((B, T, D), dtype=sdt, device=dev)
     c = Cell(int(cell_kind), int(m))
     o = make_opts(damping, window or 0, chunk, _stream_ptr(dev), flags, bandwidth, window_mode,
                   switch_mode, switch_ratio)
@@ -217,9 +223,10 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     if prof is not None:
         o.profile = ctypes.pointer(prof)
     iters = ctypes.c_int32(0)
-    rc = lib().pn_eval_ex(ctypes.byref(c), _dev_f32(params, "params"), _dev_f32(x, "x"),
-                          _dev_f32(s0, "s0"), B, T, D, int(mode), float(tol), int(max_iter),
-                          _dev_f32(out, "out"), ctypes.byref(iters), ctypes.byref(o))
+    entry = lib().pn_eval_f16 if half else lib().pn_eval_ex
+    rc = entry(ctypes.byref(c), _dev_f32(params, "params"), _dev_f32(x, "x", sdt),
+               _dev_f32(s0, "s0"), B, T, D, int(mode), float(tol), int(max_iter),
+               _dev_f32(out, "out", sdt), ctypes.byref(iters), ctypes.byref(o))
     if rc < 0:
         raise PnError(rc, last_error())
     witer = list(wit)

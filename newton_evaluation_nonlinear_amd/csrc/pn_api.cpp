@@ -67,6 +67,8 @@ struct Plan {
     int DP, cpb;           // padded D (matrix cells), channels per block (diag cell)
     bool dense, matrix_cell, mfma;
     bool advancing;        // one window sliding past its converged prefix
+    bool half;             // x and out in IEEE binary16 (channel-wise cell)
+    int hmode;             // DiagArgs::half of the channel-wise kernel
     bool persist_ok;       // shape allows the one-launch persistent solver
     int nblocks, nwin, hist_cap;
     size_t off_ctrl, off_rpart, off_fpart, off_aggA, off_aggB, off_carry, off_halo, off_w, total;
@@ -76,8 +78,10 @@ struct Plan {
 void layout(Plan& p, const Plan* other);
 
 int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int32_t mode,
-              const pn_opts* o) {
+              const pn_opts* o, bool half = false) {
     p.kind = cell->kind;
+    p.half = half;
+    p.hmode = 0;
     p.D = static_cast<int>(D);
     p.m = cell->input_dim;
     p.matrix_cell = p.kind != PN_CELL_DIAG_TANH;
@@ -99,21 +103,27 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
     p.dense = p.matrix_cell && (mode == PN_NEWTON || mode == PN_BANDED);
     p.mfma = false;
     if (!p.matrix_cell) {
-        p.cpb = std::min(256, ((p.D + 63) / 64) * 64);
+        // binary16 storage moves two adjacent channels per thread when D is even
+        p.hmode = !half ? 0 : (p.D % 2 == 0 ? 2 : 1);
+        const int groups = p.hmode == 2 ? p.D / 2 : p.D;
+        // channel groups per workgroup row: 64, 128 or 256, a divisor of the
+        // workgroup size, so every thread belongs to exactly one (chunk, group)
+        p.cpb = groups <= 64 ? 64 : groups <= 128 ? 128 : 256;
         if (chunk > 0) {
             p.L = chunk;
         } else {
-            // Longest chunk that still leaves about 2^18 threads (B x D x chunks):
-            // the per-iteration carry scan shrinks with the chunk count, while
-            // the apply sweep keeps 2^18 threads x 16 loads in flight.
+            // Longest chunk that still leaves about 2^18 threads (B x channel
+            // groups x chunks): the per-iteration carry scan shrinks with the
+            // chunk count, while the apply sweep keeps 2^18 threads x 16 loads
+            // in flight.
             int64_t L = 16;
-            while (L < 1024 && static_cast<int64_t>(B) * D * ((p.W + 2 * L - 1) / (2 * L)) >= (1 << 18)) L *= 2;
+            while (L < 1024 && static_cast<int64_t>(B) * groups * ((p.W + 2 * L - 1) / (2 * L)) >= (1 << 18)) L *= 2;
             p.L = static_cast<int>(L);
         }
         p.L = static_cast<int>(std::min<int64_t>(p.L, p.W));
         p.NC = static_cast<int>((p.W + p.L - 1) / p.L);
         DiagArgs a{};
-        a.B = p.B; a.D = p.D; a.NC = p.NC; a.cpb = p.cpb;
+        a.B = p.B; a.D = p.D; a.NC = p.NC; a.cpb = p.cpb; a.half = p.hmode;
         p.nblocks = diag_tanh_nblocks(a);
         p.DP = 0;
     } else if (p.dense && (next_pow2(p.D) == 16 || next_pow2(p.D) == 32) &&
@@ -352,7 +362,7 @@ double apply_bytes(const Plan& p, int Tw, bool first) {
     // algorithmic bytes of one apply launch: read x, read s^(i) (not for
     // i = 0, where s^(0) = s0 is implicit), write s^(i+1)
     const double rows = static_cast<double>(p.B) * Tw;
-    return rows * 4.0 * (p.m + (first ? 1 : 2) * p.D);
+    return rows * (p.half ? 2.0 : 4.0) * (p.m + (first ? 1 : 2) * p.D);
 }
 
 double apply_flops(const Plan& p, int Tw) {
@@ -416,6 +426,7 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
             da.B = p.B; da.Tw = Tw; da.D = p.D; da.L = p.L; da.NC = NC; da.cpb = p.cpb;
             da.aggA = aggA; da.aggB = aggB; da.carry = carry; da.halo = halo; da.rpart = rpart;
             da.ctrl = ctrl; da.mode = p.mode; da.lam = c.lam; da.undamped = c.lam == 1.0f;
+            da.half = p.hmode;
             nblocks = diag_tanh_nblocks(da);
         } else {
             ca = CellArgs{};
@@ -493,7 +504,10 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
         }
         r_prev = r;
     }
-    if (*K == 0) PN_HIP(launch_fill(s, ss, s0, s0s, c.p->B, Tw, c.p->D, c.st));
+    if (*K == 0) {
+        if (c.p->half) PN_HIP(launch_fill_half(s, ss, s0, s0s, c.p->B, Tw, c.p->D, c.st));
+        else PN_HIP(launch_fill(s, ss, s0, s0s, c.p->B, Tw, c.p->D, c.st));
+    }
     return PN_OK;
 }
 
@@ -694,10 +708,16 @@ int solve_persistent(SolveCtx& c, const float* x, const float* s0, float* out, i
 
 int eval_impl(const pn_cell* cell, const float* params, const float* x, const float* s0, int64_t B,
               int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter, float* out,
-              int32_t* iters_out, const pn_opts* o) {
+              int32_t* iters_out, const pn_opts* o, bool half = false) {
     g_err.clear();
     int rc = validate(cell, params, x, s0, B, T, D, mode, tol, max_iter, out, iters_out, o);
     if (rc != PN_OK) return rc;
+    if (half) {
+        if (cell->kind != PN_CELL_DIAG_TANH)
+            return fail(PN_EUNSUPPORTED, "binary16 storage supports the channel-wise cell only");
+        if (o && ((o->window > 0 && o->window < T) || o->window_mode != PN_WINDOW_CONSECUTIVE))
+            return fail(PN_EUNSUPPORTED, "binary16 storage solves the whole horizon as one window");
+    }
     if (o && o->profile) std::memset(o->profile, 0, sizeof(pn_profile));
     if (B == 0 || T == 0 || D == 0) {
         *iters_out = 0;
@@ -707,7 +727,8 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     }
     Plan p, p2;
     bool has2 = false;
-    rc = make_plans(p, p2, &has2, cell, B, T, D, mode, o);
+    if (half) rc = make_plan(p, cell, B, T, D, mode, o, true);
+    else rc = make_plans(p, p2, &has2, cell, B, T, D, mode, o);
     if (rc != PN_OK) return rc;
     if (o && o->workspace && o->workspace_bytes < p.total)
         return fail(PN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
@@ -835,6 +856,19 @@ int pn_eval(const pn_cell* cell, const float* params, const float* x, const floa
     return eval_impl(cell, params, x, s0, B, T, D, mode, tol, max_iter, out, iters_out, nullptr);
 }
 
+int pn_eval_f16(const pn_cell* cell, const float* params, const uint16_t* x, const float* s0,
+                int64_t B, int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter,
+                uint16_t* out, int32_t* iters_out, const pn_opts* opts) {
+    // the kernels address x and out in binary16 elements; the float pointer
+    // type below only carries the address
+    if (D % 2 == 0 && ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out)) & 3) != 0) {
+        g_err.clear();
+        return fail(PN_EINVAL, "binary16 x and out must be 4-byte aligned");
+    }
+    return eval_impl(cell, params, reinterpret_cast<const float*>(x), s0, B, T, D, mode, tol, max_iter,
+                     reinterpret_cast<float*>(out), iters_out, opts, true);
+}
+
 size_t pn_workspace_bytes(const pn_cell* cell, int64_t B, int64_t T, int64_t D, int32_t mode,
                           const pn_opts* opts) {
     g_err.clear();
@@ -846,7 +880,13 @@ size_t pn_workspace_bytes(const pn_cell* cell, int64_t B, int64_t T, int64_t D, 
     Plan p, p2;
     bool has2 = false;
     if (make_plans(p, p2, &has2, cell, B, T, D, mode, opts) != PN_OK) return 0;
-    return p.total;
+    size_t total = p.total;
+    if (cell->kind == PN_CELL_DIAG_TANH) {
+        // the same size also serves pn_eval_f16, whose chunking differs
+        Plan h;
+        if (make_plan(h, cell, B, T, D, mode, opts, true) == PN_OK) total = std::max(total, h.total);
+    }
+    return total;
 }
 
 size_t pn_affine_scan_workspace_bytes(int64_t B, int64_t T, int64_t D, int32_t dense,

@@ -16,6 +16,12 @@
 // Layout: lanes run along channels (row-contiguous in [B, T, D]); each thread
 // walks the L steps of its chunk serially, so loads are fully coalesced rows
 // and the recurrence stays in registers.
+//
+// Storage type S: float, or _Float16 for reduced-precision storage of x and
+// of the iterate [PN §2.3, §4.2] (compute stays float32).  With _Float16 every
+// stored state is rounded to nearest-even, and the value a thread carries on
+// to the next step is the rounded one, so the state the next step sees is
+// exactly the stored state.
 
 #include "pn_device.hpp"
 
@@ -26,46 +32,105 @@ namespace pn {
 constexpr int kU = 8;
 constexpr int kUP = 16;   // the prologue only reads x, so it prefetches twice as far
 
-template <int MODE, int PHASE>
+// Storage element of one thread: NCH adjacent channels moved as one access
+// (a float; or two binary16 values in one 4-byte access, so a wave moves as
+// many bytes per load instruction as with float storage).
+template <typename S, int NCH> struct Pack;
+template <> struct Pack<float, 1> { typedef float V; };
+template <> struct Pack<_Float16, 1> { typedef _Float16 V; };
+template <> struct Pack<_Float16, 2> { typedef _Float16 V __attribute__((ext_vector_type(2))); };
+
+template <typename S, int NCH>
+__device__ __forceinline__ void unpack(const typename Pack<S, NCH>::V& v, float (&f)[NCH]) {
+    if constexpr (NCH == 1) {
+        f[0] = static_cast<float>(v);
+    } else {
+        f[0] = static_cast<float>(v.x);
+        f[1] = static_cast<float>(v.y);
+    }
+}
+
+// Round the NCH values to the storage type; f receives the rounded values.
+template <typename S, int NCH>
+__device__ __forceinline__ typename Pack<S, NCH>::V pack(float (&f)[NCH]) {
+    typename Pack<S, NCH>::V v;
+    if constexpr (NCH == 1) {
+        v = static_cast<S>(f[0]);
+        f[0] = static_cast<float>(v);
+    } else {
+        v.x = static_cast<S>(f[0]);
+        v.y = static_cast<S>(f[1]);
+        f[0] = static_cast<float>(v.x);
+        f[1] = static_cast<float>(v.y);
+    }
+    return v;
+}
+
+// float32 value after a round trip through the storage type
+template <typename S>
+__device__ __forceinline__ float stored(float v) {
+    return static_cast<float>(static_cast<S>(v));
+}
+
+template <int MODE, int PHASE, typename S, int NCH, bool UND>
 __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
     if constexpr (PHASE != kPrologue) {
         if (g.ctrl->stop) return;    // uniform over the grid: converged earlier
     }
-    const int cpb = g.cpb;
+    typedef typename Pack<S, NCH>::V V;
+    const int cpb = g.cpb;                           // channel groups per block row
     const int dl = threadIdx.x % cpb;
     const int cl = threadIdx.x / cpb;
-    const int c = blockIdx.x * (kThreads / cpb) + cl;
-    const int d = blockIdx.y * cpb + dl;
+    // cpb is a multiple of 64, so a wavefront lies in one chunk: c, and with
+    // it every row-count test below, is uniform over the wave (scalar)
+    const int c = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / cpb) + cl);
+    const int d = (blockIdx.y * cpb + dl) * NCH;     // first channel of the group
     const int b = blockIdx.z;
     uint32_t rb = 0;
     if (c < g.NC && d < g.D) {
         const int D = g.D;
+        const int DV = D / NCH;                      // row stride in groups
         const int t0 = c * g.L;
         const int n = min(g.L, g.Tw - t0);          // steps in this chunk
-        const float a = g.a[d];
-        const float s0v = g.s0[b * g.s0s + d];
-        const float* xp = g.x + b * g.xs + static_cast<int64_t>(t0) * D + d;
+        float a[NCH], s0v[NCH];
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            a[k] = g.a[d + k];
+            s0v[k] = g.s0[b * g.s0s + d + k];
+        }
+        const V* xp = reinterpret_cast<const V*>(reinterpret_cast<const S*>(g.x) + b * g.xs +
+                                                 static_cast<int64_t>(t0) * D + d);
         const size_t ai = (static_cast<size_t>(b) * g.NC + c) * D + d;
-        float A = 1.0f, Bc = 0.0f;
+        float A[NCH], Bc[NCH];
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            A[k] = 1.0f;
+            Bc[k] = 0.0f;
+        }
         if constexpr (PHASE == kPrologue) {
             // Iteration 0: s^(0)_t = s0 for every t, so p_t = s0 throughout.
-            float xb[kUP];
+            V xb[kUP];
 #pragma unroll
-            for (int u = 0; u < kUP; ++u) xb[u] = u < n ? xp[u * D] : 0.0f;
+            for (int u = 0; u < kUP; ++u) xb[u] = u < n ? xp[u * DV] : V{};
             for (int j = 0; j < n; j += kUP) {
-                const float* xq = xp + static_cast<int64_t>(j) * D;   // row j of the chunk
-                float xn[kUP];
+                const V* xq = xp + static_cast<int64_t>(j) * DV;   // row j of the chunk
+                V xn[kUP];
 #pragma unroll
-                for (int u = 0; u < kUP; ++u) xn[u] = (j + kUP + u < n) ? xq[(kUP + u) * D] : 0.0f;
+                for (int u = 0; u < kUP; ++u) xn[u] = (j + kUP + u < n) ? xq[(kUP + u) * DV] : V{};
 #pragma unroll
                 for (int u = 0; u < kUP; ++u) {
                     if (j + u < n) {
-                        const float v = tanh_f(a * s0v + xb[u]);
-                        rb = max(rb, abs_bits(s0v - v));
-                        const float at = mode_coef<MODE>(a * (1.0f - v * v));
-                        const float bt = v - at * s0v;
-                        A = at * A;
-                        Bc = at * Bc + bt;
+                        float xt[NCH];
+                        unpack<S, NCH>(xb[u], xt);
+#pragma unroll
+                        for (int k = 0; k < NCH; ++k) {
+                            const float v = tanh_f(a[k] * s0v[k] + xt[k]);
+                            rb = max(rb, abs_bits(s0v[k] - v));
+                            const float at = mode_coef<MODE>(a[k] * (1.0f - v * v));
+                            const float bt = v - at * s0v[k];
+                            A[k] = at * A[k];
+                            Bc[k] = at * Bc[k] + bt;
+                        }
                     }
                 }
 #pragma unroll
@@ -73,68 +138,85 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
             }
         } else {
             const size_t HS = static_cast<size_t>(g.B) * g.NC * D;
-            float* sp = g.s + b * g.ss + static_cast<int64_t>(t0) * D + d;
-            // p_old: s^(i) at t0-1 (halo of the previous chunk);  shat: s^ at t0-1.
-            float p_old = (PHASE == kFirst || c == 0) ? s0v : g.halo[(g.iter & 1) * HS + ai - D];
-            float shat = g.carry[ai];
+            V* sp = reinterpret_cast<V*>(reinterpret_cast<S*>(g.s) + b * g.ss + static_cast<int64_t>(t0) * D + d);
             const bool has_next = (c + 1 < g.NC);
-            const float shat_end = has_next ? g.carry[ai + D] : 0.0f;
-            const bool und = g.undamped != 0;
             const float lam = g.lam;
-            // s^(i+1) at t0-1, exactly as the previous chunk stores it.
-            float snp = und ? shat : p_old + lam * (shat - p_old);
-            float xb[kU], sb[kU];
+            // p_old: s^(i) at t0-1 (halo of the previous chunk);  shat: s^ at t0-1;
+            // snp: s^(i+1) at t0-1, exactly as the previous chunk stores it.
+            float p_old[NCH], shat[NCH], shat_end[NCH], snp[NCH];
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                p_old[k] = (PHASE == kFirst || c == 0) ? s0v[k] : g.halo[(g.iter & 1) * HS + ai - D + k];
+                shat[k] = g.carry[ai + k];
+                shat_end[k] = has_next ? g.carry[ai + D + k] : 0.0f;
+                snp[k] = stored<S>(UND ? shat[k] : p_old[k] + lam * (shat[k] - p_old[k]));
+            }
+            V xb[kU], sb[kU];
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
-                xb[u] = u < n ? xp[u * D] : 0.0f;
-                if constexpr (PHASE == kFirst) sb[u] = s0v;
-                else sb[u] = u < n ? sp[u * D] : 0.0f;
+                xb[u] = u < n ? xp[u * DV] : V{};
+                if constexpr (PHASE != kFirst) sb[u] = u < n ? sp[u * DV] : V{};
             }
             for (int j = 0; j < n; j += kU) {
-                const float* xq = xp + static_cast<int64_t>(j) * D;   // row j of the chunk
-                float* sq = sp + static_cast<int64_t>(j) * D;
-                float xn[kU], sn_[kU];
+                const V* xq = xp + static_cast<int64_t>(j) * DV;   // row j of the chunk
+                V* sq = sp + static_cast<int64_t>(j) * DV;
+                V xn[kU], sn_[kU];
 #pragma unroll
                 for (int u = 0; u < kU; ++u) {
                     const bool in = j + kU + u < n;
-                    xn[u] = in ? xq[(kU + u) * D] : 0.0f;
-                    if constexpr (PHASE == kFirst) sn_[u] = s0v;
-                    else sn_[u] = in ? sq[(kU + u) * D] : 0.0f;
+                    xn[u] = in ? xq[(kU + u) * DV] : V{};
+                    if constexpr (PHASE != kFirst) sn_[u] = in ? sq[(kU + u) * DV] : V{};
                 }
 #pragma unroll
                 for (int u = 0; u < kU; ++u) {
                     if (j + u < n) {
-                        const float xt = xb[u];
-                        const float so = sb[u];
-                        // iteration i: map at p_t = s^(i)_{t-1}
-                        const float v = tanh_f(a * p_old + xt);
-                        const float at = mode_coef<MODE>(a * (1.0f - v * v));
-                        shat = v + at * (shat - p_old);
-                        // the chunk's last value is the one the scan hands to the next chunk
-                        if (j + u == n - 1 && has_next) shat = shat_end;
-                        const float sn = und ? shat : so + lam * (shat - so);
-                        sq[u * D] = sn;
-                        // iteration i+1: residual and affine map at p_t = s^(i+1)_{t-1}
-                        const float v2 = tanh_f(a * snp + xt);
-                        rb = max(rb, abs_bits(sn - v2));
-                        const float a2 = mode_coef<MODE>(a * (1.0f - v2 * v2));
-                        const float b2 = v2 - a2 * snp;
-                        A = a2 * A;
-                        Bc = a2 * Bc + b2;
-                        p_old = so;
-                        snp = sn;
+                        float xt[NCH], so[NCH], sn[NCH];
+                        unpack<S, NCH>(xb[u], xt);
+                        if constexpr (PHASE == kFirst) {
+#pragma unroll
+                            for (int k = 0; k < NCH; ++k) so[k] = s0v[k];
+                        } else {
+                            unpack<S, NCH>(sb[u], so);
+                        }
+#pragma unroll
+                        for (int k = 0; k < NCH; ++k) {
+                            // iteration i: map at p_t = s^(i)_{t-1}
+                            const float v = tanh_f(a[k] * p_old[k] + xt[k]);
+                            const float at = mode_coef<MODE>(a[k] * (1.0f - v * v));
+                            shat[k] = v + at * (shat[k] - p_old[k]);
+                            // the chunk's last value is the one the scan hands to the next chunk
+                            if (j + u == n - 1 && has_next) shat[k] = shat_end[k];
+                            sn[k] = UND ? shat[k] : so[k] + lam * (shat[k] - so[k]);
+                        }
+                        sq[u * DV] = pack<S, NCH>(sn);       // sn now holds the stored values
+#pragma unroll
+                        for (int k = 0; k < NCH; ++k) {
+                            // iteration i+1: residual and affine map at p_t = s^(i+1)_{t-1}
+                            const float v2 = tanh_f(a[k] * snp[k] + xt[k]);
+                            rb = max(rb, abs_bits(sn[k] - v2));
+                            const float a2 = mode_coef<MODE>(a[k] * (1.0f - v2 * v2));
+                            const float b2 = v2 - a2 * snp[k];
+                            A[k] = a2 * A[k];
+                            Bc[k] = a2 * Bc[k] + b2;
+                            p_old[k] = so[k];
+                            snp[k] = sn[k];
+                        }
                     }
                 }
 #pragma unroll
                 for (int u = 0; u < kU; ++u) {
                     xb[u] = xn[u];
-                    sb[u] = sn_[u];
+                    if constexpr (PHASE != kFirst) sb[u] = sn_[u];
                 }
             }
-            g.halo[((g.iter + 1) & 1) * HS + ai] = snp;
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) g.halo[((g.iter + 1) & 1) * HS + ai + k] = snp[k];
         }
-        g.aggA[ai] = A;
-        g.aggB[ai] = Bc;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            g.aggA[ai + k] = A[k];
+            g.aggB[ai + k] = Bc[k];
+        }
     }
     rb = block_max_u32(rb);
     if (threadIdx.x == 0) {
@@ -143,9 +225,12 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
     }
 }
 
+// Channel groups of a row: pairs for binary16 storage with even D.
+static int diag_groups(const DiagArgs& a) { return a.half == 2 ? a.D / 2 : a.D; }
+
 static dim3 diag_grid(const DiagArgs& a) {
     const int cpg = kThreads / a.cpb;
-    return dim3((a.NC + cpg - 1) / cpg, (a.D + a.cpb - 1) / a.cpb, a.B);
+    return dim3((a.NC + cpg - 1) / cpg, (diag_groups(a) + a.cpb - 1) / a.cpb, a.B);
 }
 
 int diag_tanh_nblocks(const DiagArgs& a) {
@@ -153,21 +238,36 @@ int diag_tanh_nblocks(const DiagArgs& a) {
     return static_cast<int>(g.x * g.y * g.z);
 }
 
-template <int MODE>
-static hipError_t launch_mode(int phase, const DiagArgs& a, hipStream_t st) {
+template <int MODE, typename S, int NCH, bool UND>
+static hipError_t launch_und(int phase, const DiagArgs& a, hipStream_t st) {
     const dim3 grid = diag_grid(a);
-    if (phase == kPrologue) diag_tanh_pass<MODE, kPrologue><<<grid, kThreads, 0, st>>>(a);
-    else if (phase == kFirst) diag_tanh_pass<MODE, kFirst><<<grid, kThreads, 0, st>>>(a);
-    else diag_tanh_pass<MODE, kSteady><<<grid, kThreads, 0, st>>>(a);
+    if (phase == kPrologue) diag_tanh_pass<MODE, kPrologue, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
+    else if (phase == kFirst) diag_tanh_pass<MODE, kFirst, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
+    else diag_tanh_pass<MODE, kSteady, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
     return hipGetLastError();
 }
 
-hipError_t launch_diag_tanh_pass(int phase, const DiagArgs& a, hipStream_t st) {
+// undamped (lam = 1) stores s^ itself: its own instantiation drops the damping
+template <int MODE, typename S, int NCH>
+static hipError_t launch_mode(int phase, const DiagArgs& a, hipStream_t st) {
+    return a.undamped ? launch_und<MODE, S, NCH, true>(phase, a, st)
+                      : launch_und<MODE, S, NCH, false>(phase, a, st);
+}
+
+template <typename S, int NCH>
+static hipError_t launch_store(int phase, const DiagArgs& a, hipStream_t st) {
     switch (a.mode) {
-        case kJacobi: return launch_mode<kJacobi>(phase, a, st);
-        case kPicard: return launch_mode<kPicard>(phase, a, st);
-        default: return launch_mode<kQuasiNewton>(phase, a, st);   // Newton == QN here
+        case kJacobi: return launch_mode<kJacobi, S, NCH>(phase, a, st);
+        case kPicard: return launch_mode<kPicard, S, NCH>(phase, a, st);
+        default: return launch_mode<kQuasiNewton, S, NCH>(phase, a, st);   // Newton == QN here
     }
+}
+
+// a.half: 0 float storage, 1 binary16 one channel per thread, 2 binary16 pairs
+hipError_t launch_diag_tanh_pass(int phase, const DiagArgs& a, hipStream_t st) {
+    if (a.half == 2) return launch_store<_Float16, 2>(phase, a, st);
+    if (a.half == 1) return launch_store<_Float16, 1>(phase, a, st);
+    return launch_store<float, 1>(phase, a, st);
 }
 
 // ---------------------------------------------------------------- carry scan
@@ -250,13 +350,14 @@ hipError_t launch_diag_carry(const CarryArgs& a, hipStream_t st) {
 
 // ---------------------------------------------------------------- fill
 // out[b][t][:] = s0[b][:] for a window (result when no update was applied).
-__global__ __launch_bounds__(kThreads) void fill_kernel(float* out, int64_t ss, const float* s0,
+template <typename S>
+__global__ __launch_bounds__(kThreads) void fill_kernel(S* out, int64_t ss, const float* s0,
                                                          int64_t s0s, int Tw, int D) {
     const int b = blockIdx.y;
     const int64_t n = static_cast<int64_t>(Tw) * D;
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
          e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        out[b * ss + e] = s0[b * s0s + (e % D)];
+        out[b * ss + e] = static_cast<S>(s0[b * s0s + (e % D)]);
     }
 }
 
@@ -265,7 +366,16 @@ hipError_t launch_fill(float* out, int64_t ss, const float* s0, int64_t s0s, int
     if (B == 0 || Tw == 0 || D == 0) return hipSuccess;
     const int64_t n = static_cast<int64_t>(Tw) * D;
     const int gx = static_cast<int>(std::min<int64_t>((n + kThreads - 1) / kThreads, 4096));
-    fill_kernel<<<dim3(gx, B), kThreads, 0, st>>>(out, ss, s0, s0s, Tw, D);
+    fill_kernel<float><<<dim3(gx, B), kThreads, 0, st>>>(out, ss, s0, s0s, Tw, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_half(void* out, int64_t ss, const float* s0, int64_t s0s, int B, int Tw, int D,
+                            hipStream_t st) {
+    if (B == 0 || Tw == 0 || D == 0) return hipSuccess;
+    const int64_t n = static_cast<int64_t>(Tw) * D;
+    const int gx = static_cast<int>(std::min<int64_t>((n + kThreads - 1) / kThreads, 4096));
+    fill_kernel<_Float16><<<dim3(gx, B), kThreads, 0, st>>>(static_cast<_Float16*>(out), ss, s0, s0s, Tw, D);
     return hipGetLastError();
 }
 

@@ -62,6 +62,8 @@ struct DiagArgs {
     const Ctrl* ctrl;
     int32_t mode, iter, undamped;
     float lam;
+    int32_t half;            // x and s hold IEEE binary16 (strides in elements): 1 one
+                             // channel per thread, 2 channel pairs (D even); 0 float
 };
 
 // ---------------------------------------------------------------- matrix cells
@@ -113,6 +115,8 @@ int diag_tanh_nblocks(const DiagArgs& a);
 hipError_t launch_diag_carry(const CarryArgs& a, hipStream_t st);
 hipError_t launch_dense_carry(const CarryArgs& a, hipStream_t st);
 hipError_t launch_check(const CheckArgs& c, hipStream_t st);
+hipError_t launch_fill_half(void* out, int64_t ss, const float* s0, int64_t s0s, int B, int Tw, int D,
+                            hipStream_t st);
 hipError_t launch_fill(float* out, int64_t ss, const float* s0, int64_t s0s, int B, int Tw, int D,
                        hipStream_t st);
 

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared_functions():
     text = open(os.path.join(ROOT, "include", "pn.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_expected_entry_points():
@@ -115,6 +115,24 @@ def test_switch_options():
     assert ns >= max(nq, nn)
     o = pn.make_opts()
     assert o.switch_mode == -1 and abs(o.switch_ratio - 0.5) < 1e-7
+
+
+def test_f16_entry_checks():
+    c = pn.Cell(pn.CELL_TANH_RNN, 3)
+    it = ctypes.c_int32(0)
+    p = ctypes.c_void_p(0x1000)
+    L = pn.lib()
+    assert L.pn_eval_f16(ctypes.byref(c), p, p, p, 2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
+                         ctypes.byref(it), None) == pn.EUNSUPPORTED
+    c = pn.Cell(pn.CELL_DIAG_TANH, 4)
+    o = pn.make_opts(window=2)
+    assert L.pn_eval_f16(ctypes.byref(c), p, p, p, 2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
+                         ctypes.byref(it), ctypes.byref(o)) == pn.EUNSUPPORTED
+    assert L.pn_eval_f16(ctypes.byref(c), p, p, p, -2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
+                         ctypes.byref(it), None) == pn.EINVAL
+    odd = ctypes.c_void_p(0x1002)    # pairs of binary16 values need 4-byte alignment
+    assert L.pn_eval_f16(ctypes.byref(c), p, odd, p, 2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
+                         ctypes.byref(it), None) == pn.EINVAL
 
 
 def test_euler_cell_sizes():

@@ -99,6 +99,21 @@ def test_diag_tanh_chunk_sizes(chunk):
     _parity(wl, Q, chunk=chunk)
 
 
+@pytest.mark.parametrize("D, storage", [(150, None), (190, None), (300, "f16"), (129, "f16")])
+def test_diag_tanh_widths_between_workgroup_sizes(D, storage):
+    # channel counts that do not fill a 64-multiple workgroup row
+    rng = np.random.default_rng(D)
+    B, T = 2, 700
+    wl = dict(cfg=0, cell=pn.CELL_DIAG_TANH, D=D, m=D, B=B, T=T, tol=1e-5 if storage is None else 1e-3,
+              damping=1.0, window=0, max_iter=T, params=rng.uniform(-0.9, 0.9, D).astype(np.float32),
+              x=rng.standard_normal((B, T, D)).astype(np.float32),
+              s0=(0.3 * rng.standard_normal((B, D))).astype(np.float32))
+    if storage:
+        wl.update(storage=storage, traj_tol=4 * 2.0 ** -11, x=wl["x"].astype(np.float16).astype(np.float32))
+    _parity(wl, Q)
+    _parity(wl, J)
+
+
 def test_diag_tanh_odd_width_and_damping():
     rng = np.random.default_rng(5)
     D, B, T = 77, 3, 517
@@ -326,6 +341,58 @@ def test_cfg6_lattice_switching_small():
     _parity(wl, Q)
 
 
+# ---------------------------------------------------------------- binary16 storage
+# Parity bar for stored binary16 states: the library's float32 value and the
+# oracle's float64 value of the same update can round to neighbouring binary16
+# numbers, and such a one-ulp step decays through the contraction |a| < 1; the
+# trajectories must agree within 4 binary16 ulps of the state scale
+# (4 * 2^-11 below 1).  Counts and statuses as for float32 storage.
+F16_TRAJ = 4 * 2.0 ** -11
+
+
+def _f16_case(B, T, tol=1e-3):
+    wl = _case(3, B=B, T=T)
+    wl.update(storage="f16", traj_tol=F16_TRAJ, tol=tol,
+              x=wl["x"].astype(np.float16).astype(np.float32))
+    return wl
+
+
+@pytest.mark.parametrize("mode", [Q, J, P])
+def test_f16_storage_channelwise(mode):
+    wl = _f16_case(2, 3001, tol=1e-3 if mode != P else 2e-3)
+    _parity(wl, mode)
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 3001])
+def test_f16_storage_chunks(chunk):
+    wl = _f16_case(2, 3001)
+    _parity(wl, Q, chunk=chunk)
+
+
+def test_f16_storage_odd_width_one_channel_per_thread():
+    rng = np.random.default_rng(9)
+    D, B, T = 77, 3, 517
+    wl = dict(cfg=0, cell=pn.CELL_DIAG_TANH, D=D, m=D, B=B, T=T, tol=1e-3, damping=0.7, window=0,
+              max_iter=T, params=rng.uniform(-0.9, 0.9, D).astype(np.float32),
+              x=rng.standard_normal((B, T, D)).astype(np.float16).astype(np.float32),
+              s0=(0.3 * rng.standard_normal((B, D))).astype(np.float32), storage="f16",
+              traj_tol=F16_TRAJ)
+    _parity(wl, Q)
+
+
+def test_f16_storage_jacobi_reaches_the_stored_sequence():
+    # T Jacobi updates end on s_t = f16(f(s_{t-1})); the library's float32
+    # f and the oracle's float64 f may round a few values differently
+    wl = _f16_case(2, 300, tol=0.0)
+    gpu = run_gpu(wl, J, max_iter=300)
+    ref = run_oracle(wl, J, max_iter=300)
+    assert gpu.status == ref.status == pn.NOT_CONVERGED and gpu.iters == 300
+    diff = np.abs(gpu.out_np.astype(np.float64) - ref.s)
+    print("binary16 Jacobi: max diff", diff.max(), "values differing", int((diff > 0).sum()))
+    assert diff.max() <= F16_TRAJ
+    assert np.array_equal(gpu.out_np, gpu.out_np.astype(np.float16).astype(np.float32))
+
+
 @pytest.mark.parametrize("kind", [pn.CELL_TANH_RNN, pn.CELL_GRU])
 def test_matrix_cells_wide_input(kind):
     # weights too large to stage in LDS: the kernels read them from global memory
@@ -453,6 +520,12 @@ def test_cfg4_full_newton():
 def test_cfg7_full_picard_advancing():
     wl = _case(7)
     _parity(wl, P)
+
+
+@pytest.mark.slow
+def test_cfg3_full_f16_storage():
+    wl = _f16_case(8, 65536)
+    _parity(wl, Q)
 
 
 @pytest.mark.slow
