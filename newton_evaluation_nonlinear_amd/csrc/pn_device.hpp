@@ -133,6 +133,33 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
 // per-block maxima of the previous pass, apply the stop rule (non-finite,
 // then r <= tol, then i == max_iter) and publish it to the device control
 // word and to the pinned host record.
+// The stop rule on the reduced residual bits m: -1 (continue) or a status.
+__device__ __forceinline__ int check_status(uint32_t m, const CheckArgs& c) {
+    if (m >= kNonFiniteBits) return kStNonFinite;
+    if (__uint_as_float(m) <= c.tol) return kStOk;
+    if (c.iter >= c.max_iter) return kStNotConverged;
+    return -1;
+}
+
+// Publish a decision to the device control word and the pinned host record
+// (payload, then epoch, then iter).  One thread.
+__device__ __forceinline__ void publish_check(const CheckArgs& c, uint32_t m, int st, uint32_t first) {
+    const int stop = st >= 0 ? 1 : 0;
+    c.ctrl->stop = stop;
+    c.ctrl->status = st;
+    c.ctrl->iter = c.iter;
+    c.ctrl->r_bits = m;
+    c.host->r_bits = m;
+    c.host->first = first;
+    c.host->status = st;
+    c.host->stop = stop;
+    __threadfence_system();
+    __hip_atomic_store(&c.host->epoch, c.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __threadfence_system();
+    __hip_atomic_store(&c.host->iter, c.iter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __threadfence_system();
+}
+
 // With c.advancing the check only reduces (residual max and the first step
 // over tol) and publishes; the host takes the decision and the device loop
 // keeps running.
@@ -148,27 +175,7 @@ __device__ __forceinline__ void run_check(const CheckArgs& c) {
     }
     m = block_max_u32(m);
     if (c.fpart) nf = block_max_u32(nf);
-    if (threadIdx.x == 0) {
-        int st = -1;
-        if (m >= kNonFiniteBits) st = kStNonFinite;
-        else if (__uint_as_float(m) <= c.tol) st = kStOk;
-        else if (c.iter >= c.max_iter) st = kStNotConverged;
-        if (c.advancing) st = -1;
-        const int stop = st >= 0 ? 1 : 0;
-        c.ctrl->stop = stop;
-        c.ctrl->status = st;
-        c.ctrl->iter = c.iter;
-        c.ctrl->r_bits = m;
-        c.host->r_bits = m;
-        c.host->first = ~nf;
-        c.host->status = st;
-        c.host->stop = stop;
-        __threadfence_system();
-        __hip_atomic_store(&c.host->epoch, c.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        __threadfence_system();
-        __hip_atomic_store(&c.host->iter, c.iter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        __threadfence_system();
-    }
+    if (threadIdx.x == 0) publish_check(c, m, c.advancing ? -1 : check_status(m, c), ~nf);
 }
 
 }  // namespace pn

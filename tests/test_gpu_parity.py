@@ -138,9 +138,24 @@ def test_cfg2_gru_small(mode):
 
 
 def test_cfg2_gru_picard_small():
-    # T=300 is short enough for Picard to converge, after transients near 1e27
+    # T=300 is short enough for Picard to converge, after transients near
+    # 1e27.  Picard converges here only through causality (one step of the
+    # front per update), and where the front meets the tail is decided by the
+    # rounding of those 1e27 transients: the float64 and float32 oracles
+    # already differ by 9 updates.  The count is held to the float32 oracle
+    # within 2% of T; the trajectory is compared with the float64 oracle run
+    # for exactly the library's count, and the residual must meet tol.
     wl = _case(2, B=4, T=300)
-    _parity(wl, P)
+    gpu = run_gpu(wl, P)
+    ref32 = run_oracle(wl, P, dtype=np.float32)
+    assert gpu.status == ref32.status == oracle.OK
+    assert max(ref32.hist[0]) > 1e20            # the transient regime this test is about
+    assert abs(gpu.iters - ref32.iters) <= 0.02 * 300, (gpu.iters, ref32.iters)
+    forced = run_oracle(wl, P, force_iters=[gpu.iters])
+    assert forced.status == oracle.OK
+    err = float(np.max(np.abs(gpu.out_np.astype(np.float64) - forced.s)))
+    assert err <= 1e-4 * max(1.0, float(np.max(np.abs(forced.s))))
+    assert residual64(wl, gpu.out_np) <= wl["tol"] + 1e-6
 
 
 @pytest.mark.parametrize("mode", [N, Q])
@@ -414,7 +429,16 @@ def test_persistent_and_multilaunch_paths_agree(cfg, B, T, mode):
     wl = _case(cfg, B=B, T=T)
     a = run_gpu_flags(wl, mode, pn.FLAG_PERSISTENT)
     b = run_gpu(wl, mode)
-    assert a.status == b.status and a.window_iters == b.window_iters
+    assert a.status == b.status
+    if mode == P:
+        # Picard on this GRU passes through 1e27 transients, and the two
+        # paths sum the carries in different orders (segmented in the
+        # persistent solver, one chunk after another in the few-chunk apply),
+        # which moves where the count lands (see test_cfg2_gru_picard_small)
+        assert abs(a.iters - b.iters) <= 0.02 * T
+        assert np.max(np.abs(a.out_np - b.out_np)) <= 1e-4
+        return
+    assert a.window_iters == b.window_iters
     assert np.max(np.abs(a.out_np - b.out_np)) <= 1e-5
     assert len(a.resid_hist) == len(b.resid_hist)
     if mode != P:
