@@ -864,45 +864,97 @@ hipError_t launch_check(const CheckArgs& c, hipStream_t st) {
 // ---------------------------------------------------------------- dense carry scan
 // carry[b][0] = s0[b]; carry[b][c+1] = M[b][c] carry[b][c] + bg[b][c].
 // One wavefront per batch row; lane i owns row i of every chunk map and the
-// i-th entry of the running carry.  The carry entries are broadcast with
-// readlane (no LDS, no barrier), and each lane prefetches the next chunk's row
-// into registers while it applies the current one.
-__device__ __forceinline__ float bcast_lane(float v, int k) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
+// i-th entry of the running carry.  The chain is serial, so what counts is
+// the instruction count per chunk: each lane keeps the rows of the next AH
+// chunks in registers (16-byte loads, issued AH chunks ahead, no per-element
+// branches: lanes past D read row D-1 and drop the result), and the carry is
+// broadcast through LDS (one write, DP/4 16-byte broadcast reads per chunk).
+// D not a multiple of 4 takes a plain per-element loop.
+// The register-ring chain; FULL: D == DP (no padded columns to clear).
+template <int DP, bool FULL>
+__device__ __forceinline__ void carry_chain(const CarryArgs& g, float* ys, float y) {
+    constexpr int AH = DP <= 16 ? 8 : 4;         // chunk maps in flight
+    constexpr int Q = DP / 4;                    // 16-byte pieces per row
+    const int i = threadIdx.x, D = g.D;
+    const bool live = i < D;
+    const int ir = live ? i : D - 1;
+    const size_t cb = static_cast<size_t>(blockIdx.x) * g.NC;
+    const int steps = g.NC - 1;
+    float4 ring[AH][Q];
+    float ob[AH];
+    auto load = [&](int c, float4 (&row)[Q], float& off) {
+        const float4* M = reinterpret_cast<const float4*>(g.aggA + (cb + c) * D * D + static_cast<size_t>(ir) * D);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            if constexpr (FULL) row[q] = M[q];
+            else row[q] = 4 * q < D ? M[q] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+        off = g.aggB[(cb + c) * D + ir];
+    };
+#pragma unroll
+    for (int p = 0; p < AH; ++p) load(min(p, steps - 1), ring[p], ob[p]);
+    const float4* y4 = reinterpret_cast<const float4*>(ys);
+    for (int c0 = 0; c0 < steps; c0 += AH) {
+#pragma unroll
+        for (int p = 0; p < AH; ++p) {
+            const int c = c0 + p;
+            if (c < steps) {
+                if (i < DP) ys[i] = y;
+                __builtin_amdgcn_wave_barrier();
+                float part[4] = {ob[p], 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const float4 yv = y4[q];
+                    const float4 mv = ring[p][q];
+                    part[q & 3] += mv.x * yv.x + mv.y * yv.y + mv.z * yv.z + mv.w * yv.w;
+                }
+                __builtin_amdgcn_wave_barrier();
+                const float acc = (part[0] + part[1]) + (part[2] + part[3]);
+                if constexpr (FULL) {
+                    y = acc;
+                    if (live) g.carry[(cb + c + 1) * D + i] = acc;
+                } else {
+                    y = live ? acc : 0.0f;
+                    if (live) g.carry[(cb + c + 1) * D + i] = acc;
+                }
+                load(min(c + AH, steps - 1), ring[p], ob[p]);
+            }
+        }
+    }
 }
 
 template <int DP>
 __global__ __launch_bounds__(64) void dense_carry_kernel(CarryArgs g) {
     if (g.do_check && blockIdx.x == 0) run_check(g.chk);
+    __shared__ __attribute__((aligned(16))) float ys[DP < 4 ? 4 : DP];
     const int b = blockIdx.x;
     const int i = threadIdx.x;
     const int D = g.D;
     const bool live = i < D;
+    const int ir = live ? i : D - 1;
     const size_t cb = static_cast<size_t>(b) * g.NC;
-    float y = 0.0f;
-    if (live) {
-        y = g.s0[b * g.s0s + i];
-        g.carry[cb * D + i] = y;
+    const int steps = g.NC - 1;                  // maps 0 .. NC-2 give carries 1 .. NC-1
+    float y = live ? g.s0[b * g.s0s + i] : 0.0f;
+    if (live) g.carry[cb * D + i] = y;
+    if (steps <= 0) return;
+    if (D % 4 != 0) {
+        // plain chain: row i of each map straight from memory
+        for (int c = 0; c < steps; ++c) {
+            if (i < DP) ys[i] = y;
+            __builtin_amdgcn_wave_barrier();
+            const float* M = g.aggA + (cb + c) * D * D + static_cast<size_t>(ir) * D;
+            float acc = g.aggB[(cb + c) * D + ir];
+            for (int k = 0; k < D; ++k) acc += M[k] * ys[k];
+            __builtin_amdgcn_wave_barrier();
+            y = live ? acc : 0.0f;
+            if (live) g.carry[(cb + c + 1) * D + i] = acc;
+        }
+        return;
     }
-    float cur[DP] = {}, nxt[DP] = {};
-    float bc = 0.0f, bn = 0.0f;
-    auto load = [&](int c, float (&row)[DP], float& off) {
-        const float* M = g.aggA + (cb + c) * D * D + static_cast<size_t>(i) * D;
-#pragma unroll
-        for (int k = 0; k < DP; ++k) row[k] = (live && k < D) ? M[k] : 0.0f;
-        off = live ? g.aggB[(cb + c) * D + i] : 0.0f;
-    };
-    if (g.NC > 1) load(0, cur, bc);
-    for (int c = 0; c + 1 < g.NC; ++c) {
-        if (c + 2 < g.NC) load(c + 1, nxt, bn);
-        float acc = bc;
-#pragma unroll
-        for (int k = 0; k < DP; ++k) acc += cur[k] * bcast_lane(y, k);
-        y = live ? acc : 0.0f;
-        if (live) g.carry[(cb + c + 1) * D + i] = acc;
-#pragma unroll
-        for (int k = 0; k < DP; ++k) cur[k] = nxt[k];
-        bc = bn;
+    // lanes past DP hold nothing; lanes in [D, DP) carry zeros
+    if constexpr (DP >= 4) {
+        if (D == DP) carry_chain<DP, true>(g, ys, y);
+        else carry_chain<DP, false>(g, ys, y);
     }
 }
 
