@@ -39,9 +39,12 @@ KERNEL_SOURCES = {  # source file of the dominant kernel per cell kind
 
 
 def _kernel_source(wl, mode):
-    if wl["cell"] != 0 and 8 < wl["D"] <= 32 and (
-            mode == 3 or (mode == 4 and 0 < wl["bandwidth"] < wl["D"] - 1)):
-        return "newton_evaluation_nonlinear_amd/csrc/pn_dense.hip"   # dense modes on the matrix cores
+    dense = mode == 3 or (mode == 4 and 0 < wl["bandwidth"] < wl["D"] - 1)
+    # the dense modes run on the matrix cores for D padded to 16 or 32, and to
+    # 64 for the single-gate cells (tanh RNN, Euler step)
+    mfma = 8 < wl["D"] <= 32 or (32 < wl["D"] <= 64 and wl["cell"] in (1, 3))
+    if wl["cell"] != 0 and dense and mfma:
+        return "newton_evaluation_nonlinear_amd/csrc/pn_dense.hip"
     return KERNEL_SOURCES[wl["cell"]]
 
 

@@ -126,7 +126,7 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
         a.B = p.B; a.D = p.D; a.NC = p.NC; a.cpb = p.cpb; a.half = p.hmode;
         p.nblocks = diag_tanh_nblocks(a);
         p.DP = 0;
-    } else if (p.dense && (next_pow2(p.D) == 16 || next_pow2(p.D) == 32) &&
+    } else if (p.dense && (next_pow2(p.D) == 16 || next_pow2(p.D) == 32 || next_pow2(p.D) == 64) &&
                dense_mfma_supported(p.kind, next_pow2(p.D), p.m)) {
         // Newton on the matrix cores: one wavefront per chunk; chunks long
         // enough to keep the serial carry short, with ~2048 chunks in flight

@@ -433,6 +433,359 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
     }
 }
 
+// ---------------------------------------------------------------- D padded to 64
+// The same iteration for 33 <= D <= 64 and the single-gate cells (tanh RNN,
+// Euler step).  One wavefront per chunk; the D x D map is four 32 x 32
+// accumulator tiles M[K][J] (rows 32K + krow(h, q), columns 32J + r for lane
+// l = 32h + r), and W g M is 2 x 2 output tiles of 2 x 16 steps of the
+// 32x32x2 FP32 MFMA, 128 steps per time step.  The lane's A operands,
+// wr[I][K][s] = W[32I + r][32K + krow(h, s)], also give its two rows r and
+// 32 + r of every matrix-vector product (partial sums over its k subset plus
+// the partner lane l ^ 32).  Each lane writes its own row l of the LDS rows.
+template <int CELL> struct D64Lds {
+    static constexpr int NCO = DTraits<CELL>::NCO;
+    static __host__ __device__ size_t floats(int m) {
+        return 2ull * (kSub + 1) * 64 + static_cast<size_t>(kSub) * m + 3ull * kSub * 64 +
+               static_cast<size_t>(NCO) * kSub * 64 + static_cast<size_t>(m) * 64 + 2 * 64;
+    }
+};
+
+template <int CELL, int PHASE, bool BANDED>
+__global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
+    static_assert(DTraits<CELL>::NG == 1, "single-gate cells only");
+    if constexpr (PHASE != kPrologue && PHASE != kMaps) {
+        if (g.ctrl->stop) return;
+    }
+    typedef MfmaTile<32> Tl;
+    constexpr int NCO = DTraits<CELL>::NCO;
+    constexpr int DP = 64;
+    extern __shared__ float lds[];
+    const int D = g.D, m = g.m;
+    const int lane = threadIdx.x;
+    const int r = lane & 31, h = lane >> 5;
+    const int orow = lane;                    // the row this lane writes
+    const bool olive = orow < D;
+    const bool live0 = r < D, live1 = 32 + r < D;
+    const int c = blockIdx.x, b = blockIdx.y;
+    const int t0 = c * g.L;
+    const int Lc = min(g.L, g.Tw - t0);
+    const size_t ci = static_cast<size_t>(b) * g.NC + c;
+    const size_t HS = static_cast<size_t>(g.B) * g.NC * D;
+    const float* s0 = g.s0 + b * g.s0s;
+
+    float* P = lds;                           // [kSub+1][64]
+    float* N = P + (kSub + 1) * DP;           // [kSub+1][64]
+    float* X = N + (kSub + 1) * DP;           // [kSub][m]
+    float* XP = X + kSub * m;                 // [kSub][64]
+    float* V = XP + kSub * DP;                // [kSub][64]
+    float* CO = V + kSub * DP;                // [NCO][kSub][64]
+    float* UT = CO + NCO * kSub * DP;         // [m][64]
+    float* YV = UT + m * DP;                  // [2][64]
+    (void)(V + kSub * DP);
+
+    const float* w = g.w;                     // WT[64][64] | UT[m][64] | bias | wdiag (| h)
+    const float* wUT = w + DP * DP;
+    const float* wbi = wUT + m * DP;
+    float wr[2][2][16], wj[2][2][16];
+#pragma unroll
+    for (int I = 0; I < 2; ++I)
+#pragma unroll
+        for (int K = 0; K < 2; ++K)
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const int k = 32 * K + Tl::krow(h, s), row = 32 * I + r;
+                wr[I][K][s] = w[k * DP + row];
+                wj[I][K][s] = (!BANDED || abs(k - row) <= g.band) ? wr[I][K][s] : 0.0f;
+            }
+    copy_to_lds<64>(UT, wUT, m * DP);
+    const float bias_o = wbi[orow];
+    float hs[2] = {0.0f, 0.0f};               // Euler step sizes of rows r, 32 + r
+    if constexpr (CELL == kCellEulerD) {
+        hs[0] = wbi[2 * DP + r];
+        hs[1] = wbi[2 * DP + 32 + r];
+    }
+
+    // W y for rows r and 32 + r (y: 64 floats in LDS)
+    auto matvec = [&](const float (&W)[2][2][16], const float* y, float (&o)[2]) {
+        float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int K = 0; K < 2; ++K)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 y4 = *reinterpret_cast<const float4*>(y + 32 * K + 8 * q + 4 * h);
+                const float yk[4] = {y4.x, y4.y, y4.z, y4.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    a0 += W[0][K][4 * q + t] * yk[t];
+                    a1 += W[1][K][4 * q + t] * yk[t];
+                }
+            }
+        a0 += __shfl_xor(a0, 32, 64);
+        a1 += __shfl_xor(a1, 32, 64);
+        o[0] = a0;
+        o[1] = a1;
+    };
+    // cell at row p of LDS (inputs XP row j): values and coefficients of rows r, 32 + r
+    auto eval = [&](const float* p, int j, float (&v)[2], float (&co)[2][NCO]) {
+        float u[2];
+        matvec(wr, p, u);
+#pragma unroll
+        for (int I = 0; I < 2; ++I) {
+            const float pre = u[I] + XP[j * DP + 32 * I + r];
+            if constexpr (CELL == kCellTanhRnnD) {
+                v[I] = tanh_f(pre);
+                co[I][0] = 1.0f - v[I] * v[I];
+            } else {
+                const float gv = tanh_f(pre);
+                const float pi = p[32 * I + r];
+                v[I] = pi + hs[I] * (gv - pi);
+                co[I][0] = 1.0f - hs[I];
+                co[I][NCO - 1] = hs[I] * (1.0f - gv * gv);
+            }
+        }
+    };
+    // A~ d for rows r, 32 + r, d in LDS; dd: the lane's two entries of d
+    auto jac_apply = [&](const float* d, const float (&dd)[2], const float (&co)[2][NCO], float (&o)[2]) {
+        float a[2];
+        matvec(wj, d, a);
+#pragma unroll
+        for (int I = 0; I < 2; ++I) {
+            if constexpr (CELL == kCellTanhRnnD) o[I] = co[I][0] * a[I];
+            else o[I] = co[I][0] * dd[I] + co[I][NCO - 1] * a[I];
+        }
+    };
+    auto own = [&](const float (&x)[2]) { return h ? x[1] : x[0]; };
+
+    // chunk map: identity on the live rows
+    v16f M[2][2];
+#pragma unroll
+    for (int K = 0; K < 2; ++K)
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = 32 * K + Tl::krow(h, q), col = 32 * J + r;
+                M[K][J][q] = (row == col && col < D) ? 1.0f : 0.0f;
+            }
+    float bg[2] = {0.0f, 0.0f};
+    uint32_t rb = 0;
+    const bool track = g.fpart != nullptr;
+    uint32_t fb = 0xffffffffu;
+    const bool has_next = c + 1 < g.NC;
+    const float* cr = g.carry + ci * D;
+    float shat[2] = {0.0f, 0.0f};
+    float* sg = g.s + b * g.ss + static_cast<int64_t>(t0) * D;
+    const float* xg = g.x + b * g.xs + static_cast<int64_t>(t0) * m;
+
+    // row t0-1 of the old and the new iterate (lane: its own row; shat: rows r, 32 + r)
+    {
+        float po = 0.0f, pn = 0.0f;
+        if (olive) {
+            if constexpr (PHASE == kPrologue) {
+                po = pn = s0[orow];
+            } else if constexpr (PHASE == kMaps) {
+                po = pn = c == 0 ? s0[orow] : sg[orow - D];
+            } else {
+                po = (PHASE == kFirst || c == 0) ? s0[orow] : g.halo[(g.iter & 1) * HS + (ci - 1) * D + orow];
+                pn = g.undamped ? cr[orow] : po + g.lam * (cr[orow] - po);
+            }
+        }
+        if constexpr (PHASE == kFirst || PHASE == kSteady) {
+            shat[0] = live0 ? cr[r] : 0.0f;
+            shat[1] = live1 ? cr[32 + r] : 0.0f;
+        }
+        P[orow] = po;
+        N[orow] = pn;
+    }
+
+    for (int j0 = 0; j0 < Lc; j0 += kSub) {
+        const int Sc = min(kSub, Lc - j0);
+        copy_to_lds<64>(X, xg + static_cast<int64_t>(j0) * m, Sc * m);
+        if constexpr (PHASE == kPrologue || PHASE == kFirst) {
+            for (int e = lane; e < Sc * DP; e += 64) {
+                const int q = e % DP;
+                P[DP + e] = q < D ? s0[q] : 0.0f;
+            }
+        } else {
+            copy_rows_to_lds<64>(P + DP, DP, sg + static_cast<int64_t>(j0) * D, D, Sc, D);
+        }
+        __syncthreads();
+        // input projection U x + b for the lane's own row
+        for (int j = 0; j < Sc; ++j) {
+            float a = bias_o;
+            for (int q = 0; q < m; ++q) a += UT[q * DP + orow] * X[j * m + q];
+            XP[j * DP + orow] = olive ? a : 0.0f;
+        }
+        __syncthreads();
+
+        if constexpr (PHASE != kPrologue && PHASE != kMaps) {
+            // maps of iteration i at the old iterate
+            for (int j = 0; j < Sc; ++j) {
+                float v[2], co[2][NCO];
+                eval(P + j * DP, j, v, co);
+                V[j * DP + orow] = olive ? own(v) : 0.0f;
+#pragma unroll
+                for (int q = 0; q < NCO; ++q) CO[(q * kSub + j) * DP + orow] = olive ? (h ? co[1][q] : co[0][q]) : 0.0f;
+            }
+            __syncthreads();
+            // replay from the carry, damping
+            for (int j = 0; j < Sc; ++j) {
+                float dd[2];
+                dd[0] = live0 ? shat[0] - P[j * DP + r] : 0.0f;
+                dd[1] = live1 ? shat[1] - P[j * DP + 32 + r] : 0.0f;
+                YV[orow] = own(dd);
+                __syncthreads();
+                float co[2][NCO];
+#pragma unroll
+                for (int I = 0; I < 2; ++I)
+#pragma unroll
+                    for (int q = 0; q < NCO; ++q) co[I][q] = CO[(q * kSub + j) * DP + 32 * I + r];
+                float ad[2];
+                jac_apply(YV, dd, co, ad);
+                float sn[2];
+#pragma unroll
+                for (int I = 0; I < 2; ++I) {
+                    const int row = 32 * I + r;
+                    shat[I] = V[j * DP + row] + ad[I];
+                    if (j0 + j == Lc - 1 && has_next && row < D) shat[I] = cr[D + row];
+                    const float so = P[(j + 1) * DP + row];
+                    sn[I] = g.undamped ? shat[I] : so + g.lam * (shat[I] - so);
+                }
+                N[(j + 1) * DP + orow] = olive ? own(sn) : 0.0f;
+                __syncthreads();
+            }
+            for (int e = lane; e < Sc * D; e += 64) {
+                const int j = e / D, q = e % D;
+                sg[static_cast<int64_t>(j0 + j) * D + q] = N[(j + 1) * DP + q];
+            }
+        } else {
+            for (int e = lane; e < Sc * DP; e += 64) N[DP + e] = P[DP + e];
+        }
+        __syncthreads();
+
+        // maps of iteration i+1 at the new iterate; residual
+        for (int j = 0; j < Sc; ++j) {
+            float v[2], co[2][NCO];
+            eval(N + j * DP, j, v, co);
+#pragma unroll
+            for (int I = 0; I < 2; ++I) {
+                if (32 * I + r < D) {
+                    const float d = N[(j + 1) * DP + 32 * I + r] - v[I];
+                    rb = max(rb, abs_bits(d));
+                    if (track && !(fabsf(d) <= g.tol)) fb = min(fb, static_cast<uint32_t>(j0 + j));
+                }
+            }
+            V[j * DP + orow] = olive ? own(v) : 0.0f;
+#pragma unroll
+            for (int q = 0; q < NCO; ++q) CO[(q * kSub + j) * DP + orow] = olive ? (h ? co[1][q] : co[0][q]) : 0.0f;
+        }
+        __syncthreads();
+
+        // extend the chunk map over the sub-chunk
+        for (int j = 0; j < Sc; ++j) {
+            v16f C[2][2];
+#pragma unroll
+            for (int I = 0; I < 2; ++I)
+#pragma unroll
+                for (int J = 0; J < 2; ++J) {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) C[I][J][q] = 0.0f;
+#pragma unroll
+                    for (int K = 0; K < 2; ++K)
+#pragma unroll
+                        for (int s = 0; s < 16; ++s) C[I][J] = Tl::step(wj[I][K][s], M[K][J][s], C[I][J]);
+                }
+            // offset: bg <- A_j (bg - p_j) + v_j  (p_j = N[j])
+            float dbi[2];
+            dbi[0] = live0 ? bg[0] - N[j * DP + r] : 0.0f;
+            dbi[1] = live1 ? bg[1] - N[j * DP + 32 + r] : 0.0f;
+            YV[DP + orow] = own(dbi);
+            __syncthreads();
+            {
+                float co[2][NCO];
+#pragma unroll
+                for (int I = 0; I < 2; ++I)
+#pragma unroll
+                    for (int q = 0; q < NCO; ++q) co[I][q] = CO[(q * kSub + j) * DP + 32 * I + r];
+                float ad[2];
+                jac_apply(YV + DP, dbi, co, ad);
+#pragma unroll
+                for (int I = 0; I < 2; ++I) bg[I] = V[j * DP + 32 * I + r] + ad[I];
+            }
+            // row scalings of the accumulator rows 32 I + krow(h, q)
+#pragma unroll
+            for (int I = 0; I < 2; ++I) {
+                float rs[NCO][16];
+#pragma unroll
+                for (int q = 0; q < NCO; ++q)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float4 c4 = *reinterpret_cast<const float4*>(CO + (q * kSub + j) * DP + 32 * I + 8 * u + 4 * h);
+                        rs[q][4 * u] = c4.x;
+                        rs[q][4 * u + 1] = c4.y;
+                        rs[q][4 * u + 2] = c4.z;
+                        rs[q][4 * u + 3] = c4.w;
+                    }
+#pragma unroll
+                for (int J = 0; J < 2; ++J)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        if constexpr (CELL == kCellTanhRnnD) M[I][J][q] = rs[0][q] * C[I][J][q];
+                        else M[I][J][q] = rs[0][q] * M[I][J][q] + rs[NCO - 1][q] * C[I][J][q];
+                    }
+            }
+            __syncthreads();
+        }
+        // carry the last rows into the next sub-chunk
+        const float plast = P[Sc * DP + orow];
+        const float nlast = N[Sc * DP + orow];
+        __syncthreads();
+        P[orow] = plast;
+        N[orow] = nlast;
+        __syncthreads();
+    }
+
+    if constexpr (PHASE == kMaps) {
+        if (olive) g.halo[(g.iter & 1) * HS + ci * D + orow] = N[orow];
+    } else if constexpr (PHASE != kPrologue) {
+        if (olive) g.halo[((g.iter + 1) & 1) * HS + ci * D + orow] = N[orow];
+    }
+    float* aA = g.aggA + ci * D * D;
+#pragma unroll
+    for (int K = 0; K < 2; ++K)
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = 32 * K + Tl::krow(h, q), col = 32 * J + r;
+                if (row < D && col < D) aA[row * D + col] = M[K][J][q];
+            }
+    if (olive) g.aggB[ci * D + orow] = own(bg);
+    rb = wave_max_u32(rb);
+    if (lane == 0) g.rpart[ci] = rb;
+    if (track) {
+        fb = ~wave_max_u32(~fb);
+        if (lane == 0) g.fpart[ci] = fb == 0xffffffffu ? fb : t0 + fb;
+    }
+}
+
+template <int CELL, bool BANDED>
+static hipError_t launch_dense64_b(int phase, const CellArgs& a, hipStream_t st) {
+    const size_t lds = D64Lds<CELL>::floats(a.m) * sizeof(float);
+    const dim3 grid(a.NC, a.B);
+    if (phase == kPrologue) dense64_pass<CELL, kPrologue, BANDED><<<grid, 64, lds, st>>>(a);
+    else if (phase == kFirst) dense64_pass<CELL, kFirst, BANDED><<<grid, 64, lds, st>>>(a);
+    else if (phase == kMaps) dense64_pass<CELL, kMaps, BANDED><<<grid, 64, lds, st>>>(a);
+    else dense64_pass<CELL, kSteady, BANDED><<<grid, 64, lds, st>>>(a);
+    return hipGetLastError();
+}
+
+template <int CELL>
+static hipError_t launch_dense64(int phase, const CellArgs& a, hipStream_t st) {
+    return a.band < a.D - 1 ? launch_dense64_b<CELL, true>(phase, a, st)
+                            : launch_dense64_b<CELL, false>(phase, a, st);
+}
+
 template <int CELL, int DP, bool BANDED>
 static hipError_t launch_dense_phase_b(int phase, const CellArgs& a, hipStream_t st) {
     const size_t lds = DLds<CELL, DP>::floats(a.m) * sizeof(float);
@@ -452,17 +805,26 @@ static hipError_t launch_dense_phase(int phase, const CellArgs& a, hipStream_t s
 }
 
 bool dense_mfma_supported(int kind, int DP, int m) {
+    if (DP == 64) return kind != kCellGruD && dense_mfma_lds_bytes(kind, 64, m) <= 64 * 1024;
     if (DP != 16 && DP != 32) return false;
     return dense_mfma_lds_bytes(kind, 32, m) <= 64 * 1024;
 }
 
 size_t dense_mfma_lds_bytes(int kind, int DP, int m) {
+    if (DP == 64) {
+        return (kind == kCellEulerD ? D64Lds<kCellEulerD>::floats(m) : D64Lds<kCellTanhRnnD>::floats(m)) * sizeof(float);
+    }
     if (kind == kCellTanhRnnD) return (DP == 16 ? DLds<kCellTanhRnnD, 16>::floats(m) : DLds<kCellTanhRnnD, 32>::floats(m)) * sizeof(float);
     if (kind == kCellEulerD) return (DP == 16 ? DLds<kCellEulerD, 16>::floats(m) : DLds<kCellEulerD, 32>::floats(m)) * sizeof(float);
     return (DP == 16 ? DLds<kCellGruD, 16>::floats(m) : DLds<kCellGruD, 32>::floats(m)) * sizeof(float);
 }
 
 hipError_t launch_dense_mfma_pass(int kind, int DP, int phase, const CellArgs& a, hipStream_t st) {
+    if (DP == 64) {
+        if (kind == kCellTanhRnnD) return launch_dense64<kCellTanhRnnD>(phase, a, st);
+        if (kind == kCellEulerD) return launch_dense64<kCellEulerD>(phase, a, st);
+        return hipErrorInvalidValue;
+    }
     if (kind == kCellTanhRnnD) {
         return DP == 16 ? launch_dense_phase<kCellTanhRnnD, 16>(phase, a, st)
                         : launch_dense_phase<kCellTanhRnnD, 32>(phase, a, st);
