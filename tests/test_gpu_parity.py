@@ -273,9 +273,11 @@ def _advancing_case(kind, D, m, B, T, W, seed, tol=1e-5, damping=1.0, params=Non
 def test_advancing_window_matches_oracle(kind, D, W):
     # windows that are not a multiple of the chunk, a ragged end, every mode
     wl = _advancing_case(kind, D, 4, 2, 333, W, 600 + D + W)
-    # Picard (A~ = I) is the small-step method: not run on the plain tanh RNN,
-    # where it stalls with 1e30 transients
-    for mode in (Q, N, J, pn.BANDED) + ((P,) if kind != pn.CELL_TANH_RNN else ()):
+    # Picard (A~ = I) is the small-step method: run on the Euler cell only.
+    # On the plain tanh RNN and the GRU it passes through 1e7-1e30
+    # transients, and which tail steps happen to meet tol is then decided by
+    # the rounding of those transients
+    for mode in (Q, N, J, pn.BANDED) + ((P,) if kind == pn.CELL_EULER_TANH else ()):
         _parity(wl, mode)
 
 
