@@ -1,9 +1,9 @@
 // Newton (dense Jacobian) iteration for the matrix cells with D padded to 16
 // or 32, on the FP32 matrix cores.
 //
-// One wavefront owns one chunk of L steps and walks it in sub-chunks of 32
+// One wavefront owns one chunk of L steps and walks it in sub-chunks of 16
 // steps staged through LDS.  Per sub-chunk it
-//   1. computes the input projection U x_t + b once;
+//   1. computes the input projection U x_t + b once, on the matrix cores;
 //   2. evaluates the cell at the old iterate (v_t and the Jacobian row
 //      scalings) and replays s^_t = v_t + A_t (s^_{t-1} - p_t) from the carry,
 //      damps, and stores s^(i+1) [the update of PN §1.2];
@@ -24,6 +24,9 @@
 // of the next step, so the chain never leaves registers.  The A operand
 // (W_g restricted to that k subset) is loaded once into registers and also
 // serves the matrix-vector products of the replay and the offset chain.
+// The cell evaluations of a sub-chunk are one tile product each: with the
+// step index as the A-operand row, G^T = Q W_g^T takes the same register
+// slice of W_g as its B operand (see eval_tile).
 //
 // Lane roles (64 lanes): i = lane % DP is a state row, h = lane / DP picks the
 // k subset K_h = {krow(h, s), s < KS}.  Row-vector dot products are partial
@@ -44,6 +47,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 template <int DP> struct MfmaTile;
 template <> struct MfmaTile<32> {
     static constexpr int NH = 2, KS = 16;
+    static constexpr int NSL = 8;     // accumulator slots r with krow(h, r) < kSub
     typedef v16f acc_t;
     // k index (= output row) of slot s for lane group h
     __device__ static int krow(int h, int s) { return 8 * (s >> 2) + 4 * h + (s & 3); }
@@ -53,6 +57,7 @@ template <> struct MfmaTile<32> {
 };
 template <> struct MfmaTile<16> {
     static constexpr int NH = 4, KS = 4;
+    static constexpr int NSL = 4;
     typedef v4f acc_t;
     __device__ static int krow(int h, int s) { return 4 * h + s; }
     __device__ static acc_t step(float a, float b, acc_t c) {
@@ -92,63 +97,12 @@ struct DLds {
     static __host__ __device__ size_t floats(int m) {
         return 2ull * (kSub + 1) * DP        // P, N rows
              + static_cast<size_t>(kSub) * m  // x rows
-             + static_cast<size_t>(NG) * kSub * DP   // input projection
              + static_cast<size_t>(kSub) * DP        // v
              + static_cast<size_t>(NCO) * kSub * DP  // Jacobian coefficients
              + static_cast<size_t>(NG) * m * DP      // U^T (all gates)
              + 2 * DP;                               // vector exchange
     }
 };
-
-// Cell evaluation for row p (LDS, DP floats) with the lane's partial weights
-// wr[g][s] = W_g[i][krow(h,s)].  Returns v and writes the coefficient values
-// for row i into co[q] (q < NCO).  aux holds the lane row's per-gate hidden
-// biases (GRU) or its step size in aux[0] (Euler).
-template <int CELL, int DP>
-__device__ __forceinline__ float cell_eval_row(const float (&wr)[DTraits<CELL>::NG][MfmaTile<DP>::KS],
-                                               const float* p, const float* xp, int i, int h,
-                                               const float (&aux)[3], float (&co)[DTraits<CELL>::NCO]) {
-    using Tl = MfmaTile<DP>;
-    constexpr int NG = DTraits<CELL>::NG;
-    float acc[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) acc[g] = 0.0f;
-#pragma unroll
-    for (int q = 0; q < Tl::KS / 4; ++q) {
-        const float4 p4 = kgroup<DP>(p, h, q);
-        const float pk[4] = {p4.x, p4.y, p4.z, p4.w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int g = 0; g < NG; ++g) acc[g] += wr[g][4 * q + t] * pk[t];
-    }
-#pragma unroll
-    for (int g = 0; g < NG; ++g) acc[g] = group_sum<DP>(acc[g]);
-    if constexpr (CELL == kCellTanhRnnD) {
-        const float v = tanh_f(acc[0] + xp[0]);
-        co[0] = 1.0f - v * v;
-        return v;
-    } else if constexpr (CELL == kCellEulerD) {
-        const float g = tanh_f(acc[0] + xp[0]);
-        const float pi = p[i];
-        const float hs = aux[0];
-        co[0] = 1.0f - hs;
-        co[1] = hs * (1.0f - g * g);
-        return pi + hs * (g - pi);
-    } else {
-        const float r = sigmoid_f(xp[0] + acc[0] + aux[0]);
-        const float z = sigmoid_f(xp[kSub * DP] + acc[1] + aux[1]);
-        const float gg = acc[2] + aux[2];
-        const float n = tanh_f(xp[2 * kSub * DP] + r * gg);
-        const float pi = p[i];
-        const float dn = (1.0f - z) * (1.0f - n * n);
-        co[0] = z;
-        co[1] = (pi - n) * z * (1.0f - z);
-        co[2] = dn * r;
-        co[3] = dn * gg * r * (1.0f - r);
-        return (1.0f - z) * n + z * pi;
-    }
-}
 
 // (A_t d)[i] for the difference vector d in LDS (only the lane's k subset is
 // read; d_i is passed for the diagonal GRU term).
@@ -182,6 +136,97 @@ __device__ __forceinline__ float jac_apply_row(const float (&wr)[DTraits<CELL>::
     }
 }
 
+// Input projection of the sub-chunk's steps as a tile product: XA[g] holds,
+// in slot r of lane (i, h), (U_g x_j)[i] + bias_g[i] for step j = krow(h, r).
+// The A operand is x row j = lane % DP (zero past the sub-chunk), the B
+// operand U_g[i][q] read from the transposed copy in LDS; the k index q runs
+// over m in groups of 4 NH, zero-padded.
+template <int CELL, int DP>
+__device__ __forceinline__ void proj_tile(const float* X, const float* UT, int m, int Sc, int h, int i,
+                                          const float (&bias)[3],
+                                          typename MfmaTile<DP>::acc_t (&XA)[DTraits<CELL>::NG]) {
+    using Tl = MfmaTile<DP>;
+    constexpr int NG = DTraits<CELL>::NG;
+    const int jl = i;                        // A-operand row: step index
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int r = 0; r < Tl::KS; ++r) XA[g][r] = bias[g];
+    const int SKM = ((m + 4 * Tl::NH - 1) / (4 * Tl::NH)) * 4;
+    for (int s = 0; s < SKM; ++s) {
+        const int q = 4 * Tl::NH * (s >> 2) + 4 * h + (s & 3);
+        const bool qin = q < m;
+        const float a = (jl < Sc && qin) ? X[jl * m + q] : 0.0f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const float bu = qin ? UT[(g * m + q) * DP + i] : 0.0f;
+            XA[g] = Tl::step(a, bu, XA[g]);
+        }
+    }
+}
+
+// Pre-activations of the sub-chunk at the rows Q (Q[j] = state before step j):
+// G[g] = XA[g] + (Q W_g^T) in the slot layout of proj_tile (the GRU's
+// candidate gate keeps its hidden part W_n q separate: G[2] starts at 0).
+template <int CELL, int DP>
+__device__ __forceinline__ void eval_tile(const float* Q, int Sc, int h, int i,
+                                          const float (&wr)[DTraits<CELL>::NG][MfmaTile<DP>::KS],
+                                          const typename MfmaTile<DP>::acc_t (&XA)[DTraits<CELL>::NG],
+                                          typename MfmaTile<DP>::acc_t (&G)[DTraits<CELL>::NG]) {
+    using Tl = MfmaTile<DP>;
+    constexpr int NG = DTraits<CELL>::NG;
+    const int jl = i;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        if (CELL == kCellGruD && g == 2) {
+#pragma unroll
+            for (int r = 0; r < Tl::KS; ++r) G[g][r] = 0.0f;
+        } else {
+            G[g] = XA[g];
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < Tl::KS / 4; ++q) {
+        const float4 a4 = jl < Sc ? kgroup<DP>(Q + jl * DP, h, q) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const float ak[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) G[g] = Tl::step(ak[t], wr[g][4 * q + t], G[g]);
+    }
+}
+
+// v and the Jacobian coefficients of one state at one step, from its
+// pre-activations gv (with the input projection, except the GRU candidate's
+// hidden part), the candidate's input part xn (GRU), the state p_i before
+// the step and the per-row constants aux (GRU hidden biases, Euler step size).
+template <int CELL>
+__device__ __forceinline__ float cell_point(const float (&gv)[3], float xn, float pi, const float (&aux)[3],
+                                            float (&co)[DTraits<CELL>::NCO]) {
+    if constexpr (CELL == kCellTanhRnnD) {
+        const float v = tanh_f(gv[0]);
+        co[0] = 1.0f - v * v;
+        return v;
+    } else if constexpr (CELL == kCellEulerD) {
+        const float g = tanh_f(gv[0]);
+        const float hs = aux[0];
+        co[0] = 1.0f - hs;
+        co[1] = hs * (1.0f - g * g);
+        return pi + hs * (g - pi);
+    } else {
+        const float r = sigmoid_f(gv[0] + aux[0]);
+        const float z = sigmoid_f(gv[1] + aux[1]);
+        const float gg = gv[2] + aux[2];
+        const float n = tanh_f(xn + r * gg);
+        const float dn = (1.0f - z) * (1.0f - n * n);
+        co[0] = z;
+        co[1] = (pi - n) * z * (1.0f - z);
+        co[2] = dn * r;
+        co[3] = dn * gg * r * (1.0f - r);
+        return (1.0f - z) * n + z * pi;
+    }
+}
+
 template <int CELL, int DP, int PHASE, bool BANDED>
 __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
     if constexpr (PHASE != kPrologue && PHASE != kMaps) {   // apply launches enqueued ahead
@@ -207,8 +252,7 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
     float* P = lds;                          // [kSub+1][DP]
     float* N = P + (kSub + 1) * DP;          // [kSub+1][DP]
     float* X = N + (kSub + 1) * DP;          // [kSub][m]
-    float* XP = X + kSub * m;                // [NG][kSub][DP]
-    float* V = XP + NG * kSub * DP;          // [kSub][DP]
+    float* V = X + kSub * m;                 // [kSub][DP]
     float* CO = V + kSub * DP;               // [NCO][kSub][DP]
     float* UT = CO + NCO * kSub * DP;        // [NG][m][DP]
     float* YV = UT + NG * m * DP;            // [2][DP]
@@ -290,24 +334,22 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
             copy_rows_to_lds<64>(P + DP, DP, sg + static_cast<int64_t>(j0) * D, D, Sc, D);
         }
         __syncthreads();
-        // ---- input projection U x + b_ih for every row and gate
-        for (int j = 0; j < Sc; ++j) {
-#pragma unroll
-            for (int gt = 0; gt < NG; ++gt) {
-                float a = 0.0f;
-                for (int q = h; q < m; q += Tl::NH) a += UT[(gt * m + q) * DP + i] * X[j * m + q];
-                a = group_sum<DP>(a);
-                if (h == 0) XP[(gt * kSub + j) * DP + i] = a + bias_i[gt];
-            }
-        }
-        __syncthreads();
+        // ---- input projection U x + b_ih for every row and gate (registers)
+        acc_t XA[NG];
+        proj_tile<CELL, DP>(X, UT, m, Sc, h, i, bias_i, XA);
+        acc_t G[NG];
 
         if constexpr (PHASE != kPrologue && PHASE != kMaps) {
             // ---- maps of iteration i at the old iterate, then the replay
-            for (int j = 0; j < Sc; ++j) {
-                float co[NCO];
-                const float v = cell_eval_row<CELL, DP>(wr, P + j * DP, XP + j * DP + i, i, h, bhh_l, co);
-                if (h == 0) {
+            eval_tile<CELL, DP>(P, Sc, h, i, wr, XA, G);
+#pragma unroll
+            for (int r = 0; r < Tl::NSL; ++r) {
+                const int j = Tl::krow(h, r);
+                if (j < Sc) {
+                    const float gv[3] = {G[0][r], NG > 1 ? G[NG > 1 ? 1 : 0][r] : 0.0f,
+                                         NG > 2 ? G[NG > 2 ? 2 : 0][r] : 0.0f};
+                    float co[NCO];
+                    const float v = cell_point<CELL>(gv, XA[NG - 1][r], P[j * DP + i], bhh_l, co);
                     V[j * DP + i] = live ? v : 0.0f;
 #pragma unroll
                     for (int q = 0; q < NCO; ++q) CO[(q * kSub + j) * DP + i] = live ? co[q] : 0.0f;
@@ -339,15 +381,20 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
         __syncthreads();
 
         // ---- maps of iteration i+1 at the new iterate; residual
-        for (int j = 0; j < Sc; ++j) {
-            float co[NCO];
-            const float v = cell_eval_row<CELL, DP>(wr, N + j * DP, XP + j * DP + i, i, h, bhh_l, co);
-            if (live) {
-                const float d = N[(j + 1) * DP + i] - v;
-                rb = max(rb, abs_bits(d));
-                if (track && !(fabsf(d) <= g.tol)) fb = min(fb, static_cast<uint32_t>(j0 + j));
-            }
-            if (h == 0) {
+        eval_tile<CELL, DP>(N, Sc, h, i, wr, XA, G);
+#pragma unroll
+        for (int r = 0; r < Tl::NSL; ++r) {
+            const int j = Tl::krow(h, r);
+            if (j < Sc) {
+                const float gv[3] = {G[0][r], NG > 1 ? G[NG > 1 ? 1 : 0][r] : 0.0f,
+                                     NG > 2 ? G[NG > 2 ? 2 : 0][r] : 0.0f};
+                float co[NCO];
+                const float v = cell_point<CELL>(gv, XA[NG - 1][r], N[j * DP + i], bhh_l, co);
+                if (live) {
+                    const float d = N[(j + 1) * DP + i] - v;
+                    rb = max(rb, abs_bits(d));
+                    if (track && !(fabsf(d) <= g.tol)) fb = min(fb, static_cast<uint32_t>(j0 + j));
+                }
                 V[j * DP + i] = live ? v : 0.0f;
 #pragma unroll
                 for (int q = 0; q < NCO; ++q) CO[(q * kSub + j) * DP + i] = live ? co[q] : 0.0f;
