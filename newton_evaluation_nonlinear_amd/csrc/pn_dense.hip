@@ -488,11 +488,15 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
 // 32x32x2 FP32 MFMA, 128 steps per time step.  The lane's A operands,
 // wr[I][K][s] = W[32I + r][32K + krow(h, s)], also give its two rows r and
 // 32 + r of every matrix-vector product (partial sums over its k subset plus
-// the partner lane l ^ 32).  Each lane writes its own row l of the LDS rows.
+// the partner lane l ^ 32).  The same registers are the B operand of the
+// sub-chunk's cell evaluation, two 32 x 32 tiles G_I = Q W_I^T + X U_I^T
+// with the step index as the A-operand row (tile I, slot q: step krow(h, q)
+// of state 32I + r).  Each lane writes its own row l of the LDS rows in the
+// replay and its tile entries in the evaluation.
 template <int CELL> struct D64Lds {
     static constexpr int NCO = DTraits<CELL>::NCO;
     static __host__ __device__ size_t floats(int m) {
-        return 2ull * (kSub + 1) * 64 + static_cast<size_t>(kSub) * m + 3ull * kSub * 64 +
+        return 2ull * (kSub + 1) * 64 + static_cast<size_t>(kSub) * m + 1ull * kSub * 64 +
                static_cast<size_t>(NCO) * kSub * 64 + static_cast<size_t>(m) * 64 + 2 * 64;
     }
 };
@@ -523,8 +527,7 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
     float* P = lds;                           // [kSub+1][64]
     float* N = P + (kSub + 1) * DP;           // [kSub+1][64]
     float* X = N + (kSub + 1) * DP;           // [kSub][m]
-    float* XP = X + kSub * m;                 // [kSub][64]
-    float* V = XP + kSub * DP;                // [kSub][64]
+    float* V = X + kSub * m;                  // [kSub][64]
     float* CO = V + kSub * DP;                // [NCO][kSub][64]
     float* UT = CO + NCO * kSub * DP;         // [m][64]
     float* YV = UT + m * DP;                  // [2][64]
@@ -545,7 +548,7 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
                 wj[I][K][s] = (!BANDED || abs(k - row) <= g.band) ? wr[I][K][s] : 0.0f;
             }
     copy_to_lds<64>(UT, wUT, m * DP);
-    const float bias_o = wbi[orow];
+    const float bias2[2] = {wbi[r], wbi[32 + r]};
     float hs[2] = {0.0f, 0.0f};               // Euler step sizes of rows r, 32 + r
     if constexpr (CELL == kCellEulerD) {
         hs[0] = wbi[2 * DP + r];
@@ -572,23 +575,45 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
         o[0] = a0;
         o[1] = a1;
     };
-    // cell at row p of LDS (inputs XP row j): values and coefficients of rows r, 32 + r
-    auto eval = [&](const float* p, int j, float (&v)[2], float (&co)[2][NCO]) {
-        float u[2];
-        matvec(wr, p, u);
+    // Pre-activations of the sub-chunk's steps at the rows Q (Q[j] = state
+    // before step j): G[I] slot q = (W q_j + U x_j + b)[32I + r], j = krow(h, q).
+    auto eval_tiles = [&](const float* Q, int Sc, v16f (&G)[2]) {
 #pragma unroll
-        for (int I = 0; I < 2; ++I) {
-            const float pre = u[I] + XP[j * DP + 32 * I + r];
-            if constexpr (CELL == kCellTanhRnnD) {
-                v[I] = tanh_f(pre);
-                co[I][0] = 1.0f - v[I] * v[I];
-            } else {
-                const float gv = tanh_f(pre);
-                const float pi = p[32 * I + r];
-                v[I] = pi + hs[I] * (gv - pi);
-                co[I][0] = 1.0f - hs[I];
-                co[I][NCO - 1] = hs[I] * (1.0f - gv * gv);
+        for (int I = 0; I < 2; ++I)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) G[I][q] = bias2[I];
+        const int SKM = ((m + 7) / 8) * 4;
+        for (int s2 = 0; s2 < SKM; ++s2) {
+            const int q = 8 * (s2 >> 2) + 4 * h + (s2 & 3);
+            const bool qin = q < m;
+            const float a = (r < Sc && qin) ? X[r * m + q] : 0.0f;
+#pragma unroll
+            for (int I = 0; I < 2; ++I) G[I] = Tl::step(a, qin ? UT[q * DP + 32 * I + r] : 0.0f, G[I]);
+        }
+#pragma unroll
+        for (int K = 0; K < 2; ++K)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const float4 a4 = r < Sc ? *reinterpret_cast<const float4*>(Q + r * DP + 32 * K + 8 * qq + 4 * h)
+                                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                const float ak[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int I = 0; I < 2; ++I) G[I] = Tl::step(ak[t], wr[I][K][4 * qq + t], G[I]);
             }
+    };
+    // v and coefficients of state 32I + r at step j from its pre-activation
+    auto point = [&](float pre, float pi, int I, float (&co)[NCO]) {
+        if constexpr (CELL == kCellTanhRnnD) {
+            const float v = tanh_f(pre);
+            co[0] = 1.0f - v * v;
+            return v;
+        } else {
+            const float gv = tanh_f(pre);
+            co[0] = 1.0f - hs[I];
+            co[NCO - 1] = hs[I] * (1.0f - gv * gv);
+            return pi + hs[I] * (gv - pi);
         }
     };
     // A~ d for rows r, 32 + r, d in LDS; dd: the lane's two entries of d
@@ -657,23 +682,25 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
             copy_rows_to_lds<64>(P + DP, DP, sg + static_cast<int64_t>(j0) * D, D, Sc, D);
         }
         __syncthreads();
-        // input projection U x + b for the lane's own row
-        for (int j = 0; j < Sc; ++j) {
-            float a = bias_o;
-            for (int q = 0; q < m; ++q) a += UT[q * DP + orow] * X[j * m + q];
-            XP[j * DP + orow] = olive ? a : 0.0f;
-        }
-        __syncthreads();
+        v16f G[2];
 
         if constexpr (PHASE != kPrologue && PHASE != kMaps) {
             // maps of iteration i at the old iterate
-            for (int j = 0; j < Sc; ++j) {
-                float v[2], co[2][NCO];
-                eval(P + j * DP, j, v, co);
-                V[j * DP + orow] = olive ? own(v) : 0.0f;
+            eval_tiles(P, Sc, G);
 #pragma unroll
-                for (int q = 0; q < NCO; ++q) CO[(q * kSub + j) * DP + orow] = olive ? (h ? co[1][q] : co[0][q]) : 0.0f;
-            }
+            for (int I = 0; I < 2; ++I)
+#pragma unroll
+                for (int q = 0; q < Tl::NSL; ++q) {
+                    const int j = Tl::krow(h, q), row = 32 * I + r;
+                    if (j < Sc) {
+                        float co[NCO];
+                        const float v = point(G[I][q], P[j * DP + row], I, co);
+                        const bool lv = row < D;
+                        V[j * DP + row] = lv ? v : 0.0f;
+#pragma unroll
+                        for (int u = 0; u < NCO; ++u) CO[(u * kSub + j) * DP + row] = lv ? co[u] : 0.0f;
+                    }
+                }
             __syncthreads();
             // replay from the carry, damping
             for (int j = 0; j < Sc; ++j) {
@@ -711,21 +738,26 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
         __syncthreads();
 
         // maps of iteration i+1 at the new iterate; residual
-        for (int j = 0; j < Sc; ++j) {
-            float v[2], co[2][NCO];
-            eval(N + j * DP, j, v, co);
+        eval_tiles(N, Sc, G);
 #pragma unroll
-            for (int I = 0; I < 2; ++I) {
-                if (32 * I + r < D) {
-                    const float d = N[(j + 1) * DP + 32 * I + r] - v[I];
-                    rb = max(rb, abs_bits(d));
-                    if (track && !(fabsf(d) <= g.tol)) fb = min(fb, static_cast<uint32_t>(j0 + j));
+        for (int I = 0; I < 2; ++I)
+#pragma unroll
+            for (int q = 0; q < Tl::NSL; ++q) {
+                const int j = Tl::krow(h, q), row = 32 * I + r;
+                if (j < Sc) {
+                    float co[NCO];
+                    const float v = point(G[I][q], N[j * DP + row], I, co);
+                    const bool lv = row < D;
+                    if (lv) {
+                        const float d = N[(j + 1) * DP + row] - v;
+                        rb = max(rb, abs_bits(d));
+                        if (track && !(fabsf(d) <= g.tol)) fb = min(fb, static_cast<uint32_t>(j0 + j));
+                    }
+                    V[j * DP + row] = lv ? v : 0.0f;
+#pragma unroll
+                    for (int u = 0; u < NCO; ++u) CO[(u * kSub + j) * DP + row] = lv ? co[u] : 0.0f;
                 }
             }
-            V[j * DP + orow] = olive ? own(v) : 0.0f;
-#pragma unroll
-            for (int q = 0; q < NCO; ++q) CO[(q * kSub + j) * DP + orow] = olive ? (h ? co[1][q] : co[0][q]) : 0.0f;
-        }
         __syncthreads();
 
         // extend the chunk map over the sub-chunk
