@@ -958,8 +958,101 @@ __global__ __launch_bounds__(64) void dense_carry_kernel(CarryArgs g) {
     }
 }
 
+// Wide form for D padded to 32 or 64 (D a multiple of 4): one workgroup of
+// DP x DP/4 threads per batch row.  Thread (i, p) owns the 16-byte piece p of
+// row i of every chunk map, so a chunk map arrives as one coalesced 16-byte
+// load per thread and kKW chunks are in flight per workgroup (DP/4 times the
+// bytes of the one-wavefront chain, whose time per chunk is the latency of
+// its map loads).  The DP/4 partial dot products of a row sit in adjacent
+// lanes of one 16-lane DPP row and are summed with DPP moves (swap neighbours,
+// swap pairs, mirror within 8, mirror within 16); the new carry goes through
+// a double-buffered LDS vector with one barrier per chunk.
+// Every global access of the unrolled body is unconditional (clamped
+// addresses and selects; threads of rows past D redo row D-1 and store the
+// same value again), so the compiler can count the loads issued after each
+// prefetch and wait for that one only.
+constexpr int kKW = 16;                      // chunk maps in flight per thread
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+template <int DP>
+__global__ __launch_bounds__(DP * DP / 4) void dense_carry_wide(CarryArgs g) {
+    if (g.do_check && blockIdx.x == 0) run_check(g.chk);
+    constexpr int TPR = DP / 4;              // threads per map row
+    __shared__ __attribute__((aligned(16))) float ys[2][DP];
+    const int t = threadIdx.x;
+    const int i = t / TPR, p = t % TPR;
+    const int D = g.D;
+    const bool live = i < D, pin = 4 * p < D;
+    const int ir = live ? i : D - 1;
+    const int pc = pin ? 4 * p : 0;          // clamped column of the piece
+    const int b = blockIdx.x;
+    const size_t cb = static_cast<size_t>(b) * g.NC;
+    const int steps = g.NC - 1;
+    if (p == 0) {
+        const float y0 = live ? g.s0[b * g.s0s + i] : 0.0f;
+        ys[0][i] = y0;
+        if (live) g.carry[cb * D + i] = y0;
+    }
+    if (steps <= 0) return;
+    const float* Mb = g.aggA + cb * D * D + static_cast<size_t>(ir) * D + pc;
+    const float* Bb = g.aggB + cb * D + ir;
+    float* Cb = g.carry + (cb + 1) * D + ir;
+    const size_t DD = static_cast<size_t>(D) * D;
+    float4 ring[kKW];
+    float ob[kKW];
+#pragma unroll
+    for (int u = 0; u < kKW; ++u) {
+        const int c = min(u, steps - 1);
+        ring[u] = *reinterpret_cast<const float4*>(Mb + c * DD);
+        ob[u] = Bb[static_cast<size_t>(c) * D];
+    }
+    __syncthreads();
+    // one chunk: y_i = row i of M_c . y + bg_c
+    auto step = [&](int c, const float4& m4, float off) {
+        const float4 mv = pin ? m4 : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const float4 yv = *reinterpret_cast<const float4*>(&ys[c & 1][4 * p]);
+        float part = (mv.x * yv.x + mv.y * yv.y) + (mv.z * yv.z + mv.w * yv.w);
+        part = dpp_add<0xB1>(part);                          // quad_perm [1,0,3,2]
+        part = dpp_add<0x4E>(part);                          // quad_perm [2,3,0,1]
+        if constexpr (TPR >= 8) part = dpp_add<0x141>(part);   // row_half_mirror
+        if constexpr (TPR >= 16) part = dpp_add<0x140>(part);  // row_mirror
+        const float y = part + off;
+        Cb[static_cast<size_t>(c) * D] = y;
+        if (p == 0) ys[(c + 1) & 1][i] = live ? y : 0.0f;
+    };
+    int c0 = 0;
+    for (; c0 + kKW <= steps; c0 += kKW) {
+#pragma unroll
+        for (int u = 0; u < kKW; ++u) {
+            const int c = c0 + u;
+            step(c, ring[u], ob[u]);
+            const int cn = min(c + kKW, steps - 1);
+            ring[u] = *reinterpret_cast<const float4*>(Mb + cn * DD);
+            ob[u] = Bb[static_cast<size_t>(cn) * D];
+            __syncthreads();
+        }
+    }
+    // the last steps - c0 < kKW chunks are already in ring[0 ..]
+#pragma unroll
+    for (int u = 0; u < kKW; ++u) {
+        if (c0 + u < steps) {
+            step(c0 + u, ring[u], ob[u]);
+            __syncthreads();
+        }
+    }
+}
+
 hipError_t launch_dense_carry(const CarryArgs& a, hipStream_t st) {
     const int DP = a.D <= 4 ? 4 : a.D <= 8 ? 8 : a.D <= 16 ? 16 : a.D <= 32 ? 32 : 64;
+    if (a.D % 4 == 0 && DP >= 32) {
+        if (DP == 32) dense_carry_wide<32><<<a.B, 32 * 8, 0, st>>>(a);
+        else dense_carry_wide<64><<<a.B, 64 * 16, 0, st>>>(a);
+        return hipGetLastError();
+    }
     switch (DP) {
         case 4: dense_carry_kernel<4><<<a.B, 64, 0, st>>>(a); break;
         case 8: dense_carry_kernel<8><<<a.B, 64, 0, st>>>(a); break;
