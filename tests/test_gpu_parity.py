@@ -182,6 +182,24 @@ def test_matrix_cells_other_widths(kind, D):
         _parity(wl, mode)
 
 
+@pytest.mark.parametrize("kind, D, m", [(pn.CELL_TANH_RNN, 24, 37), (pn.CELL_GRU, 16, 19),
+                                         (pn.CELL_EULER_TANH, 48, 21), (pn.CELL_TANH_RNN, 36, 5),
+                                         (pn.CELL_TANH_RNN, 64, 33)])
+def test_matrix_core_paths_input_widths(kind, D, m):
+    # the matrix-core kernels at input widths that span several k-groups of
+    # the input projection with a ragged last group, and at state widths
+    # below the padded width (the carry's rows and columns past D); a chunk
+    # length of 32 gives several chunks and a ragged last sub-chunk
+    rng = np.random.default_rng(400 + D + m)
+    B, T = 3, 333
+    params = workloads.lattice_cell_params(kind, D, m, rng)
+    wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-6, damping=1.0, window=0,
+              max_iter=T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32), bandwidth=2)
+    for mode in (N, pn.BANDED):
+        _parity(wl, mode, chunk=32)
+
+
 @pytest.mark.parametrize("k", [1, 2, 3])
 @pytest.mark.parametrize("D", [5, 12, 20, 33, 64])
 @pytest.mark.parametrize("kind", [pn.CELL_TANH_RNN, pn.CELL_GRU])

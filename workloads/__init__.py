@@ -159,7 +159,8 @@ def lattice_cell_params(kind, D, m, rng, band=2, eps=0.05, rho=0.9):
     """Locally coupled recurrent weights for tests (float32, flat C layout):
     every recurrent matrix couples units within distance ``band``, plus a
     dense part of relative size ``eps``.  tanh RNN: W rescaled to spectral
-    radius ``rho``; GRU: each W_hh gate block rescaled likewise."""
+    radius ``rho``; GRU: each W_hh gate block rescaled likewise; Euler step:
+    the tanh RNN's W, U, b and step size 0.1 for every unit."""
     i = np.arange(D)
     near = np.abs(i[:, None] - i[None, :]) <= band
 
@@ -176,6 +177,12 @@ def lattice_cell_params(kind, D, m, rng, band=2, eps=0.05, rho=0.9):
         W_ih, _, b_ih, b_hh = _gru_weights(rng, D, m)
         W_hh = np.concatenate([lattice() for _ in range(3)], axis=0)
         return np.concatenate([W_ih.ravel(), W_hh.ravel(), b_ih, b_hh]).astype(np.float32)
+    if kind == CELL_EULER_TANH:
+        W = lattice()
+        U = rng.standard_normal((D, m)) / np.sqrt(m)
+        b = rng.standard_normal(D) * 0.1
+        h = np.full(D, 0.1)
+        return np.concatenate([W.ravel(), U.ravel(), b, h]).astype(np.float32)
     raise ValueError(kind)
 
 
