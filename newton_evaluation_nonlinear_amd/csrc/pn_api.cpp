@@ -128,9 +128,12 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
         p.DP = 0;
     } else if (p.dense && (next_pow2(p.D) == 16 || next_pow2(p.D) == 32 || next_pow2(p.D) == 64) &&
                dense_mfma_supported(p.kind, next_pow2(p.D), p.m)) {
-        // Newton on the matrix cores: one wavefront per chunk; chunks long
-        // enough to keep the serial carry short, with ~2048 chunks in flight
-        // (about two wavefronts per SIMD).
+        // Newton on the matrix cores: one wavefront per chunk (two when the
+        // chunks are few); chunks long enough to keep the serial carry
+        // short, with ~2048 chunks in flight (about two wavefronts per
+        // SIMD), and shorter ones (down to 16 steps) while fewer than 1024
+        // chunks would leave SIMDs idle: each launch then takes about the
+        // time of one chunk's serial steps.
         p.mfma = true;
         p.DP = next_pow2(p.D);
         int64_t L = 64;
@@ -138,6 +141,7 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
             L = chunk;
         } else {
             while (L < 512 && static_cast<int64_t>(B) * ((p.W + 2 * L - 1) / (2 * L)) >= 2048) L *= 2;
+            while (L > 16 && static_cast<int64_t>(B) * ((p.W + L - 1) / L) < 1024) L /= 2;
         }
         p.L = static_cast<int>(std::min<int64_t>(L, p.W));
         p.NC = static_cast<int>((p.W + p.L - 1) / p.L);

@@ -90,15 +90,22 @@ template <> struct DTraits<kCellTanhRnnD> { static constexpr int NG = 1, NCO = 1
 template <> struct DTraits<kCellGruD> { static constexpr int NG = 3, NCO = 4; };
 template <> struct DTraits<kCellEulerD> { static constexpr int NG = 1, NCO = 2; };
 
-// LDS layout (floats) for one wave / one chunk.
+// Rows exchanged between the lanes of one wavefront: its LDS accesses execute
+// in program order, so a compiler barrier orders them (the data role of the
+// split kernel cannot take the workgroup barrier, which the chain wavefront
+// meets once per sub-chunk).
+__device__ __forceinline__ void wave_sync() { __builtin_amdgcn_wave_barrier(); }
+
+// LDS layout (floats) for one chunk; split: the replay's coefficients and
+// two sets of the next iteration's (one set serves all three otherwise).
 template <int CELL, int DP>
 struct DLds {
     static constexpr int NG = DTraits<CELL>::NG, NCO = DTraits<CELL>::NCO;
-    static __host__ __device__ size_t floats(int m) {
+    static __host__ __device__ size_t floats(int m, bool split) {
         return 2ull * (kSub + 1) * DP        // P, N rows
              + static_cast<size_t>(kSub) * m  // x rows
              + static_cast<size_t>(kSub) * DP        // v
-             + static_cast<size_t>(NCO) * kSub * DP  // Jacobian coefficients
+             + (split ? 3ull : 1ull) * NCO * kSub * DP  // Jacobian coefficients
              + static_cast<size_t>(NG) * m * DP      // U^T (all gates)
              + 2 * DP;                               // vector exchange
     }
@@ -227,8 +234,16 @@ __device__ __forceinline__ float cell_point(const float (&gv)[3], float xn, floa
     }
 }
 
-template <int CELL, int DP, int PHASE, bool BANDED>
-__global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
+// SPLIT: two wavefronts per chunk.  Wavefront 0 runs only the chunk-map
+// chain (the matrix-core steps and row scalings); wavefront 1 runs
+// everything else (staging, the cell tiles, replay, residual and the offset
+// chain) one sub-chunk ahead, publishing the coefficients of sub-chunk k in
+// one of two LDS buffers before the workgroup barrier k.  The dependent
+// latency chains of the two roles then overlap within one chunk, which pays
+// when there are too few chunks to fill the SIMDs with other chunks; with
+// many chunks one wavefront per chunk runs both roles (more chunks resident).
+template <int CELL, int DP, int PHASE, bool BANDED, bool SPLIT>
+__global__ __launch_bounds__(SPLIT ? 128 : 64) void dense_pass(CellArgs g) {
     if constexpr (PHASE != kPrologue && PHASE != kMaps) {   // apply launches enqueued ahead
         if (g.ctrl->stop) return;
     }
@@ -237,14 +252,16 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
     constexpr int NG = DTraits<CELL>::NG;
     constexpr int NCO = DTraits<CELL>::NCO;
     constexpr int KS = Tl::KS;
+    constexpr int COS = NCO * kSub * DP;      // floats of one coefficient set
     extern __shared__ float lds[];
     const int D = g.D, m = g.m;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int i = lane % DP, h = lane / DP;
     const bool live = i < D;
     const int c = blockIdx.x, b = blockIdx.y;
     const int t0 = c * g.L;
     const int Lc = min(g.L, g.Tw - t0);
+    const int nsub = (Lc + kSub - 1) / kSub;
     const size_t ci = static_cast<size_t>(b) * g.NC + c;
     const size_t HS = static_cast<size_t>(g.B) * g.NC * D;
     const float* s0 = g.s0 + b * g.s0s;
@@ -253,9 +270,13 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
     float* N = P + (kSub + 1) * DP;          // [kSub+1][DP]
     float* X = N + (kSub + 1) * DP;          // [kSub][m]
     float* V = X + kSub * m;                 // [kSub][DP]
-    float* CO = V + kSub * DP;               // [NCO][kSub][DP]
-    float* UT = CO + NCO * kSub * DP;        // [NG][m][DP]
+    float* COr = V + kSub * DP;              // [NCO][kSub][DP] iteration i (replay)
+    // iteration i+1, per sub-chunk parity (one wavefront: the same buffer,
+    // consumed before the next sub-chunk overwrites it)
+    float* CO2 = SPLIT ? COr + COS : COr;
+    float* UT = COr + (SPLIT ? 3 : 1) * COS; // [NG][m][DP]
     float* YV = UT + NG * m * DP;            // [2][DP]
+    auto co_set = [&](int k) { return CO2 + (SPLIT ? (k & 1) * COS : 0); };
 
     const float* w = g.w;
     // prepared layout: tanh RNN WT | UT | bias | wdiag (Euler: | h);
@@ -263,19 +284,89 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
     const float* wUT = w + NG * DP * DP;
     const float* wbi = wUT + NG * m * DP;
     const float* wbh = wbi + NG * DP;         // GRU only
+    // weights of the Jacobian products: W_g itself, or its band
+    float wj[NG][KS];
+#pragma unroll
+    for (int gt = 0; gt < NG; ++gt)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int k = Tl::krow(h, s);
+            const float wv = w[(gt * DP + k) * DP + i];
+            wj[gt][s] = (!BANDED || abs(k - i) <= g.band) ? wv : 0.0f;
+        }
+
+    // chunk map: M in accumulator layout (column lane%DP, rows krow(h, r))
+    acc_t M;
+#pragma unroll
+    for (int r = 0; r < KS; ++r) M[r] = (Tl::krow(h, r) == i && live) ? 1.0f : 0.0f;
+    // one chain step: C_g = W_g M, then M <- A_j M from the row scalings
+    auto products = [&](acc_t (&C)[NG]) {
+#pragma unroll
+        for (int gt = 0; gt < NG; ++gt) {
+#pragma unroll
+            for (int r = 0; r < KS; ++r) C[gt][r] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) C[gt] = Tl::step(wj[gt][s], M[s], C[gt]);
+        }
+    };
+    auto scale = [&](const acc_t (&C)[NG], const float* COk, int j) {
+        float rs[NCO][KS];
+#pragma unroll
+        for (int q = 0; q < NCO; ++q)
+#pragma unroll
+            for (int u = 0; u < KS / 4; ++u) {
+                const float4 c4 = kgroup<DP>(COk + (q * kSub + j) * DP, h, u);
+                rs[q][4 * u] = c4.x;
+                rs[q][4 * u + 1] = c4.y;
+                rs[q][4 * u + 2] = c4.z;
+                rs[q][4 * u + 3] = c4.w;
+            }
+#pragma unroll
+        for (int r = 0; r < KS; ++r) {
+            if constexpr (CELL == kCellTanhRnnD) {
+                M[r] = rs[0][r] * C[0][r];
+            } else if constexpr (CELL == kCellEulerD) {
+                M[r] = rs[0][r] * M[r] + rs[1][r] * C[0][r];
+            } else {
+                M[r] = rs[0][r] * M[r] + rs[1][r] * C[1][r] + rs[2][r] * C[2][r] + rs[3][r] * C[0][r];
+            }
+        }
+    };
+    auto write_map = [&]() {
+        // chunk map out: M[row][col] row-major, col = i
+        float* aA = g.aggA + ci * D * D;
+#pragma unroll
+        for (int r = 0; r < KS; ++r) {
+            const int row = Tl::krow(h, r);
+            if (row < D && live) aA[row * D + i] = M[r];
+        }
+    };
+
+    if constexpr (SPLIT) {
+        if (threadIdx.x < 64) {
+            // ---- chain wavefront: sub-chunk k once its coefficients are out (barrier k)
+            for (int k = 0; k < nsub; ++k) {
+                __syncthreads();
+                const int Sc = min(kSub, Lc - k * kSub);
+                const float* COk = co_set(k);
+                for (int j = 0; j < Sc; ++j) {
+                    acc_t C[NG];
+                    products(C);
+                    scale(C, COk, j);
+                }
+            }
+            write_map();
+            return;
+        }
+    }
+
+    // ---- data role: staging, cell tiles, replay, residual, offset chain
     float wr[NG][KS];
 #pragma unroll
     for (int gt = 0; gt < NG; ++gt)
 #pragma unroll
         for (int s = 0; s < KS; ++s) wr[gt][s] = w[(gt * DP + Tl::krow(h, s)) * DP + i];
-    // weights of the Jacobian products: wr itself, or its band
-    float wj[NG][KS];
-#pragma unroll
-    for (int gt = 0; gt < NG; ++gt)
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            wj[gt][s] = (!BANDED || abs(Tl::krow(h, s) - i) <= g.band) ? wr[gt][s] : 0.0f;
-    copy_to_lds<64>(UT, wUT, NG * m * DP);
+    copy_to_lds<64>(UT, wUT, NG * m * DP, lane);
     const float bias_i[3] = {wbi[i], NG > 1 ? wbi[DP + i] : 0.0f, NG > 2 ? wbi[2 * DP + i] : 0.0f};
     float bhh_l[3] = {0.0f, 0.0f, 0.0f};
     if constexpr (CELL == kCellGruD) {
@@ -286,15 +377,10 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
         bhh_l[0] = wbi[2 * DP + i];          // step size h_i
     }
 
-    // chunk map: M in accumulator layout (column lane%DP, rows krow(h, r)), offset bg[i]
-    acc_t M;
-#pragma unroll
-    for (int r = 0; r < KS; ++r) M[r] = (Tl::krow(h, r) == i && live) ? 1.0f : 0.0f;
-    float bg = 0.0f;
+    float bg = 0.0f;                         // chunk offset, row i
     uint32_t rb = 0;
     const bool track = g.fpart != nullptr;   // first step over tol (advancing window)
     uint32_t fb = 0xffffffffu;
-
     const bool has_next = c + 1 < g.NC;
     const float* cr = g.carry + ci * D;
     float shat = 0.0f;                       // s^ at the row before the current one (lane row i)
@@ -321,26 +407,27 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
         }
     }
 
-    for (int j0 = 0; j0 < Lc; j0 += kSub) {
+    // Sub-chunk k: stage its rows, evaluate the cell at the old iterate and
+    // replay (apply launches), store, then evaluate at the new iterate:
+    // residual, V and the coefficients of iteration i+1 (co_set(k)).
+    auto process = [&](int k) {
+        const int j0 = k * kSub;
         const int Sc = min(kSub, Lc - j0);
-        // ---- stage x rows and the old iterate rows j0 .. j0+Sc-1 (P[1..Sc])
-        copy_to_lds<64>(X, xg + static_cast<int64_t>(j0) * m, Sc * m);
+        copy_to_lds<64>(X, xg + static_cast<int64_t>(j0) * m, Sc * m, lane);
         if constexpr (PHASE == kPrologue || PHASE == kFirst) {
             for (int e = lane; e < Sc * DP; e += 64) {
                 const int q = e % DP;
                 P[DP + e] = q < D ? s0[q] : 0.0f;
             }
         } else {
-            copy_rows_to_lds<64>(P + DP, DP, sg + static_cast<int64_t>(j0) * D, D, Sc, D);
+            copy_rows_to_lds<64>(P + DP, DP, sg + static_cast<int64_t>(j0) * D, D, Sc, D, lane);
         }
-        __syncthreads();
-        // ---- input projection U x + b_ih for every row and gate (registers)
+        wave_sync();
+        // input projection U x + b_ih for every row and gate (registers)
         acc_t XA[NG];
         proj_tile<CELL, DP>(X, UT, m, Sc, h, i, bias_i, XA);
         acc_t G[NG];
-
         if constexpr (PHASE != kPrologue && PHASE != kMaps) {
-            // ---- maps of iteration i at the old iterate, then the replay
             eval_tile<CELL, DP>(P, Sc, h, i, wr, XA, G);
 #pragma unroll
             for (int r = 0; r < Tl::NSL; ++r) {
@@ -352,24 +439,24 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
                     const float v = cell_point<CELL>(gv, XA[NG - 1][r], P[j * DP + i], bhh_l, co);
                     V[j * DP + i] = live ? v : 0.0f;
 #pragma unroll
-                    for (int q = 0; q < NCO; ++q) CO[(q * kSub + j) * DP + i] = live ? co[q] : 0.0f;
+                    for (int q = 0; q < NCO; ++q) COr[(q * kSub + j) * DP + i] = live ? co[q] : 0.0f;
                 }
             }
-            __syncthreads();
+            wave_sync();
             for (int j = 0; j < Sc; ++j) {
                 const float di = live ? shat - P[j * DP + i] : 0.0f;
                 if (h == 0) YV[i] = di;
-                __syncthreads();
+                wave_sync();
                 float co[NCO];
 #pragma unroll
-                for (int q = 0; q < NCO; ++q) co[q] = CO[(q * kSub + j) * DP + i];
+                for (int q = 0; q < NCO; ++q) co[q] = COr[(q * kSub + j) * DP + i];
                 const float ad = jac_apply_row<CELL, DP>(wj, YV, h, co, di);
                 shat = V[j * DP + i] + ad;
                 if (j0 + j == Lc - 1 && has_next && live) shat = cr[D + i];
                 const float so = P[(j + 1) * DP + i];
                 const float sn = g.undamped ? shat : so + g.lam * (shat - so);
                 if (h == 0) N[(j + 1) * DP + i] = live ? sn : 0.0f;
-                __syncthreads();
+                wave_sync();
             }
             for (int e = lane; e < Sc * D; e += 64) {
                 const int j = e / D, q = e % D;
@@ -378,9 +465,8 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
         } else {
             for (int e = lane; e < Sc * DP; e += 64) N[DP + e] = P[DP + e];
         }
-        __syncthreads();
-
-        // ---- maps of iteration i+1 at the new iterate; residual
+        wave_sync();
+        float* COk = co_set(k);
         eval_tile<CELL, DP>(N, Sc, h, i, wr, XA, G);
 #pragma unroll
         for (int r = 0; r < Tl::NSL; ++r) {
@@ -397,79 +483,49 @@ __global__ __launch_bounds__(64) void dense_pass(CellArgs g) {
                 }
                 V[j * DP + i] = live ? v : 0.0f;
 #pragma unroll
-                for (int q = 0; q < NCO; ++q) CO[(q * kSub + j) * DP + i] = live ? co[q] : 0.0f;
+                for (int q = 0; q < NCO; ++q) COk[(q * kSub + j) * DP + i] = live ? co[q] : 0.0f;
             }
         }
-        __syncthreads();
+        wave_sync();
+    };
 
-        // ---- extend the chunk map over the sub-chunk
+    process(0);
+    for (int k = 0; k < nsub; ++k) {
+        if constexpr (SPLIT) __syncthreads();   // coefficients of sub-chunk k are out
+        const int Sc = min(kSub, Lc - k * kSub);
+        const float* COk = co_set(k);
         for (int j = 0; j < Sc; ++j) {
-            // W_g M for each gate, then row-scale and combine
             acc_t C[NG];
-#pragma unroll
-            for (int gt = 0; gt < NG; ++gt) {
-#pragma unroll
-                for (int r = 0; r < KS; ++r) C[gt][r] = 0.0f;
-#pragma unroll
-                for (int s = 0; s < KS; ++s) C[gt] = Tl::step(wj[gt][s], M[s], C[gt]);
-            }
-            // offset: bg <- A_j (bg - p_j) + v_j  (p_j = N[j])
+            if constexpr (!SPLIT) products(C);
+            // offset of the chunk map: bg <- A_j (bg - p_j) + v_j  (p_j = N[j])
             const float dbi = live ? bg - N[j * DP + i] : 0.0f;
             if (h == 0) YV[DP + i] = dbi;
-            __syncthreads();
-            {
-                float co[NCO];
+            wave_sync();
+            float co[NCO];
 #pragma unroll
-                for (int q = 0; q < NCO; ++q) co[q] = CO[(q * kSub + j) * DP + i];
-                bg = V[j * DP + i] + jac_apply_row<CELL, DP>(wj, YV + DP, h, co, dbi);
-            }
-            // row scalings of the lane's accumulator rows
-            float rs[NCO][KS];
-#pragma unroll
-            for (int q = 0; q < NCO; ++q)
-#pragma unroll
-                for (int u = 0; u < KS / 4; ++u) {
-                    const float4 c4 = kgroup<DP>(CO + (q * kSub + j) * DP, h, u);
-                    rs[q][4 * u] = c4.x;
-                    rs[q][4 * u + 1] = c4.y;
-                    rs[q][4 * u + 2] = c4.z;
-                    rs[q][4 * u + 3] = c4.w;
-                }
-#pragma unroll
-            for (int r = 0; r < KS; ++r) {
-                if constexpr (CELL == kCellTanhRnnD) {
-                    M[r] = rs[0][r] * C[0][r];
-                } else if constexpr (CELL == kCellEulerD) {
-                    M[r] = rs[0][r] * M[r] + rs[1][r] * C[0][r];
-                } else {
-                    M[r] = rs[0][r] * M[r] + rs[1][r] * C[1][r] + rs[2][r] * C[2][r] + rs[3][r] * C[0][r];
-                }
-            }
-            __syncthreads();
+            for (int q = 0; q < NCO; ++q) co[q] = COk[(q * kSub + j) * DP + i];
+            bg = V[j * DP + i] + jac_apply_row<CELL, DP>(wj, YV + DP, h, co, dbi);
+            if constexpr (!SPLIT) scale(C, COk, j);
+            wave_sync();
         }
-        // ---- carry the last rows into the next sub-chunk
+        // carry the last rows into the next sub-chunk
         const float plast = P[Sc * DP + i];
         const float nlast = N[Sc * DP + i];
-        __syncthreads();
+        wave_sync();
         if (h == 0) {
             P[i] = plast;
             N[i] = nlast;
         }
-        __syncthreads();
+        wave_sync();
+        if (k + 1 < nsub) process(k + 1);
     }
 
+    if constexpr (!SPLIT) write_map();
     if constexpr (PHASE == kMaps) {
         // the current iterate's last row, for the apply launch that follows
         if (h == 0 && live) g.halo[(g.iter & 1) * HS + ci * D + i] = N[i];
     } else if constexpr (PHASE != kPrologue) {
         if (h == 0 && live) g.halo[((g.iter + 1) & 1) * HS + ci * D + i] = N[i];
-    }
-    // chunk map out: M[row][col] row-major, col = i
-    float* aA = g.aggA + ci * D * D;
-#pragma unroll
-    for (int r = 0; r < KS; ++r) {
-        const int row = Tl::krow(h, r);
-        if (row < D && live) aA[row * D + i] = M[r];
     }
     if (h == 0 && live) g.aggB[ci * D + i] = bg;
     rb = wave_max_u32(rb);
@@ -865,15 +921,28 @@ static hipError_t launch_dense64(int phase, const CellArgs& a, hipStream_t st) {
                             : launch_dense64_b<CELL, false>(phase, a, st);
 }
 
+template <int CELL, int DP, bool BANDED, bool SPLIT>
+static hipError_t launch_dense_phase_s(int phase, const CellArgs& a, hipStream_t st) {
+    const size_t lds = DLds<CELL, DP>::floats(a.m, SPLIT) * sizeof(float);
+    const dim3 grid(a.NC, a.B);
+    const int nt = SPLIT ? 128 : 64;
+    if (phase == kPrologue) dense_pass<CELL, DP, kPrologue, BANDED, SPLIT><<<grid, nt, lds, st>>>(a);
+    else if (phase == kFirst) dense_pass<CELL, DP, kFirst, BANDED, SPLIT><<<grid, nt, lds, st>>>(a);
+    else if (phase == kMaps) dense_pass<CELL, DP, kMaps, BANDED, SPLIT><<<grid, nt, lds, st>>>(a);
+    else dense_pass<CELL, DP, kSteady, BANDED, SPLIT><<<grid, nt, lds, st>>>(a);
+    return hipGetLastError();
+}
+
+// Two wavefronts per chunk when the chunks alone (one wavefront each) would
+// leave SIMDs without a second chunk: at most one chunk per SIMD (the chip
+// has 1024).
+constexpr int kSplitMax = 1024;
+
 template <int CELL, int DP, bool BANDED>
 static hipError_t launch_dense_phase_b(int phase, const CellArgs& a, hipStream_t st) {
-    const size_t lds = DLds<CELL, DP>::floats(a.m) * sizeof(float);
-    const dim3 grid(a.NC, a.B);
-    if (phase == kPrologue) dense_pass<CELL, DP, kPrologue, BANDED><<<grid, 64, lds, st>>>(a);
-    else if (phase == kFirst) dense_pass<CELL, DP, kFirst, BANDED><<<grid, 64, lds, st>>>(a);
-    else if (phase == kMaps) dense_pass<CELL, DP, kMaps, BANDED><<<grid, 64, lds, st>>>(a);
-    else dense_pass<CELL, DP, kSteady, BANDED><<<grid, 64, lds, st>>>(a);
-    return hipGetLastError();
+    return static_cast<int64_t>(a.NC) * a.B <= kSplitMax
+               ? launch_dense_phase_s<CELL, DP, BANDED, true>(phase, a, st)
+               : launch_dense_phase_s<CELL, DP, BANDED, false>(phase, a, st);
 }
 
 // band < D - 1 selects the masked Jacobian weights; Newton passes band = D.
@@ -893,9 +962,10 @@ size_t dense_mfma_lds_bytes(int kind, int DP, int m) {
     if (DP == 64) {
         return (kind == kCellEulerD ? D64Lds<kCellEulerD>::floats(m) : D64Lds<kCellTanhRnnD>::floats(m)) * sizeof(float);
     }
-    if (kind == kCellTanhRnnD) return (DP == 16 ? DLds<kCellTanhRnnD, 16>::floats(m) : DLds<kCellTanhRnnD, 32>::floats(m)) * sizeof(float);
-    if (kind == kCellEulerD) return (DP == 16 ? DLds<kCellEulerD, 16>::floats(m) : DLds<kCellEulerD, 32>::floats(m)) * sizeof(float);
-    return (DP == 16 ? DLds<kCellGruD, 16>::floats(m) : DLds<kCellGruD, 32>::floats(m)) * sizeof(float);
+    // the larger (split) layout, so either launch form fits
+    if (kind == kCellTanhRnnD) return (DP == 16 ? DLds<kCellTanhRnnD, 16>::floats(m, true) : DLds<kCellTanhRnnD, 32>::floats(m, true)) * sizeof(float);
+    if (kind == kCellEulerD) return (DP == 16 ? DLds<kCellEulerD, 16>::floats(m, true) : DLds<kCellEulerD, 32>::floats(m, true)) * sizeof(float);
+    return (DP == 16 ? DLds<kCellGruD, 16>::floats(m, true) : DLds<kCellGruD, 32>::floats(m, true)) * sizeof(float);
 }
 
 hipError_t launch_dense_mfma_pass(int kind, int DP, int phase, const CellArgs& a, hipStream_t st) {

@@ -35,9 +35,10 @@ __device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v
 // flight instead of one (a plain copy loop waits for every load).
 
 // dst[e] = src[e], e < n.  Uses 16-byte accesses when both sides allow it.
+// tid: the caller's index among the NT copying threads (default threadIdx.x).
 template <int NT, int KB = 8>
-__device__ __forceinline__ void copy_to_lds(float* dst, const float* __restrict__ src, int n) {
-    const int t = threadIdx.x;
+__device__ __forceinline__ void copy_to_lds(float* dst, const float* __restrict__ src, int n, int tid = -1) {
+    const int t = tid < 0 ? static_cast<int>(threadIdx.x) : tid;
     const bool v4 = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
     int done = 0;
     if (v4) {
@@ -78,8 +79,8 @@ __device__ __forceinline__ void copy_to_lds(float* dst, const float* __restrict_
 // LDS rows of dst_stride >= cols floats; columns [cols, dst_stride) are zeroed.
 template <int NT, int KB = 8>
 __device__ __forceinline__ void copy_rows_to_lds(float* dst, int dst_stride, const float* __restrict__ src,
-                                                 int64_t src_stride, int rows, int cols) {
-    const int t = threadIdx.x;
+                                                 int64_t src_stride, int rows, int cols, int tid = -1) {
+    const int t = tid < 0 ? static_cast<int>(threadIdx.x) : tid;
     const int n = rows * dst_stride;
     for (int base = 0; base < n; base += NT * KB) {
         float v[KB];

@@ -185,11 +185,13 @@ def test_matrix_cells_other_widths(kind, D):
 @pytest.mark.parametrize("kind, D, m", [(pn.CELL_TANH_RNN, 24, 37), (pn.CELL_GRU, 16, 19),
                                          (pn.CELL_EULER_TANH, 48, 21), (pn.CELL_TANH_RNN, 36, 5),
                                          (pn.CELL_TANH_RNN, 64, 33)])
-def test_matrix_core_paths_input_widths(kind, D, m):
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_matrix_core_paths_input_widths(kind, D, m, chunk):
     # the matrix-core kernels at input widths that span several k-groups of
     # the input projection with a ragged last group, and at state widths
-    # below the padded width (the carry's rows and columns past D); a chunk
-    # length of 32 gives several chunks and a ragged last sub-chunk
+    # below the padded width (the carry's rows and columns past D); chunks of
+    # 2 or 4 sub-chunks with a ragged last one, few chunks (the two-wavefront
+    # form of the D <= 32 kernel)
     rng = np.random.default_rng(400 + D + m)
     B, T = 3, 333
     params = workloads.lattice_cell_params(kind, D, m, rng)
@@ -197,7 +199,22 @@ def test_matrix_core_paths_input_widths(kind, D, m):
               max_iter=T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
               s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32), bandwidth=2)
     for mode in (N, pn.BANDED):
-        _parity(wl, mode, chunk=32)
+        _parity(wl, mode, chunk=chunk)
+
+
+@pytest.mark.parametrize("kind, D", [(pn.CELL_TANH_RNN, 28), (pn.CELL_GRU, 32), (pn.CELL_EULER_TANH, 24)])
+def test_matrix_core_one_wavefront_form(kind, D):
+    # more chunks than SIMDs (64 x 23 = 1472): the D <= 32 matrix-core kernel
+    # runs one wavefront per chunk; three sub-chunks per chunk, the last
+    # chunk ragged (1100 = 22 x 48 + 44)
+    rng = np.random.default_rng(500 + D)
+    m, B, T = 6, 64, 1100
+    params = workloads.lattice_cell_params(kind, D, m, rng)
+    wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-6, damping=1.0, window=0,
+              max_iter=T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32), bandwidth=2)
+    for mode in (N, pn.BANDED):
+        _parity(wl, mode, chunk=48)
 
 
 @pytest.mark.parametrize("k", [1, 2, 3])
