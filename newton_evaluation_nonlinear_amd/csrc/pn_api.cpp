@@ -112,12 +112,15 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
         if (chunk > 0) {
             p.L = chunk;
         } else {
-            // Longest chunk that still leaves about 2^18 threads (B x channel
-            // groups x chunks): the per-iteration carry scan shrinks with the
-            // chunk count, while the apply sweep keeps 2^18 threads x 16 loads
-            // in flight.
+            // Longest chunk that still leaves about 2^17 threads (B x channel
+            // groups x chunks) with float storage, 2^18 with binary16: the
+            // per-iteration carry scan shrinks with the chunk count; the
+            // float sweep (two row streams in, one out per thread) runs
+            // faster with fewer, longer streams, while the binary16 sweep is
+            // bound by its vector instructions and wants the occupancy.
+            const int64_t target = p.hmode ? (1 << 18) : (1 << 17);
             int64_t L = 16;
-            while (L < 1024 && static_cast<int64_t>(B) * groups * ((p.W + 2 * L - 1) / (2 * L)) >= (1 << 18)) L *= 2;
+            while (L < 1024 && static_cast<int64_t>(B) * groups * ((p.W + 2 * L - 1) / (2 * L)) >= target) L *= 2;
             p.L = static_cast<int>(L);
         }
         p.L = static_cast<int>(std::min<int64_t>(p.L, p.W));
