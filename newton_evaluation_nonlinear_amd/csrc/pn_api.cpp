@@ -64,14 +64,18 @@ struct Plan {
     int band;              // half-bandwidth of A~_t in the dense modes (Newton: D)
     int64_t T, W;          // horizon, window length
     int L, NC;             // chunk length, chunks of a full window
+    int Lc, NCc;           // the steady updates' chunks (recompute: twice L), else L, NC
     int DP, cpb;           // padded D (matrix cells), channels per block (diag cell)
     bool dense, matrix_cell, mfma;
     bool advancing;        // one window sliding past its converged prefix
     bool half;             // x and out in IEEE binary16 (channel-wise cell)
     int hmode;             // DiagArgs::half of the channel-wise kernel
     bool persist_ok;       // shape allows the one-launch persistent solver
+    bool recompute;        // channel-wise cell, float storage: first update stores nothing,
+                           // the second recomputes s^(1) (kFirstNS, kSecondR)
     int nblocks, nwin, hist_cap;
-    size_t off_ctrl, off_rpart, off_fpart, off_aggA, off_aggB, off_carry, off_halo, off_w, total;
+    size_t off_ctrl, off_rpart, off_fpart, off_aggA, off_aggB, off_carry, off_carry0, off_halo, off_w,
+        total;
     size_t off_sync, off_winfo, off_hist;
 };
 
@@ -109,21 +113,25 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
         // channel groups per workgroup row: 64, 128 or 256, a divisor of the
         // workgroup size, so every thread belongs to exactly one (chunk, group)
         p.cpb = groups <= 64 ? 64 : groups <= 128 ? 128 : 256;
+        const bool recompute = !p.half && !p.advancing;
         if (chunk > 0) {
-            p.L = chunk;
+            p.L = p.Lc = chunk;
         } else {
-            // Longest chunk that still leaves about 2^17 threads (B x channel
-            // groups x chunks) with float storage, 2^18 with binary16: the
-            // per-iteration carry scan shrinks with the chunk count; the
-            // float sweep (two row streams in, one out per thread) runs
-            // faster with fewer, longer streams, while the binary16 sweep is
-            // bound by its vector instructions and wants the occupancy.
-            const int64_t target = p.hmode ? (1 << 18) : (1 << 17);
+            // Longest chunk that still leaves about 2^18 threads (B x channel
+            // groups x chunks): the per-iteration carry scan shrinks with the
+            // chunk count, while the sweeps that read only x (and the
+            // binary16 sweeps, bound by their vector instructions) want the
+            // occupancy.  With float storage the steady updates (two row
+            // streams in, one out per thread) run on chunks twice as long:
+            // fewer, longer streams measured faster.
             int64_t L = 16;
-            while (L < 1024 && static_cast<int64_t>(B) * groups * ((p.W + 2 * L - 1) / (2 * L)) >= target) L *= 2;
+            while (L < 1024 && static_cast<int64_t>(B) * groups * ((p.W + 2 * L - 1) / (2 * L)) >= (1 << 18)) L *= 2;
             p.L = static_cast<int>(L);
+            p.Lc = static_cast<int>(recompute ? std::min<int64_t>(2 * L, 1024) : L);
         }
         p.L = static_cast<int>(std::min<int64_t>(p.L, p.W));
+        p.Lc = static_cast<int>(std::min<int64_t>(std::max(p.Lc, p.L), p.W));
+        if (p.Lc % p.L != 0) p.Lc = p.L;    // steady chunks are whole multiples of the first ones
         p.NC = static_cast<int>((p.W + p.L - 1) / p.L);
         DiagArgs a{};
         a.B = p.B; a.D = p.D; a.NC = p.NC; a.cpb = p.cpb; a.half = p.hmode;
@@ -146,7 +154,7 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
             while (L < 512 && static_cast<int64_t>(B) * ((p.W + 2 * L - 1) / (2 * L)) >= 2048) L *= 2;
             while (L > 16 && static_cast<int64_t>(B) * ((p.W + L - 1) / L) < 1024) L /= 2;
         }
-        p.L = static_cast<int>(std::min<int64_t>(L, p.W));
+        p.L = p.Lc = static_cast<int>(std::min<int64_t>(L, p.W));
         p.NC = static_cast<int>((p.W + p.L - 1) / p.L);
         p.nblocks = p.NC * p.B;
     } else {
@@ -164,13 +172,16 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
             }
             while (L > 16 && static_cast<int64_t>(B) * ((p.W + L - 1) / L) < 1024) L /= 2;
         }
-        p.L = static_cast<int>(std::min<int64_t>(L, p.W));
+        p.L = p.Lc = static_cast<int>(std::min<int64_t>(L, p.W));
         p.NC = static_cast<int>((p.W + p.L - 1) / p.L);
         p.nblocks = p.NC * p.B;
         if (cell_pass_lds_bytes(p.kind, p.DP, p.dense, p.L, p.m) > 160 * 1024)
             return fail(PN_EUNSUPPORTED, "chunk of %d steps needs too much LDS for D=%d, m=%d", p.L, p.D, p.m);
     }
     p.nwin = static_cast<int>((T + p.W - 1) / p.W);
+    p.recompute = !p.matrix_cell && !p.half && !p.advancing;
+    if (!p.recompute) p.Lc = p.L;
+    p.NCc = static_cast<int>((p.W + p.Lc - 1) / p.Lc);
     p.persist_ok = p.matrix_cell && !p.dense && !p.advancing &&
                    cell_persist_eligible(p.kind, p.DP, p.L, p.m);
     p.hist_cap = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(p.nwin) * (p.W + 1), 1 << 16));
@@ -197,6 +208,8 @@ void layout(Plan& p, const Plan* other) {
     p.off_aggA = off; off = align_up(off + sizeof(float) * nA);
     p.off_aggB = off; off = align_up(off + sizeof(float) * bnd);
     p.off_carry = off; off = align_up(off + sizeof(float) * bnd);
+    p.off_carry0 = off;
+    if (p.recompute || (other && other->recompute)) off = align_up(off + sizeof(float) * bnd);
     p.off_halo = off; off = align_up(off + sizeof(float) * 2 * bnd);
     p.off_w = off;
     if (p.matrix_cell) off = align_up(off + sizeof(float) * prepared_weight_floats(p.kind, p.DP, p.m));
@@ -220,6 +233,9 @@ int make_plans(Plan& p, Plan& p2, bool* has2, const pn_cell* cell, int64_t B, in
     rc = make_plan(p2, cell, B, T, D, o->switch_mode, o);
     if (rc != PN_OK) return rc;
     p.persist_ok = p2.persist_ok = false;
+    p.recompute = p2.recompute = false;
+    p.Lc = p.L; p2.Lc = p2.L;
+    p.NCc = p.NC; p2.NCc = p2.NC;
     layout(p, &p2);
     layout(p2, &p);
     return PN_OK;
@@ -413,8 +429,12 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
     float* aggA = reinterpret_cast<float*>(c.ws + pp->off_aggA);
     float* aggB = reinterpret_cast<float*>(c.ws + pp->off_aggB);
     float* carry = reinterpret_cast<float*>(c.ws + pp->off_carry);
+    float* carry0 = reinterpret_cast<float*>(c.ws + pp->off_carry0);
     float* halo = reinterpret_cast<float*>(c.ws + pp->off_halo);
     const float* w = reinterpret_cast<const float*>(c.ws + pp->off_w);
+    // the first two updates of the channel-wise cell move less (kFirstNS,
+    // kSecondR): iteration 0's carries go to their own buffer
+    const bool recompute = pp->recompute && !p2;
 
     DiagArgs da{};
     CellArgs ca{};
@@ -431,9 +451,12 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
             da = DiagArgs{};
             da.a = c.params; da.x = x; da.xs = xs; da.s = s; da.ss = ss; da.s0 = s0; da.s0s = s0s;
             da.B = p.B; da.Tw = Tw; da.D = p.D; da.L = p.L; da.NC = NC; da.cpb = p.cpb;
-            da.aggA = aggA; da.aggB = aggB; da.carry = carry; da.halo = halo; da.rpart = rpart;
+            da.aggA = aggA; da.aggB = aggB; da.carry = carry; da.carry0 = carry0; da.halo = halo;
+            da.rpart = rpart;
             da.ctrl = ctrl; da.mode = p.mode; da.lam = c.lam; da.undamped = c.lam == 1.0f;
             da.half = p.hmode;
+            da.rf = 1; da.NCr = NC;
+            da.hs = static_cast<int64_t>(p.B) * p.NC * p.D;
             nblocks = diag_tanh_nblocks(da);
         } else {
             ca = CellArgs{};
@@ -465,15 +488,38 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
     cy.chk.epoch = epoch;
     hr->iter = -1;
     float r_prev = 0.0f;
+    // Chunking of the channel-wise launches with the recomputing pair: the
+    // prologue and updates 1 and 2 run on chunks of L, the later updates on
+    // chunks of Lc (a multiple of L); the first of them reads the carries
+    // and the halo of the fine chunking at chunk c * Lc / L.
+    const int NCf = (Tw + pp->L - 1) / pp->L;
+    const int NCc = (Tw + pp->Lc - 1) / pp->Lc;
+    auto grain = [&](bool coarse, int rf) {
+        da.L = coarse ? pp->Lc : pp->L;
+        da.NC = coarse ? NCc : NCf;
+        da.rf = rf;
+        da.NCr = rf > 1 ? NCf : da.NC;
+    };
     for (int i = 0;; ++i) {
         cy.chk.iter = i;
         size_t e0 = 0, e1 = 0;
+        cy.carry = (recompute && i == 0) ? carry0 : carry;
+        da.carry = cy.carry;
+        if (recompute) {
+            // the carry scans the maps of the launch before: apply(i-1), or the prologue
+            grain(i >= 3, 1);
+            cy.NC = da.NC;
+            cy.chk.nparts = diag_tanh_nblocks(da);
+        }
         PN_HIP(pp->dense ? launch_dense_carry(cy, c.st) : launch_diag_carry(cy, c.st));
-        // timing covers the steady-state apply launches (i >= 1), including
-        // the final one that exits at once
-        const bool timed = c.tm->on && i > 0;
+        const int phase = i == 0 ? (recompute ? kFirstNS : kFirst)
+                                 : (recompute && i == 1 ? kSecondR : kSteady);
+        if (recompute) grain(i >= 2, i == 2 ? pp->Lc / pp->L : 1);
+        // timing covers the steady-state apply launches, including the final
+        // one that exits at once
+        const bool timed = c.tm->on && phase == kSteady;
         if (timed) { int rc = record(c, &e0); if (rc) return rc; }
-        PN_HIP(launch_pass(i == 0 ? kFirst : kSteady, i));
+        PN_HIP(launch_pass(phase, i));
         if (timed) {
             int rc = record(c, &e1);
             if (rc) return rc;
@@ -500,6 +546,14 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
         if (stop) {
             *K = i;
             *status = st;
+            if (recompute && i == 1) {
+                // the result is s^(1), which the first update did not store
+                grain(false, 1);
+                da.carry = carry0;
+                da.force = 1;
+                PN_HIP(launch_pass(kFirst, 0));
+                da.force = 0;
+            }
             break;
         }
         if (p2 && *sw < 0 && i >= 1 && r > c.ratio * r_prev) {

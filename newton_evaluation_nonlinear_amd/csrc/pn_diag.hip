@@ -12,6 +12,13 @@
 //            iterate: residual |s_t - f_t(s_{t-1})| and the chunk's next map.
 // The apply sweep therefore moves exactly x, s^(i) in and s^(i+1) out, and
 // the following carry only touches the chunk maps.
+// With float storage the first two updates move less: s^(0) = s0 is known
+// everywhere, so the first update (kFirstNS) stores no s^(1), and the second
+// (kSecondR) replays iteration 0 again from its carries, which yields s^(1)
+// bit for bit, before replaying iteration 1 and storing s^(2).  The second
+// update then reads x only (8 bytes per element instead of 12, and 4 instead
+// of 8 for the first) at the price of one more tanh per element; if the
+// loop stops right after the first update, a kFirst launch stores s^(1).
 //
 // Layout: lanes run along channels (row-contiguous in [B, T, D]); each thread
 // walks the L steps of its chunk serially, so loads are fully coalesced rows
@@ -23,6 +30,8 @@
 // to the next step is the rounded one, so the state the next step sees is
 // exactly the stored state.
 
+#include <type_traits>
+
 #include "pn_device.hpp"
 
 namespace pn {
@@ -30,7 +39,7 @@ namespace pn {
 // Steps per prefetch group: the loads of group g+1 are issued before group g
 // is computed, so every thread keeps 2*U loads in flight.
 constexpr int kU = 8;
-constexpr int kUP = 16;   // the prologue only reads x, so it prefetches twice as far
+constexpr int kUP = 16;   // passes that only read x prefetch twice as far
 
 // Storage element of one thread: NCH adjacent channels moved as one access
 // (a float; or two binary16 values in one 4-byte access, so a wave moves as
@@ -75,8 +84,12 @@ __device__ __forceinline__ float stored(float v) {
 template <int MODE, int PHASE, typename S, int NCH, bool UND>
 __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
     if constexpr (PHASE != kPrologue) {
-        if (g.ctrl->stop) return;    // uniform over the grid: converged earlier
+        if (g.ctrl->stop && !g.force) return;    // uniform over the grid: converged earlier
     }
+    // which passes start from s0, read the stored iterate, recompute s^(1)
+    constexpr bool kFromS0 = PHASE == kFirst || PHASE == kFirstNS;
+    constexpr bool kReadS = PHASE == kSteady;
+    constexpr bool kRecompute = PHASE == kSecondR;
     typedef typename Pack<S, NCH>::V V;
     const int cpb = g.cpb;                           // channel groups per block row
     const int dl = threadIdx.x % cpb;
@@ -137,44 +150,68 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
                 for (int u = 0; u < kUP; ++u) xb[u] = xn[u];
             }
         } else {
-            const size_t HS = static_cast<size_t>(g.B) * g.NC * D;
+            // halo parity stride, and the index of this chunk in the chunking
+            // the carries and the halo were written in (rf fine chunks per
+            // chunk of this launch)
+            const size_t HS = static_cast<size_t>(g.hs);
+            const size_t ri = (static_cast<size_t>(b) * g.NCr + static_cast<size_t>(c) * g.rf) * D + d;
             V* sp = reinterpret_cast<V*>(reinterpret_cast<S*>(g.s) + b * g.ss + static_cast<int64_t>(t0) * D + d);
             const bool has_next = (c + 1 < g.NC);
             const float lam = g.lam;
             // p_old: s^(i) at t0-1 (halo of the previous chunk);  shat: s^ at t0-1;
             // snp: s^(i+1) at t0-1, exactly as the previous chunk stores it.
             float p_old[NCH], shat[NCH], shat_end[NCH], snp[NCH];
+            // kSecondR: s^ of iteration 0 entering this chunk and the next one
+            float sh0[NCH], sh0_end[NCH];
 #pragma unroll
             for (int k = 0; k < NCH; ++k) {
-                p_old[k] = (PHASE == kFirst || c == 0) ? s0v[k] : g.halo[(g.iter & 1) * HS + ai - D + k];
-                shat[k] = g.carry[ai + k];
-                shat_end[k] = has_next ? g.carry[ai + D + k] : 0.0f;
+                p_old[k] = (kFromS0 || c == 0) ? s0v[k] : g.halo[(g.iter & 1) * HS + ri - D + k];
+                shat[k] = g.carry[ri + k];
+                shat_end[k] = has_next ? g.carry[ri + static_cast<size_t>(g.rf) * D + k] : 0.0f;
                 snp[k] = stored<S>(UND ? shat[k] : p_old[k] + lam * (shat[k] - p_old[k]));
+                if constexpr (kRecompute) {
+                    sh0[k] = g.carry0[ri + k];
+                    sh0_end[k] = has_next ? g.carry0[ri + static_cast<size_t>(g.rf) * D + k] : 0.0f;
+                } else {
+                    sh0[k] = sh0_end[k] = 0.0f;
+                }
             }
-            V xb[kU], sb[kU];
+            // passes that read only x prefetch as deep as the prologue
+            constexpr int U = kReadS ? kU : kUP;
+            V xb[U], sb[U];
 #pragma unroll
-            for (int u = 0; u < kU; ++u) {
+            for (int u = 0; u < U; ++u) {
                 xb[u] = u < n ? xp[u * DV] : V{};
-                if constexpr (PHASE != kFirst) sb[u] = u < n ? sp[u * DV] : V{};
+                if constexpr (kReadS) sb[u] = u < n ? sp[u * DV] : V{};
             }
-            for (int j = 0; j < n; j += kU) {
+            for (int j = 0; j < n; j += U) {
                 const V* xq = xp + static_cast<int64_t>(j) * DV;   // row j of the chunk
                 V* sq = sp + static_cast<int64_t>(j) * DV;
-                V xn[kU], sn_[kU];
+                V xn[U], sn_[U];
 #pragma unroll
-                for (int u = 0; u < kU; ++u) {
-                    const bool in = j + kU + u < n;
-                    xn[u] = in ? xq[(kU + u) * DV] : V{};
-                    if constexpr (PHASE != kFirst) sn_[u] = in ? sq[(kU + u) * DV] : V{};
+                for (int u = 0; u < U; ++u) {
+                    const bool in = j + U + u < n;
+                    xn[u] = in ? xq[(U + u) * DV] : V{};
+                    if constexpr (kReadS) sn_[u] = in ? sq[(U + u) * DV] : V{};
                 }
 #pragma unroll
-                for (int u = 0; u < kU; ++u) {
+                for (int u = 0; u < U; ++u) {
                     if (j + u < n) {
                         float xt[NCH], so[NCH], sn[NCH];
                         unpack<S, NCH>(xb[u], xt);
-                        if constexpr (PHASE == kFirst) {
+                        if constexpr (kFromS0) {
 #pragma unroll
                             for (int k = 0; k < NCH; ++k) so[k] = s0v[k];
+                        } else if constexpr (kRecompute) {
+                            // s^(1)_t again: iteration 0's replay, p = s0 throughout
+#pragma unroll
+                            for (int k = 0; k < NCH; ++k) {
+                                const float v0 = tanh_f(a[k] * s0v[k] + xt[k]);
+                                const float a0 = mode_coef<MODE>(a[k] * (1.0f - v0 * v0));
+                                sh0[k] = v0 + a0 * (sh0[k] - s0v[k]);
+                                if (j + u == n - 1 && has_next) sh0[k] = sh0_end[k];
+                                so[k] = stored<S>(UND ? sh0[k] : s0v[k] + lam * (sh0[k] - s0v[k]));
+                            }
                         } else {
                             unpack<S, NCH>(sb[u], so);
                         }
@@ -188,7 +225,12 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
                             if (j + u == n - 1 && has_next) shat[k] = shat_end[k];
                             sn[k] = UND ? shat[k] : so[k] + lam * (shat[k] - so[k]);
                         }
-                        sq[u * DV] = pack<S, NCH>(sn);       // sn now holds the stored values
+                        if constexpr (PHASE == kFirstNS) {
+#pragma unroll
+                            for (int k = 0; k < NCH; ++k) sn[k] = stored<S>(sn[k]);
+                        } else {
+                            sq[u * DV] = pack<S, NCH>(sn);   // sn now holds the stored values
+                        }
 #pragma unroll
                         for (int k = 0; k < NCH; ++k) {
                             // iteration i+1: residual and affine map at p_t = s^(i+1)_{t-1}
@@ -204,9 +246,9 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < kU; ++u) {
+                for (int u = 0; u < U; ++u) {
                     xb[u] = xn[u];
-                    if constexpr (PHASE != kFirst) sb[u] = sn_[u];
+                    if constexpr (kReadS) sb[u] = sn_[u];
                 }
             }
 #pragma unroll
@@ -243,7 +285,15 @@ static hipError_t launch_und(int phase, const DiagArgs& a, hipStream_t st) {
     const dim3 grid = diag_grid(a);
     if (phase == kPrologue) diag_tanh_pass<MODE, kPrologue, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
     else if (phase == kFirst) diag_tanh_pass<MODE, kFirst, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
-    else diag_tanh_pass<MODE, kSteady, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
+    else if (phase == kSteady) diag_tanh_pass<MODE, kSteady, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
+    else if constexpr (std::is_same<S, float>::value) {
+        // the recomputing pair runs with float storage only
+        if (phase == kFirstNS) diag_tanh_pass<MODE, kFirstNS, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
+        else if (phase == kSecondR) diag_tanh_pass<MODE, kSecondR, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
+        else return hipErrorInvalidValue;
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -57,6 +57,7 @@ struct DiagArgs {
     float* aggA;             // [B][NC][D]
     float* aggB;             // [B][NC][D]
     const float* carry;      // [B][NC][D]
+    const float* carry0;     // [B][NC][D] carries of iteration 0 (kSecondR)
     float* halo;             // [2][B][NC][D]
     uint32_t* rpart;         // one slot per workgroup
     const Ctrl* ctrl;
@@ -64,6 +65,11 @@ struct DiagArgs {
     float lam;
     int32_t half;            // x and s hold IEEE binary16 (strides in elements): 1 one
                              // channel per thread, 2 channel pairs (D even); 0 float
+    int32_t force;           // run even when the control word says stop (the store of s^(1))
+    // Carries and halo were written on a chunking rf times finer (NCr chunks
+    // per batch row): this launch's chunk c reads them at chunk c * rf.
+    int32_t rf, NCr;
+    int64_t hs;              // halo parity stride in elements (B x the finest NC x D)
 };
 
 // ---------------------------------------------------------------- matrix cells
@@ -107,7 +113,10 @@ struct CarryArgs {
 // kPrologue: iteration-0 chunk maps at s^(0) = s0 (implicit);  kFirst /
 // kSteady: apply for i = 0 / i >= 1;  kMaps: chunk maps, residual and halo
 // of the iterate stored in s (the advancing window, after it slides).
-enum Phase { kPrologue = 0, kFirst = 1, kSteady = 2, kMaps = 3 };
+// Channel-wise cell only: kFirstNS is kFirst without the store of s^(1), and
+// kSecondR the apply for i = 1 that recomputes s^(1) from the carries of
+// iteration 0 instead of reading it (see pn_diag.hip).
+enum Phase { kPrologue = 0, kFirst = 1, kSteady = 2, kMaps = 3, kFirstNS = 4, kSecondR = 5 };
 
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_diag_tanh_pass(int phase, const DiagArgs& a, hipStream_t st);
