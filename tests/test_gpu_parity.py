@@ -114,6 +114,35 @@ def test_diag_tanh_widths_between_workgroup_sizes(D, storage):
     _parity(wl, J)
 
 
+@pytest.mark.parametrize("a, updates", [(1e-4, 1), (1e-2, 2)])
+def test_diag_converged_after_one_or_two_updates(a, updates):
+    # float storage: the first update stores nothing and the second
+    # recomputes s^(1); a stop right after update 1 must still leave s^(1)
+    # in out (a separate store launch), a stop after update 2 leaves s^(2)
+    rng = np.random.default_rng(11)
+    D, B, T = 64, 2, 900
+    wl = dict(cfg=0, cell=pn.CELL_DIAG_TANH, D=D, m=D, B=B, T=T, tol=1e-6, damping=1.0, window=0,
+              max_iter=T, params=np.full(D, a, np.float32),
+              x=rng.standard_normal((B, T, D)).astype(np.float32),
+              s0=(0.3 * rng.standard_normal((B, D))).astype(np.float32))
+    ref = _parity(wl, Q)
+    assert ref.iters == updates
+
+
+@pytest.mark.parametrize("T, window", [(3017, 0), (3017, 1000), (40, 0)])
+def test_diag_fine_and_coarse_chunkings(T, window):
+    # the prologue and the first two updates run on chunks of L, the steady
+    # updates on chunks of 2L, the first of them reading the carries and the
+    # halo of the finer chunking: an odd number of fine chunks (the last
+    # coarse chunk holds one fine chunk), windows with a short last one, and
+    # a horizon shorter than one coarse chunk
+    wl = _case(3, B=2, T=T)
+    if window:
+        wl.update(window=window, max_iter=window)
+    _parity(wl, Q, damping=0.8)
+    _parity(wl, P, tol=1e-4)
+
+
 def test_diag_tanh_odd_width_and_damping():
     rng = np.random.default_rng(5)
     D, B, T = 77, 3, 517
