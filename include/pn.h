@@ -157,7 +157,7 @@ typedef struct pn_opts {
  * PN_WINDOW_CONSECUTIVE: windows of W steps solved one after another, each
  *   to tol; max_iter caps the updates of each window; window_iters and
  *   resid_hist hold one entry / one run per window.
- * PN_WINDOW_ADVANCING (matrix cells only; the sliding window of
+ * PN_WINDOW_ADVANCING (every cell; float storage; the sliding window of
  *   [PN §1.3.1]): steps [0, a) are accepted and never change again; the
  *   window is [a, min(T, a + W)).  Each round checks the current iterate on
  *   the window, r_t = max over (b, d) of |F_t|, and r = max_t r_t (stored in

@@ -270,8 +270,6 @@ int validate(const pn_cell* cell, const float* params, const float* x, const flo
             return fail(PN_EWORKSPACE, "workspace must be 256-byte aligned");
         if (o->window_mode != PN_WINDOW_CONSECUTIVE && o->window_mode != PN_WINDOW_ADVANCING)
             return fail(PN_EINVAL, "unknown window_mode %d", o->window_mode);
-        if (o->window_mode == PN_WINDOW_ADVANCING && cell->kind == PN_CELL_DIAG_TANH)
-            return fail(PN_EUNSUPPORTED, "the advancing window supports the matrix cells only");
         if (o->switch_mode < -1 || o->switch_mode > PN_BANDED)
             return fail(PN_EINVAL, "unknown switch_mode %d", o->switch_mode);
         if (o->switch_mode >= 0) {
@@ -599,6 +597,14 @@ int solve_advancing(SolveCtx& c, const float* x, const float* s0, float* out, in
     ca.aggA = aggA; ca.aggB = aggB; ca.carry = carry; ca.halo = halo; ca.rpart = rpart;
     ca.ctrl = ctrl; ca.mode = p.mode; ca.lam = c.lam; ca.undamped = c.lam == 1.0f;
     ca.band = p.band; ca.fpart = fpart; ca.tol = c.tol;
+    DiagArgs da{};                   // the channel-wise cell (m == D, float storage)
+    da.a = c.params; da.xs = T * m; da.ss = T * D;
+    da.B = p.B; da.D = p.D; da.L = p.L; da.cpb = p.cpb;
+    da.aggA = aggA; da.aggB = aggB; da.carry = carry; da.halo = halo; da.rpart = rpart;
+    da.ctrl = ctrl; da.mode = p.mode; da.lam = c.lam; da.undamped = c.lam == 1.0f;
+    da.half = 0; da.rf = 1;
+    da.hs = static_cast<int64_t>(p.B) * p.NC * p.D;
+    da.fpart = fpart; da.tol = c.tol;
     CarryArgs cy{};
     cy.aggA = aggA; cy.aggB = aggB; cy.carry = carry; cy.B = p.B; cy.D = p.D; cy.do_check = 0;
     CheckArgs chk{};
@@ -622,8 +628,17 @@ int solve_advancing(SolveCtx& c, const float* x, const float* s0, float* out, in
         ca.NC = NC;
         cy.s0 = ca.s0; cy.s0s = ca.s0s; cy.NC = NC;
         chk.nparts = p.B * NC;
+        if (!p.matrix_cell) {
+            da.x = ca.x; da.s = ca.s; da.s0 = ca.s0; da.s0s = ca.s0s;
+            da.Tw = Tw; da.NC = NC; da.NCr = NC;
+            chk.nparts = diag_tanh_nblocks(da);
+        }
     };
     auto launch_pass = [&](int phase, int iter) -> hipError_t {
+        if (!p.matrix_cell) {
+            da.iter = iter;
+            return launch_diag_tanh_pass(phase, da, c.st);
+        }
         ca.iter = iter;
         if (p.mfma) return launch_dense_mfma_pass(p.kind, p.DP, phase, ca, c.st);
         return launch_cell_pass(p.kind, p.DP, p.dense, phase, ca, c.st);

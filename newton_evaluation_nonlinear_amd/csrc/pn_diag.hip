@@ -83,7 +83,7 @@ __device__ __forceinline__ float stored(float v) {
 
 template <int MODE, int PHASE, typename S, int NCH, bool UND>
 __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
-    if constexpr (PHASE != kPrologue) {
+    if constexpr (PHASE != kPrologue && PHASE != kMaps) {
         if (g.ctrl->stop && !g.force) return;    // uniform over the grid: converged earlier
     }
     // which passes start from s0, read the stored iterate, recompute s^(1)
@@ -100,6 +100,8 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
     const int d = (blockIdx.y * cpb + dl) * NCH;     // first channel of the group
     const int b = blockIdx.z;
     uint32_t rb = 0;
+    const bool track = g.fpart != nullptr;           // first step over tol (advancing window)
+    uint32_t fb = 0xffffffffu;
     if (c < g.NC && d < g.D) {
         const int D = g.D;
         const int DV = D / NCH;                      // row stride in groups
@@ -149,6 +151,63 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
 #pragma unroll
                 for (int u = 0; u < kUP; ++u) xb[u] = xn[u];
             }
+        } else if constexpr (PHASE == kMaps) {
+            // The iterate stored in s (the advancing window, after it slides):
+            // its residual, first step over tol, chunk maps and last row.
+            const V* sp = reinterpret_cast<const V*>(reinterpret_cast<const S*>(g.s) + b * g.ss +
+                                                     static_cast<int64_t>(t0) * D + d);
+            float prev[NCH];                         // s_{t-1}
+            if (c == 0) {
+#pragma unroll
+                for (int k = 0; k < NCH; ++k) prev[k] = s0v[k];
+            } else {
+                unpack<S, NCH>(sp[-DV], prev);
+            }
+            V xb[kU], sb[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                xb[u] = u < n ? xp[u * DV] : V{};
+                sb[u] = u < n ? sp[u * DV] : V{};
+            }
+            for (int j = 0; j < n; j += kU) {
+                const V* xq = xp + static_cast<int64_t>(j) * DV;
+                const V* sq = sp + static_cast<int64_t>(j) * DV;
+                V xn[kU], sn_[kU];
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const bool in = j + kU + u < n;
+                    xn[u] = in ? xq[(kU + u) * DV] : V{};
+                    sn_[u] = in ? sq[(kU + u) * DV] : V{};
+                }
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    if (j + u < n) {
+                        float xt[NCH], st[NCH];
+                        unpack<S, NCH>(xb[u], xt);
+                        unpack<S, NCH>(sb[u], st);
+#pragma unroll
+                        for (int k = 0; k < NCH; ++k) {
+                            const float v = tanh_f(a[k] * prev[k] + xt[k]);
+                            const float dr = st[k] - v;
+                            rb = max(rb, abs_bits(dr));
+                            if (track && !(fabsf(dr) <= g.tol)) fb = min(fb, static_cast<uint32_t>(t0 + j + u));
+                            const float at = mode_coef<MODE>(a[k] * (1.0f - v * v));
+                            const float bt = v - at * prev[k];
+                            A[k] = at * A[k];
+                            Bc[k] = at * Bc[k] + bt;
+                            prev[k] = st[k];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    xb[u] = xn[u];
+                    sb[u] = sn_[u];
+                }
+            }
+            // the iterate's last row, for the apply launch that follows
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) g.halo[(g.iter & 1) * static_cast<size_t>(g.hs) + ai + k] = prev[k];
         } else {
             // halo parity stride, and the index of this chunk in the chunking
             // the carries and the halo were written in (rf fine chunks per
@@ -236,6 +295,8 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
                             // iteration i+1: residual and affine map at p_t = s^(i+1)_{t-1}
                             const float v2 = tanh_f(a[k] * snp[k] + xt[k]);
                             rb = max(rb, abs_bits(sn[k] - v2));
+                            if (track && !(fabsf(sn[k] - v2) <= g.tol))
+                                fb = min(fb, static_cast<uint32_t>(t0 + j + u));
                             const float a2 = mode_coef<MODE>(a[k] * (1.0f - v2 * v2));
                             const float b2 = v2 - a2 * snp[k];
                             A[k] = a2 * A[k];
@@ -261,9 +322,11 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
         }
     }
     rb = block_max_u32(rb);
-    if (threadIdx.x == 0) {
-        const int bid = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
-        g.rpart[bid] = rb;
+    const int bid = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    if (threadIdx.x == 0) g.rpart[bid] = rb;
+    if (track) {
+        fb = ~block_max_u32(~fb);
+        if (threadIdx.x == 0) g.fpart[bid] = fb;
     }
 }
 
@@ -286,6 +349,7 @@ static hipError_t launch_und(int phase, const DiagArgs& a, hipStream_t st) {
     if (phase == kPrologue) diag_tanh_pass<MODE, kPrologue, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
     else if (phase == kFirst) diag_tanh_pass<MODE, kFirst, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
     else if (phase == kSteady) diag_tanh_pass<MODE, kSteady, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
+    else if (phase == kMaps) diag_tanh_pass<MODE, kMaps, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
     else if constexpr (std::is_same<S, float>::value) {
         // the recomputing pair runs with float storage only
         if (phase == kFirstNS) diag_tanh_pass<MODE, kFirstNS, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);

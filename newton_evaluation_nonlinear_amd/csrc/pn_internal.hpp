@@ -70,6 +70,9 @@ struct DiagArgs {
     // per batch row): this launch's chunk c reads them at chunk c * rf.
     int32_t rf, NCr;
     int64_t hs;              // halo parity stride in elements (B x the finest NC x D)
+    uint32_t* fpart;         // advancing window: per-block first step with r_t > tol
+                             // (window-relative; 0xffffffff if none), or null
+    float tol;
 };
 
 // ---------------------------------------------------------------- matrix cells

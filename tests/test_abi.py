@@ -96,9 +96,12 @@ def test_window_mode_checks():
     o = pn.make_opts(window_mode=2)
     rc, _ = _eval_raw(opts=o)
     assert rc == pn.EINVAL and "window_mode" in pn.last_error()
+    # every cell takes the advancing window (an empty batch passes the checks
+    # and returns before any device work)
     o = pn.make_opts(window_mode=pn.WINDOW_ADVANCING)
-    rc, _ = _eval_raw(kind=pn.CELL_DIAG_TANH, m=4, D=4, opts=o)
-    assert rc == pn.EUNSUPPORTED
+    for kind, m in ((pn.CELL_DIAG_TANH, 4), (pn.CELL_TANH_RNN, 3), (pn.CELL_GRU, 3), (pn.CELL_EULER_TANH, 3)):
+        rc, it = _eval_raw(kind=kind, m=m, D=4, B=0, opts=o)
+        assert rc == pn.OK and it == 0, kind
 
 
 def test_switch_options():
@@ -126,6 +129,9 @@ def test_f16_entry_checks():
                          ctypes.byref(it), None) == pn.EUNSUPPORTED
     c = pn.Cell(pn.CELL_DIAG_TANH, 4)
     o = pn.make_opts(window=2)
+    assert L.pn_eval_f16(ctypes.byref(c), p, p, p, 2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
+                         ctypes.byref(it), ctypes.byref(o)) == pn.EUNSUPPORTED
+    o = pn.make_opts(window_mode=pn.WINDOW_ADVANCING)
     assert L.pn_eval_f16(ctypes.byref(c), p, p, p, 2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
                          ctypes.byref(it), ctypes.byref(o)) == pn.EUNSUPPORTED
     assert L.pn_eval_f16(ctypes.byref(c), p, p, p, -2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,

@@ -331,6 +331,24 @@ def _advancing_case(kind, D, m, B, T, W, seed, tol=1e-5, damping=1.0, params=Non
                 s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32), bandwidth=2)
 
 
+@pytest.mark.parametrize("D, W", [(256, 100), (77, 256), (64, 1000)])
+@pytest.mark.parametrize("mode", [Q, J])
+def test_advancing_window_channel_wise_cell(D, W, mode):
+    # the channel-wise cell's maps-only phase and first-step tracking: a
+    # window shorter than the chunking, widths that do not fill a workgroup
+    # row, a window longer than the horizon's first converged prefix
+    rng = np.random.default_rng(700 + D + W)
+    B, T = 2, 1500
+    wl = dict(cfg=0, cell=pn.CELL_DIAG_TANH, D=D, m=D, B=B, T=T, tol=1e-5, damping=1.0, window=W,
+              window_mode="advancing", max_iter=T, params=rng.uniform(0.5, 0.95, D).astype(np.float32),
+              x=(rng.standard_normal((B, T, D)) * np.sqrt(0.5)).astype(np.float32),
+              s0=(0.3 * rng.standard_normal((B, D))).astype(np.float32))
+    _parity(wl, mode)
+    if mode == Q:
+        wl["damping"] = 0.7
+        _parity(wl, mode)
+
+
 @pytest.mark.parametrize("kind, D", [(pn.CELL_EULER_TANH, 32), (pn.CELL_EULER_TANH, 64),
                                      (pn.CELL_GRU, 16), (pn.CELL_TANH_RNN, 5)])
 @pytest.mark.parametrize("W", [40, 128])
