@@ -81,7 +81,9 @@ __device__ __forceinline__ float stored(float v) {
     return static_cast<float>(static_cast<S>(v));
 }
 
-template <int MODE, int PHASE, typename S, int NCH, bool UND>
+// TRACK: also reduce the first step whose residual exceeds tol (the
+// advancing window); compiled out otherwise.
+template <int MODE, int PHASE, typename S, int NCH, bool UND, bool TRACK = false>
 __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
     if constexpr (PHASE != kPrologue && PHASE != kMaps) {
         if (g.ctrl->stop && !g.force) return;    // uniform over the grid: converged earlier
@@ -100,8 +102,7 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
     const int d = (blockIdx.y * cpb + dl) * NCH;     // first channel of the group
     const int b = blockIdx.z;
     uint32_t rb = 0;
-    const bool track = g.fpart != nullptr;           // first step over tol (advancing window)
-    uint32_t fb = 0xffffffffu;
+    uint32_t fb = 0xffffffffu;                       // first step over tol (TRACK)
     if (c < g.NC && d < g.D) {
         const int D = g.D;
         const int DV = D / NCH;                      // row stride in groups
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
                             const float v = tanh_f(a[k] * prev[k] + xt[k]);
                             const float dr = st[k] - v;
                             rb = max(rb, abs_bits(dr));
-                            if (track && !(fabsf(dr) <= g.tol)) fb = min(fb, static_cast<uint32_t>(t0 + j + u));
+                            if (TRACK && !(fabsf(dr) <= g.tol)) fb = min(fb, static_cast<uint32_t>(t0 + j + u));
                             const float at = mode_coef<MODE>(a[k] * (1.0f - v * v));
                             const float bt = v - at * prev[k];
                             A[k] = at * A[k];
@@ -235,8 +236,9 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
                     sh0[k] = sh0_end[k] = 0.0f;
                 }
             }
-            // passes that read only x prefetch as deep as the prologue
-            constexpr int U = kReadS ? kU : kUP;
+            // float passes that read only x prefetch as deep as the prologue
+            // (binary16 sweeps are bound by their vector instructions)
+            constexpr int U = (kReadS || !std::is_same<S, float>::value) ? kU : kUP;
             V xb[U], sb[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
                             // iteration i+1: residual and affine map at p_t = s^(i+1)_{t-1}
                             const float v2 = tanh_f(a[k] * snp[k] + xt[k]);
                             rb = max(rb, abs_bits(sn[k] - v2));
-                            if (track && !(fabsf(sn[k] - v2) <= g.tol))
+                            if (TRACK && !(fabsf(sn[k] - v2) <= g.tol))
                                 fb = min(fb, static_cast<uint32_t>(t0 + j + u));
                             const float a2 = mode_coef<MODE>(a[k] * (1.0f - v2 * v2));
                             const float b2 = v2 - a2 * snp[k];
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
     rb = block_max_u32(rb);
     const int bid = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
     if (threadIdx.x == 0) g.rpart[bid] = rb;
-    if (track) {
+    if constexpr (TRACK) {
         fb = ~block_max_u32(~fb);
         if (threadIdx.x == 0) g.fpart[bid] = fb;
     }
@@ -348,11 +350,12 @@ static hipError_t launch_und(int phase, const DiagArgs& a, hipStream_t st) {
     const dim3 grid = diag_grid(a);
     if (phase == kPrologue) diag_tanh_pass<MODE, kPrologue, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
     else if (phase == kFirst) diag_tanh_pass<MODE, kFirst, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
-    else if (phase == kSteady) diag_tanh_pass<MODE, kSteady, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
-    else if (phase == kMaps) diag_tanh_pass<MODE, kMaps, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
+    else if (phase == kSteady && !a.fpart) diag_tanh_pass<MODE, kSteady, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
     else if constexpr (std::is_same<S, float>::value) {
-        // the recomputing pair runs with float storage only
-        if (phase == kFirstNS) diag_tanh_pass<MODE, kFirstNS, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
+        // the advancing window and the recomputing pair run with float storage only
+        if (phase == kSteady) diag_tanh_pass<MODE, kSteady, S, NCH, UND, true><<<grid, kThreads, 0, st>>>(a);
+        else if (phase == kMaps) diag_tanh_pass<MODE, kMaps, S, NCH, UND, true><<<grid, kThreads, 0, st>>>(a);
+        else if (phase == kFirstNS) diag_tanh_pass<MODE, kFirstNS, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
         else if (phase == kSecondR) diag_tanh_pass<MODE, kSecondR, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
         else return hipErrorInvalidValue;
     } else {
