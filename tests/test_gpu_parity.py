@@ -211,6 +211,24 @@ def test_matrix_cells_other_widths(kind, D):
         _parity(wl, mode)
 
 
+@pytest.mark.parametrize("T", [1, 2, 17])
+@pytest.mark.parametrize("kind, D", [(pn.CELL_DIAG_TANH, 64), (pn.CELL_TANH_RNN, 20), (pn.CELL_TANH_RNN, 64),
+                                     (pn.CELL_GRU, 16), (pn.CELL_EULER_TANH, 32)])
+def test_tiny_horizons(kind, D, T):
+    # one chunk of one short sub-chunk, carries with no step to take, the
+    # two-wavefront dense form with a single chunk, the channel-wise cell's
+    # first two updates on one chunk
+    rng = np.random.default_rng(800 + D + T)
+    m, B = (D if kind == pn.CELL_DIAG_TANH else 3), 3
+    params = (rng.uniform(0.5, 0.95, D).astype(np.float32) if kind == pn.CELL_DIAG_TANH
+              else workloads.random_cell_params(kind, D, m, rng, 1.0))
+    wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-6, damping=1.0, window=0, max_iter=T,
+              params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32), bandwidth=2)
+    for mode in (N, Q, J):
+        _parity(wl, mode)
+
+
 @pytest.mark.parametrize("kind, D, m", [(pn.CELL_TANH_RNN, 24, 37), (pn.CELL_GRU, 16, 19),
                                          (pn.CELL_EULER_TANH, 48, 21), (pn.CELL_TANH_RNN, 36, 5),
                                          (pn.CELL_TANH_RNN, 64, 33)])
