@@ -142,6 +142,9 @@ typedef struct pn_opts {
     int32_t* window_switch;   /* host; per window: the check that switched, or
                                  -1 (truncated to window_switch_len)           */
     int64_t window_switch_len;
+    float switch_damping;     /* 0 (default): the damping stays `damping` after
+                                 a switch; else, in (0, 1], the step damping of
+                                 the updates after it (below)                  */
 } pn_opts;
 
 /* Residual-driven switching [PN §5.3]: start each window on the coarse
@@ -149,8 +152,12 @@ typedef struct pn_opts {
  * At each check i >= 1 of a window still on `mode`, r_i > switch_ratio *
  * r_{i-1} switches it: update i (already under way) keeps `mode`, updates
  * i+1, ... use `switch_mode` (its chunk maps are rebuilt at s^(i+1) by one
- * extra sweep).  Matrix cells with consecutive windows only (PN_EUNSUPPORTED
- * otherwise).  A typical use is quasi-Newton first, then the banded or full
+ * extra sweep when it differs from `mode`) and, if switch_damping > 0, the
+ * step damping switch_damping instead of `damping` -- the other remedy the
+ * article gives for a stalling curve.  switch_mode == mode with
+ * switch_damping set switches the damping alone.  Consecutive windows, float
+ * storage (pn_eval_ex); PN_EUNSUPPORTED with the advancing window or
+ * pn_eval_f16.  A typical use is quasi-Newton first, then the banded or full
  * Jacobian. */
 
 /* pn_opts.window_mode.
@@ -181,7 +188,8 @@ enum { PN_WINDOW_CONSECUTIVE = 0, PN_WINDOW_ADVANCING = 1 };
 enum { PN_FLAG_PERSISTENT = 1 };
 
 /* Fill *o with the defaults: damping 1, chunk 0, window 0, bandwidth 1,
- * switch_mode -1, switch_ratio 0.5, everything else NULL / 0. */
+ * switch_mode -1, switch_ratio 0.5, switch_damping 0, everything else
+ * NULL / 0. */
 void pn_opts_init(pn_opts* o);
 
 /* Solve the recurrence for all B sequences [PN §1.1, §1.2].

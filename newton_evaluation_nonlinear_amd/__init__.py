@@ -58,7 +58,8 @@ class Opts(ctypes.Structure):
                 ("accepted", ctypes.POINTER(ctypes.c_int32)), ("accepted_len", ctypes.c_int64),
                 ("switch_mode", ctypes.c_int32), ("switch_ratio", ctypes.c_float),
                 ("window_switch", ctypes.POINTER(ctypes.c_int32)),
-                ("window_switch_len", ctypes.c_int64)]
+                ("window_switch_len", ctypes.c_int64),
+                ("switch_damping", ctypes.c_float)]
 
 
 _lib = None
@@ -119,7 +120,7 @@ def _stream_ptr(device):
 
 
 def make_opts(damping=1.0, window=0, chunk=0, stream=None, flags=0, bandwidth=1,
-              window_mode=WINDOW_CONSECUTIVE, switch_mode=-1, switch_ratio=0.5):
+              window_mode=WINDOW_CONSECUTIVE, switch_mode=-1, switch_ratio=0.5, switch_damping=0.0):
     o = Opts()
     lib().pn_opts_init(ctypes.byref(o))
     o.damping = float(damping)
@@ -131,6 +132,7 @@ def make_opts(damping=1.0, window=0, chunk=0, stream=None, flags=0, bandwidth=1,
     o.window_mode = int(window_mode)
     o.switch_mode = int(switch_mode)
     o.switch_ratio = float(switch_ratio)
+    o.switch_damping = float(switch_damping)
     return o
 
 
@@ -161,7 +163,8 @@ class Result:
 
 def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, damping=1.0,
          window=0, chunk=0, out=None, history=False, profile=False, workspace=None, flags=0,
-         bandwidth=1, window_mode=WINDOW_CONSECUTIVE, switch_mode=-1, switch_ratio=0.5):
+         bandwidth=1, window_mode=WINDOW_CONSECUTIVE, switch_mode=-1, switch_ratio=0.5,
+         switch_damping=0.0):
     """Solve s_t = f(s_{t-1}, x_t) for t = 1..T over the batch; see include/pn.h.
 
     params, x [B,T,m], s0 [B,D] are float32 tensors on one HIP device; with
@@ -171,7 +174,9 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     WINDOW_ADVANCING slides one window past its converged prefix (max_iter
     then defaults to T and caps the updates of the whole solve); ``switch_mode``
     >= 0 moves each window to that mode when its residual stalls
-    (r_i > switch_ratio * r_{i-1}).
+    (r_i > switch_ratio * r_{i-1}), and to the step damping
+    ``switch_damping`` if that is > 0 (``switch_mode`` == ``mode`` switches
+    the damping alone).
     Returns a ``Result`` (unpacks as ``out, iters, status``).  Negative
     library statuses raise ``PnError``.
     """
@@ -190,7 +195,7 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
         out = torch.empty((B, T, D), dtype=sdt, device=dev)
     c = Cell(int(cell_kind), int(m))
     o = make_opts(damping, window or 0, chunk, _stream_ptr(dev), flags, bandwidth, window_mode,
-                  switch_mode, switch_ratio)
+                  switch_mode, switch_ratio, switch_damping)
     nbytes = lib().pn_workspace_bytes(ctypes.byref(c), B, T, D, int(mode), ctypes.byref(o))
     if nbytes == 0:
         raise PnError(EINVAL, last_error())

@@ -276,8 +276,8 @@ int validate(const pn_cell* cell, const float* params, const float* x, const flo
             if (!(o->switch_ratio >= 0.0f)) return fail(PN_EINVAL, "switch_ratio must be >= 0");
             if (o->switch_mode == PN_BANDED && o->bandwidth < 0)
                 return fail(PN_EINVAL, "bandwidth must be >= 0");
-            if (cell->kind == PN_CELL_DIAG_TANH)
-                return fail(PN_EUNSUPPORTED, "mode switching supports the matrix cells only");
+            if (!(o->switch_damping == 0.0f || (o->switch_damping > 0.0f && o->switch_damping <= 1.0f)))
+                return fail(PN_EINVAL, "switch_damping must be 0 or lie in (0, 1]");
             if (o->window_mode == PN_WINDOW_ADVANCING)
                 return fail(PN_EUNSUPPORTED, "mode switching and the advancing window do not combine");
         }
@@ -377,6 +377,7 @@ struct SolveCtx {
     Timing* tm;
     std::vector<float>* hist;
     float ratio;             // switch_ratio (residual-driven switching)
+    float lam2;              // switch_damping: damping after a switch (0: keep lam)
 };
 
 double apply_bytes(const Plan& p, int Tw, bool first) {
@@ -417,8 +418,9 @@ int record(SolveCtx& c, size_t* idx) {
 // driven switching [PN §5.3]), the window starts on plan p and, at the first
 // check i >= 1 with r_i > ratio * r_{i-1}, moves to p2 from update i+1 on
 // (apply(i) is already enqueued): the chunk maps of p2's mode are rebuilt at
-// s^(i+1) by a maps pass, then the loop continues on p2.  *sw receives that
-// check, or -1.
+// s^(i+1) by a maps pass (unless p2 has the same mode, whose maps apply(i)
+// built), the damping becomes lam2 when that is set, and the loop continues
+// on p2.  *sw receives that check, or -1.
 int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, const float* s0,
                  int64_t s0s, int Tw, int* K, int* status, const Plan* p2, int* sw) {
     const Plan* pp = c.p;
@@ -430,6 +432,8 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
     float* carry0 = reinterpret_cast<float*>(c.ws + pp->off_carry0);
     float* halo = reinterpret_cast<float*>(c.ws + pp->off_halo);
     const float* w = reinterpret_cast<const float*>(c.ws + pp->off_w);
+    uint32_t* fpart = reinterpret_cast<uint32_t*>(c.ws + pp->off_fpart);
+    float lam = c.lam;       // step damping of the updates still to be enqueued
     // the first two updates of the channel-wise cell move less (kFirstNS,
     // kSecondR): iteration 0's carries go to their own buffer
     const bool recompute = pp->recompute && !p2;
@@ -451,7 +455,7 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
             da.B = p.B; da.Tw = Tw; da.D = p.D; da.L = p.L; da.NC = NC; da.cpb = p.cpb;
             da.aggA = aggA; da.aggB = aggB; da.carry = carry; da.carry0 = carry0; da.halo = halo;
             da.rpart = rpart;
-            da.ctrl = ctrl; da.mode = p.mode; da.lam = c.lam; da.undamped = c.lam == 1.0f;
+            da.ctrl = ctrl; da.mode = p.mode; da.lam = lam; da.undamped = lam == 1.0f;
             da.half = p.hmode;
             da.rf = 1; da.NCr = NC;
             da.hs = static_cast<int64_t>(p.B) * p.NC * p.D;
@@ -461,7 +465,7 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
             ca.w = w; ca.x = x; ca.xs = xs; ca.s = s; ca.ss = ss; ca.s0 = s0; ca.s0s = s0s;
             ca.B = p.B; ca.Tw = Tw; ca.D = p.D; ca.m = p.m; ca.L = p.L; ca.NC = NC;
             ca.aggA = aggA; ca.aggB = aggB; ca.carry = carry; ca.halo = halo; ca.rpart = rpart;
-            ca.ctrl = ctrl; ca.mode = p.mode; ca.lam = c.lam; ca.undamped = c.lam == 1.0f;
+            ca.ctrl = ctrl; ca.mode = p.mode; ca.lam = lam; ca.undamped = lam == 1.0f;
             ca.band = p.band;
             nblocks = cell_pass_nblocks(ca);
         }
@@ -557,9 +561,18 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
         if (p2 && *sw < 0 && i >= 1 && r > c.ratio * r_prev) {
             // stagnation: update i runs on the first mode; from i+1 on, p2
             *sw = i;
+            const bool new_maps = p2->mode != pp->mode;
             pp = p2;
+            if (c.lam2 > 0.0f) lam = c.lam2;
             configure(*pp);
-            PN_HIP(launch_pass(kMaps, i + 1));
+            if (new_maps) {
+                // the channel-wise maps pass also reduces the first step over
+                // tol, which nothing reads here
+                da.fpart = fpart;
+                da.tol = c.tol;
+                PN_HIP(launch_pass(kMaps, i + 1));
+                da.fpart = nullptr;
+            }
         }
         r_prev = r;
     }
@@ -793,6 +806,8 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
             return fail(PN_EUNSUPPORTED, "binary16 storage supports the channel-wise cell only");
         if (o && ((o->window > 0 && o->window < T) || o->window_mode != PN_WINDOW_CONSECUTIVE))
             return fail(PN_EUNSUPPORTED, "binary16 storage solves the whole horizon as one window");
+        if (o && o->switch_mode >= 0)
+            return fail(PN_EUNSUPPORTED, "binary16 storage does not combine with switching");
     }
     if (o && o->profile) std::memset(o->profile, 0, sizeof(pn_profile));
     if (B == 0 || T == 0 || D == 0) {
@@ -827,7 +842,7 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     tm.on = o && o->profile;
     std::vector<float> hist;
     SolveCtx c{&p, st, ws, res, params, tol, o ? o->damping : 1.0f, max_iter, &tm, &hist,
-               o ? o->switch_ratio : 0.0f};
+               o ? o->switch_ratio : 0.0f, o ? o->switch_damping : 0.0f};
     if (p.matrix_cell)
         PN_HIP(launch_prep_weights(p.kind, params, reinterpret_cast<float*>(ws + p.off_w), p.D, p.DP, p.m, st));
     size_t ev_first = 0;
@@ -918,6 +933,7 @@ void pn_opts_init(pn_opts* o) {
     o->bandwidth = 1;
     o->switch_mode = -1;
     o->switch_ratio = 0.5f;
+    o->switch_damping = 0.0f;
 }
 
 int pn_eval_ex(const pn_cell* cell, const float* params, const float* x, const float* s0, int64_t B,

@@ -36,7 +36,11 @@ Readings where the article is silent (documented alongside the build):
     stagnates.  Read as: at each check i >= 1 of a window, while still on the
     first mode, r_i > rho * r_{i-1} switches the window to the second mode
     from update i+1 on (update i, which follows check i, keeps the first
-    mode); each window starts on the first mode;
+    mode); each window starts on the first mode.  The other remedy the
+    article names for a stalling curve, more damping, is read the same way:
+    with a second damping lam2, the switch also changes the step damping
+    from lam to lam2 from update i+1 on (the second mode may equal the first,
+    which makes it a pure damping switch);
   * reduced-precision storage [PN §2.3, §4.2] (``storage="f16"``): every
     state the update stores is rounded to nearest-even IEEE binary16 and the
     iteration continues from the stored states; arithmetic is unchanged;
@@ -160,7 +164,8 @@ def _stored(s, storage):
 
 def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force, bandwidth, switch=None,
                   storage=None):
-    """One window.  ``switch`` = (second mode, rho, forced check or None)."""
+    """One window.  ``switch`` = (second mode, rho, forced check or None,
+    second damping or None)."""
     B, T = x.shape[0], x.shape[1]
     s = np.broadcast_to(np.asarray(s0, dtype=cell.dtype)[:, None, :], (B, T, cell.D)).copy()
     hist = []
@@ -182,23 +187,25 @@ def _solve_window(cell, x, s0, mode, tol, max_iter, damping, force, bandwidth, s
             status = NONFINITE if not np.isfinite(r) else (OK if r <= tol else NOT_CONVERGED)
             return s, i, status, hist, sw
         if switch is not None and sw < 0 and i >= 1:
-            mode2, rho, forced = switch
+            rho, forced = switch[1], switch[2]
             if (forced == i) if forced is not None else (r > rho * hist[-2]):
                 sw = i
-        use = switch[0] if (switch is not None and 0 <= sw < i) else mode
+        switched = switch is not None and 0 <= sw < i
+        use = switch[0] if switched else mode
+        lam = switch[3] if (switched and switch[3] is not None) else damping
         A = jacobian_approx(use, cell, p, x, bandwidth)
         s_hat = affine_recurrence(v, p, A, s0)
-        if damping == 1.0:
+        if lam == 1.0:
             s = s_hat
         else:
-            s = s + damping * (s_hat - s)
+            s = s + lam * (s_hat - s)
         s = _stored(s, storage)
         i += 1
 
 
 def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
           dtype=np.float64, force_iters=None, bandwidth=1, switch_mode=None, switch_ratio=0.5,
-          force_switch=None, storage=None):
+          force_switch=None, storage=None, switch_damping=None):
     """Parallel-in-time fixed-point solve, evaluated sequentially.
 
     kind/params follow the flat layout of ``make_cell``; x: [B, T, m];
@@ -209,7 +216,9 @@ def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
     the floating-point ambiguity band of the tolerance.  ``bandwidth`` is the
     half-bandwidth k of the banded mode.  ``switch_mode`` (with
     ``switch_ratio`` rho) turns on residual-driven switching; ``force_switch``
-    (one check index or -1 per window) replaces its decisions.  ``storage``
+    (one check index or -1 per window) replaces its decisions, and
+    ``switch_damping`` (in (0, 1], or None to keep ``damping``) is the step
+    damping after a switch.  ``storage``
     "f16" stores the iterate in binary16 (x must already hold binary16
     values); the returned trajectory is the stored one.
     """
@@ -232,7 +241,8 @@ def solve(kind, params, x, s0, mode, tol, max_iter, damping=1.0, window=0,
         switch = None
         if switch_mode is not None:
             fs = None if force_switch is None else int(force_switch[wi])
-            switch = (switch_mode, switch_ratio, fs if fs is None or fs >= 0 else 10 ** 9)
+            switch = (switch_mode, switch_ratio, fs if fs is None or fs >= 0 else 10 ** 9,
+                      switch_damping)
         s, K, st, hist, sw = _solve_window(cell, xc[:, w0:w1], s_init, mode, tol, max_iter,
                                            damping, force, bandwidth, switch, storage)
         s = _stored(s, storage)

@@ -54,7 +54,8 @@ def run_gpu(wl, mode, tol=None, max_iter=None, damping=None, window=None, chunk=
                   chunk=chunk, history=history, profile=profile,
                   bandwidth=wl.get("bandwidth", 1),
                   window_mode=pn.WINDOW_ADVANCING if advancing(wl) else pn.WINDOW_CONSECUTIVE,
-                  switch_mode=wl.get("switch_mode", -1), switch_ratio=wl.get("switch_ratio", 0.5))
+                  switch_mode=wl.get("switch_mode", -1), switch_ratio=wl.get("switch_ratio", 0.5),
+                  switch_damping=wl.get("switch_damping", 0.0))
     torch.cuda.synchronize()
     res.out_np = res.out.float().cpu().numpy()
     return res
@@ -85,7 +86,8 @@ def run_oracle(wl, mode, tol=None, max_iter=None, damping=None, window=None, dty
                          force_iters=force_iters, bandwidth=args["bandwidth"],
                          switch_mode=sm if sm >= 0 else None,
                          switch_ratio=wl.get("switch_ratio", 0.5), force_switch=force_switch,
-                         storage=wl.get("storage"))
+                         storage=wl.get("storage"),
+                         switch_damping=wl.get("switch_damping") or None)
     if ck is not None:
         _oracle_cache[ck] = r
     return r

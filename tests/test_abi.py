@@ -109,15 +109,22 @@ def test_switch_options():
                      (dict(switch_mode=pn.NEWTON, window_mode=pn.WINDOW_ADVANCING), pn.EUNSUPPORTED)]:
         rc, _ = _eval_raw(opts=pn.make_opts(**kw))
         assert rc == code, kw
-    rc, _ = _eval_raw(kind=pn.CELL_DIAG_TANH, m=4, D=4, opts=pn.make_opts(switch_mode=pn.NEWTON))
-    assert rc == pn.EUNSUPPORTED
+    for lam2 in (-0.5, 1.5, float("nan"), float("inf")):
+        rc, _ = _eval_raw(opts=pn.make_opts(switch_mode=pn.NEWTON, switch_damping=lam2))
+        assert rc == pn.EINVAL, lam2
+    # every cell accepts switching, the damping switch included (B = 0: no
+    # device work)
+    for kind, m in ((pn.CELL_DIAG_TANH, 4), (pn.CELL_TANH_RNN, 3), (pn.CELL_GRU, 3), (pn.CELL_EULER_TANH, 3)):
+        o = pn.make_opts(switch_mode=pn.QUASI_NEWTON, switch_damping=0.5)
+        rc, it = _eval_raw(kind=kind, m=m, D=4, B=0, opts=o)
+        assert rc == pn.OK and it == 0, kind
     # one workspace holds the regions of both modes
     nq = pn.workspace_bytes(pn.CELL_GRU, 8, 64, 2048, 16, pn.QUASI_NEWTON)
     nn = pn.workspace_bytes(pn.CELL_GRU, 8, 64, 2048, 16, pn.NEWTON)
     ns = pn.workspace_bytes(pn.CELL_GRU, 8, 64, 2048, 16, pn.QUASI_NEWTON, switch_mode=pn.NEWTON)
     assert ns >= max(nq, nn)
     o = pn.make_opts()
-    assert o.switch_mode == -1 and abs(o.switch_ratio - 0.5) < 1e-7
+    assert o.switch_mode == -1 and abs(o.switch_ratio - 0.5) < 1e-7 and o.switch_damping == 0.0
 
 
 def test_f16_entry_checks():
@@ -132,6 +139,9 @@ def test_f16_entry_checks():
     assert L.pn_eval_f16(ctypes.byref(c), p, p, p, 2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
                          ctypes.byref(it), ctypes.byref(o)) == pn.EUNSUPPORTED
     o = pn.make_opts(window_mode=pn.WINDOW_ADVANCING)
+    assert L.pn_eval_f16(ctypes.byref(c), p, p, p, 2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
+                         ctypes.byref(it), ctypes.byref(o)) == pn.EUNSUPPORTED
+    o = pn.make_opts(switch_mode=pn.QUASI_NEWTON, switch_damping=0.5)
     assert L.pn_eval_f16(ctypes.byref(c), p, p, p, 2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
                          ctypes.byref(it), ctypes.byref(o)) == pn.EUNSUPPORTED
     assert L.pn_eval_f16(ctypes.byref(c), p, p, p, -2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,

@@ -452,6 +452,55 @@ def test_switching_limits():
     np.testing.assert_array_equal(gi.out_np, q.out_np)
 
 
+@pytest.mark.parametrize("kind, D, mode, second, lam2", [
+    (pn.CELL_GRU, 16, Q, Q, 0.5),             # damping alone, LDS kernel
+    (pn.CELL_TANH_RNN, 32, N, N, 0.6),        # damping alone, Newton on the matrix cores
+    (pn.CELL_GRU, 64, Q, N, 0.7),             # a new mode and a new damping together
+    (pn.CELL_EULER_TANH, 32, Q, pn.BANDED, 0.5),
+    (pn.CELL_TANH_RNN, 12, Q, Q, 0.5)])
+def test_damping_on_stagnation_matches_oracle(kind, D, mode, second, lam2):
+    # the other remedy for a stalling residual curve: more step damping from
+    # the update after the stall on (two windows, each starts undamped)
+    rng = np.random.default_rng(700 + D)
+    m, B, T = 3, 2, 300
+    params = (workloads.lattice_cell_params(kind, D, m, rng) if kind != pn.CELL_EULER_TANH
+              else workloads.random_cell_params(kind, D, m, rng, 1.0))
+    wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-5, damping=1.0, window=150,
+              max_iter=150, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32), bandwidth=2,
+              switch_mode=second, switch_ratio=0.5, switch_damping=lam2)
+    _parity(wl, mode)
+
+
+@pytest.mark.parametrize("first, second, lam2, rho", [(J, Q, 0.0, 0.5), (P, Q, 0.0, 0.5), (Q, Q, 0.5, 0.5),
+                                                       (J, Q, 0.7, 0.9)])
+def test_switching_channel_wise_cell(first, second, lam2, rho):
+    # the channel-wise cell: a new mode rebuilds the chunk maps with the
+    # cell's maps pass; a new damping alone changes only the apply launches
+    wl = _case(3, B=2, T=900)
+    wl.update(window=300, max_iter=300, switch_mode=second, switch_ratio=rho, switch_damping=lam2)
+    _parity(wl, first)
+
+
+@pytest.mark.parametrize("cfg, mode", [(3, Q), (2, Q), (4, N)])
+def test_switch_to_the_same_mode_and_damping_is_the_plain_solve(cfg, mode):
+    # rho = 0 switches at check 1; switching to the same mode with damping 1
+    # changes nothing: bit for bit on the matrix cells; the plain solve of the
+    # channel-wise cell runs its first two updates as the recomputing pair on
+    # other chunk lengths (a solve that may switch does not), so there the
+    # trajectories agree to float32 rounding of the scan order
+    wl = _case(cfg, B=2, T=640)
+    plain = run_gpu(wl, mode)
+    wl.update(switch_mode=mode, switch_ratio=0.0, switch_damping=1.0)
+    g = run_gpu(wl, mode)
+    assert plain.iters >= 2 and g.window_switch[:len(g.window_iters)] == [1] * len(g.window_iters)
+    assert g.iters == plain.iters and g.status == plain.status
+    if wl["cell"] == pn.CELL_DIAG_TANH:
+        np.testing.assert_allclose(g.out_np, plain.out_np, rtol=0, atol=4e-6)
+    else:
+        np.testing.assert_array_equal(g.out_np, plain.out_np)
+
+
 def test_cfg6_lattice_switching_small():
     wl = _case(6, B=2, T=700)
     wl.update(switch_mode=pn.BANDED, switch_ratio=0.5)

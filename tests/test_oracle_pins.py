@@ -603,6 +603,102 @@ def test_switching_on_stagnation_saves_fine_updates():
     assert len(w.window_switch) == 4 and all(k >= 1 for k in w.window_switch)
 
 
+def _error_operators(A, T):
+    """Error maps of one undamped update on the affine cell f(p) = A p + x,
+    acting on the stacked trajectory error e = s - s* (T blocks of D; s0 is
+    exact): Jacobi e -> S_A e, quasi-Newton e -> (I - S_dg)^-1 (S_A - S_dg) e,
+    where S_M puts M e_{t-1} in block t and dg is diag(A)."""
+    D = A.shape[0]
+
+    def shift(M):
+        S = np.zeros((T * D, T * D))
+        for t in range(1, T):
+            S[t * D:(t + 1) * D, (t - 1) * D:t * D] = M
+        return S
+
+    SA, Sd = shift(A), shift(np.diag(np.diagonal(A)))
+    I = np.eye(T * D)
+    return SA, np.linalg.solve(I - Sd, SA - Sd)
+
+
+def test_damping_switch_closed_form_on_an_affine_cell():
+    # Jacobi with damping lam1 until the switch, then quasi-Newton with lam2:
+    # the error after K updates is N2^(K-sw-1) N1^(sw+1) e0 with
+    # N = (1 - lam) I + lam G for the mode's error map G
+    rng = np.random.default_rng(41)
+    D, T = 3, 6
+    A = 0.6 * rng.standard_normal((D, D))
+    cell = _Affine(A)
+    x = rng.standard_normal((1, T, D))
+    s0 = rng.standard_normal((1, D))
+    star = np.empty((T, D))
+    prev = s0[0]
+    for t in range(T):
+        prev = A @ prev + x[0, t]
+        star[t] = prev
+    e0 = (np.broadcast_to(s0[0], (T, D)) - star).reshape(-1)
+    GJ, GQ = _error_operators(A, T)
+    I = np.eye(T * D)
+    lam1, lam2 = 0.8, 0.45
+    N1, N2 = (1 - lam1) * I + lam1 * GJ, (1 - lam2) * I + lam2 * GQ
+    for forced, K in [(None, 7), (3, 9), (1, 2)]:
+        # rho = 0 switches at check 1 (r_1 > 0); forced replaces the decision
+        s, k, _, hist, sw = osv._solve_window(cell, x, s0, oracle.JACOBI, 0.0, 100, lam1, K, 1,
+                                              (oracle.QUASI_NEWTON, 0.0, forced, lam2))
+        assert k == K and sw == (1 if forced is None else forced)
+        n1 = min(K, sw + 1)
+        want = np.linalg.matrix_power(N2, K - n1) @ np.linalg.matrix_power(N1, n1) @ e0
+        np.testing.assert_allclose((s[0] - star).reshape(-1), want, rtol=0, atol=1e-12)
+    # no second damping: the switch keeps lam1
+    s, _, _, _, sw = osv._solve_window(cell, x, s0, oracle.JACOBI, 0.0, 100, lam1, 5, 1,
+                                       (oracle.QUASI_NEWTON, 0.0, None, None))
+    N2k = (1 - lam1) * I + lam1 * GQ
+    want = np.linalg.matrix_power(N2k, 3) @ np.linalg.matrix_power(N1, 2) @ e0
+    np.testing.assert_allclose((s[0] - star).reshape(-1), want, rtol=0, atol=1e-12)
+
+
+def test_damping_switch_replays_by_hand():
+    # rho = 0: updates 0 and 1 are undamped quasi-Newton, the rest damped Newton
+    wl = workloads.make(2, B=2, T=48)
+    cell = oracle.make_cell(wl["cell"], wl["params"], wl["D"], wl["m"])
+    x, s0 = wl["x"].astype(np.float64), wl["s0"].astype(np.float64)
+    r = oracle.solve(wl["cell"], wl["params"], wl["x"], wl["s0"], oracle.QUASI_NEWTON, 1e-9, 64,
+                     switch_mode=oracle.NEWTON, switch_ratio=0.0, switch_damping=0.5)
+    assert r.status == oracle.OK and r.window_switch == [1] and r.iters > 3
+    s = np.broadcast_to(s0[:, None], x.shape[:2] + (wl["D"],)).copy()
+    for k in range(r.iters):
+        if k <= 1:
+            s = oracle.newton_step(cell, x, s0, s, oracle.QUASI_NEWTON)
+        else:
+            s = 0.5 * s + 0.5 * oracle.newton_step(cell, x, s0, s, oracle.NEWTON)
+    np.testing.assert_allclose(r.s, s, rtol=0, atol=1e-13)
+
+
+def test_damping_switch_identities_and_fixed_point():
+    wl = workloads.make(2, B=2, T=96)
+    args = (wl["cell"], wl["params"], wl["x"], wl["s0"], oracle.QUASI_NEWTON, 1e-7, 96)
+    q = oracle.solve(*args)
+    # the same mode and no second damping (or the same one): the plain solve
+    for lam2 in (None, 1.0):
+        r = oracle.solve(*args, switch_mode=oracle.QUASI_NEWTON, switch_ratio=0.0,
+                         switch_damping=lam2)
+        assert r.window_switch == [1] and r.iters == q.iters
+        np.testing.assert_array_equal(r.s, q.s)
+    # a damping switch moves no fixed point: still the sequential trajectory
+    cell = oracle.make_cell(wl["cell"], wl["params"], wl["D"], wl["m"])
+    seq = oracle.sequential(cell, wl["x"].astype(np.float64), wl["s0"].astype(np.float64))
+    d = oracle.solve(*args, switch_mode=oracle.QUASI_NEWTON, switch_ratio=0.0, switch_damping=0.6)
+    assert d.status == oracle.OK and d.iters > q.iters
+    np.testing.assert_allclose(d.s, seq, rtol=0, atol=1e-6)
+    # the step after the switch is 0.6 of the undamped one (the damping identity)
+    f2 = oracle.solve(*args, force_iters=[2])
+    f3 = oracle.solve(*args, switch_mode=oracle.QUASI_NEWTON, switch_ratio=0.0,
+                      switch_damping=0.6, force_iters=[3])
+    full = oracle.newton_step(cell, wl["x"].astype(np.float64), wl["s0"].astype(np.float64),
+                              f2.s, oracle.QUASI_NEWTON)
+    np.testing.assert_allclose(f3.s - f2.s, 0.6 * (full - f2.s), rtol=0, atol=1e-14)
+
+
 # ---------------------------------------------------------------- advancing window [PN §1.3.1]
 
 class _Affine:
