@@ -98,12 +98,13 @@ typedef struct pn_cell {
  * HIP events on the call's stream.  They cover the steady-state launches of
  * the fused per-iteration "apply" kernel (cell + Jacobian + scan replay +
  * damping + residual + next chunk maps) for iterations i >= 1, including the
- * last launch, which finds the loop stopped and exits at once.  Algorithmic
- * bytes of a launch that runs: read x and s^(i), write s^(i+1); 0 for the
- * launch that exits. */
+ * last launches, which find the loop stopped and exit at once; with
+ * pn_opts.profile_stride n > 1, only every n-th of them (each event pair
+ * adds stream work between launches).  Algorithmic bytes of a launch that
+ * runs: read x and s^(i), write s^(i+1); 0 for a launch that exits. */
 typedef struct pn_profile {
     double apply_ms;          /* summed device time of apply launches       */
-    int32_t apply_launches;   /* launches, including early-exit ones          */
+    int32_t apply_launches;   /* timed launches, including early-exit ones    */
     double apply_bytes;       /* summed algorithmic bytes of those launches   */
     double apply_flops;       /* summed algorithmic flops: matrix-cell
                                  evaluations and, for Newton and the banded
@@ -145,6 +146,8 @@ typedef struct pn_opts {
     float switch_damping;     /* 0 (default): the damping stays `damping` after
                                  a switch; else, in (0, 1], the step damping of
                                  the updates after it (below)                  */
+    int32_t profile_stride;   /* with profile: time every n-th steady apply
+                                 launch (0 or 1: every one)                    */
 } pn_opts;
 
 /* Residual-driven switching [PN §5.3]: start each window on the coarse
@@ -188,8 +191,8 @@ enum { PN_WINDOW_CONSECUTIVE = 0, PN_WINDOW_ADVANCING = 1 };
 enum { PN_FLAG_PERSISTENT = 1 };
 
 /* Fill *o with the defaults: damping 1, chunk 0, window 0, bandwidth 1,
- * switch_mode -1, switch_ratio 0.5, switch_damping 0, everything else
- * NULL / 0. */
+ * switch_mode -1, switch_ratio 0.5, switch_damping 0, profile_stride 1,
+ * everything else NULL / 0. */
 void pn_opts_init(pn_opts* o);
 
 /* Solve the recurrence for all B sequences [PN §1.1, §1.2].

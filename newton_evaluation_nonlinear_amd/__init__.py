@@ -59,7 +59,8 @@ class Opts(ctypes.Structure):
                 ("switch_mode", ctypes.c_int32), ("switch_ratio", ctypes.c_float),
                 ("window_switch", ctypes.POINTER(ctypes.c_int32)),
                 ("window_switch_len", ctypes.c_int64),
-                ("switch_damping", ctypes.c_float)]
+                ("switch_damping", ctypes.c_float),
+                ("profile_stride", ctypes.c_int32)]
 
 
 _lib = None
@@ -177,6 +178,8 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     (r_i > switch_ratio * r_{i-1}), and to the step damping
     ``switch_damping`` if that is > 0 (``switch_mode`` == ``mode`` switches
     the damping alone).
+    ``profile`` True times every steady apply launch with HIP events, an
+    integer n > 1 every n-th (Result.profile).
     Returns a ``Result`` (unpacks as ``out, iters, status``).  Negative
     library statuses raise ``PnError``.
     """
@@ -227,6 +230,7 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     prof = Profile() if profile else None
     if prof is not None:
         o.profile = ctypes.pointer(prof)
+        o.profile_stride = int(profile)     # True: every steady launch; n: every n-th
     iters = ctypes.c_int32(0)
     entry = lib().pn_eval_f16 if half else lib().pn_eval_ex
     rc = entry(ctypes.byref(c), _dev_f32(params, "params"), _dev_f32(x, "x", sdt),

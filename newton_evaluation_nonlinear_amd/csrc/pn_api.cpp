@@ -73,6 +73,8 @@ struct Plan {
     bool persist_ok;       // shape allows the one-launch persistent solver
     bool recompute;        // channel-wise cell, float storage: first update stores nothing,
                            // the second recomputes s^(1) (kFirstNS, kSecondR)
+    bool fc;               // matrix cell, diagonal mode, few chunks: each apply sweep takes
+                           // its own check and carries (CellArgs::fc), no carry launch
     int nblocks, nwin, hist_cap;
     size_t off_ctrl, off_rpart, off_fpart, off_aggA, off_aggB, off_carry, off_carry0, off_halo, off_w,
         total;
@@ -106,6 +108,7 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
     const int chunk = o ? o->chunk : 0;
     p.dense = p.matrix_cell && (mode == PN_NEWTON || mode == PN_BANDED);
     p.mfma = false;
+    p.fc = false;
     if (!p.matrix_cell) {
         // binary16 storage moves two adjacent channels per thread when D is even
         p.hmode = !half ? 0 : (p.D % 2 == 0 ? 2 : 1);
@@ -175,6 +178,9 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
         p.L = p.Lc = static_cast<int>(std::min<int64_t>(L, p.W));
         p.NC = static_cast<int>((p.W + p.L - 1) / p.L);
         p.nblocks = p.NC * p.B;
+        // with few chunks per row, composing a chunk's carry in its own sweep
+        // costs less than a carry launch
+        p.fc = !p.dense && !p.advancing && p.NC <= kFcMaxChunks;
         if (cell_pass_lds_bytes(p.kind, p.DP, p.dense, p.L, p.m) > 160 * 1024)
             return fail(PN_EUNSUPPORTED, "chunk of %d steps needs too much LDS for D=%d, m=%d", p.L, p.D, p.m);
     }
@@ -205,8 +211,10 @@ void layout(Plan& p, const Plan* other) {
     p.off_ctrl = off; off = align_up(off + sizeof(Ctrl));
     p.off_rpart = off; off = align_up(off + sizeof(uint32_t) * nparts);
     p.off_fpart = off; off = align_up(off + sizeof(uint32_t) * nparts);
-    p.off_aggA = off; off = align_up(off + sizeof(float) * nA);
-    p.off_aggB = off; off = align_up(off + sizeof(float) * bnd);
+    // chunk maps: two sets (iterations of either parity) for fc sweeps
+    const size_t nsets = (p.fc || (other && other->fc)) ? 2 : 1;
+    p.off_aggA = off; off = align_up(off + sizeof(float) * nA * nsets);
+    p.off_aggB = off; off = align_up(off + sizeof(float) * bnd * nsets);
     p.off_carry = off; off = align_up(off + sizeof(float) * bnd);
     p.off_carry0 = off;
     if (p.recompute || (other && other->recompute)) off = align_up(off + sizeof(float) * bnd);
@@ -234,6 +242,7 @@ int make_plans(Plan& p, Plan& p2, bool* has2, const pn_cell* cell, int64_t B, in
     if (rc != PN_OK) return rc;
     p.persist_ok = p2.persist_ok = false;
     p.recompute = p2.recompute = false;
+    p.fc = p2.fc = false;
     p.Lc = p.L; p2.Lc = p2.L;
     p.NCc = p.NC; p2.NCc = p2.NC;
     layout(p, &p2);
@@ -283,6 +292,7 @@ int validate(const pn_cell* cell, const float* params, const float* x, const flo
         }
         if (o->window_switch_len < 0 || (o->window_switch_len > 0 && !o->window_switch))
             return fail(PN_EINVAL, "window_switch is NULL or its length negative");
+        if (o->profile_stride < 0) return fail(PN_EINVAL, "profile_stride must be >= 0");
     }
     if (B == 0 || T == 0 || D == 0) return PN_OK;
     if (!params || !x || !s0 || !out) return fail(PN_EINVAL, "a device pointer is NULL");
@@ -311,7 +321,7 @@ int get_res(ThreadRes** out) {
     if (r.device != dev) {
         if (!r.host) {
             void* p = nullptr;
-            PN_HIP(hipHostMalloc(&p, sizeof(HostRec), hipHostMallocMapped | hipHostMallocCoherent));
+            PN_HIP(hipHostMalloc(&p, sizeof(HostRec) * kHostRing, hipHostMallocMapped | hipHostMallocCoherent));
             r.host = static_cast<HostRec*>(p);
         }
         void* dp = nullptr;
@@ -361,9 +371,12 @@ int wait_record(volatile HostRec* hr, hipStream_t st, int32_t epoch, int32_t ite
 // ---------------------------------------------------------------- the solve
 struct Timing {
     bool on = false;
+    int stride = 1;          // time every stride-th steady apply launch
+    int64_t seen = 0;
     std::vector<std::pair<size_t, size_t>> apply;   // event index pairs
     std::vector<double> apply_bytes, apply_flops;
     size_t next = 0;
+    bool take() { return on && (seen++ % stride) == 0; }
 };
 
 struct SolveCtx {
@@ -467,6 +480,11 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
             ca.aggA = aggA; ca.aggB = aggB; ca.carry = carry; ca.halo = halo; ca.rpart = rpart;
             ca.ctrl = ctrl; ca.mode = p.mode; ca.lam = lam; ca.undamped = lam == 1.0f;
             ca.band = p.band;
+            ca.fc = p.fc;
+            if (p.fc) {
+                ca.max_iter = c.max_iter; ca.tol = c.tol; ca.host = c.res->host_dev;
+                ca.mstride = static_cast<int64_t>(p.B) * p.NC * p.D;
+            }
             nblocks = cell_pass_nblocks(ca);
         }
         cy.NC = NC;
@@ -484,11 +502,14 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
 
     configure(*pp);
     *sw = -1;
+    // fc sweeps reduce r_0 into ctrl->rmax[0] and expect rmax[1] clear
+    if (pp->fc) PN_HIP(hipMemsetAsync(ctrl, 0, sizeof(Ctrl), c.st));
     PN_HIP(launch_pass(kPrologue, 0));
-    volatile HostRec* hr = c.res->host;
+    volatile HostRec* ring = c.res->host;      // check i goes to ring[i % kHostRing]
     const int32_t epoch = ++c.res->epoch;
     cy.chk.epoch = epoch;
-    hr->iter = -1;
+    ca.epoch = epoch;
+    for (int k = 0; k < kHostRing; ++k) ring[k].iter = -1;
     float r_prev = 0.0f;
     // Chunking of the channel-wise launches with the recomputing pair: the
     // prologue and updates 1 and 2 run on chunks of L, the later updates on
@@ -502,9 +523,40 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
         da.rf = rf;
         da.NCr = rf > 1 ? NCf : da.NC;
     };
-    for (int i = 0;; ++i) {
-        cy.chk.iter = i;
+    // Apply launch k (update k).  Sweeps that take their own check (fc) are
+    // kept `ahead` launches in front of the check the host is reading: a
+    // sweep after the stop finds the control word set and exits at once.
+    const int ahead = pp->fc ? 2 : 0;
+    std::vector<int> tslot;      // launch k -> its timing entry, or -1
+    auto enqueue_apply = [&](int k) -> int {
+        const int phase = k == 0 ? (recompute ? kFirstNS : kFirst)
+                                 : (recompute && k == 1 ? kSecondR : kSteady);
+        if (recompute) grain(k >= 2, k == 2 ? pp->Lc / pp->L : 1);
+        // timing covers the steady-state apply launches, including the
+        // final ones that exit at once
+        const bool timed = phase == kSteady && c.tm->take();
         size_t e0 = 0, e1 = 0;
+        if (timed) { int rc = record(c, &e0); if (rc) return rc; }
+        PN_HIP(launch_pass(phase, k));
+        tslot.push_back(-1);
+        if (timed) {
+            int rc = record(c, &e1);
+            if (rc) return rc;
+            c.tm->apply.push_back({e0, e1});
+            c.tm->apply_bytes.push_back(0.0);   // filled in once the check says it ran
+            c.tm->apply_flops.push_back(0.0);
+            tslot.back() = static_cast<int>(c.tm->apply.size()) - 1;
+        }
+        return PN_OK;
+    };
+    for (int k = 0; k < ahead; ++k) {
+        int rc = enqueue_apply(k);
+        if (rc != PN_OK) return rc;
+    }
+    for (int i = 0;; ++i) {
+        volatile HostRec* hr = ring + i % kHostRing;
+        cy.chk.iter = i;
+        cy.chk.host = c.res->host_dev + i % kHostRing;
         cy.carry = (recompute && i == 0) ? carry0 : carry;
         da.carry = cy.carry;
         if (recompute) {
@@ -513,21 +565,11 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
             cy.NC = da.NC;
             cy.chk.nparts = diag_tanh_nblocks(da);
         }
-        PN_HIP(pp->dense ? launch_dense_carry(cy, c.st) : launch_diag_carry(cy, c.st));
-        const int phase = i == 0 ? (recompute ? kFirstNS : kFirst)
-                                 : (recompute && i == 1 ? kSecondR : kSteady);
-        if (recompute) grain(i >= 2, i == 2 ? pp->Lc / pp->L : 1);
-        // timing covers the steady-state apply launches, including the final
-        // one that exits at once
-        const bool timed = c.tm->on && phase == kSteady;
-        if (timed) { int rc = record(c, &e0); if (rc) return rc; }
-        PN_HIP(launch_pass(phase, i));
-        if (timed) {
-            int rc = record(c, &e1);
-            if (rc) return rc;
-            c.tm->apply.push_back({e0, e1});
-            c.tm->apply_bytes.push_back(0.0);   // filled below once we know if it ran
-            c.tm->apply_flops.push_back(0.0);
+        if (!pp->fc) {
+            // the check of iteration i and the carries of its maps, then update i
+            PN_HIP(pp->dense ? launch_dense_carry(cy, c.st) : launch_diag_carry(cy, c.st));
+            int rc = enqueue_apply(i);
+            if (rc != PN_OK) return rc;
         }
         {
             int rc = wait_record(hr, c.st, epoch, i);
@@ -541,9 +583,10 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
         float r;
         std::memcpy(&r, &rb, sizeof(r));
         if (c.hist) c.hist->push_back(r);
-        if (timed && !stop) {
-            c.tm->apply_bytes.back() = apply_bytes(*pp, Tw, false);
-            c.tm->apply_flops.back() = apply_flops(*pp, Tw);
+        if (!stop && tslot[i] >= 0) {
+            // update i ran
+            c.tm->apply_bytes[tslot[i]] = apply_bytes(*pp, Tw, false);
+            c.tm->apply_flops[tslot[i]] = apply_flops(*pp, Tw);
         }
         if (stop) {
             *K = i;
@@ -575,6 +618,10 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
             }
         }
         r_prev = r;
+        if (pp->fc) {
+            int rc = enqueue_apply(i + ahead);
+            if (rc != PN_OK) return rc;
+        }
     }
     if (*K == 0) {
         if (c.p->half) PN_HIP(launch_fill_half(s, ss, s0, s0s, c.p->B, Tw, c.p->D, c.st));
@@ -693,9 +740,10 @@ int solve_advancing(SolveCtx& c, const float* x, const float* s0, float* out, in
         }
         PN_HIP(p.dense ? launch_dense_carry(cy, c.st) : launch_diag_carry(cy, c.st));
         size_t e0 = 0, e1 = 0;
-        if (c.tm->on) { int rc = record(c, &e0); if (rc) return rc; }
+        const bool timed = c.tm->take();
+        if (timed) { int rc = record(c, &e0); if (rc) return rc; }
         PN_HIP(launch_pass(kSteady, i));
-        if (c.tm->on) {
+        if (timed) {
             int rc = record(c, &e1);
             if (rc) return rc;
             c.tm->apply.push_back({e0, e1});
@@ -840,6 +888,7 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     }
     Timing tm;
     tm.on = o && o->profile;
+    tm.stride = (o && o->profile_stride > 1) ? o->profile_stride : 1;
     std::vector<float> hist;
     SolveCtx c{&p, st, ws, res, params, tol, o ? o->damping : 1.0f, max_iter, &tm, &hist,
                o ? o->switch_ratio : 0.0f, o ? o->switch_damping : 0.0f};
@@ -934,6 +983,7 @@ void pn_opts_init(pn_opts* o) {
     o->switch_mode = -1;
     o->switch_ratio = 0.5f;
     o->switch_damping = 0.0f;
+    o->profile_stride = 1;
 }
 
 int pn_eval_ex(const pn_cell* cell, const float* params, const float* x, const float* s0, int64_t B,

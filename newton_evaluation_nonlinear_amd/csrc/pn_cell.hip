@@ -150,6 +150,68 @@ __device__ __forceinline__ void rows_gemm(const float* A, int lda, int nrows, in
     }
 }
 
+// The same product for K a multiple of 16, with the wavefronts on fixed
+// column tiles: WC wavefront columns share the CT = NO / 16 column tiles
+// (tile ct belongs to column ct % WC) and 4 / WC wavefront rows take the row
+// tiles in turn.  Each lane loads its A values one float4 per 16 k and uses
+// every load for all of its wavefront's column tiles.  The sum runs over k in
+// a permuted order: in k block g, MFMA step s takes k = 16 g + 4 (l / 16) + s
+// in lane l, for A and B alike.  With A's row stride lda = 4 (mod 8) floats
+// (or 4 (mod 32) for 16-float rows) the 16 rows of one float4 load fall on
+// distinct LDS banks.  A must be 16-byte aligned, lda a multiple of 4, and
+// columns K of every row readable.
+template <int NO, typename BFun>
+__device__ __forceinline__ void rows_gemm16(const float* A, int lda, int nrows, int K, BFun bval,
+                                            float* C, int ldc) {
+    constexpr int CT = NO / 16;
+    constexpr int NWAVE = kThreads / 64;
+    constexpr int WC = CT % 4 == 0 ? 4 : (CT % 2 == 0 ? 2 : 1);
+    constexpr int WR = NWAVE / WC;
+    constexpr int NT = CT / WC;                       // column tiles per wavefront
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int c16 = lane & 15, kq = lane >> 4;
+    const int wc = wave % WC, wr = wave / WC;
+    const int RT = (nrows + 15) >> 4;
+    for (int rt = wr; rt < RT; rt += WR) {
+        const int row = rt * 16 + c16;
+        const bool rin = row < nrows;
+        const float* Ar = A + (rin ? row : 0) * lda + 4 * kq;
+        v4f acc[NT];
+#pragma unroll
+        for (int q = 0; q < NT; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+        for (int g = 0; g < K; g += 16) {
+            const float4 a4 = rin ? *reinterpret_cast<const float4*>(Ar + g) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int k = g + 4 * kq + s;
+#pragma unroll
+                for (int q = 0; q < NT; ++q) {
+                    const int col = (wc + q * WC) * 16 + c16;
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bval(k, col), acc[q], 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+            const int col = (wc + q * WC) * 16 + c16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int orow = rt * 16 + kq * 4 + r;
+                if (orow < nrows) C[orow * ldc + col] = acc[q][r];
+            }
+        }
+    }
+}
+
+// LDS row strides of the cell tile: the iterate rows (P, N) and the staged x
+// rows carry 4 floats of padding (see rows_gemm16); x rows are zero-filled
+// to a multiple of 16 columns.
+template <int DP>
+__host__ __device__ constexpr int iterate_stride() { return DP + 4; }
+__host__ __device__ inline int x_stride(int m) { return ((m + 15) & ~15) + 4; }
+
 // Columns of the gate pre-activation tables: NG gates of DP rows, padded to 16.
 template <int CELL, int DP>
 struct Gates {
@@ -158,19 +220,20 @@ struct Gates {
 };
 
 // Input projection XI[j][g*DP + i] = sum_q W_ig[i][q] x_j[q] (no bias), for the
-// staged x rows X (row stride mp = m rounded up to 4, zero-padded).
+// staged x rows X (row stride x_stride(m), zero beyond column m).
 template <int CELL, int DP>
-__device__ __forceinline__ void input_projection(const float* __restrict__ w, const float* X, int mp,
+__device__ __forceinline__ void input_projection(const float* __restrict__ w, const float* X, int xs,
                                                  int Lc, int m, float* XI) {
     constexpr int NG = CellTraits<CELL>::NG, NO = Gates<CELL, DP>::NO;
     const float* UT = w + NG * DP * DP;
-    rows_gemm<0>(X, mp, Lc, mp, NO, [&](int q, int o) {
+    rows_gemm16<NO>(X, xs, Lc, (m + 15) & ~15, [&](int q, int o) {
         const int gte = o / DP, i = o - gte * DP;
         return (gte < NG && q < m) ? UT[(gte * m + q) * DP + i] : 0.0f;
     }, XI, NO);
 }
 
-// For rows j < Lc of a chunk with p_t = Pin[j] (the state one step earlier):
+// For rows j < Lc of a chunk with p_t = Pin[j] (the state one step earlier;
+// row stride iterate_stride<DP>()):
 // V[j] = f_t(p_t) and the Jacobian coefficients CO.  The recurrent products
 // W_g p_t go through the matrix cores into H (LDS); the gate nonlinearities
 // are per element.  If Sres is given, also folds |Sres[j+1] - V[j]| (the
@@ -184,10 +247,13 @@ __device__ __forceinline__ void eval_rows(const float* __restrict__ w, const flo
                                           uint32_t& rb, uint32_t* fb = nullptr, float tol = 0.0f) {
     constexpr int NG = CellTraits<CELL>::NG, NO = Gates<CELL, DP>::NO;
     constexpr int NRG = kThreads / DP;
-    rows_gemm<DP>(Pin, DP, Lc, DP, NO, [&](int k, int o) {
+    constexpr int PS = iterate_stride<DP>();
+    auto wval = [&](int k, int o) {
         const int gte = o / DP, i = o - gte * DP;
         return gte < NG ? w[(gte * DP + k) * DP + i] : 0.0f;
-    }, H, NO);
+    };
+    if constexpr (DP % 16 == 0) rows_gemm16<NO>(Pin, PS, Lc, DP, wval, H, NO);
+    else rows_gemm<DP>(Pin, PS, Lc, DP, NO, wval, H, NO);
     __syncthreads();
     const int i = threadIdx.x % DP;
     const bool live = i < D;
@@ -220,7 +286,7 @@ __device__ __forceinline__ void eval_rows(const float* __restrict__ w, const flo
             const float* wdiag = bi + DP;
             const float hi = bi[2 * DP + i];
             const float gv = tanh_f(hj[i] + xj[i] + bi[i]);
-            const float pi = Pin[o];
+            const float pi = Pin[j * PS + i];
             v = pi + hi * (gv - pi);
             const float c1 = hi * (1.0f - gv * gv);
             if constexpr (DENSE) {
@@ -236,7 +302,7 @@ __device__ __forceinline__ void eval_rows(const float* __restrict__ w, const flo
             const float z = sigmoid_f(xj[DP + i] + bi[DP + i] + hj[DP + i] + bhh[DP + i]);
             const float gg = hj[2 * DP + i] + bhh[2 * DP + i];
             const float n = tanh_f(xj[2 * DP + i] + bi[2 * DP + i] + rr * gg);
-            const float pi = Pin[o];
+            const float pi = Pin[j * PS + i];
             v = (1.0f - z) * n + z * pi;
             const float dn = (1.0f - z) * (1.0f - n * n);
             const float cz = (pi - n) * z * (1.0f - z);
@@ -254,7 +320,7 @@ __device__ __forceinline__ void eval_rows(const float* __restrict__ w, const flo
         }
         V[o] = v;
         if (Sres) {
-            const float d = Sres[o + DP] - v;
+            const float d = Sres[(j + 1) * PS + i] - v;
             rb = max(rb, abs_bits(d));
             if (fb && !(fabsf(d) <= tol)) *fb = min(*fb, static_cast<uint32_t>(j));
         }
@@ -285,12 +351,205 @@ __device__ __forceinline__ float jac_row_apply(const float* __restrict__ w, cons
     }
 }
 
+// ---------------------------------------------------------------- register-resident evaluation
+// For DP a multiple of 16 the cell is evaluated from the matrix-core
+// accumulators.  Wavefront (wc, wr) of the workgroup, wc = wave % WC with
+// WC = DP / 16, owns the state indices i = 16 wc + l % 16 (lane l) of every
+// gate; wr = wave / WC takes the row tiles rt = wr, wr + WR, ... of the chunk.
+// Accumulator g of a lane then holds gate g's pre-activation at rows
+// 16 rt + 4 (l / 16) + r, r < 4, and index i, so the gate nonlinearities run
+// on registers, and the input projection (with the biases folded in) stays in
+// registers for both evaluations of a sweep.  The recurrent weights are the
+// B operand, held in registers; the sums over k run in the permuted order of
+// rows_gemm16.  Chunks are at most kMaxChunk steps.
+constexpr int kMaxChunk = 64;
+
+template <int CELL, int DP>
+struct CellRegs {
+    static constexpr int NG = CellTraits<CELL>::NG;
+    static constexpr int WC = DP / 16;
+    static constexpr int WR = (kThreads / 64) / WC;
+    static constexpr int MAXRT = (kMaxChunk / 16 + WR - 1) / WR;   // row tiles per wavefront
+    static constexpr int KB = DP / 4;                              // B values per gate and lane
+    static constexpr int PS = iterate_stride<DP>();
+    int i, wr, kq;
+    bool live;
+    float wb[NG][KB];
+    v4f xi[MAXRT][NG];
+    float c0, c1, c2, c3, c4, c5, c6, c7, c8;     // per-index constants (biases, diagonals)
+
+    // Weights w: the prepared layout (LDS or global).
+    __device__ __forceinline__ void load(const float* __restrict__ w, int D, int m) {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        i = (wave % WC) * 16 + (lane & 15);
+        wr = wave / WC;
+        kq = lane >> 4;
+        live = i < D;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+                const int k = (kk >> 2) * 16 + 4 * kq + (kk & 3);
+                wb[g][kk] = w[(g * DP + k) * DP + i];
+            }
+        }
+        const float* bi = w + NG * DP * DP + NG * m * DP;
+        if constexpr (CELL == kCellGru) {
+            c0 = bi[i] + bi[3 * DP + i];                 // b_ir + b_hr
+            c1 = bi[DP + i] + bi[4 * DP + i];            // b_iz + b_hz
+            c2 = bi[2 * DP + i];                         // b_in
+            c3 = bi[5 * DP + i];                         // b_hn
+            c4 = bi[6 * DP + i];                         // diag W_hr
+            c5 = bi[7 * DP + i];                         // diag W_hz
+            c6 = bi[8 * DP + i];                         // diag W_hn
+        } else {
+            c0 = bi[i];                                  // b
+            c4 = bi[DP + i];                             // diag W
+            if constexpr (CELL == kCellEuler) c5 = bi[2 * DP + i];   // h
+        }
+    }
+
+    // Input projection of the staged x rows X (row stride xs, zero beyond
+    // column m) plus the biases that add to it.
+    __device__ __forceinline__ void project(const float* __restrict__ w, const float* X, int xs, int Lc, int m) {
+        const float* UT = w + NG * DP * DP;
+        const int RT = (Lc + 15) >> 4;
+        const int K = (m + 15) & ~15;
+#pragma unroll
+        for (int u = 0; u < MAXRT; ++u) {
+            const int rt = wr + WR * u;
+            if (rt >= RT) break;
+            const int row = rt * 16 + (threadIdx.x & 15);
+            const bool rin = row < Lc;
+            const float* Ar = X + (rin ? row : 0) * xs + 4 * kq;
+            v4f acc[NG];
+#pragma unroll
+            for (int g = 0; g < NG; ++g) acc[g] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+            for (int q0 = 0; q0 < K; q0 += 16) {
+                const float4 a4 = rin ? *reinterpret_cast<const float4*>(Ar + q0) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int q = q0 + 4 * kq + s;
+#pragma unroll
+                    for (int g = 0; g < NG; ++g) {
+                        const float b = q < m ? UT[(g * m + q) * DP + i] : 0.0f;
+                        acc[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], b, acc[g], 0, 0, 0);
+                    }
+                }
+            }
+            if constexpr (CELL == kCellGru) {
+                xi[u][0] = acc[0] + c0;
+                xi[u][1] = acc[1] + c1;
+                xi[u][2] = acc[2] + c2;
+            } else {
+                xi[u][0] = acc[0] + c0;
+            }
+        }
+    }
+
+    // V[j] = f_t(p_t), p_t = Pin[j] (row stride PS), and the Jacobian
+    // coefficients CO for rows j < Lc; with Sres, the residual of the
+    // trajectory held there (as eval_rows).
+    template <bool DENSE>
+    __device__ __forceinline__ void eval(const float* Pin, float* V, float* CO, int Lc, int L, int mode,
+                                         const float* Sres, uint32_t& rb, uint32_t* fb, float tol) const {
+        const int RT = (Lc + 15) >> 4;
+#pragma unroll
+        for (int u = 0; u < MAXRT; ++u) {
+            const int rt = wr + WR * u;
+            if (rt >= RT) break;
+            const int row = rt * 16 + (threadIdx.x & 15);
+            const bool rin = row < Lc;
+            const float* Ar = Pin + (rin ? row : 0) * PS + 4 * kq;
+            v4f acc[NG];
+#pragma unroll
+            for (int g = 0; g < NG; ++g) acc[g] = xi[u][g];
+            if constexpr (CELL == kCellGru) acc[2] = v4f{c3, c3, c3, c3};   // W_hn p + b_hn alone
+#pragma unroll
+            for (int kb = 0; kb < DP / 16; ++kb) {
+                const float4 a4 = rin ? *reinterpret_cast<const float4*>(Ar + 16 * kb) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+#pragma unroll
+                    for (int g = 0; g < NG; ++g)
+                        acc[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], wb[g][kb * 4 + s], acc[g], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = rt * 16 + 4 * kq + r;
+                if (j >= Lc) continue;
+                const int o = j * DP + i;
+                if (!live) {
+                    V[o] = 0.0f;
+                    if constexpr (DENSE) {
+#pragma unroll
+                        for (int q = 0; q < CellTraits<CELL>::NCO; ++q) CO[q * L * DP + o] = 0.0f;
+                    } else {
+                        CO[o] = 0.0f;
+                    }
+                    continue;
+                }
+                float v;
+                if constexpr (CELL == kCellTanhRnn) {
+                    v = tanh_f(acc[0][r]);
+                    const float d1 = 1.0f - v * v;
+                    if constexpr (DENSE) CO[o] = d1;
+                    else CO[o] = mode == kJacobi ? 0.0f : (mode == kPicard ? 1.0f : d1 * c4);
+                } else if constexpr (CELL == kCellEuler) {
+                    const float gv = tanh_f(acc[0][r]);
+                    const float pi = Pin[j * PS + i];
+                    v = pi + c5 * (gv - pi);
+                    const float d1 = c5 * (1.0f - gv * gv);
+                    if constexpr (DENSE) {
+                        CO[o] = 1.0f - c5;
+                        CO[L * DP + o] = d1;
+                    } else {
+                        CO[o] = mode == kJacobi ? 0.0f : (mode == kPicard ? 1.0f : (1.0f - c5) + d1 * c4);
+                    }
+                } else {
+                    const float rr = sigmoid_f(acc[0][r]);
+                    const float z = sigmoid_f(acc[1][r]);
+                    const float gg = acc[2][r];
+                    const float n = tanh_f(xi[u][2][r] + rr * gg);
+                    const float pi = Pin[j * PS + i];
+                    v = (1.0f - z) * n + z * pi;
+                    const float dn = (1.0f - z) * (1.0f - n * n);
+                    const float cz = (pi - n) * z * (1.0f - z);
+                    const float cn = dn * rr;
+                    const float cr = dn * gg * rr * (1.0f - rr);
+                    if constexpr (DENSE) {
+                        CO[o] = z;
+                        CO[L * DP + o] = cz;
+                        CO[2 * L * DP + o] = cn;
+                        CO[3 * L * DP + o] = cr;
+                    } else {
+                        const float jd = z + cz * c5 + cn * c6 + cr * c4;
+                        CO[o] = mode == kJacobi ? 0.0f : (mode == kPicard ? 1.0f : jd);
+                    }
+                }
+                V[o] = v;
+                if (Sres) {
+                    const float d = Sres[(j + 1) * PS + i] - v;
+                    rb = max(rb, abs_bits(d));
+                    if (fb && !(fabsf(d) <= tol)) *fb = min(*fb, static_cast<uint32_t>(j));
+                }
+            }
+        }
+    }
+};
+
 // ---------------------------------------------------------------- the fused pass
 // One tile (batch row b, chunk c) of one sweep.  `arr` is the LDS array
 // region, `w` the prepared weights (LDS or global).  Returns the tile's
 // residual bit-max through rb (the caller reduces it over the workgroup).
+// Returns false when the sweep's own check (CellArgs::fc) stops the loop:
+// the tile then writes nothing.
 template <int CELL, int DP, bool DENSE, int PHASE>
-__device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float* arr,
+__device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float* arr,
                                           const float* w, uint32_t& rb, uint32_t* fb = nullptr) {
     constexpr int NG = CellTraits<CELL>::NG;
     constexpr int NCO = DENSE ? CellTraits<CELL>::NCO : 1;
@@ -299,96 +558,186 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
     const int Lc = min(L, g.Tw - t0);
     const int tid = threadIdx.x;
     constexpr int NO = Gates<CELL, DP>::NO;
-    const int mp = (m + 3) & ~3;
-    float* P = arr;
-    float* N = P + (L + 1) * DP;
-    float* XI = N + (L + 1) * DP;            // [L][NO] input projections
-    float* H = XI + L * NO;                  // [L][NO] recurrent pre-activations
-    float* V = H + L * NO;
+    constexpr int PS = iterate_stride<DP>();
+    constexpr bool kRegs = DP % 16 == 0;     // register-resident evaluation (CellRegs)
+    const int xs = x_stride(m);
+    const int nxh = kRegs ? 0 : L * NO;
+    float* P = arr;                          // [L+1][PS] rows t0-1 .. t1-1 of s^(i)
+    float* N = P + (L + 1) * PS;             // [L+1][PS] the same rows of s^(i+1)
+    float* XI = N + (L + 1) * PS;            // [L][NO] input projections (not with kRegs)
+    float* H = XI + nxh;                     // [L][NO] recurrent pre-activations (not with kRegs)
+    float* V = H + nxh;
     float* CO = V + L * DP;
-    float* X = CO + NCO * L * DP;            // [L][mp]
-    float* DL = X + L * mp;
+    float* X = CO + NCO * L * DP;            // [L][xs]
+    float* DL = X + L * xs;
+    float* SCR = DL + DP;                    // [2][kThreads] carry segments (fc, diagonal modes)
     const size_t ci = static_cast<size_t>(b) * g.NC + c;        // chunk index
     const float* s0 = g.s0 + b * g.s0s;
+    CellRegs<CELL, kRegs ? DP : 16> cr16;    // used when kRegs
+    auto evaluate = [&](const float* Pin, const float* Sres, uint32_t* fbp) {
+        if constexpr (kRegs) cr16.template eval<DENSE>(Pin, V, CO, Lc, L, g.mode, Sres, rb, fbp, g.tol);
+        else eval_rows<CELL, DP, DENSE>(w, Pin, XI, H, V, CO, Lc, L, D, m, g.mode, Sres, rb, fbp, g.tol);
+    };
 
-    // ---- stage inputs: X rows, then the input projection (iterate-free)
+    // ---- stage inputs: X rows and the rows of the iterate the sweep starts
+    // from, with one wait; the carries of this chunk and the next (apply
+    // sweeps) are fetched first, for the replay
+    constexpr bool kApply = PHASE != kPrologue && PHASE != kMaps;
     const float* xg = g.x + b * g.xs + static_cast<int64_t>(t0) * m;
-    copy_rows_to_lds<kThreads>(X, mp, xg, m, Lc, m);
-    __syncthreads();
-    input_projection<CELL, DP>(w, X, mp, Lc, m, XI);
     const size_t HS = static_cast<size_t>(g.B) * g.NC * D;
-
+    const bool has_next = c + 1 < g.NC;
+    float c_first = 0.0f, c_next = 0.0f;
+    // fc: r_i as the sweep before reduced it (every wavefront reads the slots)
+    uint32_t r_i = 0;
+    const float* mA = g.aggA + (g.iter & 1) * g.mstride + static_cast<size_t>(b) * g.NC * D;
+    const float* mB = g.aggB + (g.iter & 1) * g.mstride + static_cast<size_t>(b) * g.NC * D;
+    float own_a = 0.0f, own_b = 0.0f;
+    if constexpr (kApply && !DENSE) {
+        if (g.fc) {
+            const int lane = tid & 63;
+            r_i = wave_max_u32(lane < kRSlots ? g.ctrl->rmax[g.iter % 3][lane][0] : 0u);
+            // The carry of chunk c, composed here from the chunk maps of
+            // iteration i: kThreads / DP segments of the chunks before c are
+            // each folded into one affine map (here), then applied to s0 in
+            // order (after the staging wait); the next chunk's carry is this
+            // chunk's map applied to it.
+            constexpr int NS = kThreads / DP;
+            const int d = tid % DP, sg_ = tid / DP;
+            const int per = (c + NS - 1) / NS;
+            const int k0 = min(c, sg_ * per), k1 = min(c, k0 + per);
+            float fa = 1.0f, fbv = 0.0f;
+            if (d < D) {
+#pragma unroll 8
+                for (int k = k0; k < k1; ++k) {
+                    const float a = mA[k * D + d];
+                    fbv = a * fbv + mB[k * D + d];
+                    fa = a * fa;
+                }
+            }
+            SCR[tid] = fa;
+            SCR[kThreads + tid] = fbv;
+            if (tid < D && has_next) {
+                own_a = mA[c * D + tid];
+                own_b = mB[c * D + tid];
+            }
+        } else if (tid < D) {
+            c_first = g.carry[ci * D + tid];
+            if (has_next) c_next = g.carry[(ci + 1) * D + tid];
+        }
+    } else if (kApply && tid < D) {
+        c_first = g.carry[ci * D + tid];
+        if (has_next) c_next = g.carry[(ci + 1) * D + tid];
+    }
+    if constexpr (kRegs) cr16.load(w, D, m);
+    copy_rows_to_lds<kThreads>(X, xs, xg, m, Lc, m);
+    float* sg = g.s + b * g.ss + static_cast<int64_t>(t0) * D;
     if constexpr (PHASE == kPrologue) {
         // s^(0) = s0 everywhere: N holds rows t0-1 .. t1-1 of s^(0).
-        for (int e = tid; e < (Lc + 1) * DP; e += kThreads) {
-            const int i = e % DP;
+        for (int e = tid; e < (Lc + 1) * PS; e += kThreads) {
+            const int i = e % PS;
             N[e] = i < D ? s0[i] : 0.0f;
         }
-        __syncthreads();
     } else if constexpr (PHASE == kMaps) {
         // N: rows t0-1 .. t1-1 of the iterate in s (this pass writes no row
         // of s, so the row before the chunk is read directly); its last row
         // is the halo the next apply reads
-        const float* sg = g.s + b * g.ss + static_cast<int64_t>(t0) * D;
-        if (tid < DP) N[tid] = tid < D ? (c == 0 ? s0[tid] : sg[tid - D]) : 0.0f;
-        copy_rows_to_lds<kThreads>(N + DP, DP, sg, D, Lc, D);
-        __syncthreads();
-        if (tid < D) g.halo[(g.iter & 1) * HS + ci * D + tid] = N[Lc * DP + tid];
-    } else {
+        if (tid < PS) N[tid] = tid < D ? (c == 0 ? s0[tid] : sg[tid - D]) : 0.0f;
+        copy_rows_to_lds<kThreads>(N + PS, PS, sg, D, Lc, D);
+    } else if constexpr (PHASE == kFirst) {
         // ---- P: rows t0-1 .. t1-1 of s^(i)
-        float* sg = g.s + b * g.ss + static_cast<int64_t>(t0) * D;
-        if constexpr (PHASE == kFirst) {
-            for (int e = tid; e < (Lc + 1) * DP; e += kThreads) {
-                const int i = e % DP;
-                P[e] = i < D ? s0[i] : 0.0f;
-            }
-        } else {
-            if (tid < DP) {
-                P[tid] = tid < D ? ((c == 0) ? s0[tid] : g.halo[(g.iter & 1) * HS + (ci - 1) * D + tid]) : 0.0f;
-            }
-            copy_rows_to_lds<kThreads>(P + DP, DP, sg, D, Lc, D);
+        for (int e = tid; e < (Lc + 1) * PS; e += kThreads) {
+            const int i = e % PS;
+            P[e] = i < D ? s0[i] : 0.0f;
         }
-        __syncthreads();
+    } else {
+        if (tid < PS) {
+            P[tid] = tid < D ? ((c == 0) ? s0[tid] : g.halo[(g.iter & 1) * HS + (ci - 1) * D + tid]) : 0.0f;
+        }
+        copy_rows_to_lds<kThreads>(P + PS, PS, sg, D, Lc, D);
+    }
+    __syncthreads();
+    if constexpr (PHASE == kMaps) {
+        if (tid < D) g.halo[(g.iter & 1) * HS + ci * D + tid] = N[Lc * PS + tid];
+    }
+    if constexpr (kApply && !DENSE) {
+        if (g.fc) {
+            // the check of iteration i, taken alike by every workgroup; block
+            // 0 publishes it and clears the slot set of the sweep after next
+            CheckArgs chk{};
+            chk.iter = g.iter;
+            chk.max_iter = g.max_iter;
+            chk.tol = g.tol;
+            chk.ctrl = g.ctrl;
+            chk.host = g.host + g.iter % kHostRing;
+            chk.epoch = g.epoch;
+            const int st = check_status(r_i, chk);
+            if (c == 0 && b == 0) {
+                if (tid < kRSlots)
+                    __hip_atomic_store(&g.ctrl->rmax[(g.iter + 2) % 3][tid][0], 0u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                if (tid == 0) publish_check(chk, r_i, st, 0xffffffffu);
+            }
+            if (st >= 0) return false;
+            if (tid < D) {
+                constexpr int NS = kThreads / DP;
+                float x = s0[tid];
+#pragma unroll
+                for (int q = 0; q < NS; ++q) x = SCR[q * DP + tid] * x + SCR[kThreads + q * DP + tid];
+                c_first = x;
+                if (has_next) c_next = own_a * x + own_b;
+            }
+        }
+    }
+    // ---- the input projection (iterate-free)
+    if constexpr (kRegs) cr16.project(w, X, xs, Lc, m);
+    else input_projection<CELL, DP>(w, X, xs, Lc, m, XI);
+
+    if constexpr (kApply) {
         // ---- maps of iteration i at p_t = P[j]
-        eval_rows<CELL, DP, DENSE>(w, P, XI, H, V, CO, Lc, L, D, m, g.mode, nullptr, rb);
+        evaluate(P, nullptr, nullptr);
         __syncthreads();
         // ---- replay from the carry, damping, N = rows t0-1 .. t1-1 of s^(i+1)
-        const bool has_next = c + 1 < g.NC;
-        const float* cr = g.carry + ci * D;
         const float lam = g.lam;
         const bool und = g.undamped != 0;
         if constexpr (!DENSE) {
             if (tid < D) {
-                float shat = cr[tid];
+                float shat = c_first;
                 N[tid] = und ? shat : P[tid] + lam * (shat - P[tid]);
-                for (int j = 0; j < Lc; ++j) {
+                // the last row of a chunk that has a successor is that
+                // chunk's carry
+                const int nrep = has_next ? Lc - 1 : Lc;
+#pragma unroll 4
+                for (int j = 0; j < nrep; ++j) {
                     const int o = j * DP + tid;
-                    shat = V[o] + CO[o] * (shat - P[o]);
-                    if (j == Lc - 1 && has_next) shat = cr[D + tid];
-                    const float so = P[o + DP];
-                    N[o + DP] = und ? shat : so + lam * (shat - so);
+                    shat = V[o] + CO[o] * (shat - P[j * PS + tid]);
+                    const float so = P[(j + 1) * PS + tid];
+                    N[(j + 1) * PS + tid] = und ? shat : so + lam * (shat - so);
                 }
-            } else if (tid < DP) {
-                for (int j = 0; j <= Lc; ++j) N[j * DP + tid] = 0.0f;
+                if (has_next) {
+                    const float so = P[Lc * PS + tid];
+                    N[Lc * PS + tid] = und ? c_next : so + lam * (c_next - so);
+                }
+            } else if (tid < PS) {
+                for (int j = 0; j <= Lc; ++j) N[j * PS + tid] = 0.0f;
             }
         } else {
             float shat = 0.0f;
             if (tid < D) {
-                shat = cr[tid];
+                shat = c_first;
                 N[tid] = und ? shat : P[tid] + lam * (shat - P[tid]);
-            } else if (tid < DP) {
-                for (int j = 0; j <= Lc; ++j) N[j * DP + tid] = 0.0f;
-                DL[tid] = 0.0f;
+            } else if (tid < PS) {
+                for (int j = 0; j <= Lc; ++j) N[j * PS + tid] = 0.0f;
+                if (tid < DP) DL[tid] = 0.0f;
             }
             for (int j = 0; j < Lc; ++j) {
                 const int o = j * DP + tid;
-                if (tid < D) DL[tid] = shat - P[o];
+                if (tid < D) DL[tid] = shat - P[j * PS + tid];
                 __syncthreads();
                 if (tid < D) {
                     shat = V[o] + jac_row_apply<CELL, DP>(w, CO, o, L, tid, D, g.band, DL);
-                    if (j == Lc - 1 && has_next) shat = cr[D + tid];
-                    const float so = P[o + DP];
-                    N[o + DP] = und ? shat : so + lam * (shat - so);
+                    if (j == Lc - 1 && has_next) shat = c_next;
+                    const float so = P[(j + 1) * PS + tid];
+                    N[(j + 1) * PS + tid] = und ? shat : so + lam * (shat - so);
                 }
                 __syncthreads();
             }
@@ -397,12 +746,12 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
         // ---- store s^(i+1) rows t0 .. t1-1 and the halo for the next chunk
         for (int e = tid; e < Lc * D; e += kThreads) {
             const int j = e / D, i = e % D;
-            sg[e] = N[(j + 1) * DP + i];
+            sg[e] = N[(j + 1) * PS + i];
         }
-        if (tid < D) g.halo[((g.iter + 1) & 1) * HS + ci * D + tid] = N[Lc * DP + tid];
+        if (tid < D) g.halo[((g.iter + 1) & 1) * HS + ci * D + tid] = N[Lc * PS + tid];
     }
     // ---- maps of iteration i+1 at the new iterate, and its residual
-    eval_rows<CELL, DP, DENSE>(w, N, XI, H, V, CO, Lc, L, D, m, g.mode, N, rb, fb, g.tol);
+    evaluate(N, N, fb);
     __syncthreads();
     if constexpr (!DENSE) {
         if (tid < D) {
@@ -410,12 +759,14 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
             for (int j = 0; j < Lc; ++j) {
                 const int o = j * DP + tid;
                 const float at = CO[o];
-                const float bt = V[o] - at * N[o];
+                const float bt = V[o] - at * N[j * PS + tid];
                 Bc = at * Bc + bt;
                 A = at * A;
             }
-            g.aggA[ci * D + tid] = A;
-            g.aggB[ci * D + tid] = Bc;
+            // the maps of iteration i+1 (of iteration 0 in the prologue)
+            const size_t mo = (PHASE == kPrologue ? 0 : ((g.iter + 1) & 1)) * g.mstride;
+            g.aggA[mo + ci * D + tid] = A;
+            g.aggB[mo + ci * D + tid] = Bc;
         }
     } else {
         // chunk map y -> M y + bg, built step by step: M <- A~_j M, bg <- A~_j (bg - p_j) + v_j.
@@ -469,7 +820,7 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
 #pragma unroll
                     for (int q = 0; q < NG; ++q) acc[q] = 0.0f;
                     for (int k = k0; k < k1; ++k) {
-                        const float yk = B0[k] - N[j * DP + k];
+                        const float yk = B0[k] - N[j * PS + k];
 #pragma unroll
                         for (int q = 0; q < NG; ++q) acc[q] += w[(q * DP + k) * DP + i] * yk;
                     }
@@ -477,9 +828,9 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
                     if constexpr (CELL == kCellTanhRnn) {
                         val = CO[o] * acc[0];
                     } else if constexpr (CELL == kCellEuler) {
-                        val = CO[o] * (B0[i] - N[o]) + CO[L * DP + o] * acc[0];
+                        val = CO[o] * (B0[i] - N[j * PS + i]) + CO[L * DP + o] * acc[0];
                     } else {
-                        val = CO[o] * (B0[i] - N[o]) + CO[L * DP + o] * acc[1] +
+                        val = CO[o] * (B0[i] - N[j * PS + i]) + CO[L * DP + o] * acc[1] +
                               CO[2 * L * DP + o] * acc[2] + CO[3 * L * DP + o] * acc[0];
                     }
                     B1[i] = V[o] + val;
@@ -493,6 +844,7 @@ __device__ __forceinline__ void cell_tile(const CellArgs& g, int c, int b, float
         for (int e = tid; e < D * D; e += kThreads) aA[e] = M0[(e / D) * MS + (e % D)];
         if (tid < D) g.aggB[ci * D + tid] = B0[tid];
     }
+    return true;
 }
 
 template <int CELL, int DP, bool DENSE, int PHASE, bool STAGE>
@@ -500,17 +852,26 @@ __global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
     if constexpr (PHASE != kPrologue && PHASE != kMaps) {   // apply launches enqueued ahead
         if (g.ctrl->stop) return;
     }
-    extern __shared__ float lds[];
+    extern __shared__ __attribute__((aligned(16))) float lds[];
     // the prepared weights are staged once per workgroup in LDS when they fit
     const int nw = STAGE ? static_cast<int>(prepared_weight_floats(CELL, DP, g.m)) : 0;
     copy_to_lds<kThreads>(lds, g.w, nw);
     const float* w = STAGE ? lds : g.w;
     uint32_t rb = 0, fb = 0xffffffffu;
-    cell_tile<CELL, DP, DENSE, PHASE>(g, blockIdx.x, blockIdx.y, lds + ((nw + 3) & ~3), w, rb,
-                                      g.fpart ? &fb : nullptr);
+    if (!cell_tile<CELL, DP, DENSE, PHASE>(g, blockIdx.x, blockIdx.y, lds + ((nw + 3) & ~3), w, rb,
+                                           g.fpart ? &fb : nullptr))
+        return;                               // the sweep's own check stopped the loop
     rb = block_max_u32(rb);
     const size_t blk = static_cast<size_t>(blockIdx.y) * g.NC + blockIdx.x;
-    if (threadIdx.x == 0) g.rpart[blk] = rb;
+    if (threadIdx.x == 0) {
+        if (g.fc) {
+            const int set = PHASE == kPrologue ? 0 : (g.iter + 1) % 3;
+            __hip_atomic_fetch_max(&g.ctrl->rmax[set][blk % kRSlots][0], rb, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            g.rpart[blk] = rb;
+        }
+    }
     if (g.fpart) {
         fb = ~block_max_u32(~fb);
         if (threadIdx.x == 0) g.fpart[blk] = fb == 0xffffffffu ? fb : blockIdx.x * g.L + fb;
@@ -559,6 +920,7 @@ static hipError_t launch_dp(int DP, int phase, const CellArgs& a, hipStream_t st
 
 hipError_t launch_cell_pass(int kind, int DP, bool dense, int phase, const CellArgs& a,
                             hipStream_t st) {
+    if (a.L > kMaxChunk) return hipErrorInvalidValue;     // the register tiles hold at most kMaxChunk rows
     if (kind == kCellTanhRnn) {
         return dense ? launch_dp<kCellTanhRnn, true>(DP, phase, a, st)
                      : launch_dp<kCellTanhRnn, false>(DP, phase, a, st);
@@ -575,18 +937,28 @@ static size_t cell_pass_array_floats(int kind, int DP, bool dense, int L, int m)
     const size_t NG = kind == kCellGru ? 3 : 1;
     const size_t NCO = dense ? (kind == kCellTanhRnn ? 1 : kind == kCellEuler ? 2 : 4) : 1;
     const size_t NO = (NG * DP + 15) & ~size_t(15);
-    const size_t mp = (m + 3) & ~3;
-    size_t f = 2ull * (L + 1) * DP + 2ull * L * NO + static_cast<size_t>(L) * DP + NCO * L * DP +
-               static_cast<size_t>(L) * mp + DP;
+    const size_t PS = DP + 4, xs = x_stride(m);     // iterate_stride<DP>()
+    const size_t nxh = DP % 16 == 0 ? 0 : static_cast<size_t>(L) * NO;   // XI, H (not with CellRegs)
+    size_t f = 2ull * (L + 1) * PS + 2ull * nxh + static_cast<size_t>(L) * DP + NCO * L * DP +
+               static_cast<size_t>(L) * xs + DP;
     if (dense) f += 2ull * DP * (DP + 1) + 2ull * DP;
+    else f += 2ull * kThreads;                        // carry segments (CellArgs::fc)
     return f;
 }
 
-// Weights go to LDS when the whole workgroup footprint stays within 150 KB
-// (of the 160 KB per compute unit).
-bool cell_pass_stages_weights(int kind, int DP, bool dense, int L, int m) {
+// The weights fit in LDS beside the tile arrays when the whole workgroup
+// footprint stays within 150 KB (of the 160 KB per compute unit).
+static bool weights_fit_lds(int kind, int DP, bool dense, int L, int m) {
     const size_t w = (prepared_weight_floats(kind, DP, m) + 3) & ~size_t(3);
     return (w + cell_pass_array_floats(kind, DP, dense, L, m)) * sizeof(float) <= 150 * 1024;
+}
+
+// A sweep stages the weights in LDS when they fit, except with the
+// register-resident evaluation of the diagonal modes (DP a multiple of 16),
+// which reads each weight once per tile into registers.
+bool cell_pass_stages_weights(int kind, int DP, bool dense, int L, int m) {
+    if (DP % 16 == 0 && !dense) return false;
+    return weights_fit_lds(kind, DP, dense, L, m);
 }
 
 size_t cell_pass_lds_bytes(int kind, int DP, bool dense, int L, int m) {
@@ -700,7 +1072,7 @@ __device__ __forceinline__ void carry_row(const CellArgs& g, int b, float* segA,
 // grid barrier.  The weights are staged in LDS once.
 template <int CELL, int DP>
 __global__ __launch_bounds__(kThreads) void cell_persist(PersistArgs a) {
-    extern __shared__ float lds[];
+    extern __shared__ __attribute__((aligned(16))) float lds[];
     __shared__ float segA[kThreads], segB[kThreads];
     CellArgs g = a.g;
     const int nw = static_cast<int>(prepared_weight_floats(CELL, DP, g.m));
@@ -781,7 +1153,7 @@ __global__ __launch_bounds__(kThreads) void cell_persist(PersistArgs a) {
 }
 
 bool cell_persist_eligible(int kind, int DP, int L, int m) {
-    return (kind == kCellTanhRnn || kind == kCellGru) && cell_pass_stages_weights(kind, DP, false, L, m);
+    return (kind == kCellTanhRnn || kind == kCellGru) && L <= kMaxChunk && weights_fit_lds(kind, DP, false, L, m);
 }
 
 template <int CELL, int DP>
@@ -802,8 +1174,10 @@ static hipError_t persist_max_blocks_t(size_t lds, int* nb) {
     return hipSuccess;
 }
 
+// the persistent solver always stages the weights
 static size_t persist_lds(int kind, int DP, int L, int m) {
-    return cell_pass_lds_bytes(kind, DP, false, L, m);
+    const size_t w = (prepared_weight_floats(kind, DP, m) + 3) & ~size_t(3);
+    return (w + cell_pass_array_floats(kind, DP, false, L, m)) * sizeof(float);
 }
 
 hipError_t cell_persist_max_blocks(int kind, int DP, int L, int m, int* nb) {

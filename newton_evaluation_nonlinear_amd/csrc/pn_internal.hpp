@@ -17,7 +17,16 @@ struct Ctrl {
     int32_t status;    // PN_OK / PN_NOT_CONVERGED / PN_NONFINITE, or -1 (running)
     int32_t iter;      // iteration index i of the last check
     uint32_t r_bits;   // bit pattern of r_i = max |F| (non-negative float)
+    // Sweeps that take their own check (CellArgs::fc): r_k is reduced into
+    // the kRSlots words rmax[k % 3][q][0] by device-scope atomic max, each
+    // workgroup of the sweep that produces it into slot (workgroup % kRSlots);
+    // the sweep that reads set k % 3 (plain loads: the set is not written
+    // while it is read) clears set (k + 2) % 3 for the sweep after it, with
+    // device-scope atomic stores.  Each word has a 256-byte line of its own.
+    uint32_t pad_[60];
+    uint32_t rmax[3][16][64];
 };
+constexpr int kRSlots = 16;
 
 // Host-visible copy (pinned, mapped) of the same record.  The device writes
 // the payload, then epoch, then iter; the host polls (epoch, iter).
@@ -29,6 +38,11 @@ struct HostRec {
     int32_t epoch;
     int32_t iter;
 };
+
+// Records of consecutive checks of a window go to kHostRing host records in
+// turn (check i to record i % kHostRing): a sweep that runs ahead of the
+// host's reading (CellArgs::fc) cannot overwrite a record not yet read.
+constexpr int kHostRing = 4;
 
 // Arguments of the per-check decision, evaluated on the device.
 struct CheckArgs {
@@ -93,14 +107,26 @@ struct CellArgs {
     const float* carry;      // [B][NC][D]
     float* halo;             // [2][B][NC][D]
     uint32_t* rpart;
-    const Ctrl* ctrl;
+    Ctrl* ctrl;
     int32_t mode, iter, undamped;
     float lam;
     int32_t band;            // Jacobian half-bandwidth (dense modes; Newton: D)
     uint32_t* fpart;         // advancing window: per-block first step with r_t > tol
                              // (window-relative; 0xffffffff if none), or null
     float tol;
+    // fc = 1 (diagonal modes, at most kFcMaxChunks chunks per row): no carry
+    // launch; every apply sweep takes the check of its iteration itself from
+    // ctrl->rmax, publishes it (block 0) to ctrl and host, and composes the
+    // carry of its chunk from the chunk maps.  The maps of iteration k are
+    // at aggA/aggB + (k & 1) * mstride.
+    int32_t fc;
+    int32_t max_iter;
+    int32_t epoch;
+    int64_t mstride;
+    HostRec* host;
 };
+
+constexpr int kFcMaxChunks = 128;
 
 struct CarryArgs {
     const float* aggA;

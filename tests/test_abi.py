@@ -162,7 +162,10 @@ def test_euler_cell_sizes():
 def test_options_defaults():
     o = pn.make_opts()
     assert o.damping == 1.0 and o.chunk == 0 and o.window == 0 and o.flags == 0
-    assert o.bandwidth == 1 and o.window_mode == pn.WINDOW_CONSECUTIVE
+    assert o.bandwidth == 1 and o.window_mode == pn.WINDOW_CONSECUTIVE and o.profile_stride == 1
+    o.profile_stride = -1
+    rc, _ = _eval_raw(opts=o)
+    assert rc == pn.EINVAL and "profile_stride" in pn.last_error()
 
 
 def test_empty_problems_succeed_without_work():

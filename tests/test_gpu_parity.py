@@ -485,20 +485,22 @@ def test_switching_channel_wise_cell(first, second, lam2, rho):
 @pytest.mark.parametrize("cfg, mode", [(3, Q), (2, Q), (4, N)])
 def test_switch_to_the_same_mode_and_damping_is_the_plain_solve(cfg, mode):
     # rho = 0 switches at check 1; switching to the same mode with damping 1
-    # changes nothing: bit for bit on the matrix cells; the plain solve of the
-    # channel-wise cell runs its first two updates as the recomputing pair on
-    # other chunk lengths (a solve that may switch does not), so there the
-    # trajectories agree to float32 rounding of the scan order
+    # changes nothing: bit for bit for Newton; a solve that may switch takes
+    # its carries from a carry launch, while the plain solve of a diagonal
+    # mode composes them in the apply sweeps (matrix cells) or runs its first
+    # two updates as the recomputing pair on other chunk lengths (the
+    # channel-wise cell), so there the trajectories agree to float32
+    # rounding of the scan order
     wl = _case(cfg, B=2, T=640)
     plain = run_gpu(wl, mode)
     wl.update(switch_mode=mode, switch_ratio=0.0, switch_damping=1.0)
     g = run_gpu(wl, mode)
     assert plain.iters >= 2 and g.window_switch[:len(g.window_iters)] == [1] * len(g.window_iters)
     assert g.iters == plain.iters and g.status == plain.status
-    if wl["cell"] == pn.CELL_DIAG_TANH:
-        np.testing.assert_allclose(g.out_np, plain.out_np, rtol=0, atol=4e-6)
-    else:
+    if mode == N:
         np.testing.assert_array_equal(g.out_np, plain.out_np)
+    else:
+        np.testing.assert_allclose(g.out_np, plain.out_np, rtol=0, atol=4e-6)
 
 
 def test_cfg6_lattice_switching_small():
@@ -641,6 +643,35 @@ def test_nonfinite_input_is_reported_at_the_oracle_iteration():
     ref = run_oracle(wl, Q)
     assert gpu.status == ref.status == oracle.NONFINITE
     assert gpu.iters == ref.iters == 0
+
+
+@pytest.mark.parametrize("chunk, T, window", [(0, 1500, 0), (16, 3000, 0), (16, 2100, 700), (0, 640, 100)])
+def test_fused_check_and_carry_launch_paths(chunk, T, window):
+    # diagonal modes of a matrix cell: with at most 128 chunks per window
+    # every apply sweep takes its own check and composes its carries; with
+    # more (16-step chunks over 3000 steps: 188) a carry launch does both
+    wl = _case(2, B=3, T=T)
+    wl.update(window=window, max_iter=window or T)
+    for mode in (Q, J):
+        _parity(wl, mode, chunk=chunk)
+
+
+def test_fused_check_stop_rules():
+    # the three stop outcomes as every workgroup of a sweep takes them
+    wl = _case(5, B=2, T=2048)
+    g = run_gpu(wl, Q, tol=1e6)
+    assert g.status == pn.OK and g.iters == 0 and g.window_iters[:2] == [0, 0]
+    np.testing.assert_array_equal(g.out_np, np.broadcast_to(wl["s0"][:, None, :], g.out_np.shape))
+    _parity(wl, Q, max_iter=3, tol=0.0)
+    g = run_gpu(wl, Q, max_iter=3, tol=0.0)
+    assert g.status == pn.NOT_CONVERGED and g.window_iters[:2] == [3, 3]
+    bad = dict(wl)
+    bad["x"] = wl["x"].copy()
+    bad["x"][0, 1500, 5] = np.nan
+    g = run_gpu(bad, Q)
+    ref = run_oracle(bad, Q)
+    assert g.status == ref.status == oracle.NONFINITE
+    assert g.window_iters[:2] == ref.window_iters[:2]
 
 
 def test_huge_tolerance_returns_the_initial_iterate():
