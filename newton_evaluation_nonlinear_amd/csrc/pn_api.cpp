@@ -220,7 +220,7 @@ void layout(Plan& p, const Plan* other) {
     if (p.recompute || (other && other->recompute)) off = align_up(off + sizeof(float) * bnd);
     p.off_halo = off; off = align_up(off + sizeof(float) * 2 * bnd);
     p.off_w = off;
-    if (p.matrix_cell) off = align_up(off + sizeof(float) * prepared_weight_floats(p.kind, p.DP, p.m));
+    if (p.matrix_cell) off = align_up(off + sizeof(float) * prepared_total_floats(p.kind, p.DP, p.m));
     p.off_sync = p.off_winfo = p.off_hist = off;
     if (p.persist_ok) {
         p.off_sync = off; off = align_up(off + 256);

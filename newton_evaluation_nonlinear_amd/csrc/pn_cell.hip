@@ -48,6 +48,19 @@ __host__ __device__ size_t prepared_weight_floats(int kind, int DP, int m) {
     return 3ull * DP * DP + 3ull * m * DP + 9ull * DP;
 }
 
+// Offset (a multiple of 4 floats) of the k-contiguous copy: WK[g][i][k] =
+// WT[g][k][i] (DP x DP per gate), then UK[g][i][q] = UT[g][q][i] for
+// q < m, 0 up to the row length K16 = m rounded up to 16.
+__host__ __device__ inline size_t kcopy_offset(int kind, int DP, int m) {
+    return (prepared_weight_floats(kind, DP, m) + 3) & ~size_t(3);
+}
+
+__host__ __device__ size_t prepared_total_floats(int kind, int DP, int m) {
+    if (DP % 16 != 0) return prepared_weight_floats(kind, DP, m);
+    const size_t NG = kind == kCellGru ? 3 : 1, K16 = (m + 15) & ~15;
+    return kcopy_offset(kind, DP, m) + NG * DP * DP + NG * DP * K16;
+}
+
 // ---------------------------------------------------------------- weight prep
 // tanh RNN: WT[k][i] = W[i][k] | UT[q][i] = U[i][q] | bias[i] | wdiag[i]
 // Euler   : the tanh RNN layout, then h[i]
@@ -106,11 +119,35 @@ __global__ __launch_bounds__(kThreads) void prep_weights_kernel(int kind, const 
     }
 }
 
+// The k-contiguous copy (prepared_total_floats), from the prepared layout
+// written by prep_weights_kernel.
+__global__ __launch_bounds__(kThreads) void prep_kcopy_kernel(int kind, float* __restrict__ w, int DP, int m,
+                                                              int n) {
+    const int NG = kind == kCellGru ? 3 : 1, K16 = (m + 15) & ~15;
+    const float* WT = w;
+    const float* UT = w + NG * DP * DP;
+    float* WK = w + kcopy_offset(kind, DP, m);
+    float* UK = WK + NG * DP * DP;
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += gridDim.x * blockDim.x) {
+        if (e < NG * DP * DP) {
+            const int g = e / (DP * DP), r = e % (DP * DP), i = r / DP, k = r % DP;
+            WK[e] = WT[(g * DP + k) * DP + i];
+        } else {
+            const int f = e - NG * DP * DP, g = f / (DP * K16), r = f % (DP * K16), i = r / K16, q = r % K16;
+            UK[f] = q < m ? UT[(g * m + q) * DP + i] : 0.0f;
+        }
+    }
+}
+
 hipError_t launch_prep_weights(int kind, const float* params, float* w, int D, int DP, int m,
                                hipStream_t st) {
     const int n = static_cast<int>(prepared_weight_floats(kind, DP, m));
     const int blocks = std::min((n + kThreads - 1) / kThreads, 1024);
     prep_weights_kernel<<<blocks, kThreads, 0, st>>>(kind, params, w, D, DP, m, n);
+    if (DP % 16 == 0) {
+        const int nk = static_cast<int>(prepared_total_floats(kind, DP, m) - kcopy_offset(kind, DP, m));
+        prep_kcopy_kernel<<<std::min((nk + kThreads - 1) / kThreads, 1024), kThreads, 0, st>>>(kind, w, DP, m, nk);
+    }
     return hipGetLastError();
 }
 
@@ -372,25 +409,49 @@ struct CellRegs {
     static constexpr int MAXRT = (kMaxChunk / 16 + WR - 1) / WR;   // row tiles per wavefront
     static constexpr int KB = DP / 4;                              // B values per gate and lane
     static constexpr int PS = iterate_stride<DP>();
+    static constexpr int KIN = DP;                                 // input widths held in registers
     int i, wr, kq;
     bool live;
     float wb[NG][KB];
+    float ub[NG][KIN / 4];       // input weights, B operand (m <= KIN)
     v4f xi[MAXRT][NG];
     float c0, c1, c2, c3, c4, c5, c6, c7, c8;     // per-index constants (biases, diagonals)
 
-    // Weights w: the prepared layout (LDS or global).
-    __device__ __forceinline__ void load(const float* __restrict__ w, int D, int m) {
+    // Weights: w the prepared layout (LDS or global), wg the whole prepared
+    // region in global memory (its k-contiguous copy: one float4 per lane and
+    // 16 k).
+    __device__ __forceinline__ void load(const float* __restrict__ w, const float* __restrict__ wg, int D, int m) {
         const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
         i = (wave % WC) * 16 + (lane & 15);
         wr = wave / WC;
         kq = lane >> 4;
         live = i < D;
+        const float* WK = wg + kcopy_offset(CELL, DP, m);
+        const int K16 = (m + 15) & ~15;
+        const float* UK = WK + NG * DP * DP;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
 #pragma unroll
-            for (int kk = 0; kk < KB; ++kk) {
-                const int k = (kk >> 2) * 16 + 4 * kq + (kk & 3);
-                wb[g][kk] = w[(g * DP + k) * DP + i];
+            for (int kb = 0; kb < DP / 16; ++kb) {
+                const float4 v = *reinterpret_cast<const float4*>(WK + (g * DP + i) * DP + 16 * kb + 4 * kq);
+                wb[g][kb * 4 + 0] = v.x;
+                wb[g][kb * 4 + 1] = v.y;
+                wb[g][kb * 4 + 2] = v.z;
+                wb[g][kb * 4 + 3] = v.w;
+            }
+        }
+        if (m <= KIN) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+#pragma unroll
+                for (int kb = 0; kb < KIN / 16; ++kb) {
+                    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    if (kb * 16 < K16) v = *reinterpret_cast<const float4*>(UK + (g * DP + i) * K16 + 16 * kb + 4 * kq);
+                    ub[g][kb * 4 + 0] = v.x;
+                    ub[g][kb * 4 + 1] = v.y;
+                    ub[g][kb * 4 + 2] = v.z;
+                    ub[g][kb * 4 + 3] = v.w;
+                }
             }
         }
         const float* bi = w + NG * DP * DP + NG * m * DP;
@@ -425,17 +486,33 @@ struct CellRegs {
             v4f acc[NG];
 #pragma unroll
             for (int g = 0; g < NG; ++g) acc[g] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            if (m <= KIN) {
+                // B from the registers loaded with the recurrent weights
+#pragma unroll
+                for (int kb = 0; kb < KIN / 16; ++kb) {
+                    if (kb * 16 >= K) break;
+                    const float4 a4 = rin ? *reinterpret_cast<const float4*>(Ar + 16 * kb) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+                        for (int g = 0; g < NG; ++g)
+                            acc[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], ub[g][kb * 4 + s], acc[g], 0, 0, 0);
+                    }
+                }
+            } else {
 #pragma unroll 4
-            for (int q0 = 0; q0 < K; q0 += 16) {
-                const float4 a4 = rin ? *reinterpret_cast<const float4*>(Ar + q0) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+                for (int q0 = 0; q0 < K; q0 += 16) {
+                    const float4 a4 = rin ? *reinterpret_cast<const float4*>(Ar + q0) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int q = q0 + 4 * kq + s;
+                    for (int s = 0; s < 4; ++s) {
+                        const int q = q0 + 4 * kq + s;
 #pragma unroll
-                    for (int g = 0; g < NG; ++g) {
-                        const float b = q < m ? UT[(g * m + q) * DP + i] : 0.0f;
-                        acc[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], b, acc[g], 0, 0, 0);
+                        for (int g = 0; g < NG; ++g) {
+                            const float b = q < m ? UT[(g * m + q) * DP + i] : 0.0f;
+                            acc[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], b, acc[g], 0, 0, 0);
+                        }
                     }
                 }
             }
@@ -592,30 +669,33 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
     const float* mA = g.aggA + (g.iter & 1) * g.mstride + static_cast<size_t>(b) * g.NC * D;
     const float* mB = g.aggB + (g.iter & 1) * g.mstride + static_cast<size_t>(b) * g.NC * D;
     float own_a = 0.0f, own_b = 0.0f;
+    // fc: the chunk maps this thread folds, loaded before the staging loads
+    // go out so that one memory round trip covers both (kFold per thread;
+    // longer segments finish after staging)
+    constexpr int kFold = (kFcMaxChunks + kThreads / DP - 1) / (kThreads / DP) < 16
+                              ? (kFcMaxChunks + kThreads / DP - 1) / (kThreads / DP) : 16;
+    float pa[kFold], pb[kFold];
+    int k0 = 0, k1 = 0;
     if constexpr (kApply && !DENSE) {
         if (g.fc) {
             const int lane = tid & 63;
             r_i = wave_max_u32(lane < kRSlots ? g.ctrl->rmax[g.iter % 3][lane][0] : 0u);
             // The carry of chunk c, composed here from the chunk maps of
             // iteration i: kThreads / DP segments of the chunks before c are
-            // each folded into one affine map (here), then applied to s0 in
-            // order (after the staging wait); the next chunk's carry is this
+            // each folded into one affine map, then applied to s0 in order
+            // (after the staging wait); the next chunk's carry is this
             // chunk's map applied to it.
             constexpr int NS = kThreads / DP;
             const int d = tid % DP, sg_ = tid / DP;
             const int per = (c + NS - 1) / NS;
-            const int k0 = min(c, sg_ * per), k1 = min(c, k0 + per);
-            float fa = 1.0f, fbv = 0.0f;
-            if (d < D) {
-#pragma unroll 8
-                for (int k = k0; k < k1; ++k) {
-                    const float a = mA[k * D + d];
-                    fbv = a * fbv + mB[k * D + d];
-                    fa = a * fa;
-                }
+            k0 = min(c, sg_ * per);
+            k1 = d < D ? min(c, k0 + per) : k0;
+#pragma unroll
+            for (int u = 0; u < kFold; ++u) {
+                const int k = k0 + u;
+                pa[u] = k < k1 ? mA[k * D + d] : 1.0f;      // padding: the identity map
+                pb[u] = k < k1 ? mB[k * D + d] : 0.0f;
             }
-            SCR[tid] = fa;
-            SCR[kThreads + tid] = fbv;
             if (tid < D && has_next) {
                 own_a = mA[c * D + tid];
                 own_b = mB[c * D + tid];
@@ -628,7 +708,7 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
         c_first = g.carry[ci * D + tid];
         if (has_next) c_next = g.carry[(ci + 1) * D + tid];
     }
-    if constexpr (kRegs) cr16.load(w, D, m);
+    if constexpr (kRegs) cr16.load(w, g.w, D, m);
     copy_rows_to_lds<kThreads>(X, xs, xg, m, Lc, m);
     float* sg = g.s + b * g.ss + static_cast<int64_t>(t0) * D;
     if constexpr (PHASE == kPrologue) {
@@ -654,6 +734,24 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
             P[tid] = tid < D ? ((c == 0) ? s0[tid] : g.halo[(g.iter & 1) * HS + (ci - 1) * D + tid]) : 0.0f;
         }
         copy_rows_to_lds<kThreads>(P + PS, PS, sg, D, Lc, D);
+    }
+    if constexpr (kApply && !DENSE) {
+        if (g.fc) {
+            float fa = 1.0f, fbv = 0.0f;
+#pragma unroll
+            for (int u = 0; u < kFold; ++u) {
+                fbv = pa[u] * fbv + pb[u];
+                fa = pa[u] * fa;
+            }
+            for (int k = k0 + kFold; k < k1; ++k) {
+                const int d = tid % DP;
+                const float a = mA[k * D + d];
+                fbv = a * fbv + mB[k * D + d];
+                fa = a * fa;
+            }
+            SCR[tid] = fa;
+            SCR[kThreads + tid] = fbv;
+        }
     }
     __syncthreads();
     if constexpr (PHASE == kMaps) {
@@ -706,8 +804,26 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
                 // the last row of a chunk that has a successor is that
                 // chunk's carry
                 const int nrep = has_next ? Lc - 1 : Lc;
-#pragma unroll 4
-                for (int j = 0; j < nrep; ++j) {
+                // eight steps at a time: their LDS loads go out together,
+                // ahead of the stores of N (which the compiler cannot tell
+                // apart from the arrays read)
+                int j = 0;
+                for (; j + 8 <= nrep; j += 8) {
+                    float v[8], co[8], pj[9];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        v[u] = V[(j + u) * DP + tid];
+                        co[u] = CO[(j + u) * DP + tid];
+                        pj[u] = P[(j + u) * PS + tid];
+                    }
+                    pj[8] = P[(j + 8) * PS + tid];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        shat = v[u] + co[u] * (shat - pj[u]);
+                        N[(j + u + 1) * PS + tid] = und ? shat : pj[u + 1] + lam * (shat - pj[u + 1]);
+                    }
+                }
+                for (; j < nrep; ++j) {
                     const int o = j * DP + tid;
                     shat = V[o] + CO[o] * (shat - P[j * PS + tid]);
                     const float so = P[(j + 1) * PS + tid];
@@ -756,6 +872,7 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
     if constexpr (!DENSE) {
         if (tid < D) {
             float A = 1.0f, Bc = 0.0f;
+#pragma unroll 8
             for (int j = 0; j < Lc; ++j) {
                 const int o = j * DP + tid;
                 const float at = CO[o];

@@ -161,6 +161,10 @@ hipError_t launch_fill(float* out, int64_t ss, const float* s0, int64_t s0s, int
 hipError_t launch_prep_weights(int kind, const float* params, float* w, int D, int DP, int m,
                                hipStream_t st);
 __host__ __device__ size_t prepared_weight_floats(int kind, int DP, int m);
+// The whole prepared region in the workspace: the layout above and, for DP a
+// multiple of 16, a copy of the weight matrices with k contiguous per
+// (gate, i) row, from which the register-resident evaluation loads float4s.
+__host__ __device__ size_t prepared_total_floats(int kind, int DP, int m);
 hipError_t launch_cell_pass(int kind, int DP, bool dense, int phase, const CellArgs& a,
                             hipStream_t st);
 size_t cell_pass_lds_bytes(int kind, int DP, bool dense, int L, int m);
