@@ -263,10 +263,11 @@ def main():
     for _ in range(args.warmup):
         warm = solve(False)
     torch.cuda.synchronize()
-    # HIP events around a launch add stream work between launches: on
-    # solves of many short launches only a sample of about 64 per solve is
-    # timed (every n-th steady launch), enough for the average launch time
-    stride = max(1, (warm.iters if warm is not None else 0) // 64)
+    # Timing events cost several microseconds per timed launch (about 6.5 us
+    # on a 15 us launch), so a solve of many launches times a sample of
+    # about four of them (every n-th steady launch); the launches of a solve
+    # are alike, and the timed steps give tens of samples
+    stride = max(1, (warm.iters if warm is not None else 0) // 4)
     results = []
     t0 = time.perf_counter()
     for _ in range(args.steps):

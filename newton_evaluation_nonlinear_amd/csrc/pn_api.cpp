@@ -9,7 +9,10 @@
 //     apply(i)   fused update s^(i) -> s^(i+1) (exits at once if stopped)
 // The host reads the decision of carry(i) while apply(i) runs, so the GPU is
 // never idle waiting for the host; after the stop, one apply launch exits
-// immediately.  Stop rule and counting follow include/pn.h.
+// immediately.  Matrix cells in the diagonal modes with few chunks per
+// window skip the carry launch: each apply sweep takes its own check and
+// composes its carries (CellArgs::fc), and the host keeps two sweeps queued.
+// Stop rule and counting follow include/pn.h.
 
 #include <hip/hip_runtime.h>
 
@@ -335,6 +338,8 @@ int get_res(ThreadRes** out) {
     return PN_OK;
 }
 
+thread_local LaunchTiming g_launch_timing;
+
 int timing_event(ThreadRes* r, size_t idx, hipEvent_t* ev) {
     while (r->timing.size() <= idx) {
         hipEvent_t e;
@@ -416,6 +421,30 @@ double apply_flops(const Plan& p, int Tw) {
         per += 2.0 * D * D * nz + 2.0 * (2.0 * NG * D * nz);
     }
     return static_cast<double>(p.B) * Tw * per;
+}
+
+// Timing of the next steady apply launch: two events that the launch
+// records with its own dispatch (launch_maybe_timed).  After the launch,
+// check_timed_launch confirms the launch took the request.
+int request_timing(SolveCtx& c, size_t* i0, size_t* i1) {
+    hipEvent_t e0, e1;
+    int rc = timing_event(c.res, c.tm->next, &e0);
+    if (rc != PN_OK) return rc;
+    rc = timing_event(c.res, c.tm->next + 1, &e1);
+    if (rc != PN_OK) return rc;
+    *i0 = c.tm->next;
+    *i1 = c.tm->next + 1;
+    c.tm->next += 2;
+    g_launch_timing = LaunchTiming{e0, e1};
+    return PN_OK;
+}
+
+int check_timed_launch() {
+    if (g_launch_timing.start) {
+        g_launch_timing = LaunchTiming{};
+        return fail(PN_EHIP, "a timed launch did not record its events");
+    }
+    return PN_OK;
 }
 
 int record(SolveCtx& c, size_t* idx) {
@@ -536,11 +565,11 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
         // final ones that exit at once
         const bool timed = phase == kSteady && c.tm->take();
         size_t e0 = 0, e1 = 0;
-        if (timed) { int rc = record(c, &e0); if (rc) return rc; }
+        if (timed) { int rc = request_timing(c, &e0, &e1); if (rc) return rc; }
         PN_HIP(launch_pass(phase, k));
         tslot.push_back(-1);
         if (timed) {
-            int rc = record(c, &e1);
+            int rc = check_timed_launch();
             if (rc) return rc;
             c.tm->apply.push_back({e0, e1});
             c.tm->apply_bytes.push_back(0.0);   // filled in once the check says it ran
@@ -741,10 +770,10 @@ int solve_advancing(SolveCtx& c, const float* x, const float* s0, float* out, in
         PN_HIP(p.dense ? launch_dense_carry(cy, c.st) : launch_diag_carry(cy, c.st));
         size_t e0 = 0, e1 = 0;
         const bool timed = c.tm->take();
-        if (timed) { int rc = record(c, &e0); if (rc) return rc; }
+        if (timed) { int rc = request_timing(c, &e0, &e1); if (rc) return rc; }
         PN_HIP(launch_pass(kSteady, i));
         if (timed) {
-            int rc = record(c, &e1);
+            int rc = check_timed_launch();
             if (rc) return rc;
             c.tm->apply.push_back({e0, e1});
             c.tm->apply_bytes.push_back(apply_bytes(p, Tw, false));
@@ -972,6 +1001,10 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
 }
 
 }  // namespace
+
+namespace pn {
+LaunchTiming& launch_timing() { return g_launch_timing; }
+}  // namespace pn
 
 extern "C" {
 

@@ -30,6 +30,7 @@
 // LDS; padded rows/columns are kept at zero.
 
 #include "pn_device.hpp"
+#include "pn_launch.hpp"
 
 namespace pn {
 
@@ -1003,8 +1004,7 @@ static hipError_t launch_one(const CellArgs& a, size_t lds, hipStream_t st) {
             reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (attr != hipSuccess) return attr;
     }
-    k<<<dim3(a.NC, a.B), kThreads, lds, st>>>(a);
-    return hipGetLastError();
+    return launch_maybe_timed(k, dim3(a.NC, a.B), dim3(kThreads), lds, st, a);
 }
 
 template <int CELL, int DP, bool DENSE>

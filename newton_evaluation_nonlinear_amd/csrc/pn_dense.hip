@@ -33,6 +33,7 @@
 // sums over K_h combined across the NH = 64 / DP lane groups.
 
 #include "pn_device.hpp"
+#include "pn_launch.hpp"
 
 namespace pn {
 
@@ -911,7 +912,7 @@ static hipError_t launch_dense64_b(int phase, const CellArgs& a, hipStream_t st)
     if (phase == kPrologue) dense64_pass<CELL, kPrologue, BANDED><<<grid, 64, lds, st>>>(a);
     else if (phase == kFirst) dense64_pass<CELL, kFirst, BANDED><<<grid, 64, lds, st>>>(a);
     else if (phase == kMaps) dense64_pass<CELL, kMaps, BANDED><<<grid, 64, lds, st>>>(a);
-    else dense64_pass<CELL, kSteady, BANDED><<<grid, 64, lds, st>>>(a);
+    else return launch_maybe_timed(dense64_pass<CELL, kSteady, BANDED>, grid, dim3(64), lds, st, a);
     return hipGetLastError();
 }
 
@@ -929,7 +930,7 @@ static hipError_t launch_dense_phase_s(int phase, const CellArgs& a, hipStream_t
     if (phase == kPrologue) dense_pass<CELL, DP, kPrologue, BANDED, SPLIT><<<grid, nt, lds, st>>>(a);
     else if (phase == kFirst) dense_pass<CELL, DP, kFirst, BANDED, SPLIT><<<grid, nt, lds, st>>>(a);
     else if (phase == kMaps) dense_pass<CELL, DP, kMaps, BANDED, SPLIT><<<grid, nt, lds, st>>>(a);
-    else dense_pass<CELL, DP, kSteady, BANDED, SPLIT><<<grid, nt, lds, st>>>(a);
+    else return launch_maybe_timed(dense_pass<CELL, DP, kSteady, BANDED, SPLIT>, grid, dim3(nt), lds, st, a);
     return hipGetLastError();
 }
 

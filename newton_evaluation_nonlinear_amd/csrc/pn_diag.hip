@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "pn_device.hpp"
+#include "pn_launch.hpp"
 
 namespace pn {
 
@@ -350,10 +351,12 @@ static hipError_t launch_und(int phase, const DiagArgs& a, hipStream_t st) {
     const dim3 grid = diag_grid(a);
     if (phase == kPrologue) diag_tanh_pass<MODE, kPrologue, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
     else if (phase == kFirst) diag_tanh_pass<MODE, kFirst, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
-    else if (phase == kSteady && !a.fpart) diag_tanh_pass<MODE, kSteady, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
+    else if (phase == kSteady && !a.fpart)
+        return launch_maybe_timed(diag_tanh_pass<MODE, kSteady, S, NCH, UND>, grid, dim3(kThreads), 0, st, a);
     else if constexpr (std::is_same<S, float>::value) {
         // the advancing window and the recomputing pair run with float storage only
-        if (phase == kSteady) diag_tanh_pass<MODE, kSteady, S, NCH, UND, true><<<grid, kThreads, 0, st>>>(a);
+        if (phase == kSteady)
+            return launch_maybe_timed(diag_tanh_pass<MODE, kSteady, S, NCH, UND, true>, grid, dim3(kThreads), 0, st, a);
         else if (phase == kMaps) diag_tanh_pass<MODE, kMaps, S, NCH, UND, true><<<grid, kThreads, 0, st>>>(a);
         else if (phase == kFirstNS) diag_tanh_pass<MODE, kFirstNS, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
         else if (phase == kSecondR) diag_tanh_pass<MODE, kSecondR, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);

@@ -147,6 +147,13 @@ struct CarryArgs {
 // iteration 0 instead of reading it (see pn_diag.hip).
 enum Phase { kPrologue = 0, kFirst = 1, kSteady = 2, kMaps = 3, kFirstNS = 4, kSecondR = 5 };
 
+// Timing request for the next steady apply launch of this thread: the
+// launcher records these events around the kernel itself and clears them.
+struct LaunchTiming {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchTiming& launch_timing();
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_diag_tanh_pass(int phase, const DiagArgs& a, hipStream_t st);
 int diag_tanh_nblocks(const DiagArgs& a);
