@@ -416,7 +416,9 @@ struct CellRegs {
     float wb[NG][KB];
     float ub[NG][KIN / 4];       // input weights, B operand (m <= KIN)
     v4f xi[MAXRT][NG];
-    float c0, c1, c2, c3, c4, c5, c6, c7, c8;     // per-index constants (biases, diagonals)
+    // per-index constants (biases, diagonals), kept as loaded: a use right
+    // after the load would wait for every load issued before it
+    float c0, c0b, c1, c1b, c2, c3, c4, c5, c6;
 
     // Weights: w the prepared layout (LDS or global), wg the whole prepared
     // region in global memory (its k-contiguous copy: one float4 per lane and
@@ -457,8 +459,10 @@ struct CellRegs {
         }
         const float* bi = w + NG * DP * DP + NG * m * DP;
         if constexpr (CELL == kCellGru) {
-            c0 = bi[i] + bi[3 * DP + i];                 // b_ir + b_hr
-            c1 = bi[DP + i] + bi[4 * DP + i];            // b_iz + b_hz
+            c0 = bi[i];                                  // b_ir (+ b_hr)
+            c0b = bi[3 * DP + i];
+            c1 = bi[DP + i];                             // b_iz (+ b_hz)
+            c1b = bi[4 * DP + i];
             c2 = bi[2 * DP + i];                         // b_in
             c3 = bi[5 * DP + i];                         // b_hn
             c4 = bi[6 * DP + i];                         // diag W_hr
@@ -518,8 +522,8 @@ struct CellRegs {
                 }
             }
             if constexpr (CELL == kCellGru) {
-                xi[u][0] = acc[0] + c0;
-                xi[u][1] = acc[1] + c1;
+                xi[u][0] = acc[0] + (c0 + c0b);
+                xi[u][1] = acc[1] + (c1 + c1b);
                 xi[u][2] = acc[2] + c2;
             } else {
                 xi[u][0] = acc[0] + c0;
@@ -665,8 +669,10 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
     const size_t HS = static_cast<size_t>(g.B) * g.NC * D;
     const bool has_next = c + 1 < g.NC;
     float c_first = 0.0f, c_next = 0.0f;
-    // fc: r_i as the sweep before reduced it (every wavefront reads the slots)
-    uint32_t r_i = 0;
+    // fc: r_i as the sweep before reduced it (every wavefront reads the
+    // slots; reduced after the staging wait) and the control word
+    uint32_t r_raw = 0;
+    int stop_before = 0;
     const float* mA = g.aggA + (g.iter & 1) * g.mstride + static_cast<size_t>(b) * g.NC * D;
     const float* mB = g.aggB + (g.iter & 1) * g.mstride + static_cast<size_t>(b) * g.NC * D;
     float own_a = 0.0f, own_b = 0.0f;
@@ -680,7 +686,8 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
     if constexpr (kApply && !DENSE) {
         if (g.fc) {
             const int lane = tid & 63;
-            r_i = wave_max_u32(lane < kRSlots ? g.ctrl->rmax[g.iter % 3][lane][0] : 0u);
+            r_raw = lane < kRSlots ? g.ctrl->rmax[g.iter % 3][lane][0] : 0u;
+            stop_before = g.ctrl->stop;
             // The carry of chunk c, composed here from the chunk maps of
             // iteration i: kThreads / DP segments of the chunks before c are
             // each folded into one affine map, then applied to s0 in order
@@ -760,8 +767,11 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
     }
     if constexpr (kApply && !DENSE) {
         if (g.fc) {
+            // the loop stopped at an earlier check: this launch was queued ahead
+            if (stop_before) return false;
             // the check of iteration i, taken alike by every workgroup; block
             // 0 publishes it and clears the slot set of the sweep after next
+            const uint32_t r_i = wave_max_u32(r_raw);
             CheckArgs chk{};
             chk.iter = g.iter;
             chk.max_iter = g.max_iter;
@@ -968,7 +978,7 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
 template <int CELL, int DP, bool DENSE, int PHASE, bool STAGE>
 __global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
     if constexpr (PHASE != kPrologue && PHASE != kMaps) {   // apply launches enqueued ahead
-        if (g.ctrl->stop) return;
+        if (!g.fc && g.ctrl->stop) return;                   // (fc: read with the staging loads)
     }
     extern __shared__ __attribute__((aligned(16))) float lds[];
     // the prepared weights are staged once per workgroup in LDS when they fit
