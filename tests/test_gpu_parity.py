@@ -656,6 +656,23 @@ def test_fused_check_and_carry_launch_paths(chunk, T, window):
         _parity(wl, mode, chunk=chunk)
 
 
+@pytest.mark.parametrize("kind, D, m", [(pn.CELL_TANH_RNN, 32, 5), (pn.CELL_GRU, 32, 40),
+                                        (pn.CELL_EULER_TANH, 16, 3), (pn.CELL_GRU, 20, 7)])
+@pytest.mark.parametrize("T, chunk", [(2048, 16), (2049, 16), (16, 16)])
+def test_fused_check_chunk_count_limits(kind, D, m, T, chunk):
+    # 128 chunks per window (the most an apply sweep composes itself), 129
+    # (a carry launch), and a single chunk; input widths below and above D
+    # (register and memory operands of the projection); step damping
+    rng = np.random.default_rng(900 + D + m)
+    params = workloads.random_cell_params(kind, D, m, rng, 1.0)
+    B = 2
+    wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-5, damping=0.7, window=0,
+              max_iter=T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32))
+    for mode in ((Q, J) if T <= 16 else (Q,)):
+        _parity(wl, mode, chunk=chunk)
+
+
 def test_fused_check_stop_rules():
     # the three stop outcomes as every workgroup of a sweep takes them
     wl = _case(5, B=2, T=2048)
