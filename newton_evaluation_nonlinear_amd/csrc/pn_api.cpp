@@ -76,8 +76,9 @@ struct Plan {
     bool persist_ok;       // shape allows the one-launch persistent solver
     bool recompute;        // channel-wise cell, float storage: first update stores nothing,
                            // the second recomputes s^(1) (kFirstNS, kSecondR)
-    bool fc;               // matrix cell, diagonal mode, few chunks: each apply sweep takes
-                           // its own check and carries (CellArgs::fc), no carry launch
+    int fc;                // matrix cell, diagonal mode, few chunks (CellArgs::fc): the apply
+                           // sweeps compose their own carries (kFcCarry) and, with
+                           // consecutive windows, take their own check (kFcCheck)
     int nblocks, nwin, hist_cap;
     size_t off_ctrl, off_rpart, off_fpart, off_aggA, off_aggB, off_carry, off_carry0, off_halo, off_w,
         total;
@@ -111,7 +112,7 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
     const int chunk = o ? o->chunk : 0;
     p.dense = p.matrix_cell && (mode == PN_NEWTON || mode == PN_BANDED);
     p.mfma = false;
-    p.fc = false;
+    p.fc = 0;
     if (!p.matrix_cell) {
         // binary16 storage moves two adjacent channels per thread when D is even
         p.hmode = !half ? 0 : (p.D % 2 == 0 ? 2 : 1);
@@ -183,7 +184,7 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
         p.nblocks = p.NC * p.B;
         // with few chunks per row, composing a chunk's carry in its own sweep
         // costs less than a carry launch
-        p.fc = !p.dense && !p.advancing && p.NC <= kFcMaxChunks;
+        if (!p.dense && p.NC <= kFcMaxChunks) p.fc = p.advancing ? kFcCarry : (kFcCarry | kFcCheck);
         if (cell_pass_lds_bytes(p.kind, p.DP, p.dense, p.L, p.m) > 160 * 1024)
             return fail(PN_EUNSUPPORTED, "chunk of %d steps needs too much LDS for D=%d, m=%d", p.L, p.D, p.m);
     }
@@ -245,7 +246,7 @@ int make_plans(Plan& p, Plan& p2, bool* has2, const pn_cell* cell, int64_t B, in
     if (rc != PN_OK) return rc;
     p.persist_ok = p2.persist_ok = false;
     p.recompute = p2.recompute = false;
-    p.fc = p2.fc = false;
+    p.fc = p2.fc = 0;
     p.Lc = p.L; p2.Lc = p2.L;
     p.NCc = p.NC; p2.NCc = p2.NC;
     layout(p, &p2);
@@ -532,7 +533,7 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
     configure(*pp);
     *sw = -1;
     // fc sweeps reduce r_0 into ctrl->rmax[0] and expect rmax[1] clear
-    if (pp->fc) PN_HIP(hipMemsetAsync(ctrl, 0, sizeof(Ctrl), c.st));
+    if (pp->fc & kFcCheck) PN_HIP(hipMemsetAsync(ctrl, 0, sizeof(Ctrl), c.st));
     PN_HIP(launch_pass(kPrologue, 0));
     volatile HostRec* ring = c.res->host;      // check i goes to ring[i % kHostRing]
     const int32_t epoch = ++c.res->epoch;
@@ -555,7 +556,7 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
     // Apply launch k (update k).  Sweeps that take their own check (fc) are
     // kept `ahead` launches in front of the check the host is reading: a
     // sweep after the stop finds the control word set and exits at once.
-    const int ahead = pp->fc ? 2 : 0;
+    const int ahead = (pp->fc & kFcCheck) ? 2 : 0;
     std::vector<int> tslot;      // launch k -> its timing entry, or -1
     auto enqueue_apply = [&](int k) -> int {
         const int phase = k == 0 ? (recompute ? kFirstNS : kFirst)
@@ -594,7 +595,7 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
             cy.NC = da.NC;
             cy.chk.nparts = diag_tanh_nblocks(da);
         }
-        if (!pp->fc) {
+        if (!(pp->fc & kFcCheck)) {
             // the check of iteration i and the carries of its maps, then update i
             PN_HIP(pp->dense ? launch_dense_carry(cy, c.st) : launch_diag_carry(cy, c.st));
             int rc = enqueue_apply(i);
@@ -647,7 +648,7 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
             }
         }
         r_prev = r;
-        if (pp->fc) {
+        if (pp->fc & kFcCheck) {
             int rc = enqueue_apply(i + ahead);
             if (rc != PN_OK) return rc;
         }
@@ -686,6 +687,10 @@ int solve_advancing(SolveCtx& c, const float* x, const float* s0, float* out, in
     ca.aggA = aggA; ca.aggB = aggB; ca.carry = carry; ca.halo = halo; ca.rpart = rpart;
     ca.ctrl = ctrl; ca.mode = p.mode; ca.lam = c.lam; ca.undamped = c.lam == 1.0f;
     ca.band = p.band; ca.fpart = fpart; ca.tol = c.tol;
+    ca.fc = p.fc;                    // kFcCarry or 0: the check stays a launch of its own
+    // two sets of chunk maps only with kFcCarry (one set, read by the carry
+    // launch, otherwise)
+    ca.mstride = p.fc ? static_cast<int64_t>(p.B) * p.NC * p.D : 0;
     DiagArgs da{};                   // the channel-wise cell (m == D, float storage)
     da.a = c.params; da.xs = T * m; da.ss = T * D;
     da.B = p.B; da.D = p.D; da.L = p.L; da.cpb = p.cpb;
@@ -767,7 +772,7 @@ int solve_advancing(SolveCtx& c, const float* x, const float* s0, float* out, in
             ma = a;
             me = e;
         }
-        PN_HIP(p.dense ? launch_dense_carry(cy, c.st) : launch_diag_carry(cy, c.st));
+        if (!(p.fc & kFcCarry)) PN_HIP(p.dense ? launch_dense_carry(cy, c.st) : launch_diag_carry(cy, c.st));
         size_t e0 = 0, e1 = 0;
         const bool timed = c.tm->take();
         if (timed) { int rc = request_timing(c, &e0, &e1); if (rc) return rc; }

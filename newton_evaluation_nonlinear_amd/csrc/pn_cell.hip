@@ -684,10 +684,12 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
     float pa[kFold], pb[kFold];
     int k0 = 0, k1 = 0;
     if constexpr (kApply && !DENSE) {
-        if (g.fc) {
+        if (g.fc & kFcCheck) {
             const int lane = tid & 63;
             r_raw = lane < kRSlots ? g.ctrl->rmax[g.iter % 3][lane][0] : 0u;
             stop_before = g.ctrl->stop;
+        }
+        if (g.fc & kFcCarry) {
             // The carry of chunk c, composed here from the chunk maps of
             // iteration i: kThreads / DP segments of the chunks before c are
             // each folded into one affine map, then applied to s0 in order
@@ -744,7 +746,7 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
         copy_rows_to_lds<kThreads>(P + PS, PS, sg, D, Lc, D);
     }
     if constexpr (kApply && !DENSE) {
-        if (g.fc) {
+        if (g.fc & kFcCarry) {
             float fa = 1.0f, fbv = 0.0f;
 #pragma unroll
             for (int u = 0; u < kFold; ++u) {
@@ -766,7 +768,7 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
         if (tid < D) g.halo[(g.iter & 1) * HS + ci * D + tid] = N[Lc * PS + tid];
     }
     if constexpr (kApply && !DENSE) {
-        if (g.fc) {
+        if (g.fc & kFcCheck) {
             // the loop stopped at an earlier check: this launch was queued ahead
             if (stop_before) return false;
             // the check of iteration i, taken alike by every workgroup; block
@@ -787,14 +789,15 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
                 if (tid == 0) publish_check(chk, r_i, st, 0xffffffffu);
             }
             if (st >= 0) return false;
-            if (tid < D) {
-                constexpr int NS = kThreads / DP;
-                float x = s0[tid];
+        }
+        if ((g.fc & kFcCarry) && tid < D) {
+            // the folded segments applied to s0 in order
+            constexpr int NS = kThreads / DP;
+            float x = s0[tid];
 #pragma unroll
-                for (int q = 0; q < NS; ++q) x = SCR[q * DP + tid] * x + SCR[kThreads + q * DP + tid];
-                c_first = x;
-                if (has_next) c_next = own_a * x + own_b;
-            }
+            for (int q = 0; q < NS; ++q) x = SCR[q * DP + tid] * x + SCR[kThreads + q * DP + tid];
+            c_first = x;
+            if (has_next) c_next = own_a * x + own_b;
         }
     }
     // ---- the input projection (iterate-free)
@@ -891,8 +894,10 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
                 Bc = at * Bc + bt;
                 A = at * A;
             }
-            // the maps of iteration i+1 (of iteration 0 in the prologue)
-            const size_t mo = (PHASE == kPrologue ? 0 : ((g.iter + 1) & 1)) * g.mstride;
+            // the maps of iteration i+1 (of iteration 0 in the prologue; a
+            // maps pass launched with iter i writes those of iteration i)
+            const size_t mo = (PHASE == kPrologue ? 0 : PHASE == kMaps ? (g.iter & 1) : ((g.iter + 1) & 1)) *
+                              g.mstride;
             g.aggA[mo + ci * D + tid] = A;
             g.aggB[mo + ci * D + tid] = Bc;
         }
@@ -978,7 +983,7 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
 template <int CELL, int DP, bool DENSE, int PHASE, bool STAGE>
 __global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
     if constexpr (PHASE != kPrologue && PHASE != kMaps) {   // apply launches enqueued ahead
-        if (!g.fc && g.ctrl->stop) return;                   // (fc: read with the staging loads)
+        if (!(g.fc & kFcCheck) && g.ctrl->stop) return;      // (else read with the staging loads)
     }
     extern __shared__ __attribute__((aligned(16))) float lds[];
     // the prepared weights are staged once per workgroup in LDS when they fit
@@ -992,7 +997,7 @@ __global__ __launch_bounds__(kThreads) void cell_pass(CellArgs g) {
     rb = block_max_u32(rb);
     const size_t blk = static_cast<size_t>(blockIdx.y) * g.NC + blockIdx.x;
     if (threadIdx.x == 0) {
-        if (g.fc) {
+        if (g.fc & kFcCheck) {
             const int set = PHASE == kPrologue ? 0 : (g.iter + 1) % 3;
             __hip_atomic_fetch_max(&g.ctrl->rmax[set][blk % kRSlots][0], rb, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);

@@ -114,11 +114,12 @@ struct CellArgs {
     uint32_t* fpart;         // advancing window: per-block first step with r_t > tol
                              // (window-relative; 0xffffffff if none), or null
     float tol;
-    // fc = 1 (diagonal modes, at most kFcMaxChunks chunks per row): no carry
-    // launch; every apply sweep takes the check of its iteration itself from
-    // ctrl->rmax, publishes it (block 0) to ctrl and host, and composes the
-    // carry of its chunk from the chunk maps.  The maps of iteration k are
-    // at aggA/aggB + (k & 1) * mstride.
+    // fc (diagonal modes, at most kFcMaxChunks chunks per row), bits:
+    // kFcCarry: no carry launch; every apply sweep composes the carry of its
+    //   chunk from the chunk maps, which for iteration k are at aggA/aggB +
+    //   (k & 1) * mstride (a maps pass launched with iter k writes set k & 1);
+    // kFcCheck: every apply sweep also takes the check of its iteration from
+    //   ctrl->rmax and publishes it (block 0) to ctrl and host.
     int32_t fc;
     int32_t max_iter;
     int32_t epoch;
@@ -127,6 +128,7 @@ struct CellArgs {
 };
 
 constexpr int kFcMaxChunks = 128;
+constexpr int kFcCarry = 1, kFcCheck = 2;
 
 struct CarryArgs {
     const float* aggA;

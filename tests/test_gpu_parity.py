@@ -381,6 +381,13 @@ def test_advancing_window_matches_oracle(kind, D, W):
         _parity(wl, mode)
 
 
+def test_advancing_window_carry_launch_path():
+    # a 2100-step window of 16-step chunks (132 chunks) is past what an apply
+    # sweep composes itself: its carries come from a carry launch
+    wl = _advancing_case(pn.CELL_EULER_TANH, 16, 3, 2, 2500, 2100, 640)
+    _parity(wl, Q)
+
+
 def test_advancing_window_damped():
     wl = _advancing_case(pn.CELL_EULER_TANH, 16, 3, 3, 400, 96, 610, damping=0.7)
     for mode in (Q, N):
