@@ -762,13 +762,19 @@ int solve_advancing(SolveCtx& c, const float* x, const float* s0, float* out, in
         if (a >= T) { *K = i; *status = PN_OK; break; }
         if (i == c.max_iter) { *K = i; *status = PN_NOT_CONVERGED; break; }
         const int64_t e_new = std::min<int64_t>(T, a + W);
-        if (e_new > e)
+        // steps entering the window start from its last state: the maps pass
+        // of the matrix cells' tile kernel writes them itself
+        const bool tile_fill = p.matrix_cell && !p.mfma;
+        if (e_new > e && !tile_fill)
             PN_HIP(launch_fill(out + e * D, T * D, out + (e - 1) * D, T * D, p.B,
                                static_cast<int>(e_new - e), p.D, c.st));
+        const int fill_rows = tile_fill ? static_cast<int>(e_new - e) : 0;
         e = e_new;
         set_window();
         if (a != ma || e != me) {
+            ca.fill_rows = fill_rows;
             PN_HIP(launch_pass(kMaps, i));
+            ca.fill_rows = 0;
             ma = a;
             me = e;
         }

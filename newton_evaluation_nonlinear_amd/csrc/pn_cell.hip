@@ -728,11 +728,22 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
             N[e] = i < D ? s0[i] : 0.0f;
         }
     } else if constexpr (PHASE == kMaps) {
-        // N: rows t0-1 .. t1-1 of the iterate in s (this pass writes no row
-        // of s, so the row before the chunk is read directly); its last row
-        // is the halo the next apply reads
-        if (tid < PS) N[tid] = tid < D ? (c == 0 ? s0[tid] : sg[tid - D]) : 0.0f;
-        copy_rows_to_lds<kThreads>(N + PS, PS, sg, D, Lc, D);
+        // N: rows t0-1 .. t1-1 of the iterate in s; its last row is the halo
+        // the next apply reads.  Rows from ff on (window-relative) are new
+        // steps: they start from the state before them, row ff-1 (or s0),
+        // which this pass does not write, and are written to s here.
+        const int ff = g.Tw - g.fill_rows;
+        const float* sw = g.s + b * g.ss;                    // window row 0
+        auto fillv = [&](int i) { return ff == 0 ? s0[i] : sw[static_cast<int64_t>(ff - 1) * D + i]; };
+        if (tid < PS) N[tid] = tid < D ? (c == 0 ? s0[tid] : (t0 - 1 >= ff ? fillv(tid) : sg[tid - D])) : 0.0f;
+        const int nld = max(0, min(Lc, ff - t0));           // rows already in s
+        copy_rows_to_lds<kThreads>(N + PS, PS, sg, D, nld, D);
+        for (int e = tid; e < (Lc - nld) * PS; e += kThreads) {
+            const int j = nld + e / PS, i = e % PS;
+            const float v = i < D ? fillv(i) : 0.0f;
+            N[(j + 1) * PS + i] = v;
+            if (i < D) sg[j * D + i] = v;
+        }
     } else if constexpr (PHASE == kFirst) {
         // ---- P: rows t0-1 .. t1-1 of s^(i)
         for (int e = tid; e < (Lc + 1) * PS; e += kThreads) {

@@ -121,6 +121,10 @@ struct CellArgs {
     // kFcCheck: every apply sweep also takes the check of its iteration from
     //   ctrl->rmax and publishes it (block 0) to ctrl and host.
     int32_t fc;
+    // maps pass of the advancing window: the last fill_rows rows of the
+    // window are new steps; the pass starts them from the state before them
+    // (stored in s) and writes them (0: none)
+    int32_t fill_rows;
     int32_t max_iter;
     int32_t epoch;
     int64_t mstride;
