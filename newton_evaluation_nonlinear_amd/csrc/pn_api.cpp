@@ -887,6 +887,7 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
               int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter, float* out,
               int32_t* iters_out, const pn_opts* o, bool half = false) {
     g_err.clear();
+    g_launch_timing = LaunchTiming{};     // no request left over from a failed call
     int rc = validate(cell, params, x, s0, B, T, D, mode, tol, max_iter, out, iters_out, o);
     if (rc != PN_OK) return rc;
     if (half) {
