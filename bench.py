@@ -69,6 +69,18 @@ def _traffic(name, src, launch_bytes_alg):
 CPU_SECONDS = 10.0    # CPU work of the oracle baseline (one thread)
 
 
+def _cpu_sample(cfg, mode):
+    """The bounded sample of a workload the CPU baselines run (B and T)."""
+    samples = {3: dict(B=8, T=32768), 2: dict(B=16, T=2048), 4: dict(B=8, T=4096),
+               1: dict(B=None, T=None), 5: dict(B=4, T=4096), 6: dict(B=8, T=4096),
+               7: dict(B=None, T=None)}
+    if cfg == 2 and mode == 1:
+        # float64 Picard on this GRU needs ~T updates (it converges only
+        # through its causality bound), so the sample is shorter in time
+        return dict(B=16, T=256)
+    return samples.get(cfg, dict(B=1, T=4096))
+
+
 def cpu_baseline(cfg, mode, switch_mode=-1, switch_ratio=0.5, storage=None):
     """The float64 oracle on a bounded sample of the workload, one thread."""
     import numpy as np
@@ -76,15 +88,7 @@ def cpu_baseline(cfg, mode, switch_mode=-1, switch_ratio=0.5, storage=None):
     import oracle
     import workloads
 
-    samples = {3: dict(B=8, T=32768), 2: dict(B=16, T=2048), 4: dict(B=8, T=4096),
-               1: dict(B=None, T=None), 5: dict(B=4, T=4096), 6: dict(B=8, T=4096),
-               7: dict(B=None, T=None)}
-    sm = samples.get(cfg, dict(B=1, T=4096))
-    if cfg == 2 and mode == 1:
-        # float64 Picard on this GRU needs ~T updates (it converges only
-        # through its causality bound), so the sample is shorter in time
-        sm = dict(B=16, T=256)
-    wl = workloads.make(cfg, **sm)
+    wl = workloads.make(cfg, **_cpu_sample(cfg, mode))
     if storage == "f16":
         wl["tol"] = F16_TOL
         wl["x"] = wl["x"].astype(np.float16).astype(np.float32)
@@ -112,6 +116,83 @@ def cpu_baseline(cfg, mode, switch_mode=-1, switch_ratio=0.5, storage=None):
                       f"T={wl['T']} (D={wl['D']}): {r.iters} updates, status {r.status}; "
                       f"{reps} runs, {el:.1f} s on one host thread",
             "seconds": el}
+
+
+# ---------------------------------------------------------------- CPU detail
+# Inherited by forked workers (no pickling of the sample arrays).
+_DETAIL = {}
+
+
+def _detail_rows(job):
+    """One worker of the batch split: the rows [b0, b1) of the sample."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    what, b0, b1 = job
+    d = _DETAIL
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        if what == "sequential":
+            oracle.sequential(d["cell"], d["x64"][b0:b1], d["s064"][b0:b1])
+        elif d["wl"]["window_mode"] == "advancing":
+            wl = d["wl"]
+            oracle.solve_advancing(d["cell"], wl["x"][b0:b1], wl["s0"][b0:b1], d["mode"], wl["tol"],
+                                   wl["max_iter"], wl["window"], wl["damping"], wl["bandwidth"])
+        else:
+            wl = d["wl"]
+            oracle.solve(wl["cell"], wl["params"], wl["x"][b0:b1], wl["s0"][b0:b1], d["mode"], wl["tol"],
+                         wl["max_iter"], wl["damping"], wl["window"], bandwidth=wl["bandwidth"],
+                         switch_mode=d["switch_mode"], switch_ratio=d["switch_ratio"],
+                         storage=d["storage"])
+        return time.perf_counter() - t0
+
+
+def cpu_detail(cfg, mode, switch_mode=-1, switch_ratio=0.5, storage=None):
+    """The float64 sequential loop and the float64 oracle solve on the CPU
+    baseline's sample: each on one core, then split across the batch rows
+    over the host's cores (forked workers, one row range each).  The split
+    solves stop on their own rows' residuals, not the batch-global rule."""
+    import multiprocessing as mp
+    import numpy as np
+    import oracle
+    import workloads
+
+    wl = workloads.make(cfg, **_cpu_sample(cfg, mode))
+    if storage == "f16":
+        wl["tol"] = F16_TOL
+        wl["x"] = wl["x"].astype(np.float16).astype(np.float32)
+    cell = oracle.make_cell(wl["cell"], wl["params"], wl["D"], wl["m"])
+    _DETAIL.clear()
+    _DETAIL.update(wl=wl, cell=cell, mode=mode, storage=storage, switch_ratio=switch_ratio,
+                   switch_mode=switch_mode if switch_mode >= 0 else None,
+                   x64=wl["x"].astype(np.float64), s064=wl["s0"].astype(np.float64))
+    B = wl["B"]
+    n = wl["B"] * wl["T"] * wl["D"]
+    cores = len(os.sched_getaffinity(0))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "")
+    except OSError:
+        pass
+    out = {"cores_available": cores, "cpu_model": model,
+           "sample": f"B={B}, T={wl['T']}, D={wl['D']} of the same workload"}
+    single = {}
+    for what in ("sequential", "solve"):
+        el = _detail_rows((what, 0, B))
+        single[what] = {"seconds": el, "state_updates_per_s": n / el}
+    out["single_core"] = single
+    workers = min(cores, B, 16)
+    edges = [B * k // workers for k in range(workers + 1)]
+    split = {"workers": workers}
+    with mp.get_context("fork").Pool(workers) as pool:
+        for what in ("sequential", "solve"):
+            t0 = time.perf_counter()
+            pool.map(_detail_rows, [(what, edges[k], edges[k + 1]) for k in range(workers)])
+            el = time.perf_counter() - t0
+            split[what] = {"seconds": el, "state_updates_per_s": n / el}
+    out["batch_split"] = split
+    _DETAIL.clear()
+    return out
 
 
 COPY_PROBE_BYTES = 64 * 1024 * 1024 * 4   # read once and written once by the probe copy
@@ -208,6 +289,9 @@ def main():
                     help="f16: x and the iterate stored in binary16 (channel-wise cell), "
                          "float32 arithmetic, tol 1e-3")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-detail", action="store_true",
+                    help="also time the float64 sequential loop and oracle solve on one core "
+                         "and split across the batch over the host's cores (cpu_detail)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 256 MiB device copy first (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -327,6 +411,9 @@ def main():
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.config, mode, smode, args.switch_ratio,
                                             "f16" if half else None)
+    if args.cpu_detail:
+        line["cpu_detail"] = cpu_detail(args.config, mode, smode, args.switch_ratio,
+                                        "f16" if half else None)
     print(json.dumps(line), flush=True)
 
 
