@@ -69,6 +69,12 @@ def _traffic(name, src, launch_bytes_alg):
 CPU_SECONDS = 10.0    # CPU work of the oracle baseline (one thread)
 
 
+def _json_float(v):
+    """v, or its name ("inf", "nan") where strict JSON has no number for it."""
+    import math
+    return float(v) if math.isfinite(v) else str(v)
+
+
 def _cpu_sample(cfg, mode):
     """The bounded sample of a workload the CPU baselines run (B and T)."""
     samples = {3: dict(B=8, T=32768), 2: dict(B=16, T=2048), 4: dict(B=8, T=4096),
@@ -332,7 +338,7 @@ def main():
     def solve(profile):
         return pn.eval(wl["cell"], params, x, s0, mode=mode, tol=wl["tol"],
                        max_iter=wl["max_iter"], damping=wl["damping"], window=wl["window"],
-                       chunk=args.chunk, out=out, workspace=ws, profile=profile,
+                       chunk=args.chunk, out=out, workspace=ws, profile=profile, history=True,
                        bandwidth=wl["bandwidth"], window_mode=wmode, switch_mode=smode,
                        switch_ratio=args.switch_ratio)
 
@@ -352,10 +358,12 @@ def main():
     # about four of them (every n-th steady launch); the launches of a solve
     # are alike, and the timed steps give tens of samples
     stride = max(1, (warm.iters if warm is not None else 0) // 4)
-    results = []
+    results, step_ms = [], []
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        results.append(solve(stride))
+        ts = time.perf_counter()
+        results.append(solve(stride))          # a solve returns once its stream is idle
+        step_ms.append((time.perf_counter() - ts) * 1e3)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) / args.steps * 1e3
@@ -394,6 +402,7 @@ def main():
     line = {
         "metric": METRIC, "value": value, "unit": "state-updates/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "ms_per_step_median": sorted(step_ms)[len(step_ms) // 2],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32 arithmetic, f16 storage" if half else "f32",
         "data": "synthetic (seeded PCG64 draws, no dataset)",
@@ -405,6 +414,7 @@ def main():
                    **({"switch_to": workloads.MODE_NAMES[smode], "switch_ratio": args.switch_ratio,
                        "window_switch_first": last.window_switch[:4]} if smode >= 0 else {}),
                    "iters": last.iters, "window_iters_first": last.window_iters[:4],
+                   "final_residual": _json_float(last.resid_hist[-1]) if last.resid_hist else None,
                    "status": last.status, "parallelism": "single GPU"},
         "roofline": roof,
     }
