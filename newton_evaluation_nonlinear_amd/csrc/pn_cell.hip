@@ -27,7 +27,11 @@
 //     matrix-vector chain.
 // The input projection U x_t (+ bias) does not depend on the iterate and is
 // computed once per sweep.  D is padded to DP (a power of two <= 64) inside
-// LDS; padded rows/columns are kept at zero.
+// LDS; padded rows/columns are kept at zero.  For DP a multiple of 16 the
+// cell is evaluated from matrix-core accumulators with the weights in
+// registers (CellRegs).  In the diagonal modes with few chunks per window a
+// sweep composes its own carries from the chunk maps and, with consecutive
+// windows, takes its own check (CellArgs::fc), so an iteration is one launch.
 
 #include "pn_device.hpp"
 #include "pn_launch.hpp"
