@@ -664,12 +664,15 @@ def test_fused_check_and_carry_launch_paths(chunk, T, window):
 
 
 @pytest.mark.parametrize("kind, D, m", [(pn.CELL_TANH_RNN, 32, 5), (pn.CELL_GRU, 32, 40),
-                                        (pn.CELL_EULER_TANH, 16, 3), (pn.CELL_GRU, 20, 7)])
+                                        (pn.CELL_EULER_TANH, 16, 3), (pn.CELL_GRU, 20, 7),
+                                        (pn.CELL_GRU, 64, 12)])
 @pytest.mark.parametrize("T, chunk", [(2048, 16), (2049, 16), (16, 16)])
 def test_fused_check_chunk_count_limits(kind, D, m, T, chunk):
     # 128 chunks per window (the most an apply sweep composes itself), 129
     # (a carry launch), and a single chunk; input widths below and above D
-    # (register and memory operands of the projection); step damping
+    # (register and memory operands of the projection); step damping.  At D
+    # padded to 64 a workgroup folds the maps before its chunk in 4
+    # segments of up to 32, past the 16 each thread loads ahead of staging.
     rng = np.random.default_rng(900 + D + m)
     params = workloads.random_cell_params(kind, D, m, rng, 1.0)
     B = 2
