@@ -763,8 +763,8 @@ int solve_advancing(SolveCtx& c, const float* x, const float* s0, float* out, in
         if (i == c.max_iter) { *K = i; *status = PN_NOT_CONVERGED; break; }
         const int64_t e_new = std::min<int64_t>(T, a + W);
         // steps entering the window start from its last state: the maps pass
-        // of the matrix cells' tile kernel writes them itself
-        const bool tile_fill = p.matrix_cell && !p.mfma;
+        // of the matrix cells' kernels writes them itself
+        const bool tile_fill = p.matrix_cell;
         if (e_new > e && !tile_fill)
             PN_HIP(launch_fill(out + e * D, T * D, out + (e - 1) * D, T * D, p.B,
                                static_cast<int>(e_new - e), p.D, c.st));

@@ -37,6 +37,23 @@
 
 namespace pn {
 
+// Maps pass of the advancing window: stage Sc rows of the iterate (window
+// rows tq0 ..) into dst (row stride DP).  Rows from ff on are new steps that
+// start from fillrow (the state before them, which this pass does not write)
+// and are stored to s (sgj: the same rows in s).
+template <int NT>
+__device__ __forceinline__ void stage_maps_rows(float* dst, int DP, float* sgj, int D, int Sc, int tq0, int ff,
+                                                const float* fillrow, int tid) {
+    const int nld = max(0, min(Sc, ff - tq0));
+    copy_rows_to_lds<NT>(dst, DP, sgj, D, nld, D, tid);
+    for (int e = tid; e < (Sc - nld) * DP; e += NT) {
+        const int j = nld + e / DP, q = e % DP;
+        const float v = q < D ? fillrow[q] : 0.0f;
+        dst[j * DP + q] = v;
+        if (q < D) sgj[j * D + q] = v;
+    }
+}
+
 constexpr int kCellTanhRnnD = 1;
 constexpr int kCellGruD = 2;
 constexpr int kCellEulerD = 3;
@@ -386,6 +403,9 @@ __global__ __launch_bounds__(SPLIT ? 128 : 64) void dense_pass(CellArgs g) {
     const float* cr = g.carry + ci * D;
     float shat = 0.0f;                       // s^ at the row before the current one (lane row i)
     float* sg = g.s + b * g.ss + static_cast<int64_t>(t0) * D;
+    // maps pass of the advancing window: new steps from window row ff on
+    const int ff = g.Tw - g.fill_rows;
+    const float* fillrow = ff == 0 ? s0 : g.s + b * g.ss + static_cast<int64_t>(ff - 1) * D;
     const float* xg = g.x + b * g.xs + static_cast<int64_t>(t0) * m;
 
     // row t0-1 of the old and the new iterate
@@ -395,7 +415,8 @@ __global__ __launch_bounds__(SPLIT ? 128 : 64) void dense_pass(CellArgs g) {
             if constexpr (PHASE == kPrologue) {
                 po = pn = s0[i];
             } else if constexpr (PHASE == kMaps) {
-                po = pn = c == 0 ? s0[i] : sg[i - D];   // this pass writes no row of s
+                // rows from ff on are new steps (fill_rows): they start from fillrow
+                po = pn = c == 0 ? s0[i] : (t0 - 1 >= ff ? fillrow[i] : sg[i - D]);
             } else {
                 po = (PHASE == kFirst || c == 0) ? s0[i] : g.halo[(g.iter & 1) * HS + (ci - 1) * D + i];
                 shat = cr[i];
@@ -420,6 +441,8 @@ __global__ __launch_bounds__(SPLIT ? 128 : 64) void dense_pass(CellArgs g) {
                 const int q = e % DP;
                 P[DP + e] = q < D ? s0[q] : 0.0f;
             }
+        } else if constexpr (PHASE == kMaps) {
+            stage_maps_rows<64>(P + DP, DP, sg + static_cast<int64_t>(j0) * D, D, Sc, t0 + j0, ff, fillrow, lane);
         } else {
             copy_rows_to_lds<64>(P + DP, DP, sg + static_cast<int64_t>(j0) * D, D, Sc, D, lane);
         }
@@ -704,6 +727,9 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
     const float* cr = g.carry + ci * D;
     float shat[2] = {0.0f, 0.0f};
     float* sg = g.s + b * g.ss + static_cast<int64_t>(t0) * D;
+    // maps pass of the advancing window: new steps from window row ff on
+    const int ff = g.Tw - g.fill_rows;
+    const float* fillrow = ff == 0 ? s0 : g.s + b * g.ss + static_cast<int64_t>(ff - 1) * D;
     const float* xg = g.x + b * g.xs + static_cast<int64_t>(t0) * m;
 
     // row t0-1 of the old and the new iterate (lane: its own row; shat: rows r, 32 + r)
@@ -713,7 +739,7 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
             if constexpr (PHASE == kPrologue) {
                 po = pn = s0[orow];
             } else if constexpr (PHASE == kMaps) {
-                po = pn = c == 0 ? s0[orow] : sg[orow - D];
+                po = pn = c == 0 ? s0[orow] : (t0 - 1 >= ff ? fillrow[orow] : sg[orow - D]);
             } else {
                 po = (PHASE == kFirst || c == 0) ? s0[orow] : g.halo[(g.iter & 1) * HS + (ci - 1) * D + orow];
                 pn = g.undamped ? cr[orow] : po + g.lam * (cr[orow] - po);
@@ -735,6 +761,9 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
                 const int q = e % DP;
                 P[DP + e] = q < D ? s0[q] : 0.0f;
             }
+        } else if constexpr (PHASE == kMaps) {
+            stage_maps_rows<64>(P + DP, DP, sg + static_cast<int64_t>(j0) * D, D, Sc, t0 + j0, ff, fillrow,
+                                threadIdx.x);
         } else {
             copy_rows_to_lds<64>(P + DP, DP, sg + static_cast<int64_t>(j0) * D, D, Sc, D);
         }
