@@ -183,8 +183,11 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
         p.NC = static_cast<int>((p.W + p.L - 1) / p.L);
         p.nblocks = p.NC * p.B;
         // with few chunks per row, composing a chunk's carry in its own sweep
-        // costs less than a carry launch
-        if (!p.dense && p.NC <= kFcMaxChunks) p.fc = p.advancing ? kFcCarry : (kFcCarry | kFcCheck);
+        // costs less than a carry launch; past kFcMaxBlocks workgroups their
+        // residual atomics would contend on the 16 slots, while a carry
+        // launch costs little next to such a sweep
+        if (!p.dense && p.NC <= kFcMaxChunks && static_cast<int64_t>(p.B) * p.NC <= kFcMaxBlocks)
+            p.fc = p.advancing ? kFcCarry : (kFcCarry | kFcCheck);
         if (cell_pass_lds_bytes(p.kind, p.DP, p.dense, p.L, p.m) > 160 * 1024)
             return fail(PN_EUNSUPPORTED, "chunk of %d steps needs too much LDS for D=%d, m=%d", p.L, p.D, p.m);
     }

@@ -132,6 +132,7 @@ struct CellArgs {
 };
 
 constexpr int kFcMaxChunks = 128;
+constexpr int kFcMaxBlocks = 16384;      // workgroups of one sweep (B x chunks)
 constexpr int kFcCarry = 1, kFcCheck = 2;
 
 struct CarryArgs {

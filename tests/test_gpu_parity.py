@@ -683,6 +683,19 @@ def test_fused_check_chunk_count_limits(kind, D, m, T, chunk):
         _parity(wl, mode, chunk=chunk)
 
 
+@pytest.mark.parametrize("B", [128, 130])
+def test_fused_check_workgroup_limit(B):
+    # 128 chunks over 128 rows is the most workgroups an in-sweep check
+    # takes (16384); 130 rows go back to the carry launch
+    rng = np.random.default_rng(950 + B)
+    D, m, T = 16, 8, 1024
+    params = workloads.random_cell_params(pn.CELL_GRU, D, m, rng, 1.0)
+    wl = dict(cfg=0, cell=pn.CELL_GRU, D=D, m=m, B=B, T=T, tol=1e-5, damping=1.0, window=0,
+              max_iter=T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32))
+    _parity(wl, Q, chunk=8)
+
+
 def test_fused_check_stop_rules():
     # the three stop outcomes as every workgroup of a sweep takes them
     wl = _case(5, B=2, T=2048)
