@@ -349,14 +349,19 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    warm = None
-    for _ in range(args.warmup):
-        warm = solve(False)
-    torch.cuda.synchronize()
     # Timing events cost several microseconds per timed launch (about 6.5 us
     # on a 15 us launch), so a solve of many launches times a sample of
     # about four of them (every n-th steady launch); the launches of a solve
-    # are alike, and the timed steps give tens of samples
+    # are alike, and the timed steps give tens of samples.  The last warm-up
+    # solve (from the second on) times launches too, so that the events
+    # exist before the timed region.
+    warm = None
+    for k in range(args.warmup):
+        if k == args.warmup - 1 and warm is not None:
+            solve(max(1, warm.iters // 4))
+        else:
+            warm = solve(False)
+    torch.cuda.synchronize()
     stride = max(1, (warm.iters if warm is not None else 0) // 4)
     results, step_ms = [], []
     t0 = time.perf_counter()
