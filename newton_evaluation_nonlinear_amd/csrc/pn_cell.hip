@@ -827,7 +827,30 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
         const float lam = g.lam;
         const bool und = g.undamped != 0;
         if constexpr (!DENSE) {
-            if (tid < D) {
+            if (g.mode == kJacobi) {
+                // A~ = 0: row j of s^ is v_{j-1} itself, so the rows are
+                // independent of one another.  Row 0 (the carry) and, with a
+                // successor, row Lc (that chunk's carry) come from the values
+                // thread i holds for state i.
+                const int jl = has_next ? Lc - 1 : Lc;       // rows 1 .. jl from V
+                for (int e = tid; e < jl * PS; e += kThreads) {
+                    const int j = 1 + e / PS, i = e % PS;
+                    float val = 0.0f;
+                    if (i < D) {
+                        const float sh = V[(j - 1) * DP + i], so = P[j * PS + i];
+                        val = und ? sh : so + lam * (sh - so);
+                    }
+                    N[j * PS + i] = val;
+                }
+                if (tid < PS) {
+                    const bool lv = tid < D;
+                    N[tid] = lv ? (und ? c_first : P[tid] + lam * (c_first - P[tid])) : 0.0f;
+                    if (has_next) {
+                        const float so = P[Lc * PS + tid];
+                        N[Lc * PS + tid] = lv ? (und ? c_next : so + lam * (c_next - so)) : 0.0f;
+                    }
+                }
+            } else if (tid < D) {
                 float shat = c_first;
                 N[tid] = und ? shat : P[tid] + lam * (shat - P[tid]);
                 // the last row of a chunk that has a successor is that
@@ -899,7 +922,13 @@ __device__ __forceinline__ bool cell_tile(const CellArgs& g, int c, int b, float
     evaluate(N, N, fb);
     __syncthreads();
     if constexpr (!DENSE) {
-        if (tid < D) {
+        if (tid < D && g.mode == kJacobi) {
+            // A~ = 0: the chunk map is y -> v at the chunk's last step
+            const size_t mo = (PHASE == kPrologue ? 0 : PHASE == kMaps ? (g.iter & 1) : ((g.iter + 1) & 1)) *
+                              g.mstride;
+            g.aggA[mo + ci * D + tid] = 0.0f;
+            g.aggB[mo + ci * D + tid] = V[(Lc - 1) * DP + tid];
+        } else if (tid < D) {
             float A = 1.0f, Bc = 0.0f;
 #pragma unroll 8
             for (int j = 0; j < Lc; ++j) {
