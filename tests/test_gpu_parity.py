@@ -790,3 +790,22 @@ def test_cfg6_full_banded():
 @pytest.mark.slow
 def test_cfg5_full_damped_windows():
     _parity(_case(5), Q)
+
+
+# ---------------------------------------------------------------- per-call measurements
+@pytest.mark.parametrize("cfg, mode", [(3, Q), (2, Q), (4, N), (7, Q)])
+def test_profile_times_steady_launches(cfg, mode):
+    # every steady apply launch, or every third (profile_stride), is timed;
+    # launches that ran carry algorithmic bytes; timing changes no result
+    wl = _case(cfg, B=2, T=1024)
+    full = run_gpu(wl, mode, profile=True)
+    p = full.profile
+    assert p["apply_launches"] >= 1 and p["apply_ms"] > 0 and p["total_ms"] >= p["apply_ms"]
+    if full.iters >= 2:
+        assert p["apply_bytes"] > 0
+    sampled = run_gpu(wl, mode, profile=3)
+    assert sampled.iters == full.iters
+    assert sampled.profile["apply_launches"] == -(-p["apply_launches"] // 3)
+    np.testing.assert_array_equal(sampled.out_np, full.out_np)
+    plain = run_gpu(wl, mode)
+    np.testing.assert_array_equal(plain.out_np, full.out_np)
