@@ -937,7 +937,8 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     SolveCtx c{&p, st, ws, res, params, tol, o ? o->damping : 1.0f, max_iter, &tm, &hist,
                o ? o->switch_ratio : 0.0f, o ? o->switch_damping : 0.0f};
     if (p.matrix_cell)
-        PN_HIP(launch_prep_weights(p.kind, params, reinterpret_cast<float*>(ws + p.off_w), p.D, p.DP, p.m, st));
+        PN_HIP(launch_prep_weights(p.kind, params, reinterpret_cast<float*>(ws + p.off_w), p.D, p.DP, p.m,
+                                   !p.mfma || (has2 && !p2.mfma), st));
     size_t ev_first = 0;
     if (tm.on) { rc = record(c, &ev_first); if (rc) return rc; }
     int total = 0, overall = PN_OK;

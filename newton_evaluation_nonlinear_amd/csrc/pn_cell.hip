@@ -144,12 +144,12 @@ __global__ __launch_bounds__(kThreads) void prep_kcopy_kernel(int kind, float* _
     }
 }
 
-hipError_t launch_prep_weights(int kind, const float* params, float* w, int D, int DP, int m,
+hipError_t launch_prep_weights(int kind, const float* params, float* w, int D, int DP, int m, bool with_kcopy,
                                hipStream_t st) {
     const int n = static_cast<int>(prepared_weight_floats(kind, DP, m));
     const int blocks = std::min((n + kThreads - 1) / kThreads, 1024);
     prep_weights_kernel<<<blocks, kThreads, 0, st>>>(kind, params, w, D, DP, m, n);
-    if (DP % 16 == 0) {
+    if (with_kcopy && DP % 16 == 0) {
         const int nk = static_cast<int>(prepared_total_floats(kind, DP, m) - kcopy_offset(kind, DP, m));
         prep_kcopy_kernel<<<std::min((nk + kThreads - 1) / kThreads, 1024), kThreads, 0, st>>>(kind, w, DP, m, nk);
     }

@@ -172,7 +172,8 @@ hipError_t launch_fill_half(void* out, int64_t ss, const float* s0, int64_t s0s,
 hipError_t launch_fill(float* out, int64_t ss, const float* s0, int64_t s0s, int B, int Tw, int D,
                        hipStream_t st);
 
-hipError_t launch_prep_weights(int kind, const float* params, float* w, int D, int DP, int m,
+// with_kcopy: also write the k-contiguous copy (read by the tile kernel only)
+hipError_t launch_prep_weights(int kind, const float* params, float* w, int D, int DP, int m, bool with_kcopy,
                                hipStream_t st);
 __host__ __device__ size_t prepared_weight_floats(int kind, int DP, int m);
 // The whole prepared region in the workspace: the layout above and, for DP a
