@@ -730,6 +730,13 @@ def test_deterministic_bitwise():
     a = run_gpu(wl, N)
     b = run_gpu(wl, N)
     assert a.iters == b.iters and np.array_equal(a.out_np, b.out_np)
+    # the in-sweep check and carries: atomic maxima and a fixed fold order
+    for cfg, T in ((2, 2048), (5, 4096)):
+        wl = _case(cfg, B=4, T=T)
+        a = run_gpu(wl, Q)
+        b = run_gpu(wl, Q)
+        assert a.window_iters == b.window_iters and np.array_equal(a.out_np, b.out_np)
+        assert a.resid_hist == b.resid_hist
 
 
 # ---------------------------------------------------------------- full sizes
