@@ -705,6 +705,10 @@ def test_fused_check_stop_rules():
     _parity(wl, Q, max_iter=3, tol=0.0)
     g = run_gpu(wl, Q, max_iter=3, tol=0.0)
     assert g.status == pn.NOT_CONVERGED and g.window_iters[:2] == [3, 3]
+    g = run_gpu(wl, Q, max_iter=0, tol=0.0)
+    assert g.status == pn.NOT_CONVERGED and g.iters == 0 and g.window_iters[:2] == [0, 0]
+    ref = run_oracle(wl, Q, max_iter=0, tol=0.0)
+    np.testing.assert_array_equal(g.out_np, ref.s.astype(np.float32))
     bad = dict(wl)
     bad["x"] = wl["x"].copy()
     bad["x"][0, 1500, 5] = np.nan
