@@ -35,12 +35,16 @@
  * Memory conventions (all functions):
  *   - float pointers named params, x, s0, out, A, b are DEVICE pointers to
  *     C-contiguous float32 arrays owned by the caller; the library never
- *     frees them.  out must not alias any input.
+ *     frees them.
  *   - x is [B, T, m]; s0 is [B, D]; out is [B, T, D] and receives s_1..s_T.
  *   - pointers named *_hist, *_iters, iters_out, profile are HOST pointers.
  *   - calls block until the result is complete on the device.
- *   - on a negative (error) status nothing is written to out; the message
- *     is available from pn_last_error() on the calling thread.
+ *   - on a negative (error) status the message is available from
+ *     pn_last_error() on the calling thread.  Argument, size and workspace
+ *     errors are found before any device work and leave out untouched; once
+ *     kernels have been enqueued (PN_EHIP from a failed launch, copy or
+ *     wait), out is unspecified.
+ *   - out must not share a byte with x, s0 or params (PN_EINVAL otherwise).
  *   - thread-safe when concurrent calls use distinct streams and workspaces.
  */
 #ifndef PN_H
@@ -217,8 +221,10 @@ int pn_eval_ex(const pn_cell* cell, const float* params, const float* x, const f
                float* out, int32_t* iters_out, const pn_opts* opts);
 
 /* Bytes of workspace pn_eval_ex (and pn_eval_f16) needs for this problem
- * with these options (uses opts->window and opts->chunk; opts may be NULL).  Returns 0 and sets
- * the last error for invalid or unsupported arguments. */
+ * with these options (opts may be NULL).  The size depends on the window and
+ * also on the chunk, the mode switch and the bandwidth, so the whole option
+ * block is taken rather than the window alone.  Returns 0 and sets the last
+ * error for invalid or unsupported arguments. */
 size_t pn_workspace_bytes(const pn_cell* cell, int64_t B, int64_t T, int64_t D,
                           int32_t mode, const pn_opts* opts);
 

@@ -116,6 +116,50 @@ def _dev_f32(t, name, dtype=torch.float32):
     return t.data_ptr()
 
 
+def param_count(cell_kind, D, m):
+    """Length of the flat parameter vector of a cell (layouts in include/pn.h)."""
+    k = int(cell_kind)
+    if k == CELL_DIAG_TANH:
+        return D
+    if k == CELL_TANH_RNN:
+        return D * D + D * m + D
+    if k == CELL_GRU:
+        return 3 * D * m + 3 * D * D + 6 * D
+    if k == CELL_EULER_TANH:
+        return D * D + D * m + 2 * D
+    raise ValueError(f"unknown cell kind {cell_kind}")
+
+
+def _check_shapes(cell_kind, params, x, s0, out, sdt):
+    """Shapes, lengths and devices the C side cannot see; raises ValueError
+    before any launch."""
+    for name, t in (("params", params), ("x", x), ("s0", s0)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+    if x.dim() != 3:
+        raise ValueError(f"x must be [B, T, m], got shape {tuple(x.shape)}")
+    if s0.dim() != 2:
+        raise ValueError(f"s0 must be [B, D], got shape {tuple(s0.shape)}")
+    B, T, m = x.shape
+    D = s0.shape[1]
+    if s0.shape[0] != B:
+        raise ValueError("x and s0 disagree on B")
+    need = param_count(cell_kind, D, m)
+    if params.numel() != need:
+        raise ValueError(f"params holds {params.numel()} values; cell kind {int(cell_kind)} with "
+                         f"D={D}, m={m} needs {need}")
+    if out is not None:
+        if not isinstance(out, torch.Tensor):
+            raise TypeError("out must be a torch tensor")
+        if tuple(out.shape) != (B, T, D):
+            raise ValueError(f"out must have shape {(B, T, D)}, got {tuple(out.shape)}")
+        if out.dtype != sdt:
+            raise ValueError(f"out must be {sdt}")
+    devs = {t.device for t in (params, x, s0) + ((out,) if out is not None else ())}
+    if len(devs) != 1:
+        raise ValueError(f"params, x, s0 and out must live on one device, got {sorted(map(str, devs))}")
+
+
 def _stream_ptr(device):
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -183,17 +227,16 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     Returns a ``Result`` (unpacks as ``out, iters, status``).  Negative
     library statuses raise ``PnError``.
     """
+    half = isinstance(x, torch.Tensor) and x.dtype == torch.float16
+    sdt = torch.float16 if half else torch.float32
+    _check_shapes(cell_kind, params, x, s0, out, sdt)
     B, T, m = x.shape
     D = s0.shape[1]
-    if s0.shape[0] != B:
-        raise ValueError("x and s0 disagree on B")
     W = T if window in (0, None) else int(window)
     advancing = int(window_mode) == WINDOW_ADVANCING
     if max_iter is None:
         max_iter = T if advancing else W
     dev = x.device
-    half = x.dtype == torch.float16
-    sdt = torch.float16 if half else torch.float32
     if out is None:
         out = torch.empty((B, T, D), dtype=sdt, device=dev)
     c = Cell(int(cell_kind), int(m))
@@ -257,7 +300,18 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
 
 def affine_scan(A, b, s0, dense=False, chunk=0, out=None):
     """out_t = A_t out_{t-1} + b_t (A diagonal [B,T,D] or dense [B,T,D,D])."""
+    if b.dim() != 3:
+        raise ValueError(f"b must be [B, T, D], got shape {tuple(b.shape)}")
     B, T, D = b.shape
+    want = (B, T, D, D) if dense else (B, T, D)
+    if tuple(A.shape) != want:
+        raise ValueError(f"A must have shape {want}, got {tuple(A.shape)}")
+    if tuple(s0.shape) != (B, D):
+        raise ValueError(f"s0 must have shape {(B, D)}, got {tuple(s0.shape)}")
+    if out is not None and tuple(out.shape) != (B, T, D):
+        raise ValueError(f"out must have shape {(B, T, D)}, got {tuple(out.shape)}")
+    if len({t.device for t in (A, b, s0) + ((out,) if out is not None else ())}) != 1:
+        raise ValueError("A, b, s0 and out must live on one device")
     if out is None:
         out = torch.empty_like(b)
     o = make_opts(chunk=chunk, stream=_stream_ptr(b.device))

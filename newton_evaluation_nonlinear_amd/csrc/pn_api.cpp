@@ -257,9 +257,27 @@ int make_plans(Plan& p, Plan& p2, bool* has2, const pn_cell* cell, int64_t B, in
     return PN_OK;
 }
 
+// Number of floats in the flat parameter vector of a cell (layouts in pn.h).
+int64_t param_floats(int kind, int64_t D, int64_t m) {
+    switch (kind) {
+        case PN_CELL_DIAG_TANH: return D;
+        case PN_CELL_TANH_RNN: return D * D + D * m + D;
+        case PN_CELL_GRU: return 3 * D * m + 3 * D * D + 6 * D;
+        default: return D * D + D * m + 2 * D;   // PN_CELL_EULER_TANH
+    }
+}
+
+// [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + static_cast<uint64_t>(nb) && pb < pa + static_cast<uint64_t>(na);
+}
+
+// es: bytes per element of x and out (4 float, 2 binary16); 0 skips the
+// aliasing check (sizing calls pass placeholder pointers).
 int validate(const pn_cell* cell, const float* params, const float* x, const float* s0, int64_t B,
              int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter, const float* out,
-             const int32_t* iters_out, const pn_opts* o) {
+             const int32_t* iters_out, const pn_opts* o, int es = 4) {
     if (!cell) return fail(PN_EINVAL, "cell is NULL");
     if (!iters_out) return fail(PN_EINVAL, "iters_out is NULL");
     if (B < 0 || T < 0 || D < 0) return fail(PN_EINVAL, "negative size (B=%lld T=%lld D=%lld)",
@@ -308,6 +326,16 @@ int validate(const pn_cell* cell, const float* params, const float* x, const flo
     if (B > 65535) return fail(PN_EUNSUPPORTED, "B must be <= 65535");
     if (T >= (int64_t(1) << 31) || D >= (int64_t(1) << 24) || cell->input_dim >= (1 << 24))
         return fail(PN_EUNSUPPORTED, "size too large");
+    if (es > 0) {
+        // out is written while the inputs are still read: it must not share
+        // a byte with any of them
+        const int64_t nout = B * T * D * es;
+        if (overlaps(out, nout, x, B * T * cell->input_dim * es))
+            return fail(PN_EINVAL, "out overlaps x");
+        if (overlaps(out, nout, s0, B * D * 4)) return fail(PN_EINVAL, "out overlaps s0");
+        if (overlaps(out, nout, params, param_floats(cell->kind, D, cell->input_dim) * 4))
+            return fail(PN_EINVAL, "out overlaps params");
+    }
     return PN_OK;
 }
 
@@ -886,12 +914,31 @@ int solve_persistent(SolveCtx& c, const float* x, const float* s0, float* out, i
     return PN_OK;
 }
 
+// Frees a workspace the library allocated for one call on every exit path.
+struct OwnedWorkspace {
+    void* p = nullptr;
+    hipStream_t st = nullptr;
+    ~OwnedWorkspace() {
+        if (p) {
+            (void)hipFreeAsync(p, st);
+            (void)hipStreamSynchronize(st);
+        }
+    }
+    hipError_t release() {
+        void* q = p;
+        p = nullptr;
+        hipError_t e = hipFreeAsync(q, st);
+        hipError_t e2 = hipStreamSynchronize(st);
+        return e != hipSuccess ? e : e2;
+    }
+};
+
 int eval_impl(const pn_cell* cell, const float* params, const float* x, const float* s0, int64_t B,
               int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter, float* out,
               int32_t* iters_out, const pn_opts* o, bool half = false) {
     g_err.clear();
     g_launch_timing = LaunchTiming{};     // no request left over from a failed call
-    int rc = validate(cell, params, x, s0, B, T, D, mode, tol, max_iter, out, iters_out, o);
+    int rc = validate(cell, params, x, s0, B, T, D, mode, tol, max_iter, out, iters_out, o, half ? 2 : 4);
     if (rc != PN_OK) return rc;
     if (half) {
         if (cell->kind != PN_CELL_DIAG_TANH)
@@ -921,14 +968,15 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     if (rc != PN_OK) return rc;
     hipStream_t st = o ? static_cast<hipStream_t>(o->stream) : nullptr;
     char* ws = nullptr;
-    bool own_ws = false;
+    OwnedWorkspace own;
     if (o && o->workspace) {
         ws = static_cast<char*>(o->workspace);
     } else {
         void* q = nullptr;
         PN_HIP(hipMallocAsync(&q, p.total, st));
+        own.p = q;
+        own.st = st;
         ws = static_cast<char*>(q);
-        own_ws = true;
     }
     Timing tm;
     tm.on = o && o->profile;
@@ -954,10 +1002,7 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     if (p.advancing) {
         int K = 0, status = PN_OK;
         rc = solve_advancing(c, x, s0, out, T, &K, &status, &accepted);
-        if (rc != PN_OK) {
-            if (own_ws) { (void)hipFreeAsync(ws, st); (void)hipStreamSynchronize(st); }
-            return rc;
-        }
+        if (rc != PN_OK) return rc;
         total = K;
         wit.push_back(K);
         overall = status;
@@ -971,10 +1016,7 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
         const int64_t s0s = w0 == 0 ? D : T * D;
         int K = 0, status = PN_OK, swi = -1;
         rc = solve_window(c, xw, T * m, sw, T * D, s0w, s0s, Tw, &K, &status, has2 ? &p2 : nullptr, &swi);
-        if (rc != PN_OK) {
-            if (own_ws) { (void)hipFreeAsync(ws, st); (void)hipStreamSynchronize(st); }
-            return rc;
-        }
+        if (rc != PN_OK) return rc;
         total += K;
         wit.push_back(K);
         wsw.push_back(swi);
@@ -984,10 +1026,7 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     size_t ev_last = 0;
     if (tm.on) { rc = record(c, &ev_last); if (rc) return rc; }
     PN_HIP(hipStreamSynchronize(st));
-    if (own_ws) {
-        PN_HIP(hipFreeAsync(ws, st));
-        PN_HIP(hipStreamSynchronize(st));
-    }
+    if (own.p) PN_HIP(own.release());
     *iters_out = total;
     if (o) {
         for (int64_t k = 0; k < o->window_iters_len && k < static_cast<int64_t>(wit.size()); ++k)
@@ -1065,7 +1104,7 @@ size_t pn_workspace_bytes(const pn_cell* cell, int64_t B, int64_t T, int64_t D, 
     g_err.clear();
     int32_t dummy = 0;
     static const float kDummy = 0.0f;
-    int rc = validate(cell, &kDummy, &kDummy, &kDummy, B, T, D, mode, 0.0f, 0, &kDummy, &dummy, opts);
+    int rc = validate(cell, &kDummy, &kDummy, &kDummy, B, T, D, mode, 0.0f, 0, &kDummy, &dummy, opts, 0);
     if (rc != PN_OK) return 0;
     if (B == 0 || T == 0 || D == 0) return kAlign;
     Plan p, p2;

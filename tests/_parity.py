@@ -3,18 +3,22 @@
 Acceptance for one solve (status, counts, trajectory, residual):
   1. status equals the oracle's (float64 oracle; for a non-finite outcome the
      float32 oracle, whose arithmetic is the library's);
-  2. updates per window equal the oracle's.  The count is an integer decided
-     by a floating-point comparison r <= tol; where the oracle's residual at
-     the deciding iteration lies within the ambiguity band of tol (2% of tol
-     plus two float32 ulps of the state scale), the float32 decision may
+  2. updates per window equal the float64 oracle's.  The count is an integer
+     decided by a floating-point comparison r <= tol; where the oracle's
+     residual at the deciding iteration lies within the ambiguity band of tol
+     (2% of tol plus two float32 ulps of the state scale, plus, where that
+     does not cover it, the float32 rounding of the residual at that check as
+     the oracle itself measures it in float32), the float32 decision may
      legitimately land on the other side, so a count one off is accepted
-     there.  Where the float64 count differs by more, the
-     decision is taken in the library's precision: the counts must then match
-     the float32 oracle (same band).  This happens only on runs with huge
-     transients (Picard on the GRU reaches 1e20+), where the precision itself
-     moves the count.  The trajectory is then compared with the float64 oracle
-     run for exactly the library's counts (both are valid stopping points; the
-     trajectory at the chosen count is what stays unique);
+     there (every such use is logged, see ``BAND_LOG``); with
+     ``exact=True`` no band is allowed at all.  A case may opt in, with
+     ``f32_count=True``, to taking the count decision in the library's
+     precision (the float32 oracle, same band) where the float64 count
+     differs by more: only runs whose iterates pass through huge transients
+     (Picard on the GRU, 1e20 and more) do, because there the precision
+     itself moves the count.  The trajectory is compared with the float64
+     oracle run for exactly the library's counts (both are valid stopping
+     points; the trajectory at the chosen count is what stays unique);
   3. max |s_gpu - s_oracle| <= 1e-4 * max(1, max |s_oracle|);
   4. the float64 residual of s_gpu, recomputed by the oracle, is <= tol + 1e-6
      for converged runs, and the library's own reported residual is <= tol.
@@ -34,6 +38,11 @@ COUNT_BAND = 0.02          # relative part of the ambiguity band around tol
 ULP1 = 2.0 ** -23          # float32 spacing at 1.0
 
 _oracle_cache = {}
+
+# Every acceptance that needed the one-off band or the float32 count
+# reference: (label, mode, kind, library counts, oracle counts).  conftest.py
+# prints it at the end of the session.
+BAND_LOG = []
 
 
 def to_dev(wl):
@@ -108,16 +117,20 @@ def _windows(T, W):
     return [(w0, min(T, w0 + W)) for w0 in range(0, T, W)]
 
 
-def _counts_within_band(gw, ref, tol):
+def _counts_within_band(gw, ref, tol, ref32=None):
     """Counts equal, or one off where ref's residual at the deciding iteration
     lies within the ambiguity band of tol: COUNT_BAND relative, plus two float32
     ulps of the state scale, the resolution at which a float32 residual
-    |s_t - f_t(s_{t-1})| of states of that size can be computed at all."""
+    |s_t - f_t(s_{t-1})| of states of that size can be computed at all.  With
+    ref32 (the same solve in float32, forced to ref's counts) the band also
+    takes |r32 - r64| at that check: the measured rounding of a float32
+    residual whose D-term products move it by more than two ulps (wide D at
+    tight tol)."""
     if len(gw) != len(ref.window_iters):
         return False
     finite = ref.s[np.isfinite(ref.s)]
     scale = max(1.0, float(np.max(np.abs(finite)))) if finite.size else 1.0
-    band = COUNT_BAND * tol + 2 * ULP1 * scale
+    base = COUNT_BAND * tol + 2 * ULP1 * scale
     for w, (kg, ko) in enumerate(zip(gw, ref.window_iters)):
         if kg == ko:
             continue
@@ -128,6 +141,9 @@ def _counts_within_band(gw, ref, tol):
         r = h[k] if k < len(h) else None
         if r is None:
             return False
+        band = base
+        if ref32 is not None and w < len(ref32.hist) and k < len(ref32.hist[w]):
+            band += abs(float(ref32.hist[w][k]) - float(r))
         if kg > ko and not r >= tol - band:
             return False
         if kg < ko and not r <= tol + band:
@@ -161,9 +177,20 @@ def _follow_switch(wl, mode, gpu, ref, tol, max_iter, damping, window, msg):
     return forced, gsw
 
 
+def _rounding_reference(wl, mode, ref, tol, max_iter, damping, window, fsw):
+    """The float64 oracle's solve redone in float32 with the same counts, so
+    that its residual history measures float32 rounding at every check."""
+    return run_oracle(wl, mode, tol=tol, max_iter=max_iter, damping=damping, window=window,
+                      dtype=np.float32, force_iters=list(ref.window_iters), force_switch=fsw)
+
+
 def check_parity(wl, mode, gpu, ref, tol=None, window=None, damping=None, max_iter=None,
-                 label=""):
-    """Apply the acceptance rules; returns the oracle result the trajectory was compared with."""
+                 label="", exact=False, f32_count=False):
+    """Apply the acceptance rules; returns the oracle result the trajectory was compared with.
+
+    exact: the per-window counts must equal the float64 oracle's, no band.
+    f32_count: where the float64 count differs beyond the band, hold the
+    count to the float32 oracle instead (transient-dominated runs only)."""
     tol = wl["tol"] if tol is None else tol
     window = wl["window"] if window is None else window
     damping = wl["damping"] if damping is None else damping
@@ -179,14 +206,23 @@ def check_parity(wl, mode, gpu, ref, tol=None, window=None, damping=None, max_it
     cmp_ref = ref
     if gw != list(ref.window_iters):
         assert len(gw) == nw, msg
-        if not _counts_within_band(gw, ref, tol):
-            # The count differs beyond the tolerance band: take the decision in
-            # the library's precision (float32 oracle) as the count reference.
+        assert not exact, f"{msg}: counts must equal the float64 oracle's exactly"
+        if _counts_within_band(gw, ref, tol):
+            BAND_LOG.append((label, mode, "one-off band", gw, list(ref.window_iters)))
+        elif _counts_within_band(gw, ref, tol, _rounding_reference(wl, mode, ref, tol, max_iter, damping,
+                                                                   window, fsw)):
+            BAND_LOG.append((label, mode, "one-off band with measured float32 rounding", gw,
+                             list(ref.window_iters)))
+        else:
+            assert f32_count, f"{msg}: counts differ from the float64 oracle beyond the band"
+            # Transient-dominated run: the decision is taken in the library's
+            # precision (float32 oracle) as the count reference.
             ref32 = run_oracle(wl, mode, tol=tol, max_iter=max_iter, damping=damping,
                                window=window, dtype=np.float32, force_switch=fsw)
             msg += f" float32-oracle(status={ref32.status}, win={ref32.window_iters[:8]})"
             assert ref32.status == gpu.status, msg
             assert _counts_within_band(gw, ref32, tol), msg
+            BAND_LOG.append((label, mode, "float32 count reference", gw, list(ref.window_iters)))
         cmp_ref = run_oracle(wl, mode, tol=tol, max_iter=max_iter, damping=damping, window=window,
                              force_iters=gw, force_switch=fsw)
     s_ref = cmp_ref.s

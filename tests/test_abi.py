@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import newton_evaluation_nonlinear_amd as pn
 
@@ -34,14 +35,20 @@ def test_version_and_last_error():
     assert pn.last_error() == ""
 
 
+# Placeholder device addresses, 4 GiB apart so that no two arrays overlap
+# (nothing is dereferenced: every call below fails or returns before device work).
+FAKE = {"params": 1 << 32, "x": 2 << 32, "s0": 3 << 32, "out": 4 << 32}
+
+
 def _eval_raw(kind=pn.CELL_TANH_RNN, m=3, B=2, T=5, D=4, mode=pn.NEWTON, tol=1e-5, max_iter=5,
-              ptr=1, opts=None, iters=True):
+              ptr=1, opts=None, iters=True, addrs=None, entry="pn_eval_ex"):
     c = pn.Cell(kind, m)
     it = ctypes.c_int32(-7)
-    p = ctypes.c_void_p(ptr) if ptr else None
-    rc = pn.lib().pn_eval_ex(ctypes.byref(c), p, p, p, B, T, D, mode, tol, max_iter, p,
-                             ctypes.byref(it) if iters else None,
-                             ctypes.byref(opts) if opts is not None else None)
+    a = dict(FAKE, **(addrs or {}))
+    p = {k: (ctypes.c_void_p(v) if ptr else None) for k, v in a.items()}
+    rc = getattr(pn.lib(), entry)(ctypes.byref(c), p["params"], p["x"], p["s0"], B, T, D, mode, tol,
+                                  max_iter, p["out"], ctypes.byref(it) if iters else None,
+                                  ctypes.byref(opts) if opts is not None else None)
     return rc, it.value
 
 
@@ -130,25 +137,25 @@ def test_switch_options():
 def test_f16_entry_checks():
     c = pn.Cell(pn.CELL_TANH_RNN, 3)
     it = ctypes.c_int32(0)
-    p = ctypes.c_void_p(0x1000)
+    pp, px, ps, po = (ctypes.c_void_p(FAKE[k]) for k in ("params", "x", "s0", "out"))
     L = pn.lib()
-    assert L.pn_eval_f16(ctypes.byref(c), p, p, p, 2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
-                         ctypes.byref(it), None) == pn.EUNSUPPORTED
+
+    def call(cell, x=px, B=2, opts=None):
+        return L.pn_eval_f16(ctypes.byref(cell), pp, x, ps, B, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, po,
+                             ctypes.byref(it), ctypes.byref(opts) if opts is not None else None)
+
+    assert call(c) == pn.EUNSUPPORTED
     c = pn.Cell(pn.CELL_DIAG_TANH, 4)
-    o = pn.make_opts(window=2)
-    assert L.pn_eval_f16(ctypes.byref(c), p, p, p, 2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
-                         ctypes.byref(it), ctypes.byref(o)) == pn.EUNSUPPORTED
-    o = pn.make_opts(window_mode=pn.WINDOW_ADVANCING)
-    assert L.pn_eval_f16(ctypes.byref(c), p, p, p, 2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
-                         ctypes.byref(it), ctypes.byref(o)) == pn.EUNSUPPORTED
-    o = pn.make_opts(switch_mode=pn.QUASI_NEWTON, switch_damping=0.5)
-    assert L.pn_eval_f16(ctypes.byref(c), p, p, p, 2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
-                         ctypes.byref(it), ctypes.byref(o)) == pn.EUNSUPPORTED
-    assert L.pn_eval_f16(ctypes.byref(c), p, p, p, -2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
-                         ctypes.byref(it), None) == pn.EINVAL
-    odd = ctypes.c_void_p(0x1002)    # pairs of binary16 values need 4-byte alignment
-    assert L.pn_eval_f16(ctypes.byref(c), p, odd, p, 2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5, p,
-                         ctypes.byref(it), None) == pn.EINVAL
+    assert call(c, opts=pn.make_opts(window=2)) == pn.EUNSUPPORTED
+    assert call(c, opts=pn.make_opts(window_mode=pn.WINDOW_ADVANCING)) == pn.EUNSUPPORTED
+    assert call(c, opts=pn.make_opts(switch_mode=pn.QUASI_NEWTON, switch_damping=0.5)) == pn.EUNSUPPORTED
+    assert call(c, B=-2) == pn.EINVAL
+    # pairs of binary16 values need 4-byte alignment
+    assert call(c, x=ctypes.c_void_p(FAKE["x"] + 2)) == pn.EINVAL
+    # out in binary16 covers 2 bytes per state: [2,5,4] -> 80 bytes
+    assert L.pn_eval_f16(ctypes.byref(c), pp, px, ps, 2, 5, 4, pn.QUASI_NEWTON, 1e-3, 5,
+                         ctypes.c_void_p(FAKE["x"] + 76), ctypes.byref(it), None) == pn.EINVAL
+    assert "overlaps x" in pn.last_error()
 
 
 def test_euler_cell_sizes():
@@ -215,3 +222,42 @@ def test_undersized_workspace_is_rejected_before_any_device_work():
     rc, _ = _eval_raw(kind=pn.CELL_GRU, m=8, B=64, T=2048, D=16, mode=pn.QUASI_NEWTON, opts=o)
     assert rc == pn.EWORKSPACE
     assert "smaller" in pn.last_error()
+
+
+@pytest.mark.parametrize("inp", ["x", "s0", "params"])
+def test_out_overlapping_an_input_is_rejected(inp):
+    # out [B,T,D] = [2,5,4] floats: starting inside the input, at its first
+    # byte, or ending on its first byte all overlap; one byte past does not
+    for delta, bad in ((0, True), (-(2 * 5 * 4 * 4) + 1, True), (-(2 * 5 * 4 * 4), False), (8, True)):
+        rc, _ = _eval_raw(addrs={"out": FAKE[inp] + delta})
+        if bad:
+            assert rc == pn.EINVAL and "overlaps " + inp in pn.last_error(), (inp, delta)
+        else:
+            assert not (rc == pn.EINVAL and "overlaps" in pn.last_error()), (inp, delta)
+
+
+def test_python_binding_checks_shapes_before_any_launch():
+    # CPU tensors: the shape, length and device checks come first, so these
+    # raise ValueError without a GPU
+    D, m, B, T = 4, 3, 2, 5
+    x = torch.zeros(B, T, m)
+    s0 = torch.zeros(B, D)
+    good = torch.zeros(pn.param_count(pn.CELL_GRU, D, m))
+    assert pn.param_count(pn.CELL_GRU, D, m) == 3 * D * m + 3 * D * D + 6 * D
+    assert pn.param_count(pn.CELL_TANH_RNN, D, m) == D * D + D * m + D
+    assert pn.param_count(pn.CELL_EULER_TANH, D, m) == D * D + D * m + 2 * D
+    assert pn.param_count(pn.CELL_DIAG_TANH, D, D) == D
+    with pytest.raises(ValueError, match="params holds"):
+        pn.eval(pn.CELL_GRU, good[:-1], x, s0)
+    with pytest.raises(ValueError, match="out must have shape"):
+        pn.eval(pn.CELL_GRU, good, x, s0, out=torch.zeros(B, T, D + 1))
+    with pytest.raises(ValueError, match="disagree on B"):
+        pn.eval(pn.CELL_GRU, good, x, torch.zeros(B + 1, D))
+    with pytest.raises(ValueError, match="x must be"):
+        pn.eval(pn.CELL_GRU, good, x[0], s0)
+    with pytest.raises(ValueError, match="unknown cell kind"):
+        pn.eval(9, good, x, s0)
+    with pytest.raises(ValueError, match="A must have shape"):
+        pn.affine_scan(torch.zeros(B, T, D), torch.zeros(B, T, D), s0, dense=True)
+    with pytest.raises(ValueError, match="s0 must have shape"):
+        pn.affine_scan(torch.zeros(B, T, D), torch.zeros(B, T, D), torch.zeros(B, D + 1))

@@ -52,7 +52,7 @@ def _report_residual_agreement(gpu, ref):
     print(f"   residual agreement: max relative |r_gpu - r_oracle| / r_oracle = {worst:.2e}", flush=True)
 
 
-def _parity(wl, mode, **kw):
+def _parity(wl, mode, exact=False, f32_count=False, **kw):
     print(f"[parity] {_label(wl)} mode={mode} {kw}", flush=True)
     okw = {k: v for k, v in kw.items() if k != "chunk"}
     ref = run_oracle(wl, mode, **okw)
@@ -71,7 +71,7 @@ def _parity(wl, mode, **kw):
         assert gpu.status == ref32.status == oracle.NONFINITE
         assert gpu.iters == ref32.iters
         return ref32
-    return check_parity(wl, mode, gpu, ref, label=_label(wl),
+    return check_parity(wl, mode, gpu, ref, label=_label(wl), exact=exact, f32_count=f32_count,
                         **{k: v for k, v in kw.items() if k in ("tol", "window", "damping", "max_iter")})
 
 
@@ -156,7 +156,7 @@ def test_diag_tanh_odd_width_and_damping():
 
 def test_cfg1_newton_full():
     wl = _case(1)
-    ref = _parity(wl, N)
+    ref = _parity(wl, N, exact=True)
     assert ref.iters == 4
 
 
@@ -167,24 +167,17 @@ def test_cfg2_gru_small(mode):
 
 
 def test_cfg2_gru_picard_small():
-    # T=300 is short enough for Picard to converge, after transients near
-    # 1e27.  Picard converges here only through causality (one step of the
-    # front per update), and where the front meets the tail is decided by the
-    # rounding of those 1e27 transients: the float64 and float32 oracles
-    # already differ by 9 updates.  The count is held to the float32 oracle
-    # within 2% of T; the trajectory is compared with the float64 oracle run
-    # for exactly the library's count, and the residual must meet tol.
-    wl = _case(2, B=4, T=300)
-    gpu = run_gpu(wl, P)
-    ref32 = run_oracle(wl, P, dtype=np.float32)
-    assert gpu.status == ref32.status == oracle.OK
-    assert max(ref32.hist[0]) > 1e20            # the transient regime this test is about
-    assert abs(gpu.iters - ref32.iters) <= 0.02 * 300, (gpu.iters, ref32.iters)
-    forced = run_oracle(wl, P, force_iters=[gpu.iters])
-    assert forced.status == oracle.OK
-    err = float(np.max(np.abs(gpu.out_np.astype(np.float64) - forced.s)))
-    assert err <= 1e-4 * max(1.0, float(np.max(np.abs(forced.s))))
-    assert residual64(wl, gpu.out_np) <= wl["tol"] + 1e-6
+    # Picard on this GRU converges only through causality (one exact step per
+    # update), past transients that grow with T.  At T = 64 they stay near
+    # 4e7, the float64 and float32 oracles agree on the count (60), and the
+    # library is held to the float64 count with the usual band, no float32
+    # reference.  Longer horizons are the transient-dominated regime where
+    # the precision itself moves the count (T = 300: 1e27 transients, the
+    # two oracle precisions 9 updates apart); the full workload's outcome
+    # (non-finite at the float32 oracle's update) is tested at full size.
+    wl = _case(2, B=4, T=64)
+    ref = _parity(wl, P)
+    assert ref.status == oracle.OK and max(ref.hist[0]) > 1e7
 
 
 @pytest.mark.parametrize("mode", [N, Q])
@@ -582,7 +575,7 @@ def test_matrix_cells_wide_input(kind):
 
 
 @pytest.mark.parametrize("cfg, B, T, mode", [(5, 2, 2500, Q), (2, 4, 300, Q), (2, 4, 300, J),
-                                            (2, 4, 300, P)])
+                                            (2, 4, 64, P)])
 def test_persistent_and_multilaunch_paths_agree(cfg, B, T, mode):
     # the one-launch cooperative solver and the launch-per-phase driver run the
     # same tile arithmetic; both must meet the oracle bar and agree on counts
@@ -590,20 +583,12 @@ def test_persistent_and_multilaunch_paths_agree(cfg, B, T, mode):
     a = run_gpu_flags(wl, mode, pn.FLAG_PERSISTENT)
     b = run_gpu(wl, mode)
     assert a.status == b.status
-    if mode == P:
-        # Picard on this GRU passes through 1e27 transients, and the two
-        # paths sum the carries in different orders (segmented in the
-        # persistent solver, one chunk after another in the few-chunk apply),
-        # which moves where the count lands (see test_cfg2_gru_picard_small)
-        assert abs(a.iters - b.iters) <= 0.02 * T
-        assert np.max(np.abs(a.out_np - b.out_np)) <= 1e-4
-        return
     assert a.window_iters == b.window_iters
     assert np.max(np.abs(a.out_np - b.out_np)) <= 1e-5
     assert len(a.resid_hist) == len(b.resid_hist)
-    if mode != P:
-        ref = run_oracle(wl, mode)
-        check_parity(wl, mode, a, ref, label=_label(wl) + " persistent")
+    ref = run_oracle(wl, mode)
+    check_parity(wl, mode, a, ref, label=_label(wl) + " persistent")
+    check_parity(wl, mode, b, ref, label=_label(wl) + " launch per phase")
 
 
 # ---------------------------------------------------------------- the scan alone
@@ -748,14 +733,14 @@ def test_deterministic_bitwise():
 @pytest.mark.slow
 def test_cfg3_full_quasi_newton():
     wl = _case(3)
-    ref = _parity(wl, Q)
+    ref = _parity(wl, Q, exact=True)
     assert ref.status == oracle.OK
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("mode", [Q, N, J])
 def test_cfg2_full(mode):
-    _parity(_case(2), mode)
+    _parity(_case(2), mode, exact=True)
 
 
 @pytest.mark.slow
@@ -770,7 +755,7 @@ def test_cfg2_full_picard_outcome():
 
 @pytest.mark.slow
 def test_cfg4_full_newton():
-    _parity(_case(4), N)
+    _parity(_case(4), N, exact=True)
 
 
 @pytest.mark.slow
@@ -800,7 +785,22 @@ def test_cfg6_full_banded():
 
 @pytest.mark.slow
 def test_cfg5_full_damped_windows():
-    _parity(_case(5), Q)
+    # window by window against the float64 oracle.  One window is decided
+    # 0.03% from tol (window 20: r_38 = 1.00033e-5 in float64), closer than
+    # a float32 residual resolves, so its count may be one off and is logged;
+    # every other window must match exactly.
+    wl = _case(5)
+    ref = run_oracle(wl, Q)
+    gpu = run_gpu(wl, Q)
+    print(f"   gpu windows {gpu.window_iters}\n   oracle windows {ref.window_iters}", flush=True)
+    tol = wl["tol"]
+    close = {w for w, h in enumerate(ref.hist)
+             if abs(h[ref.window_iters[w] - 1] - tol) <= 0.001 * tol or abs(h[ref.window_iters[w]] - tol) <= 0.001 * tol}
+    assert close == {20}
+    for w, (kg, ko) in enumerate(zip(gpu.window_iters, ref.window_iters)):
+        assert kg == ko or w in close, (w, kg, ko)
+    check_parity(wl, Q, gpu, ref, label=_label(wl))
+    assert len(ref.window_iters) == 32
 
 
 # ---------------------------------------------------------------- per-call measurements

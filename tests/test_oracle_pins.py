@@ -64,6 +64,69 @@ def test_sequential_gru_matches_torch_gru():
     np.testing.assert_allclose(got, out.numpy(), rtol=0, atol=1e-12)
 
 
+def _flat_from_torch_gru(mod):
+    """The flat parameter vector of the C interface, W_ih | W_hh | b_ih | b_hh,
+    taken from a torch.nn.GRU's own tensors in their storage order."""
+    return np.concatenate([t.detach().numpy().ravel() for t in
+                           (mod.weight_ih_l0, mod.weight_hh_l0, mod.bias_ih_l0, mod.bias_hh_l0)])
+
+
+def _flat_from_torch_rnn(mod):
+    """W | U | b for a torch.nn.RNN(tanh): W is weight_hh, U weight_ih, and the
+    two torch biases act as one sum."""
+    return np.concatenate([mod.weight_hh_l0.detach().numpy().ravel(),
+                           mod.weight_ih_l0.detach().numpy().ravel(),
+                           (mod.bias_ih_l0 + mod.bias_hh_l0).detach().numpy()])
+
+
+@pytest.mark.parametrize("D, m", [(6, 4), (5, 9)])
+def test_flat_gru_layout_parses_torch_parameters(D, m):
+    # The flat layout itself, not cell fields copied back into torch: a
+    # freshly initialised torch.nn.GRU (its own weights, every bias nonzero
+    # and different) is flattened in the documented order and parsed by
+    # make_cell; a swap of b_ih and b_hh (which only matters for the
+    # candidate's b_hn inside the reset product), of two gates, or of the
+    # input and hidden blocks fails this.
+    torch.manual_seed(10 + D)
+    mod = torch.nn.GRU(m, D, batch_first=True).double()
+    with torch.no_grad():
+        mod.bias_ih_l0.uniform_(-1.0, 1.0)
+        mod.bias_hh_l0.uniform_(-1.0, 1.0)
+        mod.weight_hh_l0.mul_(2.0)
+    flat = _flat_from_torch_gru(mod)
+    cell = oracle.make_cell(oracle.CELL_GRU, flat, D, m)
+    rng = np.random.default_rng(20 + D)
+    B, T = 3, 13
+    x = rng.standard_normal((B, T, m))
+    s0 = 0.5 * rng.standard_normal((B, D))
+    with torch.no_grad():
+        ref, _ = mod(torch.from_numpy(x), torch.from_numpy(s0)[None])
+    np.testing.assert_allclose(oracle.sequential(cell, x, s0), ref.numpy(), rtol=0, atol=1e-12)
+    # the same holds for the swapped-bias vector only if b_hn does not matter,
+    # which it does here
+    n_ih, n_hh = 3 * D * m, 3 * D * D
+    swapped = flat.copy()
+    swapped[n_ih + n_hh:n_ih + n_hh + 3 * D] = flat[n_ih + n_hh + 3 * D:]
+    swapped[n_ih + n_hh + 3 * D:] = flat[n_ih + n_hh:n_ih + n_hh + 3 * D]
+    bad = oracle.sequential(oracle.make_cell(oracle.CELL_GRU, swapped, D, m), x, s0)
+    assert np.max(np.abs(bad - ref.numpy())) > 1e-3
+
+
+def test_flat_rnn_layout_parses_torch_parameters():
+    D, m = 5, 3
+    torch.manual_seed(31)
+    mod = torch.nn.RNN(m, D, nonlinearity="tanh", batch_first=True).double()
+    with torch.no_grad():
+        mod.weight_hh_l0.mul_(2.0)
+    cell = oracle.make_cell(oracle.CELL_TANH_RNN, _flat_from_torch_rnn(mod), D, m)
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((2, 11, m))
+    s0 = rng.standard_normal((2, D))
+    with torch.no_grad():
+        ref, _ = mod(torch.from_numpy(x), torch.from_numpy(s0)[None])
+    np.testing.assert_allclose(oracle.sequential(cell, x, s0), ref.numpy(), rtol=0, atol=1e-12)
+
+
 def test_sequential_diag_tanh_is_an_rnn_with_diagonal_weights():
     # tanh(a*s + x) is torch's Elman RNN with W_hh = diag(a), W_ih = I, no bias.
     D, B, T = 7, 2, 23
