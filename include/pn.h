@@ -220,6 +220,25 @@ int pn_eval_ex(const pn_cell* cell, const float* params, const float* x, const f
                int64_t B, int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter,
                float* out, int32_t* iters_out, const pn_opts* opts);
 
+/* pn_eval_ex for callers that cannot allocate device memory (serving loops
+ * and harnesses that forbid allocation during a call): the same solve, with
+ * the same arguments, options and results, run on a static device scratch
+ * that the library holds on each GPU it runs on until the process ends
+ * (32 MiB, enough for every workload in this repository's benchmarks).  The
+ * call itself allocates nothing: no device or pinned memory, no events.
+ * opts->workspace must be NULL and opts->profile NULL (PN_EINVAL otherwise);
+ * a problem whose workspace (pn_workspace_bytes) exceeds the scratch less
+ * 256 bytes of check records returns PN_EWORKSPACE before any device work.
+ * The host reads each convergence check back with a copy after draining the
+ * stream, so iterations do not overlap the host's reading as in pn_eval_ex.
+ * Every call on a GPU shares that GPU's scratch, which keeps the contents
+ * of the last call (the library clears what must start at zero): calls that
+ * overlap on one GPU, from any threads or streams, race and must not be
+ * made. */
+int pn_eval_noalloc(const pn_cell* cell, const float* params, const float* x, const float* s0,
+                    int64_t B, int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter,
+                    float* out, int32_t* iters_out, const pn_opts* opts);
+
 /* Bytes of workspace pn_eval_ex (and pn_eval_f16) needs for this problem
  * with these options (opts may be NULL).  The size depends on the window and
  * also on the chunk, the mode switch and the bandwidth, so the whole option

@@ -25,8 +25,9 @@ EINVAL, EUNSUPPORTED, EHIP, EWORKSPACE = -1, -2, -3, -4
 FLAG_PERSISTENT = 1
 WINDOW_CONSECUTIVE, WINDOW_ADVANCING = 0, 1
 
-EXPORTED = ("pn_opts_init", "pn_eval", "pn_eval_ex", "pn_eval_f16", "pn_workspace_bytes",
-            "pn_affine_scan", "pn_affine_scan_workspace_bytes", "pn_last_error", "pn_version")
+EXPORTED = ("pn_opts_init", "pn_eval", "pn_eval_ex", "pn_eval_f16", "pn_eval_noalloc",
+            "pn_workspace_bytes", "pn_affine_scan", "pn_affine_scan_workspace_bytes", "pn_last_error",
+            "pn_version")
 
 
 class PnError(RuntimeError):
@@ -86,6 +87,8 @@ def lib():
         L.pn_eval_ex.restype = ctypes.c_int
         L.pn_eval_f16.argtypes = sig + [ctypes.POINTER(Opts)]
         L.pn_eval_f16.restype = ctypes.c_int
+        L.pn_eval_noalloc.argtypes = sig + [ctypes.POINTER(Opts)]
+        L.pn_eval_noalloc.restype = ctypes.c_int
         L.pn_workspace_bytes.argtypes = [ctypes.POINTER(Cell), i64, i64, i64, i32, ctypes.POINTER(Opts)]
         L.pn_workspace_bytes.restype = ctypes.c_size_t
         L.pn_affine_scan.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, ctypes.POINTER(Opts)]
@@ -209,7 +212,7 @@ class Result:
 def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, damping=1.0,
          window=0, chunk=0, out=None, history=False, profile=False, workspace=None, flags=0,
          bandwidth=1, window_mode=WINDOW_CONSECUTIVE, switch_mode=-1, switch_ratio=0.5,
-         switch_damping=0.0):
+         switch_damping=0.0, noalloc=False):
     """Solve s_t = f(s_{t-1}, x_t) for t = 1..T over the batch; see include/pn.h.
 
     params, x [B,T,m], s0 [B,D] are float32 tensors on one HIP device; with
@@ -224,6 +227,8 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     the damping alone).
     ``profile`` True times every steady apply launch with HIP events, an
     integer n > 1 every n-th (Result.profile).
+    ``noalloc`` runs pn_eval_noalloc: no workspace is allocated, the library
+    uses its static device scratch (float storage; no profile, no workspace).
     Returns a ``Result`` (unpacks as ``out, iters, status``).  Negative
     library statuses raise ``PnError``.
     """
@@ -242,15 +247,19 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
     c = Cell(int(cell_kind), int(m))
     o = make_opts(damping, window or 0, chunk, _stream_ptr(dev), flags, bandwidth, window_mode,
                   switch_mode, switch_ratio, switch_damping)
-    nbytes = lib().pn_workspace_bytes(ctypes.byref(c), B, T, D, int(mode), ctypes.byref(o))
-    if nbytes == 0:
-        raise PnError(EINVAL, last_error())
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
-    base = workspace.data_ptr()
-    aligned = (base + 255) // 256 * 256
-    o.workspace = aligned
-    o.workspace_bytes = workspace.numel() - (aligned - base)
+    if noalloc:
+        if half or workspace is not None or profile:
+            raise ValueError("noalloc takes float storage and neither a workspace nor profiling")
+    else:
+        nbytes = lib().pn_workspace_bytes(ctypes.byref(c), B, T, D, int(mode), ctypes.byref(o))
+        if nbytes == 0:
+            raise PnError(EINVAL, last_error())
+        if workspace is None or workspace.numel() < nbytes:
+            workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+        base = workspace.data_ptr()
+        aligned = (base + 255) // 256 * 256
+        o.workspace = aligned
+        o.workspace_bytes = workspace.numel() - (aligned - base)
     nwin = 1 if advancing else (max(1, -(-T // W)) if T > 0 else 1)
     wit = (ctypes.c_int32 * nwin)()
     o.window_iters = wit
@@ -275,7 +284,7 @@ def eval(cell_kind, params, x, s0, mode=QUASI_NEWTON, tol=1e-5, max_iter=None, d
         o.profile = ctypes.pointer(prof)
         o.profile_stride = int(profile)     # True: every steady launch; n: every n-th
     iters = ctypes.c_int32(0)
-    entry = lib().pn_eval_f16 if half else lib().pn_eval_ex
+    entry = lib().pn_eval_noalloc if noalloc else (lib().pn_eval_f16 if half else lib().pn_eval_ex)
     rc = entry(ctypes.byref(c), _dev_f32(params, "params"), _dev_f32(x, "x", sdt),
                _dev_f32(s0, "s0"), B, T, D, int(mode), float(tol), int(max_iter),
                _dev_f32(out, "out", sdt), ctypes.byref(iters), ctypes.byref(o))

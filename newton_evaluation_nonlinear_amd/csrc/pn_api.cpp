@@ -342,12 +342,20 @@ int validate(const pn_cell* cell, const float* params, const float* x, const flo
 // ---------------------------------------------------------------- per-thread resources
 struct ThreadRes {
     int device = -1;
-    HostRec* host = nullptr;     // pinned
-    HostRec* host_dev = nullptr; // device-usable alias
+    HostRec* host = nullptr;     // pinned (or, with dev_ring, a plain host shadow)
+    HostRec* host_dev = nullptr; // device-usable alias (or, with dev_ring, device memory)
+    bool dev_ring = false;       // records live in device memory: copy each back to read it
     int32_t epoch = 0;           // per-thread call counter
     std::vector<hipEvent_t> timing;   // pool of timing events
 };
 thread_local ThreadRes g_res;
+
+// pn_eval_noalloc: the record ring at the start of the static scratch, and
+// the epochs of its calls (unique across threads, so a stale record of an
+// earlier call never matches)
+constexpr size_t kStaticRingBytes = 256;
+static_assert(sizeof(HostRec) * kHostRing <= kStaticRingBytes, "record ring");
+std::atomic<int32_t> g_static_epoch{1};
 
 int get_res(ThreadRes** out) {
     int dev = 0;
@@ -385,7 +393,17 @@ int timing_event(ThreadRes* r, size_t idx, hipEvent_t* ev) {
 // Wait until the check of iteration `iter` (call `epoch`) has published its
 // record in pinned host memory.  Polls the record; every few thousand polls
 // asks the runtime whether the stream failed or drained without writing it.
-int wait_record(volatile HostRec* hr, hipStream_t st, int32_t epoch, int32_t iter) {
+int wait_record(const ThreadRes* res, volatile HostRec* hr, hipStream_t st, int32_t epoch, int32_t iter) {
+    if (res->dev_ring) {
+        // records in device memory: the stream holds the check that writes
+        // this one; drain it and copy the record into the host shadow
+        HostRec* shadow = const_cast<HostRec*>(hr);
+        const HostRec* src = res->host_dev + (shadow - res->host);
+        PN_HIP(hipMemcpyAsync(shadow, src, sizeof(HostRec), hipMemcpyDeviceToHost, st));
+        PN_HIP(hipStreamSynchronize(st));
+        if (hr->iter == iter && hr->epoch == epoch) return PN_OK;
+        return fail(PN_EHIP, "stream drained without publishing iteration %d", iter);
+    }
     using clk = std::chrono::steady_clock;
     const auto t0 = clk::now();
     for (uint64_t n = 1;; ++n) {
@@ -633,7 +651,7 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
             if (rc != PN_OK) return rc;
         }
         {
-            int rc = wait_record(hr, c.st, epoch, i);
+            int rc = wait_record(c.res, hr, c.st, epoch, i);
             if (rc != PN_OK) return rc;
         }
         const int stop = hr->stop;
@@ -778,7 +796,7 @@ int solve_advancing(SolveCtx& c, const float* x, const float* s0, float* out, in
     int64_t ma = a, me = e;          // the window the chunk maps on the device belong to
     for (int i = 0;;) {
         {
-            int rc = wait_record(hr, c.st, epoch, i);
+            int rc = wait_record(c.res, hr, c.st, epoch, i);
             if (rc != PN_OK) return rc;
         }
         const uint32_t rb = hr->r_bits;
@@ -914,6 +932,16 @@ int solve_persistent(SolveCtx& c, const float* x, const float* s0, float* out, i
     return PN_OK;
 }
 
+// Where a solve's device memory and check records come from when the caller
+// brings neither a workspace nor a pinned record ring: the library's static
+// device scratch (pn_eval_noalloc).  Records then live in device memory and
+// the host reads each one back with a copy after synchronising the stream.
+struct Backing {
+    char* ws;                // 256-byte aligned device memory for the plan's regions
+    size_t bytes;
+    ThreadRes* res;          // dev_ring set, host = a host shadow array
+};
+
 // Frees a workspace the library allocated for one call on every exit path.
 struct OwnedWorkspace {
     void* p = nullptr;
@@ -935,7 +963,7 @@ struct OwnedWorkspace {
 
 int eval_impl(const pn_cell* cell, const float* params, const float* x, const float* s0, int64_t B,
               int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter, float* out,
-              int32_t* iters_out, const pn_opts* o, bool half = false) {
+              int32_t* iters_out, const pn_opts* o, bool half = false, const Backing* bk = nullptr) {
     g_err.clear();
     g_launch_timing = LaunchTiming{};     // no request left over from a failed call
     int rc = validate(cell, params, x, s0, B, T, D, mode, tol, max_iter, out, iters_out, o, half ? 2 : 4);
@@ -963,13 +991,22 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     if (o && o->workspace && o->workspace_bytes < p.total)
         return fail(PN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                     o->workspace_bytes, p.total);
+    if (bk && bk->bytes < p.total)
+        return fail(PN_EWORKSPACE, "problem needs %zu bytes of scratch; the static scratch holds %zu",
+                    p.total, bk->bytes);
     ThreadRes* res;
-    rc = get_res(&res);
-    if (rc != PN_OK) return rc;
+    if (bk) {
+        res = bk->res;
+    } else {
+        rc = get_res(&res);
+        if (rc != PN_OK) return rc;
+    }
     hipStream_t st = o ? static_cast<hipStream_t>(o->stream) : nullptr;
     char* ws = nullptr;
     OwnedWorkspace own;
-    if (o && o->workspace) {
+    if (bk) {
+        ws = bk->ws;
+    } else if (o && o->workspace) {
         ws = static_cast<char*>(o->workspace);
     } else {
         void* q = nullptr;
@@ -1097,6 +1134,43 @@ int pn_eval_f16(const pn_cell* cell, const float* params, const uint16_t* x, con
     }
     return eval_impl(cell, params, reinterpret_cast<const float*>(x), s0, B, T, D, mode, tol, max_iter,
                      reinterpret_cast<float*>(out), iters_out, opts, true);
+}
+
+int pn_eval_noalloc(const pn_cell* cell, const float* params, const float* x, const float* s0,
+                    int64_t B, int64_t T, int64_t D, int32_t mode, float tol, int32_t max_iter,
+                    float* out, int32_t* iters_out, const pn_opts* opts) {
+    g_err.clear();
+    if (opts && (opts->workspace || opts->workspace_bytes))
+        return fail(PN_EINVAL, "pn_eval_noalloc runs on the static scratch: opts->workspace must be NULL");
+    if (opts && opts->profile)
+        return fail(PN_EINVAL, "profiling creates timing events, which pn_eval_noalloc does not");
+    int rc = validate(cell, params, x, s0, B, T, D, mode, tol, max_iter, out, iters_out, opts);
+    if (rc != PN_OK) return rc;
+    if (B == 0 || T == 0 || D == 0) return eval_impl(cell, params, x, s0, B, T, D, mode, tol, max_iter,
+                                                     out, iters_out, opts);
+    // the size check comes before any device call
+    Plan p, p2;
+    bool has2 = false;
+    rc = make_plans(p, p2, &has2, cell, B, T, D, mode, opts);
+    if (rc != PN_OK) return rc;
+    if (p.total > kStaticScratchBytes - kStaticRingBytes)
+        return fail(PN_EWORKSPACE, "problem needs %zu bytes of scratch; pn_eval_noalloc has %zu",
+                    p.total, kStaticScratchBytes - kStaticRingBytes);
+    void* base = nullptr;
+    size_t bytes = 0;
+    const hipError_t e = static_scratch(&base, &bytes);
+    if (e != hipSuccess) return fail(PN_EHIP, "static scratch lookup failed: %s", hipGetErrorString(e));
+    // check records go to the first kStaticRingBytes of the scratch; the
+    // host reads each back into this shadow
+    HostRec shadow[kHostRing];
+    ThreadRes r;
+    (void)hipGetDevice(&r.device);
+    r.host = shadow;
+    r.host_dev = static_cast<HostRec*>(base);
+    r.dev_ring = true;
+    r.epoch = g_static_epoch.fetch_add(1 << 16);
+    Backing bk{static_cast<char*>(base) + kStaticRingBytes, bytes - kStaticRingBytes, &r};
+    return eval_impl(cell, params, x, s0, B, T, D, mode, tol, max_iter, out, iters_out, opts, false, &bk);
 }
 
 size_t pn_workspace_bytes(const pn_cell* cell, int64_t B, int64_t T, int64_t D, int32_t mode,

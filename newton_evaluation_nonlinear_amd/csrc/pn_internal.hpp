@@ -213,6 +213,11 @@ bool cell_persist_eligible(int kind, int DP, int L, int m);
 hipError_t cell_persist_max_blocks(int kind, int DP, int L, int m, int* nblocks);
 hipError_t launch_cell_persist(int kind, int DP, int nblocks, const PersistArgs& a, hipStream_t st);
 
+// Static device scratch of pn_eval_noalloc (pn_static.hip): its device
+// address on the current device (looked up once per device) and its size.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+hipError_t static_scratch(void** ptr, size_t* bytes);
+
 // Standalone affine scan.
 struct ScanArgs {
     const float* A;          // diag [B][T][D] or dense [B][T][D][D]
