@@ -194,6 +194,14 @@ enum { PN_WINDOW_CONSECUTIVE = 0, PN_WINDOW_ADVANCING = 1 };
  * the faster one for the shapes measured here. */
 enum { PN_FLAG_PERSISTENT = 1 };
 
+/* pn_opts.flags.  A solve of a matrix cell with D <= 8 whose windows hold at
+ * most 1024 (D <= 4) or 512 (D <= 8) (b, t) pairs runs by default in one
+ * launch of a single workgroup, every window, iteration and check included
+ * (float storage, consecutive windows, no switching, chunk 0, max_iter <=
+ * 16384).  PN_FLAG_MULTI_LAUNCH keeps such a solve on the launch-per-phase
+ * driver instead. */
+enum { PN_FLAG_MULTI_LAUNCH = 2 };
+
 /* Fill *o with the defaults: damping 1, chunk 0, window 0, bandwidth 1,
  * switch_mode -1, switch_ratio 0.5, switch_damping 0, profile_stride 1,
  * everything else NULL / 0. */

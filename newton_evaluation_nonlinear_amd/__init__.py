@@ -22,7 +22,7 @@ CELL_DIAG_TANH, CELL_TANH_RNN, CELL_GRU, CELL_EULER_TANH = 0, 1, 2, 3
 JACOBI, PICARD, QUASI_NEWTON, NEWTON, BANDED = 0, 1, 2, 3, 4
 OK, NOT_CONVERGED, NONFINITE = 0, 1, 2
 EINVAL, EUNSUPPORTED, EHIP, EWORKSPACE = -1, -2, -3, -4
-FLAG_PERSISTENT = 1
+FLAG_PERSISTENT, FLAG_MULTI_LAUNCH = 1, 2
 WINDOW_CONSECUTIVE, WINDOW_ADVANCING = 0, 1
 
 EXPORTED = ("pn_opts_init", "pn_eval", "pn_eval_ex", "pn_eval_f16", "pn_eval_noalloc",

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpn.so")
 
-SOURCES = ["pn_api.cpp", "pn_diag.hip", "pn_cell.hip", "pn_dense.hip", "pn_scan.hip", "pn_static.hip"]
+SOURCES = ["pn_api.cpp", "pn_diag.hip", "pn_cell.hip", "pn_dense.hip", "pn_scan.hip", "pn_static.hip", "pn_small.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -53,6 +53,7 @@ int fail(int code, const char* fmt, ...) {
     } while (0)
 
 constexpr size_t kAlign = 256;
+constexpr int32_t kSmallMaxIter = 1 << 14;   // updates per window the one-workgroup solver takes on
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int next_pow2(int v) {
@@ -74,6 +75,8 @@ struct Plan {
     bool half;             // x and out in IEEE binary16 (channel-wise cell)
     int hmode;             // DiagArgs::half of the channel-wise kernel
     bool persist_ok;       // shape allows the one-launch persistent solver
+    bool small;            // the window fits one workgroup: every window, iteration and
+                           // check in one launch (pn_small.hip)
     bool recompute;        // channel-wise cell, float storage: first update stores nothing,
                            // the second recomputes s^(1) (kFirstNS, kSecondR)
     int fc;                // matrix cell, diagonal mode, few chunks (CellArgs::fc): the apply
@@ -197,6 +200,12 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
     p.NCc = static_cast<int>((p.W + p.Lc - 1) / p.Lc);
     p.persist_ok = p.matrix_cell && !p.dense && !p.advancing &&
                    cell_persist_eligible(p.kind, p.DP, p.L, p.m);
+    // A window of at most a few hundred (b, t) pairs of a narrow matrix cell
+    // is latency, not work: one workgroup runs the whole solve.  An explicit
+    // chunk or PN_FLAG_MULTI_LAUNCH keeps the multi-launch driver.
+    p.small = p.matrix_cell && !half && !p.advancing && chunk == 0 &&
+              !(o && (o->flags & PN_FLAG_MULTI_LAUNCH)) && p.D <= 8 &&
+              static_cast<int64_t>(p.B) * p.W <= small_max_pairs_for(p.D);
     p.hist_cap = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(p.nwin) * (p.W + 1), 1 << 16));
     layout(p, nullptr);
     return PN_OK;
@@ -229,7 +238,7 @@ void layout(Plan& p, const Plan* other) {
     p.off_w = off;
     if (p.matrix_cell) off = align_up(off + sizeof(float) * prepared_total_floats(p.kind, p.DP, p.m));
     p.off_sync = p.off_winfo = p.off_hist = off;
-    if (p.persist_ok) {
+    if (p.persist_ok || p.small) {
         p.off_sync = off; off = align_up(off + 256);
         p.off_winfo = off; off = align_up(off + sizeof(int32_t) * 2 * p.nwin);
         p.off_hist = off; off = align_up(off + sizeof(float) * p.hist_cap);
@@ -248,6 +257,7 @@ int make_plans(Plan& p, Plan& p2, bool* has2, const pn_cell* cell, int64_t B, in
     rc = make_plan(p2, cell, B, T, D, o->switch_mode, o);
     if (rc != PN_OK) return rc;
     p.persist_ok = p2.persist_ok = false;
+    p.small = p2.small = false;
     p.recompute = p2.recompute = false;
     p.fc = p2.fc = 0;
     p.Lc = p.L; p2.Lc = p2.L;
@@ -347,8 +357,34 @@ struct ThreadRes {
     bool dev_ring = false;       // records live in device memory: copy each back to read it
     int32_t epoch = 0;           // per-thread call counter
     std::vector<hipEvent_t> timing;   // pool of timing events
+    // pinned (mapped) buffer the one-workgroup solver writes its per-window
+    // counts and residual history to; grown on demand
+    char* small_host = nullptr;
+    char* small_dev = nullptr;
+    size_t small_cap = 0;
 };
 thread_local ThreadRes g_res;
+
+// A pinned buffer of at least `bytes` for the one-workgroup solver's results
+// (the previous call has completed: every call ends with a stream sync).
+int small_info_buffer(ThreadRes* r, size_t bytes, char** host, char** dev) {
+    if (r->small_cap < bytes) {
+        if (r->small_host) PN_HIP(hipHostFree(r->small_host));
+        r->small_host = r->small_dev = nullptr;
+        r->small_cap = 0;
+        const size_t cap = std::max<size_t>(bytes, 4096);
+        void* p = nullptr;
+        PN_HIP(hipHostMalloc(&p, cap, hipHostMallocMapped | hipHostMallocCoherent));
+        r->small_host = static_cast<char*>(p);
+        r->small_cap = cap;
+    }
+    void* dp = nullptr;
+    PN_HIP(hipHostGetDevicePointer(&dp, r->small_host, 0));
+    r->small_dev = static_cast<char*>(dp);
+    *host = r->small_host;
+    *dev = r->small_dev;
+    return PN_OK;
+}
 
 // pn_eval_noalloc: the record ring at the start of the static scratch, and
 // the epochs of its calls (unique across threads, so a stale record of an
@@ -942,6 +978,74 @@ struct Backing {
     ThreadRes* res;          // dev_ring set, host = a host shadow array
 };
 
+// The whole solve in one launch of the one-workgroup solver, then one copy of
+// its per-window counts, statuses and residual history back to the host.
+int solve_small(SolveCtx& c, const float* x, const float* s0, float* out, int64_t T,
+                std::vector<int>* wit, int* total, int* overall) {
+    const Plan& p = *c.p;
+    char* ws = c.ws;
+    SmallArgs a{};
+    a.params = c.params; a.x = x; a.s0 = s0; a.out = out; a.T = T;
+    a.W = static_cast<int32_t>(p.W); a.nwin = p.nwin; a.B = p.B; a.D = p.D; a.m = p.m;
+    a.mode = p.mode; a.band = p.band; a.max_iter = c.max_iter;
+    a.undamped = c.lam == 1.0f; a.tol = c.tol; a.lam = c.lam;
+    // results region [hist_len | win_iters, win_status | history], laid out
+    // as in the workspace: written straight to pinned host memory, or, for
+    // pn_eval_noalloc (records in device memory), to the workspace and copied
+    // back once
+    const size_t nbytes = p.off_hist + sizeof(float) * p.hist_cap - p.off_sync;
+    char* dev_info = ws + p.off_sync;
+    const char* host_info = nullptr;
+    std::vector<char> copy;
+    if (!c.res->dev_ring) {
+        char* h = nullptr;
+        int rc = small_info_buffer(c.res, nbytes, &h, &dev_info);
+        if (rc != PN_OK) return rc;
+        host_info = h;
+    }
+    a.hist_len = reinterpret_cast<int32_t*>(dev_info);
+    a.win_iters = reinterpret_cast<int32_t*>(dev_info + (p.off_winfo - p.off_sync));
+    a.win_status = a.win_iters + p.nwin;
+    a.hist = reinterpret_cast<float*>(dev_info + (p.off_hist - p.off_sync));
+    a.hist_cap = p.hist_cap;
+    const bool timed = c.tm->take();
+    size_t e0 = 0, e1 = 0;
+    if (timed) { int rc = request_timing(c, &e0, &e1); if (rc) return rc; }
+    PN_HIP(launch_small_solve(p.kind, p.dense, a, c.st));
+    if (timed) { int rc = check_timed_launch(); if (rc) return rc; }
+    if (c.res->dev_ring) {
+        copy.resize(nbytes);
+        PN_HIP(hipMemcpyAsync(copy.data(), dev_info, nbytes, hipMemcpyDeviceToHost, c.st));
+        host_info = copy.data();
+    }
+    PN_HIP(hipStreamSynchronize(c.st));
+    int32_t hlen = 0;
+    std::memcpy(&hlen, host_info, sizeof(hlen));
+    const int32_t* wi = reinterpret_cast<const int32_t*>(host_info + (p.off_winfo - p.off_sync));
+    const float* hist = reinterpret_cast<const float*>(host_info + (p.off_hist - p.off_sync));
+    if (c.hist) c.hist->assign(hist, hist + std::min(hlen, p.hist_cap));
+    *total = 0;
+    *overall = PN_OK;
+    double bytes = 0.0, flops = 0.0;
+    for (int w = 0; w < p.nwin; ++w) {
+        const int K = wi[w], st = wi[p.nwin + w];
+        if (K < 0) break;
+        const int Tw = static_cast<int>(std::min<int64_t>(p.W, T - static_cast<int64_t>(w) * p.W));
+        wit->push_back(K);
+        *total += K;
+        if (K > 0) bytes += apply_bytes(p, Tw, true) + (K - 1) * apply_bytes(p, Tw, false);
+        flops += K * apply_flops(p, Tw);
+        if (st == PN_NONFINITE) { *overall = PN_NONFINITE; break; }
+        if (st == PN_NOT_CONVERGED) *overall = PN_NOT_CONVERGED;
+    }
+    if (timed) {
+        c.tm->apply.push_back({e0, e1});
+        c.tm->apply_bytes.push_back(bytes);
+        c.tm->apply_flops.push_back(flops);
+    }
+    return PN_OK;
+}
+
 // Frees a workspace the library allocated for one call on every exit path.
 struct OwnedWorkspace {
     void* p = nullptr;
@@ -1021,7 +1125,11 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     std::vector<float> hist;
     SolveCtx c{&p, st, ws, res, params, tol, o ? o->damping : 1.0f, max_iter, &tm, &hist,
                o ? o->switch_ratio : 0.0f, o ? o->switch_damping : 0.0f};
-    if (p.matrix_cell)
+    // the one-workgroup solver reads the flat parameters itself; a cap of
+    // more updates per window than kSmallMaxIter goes to the multi-launch
+    // driver, whose host-side wait is bounded
+    const bool small = p.small && max_iter <= kSmallMaxIter;
+    if (p.matrix_cell && !small)
         PN_HIP(launch_prep_weights(p.kind, params, reinterpret_cast<float*>(ws + p.off_w), p.D, p.DP, p.m,
                                    !p.mfma || (has2 && !p2.mfma), st));
     size_t ev_first = 0;
@@ -1031,7 +1139,11 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     std::vector<int32_t> accepted, wsw;
     const int64_t m = p.m;
     bool persisted = false;
-    if (p.persist_ok && o && (o->flags & PN_FLAG_PERSISTENT)) {
+    if (small) {
+        rc = solve_small(c, x, s0, out, T, &wit, &total, &overall);
+        if (rc != PN_OK) return rc;
+        persisted = true;
+    } else if (p.persist_ok && o && (o->flags & PN_FLAG_PERSISTENT)) {
         rc = solve_persistent(c, x, s0, out, T, &wit, &total, &overall);
         if (rc == PN_OK) persisted = true;
         else if (rc != PN_EUNSUPPORTED) return rc;

@@ -218,6 +218,27 @@ hipError_t launch_cell_persist(int kind, int DP, int nblocks, const PersistArgs&
 constexpr size_t kStaticScratchBytes = size_t(32) << 20;
 hipError_t static_scratch(void** ptr, size_t* bytes);
 
+// One-workgroup solver (pn_small.hip): matrix cells with D <= 8 whose window
+// holds at most small_max_pairs_for(D) (b, t) pairs; every window, iteration
+// and check in one launch.  Results go to device memory: per window the
+// updates (-1: not reached) and status, and the residual history.
+struct SmallArgs {
+    const float* params;
+    const float* x;          // [B][T][m]
+    const float* s0;         // [B][D]
+    float* out;              // [B][T][D]
+    int64_t T;
+    int32_t W, nwin, B, D, m, mode, band, max_iter, undamped;
+    float tol, lam;
+    int32_t* win_iters;      // [nwin]
+    int32_t* win_status;     // [nwin]
+    int32_t* hist_len;       // checks taken (the history keeps the first hist_cap)
+    float* hist;
+    int32_t hist_cap;
+};
+int small_max_pairs_for(int D);
+hipError_t launch_small_solve(int kind, bool dense, const SmallArgs& a, hipStream_t st);
+
 // Standalone affine scan.
 struct ScanArgs {
     const float* A;          // diag [B][T][D] or dense [B][T][D][D]

@@ -53,7 +53,7 @@ def to_dev(wl):
 
 
 def run_gpu(wl, mode, tol=None, max_iter=None, damping=None, window=None, chunk=0, history=True,
-            profile=False):
+            profile=False, flags=0):
     params, x, s0 = to_dev(wl)
     res = pn.eval(wl["cell"], params, x, s0, mode=mode,
                   tol=wl["tol"] if tol is None else tol,
@@ -64,7 +64,7 @@ def run_gpu(wl, mode, tol=None, max_iter=None, damping=None, window=None, chunk=
                   bandwidth=wl.get("bandwidth", 1),
                   window_mode=pn.WINDOW_ADVANCING if advancing(wl) else pn.WINDOW_CONSECUTIVE,
                   switch_mode=wl.get("switch_mode", -1), switch_ratio=wl.get("switch_ratio", 0.5),
-                  switch_damping=wl.get("switch_damping", 0.0))
+                  switch_damping=wl.get("switch_damping", 0.0), flags=flags)
     torch.cuda.synchronize()
     res.out_np = res.out.float().cpu().numpy()
     return res

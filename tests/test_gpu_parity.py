@@ -54,7 +54,7 @@ def _report_residual_agreement(gpu, ref):
 
 def _parity(wl, mode, exact=False, f32_count=False, **kw):
     print(f"[parity] {_label(wl)} mode={mode} {kw}", flush=True)
-    okw = {k: v for k, v in kw.items() if k != "chunk"}
+    okw = {k: v for k, v in kw.items() if k not in ("chunk", "flags")}
     ref = run_oracle(wl, mode, **okw)
     gpu = run_gpu(wl, mode, **kw)
     print(f"   gpu iters={gpu.iters} win={gpu.window_iters[:6]} status={gpu.status} "
@@ -154,9 +154,11 @@ def test_diag_tanh_odd_width_and_damping():
     _parity(wl, J)
 
 
-def test_cfg1_newton_full():
+@pytest.mark.parametrize("flags", [0, pn.FLAG_MULTI_LAUNCH])
+def test_cfg1_newton_full(flags):
+    # one workgroup (default) and the launch-per-phase driver
     wl = _case(1)
-    ref = _parity(wl, N, exact=True)
+    ref = _parity(wl, N, exact=True, flags=flags)
     assert ref.iters == 4
 
 
@@ -191,9 +193,12 @@ def test_cfg5_gru_damped_windows_small():
     _parity(wl, Q)
 
 
+@pytest.mark.parametrize("flags", [0, pn.FLAG_MULTI_LAUNCH])
 @pytest.mark.parametrize("D", [1, 3, 5, 12, 16, 20, 32, 33, 64])
 @pytest.mark.parametrize("kind", [pn.CELL_TANH_RNN, pn.CELL_GRU])
-def test_matrix_cells_other_widths(kind, D):
+def test_matrix_cells_other_widths(kind, D, flags):
+    if flags and D > 8:
+        pytest.skip("only D <= 8 has a one-workgroup form to switch off")
     rng = np.random.default_rng(100 + D)
     m, B, T = 3, 2, 150
     params = workloads.random_cell_params(kind, D, m, rng, 1.0)
@@ -201,7 +206,7 @@ def test_matrix_cells_other_widths(kind, D):
               max_iter=T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
               s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32))
     for mode in (N, Q):
-        _parity(wl, mode)
+        _parity(wl, mode, flags=flags)
 
 
 @pytest.mark.parametrize("T", [1, 2, 17])
@@ -220,6 +225,8 @@ def test_tiny_horizons(kind, D, T):
               s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32), bandwidth=2)
     for mode in (N, Q, J):
         _parity(wl, mode)
+        if kind != pn.CELL_DIAG_TANH and D <= 8:
+            _parity(wl, mode, flags=pn.FLAG_MULTI_LAUNCH)
 
 
 @pytest.mark.parametrize("kind, D, m", [(pn.CELL_TANH_RNN, 24, 37), (pn.CELL_GRU, 16, 19),
@@ -589,6 +596,71 @@ def test_persistent_and_multilaunch_paths_agree(cfg, B, T, mode):
     ref = run_oracle(wl, mode)
     check_parity(wl, mode, a, ref, label=_label(wl) + " persistent")
     check_parity(wl, mode, b, ref, label=_label(wl) + " launch per phase")
+
+
+# ---------------------------------------------------------------- one workgroup
+
+def _small_case(kind, D, B, T, seed, m=3, tol=1e-6, damping=1.0, window=0, scale=1.0):
+    rng = np.random.default_rng(seed)
+    params = workloads.random_cell_params(kind, D, m, rng, scale)
+    return dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=tol, damping=damping, window=window,
+                max_iter=(window or T), params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
+                s0=(0.3 * rng.standard_normal((B, D))).astype(np.float32), bandwidth=1)
+
+
+@pytest.mark.parametrize("kind", [pn.CELL_TANH_RNN, pn.CELL_GRU, pn.CELL_EULER_TANH])
+@pytest.mark.parametrize("D, B, T", [(1, 3, 80), (3, 1, 1024), (4, 4, 256), (5, 2, 256), (8, 3, 170),
+                                     (2, 7, 33)])
+def test_one_workgroup_solver_every_mode(kind, D, B, T):
+    # one step per thread (B*T <= 256), up to four (1024 pairs at D <= 4,
+    # 512 at D <= 8), ragged thread tails, rows that start inside a thread's
+    # steps; every mode, the band at k = 1
+    wl = _small_case(kind, D, B, T, 1300 + 10 * D + B + kind)
+    for mode in (N, Q, J, P, pn.BANDED):
+        if mode == P and max(run_oracle(wl, P).hist[0]) > 1e3:
+            # Picard through huge transients (1e33 on some of these random
+            # cells): the count is set by their rounding, see
+            # test_cfg2_gru_picard_small
+            continue
+        _parity(wl, mode)
+
+
+@pytest.mark.parametrize("kind", [pn.CELL_TANH_RNN, pn.CELL_GRU])
+def test_one_workgroup_solver_windows_and_damping(kind):
+    # consecutive windows with a short last one, step damping, the window's
+    # initial state carried from the window before
+    wl = _small_case(kind, 6, 2, 500, 1400 + kind, tol=1e-5, damping=0.6, window=96)
+    for mode in (Q, N):
+        _parity(wl, mode)
+
+
+def test_one_workgroup_solver_limits_and_outcomes():
+    # 1024 pairs at D = 4 and 512 at D = 8 run in one workgroup, one more
+    # pair goes to the multi-launch driver; both meet the bar
+    for D, B, T in ((4, 4, 256), (4, 1, 1025), (8, 2, 256), (8, 1, 513)):
+        _parity(_small_case(pn.CELL_TANH_RNN, D, B, T, 1500 + D + T), N)
+    wl = _small_case(pn.CELL_GRU, 4, 2, 120, 1510)
+    for mi in (0, 1, 2):
+        gpu = run_gpu(wl, Q, max_iter=mi, tol=0.0)
+        ref = run_oracle(wl, Q, max_iter=mi, tol=0.0)
+        assert gpu.status == ref.status == oracle.NOT_CONVERGED and gpu.iters == ref.iters == mi
+        assert np.max(np.abs(gpu.out_np - ref.s)) <= 1e-4
+        assert len(gpu.resid_hist) == mi + 1
+    gpu = run_gpu(wl, N, tol=1e6)
+    assert gpu.status == pn.OK and gpu.iters == 0
+    np.testing.assert_array_equal(gpu.out_np, np.broadcast_to(wl["s0"][:, None, :], gpu.out_np.shape))
+    bad = dict(wl)
+    bad["x"] = wl["x"].copy()
+    bad["x"][1, 70, 2] = np.nan
+    gpu = run_gpu(bad, N)
+    ref = run_oracle(bad, N)
+    assert gpu.status == ref.status == oracle.NONFINITE and gpu.iters == ref.iters == 0
+    # a non-finite window stops the solve: later windows are not reached
+    bad.update(window=40, max_iter=40)
+    gpu = run_gpu(bad, Q)
+    ref = run_oracle(bad, Q)
+    assert gpu.status == ref.status == oracle.NONFINITE
+    assert gpu.window_iters[:len(ref.window_iters)] == ref.window_iters
 
 
 # ---------------------------------------------------------------- the scan alone
