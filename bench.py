@@ -201,6 +201,36 @@ def cpu_detail(cfg, mode, switch_mode=-1, switch_ratio=0.5, storage=None):
     return out
 
 
+CEILING_BYTES = 512 << 20      # per array: the headline's x (8 x 65536 x 256 floats)
+CEILING_PATTERNS = (("read", 0), ("write", 1), ("copy", 2), ("2r1w_flat", 3), ("2r1w_rows", 4))
+
+
+def ceilings(reps=10):
+    """Measured ceilings of this GPU from libpn_ceiling.so (include/pn_ceiling.h):
+    GB/s of plain streaming kernels and TFLOP/s of a plain FP32 matrix-core
+    loop, best and median of `reps` event-timed launches."""
+    import ctypes
+    path = os.path.join(ROOT, "newton_evaluation_nonlinear_amd", "libpn_ceiling.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build with `python -m newton_evaluation_nonlinear_amd._build`")
+    L = ctypes.CDLL(path)
+    dbl = ctypes.c_double
+    L.pnc_hbm.argtypes = [ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(dbl), ctypes.POINTER(dbl)]
+    L.pnc_mfma_f32.argtypes = [ctypes.c_int, ctypes.POINTER(dbl), ctypes.POINTER(dbl)]
+    L.pnc_last_error.restype = ctypes.c_char_p
+    out = {"unit": "GB/s", "bytes_per_array": CEILING_BYTES, "reps": reps}
+    for name, pat in CEILING_PATTERNS:
+        best, med = dbl(0.0), dbl(0.0)
+        if L.pnc_hbm(pat, CEILING_BYTES, reps, ctypes.byref(best), ctypes.byref(med)) != 0:
+            raise SystemExit("ceiling microbenchmark failed: " + L.pnc_last_error().decode())
+        out[name] = {"best": best.value, "median": med.value}
+    best, med = dbl(0.0), dbl(0.0)
+    if L.pnc_mfma_f32(reps, ctypes.byref(best), ctypes.byref(med)) != 0:
+        raise SystemExit("ceiling microbenchmark failed: " + L.pnc_last_error().decode())
+    out["mfma_f32_tflops"] = {"best": best.value, "median": med.value}
+    return out
+
+
 COPY_PROBE_BYTES = 64 * 1024 * 1024 * 4   # read once and written once by the probe copy
 
 
@@ -294,10 +324,11 @@ def main():
     ap.add_argument("--storage", choices=("f32", "f16"), default="f32",
                     help="f16: x and the iterate stored in binary16 (channel-wise cell), "
                          "float32 arithmetic, tol 1e-3")
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-detail", action="store_true",
-                    help="also time the float64 sequential loop and oracle solve on one core "
-                         "and split across the batch over the host's cores (cpu_detail)")
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the CPU baselines (cpu_baseline and cpu_detail)")
+    ap.add_argument("--cpu-detail", action="store_true", help=argparse.SUPPRESS)   # now the default
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the ceiling microbenchmarks (libpn_ceiling.so)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 256 MiB device copy first (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -428,12 +459,25 @@ def main():
                    "status": last.status, "parallelism": "single GPU"},
         "roofline": roof,
     }
+    if not args.no_ceiling:
+        ceil = ceilings()
+        line["ceilings"] = ceil
+        if roof["bound"] == "hbm":
+            # the pattern of the steady apply kernel: two row streams in, one out
+            c = ceil["2r1w_rows"]["median"]
+            roof.update(measured_ceiling={"pattern": "2r1w_rows", "value": c, "unit": "GB/s"},
+                        frac_of_measured_ceiling=roof["achieved"] / c)
+        elif roof["bound"] == "mfma":
+            c = ceil["mfma_f32_tflops"]["median"]
+            roof.update(measured_ceiling={"pattern": "mfma_f32", "value": c, "unit": "TFLOP/s"},
+                        frac_of_measured_ceiling=roof["achieved"] / c)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.config, mode, smode, args.switch_ratio,
                                             "f16" if half else None)
-    if args.cpu_detail:
         line["cpu_detail"] = cpu_detail(args.config, mode, smode, args.switch_ratio,
                                         "f16" if half else None)
+        line["cpu_detail"]["context"] = ("the article's A100 timings of an unspecified T=2048 RNN "
+                                         "forward: sequential 12.3 ms, Picard 4.2 ms, quasi-Newton 3.1 ms")
     print(json.dumps(line), flush=True)
 
 

@@ -3,7 +3,8 @@
     python -m newton_evaluation_nonlinear_amd._build
 
 Each source is compiled to an object in parallel (the device code of every
-file is self-contained), then the objects are linked into one shared library.
+file is self-contained), then the objects are linked into libpn.so; the
+ceiling microbenchmarks (pn_ceiling.hip) become libpn_ceiling.so.
 """
 
 import os
@@ -16,6 +17,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpn.so")
+# the ceiling microbenchmarks (a measurement tool, include/pn_ceiling.h)
+CEILING_LIB = os.path.join(HERE, "libpn_ceiling.so")
+CEILING_SOURCES = ["pn_ceiling.hip"]
 
 SOURCES = ["pn_api.cpp", "pn_diag.hip", "pn_cell.hip", "pn_dense.hip", "pn_scan.hip", "pn_static.hip", "pn_small.hip"]
 
@@ -52,11 +56,19 @@ def build(verbose=False):
             objs.append(obj)
             cmds.append([hipcc()] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-c",
                                              os.path.join(CSRC, src), "-o", obj])
+        cobjs = []
+        for src in CEILING_SOURCES:
+            obj = os.path.join(tmpd, src + ".o")
+            cobjs.append(obj)
+            cmds.append([hipcc()] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-c",
+                                             os.path.join(CSRC, src), "-o", obj])
         workers = min(len(cmds), max(1, (os.cpu_count() or 1)))
         with ThreadPoolExecutor(max_workers=workers) as ex:
             logs = list(ex.map(_run, cmds))
         tmp = LIB + ".tmp"
         logs.append(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs))
+        ctmp = CEILING_LIB + ".tmp"
+        logs.append(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", ctmp] + cobjs))
     if verbose:
         for cmd in cmds:
             print(" ".join(cmd), flush=True)
@@ -65,6 +77,7 @@ def build(verbose=False):
             if lines:
                 sys.stderr.write("\n".join(lines) + "\n")
     os.replace(tmp, LIB)
+    os.replace(ctmp, CEILING_LIB)
     return LIB
 
 

@@ -1,0 +1,242 @@
+// Ceiling microbenchmarks: what plain streaming kernels and a plain FP32
+// matrix-core loop attain on this GPU, measured with HIP events.  They give
+// the solver's kernels a measured ceiling next to the data-sheet peaks
+// (HBM 8 TB/s, FP32 matrix 157.3 TFLOP/s).
+//
+// Patterns (bytes moved per repetition in brackets, n = bytes per array):
+//   PNC_READ       sum of one array                          [n]
+//   PNC_WRITE      fill of one array                         [n]
+//   PNC_COPY       y = x                                     [2n]
+//   PNC_2R1W       s = x + 0.5 s, flat float4 grid stride    [3n]
+//   PNC_2R1W_ROWS  s = x + 0.5 s in the access order of the channel-wise
+//                  apply kernel: [8, T, 256] float arrays, one workgroup per
+//                  (batch row, 1024-step chunk), one channel per thread, rows
+//                  walked in order with 8-step register prefetch      [3n]
+// The MFMA loop runs independent chains of v_mfma_f32_32x32x2f32 on register
+// operands (4096 flops each) on every SIMD.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <functional>
+#include <string>
+#include <vector>
+
+#include "../../include/pn_ceiling.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(const char* what, hipError_t e) {
+    g_err = std::string(what) + ": " + hipGetErrorString(e);
+    return -1;
+}
+
+#define PNC_HIP(call)                          \
+    do {                                       \
+        hipError_t e_ = (call);                \
+        if (e_ != hipSuccess) return fail(#call, e_); \
+    } while (0)
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void k_read(const float4* __restrict__ x, size_t n4, float* __restrict__ out) {
+    float acc = 0.0f;
+    for (size_t i = blockIdx.x * static_cast<size_t>(kThreads) + threadIdx.x; i < n4;
+         i += static_cast<size_t>(gridDim.x) * kThreads) {
+        const float4 v = x[i];
+        acc += (v.x + v.y) + (v.z + v.w);
+    }
+    out[blockIdx.x * kThreads + threadIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void k_write(float4* __restrict__ y, size_t n4) {
+    const float4 v = make_float4(1.0f, 2.0f, 3.0f, 4.0f);
+    for (size_t i = blockIdx.x * static_cast<size_t>(kThreads) + threadIdx.x; i < n4;
+         i += static_cast<size_t>(gridDim.x) * kThreads)
+        y[i] = v;
+}
+
+__global__ __launch_bounds__(kThreads) void k_copy(const float4* __restrict__ x, float4* __restrict__ y, size_t n4) {
+    for (size_t i = blockIdx.x * static_cast<size_t>(kThreads) + threadIdx.x; i < n4;
+         i += static_cast<size_t>(gridDim.x) * kThreads)
+        y[i] = x[i];
+}
+
+__global__ __launch_bounds__(kThreads) void k_2r1w(const float4* __restrict__ x, float4* __restrict__ s, size_t n4) {
+    for (size_t i = blockIdx.x * static_cast<size_t>(kThreads) + threadIdx.x; i < n4;
+         i += static_cast<size_t>(gridDim.x) * kThreads) {
+        const float4 a = x[i], b = s[i];
+        s[i] = make_float4(a.x + 0.5f * b.x, a.y + 0.5f * b.y, a.z + 0.5f * b.z, a.w + 0.5f * b.w);
+    }
+}
+
+// [B][T][D] with D = 256: block (chunk c, batch row b), thread = channel
+constexpr int kRowsD = 256, kRowsB = 8, kRowsL = 1024, kPre = 8;
+
+__global__ __launch_bounds__(kThreads) void k_2r1w_rows(const float* __restrict__ x, float* __restrict__ s, int T) {
+    const int c = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int t0 = c * kRowsL;
+    const int n = min(kRowsL, T - t0);
+    const size_t base = (static_cast<size_t>(b) * T + t0) * kRowsD + d;
+    const float* xp = x + base;
+    float* sp = s + base;
+    int t = 0;
+    for (; t + kPre <= n; t += kPre) {
+        float xv[kPre], sv[kPre];
+#pragma unroll
+        for (int u = 0; u < kPre; ++u) {
+            xv[u] = xp[static_cast<size_t>(t + u) * kRowsD];
+            sv[u] = sp[static_cast<size_t>(t + u) * kRowsD];
+        }
+#pragma unroll
+        for (int u = 0; u < kPre; ++u) sp[static_cast<size_t>(t + u) * kRowsD] = xv[u] + 0.5f * sv[u];
+    }
+    for (; t < n; ++t) sp[static_cast<size_t>(t) * kRowsD] = xp[static_cast<size_t>(t) * kRowsD] + 0.5f * sp[static_cast<size_t>(t) * kRowsD];
+}
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+constexpr int kMfmaChains = 4;
+
+__global__ __launch_bounds__(kThreads) void k_mfma(int iters, float* __restrict__ out) {
+    v16f acc[kMfmaChains];
+#pragma unroll
+    for (int q = 0; q < kMfmaChains; ++q) acc[q] = v16f{};
+    const float a = 1.0f + 1e-7f * threadIdx.x, b = 1.0f - 1e-7f * threadIdx.x;
+    for (int k = 0; k < iters; ++k) {
+#pragma unroll
+        for (int q = 0; q < kMfmaChains; ++q) acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[q], 0, 0, 0);
+    }
+    float r = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kMfmaChains; ++q) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) r += acc[q][e];
+    }
+    out[blockIdx.x * kThreads + threadIdx.x] = r;
+}
+
+int timed(hipStream_t st, int reps, const std::function<void()>& launch, std::vector<float>* ms) {
+    hipEvent_t e0, e1;
+    PNC_HIP(hipEventCreate(&e0));
+    PNC_HIP(hipEventCreate(&e1));
+    launch();          // warm-up
+    PNC_HIP(hipGetLastError());
+    PNC_HIP(hipStreamSynchronize(st));
+    for (int r = 0; r < reps; ++r) {
+        PNC_HIP(hipEventRecord(e0, st));
+        launch();
+        PNC_HIP(hipEventRecord(e1, st));
+        PNC_HIP(hipEventSynchronize(e1));
+        float t = 0.0f;
+        PNC_HIP(hipEventElapsedTime(&t, e0, e1));
+        ms->push_back(t);
+    }
+    PNC_HIP(hipGetLastError());
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return 0;
+}
+
+void best_median(std::vector<float> ms, double work, double* best, double* median) {
+    std::sort(ms.begin(), ms.end());
+    *best = work / (ms.front() * 1e-3);
+    *median = work / (ms[ms.size() / 2] * 1e-3);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pnc_hbm(int pattern, size_t bytes, int reps, double* best_gbs, double* median_gbs) {
+    g_err.clear();
+    if (!best_gbs || !median_gbs || reps < 1 || pattern < PNC_READ || pattern > PNC_2R1W_ROWS) {
+        g_err = "bad argument";
+        return -1;
+    }
+    int dev = 0, cus = 0;
+    PNC_HIP(hipGetDevice(&dev));
+    PNC_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    size_t n4 = bytes / 16;
+    int T = 0;
+    if (pattern == PNC_2R1W_ROWS) {
+        T = static_cast<int>(bytes / (sizeof(float) * kRowsB * kRowsD));
+        T = std::max(kRowsL, T / kRowsL * kRowsL);
+        n4 = static_cast<size_t>(kRowsB) * T * kRowsD / 4;
+    }
+    const size_t nbytes = n4 * 16;
+    hipStream_t st;
+    PNC_HIP(hipStreamCreate(&st));
+    float *x = nullptr, *y = nullptr, *out = nullptr;
+    const int grid = cus * 8;
+    PNC_HIP(hipMalloc(&x, nbytes));
+    PNC_HIP(hipMalloc(&y, nbytes));
+    PNC_HIP(hipMalloc(&out, sizeof(float) * grid * kThreads));
+    PNC_HIP(hipMemsetAsync(x, 0, nbytes, st));
+    PNC_HIP(hipMemsetAsync(y, 0, nbytes, st));
+    std::vector<float> ms;
+    double moved = 0.0;
+    int rc = 0;
+    switch (pattern) {
+        case PNC_READ:
+            moved = nbytes;
+            rc = timed(st, reps, [&] { k_read<<<grid, kThreads, 0, st>>>(reinterpret_cast<const float4*>(x), n4, out); }, &ms);
+            break;
+        case PNC_WRITE:
+            moved = nbytes;
+            rc = timed(st, reps, [&] { k_write<<<grid, kThreads, 0, st>>>(reinterpret_cast<float4*>(y), n4); }, &ms);
+            break;
+        case PNC_COPY:
+            moved = 2.0 * nbytes;
+            rc = timed(st, reps, [&] { k_copy<<<grid, kThreads, 0, st>>>(reinterpret_cast<const float4*>(x), reinterpret_cast<float4*>(y), n4); }, &ms);
+            break;
+        case PNC_2R1W:
+            moved = 3.0 * nbytes;
+            rc = timed(st, reps, [&] { k_2r1w<<<grid, kThreads, 0, st>>>(reinterpret_cast<const float4*>(x), reinterpret_cast<float4*>(y), n4); }, &ms);
+            break;
+        default:
+            moved = 3.0 * nbytes;
+            rc = timed(st, reps, [&] { k_2r1w_rows<<<dim3(T / kRowsL, kRowsB), kThreads, 0, st>>>(x, y, T); }, &ms);
+            break;
+    }
+    (void)hipStreamSynchronize(st);
+    (void)hipFree(x);
+    (void)hipFree(y);
+    (void)hipFree(out);
+    (void)hipStreamDestroy(st);
+    if (rc != 0) return rc;
+    best_median(ms, moved / 1e9, best_gbs, median_gbs);
+    return 0;
+}
+
+int pnc_mfma_f32(int reps, double* best_tflops, double* median_tflops) {
+    g_err.clear();
+    if (!best_tflops || !median_tflops || reps < 1) {
+        g_err = "bad argument";
+        return -1;
+    }
+    int dev = 0, cus = 0;
+    PNC_HIP(hipGetDevice(&dev));
+    PNC_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    hipStream_t st;
+    PNC_HIP(hipStreamCreate(&st));
+    const int grid = cus * 2;            // 8 wavefronts per CU, two per SIMD
+    const int iters = 4096;
+    float* out = nullptr;
+    PNC_HIP(hipMalloc(&out, sizeof(float) * grid * kThreads));
+    std::vector<float> ms;
+    const int rc = timed(st, reps, [&] { k_mfma<<<grid, kThreads, 0, st>>>(iters, out); }, &ms);
+    (void)hipStreamSynchronize(st);
+    (void)hipFree(out);
+    (void)hipStreamDestroy(st);
+    if (rc != 0) return rc;
+    const double flops = static_cast<double>(grid) * (kThreads / 64) * iters * kMfmaChains * 4096.0;
+    best_median(ms, flops / 1e12, best_tflops, median_tflops);
+    return 0;
+}
+
+const char* pnc_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

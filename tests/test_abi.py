@@ -261,3 +261,20 @@ def test_python_binding_checks_shapes_before_any_launch():
         pn.affine_scan(torch.zeros(B, T, D), torch.zeros(B, T, D), s0, dense=True)
     with pytest.raises(ValueError, match="s0 must have shape"):
         pn.affine_scan(torch.zeros(B, T, D), torch.zeros(B, T, D), torch.zeros(B, D + 1))
+
+
+def test_ceiling_tool_exports_every_declared_symbol():
+    text = open(os.path.join(ROOT, "include", "pn_ceiling.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(pnc_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["pnc_hbm", "pnc_last_error", "pnc_mfma_f32"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "newton_evaluation_nonlinear_amd", "libpn_ceiling.so"))
+    for name in names:
+        assert hasattr(lib, name), name
+    # argument checks come before any device call
+    d = ctypes.c_double(0.0)
+    lib.pnc_hbm.argtypes = [ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                            ctypes.POINTER(ctypes.c_double)]
+    lib.pnc_last_error.restype = ctypes.c_char_p
+    assert lib.pnc_hbm(9, 1 << 20, 1, ctypes.byref(d), ctypes.byref(d)) == -1
+    assert lib.pnc_last_error().decode() == "bad argument"
