@@ -77,6 +77,8 @@ struct Plan {
     bool persist_ok;       // shape allows the one-launch persistent solver
     bool small;            // the window fits one workgroup: every window, iteration and
                            // check in one launch (pn_small.hip)
+    bool resident_ok;      // shape has the one-launch resident form (cell_resident), used
+                           // when all B x NC chunks fit on the device at once
     bool recompute;        // channel-wise cell, float storage: first update stores nothing,
                            // the second recomputes s^(1) (kFirstNS, kSecondR)
     int fc;                // matrix cell, diagonal mode, few chunks (CellArgs::fc): the apply
@@ -206,6 +208,8 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
     p.small = p.matrix_cell && !half && !p.advancing && chunk == 0 &&
               !(o && (o->flags & PN_FLAG_MULTI_LAUNCH)) && p.D <= 8 &&
               static_cast<int64_t>(p.B) * p.W <= small_max_pairs_for(p.D);
+    p.resident_ok = p.matrix_cell && !p.dense && !half && !p.advancing && (p.fc & kFcCheck) &&
+                    p.DP % 16 == 0 && !p.small;
     p.hist_cap = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(p.nwin) * (p.W + 1), 1 << 16));
     layout(p, nullptr);
     return PN_OK;
@@ -238,7 +242,7 @@ void layout(Plan& p, const Plan* other) {
     p.off_w = off;
     if (p.matrix_cell) off = align_up(off + sizeof(float) * prepared_total_floats(p.kind, p.DP, p.m));
     p.off_sync = p.off_winfo = p.off_hist = off;
-    if (p.persist_ok || p.small) {
+    if (p.persist_ok || p.small || p.resident_ok) {
         p.off_sync = off; off = align_up(off + 256);
         p.off_winfo = off; off = align_up(off + sizeof(int32_t) * 2 * p.nwin);
         p.off_hist = off; off = align_up(off + sizeof(float) * p.hist_cap);
@@ -258,6 +262,7 @@ int make_plans(Plan& p, Plan& p2, bool* has2, const pn_cell* cell, int64_t B, in
     if (rc != PN_OK) return rc;
     p.persist_ok = p2.persist_ok = false;
     p.small = p2.small = false;
+    p.resident_ok = p2.resident_ok = false;
     p.recompute = p2.recompute = false;
     p.fc = p2.fc = 0;
     p.Lc = p.L; p2.Lc = p2.L;
@@ -978,51 +983,46 @@ struct Backing {
     ThreadRes* res;          // dev_ring set, host = a host shadow array
 };
 
-// The whole solve in one launch of the one-workgroup solver, then one copy of
-// its per-window counts, statuses and residual history back to the host.
-int solve_small(SolveCtx& c, const float* x, const float* s0, float* out, int64_t T,
-                std::vector<int>* wit, int* total, int* overall) {
-    const Plan& p = *c.p;
-    char* ws = c.ws;
-    SmallArgs a{};
-    a.params = c.params; a.x = x; a.s0 = s0; a.out = out; a.T = T;
-    a.W = static_cast<int32_t>(p.W); a.nwin = p.nwin; a.B = p.B; a.D = p.D; a.m = p.m;
-    a.mode = p.mode; a.band = p.band; a.max_iter = c.max_iter;
-    a.undamped = c.lam == 1.0f; a.tol = c.tol; a.lam = c.lam;
-    // results region [hist_len | win_iters, win_status | history], laid out
-    // as in the workspace: written straight to pinned host memory, or, for
-    // pn_eval_noalloc (records in device memory), to the workspace and copied
-    // back once
-    const size_t nbytes = p.off_hist + sizeof(float) * p.hist_cap - p.off_sync;
-    char* dev_info = ws + p.off_sync;
-    const char* host_info = nullptr;
+// Where a one-launch solver writes its per-window counts, statuses and
+// residual history ([hist_len | win_iters, win_status | history], laid out as
+// the workspace region off_sync .. off_hist + hist_cap): straight to pinned
+// host memory, or, for pn_eval_noalloc (records in device memory), to the
+// workspace, copied back once after the launch.
+struct OneLaunchInfo {
+    size_t nbytes = 0;
+    char* dev = nullptr;
+    const char* host = nullptr;
     std::vector<char> copy;
+};
+
+int one_launch_info(SolveCtx& c, OneLaunchInfo* inf) {
+    const Plan& p = *c.p;
+    inf->nbytes = p.off_hist + sizeof(float) * p.hist_cap - p.off_sync;
+    inf->dev = c.ws + p.off_sync;
     if (!c.res->dev_ring) {
         char* h = nullptr;
-        int rc = small_info_buffer(c.res, nbytes, &h, &dev_info);
+        int rc = small_info_buffer(c.res, inf->nbytes, &h, &inf->dev);
         if (rc != PN_OK) return rc;
-        host_info = h;
+        inf->host = h;
     }
-    a.hist_len = reinterpret_cast<int32_t*>(dev_info);
-    a.win_iters = reinterpret_cast<int32_t*>(dev_info + (p.off_winfo - p.off_sync));
-    a.win_status = a.win_iters + p.nwin;
-    a.hist = reinterpret_cast<float*>(dev_info + (p.off_hist - p.off_sync));
-    a.hist_cap = p.hist_cap;
-    const bool timed = c.tm->take();
-    size_t e0 = 0, e1 = 0;
-    if (timed) { int rc = request_timing(c, &e0, &e1); if (rc) return rc; }
-    PN_HIP(launch_small_solve(p.kind, p.dense, a, c.st));
-    if (timed) { int rc = check_timed_launch(); if (rc) return rc; }
+    return PN_OK;
+}
+
+// After the launch: bring the results to the host and fill counts, statuses,
+// history and the profile entry of the launch.
+int one_launch_results(SolveCtx& c, OneLaunchInfo* inf, int64_t T, std::vector<int>* wit, int* total,
+                       int* overall, bool timed, size_t e0, size_t e1) {
+    const Plan& p = *c.p;
     if (c.res->dev_ring) {
-        copy.resize(nbytes);
-        PN_HIP(hipMemcpyAsync(copy.data(), dev_info, nbytes, hipMemcpyDeviceToHost, c.st));
-        host_info = copy.data();
+        inf->copy.resize(inf->nbytes);
+        PN_HIP(hipMemcpyAsync(inf->copy.data(), inf->dev, inf->nbytes, hipMemcpyDeviceToHost, c.st));
+        inf->host = inf->copy.data();
     }
     PN_HIP(hipStreamSynchronize(c.st));
     int32_t hlen = 0;
-    std::memcpy(&hlen, host_info, sizeof(hlen));
-    const int32_t* wi = reinterpret_cast<const int32_t*>(host_info + (p.off_winfo - p.off_sync));
-    const float* hist = reinterpret_cast<const float*>(host_info + (p.off_hist - p.off_sync));
+    std::memcpy(&hlen, inf->host, sizeof(hlen));
+    const int32_t* wi = reinterpret_cast<const int32_t*>(inf->host + (p.off_winfo - p.off_sync));
+    const float* hist = reinterpret_cast<const float*>(inf->host + (p.off_hist - p.off_sync));
     if (c.hist) c.hist->assign(hist, hist + std::min(hlen, p.hist_cap));
     *total = 0;
     *overall = PN_OK;
@@ -1043,6 +1043,89 @@ int solve_small(SolveCtx& c, const float* x, const float* s0, float* out, int64_
         c.tm->apply_bytes.push_back(bytes);
         c.tm->apply_flops.push_back(flops);
     }
+    return PN_OK;
+}
+
+// The whole solve in one launch of the one-workgroup solver.
+int solve_small(SolveCtx& c, const float* x, const float* s0, float* out, int64_t T,
+                std::vector<int>* wit, int* total, int* overall) {
+    const Plan& p = *c.p;
+    OneLaunchInfo inf;
+    int rc = one_launch_info(c, &inf);
+    if (rc != PN_OK) return rc;
+    SmallArgs a{};
+    a.params = c.params; a.x = x; a.s0 = s0; a.out = out; a.T = T;
+    a.W = static_cast<int32_t>(p.W); a.nwin = p.nwin; a.B = p.B; a.D = p.D; a.m = p.m;
+    a.mode = p.mode; a.band = p.band; a.max_iter = c.max_iter;
+    a.undamped = c.lam == 1.0f; a.tol = c.tol; a.lam = c.lam;
+    a.hist_len = reinterpret_cast<int32_t*>(inf.dev);
+    a.win_iters = reinterpret_cast<int32_t*>(inf.dev + (p.off_winfo - p.off_sync));
+    a.win_status = a.win_iters + p.nwin;
+    a.hist = reinterpret_cast<float*>(inf.dev + (p.off_hist - p.off_sync));
+    a.hist_cap = p.hist_cap;
+    const bool timed = c.tm->take();
+    size_t e0 = 0, e1 = 0;
+    if (timed) { rc = request_timing(c, &e0, &e1); if (rc) return rc; }
+    PN_HIP(launch_small_solve(p.kind, p.dense, a, c.st));
+    if (timed) { rc = check_timed_launch(); if (rc) return rc; }
+    return one_launch_results(c, &inf, T, wit, total, overall, timed, e0, e1);
+}
+
+// The whole solve as one cooperative launch of the resident solver.  Returns
+// PN_EUNSUPPORTED (nothing launched) when the chunks do not all fit on the
+// device at once.
+int solve_resident(SolveCtx& c, const float* x, const float* s0, float* out, int64_t T,
+                   std::vector<int>* wit, int* total, int* overall) {
+    const Plan& p = *c.p;
+    int dev = 0, coop = 0, nb = 0;
+    PN_HIP(hipGetDevice(&dev));
+    PN_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
+    if (!coop) return PN_EUNSUPPORTED;
+    PN_HIP(cell_resident_max_blocks(p.kind, p.DP, p.L, p.m, &nb));
+    if (static_cast<int64_t>(p.B) * p.NC > nb) return PN_EUNSUPPORTED;
+    OneLaunchInfo inf;
+    int rc = one_launch_info(c, &inf);
+    if (rc != PN_OK) return rc;
+    char* ws = c.ws;
+    ResidentArgs a{};
+    a.w = reinterpret_cast<const float*>(ws + p.off_w);
+    a.x = x; a.out = out; a.s0 = s0; a.T = T;
+    a.W = static_cast<int32_t>(p.W); a.nwin = p.nwin; a.B = p.B; a.D = p.D; a.m = p.m; a.L = p.L;
+    a.NC = p.NC; a.mode = p.mode; a.undamped = c.lam == 1.0f; a.max_iter = c.max_iter;
+    a.lam = c.lam; a.tol = c.tol;
+    a.mapA = reinterpret_cast<float*>(ws + p.off_aggA);
+    a.mapB = reinterpret_cast<float*>(ws + p.off_aggB);
+    a.halo = reinterpret_cast<float*>(ws + p.off_halo);
+    a.s0n = reinterpret_cast<float*>(ws + p.off_carry);
+    Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + p.off_ctrl);
+    a.rslot = &ctrl->rmax[0][0][0];
+    a.bar = &ctrl->bar;
+    a.err = &ctrl->bar_err;
+    a.hist_len = reinterpret_cast<int32_t*>(inf.dev);
+    a.win_iters = reinterpret_cast<int32_t*>(inf.dev + (p.off_winfo - p.off_sync));
+    a.win_status = a.win_iters + p.nwin;
+    a.hist = reinterpret_cast<float*>(inf.dev + (p.off_hist - p.off_sync));
+    a.hist_cap = p.hist_cap;
+    // residual slots, barrier counter and error flag start at zero
+    PN_HIP(hipMemsetAsync(ctrl, 0, sizeof(Ctrl), c.st));
+    const bool timed = c.tm->take();
+    size_t e0 = 0, e1 = 0;
+    if (timed) { rc = request_timing(c, &e0, &e1); if (rc) return rc; }
+    {
+        const hipError_t le = launch_cell_resident(p.kind, p.DP, a, c.st);
+        if (le == hipErrorCooperativeLaunchTooLarge) {
+            (void)hipGetLastError();
+            g_launch_timing = LaunchTiming{};
+            return PN_EUNSUPPORTED;
+        }
+        if (le != hipSuccess) return fail(PN_EHIP, "cooperative launch failed: %s", hipGetErrorString(le));
+    }
+    if (timed) { rc = check_timed_launch(); if (rc) return rc; }
+    rc = one_launch_results(c, &inf, T, wit, total, overall, timed, e0, e1);
+    if (rc != PN_OK) return rc;
+    unsigned err = 0;
+    PN_HIP(hipMemcpy(&err, a.err, sizeof(err), hipMemcpyDeviceToHost));
+    if (err != 0) return fail(PN_EHIP, "grid barrier of the resident solver timed out");
     return PN_OK;
 }
 
@@ -1139,11 +1222,17 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     std::vector<int32_t> accepted, wsw;
     const int64_t m = p.m;
     bool persisted = false;
+    const bool multi = o && (o->flags & (PN_FLAG_MULTI_LAUNCH | PN_FLAG_PERSISTENT));
     if (small) {
         rc = solve_small(c, x, s0, out, T, &wit, &total, &overall);
         if (rc != PN_OK) return rc;
         persisted = true;
-    } else if (p.persist_ok && o && (o->flags & PN_FLAG_PERSISTENT)) {
+    } else if (p.resident_ok && !multi && max_iter <= kSmallMaxIter) {
+        rc = solve_resident(c, x, s0, out, T, &wit, &total, &overall);
+        if (rc == PN_OK) persisted = true;
+        else if (rc != PN_EUNSUPPORTED) return rc;
+    }
+    if (!persisted && p.persist_ok && o && (o->flags & PN_FLAG_PERSISTENT)) {
         rc = solve_persistent(c, x, s0, out, T, &wit, &total, &overall);
         if (rc == PN_OK) persisted = true;
         else if (rc != PN_EUNSUPPORTED) return rc;

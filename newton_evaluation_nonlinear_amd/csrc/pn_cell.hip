@@ -1613,4 +1613,353 @@ hipError_t launch_dense_carry(const CarryArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------- resident solver
+// The whole solve of a matrix cell in a diagonal mode as one cooperative
+// launch, for shapes whose B x NC chunks are co-resident (one workgroup per
+// chunk).  Unlike cell_persist, a workgroup keeps its chunk on chip for the
+// whole window: the rows of the iterate in LDS, the input projections and the
+// weights in registers (CellRegs), and the per-step coefficients of the last
+// evaluation in LDS, which are the maps of the next update.  An iteration is
+// therefore one evaluation (at the new iterate) instead of two, and the only
+// traffic between workgroups is small: the chunk maps of the iteration, the
+// last row of every chunk (the next chunk's halo), the residual maxima and the
+// next window's initial state.  These go through relaxed device-scope atomic
+// loads and stores, which are coherent across the XCDs' L2 caches without
+// cache-wide fences; a grid barrier (a relaxed atomic counter, entered after
+// every memory operation of the workgroup has completed) separates the
+// iterations.  Every wait is bounded: on a timeout the error flag is set and
+// every workgroup leaves, so a broken barrier cannot hang the device.
+__device__ __forceinline__ float ld_dev(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Grid barrier: the workgroup's memory operations complete (s_waitcnt 0),
+// then one arrival per workgroup on a counter that only grows; wait for
+// epoch x gridsize arrivals.
+__device__ __forceinline__ bool resident_sync(const ResidentArgs& a, unsigned& epoch, unsigned nblocks) {
+    __shared__ int ok;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    ++epoch;
+    if (threadIdx.x == 0) {
+        ok = 1;
+        __hip_atomic_fetch_add(a.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned target = epoch * nblocks;
+        unsigned spins = 0;
+        while (__hip_atomic_load(a.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins > (1u << 24) || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = 0;
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    return ok != 0;
+}
+
+template <int CELL, int DP>
+__global__ __launch_bounds__(kThreads) void cell_resident(ResidentArgs a) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    constexpr int PS = iterate_stride<DP>();
+    constexpr int NS = kThreads / DP;            // fold segments per channel
+    const int L = a.L, m = a.m, D = a.D, B = a.B;
+    const int xs = x_stride(m);
+    const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const unsigned nblocks = gridDim.x * gridDim.y;
+    float* Pb = lds;                             // [L+1][PS] rows t0-1 .. t1-1 of the iterate
+    float* Nb = Pb + (L + 1) * PS;               // [L+1][PS] the same rows of the next iterate
+    float* V = Nb + (L + 1) * PS;                // [L][DP] f at the iterate
+    float* CO = V + L * DP;                      // [L][DP] diagonal coefficients
+    float* X = CO + L * DP;                      // [L][xs]
+    float* SCR = X + L * xs;                     // [2][kThreads] fold segments
+    float* S0 = SCR + 2 * kThreads;              // [DP] initial state of the window
+    CellRegs<CELL, DP> cr;
+    cr.load(a.w, a.w, D, m);
+    const size_t HS = static_cast<size_t>(B) * a.NC * D;   // parity stride of maps and halo
+    unsigned epoch = 0;
+    int hist_pos = 0, q = 0;                     // q: checks taken so far (residual slot sets rotate)
+    float own_a = 1.0f, own_b = 0.0f;            // this chunk's map of the current iteration (tid < D)
+    for (int wi = 0; wi < a.nwin; ++wi) {
+        const int64_t w0 = static_cast<int64_t>(wi) * a.W;
+        const int Tw = static_cast<int>(a.T - w0 < a.W ? a.T - w0 : a.W);
+        const int NCw = (Tw + L - 1) / L;
+        const bool active = c < NCw;
+        const int t0 = c * L;
+        const int Lc = active ? min(L, Tw - t0) : 0;
+        const bool has_next = c + 1 < NCw;
+        float* P = Pb;
+        float* N = Nb;
+        if (tid < DP)
+            S0[tid] = tid < D ? (wi == 0 ? a.s0[static_cast<int64_t>(b) * D + tid] : ld_dev(a.s0n + b * D + tid)) : 0.0f;
+        uint32_t rb = 0;
+        if (active) {
+            copy_rows_to_lds<kThreads>(X, xs, a.x + (static_cast<int64_t>(b) * a.T + w0 + t0) * m, m, Lc, m);
+            __syncthreads();
+            // s^(0) = s0 on every row
+            for (int e = tid; e < (Lc + 1) * PS; e += kThreads) {
+                const int i = e % PS;
+                P[e] = i < DP ? S0[i] : 0.0f;
+            }
+            cr.project(a.w, X, xs, Lc, m);
+            __syncthreads();
+            // the maps of iteration 0 and r_0
+            cr.template eval<false>(P, V, CO, Lc, L, a.mode, P, rb, nullptr, a.tol);
+            __syncthreads();
+        }
+        if (tid < D && active) {
+            float A = 1.0f, Bc = 0.0f;
+            if (a.mode == kJacobi) {
+                A = 0.0f;
+                Bc = V[(Lc - 1) * DP + tid];
+            } else {
+                for (int j = 0; j < Lc; ++j) {
+                    const float at = CO[j * DP + tid];
+                    Bc = at * Bc + (V[j * DP + tid] - at * P[j * PS + tid]);
+                    A = at * A;
+                }
+            }
+            own_a = A;
+            own_b = Bc;
+            const size_t ci = static_cast<size_t>(b) * a.NC + c;
+            st_dev(a.mapA + ci * D + tid, A);
+            st_dev(a.mapB + ci * D + tid, Bc);
+        }
+        rb = block_max_u32(rb);
+        if (tid == 0 && active)
+            __hip_atomic_fetch_max(a.rslot + ((q % 3) * kRSlots + (b * a.NC + c) % kRSlots) * 64, rb,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!resident_sync(a, epoch, nblocks)) return;
+        int K = 0, status = kStOk;
+        for (int i = 0;; ++i, ++q) {
+            // the check of iteration i, taken alike by every workgroup
+            const int lane = tid & 63;
+            uint32_t rv = lane < kRSlots ? __hip_atomic_load(a.rslot + ((q % 3) * kRSlots + lane) * 64,
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+            const uint32_t r_i = wave_max_u32(rv);
+            int st = -1;
+            if (r_i >= kNonFiniteBits) st = kStNonFinite;
+            else if (__uint_as_float(r_i) <= a.tol) st = kStOk;
+            else if (i >= a.max_iter) st = kStNotConverged;
+            if (c == 0 && b == 0) {
+                if (tid == 0 && hist_pos < a.hist_cap) a.hist[hist_pos] = __uint_as_float(r_i);
+                if (tid < kRSlots)
+                    __hip_atomic_store(a.rslot + (((q + 2) % 3) * kRSlots + tid) * 64, 0u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+            ++hist_pos;
+            if (st >= 0) {
+                K = i;
+                status = st;
+                ++q;
+                break;
+            }
+            uint32_t rbn = 0;
+            if (active) {
+                const int par = i & 1;
+                const size_t ci = static_cast<size_t>(b) * a.NC + c;
+                // row t0-1 of s^(i): the window's s0 before the first chunk
+                // or at i = 0, else the previous chunk's last row
+                if (tid < PS)
+                    P[tid] = tid < D ? ((c == 0 || i == 0) ? S0[tid] : ld_dev(a.halo + par * HS + (ci - 1) * D + tid)) : 0.0f;
+                // the carry: NS segments of the maps of the chunks before c,
+                // each folded into one map, then applied to s0 in order
+                {
+                    const int d = tid % DP, sg_ = tid / DP;
+                    const int per = (c + NS - 1) / NS;
+                    const int k0 = min(c, sg_ * per);
+                    const int k1 = d < D ? min(c, k0 + per) : k0;
+                    const float* mA = a.mapA + par * HS + static_cast<size_t>(b) * a.NC * D;
+                    const float* mB = a.mapB + par * HS + static_cast<size_t>(b) * a.NC * D;
+                    // up to kRF maps per segment are loaded together, then folded
+                    constexpr int kRF = 16;
+                    float pa[kRF], pb[kRF];
+#pragma unroll
+                    for (int u = 0; u < kRF; ++u) {
+                        const int k = k0 + u;
+                        pa[u] = k < k1 ? ld_dev(mA + k * D + d) : 1.0f;
+                        pb[u] = k < k1 ? ld_dev(mB + k * D + d) : 0.0f;
+                    }
+                    float fa = 1.0f, fbv = 0.0f;
+#pragma unroll
+                    for (int u = 0; u < kRF; ++u) {
+                        fbv = pa[u] * fbv + pb[u];
+                        fa = pa[u] * fa;
+                    }
+                    for (int k = k0 + kRF; k < k1; ++k) {
+                        const float ak = ld_dev(mA + k * D + d);
+                        fbv = ak * fbv + ld_dev(mB + k * D + d);
+                        fa = ak * fa;
+                    }
+                    SCR[tid] = fa;
+                    SCR[kThreads + tid] = fbv;
+                }
+                __syncthreads();
+                float c_first = 0.0f, c_next = 0.0f;
+                if (tid < D) {
+                    float xv = S0[tid];
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) xv = SCR[s * DP + tid] * xv + SCR[kThreads + s * DP + tid];
+                    c_first = xv;
+                    c_next = own_a * xv + own_b;
+                }
+                // replay from the carry, damping: N = rows t0-1 .. t1-1 of s^(i+1)
+                const float lam = a.lam;
+                const bool und = a.undamped != 0;
+                if (a.mode == kJacobi) {
+                    const int jl = has_next ? Lc - 1 : Lc;
+                    for (int e = tid; e < jl * PS; e += kThreads) {
+                        const int j = 1 + e / PS, ii = e % PS;
+                        float val = 0.0f;
+                        if (ii < D) {
+                            const float sh = V[(j - 1) * DP + ii], so = P[j * PS + ii];
+                            val = und ? sh : so + lam * (sh - so);
+                        }
+                        N[j * PS + ii] = val;
+                    }
+                    if (tid < PS) {
+                        const bool lv = tid < D;
+                        N[tid] = lv ? (und ? c_first : P[tid] + lam * (c_first - P[tid])) : 0.0f;
+                        if (has_next) {
+                            const float so = P[Lc * PS + tid];
+                            N[Lc * PS + tid] = lv ? (und ? c_next : so + lam * (c_next - so)) : 0.0f;
+                        }
+                    }
+                } else if (tid < D) {
+                    float shat = c_first;
+                    N[tid] = und ? shat : P[tid] + lam * (shat - P[tid]);
+                    const int nrep = has_next ? Lc - 1 : Lc;
+                    for (int j = 0; j < nrep; ++j) {
+                        const int o = j * DP + tid;
+                        shat = V[o] + CO[o] * (shat - P[j * PS + tid]);
+                        const float so = P[(j + 1) * PS + tid];
+                        N[(j + 1) * PS + tid] = und ? shat : so + lam * (shat - so);
+                    }
+                    if (has_next) {
+                        const float so = P[Lc * PS + tid];
+                        N[Lc * PS + tid] = und ? c_next : so + lam * (c_next - so);
+                    }
+                } else if (tid < PS) {
+                    for (int j = 0; j <= Lc; ++j) N[j * PS + tid] = 0.0f;
+                }
+                __syncthreads();
+                // the maps of iteration i+1 at s^(i+1), and r_{i+1}
+                cr.template eval<false>(N, V, CO, Lc, L, a.mode, N, rbn, nullptr, a.tol);
+                __syncthreads();
+                if (tid < D) {
+                    float A = 1.0f, Bc = 0.0f;
+                    if (a.mode == kJacobi) {
+                        A = 0.0f;
+                        Bc = V[(Lc - 1) * DP + tid];
+                    } else {
+                        for (int j = 0; j < Lc; ++j) {
+                            const float at = CO[j * DP + tid];
+                            Bc = at * Bc + (V[j * DP + tid] - at * N[j * PS + tid]);
+                            A = at * A;
+                        }
+                    }
+                    own_a = A;
+                    own_b = Bc;
+                    st_dev(a.mapA + (par ^ 1) * HS + ci * D + tid, A);
+                    st_dev(a.mapB + (par ^ 1) * HS + ci * D + tid, Bc);
+                    st_dev(a.halo + (par ^ 1) * HS + ci * D + tid, N[Lc * PS + tid]);
+                }
+                float* t = P; P = N; N = t;
+            }
+            rbn = block_max_u32(rbn);
+            if (tid == 0 && active)
+                __hip_atomic_fetch_max(a.rslot + (((q + 1) % 3) * kRSlots + (b * a.NC + c) % kRSlots) * 64, rbn,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (!resident_sync(a, epoch, nblocks)) return;
+        }
+        // the window's result: rows t0 .. t1-1 of the last iterate, and the
+        // next window's initial state from the last chunk
+        if (active) {
+            float* o = a.out + (static_cast<int64_t>(b) * a.T + w0 + t0) * D;
+            for (int e = tid; e < Lc * D; e += kThreads) {
+                const int j = e / D, i = e % D;
+                o[e] = P[(j + 1) * PS + i];
+            }
+            if (!has_next && tid < D) st_dev(a.s0n + b * D + tid, P[Lc * PS + tid]);
+        }
+        if (c == 0 && b == 0 && tid == 0) {
+            a.win_iters[wi] = K;
+            a.win_status[wi] = status;
+            *a.hist_len = hist_pos;
+        }
+        if (status == kStNonFinite) break;
+        if (!resident_sync(a, epoch, nblocks)) return;
+    }
+}
+
+size_t resident_lds_bytes(int DP, int L, int m) {
+    const size_t PS = DP + 4, xs = x_stride(m);
+    return sizeof(float) * (2ull * (L + 1) * PS + 2ull * L * DP + static_cast<size_t>(L) * xs + 2ull * kThreads + DP);
+}
+
+template <int CELL, int DP>
+static hipError_t resident_blocks_t(size_t lds, int* nb) {
+    int per_cu = 0, dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (lds > 64 * 1024) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(cell_resident<CELL, DP>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cell_resident<CELL, DP>, kThreads, lds);
+    if (e != hipSuccess) return e;
+    *nb = per_cu * ncu;
+    return hipSuccess;
+}
+
+template <int CELL, int DP>
+static hipError_t launch_resident_t(const ResidentArgs& a, size_t lds, hipStream_t st) {
+    void* args[] = {const_cast<ResidentArgs*>(&a)};
+    LaunchTiming& t = launch_timing();
+    if (t.start) {
+        hipError_t e = hipEventRecord(t.start, st);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(cell_resident<CELL, DP>),
+                                              dim3(a.NC, a.B), dim3(kThreads), args, static_cast<unsigned>(lds), st);
+    if (e != hipSuccess) return e;
+    if (t.start) {
+        e = hipEventRecord(t.stop, st);
+        t = LaunchTiming{};
+    }
+    return e;
+}
+
+// Blocks of cell_resident that fit on the device at once (0 when the shape
+// has no resident form: D padded to 16, 32 or 64, tanh RNN, GRU or Euler).
+hipError_t cell_resident_max_blocks(int kind, int DP, int L, int m, int* nb) {
+    *nb = 0;
+    const size_t lds = resident_lds_bytes(DP, L, m);
+    if (lds > 160 * 1024 || L > kMaxChunk) return hipSuccess;
+#define PN_RES_CASE(K, DPV) if (kind == K && DP == DPV) return resident_blocks_t<K, DPV>(lds, nb);
+    PN_RES_CASE(kCellTanhRnn, 16) PN_RES_CASE(kCellTanhRnn, 32) PN_RES_CASE(kCellTanhRnn, 64)
+    PN_RES_CASE(kCellGru, 16) PN_RES_CASE(kCellGru, 32) PN_RES_CASE(kCellGru, 64)
+    PN_RES_CASE(kCellEuler, 16) PN_RES_CASE(kCellEuler, 32) PN_RES_CASE(kCellEuler, 64)
+#undef PN_RES_CASE
+    return hipSuccess;
+}
+
+hipError_t launch_cell_resident(int kind, int DP, const ResidentArgs& a, hipStream_t st) {
+    const size_t lds = resident_lds_bytes(DP, a.L, a.m);
+#define PN_RES_CASE(K, DPV) if (kind == K && DP == DPV) return launch_resident_t<K, DPV>(a, lds, st);
+    PN_RES_CASE(kCellTanhRnn, 16) PN_RES_CASE(kCellTanhRnn, 32) PN_RES_CASE(kCellTanhRnn, 64)
+    PN_RES_CASE(kCellGru, 16) PN_RES_CASE(kCellGru, 32) PN_RES_CASE(kCellGru, 64)
+    PN_RES_CASE(kCellEuler, 16) PN_RES_CASE(kCellEuler, 32) PN_RES_CASE(kCellEuler, 64)
+#undef PN_RES_CASE
+    return hipErrorInvalidValue;
+}
+
 }  // namespace pn

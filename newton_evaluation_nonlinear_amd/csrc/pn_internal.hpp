@@ -23,7 +23,9 @@ struct Ctrl {
     // the sweep that reads set k % 3 (plain loads: the set is not written
     // while it is read) clears set (k + 2) % 3 for the sweep after it, with
     // device-scope atomic stores.  Each word has a 256-byte line of its own.
-    uint32_t pad_[60];
+    // The resident solver's grid barrier: arrivals and the timeout flag.
+    uint32_t bar, bar_err;
+    uint32_t pad_[58];
     uint32_t rmax[3][16][64];
 };
 constexpr int kRSlots = 16;
@@ -238,6 +240,34 @@ struct SmallArgs {
 };
 int small_max_pairs_for(int D);
 hipError_t launch_small_solve(int kind, bool dense, const SmallArgs& a, hipStream_t st);
+
+// Resident solver (pn_cell.hip, cell_resident): the whole solve of a matrix
+// cell in a diagonal mode as one cooperative launch of B x NC co-resident
+// workgroups that keep their chunk on chip; see the kernel's comment.
+struct ResidentArgs {
+    const float* w;          // prepared weights (global)
+    const float* x;          // [B][T][m]
+    float* out;              // [B][T][D]
+    const float* s0;         // [B][D]
+    int64_t T;
+    int32_t W, nwin, B, D, m, L, NC, mode, undamped, max_iter;
+    float lam, tol;
+    float* mapA;             // [2][B][NC][D] chunk maps by iteration parity
+    float* mapB;
+    float* halo;             // [2][B][NC][D] last row of every chunk, by parity
+    float* s0n;              // [B][D] initial state of the next window
+    uint32_t* rslot;         // [3][kRSlots][64] residual maxima, one 256-byte line per slot
+    unsigned* bar;           // grid barrier arrivals (zero at launch)
+    unsigned* err;           // set on a barrier timeout
+    int32_t* win_iters;      // [nwin] (-1: not reached)
+    int32_t* win_status;
+    int32_t* hist_len;
+    float* hist;
+    int32_t hist_cap;
+};
+
+hipError_t cell_resident_max_blocks(int kind, int DP, int L, int m, int* nb);
+hipError_t launch_cell_resident(int kind, int DP, const ResidentArgs& a, hipStream_t st);
 
 // Standalone affine scan.
 struct ScanArgs {

@@ -663,6 +663,45 @@ def test_one_workgroup_solver_limits_and_outcomes():
     assert gpu.window_iters[:len(ref.window_iters)] == ref.window_iters
 
 
+# ---------------------------------------------------------------- resident solver
+
+@pytest.mark.parametrize("kind, D, m", [(pn.CELL_GRU, 64, 32), (pn.CELL_GRU, 16, 8), (pn.CELL_TANH_RNN, 32, 5),
+                                        (pn.CELL_EULER_TANH, 48, 21), (pn.CELL_GRU, 24, 40)])
+@pytest.mark.parametrize("window", [0, 700])
+def test_resident_solver_matches_oracle(kind, D, m, window):
+    # one cooperative launch keeps every chunk on chip (diagonal modes, few
+    # chunks); windows with a short last one, step damping, every diagonal mode
+    rng = np.random.default_rng(1700 + D + m + window)
+    params = workloads.random_cell_params(kind, D, m, rng, 1.0)
+    B, T = 3, 1500
+    wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-5, damping=0.7 if window else 1.0,
+              window=window, max_iter=window or T, params=params,
+              x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32))
+    for mode in (Q, J):
+        _parity(wl, mode)
+        _parity(wl, mode, flags=pn.FLAG_MULTI_LAUNCH)
+
+
+def test_resident_solver_outcomes():
+    wl = _case(5, B=2, T=2048)
+    g = run_gpu(wl, Q, tol=1e6)
+    assert g.status == pn.OK and g.iters == 0 and g.window_iters[:2] == [0, 0]
+    np.testing.assert_array_equal(g.out_np, np.broadcast_to(wl["s0"][:, None, :], g.out_np.shape))
+    for mi in (0, 1, 3):
+        g = run_gpu(wl, Q, max_iter=mi, tol=0.0)
+        ref = run_oracle(wl, Q, max_iter=mi, tol=0.0)
+        assert g.status == ref.status == oracle.NOT_CONVERGED and g.window_iters[:2] == [mi, mi]
+        assert np.max(np.abs(g.out_np - ref.s)) <= 1e-4
+    bad = dict(wl)
+    bad["x"] = wl["x"].copy()
+    bad["x"][0, 1500, 5] = np.nan
+    g = run_gpu(bad, Q)
+    ref = run_oracle(bad, Q)
+    assert g.status == ref.status == oracle.NONFINITE
+    assert g.window_iters[:len(ref.window_iters)] == ref.window_iters
+
+
 # ---------------------------------------------------------------- the scan alone
 
 @pytest.mark.parametrize("dense", [False, True])
@@ -717,7 +756,7 @@ def test_fused_check_and_carry_launch_paths(chunk, T, window):
     wl = _case(2, B=3, T=T)
     wl.update(window=window, max_iter=window or T)
     for mode in (Q, J):
-        _parity(wl, mode, chunk=chunk)
+        _parity(wl, mode, chunk=chunk, flags=pn.FLAG_MULTI_LAUNCH)
 
 
 @pytest.mark.parametrize("kind, D, m", [(pn.CELL_TANH_RNN, 32, 5), (pn.CELL_GRU, 32, 40),
@@ -737,6 +776,7 @@ def test_fused_check_chunk_count_limits(kind, D, m, T, chunk):
               max_iter=T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
               s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32))
     for mode in ((Q, J) if T <= 16 else (Q,)):
+        _parity(wl, mode, chunk=chunk, flags=pn.FLAG_MULTI_LAUNCH)
         _parity(wl, mode, chunk=chunk)
 
 
@@ -750,7 +790,7 @@ def test_fused_check_workgroup_limit(B):
     wl = dict(cfg=0, cell=pn.CELL_GRU, D=D, m=m, B=B, T=T, tol=1e-5, damping=1.0, window=0,
               max_iter=T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
               s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32))
-    _parity(wl, Q, chunk=8)
+    _parity(wl, Q, chunk=8, flags=pn.FLAG_MULTI_LAUNCH)
 
 
 def test_fused_check_stop_rules():
