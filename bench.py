@@ -310,6 +310,44 @@ def summarize_pmc(args, fetch_dir, write_dir):
     print(json.dumps(out))
 
 
+def scan_bench(reps=20):
+    """The exported scan step alone (pn_affine_scan) on the headline's shape
+    (diagonal A, B=8, T=65536, D=256) and a dense one (B=4, T=4096, D=64):
+    time per call (host-timed, blocking) and the algorithmic rate: A and b read
+    once, out written once."""
+    import numpy as np
+    import torch
+    import newton_evaluation_nonlinear_amd as pn
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(5)
+    res = {}
+    for name, (B, T, D, dense) in (("diag_b8_t65536_d256", (8, 65536, 256, False)),
+                                   ("dense_b4_t4096_d64", (4, 4096, 64, True))):
+        shape = (B, T, D, D) if dense else (B, T, D)
+        A = torch.rand(shape, device=dev, generator=gen) * (0.45 / (D ** 0.5 if dense else 1.0)) + \
+            (0.0 if dense else 0.5)
+        b = torch.randn((B, T, D), device=dev, generator=gen)
+        s0 = torch.randn((B, D), device=dev, generator=gen)
+        out = torch.empty_like(b)
+        for _ in range(3):
+            pn.affine_scan(A, b, s0, dense=dense, out=out)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            pn.affine_scan(A, b, s0, dense=dense, out=out)
+            ts.append(time.perf_counter() - t0)
+        ts.sort()
+        med = ts[len(ts) // 2]
+        nbytes = 4.0 * (A.numel() + b.numel() + out.numel())
+        res[name] = {"ms_median": med * 1e3, "alg_gbs": nbytes / med / 1e9,
+                     "frac_of_8tbs": nbytes / med / 8e12, "alg_bytes": nbytes,
+                     "dense": dense, "B": B, "T": T, "D": D}
+        del A, b, s0, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -334,7 +372,12 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --copy-probe` into profiles/<workload>_traffic.json")
+    ap.add_argument("--scan", action="store_true",
+                    help="time the exported scan step alone (pn_affine_scan) and print one JSON line")
     args = ap.parse_args()
+    if args.scan:
+        print(json.dumps({"scan": scan_bench()}), flush=True)
+        return
     if args.pmc_summary:
         summarize_pmc(args, *args.pmc_summary)
         return

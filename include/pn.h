@@ -272,8 +272,12 @@ int pn_eval_f16(const pn_cell* cell, const float* params, const uint16_t* x, con
 /* The scan step alone [PN §2.1]: out_t = A_t out_{t-1} + b_t, out_0 = s0,
  * for t = 1..T.  A is device [B, T, D] (dense = 0: diagonal A_t) or
  * [B, T, D, D] (dense = 1, row-major, 1 <= D <= 64); b device [B, T, D];
- * s0 device [B, D]; out device [B, T, D].  Uses opts->stream, workspace,
- * chunk; returns PN_OK or an error code. */
+ * s0 device [B, D]; out device [B, T, D], sharing no byte with the inputs.
+ * Diagonal A runs in one pass with a decoupled look-back over 32-step
+ * chunks (A and b read once, out written once); dense A composes chunk
+ * maps, scans their carries and replays (opts->chunk steps per chunk, 0 =
+ * 32).  Uses opts->stream and opts->workspace (NULL: allocated per call);
+ * returns PN_OK or an error code. */
 int pn_affine_scan(const float* A, const float* b, const float* s0, int64_t B, int64_t T,
                    int64_t D, int32_t dense, float* out, const pn_opts* opts);
 

@@ -1400,11 +1400,19 @@ size_t pn_affine_scan_workspace_bytes(int64_t B, int64_t T, int64_t D, int32_t d
     if (B < 0 || T < 0 || D < 0) { fail(PN_EINVAL, "negative size"); return 0; }
     if (dense && D > 64) { fail(PN_EUNSUPPORTED, "dense scan supports D <= 64"); return 0; }
     if (B == 0 || T == 0 || D == 0) return kAlign;
-    const int chunk = opts && opts->chunk > 0 ? opts->chunk : (dense ? 32 : 128);
+    if (!dense) {
+        // one-pass look-back: chunk maps, end states, flags, ticket and error word
+        const int64_t L = std::min<int64_t>(kLbChunk, T);
+        const int64_t NC = (T + L - 1) / L;
+        const int64_t nblk = (D + kLbChannels - 1) / kLbChannels;
+        const size_t bnd = static_cast<size_t>(B) * NC * D;
+        return 3 * align_up(sizeof(float) * bnd) + align_up(sizeof(uint32_t) * B * NC * nblk) + kAlign;
+    }
+    const int chunk = opts && opts->chunk > 0 ? opts->chunk : 32;
     const int64_t L = std::min<int64_t>(chunk, T);
     const int64_t NC = (T + L - 1) / L;
     const size_t bnd = static_cast<size_t>(B) * NC * D;
-    return align_up(sizeof(float) * bnd * (dense ? D : 1)) + 2 * align_up(sizeof(float) * bnd);
+    return align_up(sizeof(float) * bnd * D) + 2 * align_up(sizeof(float) * bnd);
 }
 
 int pn_affine_scan(const float* A, const float* b, const float* s0, int64_t B, int64_t T, int64_t D,
@@ -1419,10 +1427,14 @@ int pn_affine_scan(const float* A, const float* b, const float* s0, int64_t B, i
     if (!A || !b || !s0 || !out) return fail(PN_EINVAL, "a device pointer is NULL");
     if (dense && D > 64) return fail(PN_EUNSUPPORTED, "dense scan supports D <= 64");
     if (B > 65535 || T >= (int64_t(1) << 31)) return fail(PN_EUNSUPPORTED, "size too large");
+    const int64_t nout = B * T * D * 4;
+    if (overlaps(out, nout, A, nout * (dense ? D : 1)) || overlaps(out, nout, b, nout) ||
+        overlaps(out, nout, s0, B * D * 4))
+        return fail(PN_EINVAL, "out overlaps an input");
     const size_t need = pn_affine_scan_workspace_bytes(B, T, D, dense, opts);
     hipStream_t st = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
     char* ws = nullptr;
-    bool own = false;
+    OwnedWorkspace own;
     if (opts && opts->workspace) {
         if (opts->workspace_bytes < need)
             return fail(PN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
@@ -1431,10 +1443,36 @@ int pn_affine_scan(const float* A, const float* b, const float* s0, int64_t B, i
     } else {
         void* q = nullptr;
         PN_HIP(hipMallocAsync(&q, need, st));
+        own.p = q;
+        own.st = st;
         ws = static_cast<char*>(q);
-        own = true;
     }
-    const int chunk = opts && opts->chunk > 0 ? opts->chunk : (dense ? 32 : 128);
+    if (!dense) {
+        LookbackArgs a{};
+        a.A = A; a.b = b; a.s0 = s0; a.out = out;
+        a.B = static_cast<int>(B); a.T = static_cast<int>(T); a.D = static_cast<int>(D);
+        a.L = static_cast<int>(std::min<int64_t>(kLbChunk, T));
+        a.NC = static_cast<int>((T + a.L - 1) / a.L);
+        a.nblk = static_cast<int>((D + kLbChannels - 1) / kLbChannels);
+        const size_t bnd = static_cast<size_t>(B) * a.NC * D;
+        size_t off = 0;
+        a.aggA = reinterpret_cast<float*>(ws + off); off += align_up(sizeof(float) * bnd);
+        a.aggB = reinterpret_cast<float*>(ws + off); off += align_up(sizeof(float) * bnd);
+        a.yv = reinterpret_cast<float*>(ws + off); off += align_up(sizeof(float) * bnd);
+        const size_t nflag = align_up(sizeof(uint32_t) * B * a.NC * a.nblk);
+        a.flag = reinterpret_cast<uint32_t*>(ws + off);
+        a.ticket = reinterpret_cast<uint32_t*>(ws + off + nflag);
+        a.err = a.ticket + 1;
+        PN_HIP(hipMemsetAsync(a.flag, 0, nflag + kAlign, st));
+        PN_HIP(launch_scan_lookback(a, st));
+        uint32_t err = 0;
+        PN_HIP(hipMemcpyAsync(&err, a.err, sizeof(err), hipMemcpyDeviceToHost, st));
+        PN_HIP(hipStreamSynchronize(st));
+        if (own.p) PN_HIP(own.release());
+        if (err != 0) return fail(PN_EHIP, "a look-back wait of the scan timed out");
+        return PN_OK;
+    }
+    const int chunk = opts && opts->chunk > 0 ? opts->chunk : 32;
     const int L = static_cast<int>(std::min<int64_t>(chunk, T));
     const int NC = static_cast<int>((T + L - 1) / L);
     const size_t bnd = static_cast<size_t>(B) * NC * D;
@@ -1442,18 +1480,18 @@ int pn_affine_scan(const float* A, const float* b, const float* s0, int64_t B, i
     a.A = A; a.b = b; a.out = out;
     a.B = static_cast<int>(B); a.T = static_cast<int>(T); a.D = static_cast<int>(D); a.L = L; a.NC = NC;
     a.aggA = reinterpret_cast<float*>(ws);
-    a.aggB = reinterpret_cast<float*>(ws + align_up(sizeof(float) * bnd * (dense ? D : 1)));
+    a.aggB = reinterpret_cast<float*>(ws + align_up(sizeof(float) * bnd * D));
     float* carry = reinterpret_cast<float*>(reinterpret_cast<char*>(a.aggB) + align_up(sizeof(float) * bnd));
     a.carry = carry;
-    const int DP = dense ? std::max(4, next_pow2(static_cast<int>(D))) : 0;
-    PN_HIP(launch_scan_aggregate(dense != 0, DP, a, st));
+    const int DP = std::max(4, next_pow2(static_cast<int>(D)));
+    PN_HIP(launch_scan_aggregate(true, DP, a, st));
     CarryArgs cy{};
     cy.aggA = a.aggA; cy.aggB = a.aggB; cy.carry = carry; cy.s0 = s0; cy.s0s = D;
     cy.B = a.B; cy.D = a.D; cy.NC = NC; cy.do_check = 0;
-    PN_HIP(dense ? launch_dense_carry(cy, st) : launch_diag_carry(cy, st));
-    PN_HIP(launch_scan_apply(dense != 0, DP, a, st));
-    if (own) PN_HIP(hipFreeAsync(ws, st));
+    PN_HIP(launch_dense_carry(cy, st));
+    PN_HIP(launch_scan_apply(true, DP, a, st));
     PN_HIP(hipStreamSynchronize(st));
+    if (own.p) PN_HIP(own.release());
     return PN_OK;
 }
 

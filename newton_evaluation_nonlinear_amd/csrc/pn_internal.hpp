@@ -282,4 +282,22 @@ struct ScanArgs {
 hipError_t launch_scan_aggregate(bool dense, int DP, const ScanArgs& a, hipStream_t st);
 hipError_t launch_scan_apply(bool dense, int DP, const ScanArgs& a, hipStream_t st);
 
+// Diagonal scan in one pass with a decoupled look-back (pn_scan.hip).
+constexpr int kLbChunk = 32;       // steps per chunk (held in registers)
+constexpr int kLbChannels = 256;   // channels per workgroup (one per thread)
+struct LookbackArgs {
+    const float* A;          // [B][T][D]
+    const float* b;          // [B][T][D]
+    const float* s0;         // [B][D]
+    float* out;              // [B][T][D]
+    int32_t B, T, D, L, NC, nblk;
+    float* aggA;             // [B][NC][D] chunk maps
+    float* aggB;
+    float* yv;               // [B][NC][D] state at the end of each chunk
+    uint32_t* flag;          // [B][NC][nblk]: 0 nothing, 1 map published, 2 end state published
+    uint32_t* ticket;        // workgroup order (zero at launch)
+    uint32_t* err;           // set when a look-back wait times out
+};
+hipError_t launch_scan_lookback(const LookbackArgs& a, hipStream_t st);
+
 }  // namespace pn

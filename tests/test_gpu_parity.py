@@ -704,26 +704,58 @@ def test_resident_solver_outcomes():
 
 # ---------------------------------------------------------------- the scan alone
 
-@pytest.mark.parametrize("dense", [False, True])
-@pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 1000])
-def test_affine_scan(dense, T):
-    rng = np.random.default_rng(T + 10 * dense)
-    B, D = 3, (5 if dense else 70)
-    A = rng.uniform(-1, 1, (B, T, D, D) if dense else (B, T, D)).astype(np.float32)
+def _scan_case(B, T, D, dense, seed, unit=False):
+    rng = np.random.default_rng(seed)
     if dense:
-        A /= np.sqrt(D)
-    A[:, ::7] = 0.0
-    if not dense:
+        A = rng.uniform(-1, 1, (B, T, D, D)).astype(np.float32) / np.float32(np.sqrt(D))
+        A[:, ::7] = 0.0
+    else:
+        A = rng.uniform(-1, 1, (B, T, D)).astype(np.float32)
+        A[:, ::7] = 0.0
         A[:, 3::11] = 1.0
+        if unit:
+            # |a| = 1 exactly: prefix sums and alternating sums, no decay
+            A = np.where(rng.uniform(size=(B, T, D)) < 0.5, 1.0, -1.0).astype(np.float32)
     b = rng.standard_normal((B, T, D)).astype(np.float32)
     s0 = rng.standard_normal((B, D)).astype(np.float32)
+    return A, b, s0
+
+
+def _check_scan(A, b, s0, dense, bar):
     dev = torch.device("cuda:0")
     out = pn.affine_scan(torch.from_numpy(A).to(dev), torch.from_numpy(b).to(dev),
                          torch.from_numpy(s0).to(dev), dense=dense).cpu().numpy()
-    ref = oracle.affine_recurrence(b.astype(np.float64), np.zeros((B, T, D)), A.astype(np.float64),
+    ref = oracle.affine_recurrence(b.astype(np.float64), np.zeros(b.shape), A.astype(np.float64),
                                    s0.astype(np.float64))
-    scale = max(1.0, np.abs(ref).max())
-    assert np.max(np.abs(out - ref)) <= 2e-5 * scale * max(1.0, np.sqrt(T) / 4)
+    scale = max(1.0, float(np.abs(ref).max()))
+    err = float(np.max(np.abs(out - ref)))
+    assert err <= bar * scale, (err, scale)
+
+
+@pytest.mark.parametrize("dense", [False, True])
+@pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 1000])
+def test_affine_scan(dense, T):
+    # one chunk, a ragged tail, several chunks; zero and unit coefficients
+    B, D = 3, (5 if dense else 70)
+    A, b, s0 = _scan_case(B, T, D, dense, T + 10 * dense)
+    _check_scan(A, b, s0, dense, 2e-5 * max(1.0, np.sqrt(T) / 4))
+
+
+def test_affine_scan_long_horizon_and_unit_coefficients():
+    # T = 65536 (2048 chunks in one look-back chain per channel block), D
+    # across two channel blocks; then |a| = 1 exactly, where nothing decays
+    # and the sums grow like sqrt(T)
+    A, b, s0 = _scan_case(2, 65536, 300, False, 31)
+    _check_scan(A, b, s0, False, 1e-4)
+    A, b, s0 = _scan_case(2, 65536, 64, False, 32, unit=True)
+    # float32 sums of 65536 unit-variance terms: relative error ~ sqrt(T) ulps
+    _check_scan(A, b, s0, False, 2e-5 * np.sqrt(65536) / 4)
+
+
+@pytest.mark.parametrize("D", [33, 64])
+def test_affine_scan_dense_wide(D):
+    A, b, s0 = _scan_case(2, 600, D, True, 40 + D)
+    _check_scan(A, b, s0, True, 1e-4)
 
 
 # ---------------------------------------------------------------- outcomes and edge cases
