@@ -1099,15 +1099,16 @@ int solve_resident(SolveCtx& c, const float* x, const float* s0, float* out, int
     a.s0n = reinterpret_cast<float*>(ws + p.off_carry);
     Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + p.off_ctrl);
     a.rslot = &ctrl->rmax[0][0][0];
-    a.bar = &ctrl->bar;
+    a.bar = reinterpret_cast<unsigned*>(ws + p.off_rpart);   // one arrival word per workgroup
     a.err = &ctrl->bar_err;
     a.hist_len = reinterpret_cast<int32_t*>(inf.dev);
     a.win_iters = reinterpret_cast<int32_t*>(inf.dev + (p.off_winfo - p.off_sync));
     a.win_status = a.win_iters + p.nwin;
     a.hist = reinterpret_cast<float*>(inf.dev + (p.off_hist - p.off_sync));
     a.hist_cap = p.hist_cap;
-    // residual slots, barrier counter and error flag start at zero
+    // residual slots, arrival words and error flag start at zero
     PN_HIP(hipMemsetAsync(ctrl, 0, sizeof(Ctrl), c.st));
+    PN_HIP(hipMemsetAsync(a.bar, 0, sizeof(unsigned) * p.B * p.NC, c.st));
     const bool timed = c.tm->take();
     size_t e0 = 0, e1 = 0;
     if (timed) { rc = request_timing(c, &e0, &e1); if (rc) return rc; }

@@ -406,12 +406,12 @@ __device__ __forceinline__ float jac_row_apply(const float* __restrict__ w, cons
 // rows_gemm16.  Chunks are at most kMaxChunk steps.
 constexpr int kMaxChunk = 64;
 
-template <int CELL, int DP>
+template <int CELL, int DP, int MAXC = kMaxChunk>
 struct CellRegs {
     static constexpr int NG = CellTraits<CELL>::NG;
     static constexpr int WC = DP / 16;
     static constexpr int WR = (kThreads / 64) / WC;
-    static constexpr int MAXRT = (kMaxChunk / 16 + WR - 1) / WR;   // row tiles per wavefront
+    static constexpr int MAXRT = (MAXC / 16 + WR - 1) / WR;        // row tiles per wavefront
     static constexpr int KB = DP / 4;                              // B values per gate and lane
     static constexpr int PS = iterate_stride<DP>();
     static constexpr int KIN = DP;                                 // input widths held in registers
@@ -1638,26 +1638,33 @@ __device__ __forceinline__ void st_dev(float* p, float v) {
 }
 
 // Grid barrier: the workgroup's memory operations complete (s_waitcnt 0),
-// then one arrival per workgroup on a counter that only grows; wait for
-// epoch x gridsize arrivals.
+// then the workgroup stores the barrier's epoch into its own arrival word (a
+// store, not a read-modify-write: no two workgroups touch one word), and its
+// first wavefront polls every arrival word, 64 per load instruction, until
+// all hold at least this epoch.  The wait is bounded.
 __device__ __forceinline__ bool resident_sync(const ResidentArgs& a, unsigned& epoch, unsigned nblocks) {
     __shared__ int ok;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     ++epoch;
-    if (threadIdx.x == 0) {
-        ok = 1;
-        __hip_atomic_fetch_add(a.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned target = epoch * nblocks;
+    if (threadIdx.x < 64) {
+        const unsigned blk = blockIdx.y * gridDim.x + blockIdx.x;
+        if (threadIdx.x == 0) __hip_atomic_store(a.bar + blk, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         unsigned spins = 0;
-        while (__hip_atomic_load(a.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        int good = 1;
+        for (;;) {
+            int done = 1;
+            for (unsigned k = threadIdx.x; k < nblocks; k += 64)
+                done &= __hip_atomic_load(a.bar + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= epoch;
+            if (__all(done)) break;
             __builtin_amdgcn_s_sleep(1);
-            if (++spins > (1u << 24) || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-                __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                ok = 0;
+            if (++spins > (1u << 22) || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                if (threadIdx.x == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                good = 0;
                 break;
             }
         }
+        if (threadIdx.x == 0) ok = good;
     }
     __syncthreads();
     return ok != 0;
@@ -1776,8 +1783,9 @@ __global__ __launch_bounds__(kThreads) void cell_resident(ResidentArgs a) {
                     const int k1 = d < D ? min(c, k0 + per) : k0;
                     const float* mA = a.mapA + par * HS + static_cast<size_t>(b) * a.NC * D;
                     const float* mB = a.mapB + par * HS + static_cast<size_t>(b) * a.NC * D;
-                    // up to kRF maps per segment are loaded together, then folded
-                    constexpr int kRF = 16;
+                    // up to kRF maps per segment (at most kFcMaxChunks chunks over NS
+                    // segments) are loaded together, then folded
+                    constexpr int kRF = (kFcMaxChunks + NS - 1) / NS < 16 ? (kFcMaxChunks + NS - 1) / NS : 16;
                     float pa[kRF], pb[kRF];
 #pragma unroll
                     for (int u = 0; u < kRF; ++u) {
@@ -1834,7 +1842,24 @@ __global__ __launch_bounds__(kThreads) void cell_resident(ResidentArgs a) {
                     float shat = c_first;
                     N[tid] = und ? shat : P[tid] + lam * (shat - P[tid]);
                     const int nrep = has_next ? Lc - 1 : Lc;
-                    for (int j = 0; j < nrep; ++j) {
+                    // eight steps at a time: their LDS loads go out together
+                    int j = 0;
+                    for (; j + 8 <= nrep; j += 8) {
+                        float v[8], co[8], pj[9];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            v[u] = V[(j + u) * DP + tid];
+                            co[u] = CO[(j + u) * DP + tid];
+                            pj[u] = P[(j + u) * PS + tid];
+                        }
+                        pj[8] = P[(j + 8) * PS + tid];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            shat = v[u] + co[u] * (shat - pj[u]);
+                            N[(j + u + 1) * PS + tid] = und ? shat : pj[u + 1] + lam * (shat - pj[u + 1]);
+                        }
+                    }
+                    for (; j < nrep; ++j) {
                         const int o = j * DP + tid;
                         shat = V[o] + CO[o] * (shat - P[j * PS + tid]);
                         const float so = P[(j + 1) * PS + tid];
@@ -1857,6 +1882,7 @@ __global__ __launch_bounds__(kThreads) void cell_resident(ResidentArgs a) {
                         A = 0.0f;
                         Bc = V[(Lc - 1) * DP + tid];
                     } else {
+#pragma unroll 8
                         for (int j = 0; j < Lc; ++j) {
                             const float at = CO[j * DP + tid];
                             Bc = at * Bc + (V[j * DP + tid] - at * N[j * PS + tid]);

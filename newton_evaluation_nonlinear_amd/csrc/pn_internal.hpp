@@ -23,9 +23,9 @@ struct Ctrl {
     // the sweep that reads set k % 3 (plain loads: the set is not written
     // while it is read) clears set (k + 2) % 3 for the sweep after it, with
     // device-scope atomic stores.  Each word has a 256-byte line of its own.
-    // The resident solver's grid barrier: arrivals and the timeout flag.
-    uint32_t bar, bar_err;
-    uint32_t pad_[58];
+    // The resident solver's grid-barrier timeout flag.
+    uint32_t bar_err;
+    uint32_t pad_[59];
     uint32_t rmax[3][16][64];
 };
 constexpr int kRSlots = 16;
@@ -257,7 +257,7 @@ struct ResidentArgs {
     float* halo;             // [2][B][NC][D] last row of every chunk, by parity
     float* s0n;              // [B][D] initial state of the next window
     uint32_t* rslot;         // [3][kRSlots][64] residual maxima, one 256-byte line per slot
-    unsigned* bar;           // grid barrier arrivals (zero at launch)
+    unsigned* bar;           // [B * NC] grid barrier arrival words (zero at launch)
     unsigned* err;           // set on a barrier timeout
     int32_t* win_iters;      // [nwin] (-1: not reached)
     int32_t* win_status;
