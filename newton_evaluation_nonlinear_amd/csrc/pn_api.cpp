@@ -1081,8 +1081,15 @@ int solve_resident(SolveCtx& c, const float* x, const float* s0, float* out, int
     PN_HIP(hipGetDevice(&dev));
     PN_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
     if (!coop) return PN_EUNSUPPORTED;
-    PN_HIP(cell_resident_max_blocks(p.kind, p.DP, p.L, p.m, &nb));
-    if (static_cast<int64_t>(p.B) * p.NC > nb) return PN_EUNSUPPORTED;
+    // one chunk per workgroup, else (D padded to 16) four strided chunks per workgroup
+    int cpw = 1;
+    PN_HIP(cell_resident_max_blocks(p.kind, p.DP, p.L, p.m, 1, &nb));
+    if (static_cast<int64_t>(p.B) * p.NC > nb) {
+        cpw = 4;
+        nb = 0;
+        if (p.DP == 16) PN_HIP(cell_resident_max_blocks(p.kind, p.DP, p.L, p.m, cpw, &nb));
+        if (static_cast<int64_t>(p.B) * ((p.NC + cpw - 1) / cpw) > nb) return PN_EUNSUPPORTED;
+    }
     OneLaunchInfo inf;
     int rc = one_launch_info(c, &inf);
     if (rc != PN_OK) return rc;
@@ -1108,12 +1115,12 @@ int solve_resident(SolveCtx& c, const float* x, const float* s0, float* out, int
     a.hist_cap = p.hist_cap;
     // residual slots, arrival words and error flag start at zero
     PN_HIP(hipMemsetAsync(ctrl, 0, sizeof(Ctrl), c.st));
-    PN_HIP(hipMemsetAsync(a.bar, 0, sizeof(unsigned) * p.B * p.NC, c.st));
+    PN_HIP(hipMemsetAsync(a.bar, 0, sizeof(unsigned) * p.B * ((p.NC + cpw - 1) / cpw), c.st));
     const bool timed = c.tm->take();
     size_t e0 = 0, e1 = 0;
     if (timed) { rc = request_timing(c, &e0, &e1); if (rc) return rc; }
     {
-        const hipError_t le = launch_cell_resident(p.kind, p.DP, a, c.st);
+        const hipError_t le = launch_cell_resident(p.kind, p.DP, cpw, a, c.st);
         if (le == hipErrorCooperativeLaunchTooLarge) {
             (void)hipGetLastError();
             g_launch_timing = LaunchTiming{};

@@ -1598,8 +1598,9 @@ __global__ __launch_bounds__(DP * DP / 4) void dense_carry_wide(CarryArgs g) {
 
 hipError_t launch_dense_carry(const CarryArgs& a, hipStream_t st) {
     const int DP = a.D <= 4 ? 4 : a.D <= 8 ? 8 : a.D <= 16 ? 16 : a.D <= 32 ? 32 : 64;
-    if (a.D % 4 == 0 && DP >= 32) {
-        if (DP == 32) dense_carry_wide<32><<<a.B, 32 * 8, 0, st>>>(a);
+    if (a.D % 4 == 0 && DP >= 16) {
+        if (DP == 16) dense_carry_wide<16><<<a.B, 16 * 4, 0, st>>>(a);
+        else if (DP == 32) dense_carry_wide<32><<<a.B, 32 * 8, 0, st>>>(a);
         else dense_carry_wide<64><<<a.B, 64 * 16, 0, st>>>(a);
         return hipGetLastError();
     }
@@ -1626,8 +1627,8 @@ hipError_t launch_dense_carry(const CarryArgs& a, hipStream_t st) {
 // last row of every chunk (the next chunk's halo), the residual maxima and the
 // next window's initial state.  These go through relaxed device-scope atomic
 // loads and stores, which are coherent across the XCDs' L2 caches without
-// cache-wide fences; a grid barrier (a relaxed atomic counter, entered after
-// every memory operation of the workgroup has completed) separates the
+// cache-wide fences; a grid barrier (one arrival word per workgroup, stored
+// after every memory operation of the workgroup has completed) separates the
 // iterations.  Every wait is bounded: on a timeout the error flag is set and
 // every workgroup leaves, so a broken barrier cannot hang the device.
 __device__ __forceinline__ float ld_dev(const float* p) {
@@ -1670,76 +1671,101 @@ __device__ __forceinline__ bool resident_sync(const ResidentArgs& a, unsigned& e
     return ok != 0;
 }
 
-template <int CELL, int DP>
-__global__ __launch_bounds__(kThreads) void cell_resident(ResidentArgs a) {
+// CPW chunks per workgroup: chunk bx + k * gridDim.x of the batch row, k <
+// CPW, so that more chunks than co-resident workgroups still fit (workload 2:
+// 2048 chunks over 512 workgroups).  Each chunk keeps its own LDS region; the
+// fold, the replay and the map composition of the CPW chunks run side by
+// side on disjoint thread groups, the evaluations one chunk after another.
+// The replay works in place on the chunk's rows: the old row is read before
+// the new one is written over it.
+template <int CELL, int DP, int CPW>
+__global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(ResidentArgs a) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     constexpr int PS = iterate_stride<DP>();
-    constexpr int NS = kThreads / DP;            // fold segments per channel
+    constexpr int TG = kThreads / CPW;           // threads per chunk in the fold
+    constexpr int NS = TG / DP;                  // fold segments per channel
+    static_assert(NS >= 1, "CPW x DP must not exceed the workgroup");
     const int L = a.L, m = a.m, D = a.D, B = a.B;
     const int xs = x_stride(m);
-    const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int bx = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int GX = gridDim.x;
     const unsigned nblocks = gridDim.x * gridDim.y;
-    float* Pb = lds;                             // [L+1][PS] rows t0-1 .. t1-1 of the iterate
-    float* Nb = Pb + (L + 1) * PS;               // [L+1][PS] the same rows of the next iterate
-    float* V = Nb + (L + 1) * PS;                // [L][DP] f at the iterate
-    float* CO = V + L * DP;                      // [L][DP] diagonal coefficients
-    float* X = CO + L * DP;                      // [L][xs]
-    float* SCR = X + L * xs;                     // [2][kThreads] fold segments
+    const int per_chunk = (L + 1) * PS + 2 * L * DP + L * xs;
+    float* SCR = lds + CPW * per_chunk;          // [2][kThreads] fold segments
     float* S0 = SCR + 2 * kThreads;              // [DP] initial state of the window
+    auto Sk = [&](int k) { return lds + k * per_chunk; };                 // [L+1][PS] rows t0-1 .. t1-1
+    auto Vk = [&](int k) { return lds + k * per_chunk + (L + 1) * PS; };  // [L][DP]
+    auto COk = [&](int k) { return Vk(k) + L * DP; };                       // [L][DP]
+    auto Xk = [&](int k) { return COk(k) + L * DP; };                       // [L][xs]
     CellRegs<CELL, DP> cr;
     cr.load(a.w, a.w, D, m);
     const size_t HS = static_cast<size_t>(B) * a.NC * D;   // parity stride of maps and halo
     unsigned epoch = 0;
-    int hist_pos = 0, q = 0;                     // q: checks taken so far (residual slot sets rotate)
-    float own_a = 1.0f, own_b = 0.0f;            // this chunk's map of the current iteration (tid < D)
+    int hist_pos = 0, q = 0;
+    // the thread's (chunk, channel) in the replay and the composition
+    const int rk = tid / DP, ri = tid % DP;
+    const bool rthr = rk < CPW && ri < D;
+    float own_a = 1.0f, own_b = 0.0f;            // map of chunk (rk) of the current iteration, channel ri
     for (int wi = 0; wi < a.nwin; ++wi) {
         const int64_t w0 = static_cast<int64_t>(wi) * a.W;
         const int Tw = static_cast<int>(a.T - w0 < a.W ? a.T - w0 : a.W);
         const int NCw = (Tw + L - 1) / L;
-        const bool active = c < NCw;
-        const int t0 = c * L;
-        const int Lc = active ? min(L, Tw - t0) : 0;
-        const bool has_next = c + 1 < NCw;
-        float* P = Pb;
-        float* N = Nb;
+        auto chunk = [&](int k) { return bx + k * GX; };
+        auto active = [&](int k) { return chunk(k) < NCw; };
+        auto rows = [&](int k) { return active(k) ? min(L, Tw - chunk(k) * L) : 0; };
         if (tid < DP)
             S0[tid] = tid < D ? (wi == 0 ? a.s0[static_cast<int64_t>(b) * D + tid] : ld_dev(a.s0n + b * D + tid)) : 0.0f;
         uint32_t rb = 0;
-        if (active) {
-            copy_rows_to_lds<kThreads>(X, xs, a.x + (static_cast<int64_t>(b) * a.T + w0 + t0) * m, m, Lc, m);
-            __syncthreads();
-            // s^(0) = s0 on every row
-            for (int e = tid; e < (Lc + 1) * PS; e += kThreads) {
-                const int i = e % PS;
-                P[e] = i < DP ? S0[i] : 0.0f;
-            }
-            cr.project(a.w, X, xs, Lc, m);
-            __syncthreads();
-            // the maps of iteration 0 and r_0
-            cr.template eval<false>(P, V, CO, Lc, L, a.mode, P, rb, nullptr, a.tol);
-            __syncthreads();
+#pragma unroll
+        for (int k = 0; k < CPW; ++k) {
+            if (active(k))
+                copy_rows_to_lds<kThreads>(Xk(k), xs, a.x + (static_cast<int64_t>(b) * a.T + w0 + chunk(k) * L) * m,
+                                           m, rows(k), m);
         }
-        if (tid < D && active) {
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < CPW; ++k) {
+            if (!active(k)) continue;
+            float* S = Sk(k);
+            for (int e = tid; e < (rows(k) + 1) * PS; e += kThreads) {
+                const int i = e % PS;
+                S[e] = i < DP ? S0[i] : 0.0f;
+            }
+        }
+        __syncthreads();
+        // the maps of iteration 0 at s^(0) = s0, and r_0 (one chunk after another)
+#pragma unroll 1
+        for (int k = 0; k < CPW; ++k) {
+            if (!active(k)) continue;
+            cr.project(a.w, Xk(k), xs, rows(k), m);
+            cr.template eval<false>(Sk(k), Vk(k), COk(k), rows(k), L, a.mode, Sk(k), rb, nullptr, a.tol);
+        }
+        __syncthreads();
+        if (rthr && active(rk)) {
+            const int Lc = rows(rk);
+            const float* V = Vk(rk);
+            const float* CO = COk(rk);
+            const float* S = Sk(rk);
             float A = 1.0f, Bc = 0.0f;
             if (a.mode == kJacobi) {
                 A = 0.0f;
-                Bc = V[(Lc - 1) * DP + tid];
+                Bc = V[(Lc - 1) * DP + ri];
             } else {
                 for (int j = 0; j < Lc; ++j) {
-                    const float at = CO[j * DP + tid];
-                    Bc = at * Bc + (V[j * DP + tid] - at * P[j * PS + tid]);
+                    const float at = CO[j * DP + ri];
+                    Bc = at * Bc + (V[j * DP + ri] - at * S[j * PS + ri]);
                     A = at * A;
                 }
             }
             own_a = A;
             own_b = Bc;
-            const size_t ci = static_cast<size_t>(b) * a.NC + c;
-            st_dev(a.mapA + ci * D + tid, A);
-            st_dev(a.mapB + ci * D + tid, Bc);
+            const size_t ci = static_cast<size_t>(b) * a.NC + chunk(rk);
+            st_dev(a.mapA + ci * D + ri, A);
+            st_dev(a.mapB + ci * D + ri, Bc);
         }
         rb = block_max_u32(rb);
-        if (tid == 0 && active)
-            __hip_atomic_fetch_max(a.rslot + ((q % 3) * kRSlots + (b * a.NC + c) % kRSlots) * 64, rb,
+        if (tid == 0 && active(0))
+            __hip_atomic_fetch_max(a.rslot + ((q % 3) * kRSlots + (b * GX + bx) % kRSlots) * 64, rb,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (!resident_sync(a, epoch, nblocks)) return;
         int K = 0, status = kStOk;
@@ -1753,7 +1779,7 @@ __global__ __launch_bounds__(kThreads) void cell_resident(ResidentArgs a) {
             if (r_i >= kNonFiniteBits) st = kStNonFinite;
             else if (__uint_as_float(r_i) <= a.tol) st = kStOk;
             else if (i >= a.max_iter) st = kStNotConverged;
-            if (c == 0 && b == 0) {
+            if (bx == 0 && b == 0) {
                 if (tid == 0 && hist_pos < a.hist_cap) a.hist[hist_pos] = __uint_as_float(r_i);
                 if (tid < kRSlots)
                     __hip_atomic_store(a.rslot + (((q + 2) % 3) * kRSlots + tid) * 64, 0u, __ATOMIC_RELAXED,
@@ -1766,154 +1792,159 @@ __global__ __launch_bounds__(kThreads) void cell_resident(ResidentArgs a) {
                 ++q;
                 break;
             }
-            uint32_t rbn = 0;
-            if (active) {
-                const int par = i & 1;
-                const size_t ci = static_cast<size_t>(b) * a.NC + c;
-                // row t0-1 of s^(i): the window's s0 before the first chunk
-                // or at i = 0, else the previous chunk's last row
-                if (tid < PS)
-                    P[tid] = tid < D ? ((c == 0 || i == 0) ? S0[tid] : ld_dev(a.halo + par * HS + (ci - 1) * D + tid)) : 0.0f;
-                // the carry: NS segments of the maps of the chunks before c,
-                // each folded into one map, then applied to s0 in order
-                {
-                    const int d = tid % DP, sg_ = tid / DP;
-                    const int per = (c + NS - 1) / NS;
-                    const int k0 = min(c, sg_ * per);
-                    const int k1 = d < D ? min(c, k0 + per) : k0;
-                    const float* mA = a.mapA + par * HS + static_cast<size_t>(b) * a.NC * D;
-                    const float* mB = a.mapB + par * HS + static_cast<size_t>(b) * a.NC * D;
-                    // up to kRF maps per segment (at most kFcMaxChunks chunks over NS
-                    // segments) are loaded together, then folded
-                    constexpr int kRF = (kFcMaxChunks + NS - 1) / NS < 16 ? (kFcMaxChunks + NS - 1) / NS : 16;
-                    float pa[kRF], pb[kRF];
+            const int par = i & 1;
+            // the carries: per chunk, NS segments of the maps of the chunks
+            // before it, each folded into one map, applied to s0 after the barrier
+            {
+                const int fk = tid / TG, tl = tid % TG;
+                const int d = tl % DP, sg_ = tl / DP;
+                const int c = chunk(fk);
+                const int cc = active(fk) ? c : 0;
+                const int per = (cc + NS - 1) / NS;
+                const int k0 = min(cc, sg_ * per);
+                const int k1 = d < D ? min(cc, k0 + per) : k0;
+                const float* mA = a.mapA + par * HS + static_cast<size_t>(b) * a.NC * D;
+                const float* mB = a.mapB + par * HS + static_cast<size_t>(b) * a.NC * D;
+                constexpr int kRF = (kFcMaxChunks + NS - 1) / NS < 16 ? (kFcMaxChunks + NS - 1) / NS : 16;
+                float pa[kRF], pb[kRF];
 #pragma unroll
-                    for (int u = 0; u < kRF; ++u) {
-                        const int k = k0 + u;
-                        pa[u] = k < k1 ? ld_dev(mA + k * D + d) : 1.0f;
-                        pb[u] = k < k1 ? ld_dev(mB + k * D + d) : 0.0f;
-                    }
-                    float fa = 1.0f, fbv = 0.0f;
-#pragma unroll
-                    for (int u = 0; u < kRF; ++u) {
-                        fbv = pa[u] * fbv + pb[u];
-                        fa = pa[u] * fa;
-                    }
-                    for (int k = k0 + kRF; k < k1; ++k) {
-                        const float ak = ld_dev(mA + k * D + d);
-                        fbv = ak * fbv + ld_dev(mB + k * D + d);
-                        fa = ak * fa;
-                    }
-                    SCR[tid] = fa;
-                    SCR[kThreads + tid] = fbv;
+                for (int u = 0; u < kRF; ++u) {
+                    const int kk = k0 + u;
+                    pa[u] = kk < k1 ? ld_dev(mA + kk * D + d) : 1.0f;
+                    pb[u] = kk < k1 ? ld_dev(mB + kk * D + d) : 0.0f;
                 }
-                __syncthreads();
-                float c_first = 0.0f, c_next = 0.0f;
-                if (tid < D) {
-                    float xv = S0[tid];
+                float fa = 1.0f, fbv = 0.0f;
 #pragma unroll
-                    for (int s = 0; s < NS; ++s) xv = SCR[s * DP + tid] * xv + SCR[kThreads + s * DP + tid];
-                    c_first = xv;
-                    c_next = own_a * xv + own_b;
+                for (int u = 0; u < kRF; ++u) {
+                    fbv = pa[u] * fbv + pb[u];
+                    fa = pa[u] * fa;
                 }
-                // replay from the carry, damping: N = rows t0-1 .. t1-1 of s^(i+1)
-                const float lam = a.lam;
-                const bool und = a.undamped != 0;
+                for (int kk = k0 + kRF; kk < k1; ++kk) {
+                    const float ak = ld_dev(mA + kk * D + d);
+                    fbv = ak * fbv + ld_dev(mB + kk * D + d);
+                    fa = ak * fa;
+                }
+                SCR[tid] = fa;
+                SCR[kThreads + tid] = fbv;
+            }
+            // row t0-1 of s^(i): the window's s0 before the first chunk or
+            // at i = 0, else the previous chunk's last row
+            float hrow = 0.0f;
+            if (rthr && active(rk)) {
+                const int c = chunk(rk);
+                hrow = (c == 0 || i == 0) ? S0[ri]
+                                          : ld_dev(a.halo + par * HS + (static_cast<size_t>(b) * a.NC + c - 1) * D + ri);
+            }
+            __syncthreads();
+            // replay from the carry, damping, in place: rows t0-1 .. t1-1 of s^(i+1)
+            const float lam = a.lam;
+            const bool und = a.undamped != 0;
+            if (rthr && active(rk)) {
+                const int c = chunk(rk);
+                const int Lc = rows(rk);
+                const bool has_next = c + 1 < NCw;
+                float xv = S0[ri];
+#pragma unroll
+                for (int sgi = 0; sgi < NS; ++sgi)
+                    xv = SCR[rk * TG + sgi * DP + ri] * xv + SCR[kThreads + rk * TG + sgi * DP + ri];
+                const float c_first = xv;
+                const float c_next = own_a * xv + own_b;
+                float* S = Sk(rk);
+                const float* V = Vk(rk);
+                const float* CO = COk(rk);
+                float pold = hrow;                   // old value of the row being replaced
+                float shat = c_first;
+                S[ri] = und ? shat : pold + lam * (shat - pold);
+                const int nrep = has_next ? Lc - 1 : Lc;
                 if (a.mode == kJacobi) {
-                    const int jl = has_next ? Lc - 1 : Lc;
-                    for (int e = tid; e < jl * PS; e += kThreads) {
-                        const int j = 1 + e / PS, ii = e % PS;
-                        float val = 0.0f;
-                        if (ii < D) {
-                            const float sh = V[(j - 1) * DP + ii], so = P[j * PS + ii];
-                            val = und ? sh : so + lam * (sh - so);
-                        }
-                        N[j * PS + ii] = val;
+                    for (int j = 0; j < nrep; ++j) {
+                        const float so = S[(j + 1) * PS + ri];
+                        const float sh = V[j * DP + ri];
+                        S[(j + 1) * PS + ri] = und ? sh : so + lam * (sh - so);
                     }
-                    if (tid < PS) {
-                        const bool lv = tid < D;
-                        N[tid] = lv ? (und ? c_first : P[tid] + lam * (c_first - P[tid])) : 0.0f;
-                        if (has_next) {
-                            const float so = P[Lc * PS + tid];
-                            N[Lc * PS + tid] = lv ? (und ? c_next : so + lam * (c_next - so)) : 0.0f;
-                        }
-                    }
-                } else if (tid < D) {
-                    float shat = c_first;
-                    N[tid] = und ? shat : P[tid] + lam * (shat - P[tid]);
-                    const int nrep = has_next ? Lc - 1 : Lc;
-                    // eight steps at a time: their LDS loads go out together
+                } else {
                     int j = 0;
                     for (; j + 8 <= nrep; j += 8) {
-                        float v[8], co[8], pj[9];
+                        float v[8], co[8], po[8];
 #pragma unroll
                         for (int u = 0; u < 8; ++u) {
-                            v[u] = V[(j + u) * DP + tid];
-                            co[u] = CO[(j + u) * DP + tid];
-                            pj[u] = P[(j + u) * PS + tid];
+                            v[u] = V[(j + u) * DP + ri];
+                            co[u] = CO[(j + u) * DP + ri];
+                            po[u] = S[(j + u + 1) * PS + ri];
                         }
-                        pj[8] = P[(j + 8) * PS + tid];
 #pragma unroll
                         for (int u = 0; u < 8; ++u) {
-                            shat = v[u] + co[u] * (shat - pj[u]);
-                            N[(j + u + 1) * PS + tid] = und ? shat : pj[u + 1] + lam * (shat - pj[u + 1]);
+                            shat = v[u] + co[u] * (shat - pold);
+                            pold = po[u];
+                            S[(j + u + 1) * PS + ri] = und ? shat : pold + lam * (shat - pold);
                         }
                     }
                     for (; j < nrep; ++j) {
-                        const int o = j * DP + tid;
-                        shat = V[o] + CO[o] * (shat - P[j * PS + tid]);
-                        const float so = P[(j + 1) * PS + tid];
-                        N[(j + 1) * PS + tid] = und ? shat : so + lam * (shat - so);
+                        shat = V[j * DP + ri] + CO[j * DP + ri] * (shat - pold);
+                        pold = S[(j + 1) * PS + ri];
+                        S[(j + 1) * PS + ri] = und ? shat : pold + lam * (shat - pold);
                     }
-                    if (has_next) {
-                        const float so = P[Lc * PS + tid];
-                        N[Lc * PS + tid] = und ? c_next : so + lam * (c_next - so);
-                    }
-                } else if (tid < PS) {
-                    for (int j = 0; j <= Lc; ++j) N[j * PS + tid] = 0.0f;
                 }
-                __syncthreads();
-                // the maps of iteration i+1 at s^(i+1), and r_{i+1}
-                cr.template eval<false>(N, V, CO, Lc, L, a.mode, N, rbn, nullptr, a.tol);
-                __syncthreads();
-                if (tid < D) {
-                    float A = 1.0f, Bc = 0.0f;
-                    if (a.mode == kJacobi) {
-                        A = 0.0f;
-                        Bc = V[(Lc - 1) * DP + tid];
-                    } else {
+                if (has_next) {
+                    const float so = S[Lc * PS + ri];
+                    S[Lc * PS + ri] = und ? c_next : so + lam * (c_next - so);
+                }
+            }
+            __syncthreads();
+            // the maps of iteration i+1 at s^(i+1), and r_{i+1}
+            uint32_t rbn = 0;
+#pragma unroll 1
+            for (int k = 0; k < CPW; ++k) {
+                if (!active(k)) continue;
+                if (CPW > 1) cr.project(a.w, Xk(k), xs, rows(k), m);
+                cr.template eval<false>(Sk(k), Vk(k), COk(k), rows(k), L, a.mode, Sk(k), rbn, nullptr, a.tol);
+            }
+            __syncthreads();
+            if (rthr && active(rk)) {
+                const int Lc = rows(rk);
+                const float* V = Vk(rk);
+                const float* CO = COk(rk);
+                const float* S = Sk(rk);
+                float A = 1.0f, Bc = 0.0f;
+                if (a.mode == kJacobi) {
+                    A = 0.0f;
+                    Bc = V[(Lc - 1) * DP + ri];
+                } else {
 #pragma unroll 8
-                        for (int j = 0; j < Lc; ++j) {
-                            const float at = CO[j * DP + tid];
-                            Bc = at * Bc + (V[j * DP + tid] - at * N[j * PS + tid]);
-                            A = at * A;
-                        }
+                    for (int j = 0; j < Lc; ++j) {
+                        const float at = CO[j * DP + ri];
+                        Bc = at * Bc + (V[j * DP + ri] - at * S[j * PS + ri]);
+                        A = at * A;
                     }
-                    own_a = A;
-                    own_b = Bc;
-                    st_dev(a.mapA + (par ^ 1) * HS + ci * D + tid, A);
-                    st_dev(a.mapB + (par ^ 1) * HS + ci * D + tid, Bc);
-                    st_dev(a.halo + (par ^ 1) * HS + ci * D + tid, N[Lc * PS + tid]);
                 }
-                float* t = P; P = N; N = t;
+                own_a = A;
+                own_b = Bc;
+                const size_t ci = static_cast<size_t>(b) * a.NC + chunk(rk);
+                st_dev(a.mapA + (par ^ 1) * HS + ci * D + ri, A);
+                st_dev(a.mapB + (par ^ 1) * HS + ci * D + ri, Bc);
+                st_dev(a.halo + (par ^ 1) * HS + ci * D + ri, S[Lc * PS + ri]);
             }
             rbn = block_max_u32(rbn);
-            if (tid == 0 && active)
-                __hip_atomic_fetch_max(a.rslot + (((q + 1) % 3) * kRSlots + (b * a.NC + c) % kRSlots) * 64, rbn,
+            if (tid == 0 && active(0))
+                __hip_atomic_fetch_max(a.rslot + (((q + 1) % 3) * kRSlots + (b * GX + bx) % kRSlots) * 64, rbn,
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (!resident_sync(a, epoch, nblocks)) return;
         }
-        // the window's result: rows t0 .. t1-1 of the last iterate, and the
-        // next window's initial state from the last chunk
-        if (active) {
-            float* o = a.out + (static_cast<int64_t>(b) * a.T + w0 + t0) * D;
+        // the window's result: the chunks' rows of the last iterate, and the
+        // next window's initial state from the row's last chunk
+#pragma unroll
+        for (int k = 0; k < CPW; ++k) {
+            if (!active(k)) continue;
+            const int c = chunk(k), Lc = rows(k);
+            const float* S = Sk(k);
+            float* o = a.out + (static_cast<int64_t>(b) * a.T + w0 + c * L) * D;
             for (int e = tid; e < Lc * D; e += kThreads) {
-                const int j = e / D, i = e % D;
-                o[e] = P[(j + 1) * PS + i];
+                const int j = e / D, ii = e % D;
+                o[e] = S[(j + 1) * PS + ii];
             }
-            if (!has_next && tid < D) st_dev(a.s0n + b * D + tid, P[Lc * PS + tid]);
+            if (c + 1 == NCw && tid < D) st_dev(a.s0n + b * D + tid, S[Lc * PS + tid]);
         }
-        if (c == 0 && b == 0 && tid == 0) {
+        if (bx == 0 && b == 0 && tid == 0) {
             a.win_iters[wi] = K;
             a.win_status[wi] = status;
             *a.hist_len = hist_pos;
@@ -1923,12 +1954,13 @@ __global__ __launch_bounds__(kThreads) void cell_resident(ResidentArgs a) {
     }
 }
 
-size_t resident_lds_bytes(int DP, int L, int m) {
+size_t resident_lds_bytes(int DP, int L, int m, int cpw) {
     const size_t PS = DP + 4, xs = x_stride(m);
-    return sizeof(float) * (2ull * (L + 1) * PS + 2ull * L * DP + static_cast<size_t>(L) * xs + 2ull * kThreads + DP);
+    const size_t per = (L + 1) * PS + 2ull * L * DP + static_cast<size_t>(L) * xs;
+    return sizeof(float) * (cpw * per + 2ull * kThreads + DP);
 }
 
-template <int CELL, int DP>
+template <int CELL, int DP, int CPW>
 static hipError_t resident_blocks_t(size_t lds, int* nb) {
     int per_cu = 0, dev = 0, ncu = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -1936,17 +1968,17 @@ static hipError_t resident_blocks_t(size_t lds, int* nb) {
     e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     if (lds > 64 * 1024) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(cell_resident<CELL, DP>),
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(cell_resident<CELL, DP, CPW>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cell_resident<CELL, DP>, kThreads, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cell_resident<CELL, DP, CPW>, kThreads, lds);
     if (e != hipSuccess) return e;
     *nb = per_cu * ncu;
     return hipSuccess;
 }
 
-template <int CELL, int DP>
+template <int CELL, int DP, int CPW>
 static hipError_t launch_resident_t(const ResidentArgs& a, size_t lds, hipStream_t st) {
     void* args[] = {const_cast<ResidentArgs*>(&a)};
     LaunchTiming& t = launch_timing();
@@ -1954,8 +1986,9 @@ static hipError_t launch_resident_t(const ResidentArgs& a, size_t lds, hipStream
         hipError_t e = hipEventRecord(t.start, st);
         if (e != hipSuccess) return e;
     }
-    hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(cell_resident<CELL, DP>),
-                                              dim3(a.NC, a.B), dim3(kThreads), args, static_cast<unsigned>(lds), st);
+    const int gx = (a.NC + CPW - 1) / CPW;
+    hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(cell_resident<CELL, DP, CPW>),
+                                              dim3(gx, a.B), dim3(kThreads), args, static_cast<unsigned>(lds), st);
     if (e != hipSuccess) return e;
     if (t.start) {
         e = hipEventRecord(t.stop, st);
@@ -1964,26 +1997,29 @@ static hipError_t launch_resident_t(const ResidentArgs& a, size_t lds, hipStream
     return e;
 }
 
-// Blocks of cell_resident that fit on the device at once (0 when the shape
-// has no resident form: D padded to 16, 32 or 64, tanh RNN, GRU or Euler).
-hipError_t cell_resident_max_blocks(int kind, int DP, int L, int m, int* nb) {
+// Blocks of cell_resident with cpw chunks per workgroup that fit on the
+// device at once (0 when the shape has no resident form: D padded to 16, 32
+// or 64; cpw 1, or 4 at D padded to 16).
+hipError_t cell_resident_max_blocks(int kind, int DP, int L, int m, int cpw, int* nb) {
     *nb = 0;
-    const size_t lds = resident_lds_bytes(DP, L, m);
+    const size_t lds = resident_lds_bytes(DP, L, m, cpw);
     if (lds > 160 * 1024 || L > kMaxChunk) return hipSuccess;
-#define PN_RES_CASE(K, DPV) if (kind == K && DP == DPV) return resident_blocks_t<K, DPV>(lds, nb);
-    PN_RES_CASE(kCellTanhRnn, 16) PN_RES_CASE(kCellTanhRnn, 32) PN_RES_CASE(kCellTanhRnn, 64)
-    PN_RES_CASE(kCellGru, 16) PN_RES_CASE(kCellGru, 32) PN_RES_CASE(kCellGru, 64)
-    PN_RES_CASE(kCellEuler, 16) PN_RES_CASE(kCellEuler, 32) PN_RES_CASE(kCellEuler, 64)
+#define PN_RES_CASE(K, DPV, C) if (kind == K && DP == DPV && cpw == C) return resident_blocks_t<K, DPV, C>(lds, nb);
+    PN_RES_CASE(kCellTanhRnn, 16, 1) PN_RES_CASE(kCellTanhRnn, 32, 1) PN_RES_CASE(kCellTanhRnn, 64, 1)
+    PN_RES_CASE(kCellGru, 16, 1) PN_RES_CASE(kCellGru, 32, 1) PN_RES_CASE(kCellGru, 64, 1)
+    PN_RES_CASE(kCellEuler, 16, 1) PN_RES_CASE(kCellEuler, 32, 1) PN_RES_CASE(kCellEuler, 64, 1)
+    PN_RES_CASE(kCellTanhRnn, 16, 4) PN_RES_CASE(kCellGru, 16, 4) PN_RES_CASE(kCellEuler, 16, 4)
 #undef PN_RES_CASE
     return hipSuccess;
 }
 
-hipError_t launch_cell_resident(int kind, int DP, const ResidentArgs& a, hipStream_t st) {
-    const size_t lds = resident_lds_bytes(DP, a.L, a.m);
-#define PN_RES_CASE(K, DPV) if (kind == K && DP == DPV) return launch_resident_t<K, DPV>(a, lds, st);
-    PN_RES_CASE(kCellTanhRnn, 16) PN_RES_CASE(kCellTanhRnn, 32) PN_RES_CASE(kCellTanhRnn, 64)
-    PN_RES_CASE(kCellGru, 16) PN_RES_CASE(kCellGru, 32) PN_RES_CASE(kCellGru, 64)
-    PN_RES_CASE(kCellEuler, 16) PN_RES_CASE(kCellEuler, 32) PN_RES_CASE(kCellEuler, 64)
+hipError_t launch_cell_resident(int kind, int DP, int cpw, const ResidentArgs& a, hipStream_t st) {
+    const size_t lds = resident_lds_bytes(DP, a.L, a.m, cpw);
+#define PN_RES_CASE(K, DPV, C) if (kind == K && DP == DPV && cpw == C) return launch_resident_t<K, DPV, C>(a, lds, st);
+    PN_RES_CASE(kCellTanhRnn, 16, 1) PN_RES_CASE(kCellTanhRnn, 32, 1) PN_RES_CASE(kCellTanhRnn, 64, 1)
+    PN_RES_CASE(kCellGru, 16, 1) PN_RES_CASE(kCellGru, 32, 1) PN_RES_CASE(kCellGru, 64, 1)
+    PN_RES_CASE(kCellEuler, 16, 1) PN_RES_CASE(kCellEuler, 32, 1) PN_RES_CASE(kCellEuler, 64, 1)
+    PN_RES_CASE(kCellTanhRnn, 16, 4) PN_RES_CASE(kCellGru, 16, 4) PN_RES_CASE(kCellEuler, 16, 4)
 #undef PN_RES_CASE
     return hipErrorInvalidValue;
 }

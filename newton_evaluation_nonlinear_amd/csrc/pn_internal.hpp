@@ -266,8 +266,10 @@ struct ResidentArgs {
     int32_t hist_cap;
 };
 
-hipError_t cell_resident_max_blocks(int kind, int DP, int L, int m, int* nb);
-hipError_t launch_cell_resident(int kind, int DP, const ResidentArgs& a, hipStream_t st);
+// cpw: chunks per workgroup (1, or 4 at D padded to 16); the grid is
+// ceil(NC / cpw) x B workgroups
+hipError_t cell_resident_max_blocks(int kind, int DP, int L, int m, int cpw, int* nb);
+hipError_t launch_cell_resident(int kind, int DP, int cpw, const ResidentArgs& a, hipStream_t st);
 
 // Standalone affine scan.
 struct ScanArgs {

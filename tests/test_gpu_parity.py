@@ -683,6 +683,21 @@ def test_resident_solver_matches_oracle(kind, D, m, window):
         _parity(wl, mode, flags=pn.FLAG_MULTI_LAUNCH)
 
 
+@pytest.mark.parametrize("kind, window", [(pn.CELL_GRU, 0), (pn.CELL_TANH_RNN, 300), (pn.CELL_EULER_TANH, 0)])
+def test_resident_solver_four_chunks_per_workgroup(kind, window):
+    # more chunks than co-resident workgroups at D padded to 16: each
+    # workgroup takes four strided chunks (32-step chunks, 1280 of them)
+    rng = np.random.default_rng(1800 + kind + window)
+    D, m, B, T = 16, 8, 40, 1024
+    params = workloads.random_cell_params(kind, D, m, rng, 1.0)
+    wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-5, damping=0.8 if window else 1.0,
+              window=window, max_iter=window or T, params=params,
+              x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32))
+    for mode in (Q, J):
+        _parity(wl, mode)
+
+
 def test_resident_solver_outcomes():
     wl = _case(5, B=2, T=2048)
     g = run_gpu(wl, Q, tol=1e6)
