@@ -79,6 +79,8 @@ struct Plan {
                            // check in one launch (pn_small.hip)
     bool resident_ok;      // shape has the one-launch resident form (cell_resident), used
                            // when all B x NC chunks fit on the device at once
+    bool adv_resident_ok;  // advancing window with a one-launch resident form
+                           // (cell_resident_adv), used when its chunks fit at once
     bool recompute;        // channel-wise cell, float storage: first update stores nothing,
                            // the second recomputes s^(1) (kFirstNS, kSecondR)
     int fc;                // matrix cell, diagonal mode, few chunks (CellArgs::fc): the apply
@@ -87,7 +89,7 @@ struct Plan {
     int nblocks, nwin, hist_cap;
     size_t off_ctrl, off_rpart, off_fpart, off_aggA, off_aggB, off_carry, off_carry0, off_halo, off_w,
         total;
-    size_t off_sync, off_winfo, off_hist;
+    size_t off_sync, off_winfo, off_hist, off_acc, off_info_end;
 };
 
 void layout(Plan& p, const Plan* other);
@@ -210,6 +212,7 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
               static_cast<int64_t>(p.B) * p.W <= small_max_pairs_for(p.D);
     p.resident_ok = p.matrix_cell && !p.dense && !half && !p.advancing && (p.fc & kFcCheck) &&
                     p.DP % 16 == 0 && !p.small;
+    p.adv_resident_ok = p.matrix_cell && p.advancing && !p.dense && !half && p.DP % 16 == 0 && p.DP <= 64;
     p.hist_cap = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(p.nwin) * (p.W + 1), 1 << 16));
     layout(p, nullptr);
     return PN_OK;
@@ -232,7 +235,7 @@ void layout(Plan& p, const Plan* other) {
     p.off_rpart = off; off = align_up(off + sizeof(uint32_t) * nparts);
     p.off_fpart = off; off = align_up(off + sizeof(uint32_t) * nparts);
     // chunk maps: two sets (iterations of either parity) for fc sweeps
-    const size_t nsets = (p.fc || (other && other->fc)) ? 2 : 1;
+    const size_t nsets = (p.fc || p.adv_resident_ok || (other && other->fc)) ? 2 : 1;
     p.off_aggA = off; off = align_up(off + sizeof(float) * nA * nsets);
     p.off_aggB = off; off = align_up(off + sizeof(float) * bnd * nsets);
     p.off_carry = off; off = align_up(off + sizeof(float) * bnd);
@@ -241,12 +244,15 @@ void layout(Plan& p, const Plan* other) {
     p.off_halo = off; off = align_up(off + sizeof(float) * 2 * bnd);
     p.off_w = off;
     if (p.matrix_cell) off = align_up(off + sizeof(float) * prepared_total_floats(p.kind, p.DP, p.m));
-    p.off_sync = p.off_winfo = p.off_hist = off;
-    if (p.persist_ok || p.small || p.resident_ok) {
+    p.off_sync = p.off_winfo = p.off_hist = p.off_acc = off;
+    if (p.persist_ok || p.small || p.resident_ok || p.adv_resident_ok) {
         p.off_sync = off; off = align_up(off + 256);
         p.off_winfo = off; off = align_up(off + sizeof(int32_t) * 2 * p.nwin);
         p.off_hist = off; off = align_up(off + sizeof(float) * p.hist_cap);
+        p.off_acc = off;
+        if (p.adv_resident_ok) off = align_up(off + sizeof(int32_t) * p.hist_cap);
     }
+    p.off_info_end = off;
     p.total = off;
 }
 
@@ -263,6 +269,7 @@ int make_plans(Plan& p, Plan& p2, bool* has2, const pn_cell* cell, int64_t B, in
     p.persist_ok = p2.persist_ok = false;
     p.small = p2.small = false;
     p.resident_ok = p2.resident_ok = false;
+    p.adv_resident_ok = p2.adv_resident_ok = false;
     p.recompute = p2.recompute = false;
     p.fc = p2.fc = 0;
     p.Lc = p.L; p2.Lc = p2.L;
@@ -984,8 +991,8 @@ struct Backing {
 };
 
 // Where a one-launch solver writes its per-window counts, statuses and
-// residual history ([hist_len | win_iters, win_status | history], laid out as
-// the workspace region off_sync .. off_hist + hist_cap): straight to pinned
+// residual history ([hist_len | win_iters, win_status | history | accepted
+// steps], laid out as the workspace region off_sync .. off_info_end): straight to pinned
 // host memory, or, for pn_eval_noalloc (records in device memory), to the
 // workspace, copied back once after the launch.
 struct OneLaunchInfo {
@@ -997,7 +1004,7 @@ struct OneLaunchInfo {
 
 int one_launch_info(SolveCtx& c, OneLaunchInfo* inf) {
     const Plan& p = *c.p;
-    inf->nbytes = p.off_hist + sizeof(float) * p.hist_cap - p.off_sync;
+    inf->nbytes = p.off_info_end - p.off_sync;
     inf->dev = c.ws + p.off_sync;
     if (!c.res->dev_ring) {
         char* h = nullptr;
@@ -1137,6 +1144,104 @@ int solve_resident(SolveCtx& c, const float* x, const float* s0, float* out, int
     return PN_OK;
 }
 
+// The advancing window as one cooperative launch of cell_resident_adv: the
+// shortest chunk (from the plan's on) whose B x ceil(W / L) workgroups are
+// co-resident.  Returns PN_EUNSUPPORTED (nothing launched) when none fits.
+int solve_advancing_resident(SolveCtx& c, const float* x, const float* s0, float* out, int64_t T, int* K,
+                             int* status, std::vector<int32_t>* accepted) {
+    const Plan& p = *c.p;
+    int dev = 0, coop = 0;
+    PN_HIP(hipGetDevice(&dev));
+    PN_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
+    if (!coop) return PN_EUNSUPPORTED;
+    int L = 0, NC = 0;
+    for (int64_t Lt = p.L; Lt <= 64; Lt *= 2) {
+        const int nc = static_cast<int>((p.W + Lt - 1) / Lt);
+        int nb = 0;
+        PN_HIP(cell_resident_adv_max_blocks(p.kind, p.DP, static_cast<int>(Lt), p.m, &nb));
+        if (static_cast<int64_t>(p.B) * nc <= nb) {
+            L = static_cast<int>(Lt);
+            NC = nc;
+            break;
+        }
+        if (Lt >= p.W) break;
+    }
+    if (L == 0) return PN_EUNSUPPORTED;
+    OneLaunchInfo inf;
+    int rc = one_launch_info(c, &inf);
+    if (rc != PN_OK) return rc;
+    char* ws = c.ws;
+    ResidentArgs a{};
+    a.w = reinterpret_cast<const float*>(ws + p.off_w);
+    a.x = x; a.out = out; a.s0 = s0; a.T = T;
+    a.W = static_cast<int32_t>(p.W); a.nwin = 1; a.B = p.B; a.D = p.D; a.m = p.m; a.L = L;
+    a.NC = NC; a.mode = p.mode; a.undamped = c.lam == 1.0f; a.max_iter = c.max_iter;
+    a.lam = c.lam; a.tol = c.tol;
+    a.mapA = reinterpret_cast<float*>(ws + p.off_aggA);
+    a.mapB = reinterpret_cast<float*>(ws + p.off_aggB);
+    Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + p.off_ctrl);
+    a.rslot = &ctrl->rmax[0][0][0];
+    a.bar = reinterpret_cast<unsigned*>(ws + p.off_rpart);   // one arrival word per workgroup
+    a.err = &ctrl->bar_err;
+    a.hist_len = reinterpret_cast<int32_t*>(inf.dev);
+    a.win_iters = reinterpret_cast<int32_t*>(inf.dev + (p.off_winfo - p.off_sync));
+    a.win_status = a.win_iters + p.nwin;
+    a.hist = reinterpret_cast<float*>(inf.dev + (p.off_hist - p.off_sync));
+    a.hist_cap = p.hist_cap;
+    a.acc = reinterpret_cast<int32_t*>(inf.dev + (p.off_acc - p.off_sync));
+    a.acc_cap = p.hist_cap;
+    // residual and first-step slots, arrival words and error flag start at zero
+    PN_HIP(hipMemsetAsync(ctrl, 0, sizeof(Ctrl), c.st));
+    PN_HIP(hipMemsetAsync(a.bar, 0, sizeof(unsigned) * p.B * NC, c.st));
+    const bool timed = c.tm->take();
+    size_t e0 = 0, e1 = 0;
+    if (timed) { rc = request_timing(c, &e0, &e1); if (rc) return rc; }
+    {
+        const hipError_t le = launch_cell_resident_adv(p.kind, p.DP, a, c.st);
+        if (le == hipErrorCooperativeLaunchTooLarge) {
+            (void)hipGetLastError();
+            g_launch_timing = LaunchTiming{};
+            return PN_EUNSUPPORTED;
+        }
+        if (le != hipSuccess) return fail(PN_EHIP, "cooperative launch failed: %s", hipGetErrorString(le));
+    }
+    if (timed) { rc = check_timed_launch(); if (rc) return rc; }
+    if (c.res->dev_ring) {
+        inf.copy.resize(inf.nbytes);
+        PN_HIP(hipMemcpyAsync(inf.copy.data(), inf.dev, inf.nbytes, hipMemcpyDeviceToHost, c.st));
+        inf.host = inf.copy.data();
+    }
+    PN_HIP(hipStreamSynchronize(c.st));
+    unsigned err = 0;
+    PN_HIP(hipMemcpy(&err, a.err, sizeof(err), hipMemcpyDeviceToHost));
+    if (err != 0) return fail(PN_EHIP, "grid barrier of the resident solver timed out");
+    int32_t hlen = 0;
+    std::memcpy(&hlen, inf.host, sizeof(hlen));
+    const int32_t* wi = reinterpret_cast<const int32_t*>(inf.host + (p.off_winfo - p.off_sync));
+    const float* hist = reinterpret_cast<const float*>(inf.host + (p.off_hist - p.off_sync));
+    const int32_t* acc = reinterpret_cast<const int32_t*>(inf.host + (p.off_acc - p.off_sync));
+    *K = wi[0];
+    *status = wi[p.nwin];
+    if (c.hist) c.hist->assign(hist, hist + std::min(hlen, p.hist_cap));
+    const int rounds = std::min(*status == PN_NONFINITE ? hlen - 1 : hlen, p.hist_cap);
+    accepted->assign(acc, acc + std::max(rounds, 0));
+    if (timed) {
+        // the windows the updates ran on, from the accepted steps
+        double bytes = 0.0, flops = 0.0;
+        int64_t A = 0;
+        for (int k = 0; k < *K && k < static_cast<int>(accepted->size()); ++k) {
+            A += (*accepted)[k];
+            const int Tw = static_cast<int>(std::min<int64_t>(T, A + p.W) - A);
+            bytes += apply_bytes(p, Tw, false);
+            flops += apply_flops(p, Tw);
+        }
+        c.tm->apply.push_back({e0, e1});
+        c.tm->apply_bytes.push_back(bytes);
+        c.tm->apply_flops.push_back(flops);
+    }
+    return PN_OK;
+}
+
 // Frees a workspace the library allocated for one call on every exit path.
 struct OwnedWorkspace {
     void* p = nullptr;
@@ -1247,7 +1352,15 @@ int eval_impl(const pn_cell* cell, const float* params, const float* x, const fl
     }
     if (p.advancing) {
         int K = 0, status = PN_OK;
-        rc = solve_advancing(c, x, s0, out, T, &K, &status, &accepted);
+        // one launch when the chunks fit at once and the history holds every check
+        rc = PN_EUNSUPPORTED;
+        if (p.adv_resident_ok && !multi && max_iter < p.hist_cap)
+            rc = solve_advancing_resident(c, x, s0, out, T, &K, &status, &accepted);
+        if (rc == PN_EUNSUPPORTED) {
+            accepted.clear();
+            if (c.hist) c.hist->clear();
+            rc = solve_advancing(c, x, s0, out, T, &K, &status, &accepted);
+        }
         if (rc != PN_OK) return rc;
         total = K;
         wit.push_back(K);

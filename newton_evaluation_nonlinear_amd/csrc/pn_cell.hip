@@ -1954,6 +1954,324 @@ __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(Resid
     }
 }
 
+// ---------------------------------------------------------------- resident advancing window
+// The advancing window [PN §1.3.1] of a matrix cell in a diagonal mode as one
+// cooperative launch: workgroup (c, b) owns chunk c of batch row b of the
+// current window [A, E), steps A + cL .. A + (c+1)L - 1.  A round is
+//   check:  r_t of the current iterate on [A, E) and the first step over tol,
+//           reduced over the grid (slot words 0 and 1), read alike by every
+//           workgroup, which then all take the same decision;
+//   slide:  A moves past the accepted prefix, E = min(T, A + W); when the
+//           window moved, every workgroup stages its chunk of the new window
+//           from the iterate in `out` (steps from the old E on start from the
+//           old window's last state) and evaluates the cell there;
+//   update: the chunk map, a grid barrier, the carry folded from the maps of
+//           the chunks before it applied to the accepted state s_{A-1}, the
+//           replay with damping, and the evaluation at the new iterate,
+//           which is the next check; the chunk's rows go back to `out`.
+// Rows travel between workgroups only through `out`, with device-scope
+// loads and stores; the window never needs the host.
+template <int CELL, int DP>
+__global__ __launch_bounds__(kThreads, 1) void cell_resident_adv(ResidentArgs a) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    constexpr int PS = iterate_stride<DP>();
+    constexpr int NS = kThreads / DP;            // fold segments per channel
+    const int L = a.L, m = a.m, D = a.D;
+    const int64_t T = a.T, W = a.W;
+    const int xs = x_stride(m);
+    const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int GX = gridDim.x;
+    const unsigned nblocks = gridDim.x * gridDim.y;
+    const bool lead = c == 0 && b == 0;
+    float* S = lds;                              // [L+1][PS] rows t0-1 .. t0+L-1 of the iterate
+    float* V = S + (L + 1) * PS;                 // [L][DP] f_t at the iterate
+    float* CO = V + L * DP;                      // [L][DP] diagonal coefficients
+    float* X = CO + L * DP;                      // [L][xs]
+    float* SCR = X + L * xs;                     // [2][kThreads] fold segments
+    float* S0 = SCR + 2 * kThreads;              // [DP] accepted state s_{A-1}
+    float* FILL = S0 + DP;                       // [DP] start value of steps entering the window
+    float* outb = a.out + static_cast<int64_t>(b) * T * D;
+    const float* s0b = a.s0 + static_cast<int64_t>(b) * D;
+    CellRegs<CELL, DP> cr;
+    cr.load(a.w, a.w, D, m);
+    unsigned epoch = 0;
+    const bool rthr = tid < D;                   // replay / composition thread of channel tid
+    float own_a = 1.0f, own_b = 0.0f;
+
+    // the chunk of window [A, E) with the iterate's rows below Ev read from
+    // out and the rest set to the fill value; returns the chunk's rows
+    auto stage = [&](int64_t A, int64_t E, int64_t Ev) -> int {
+        const int64_t t0 = A + static_cast<int64_t>(c) * L;
+        const int Lc = t0 < E ? static_cast<int>(E - t0 < L ? E - t0 : L) : 0;
+        if (tid < DP) {
+            float sv = 0.0f, fv = 0.0f;
+            if (tid < D) {
+                sv = A == 0 ? s0b[tid] : ld_dev(outb + (A - 1) * D + tid);
+                fv = Ev == 0 ? s0b[tid] : ld_dev(outb + (Ev - 1) * D + tid);
+            }
+            S0[tid] = sv;
+            FILL[tid] = fv;
+        }
+        if (Lc > 0) copy_rows_to_lds<kThreads>(X, xs, a.x + (static_cast<int64_t>(b) * T + t0) * m, m, Lc, m);
+        __syncthreads();
+        for (int e = tid; e < (Lc + 1) * PS; e += kThreads) {
+            const int r = e / PS, i = e - r * PS;
+            const int64_t t = t0 - 1 + r;
+            float v = 0.0f;
+            if (i < D) v = t < 0 ? s0b[i] : (t < Ev ? ld_dev(outb + t * D + i) : FILL[i]);
+            S[e] = v;
+        }
+        __syncthreads();
+        return Lc;
+    };
+    // the chunk's rows of the iterate back to out
+    auto write_rows = [&](int64_t t0, int Lc) {
+        for (int e = tid; e < Lc * D; e += kThreads) {
+            const int j = e / D, i = e - j * D;
+            st_dev(outb + (t0 + j) * D + i, S[(j + 1) * PS + i]);
+        }
+    };
+    // residual maximum and first step over tol of the chunk into check q's slots
+    auto publish = [&](int q, uint32_t rb, uint32_t fb, int64_t rel0) {
+        rb = block_max_u32(rb);
+        const uint32_t nf = block_max_u32(fb == 0xffffffffu ? 0u : ~static_cast<uint32_t>(rel0 + fb));
+        if (tid == 0) {
+            uint32_t* sl = a.rslot + ((q % 3) * kRSlots + (b * GX + c) % kRSlots) * 64;
+            __hip_atomic_fetch_max(sl, rb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_max(sl + 1, nf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+
+    // round 0: the initial iterate s0 on [0, E), written out, and its check
+    int64_t A = 0, E = T < W ? T : W;
+    int Lc = stage(0, E, 0);
+    {
+        uint32_t rb = 0, fb = 0xffffffffu;
+        if (Lc > 0) {
+            cr.project(a.w, X, xs, Lc, m);
+            cr.template eval<false>(S, V, CO, Lc, L, a.mode, S, rb, &fb, a.tol);
+            write_rows(static_cast<int64_t>(c) * L, Lc);
+        }
+        publish(0, rb, fb, static_cast<int64_t>(c) * L);
+    }
+    if (!resident_sync(a, epoch, nblocks)) return;
+    int K = 0, status = kStOk, hist_pos = 0;
+    for (int i = 0, q = 0;; ++q) {
+        // the check of round q (i updates so far), taken alike by every workgroup
+        const int lane = tid & 63;
+        const uint32_t* sl = a.rslot + ((q % 3) * kRSlots + (lane < kRSlots ? lane : 0)) * 64;
+        const uint32_t rv = lane < kRSlots ? __hip_atomic_load(sl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+        const uint32_t fv = lane < kRSlots ? __hip_atomic_load(sl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+        const uint32_t r_q = wave_max_u32(rv);
+        const uint32_t first = ~wave_max_u32(fv);
+        if (lead) {
+            if (tid == 0 && hist_pos < a.hist_cap) a.hist[hist_pos] = __uint_as_float(r_q);
+            if (tid < kRSlots) {
+                uint32_t* cl = a.rslot + (((q + 2) % 3) * kRSlots + tid) * 64;
+                __hip_atomic_store(cl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(cl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        ++hist_pos;
+        if (r_q >= kNonFiniteBits) { K = i; status = kStNonFinite; break; }
+        const int64_t acc = static_cast<int64_t>(first) < E - A ? static_cast<int64_t>(first) : E - A;
+        if (lead && tid == 0 && q < a.acc_cap) a.acc[q] = static_cast<int32_t>(acc);
+        A += acc;
+        if (A >= T) { K = i; status = kStOk; break; }
+        if (i >= a.max_iter) { K = i; status = kStNotConverged; break; }
+        const int64_t En = T < A + W ? T : A + W;
+        const int64_t t0 = A + static_cast<int64_t>(c) * L;
+        if (acc != 0 || En != E) {
+            // the moved window: stage the chunk at the current iterate and evaluate
+            Lc = stage(A, En, E);
+            if (Lc > 0) {
+                uint32_t rb_unused = 0;
+                cr.project(a.w, X, xs, Lc, m);
+                cr.template eval<false>(S, V, CO, Lc, L, a.mode, nullptr, rb_unused, nullptr, a.tol);
+            }
+            __syncthreads();
+        }
+        E = En;
+        const int NCw = static_cast<int>((E - A + L - 1) / L);
+        const int par = i & 1;
+        const size_t HS = static_cast<size_t>(a.B) * a.NC * D;
+        float* mA = a.mapA + par * HS + static_cast<size_t>(b) * a.NC * D;
+        float* mB = a.mapB + par * HS + static_cast<size_t>(b) * a.NC * D;
+        // the chunk map of update i
+        if (rthr && Lc > 0) {
+            float Am = 1.0f, Bm = 0.0f;
+            if (a.mode == kJacobi) {
+                Am = 0.0f;
+                Bm = V[(Lc - 1) * DP + tid];
+            } else {
+#pragma unroll 8
+                for (int j = 0; j < Lc; ++j) {
+                    const float at = CO[j * DP + tid];
+                    Bm = at * Bm + (V[j * DP + tid] - at * S[j * PS + tid]);
+                    Am = at * Am;
+                }
+            }
+            own_a = Am;
+            own_b = Bm;
+            st_dev(mA + static_cast<size_t>(c) * D + tid, Am);
+            st_dev(mB + static_cast<size_t>(c) * D + tid, Bm);
+        }
+        if (!resident_sync(a, epoch, nblocks)) return;
+        if (Lc > 0) {
+            // the carry of chunk c: NS segments of the maps of the chunks before it
+            {
+                const int d = tid % DP, sg_ = tid / DP;
+                const int per = (c + NS - 1) / NS;
+                const int k0 = min(c, sg_ * per);
+                const int k1 = d < D ? min(c, k0 + per) : k0;
+                float fa = 1.0f, fbv = 0.0f;
+                for (int kk = k0; kk < k1; ++kk) {
+                    const float ak = ld_dev(mA + kk * D + d);
+                    fbv = ak * fbv + ld_dev(mB + kk * D + d);
+                    fa = ak * fa;
+                }
+                SCR[tid] = fa;
+                SCR[kThreads + tid] = fbv;
+            }
+            __syncthreads();
+            // replay from the carry, damping, in place: rows t0-1 .. t0+Lc-1 of the new iterate
+            if (rthr) {
+                const float lam = a.lam;
+                const bool und = a.undamped != 0;
+                const bool has_next = c + 1 < NCw;
+                float xv = S0[tid];
+#pragma unroll
+                for (int sgi = 0; sgi < NS; ++sgi) xv = SCR[sgi * DP + tid] * xv + SCR[kThreads + sgi * DP + tid];
+                const float c_next = own_a * xv + own_b;
+                float pold = S[tid];
+                float shat = xv;
+                S[tid] = und ? shat : pold + lam * (shat - pold);
+                const int nrep = has_next ? Lc - 1 : Lc;
+                if (a.mode == kJacobi) {
+                    for (int j = 0; j < nrep; ++j) {
+                        const float so = S[(j + 1) * PS + tid];
+                        const float sh = V[j * DP + tid];
+                        S[(j + 1) * PS + tid] = und ? sh : so + lam * (sh - so);
+                    }
+                } else {
+                    int j = 0;
+                    for (; j + 8 <= nrep; j += 8) {
+                        float v[8], co[8], po[8];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            v[u] = V[(j + u) * DP + tid];
+                            co[u] = CO[(j + u) * DP + tid];
+                            po[u] = S[(j + u + 1) * PS + tid];
+                        }
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            shat = v[u] + co[u] * (shat - pold);
+                            pold = po[u];
+                            S[(j + u + 1) * PS + tid] = und ? shat : pold + lam * (shat - pold);
+                        }
+                    }
+                    for (; j < nrep; ++j) {
+                        shat = V[j * DP + tid] + CO[j * DP + tid] * (shat - pold);
+                        pold = S[(j + 1) * PS + tid];
+                        S[(j + 1) * PS + tid] = und ? shat : pold + lam * (shat - pold);
+                    }
+                }
+                if (has_next) {
+                    const float so = S[Lc * PS + tid];
+                    S[Lc * PS + tid] = und ? c_next : so + lam * (c_next - so);
+                }
+            }
+            __syncthreads();
+        }
+        // the check of the next round: the cell at the new iterate
+        uint32_t rb = 0, fb = 0xffffffffu;
+        if (Lc > 0) {
+            cr.template eval<false>(S, V, CO, Lc, L, a.mode, S, rb, &fb, a.tol);
+            write_rows(t0, Lc);
+        }
+        ++i;
+        publish(q + 1, rb, fb, static_cast<int64_t>(c) * L);
+        if (!resident_sync(a, epoch, nblocks)) return;
+    }
+    // steps the window never reached hold the last state of the window
+    if (E < T) {
+        const int64_t n = (T - E) * D;
+        for (int64_t e = static_cast<int64_t>(c) * kThreads + tid; e < n; e += static_cast<int64_t>(GX) * kThreads) {
+            const int i = static_cast<int>(e % D);
+            outb[E * D + e] = ld_dev(outb + (E - 1) * D + i);
+        }
+    }
+    if (lead && tid == 0) {
+        a.win_iters[0] = K;
+        a.win_status[0] = status;
+        *a.hist_len = hist_pos;
+    }
+}
+
+size_t resident_adv_lds_bytes(int DP, int L, int m) {
+    const size_t PS = DP + 4, xs = x_stride(m);
+    const size_t n = (L + 1) * PS + 2ull * L * DP + static_cast<size_t>(L) * xs + 2ull * kThreads + 2ull * DP;
+    return sizeof(float) * n;
+}
+
+template <int CELL, int DP>
+static hipError_t resident_adv_blocks_t(size_t lds, int* nb) {
+    int per_cu = 0, dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (lds > 64 * 1024) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(cell_resident_adv<CELL, DP>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cell_resident_adv<CELL, DP>, kThreads, lds);
+    if (e != hipSuccess) return e;
+    *nb = per_cu * ncu;
+    return hipSuccess;
+}
+
+template <int CELL, int DP>
+static hipError_t launch_resident_adv_t(const ResidentArgs& a, size_t lds, hipStream_t st) {
+    void* args[] = {const_cast<ResidentArgs*>(&a)};
+    LaunchTiming& t = launch_timing();
+    if (t.start) {
+        hipError_t e = hipEventRecord(t.start, st);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(cell_resident_adv<CELL, DP>),
+                                              dim3(a.NC, a.B), dim3(kThreads), args, static_cast<unsigned>(lds), st);
+    if (e != hipSuccess) return e;
+    if (t.start) {
+        e = hipEventRecord(t.stop, st);
+        t = LaunchTiming{};
+    }
+    return e;
+}
+
+hipError_t cell_resident_adv_max_blocks(int kind, int DP, int L, int m, int* nb) {
+    *nb = 0;
+    const size_t lds = resident_adv_lds_bytes(DP, L, m);
+    if (lds > 160 * 1024 || L > kMaxChunk) return hipSuccess;
+#define PN_RES_CASE(K, DPV) if (kind == K && DP == DPV) return resident_adv_blocks_t<K, DPV>(lds, nb);
+    PN_RES_CASE(kCellTanhRnn, 16) PN_RES_CASE(kCellTanhRnn, 32) PN_RES_CASE(kCellTanhRnn, 64)
+    PN_RES_CASE(kCellGru, 16) PN_RES_CASE(kCellGru, 32) PN_RES_CASE(kCellGru, 64)
+    PN_RES_CASE(kCellEuler, 16) PN_RES_CASE(kCellEuler, 32) PN_RES_CASE(kCellEuler, 64)
+#undef PN_RES_CASE
+    return hipSuccess;
+}
+
+hipError_t launch_cell_resident_adv(int kind, int DP, const ResidentArgs& a, hipStream_t st) {
+    const size_t lds = resident_adv_lds_bytes(DP, a.L, a.m);
+#define PN_RES_CASE(K, DPV) if (kind == K && DP == DPV) return launch_resident_adv_t<K, DPV>(a, lds, st);
+    PN_RES_CASE(kCellTanhRnn, 16) PN_RES_CASE(kCellTanhRnn, 32) PN_RES_CASE(kCellTanhRnn, 64)
+    PN_RES_CASE(kCellGru, 16) PN_RES_CASE(kCellGru, 32) PN_RES_CASE(kCellGru, 64)
+    PN_RES_CASE(kCellEuler, 16) PN_RES_CASE(kCellEuler, 32) PN_RES_CASE(kCellEuler, 64)
+#undef PN_RES_CASE
+    return hipErrorInvalidValue;
+}
+
 size_t resident_lds_bytes(int DP, int L, int m, int cpw) {
     const size_t PS = DP + 4, xs = x_stride(m);
     const size_t per = (L + 1) * PS + 2ull * L * DP + static_cast<size_t>(L) * xs;

@@ -264,12 +264,18 @@ struct ResidentArgs {
     int32_t* hist_len;
     float* hist;
     int32_t hist_cap;
+    int32_t* acc;            // advancing window: steps accepted at each check
+    int32_t acc_cap;
 };
 
 // cpw: chunks per workgroup (1, or 4 at D padded to 16); the grid is
 // ceil(NC / cpw) x B workgroups
 hipError_t cell_resident_max_blocks(int kind, int DP, int L, int m, int cpw, int* nb);
 hipError_t launch_cell_resident(int kind, int DP, int cpw, const ResidentArgs& a, hipStream_t st);
+// The advancing window as one cooperative launch: one chunk of L steps per
+// workgroup, grid NC x B with NC = ceil(W / L).
+hipError_t cell_resident_adv_max_blocks(int kind, int DP, int L, int m, int* nb);
+hipError_t launch_cell_resident_adv(int kind, int DP, const ResidentArgs& a, hipStream_t st);
 
 // Standalone affine scan.
 struct ScanArgs {

@@ -284,6 +284,8 @@ def check_parity_advancing(wl, mode, gpu, ref, label=""):
             if acc < len(r_t):
                 assert r_t[acc] >= tol - band, f"{msg}: check {k} rejected r={r_t[acc]:.4e}"
         assert forced.status == gpu.status and forced.iters == gpu.iters, msg
+        BAND_LOG.append((label, mode, f"advancing decisions within the band ({len(off)} differ)",
+                         [gpu.iters], [ref.iters]))
         cmp_ref = forced
     assert gpu.status == cmp_ref.status, msg
     s_ref = cmp_ref.s

@@ -60,7 +60,7 @@ def _parity(wl, mode, exact=False, f32_count=False, **kw):
     print(f"   gpu iters={gpu.iters} win={gpu.window_iters[:6]} status={gpu.status} "
           f"oracle iters={ref.iters} win={ref.window_iters[:6]} status={ref.status}", flush=True)
     if advancing(wl):
-        assert not kw, "the advancing-window cases run with the workload's own settings"
+        assert set(kw) <= {"flags"}, "the advancing-window cases run with the workload's own settings"
         return check_parity_advancing(wl, mode, gpu, ref, label=_label(wl))
     _report_residual_agreement(gpu, ref)
     if ref.status == oracle.NONFINITE or gpu.status == pn.NONFINITE:
@@ -370,15 +370,44 @@ def test_advancing_window_channel_wise_cell(D, W, mode):
 @pytest.mark.parametrize("kind, D", [(pn.CELL_EULER_TANH, 32), (pn.CELL_EULER_TANH, 64),
                                      (pn.CELL_GRU, 16), (pn.CELL_TANH_RNN, 5)])
 @pytest.mark.parametrize("W", [40, 128])
-def test_advancing_window_matches_oracle(kind, D, W):
-    # windows that are not a multiple of the chunk, a ragged end, every mode
+@pytest.mark.parametrize("flags", [0, pn.FLAG_MULTI_LAUNCH])
+def test_advancing_window_matches_oracle(kind, D, W, flags):
+    # windows that are not a multiple of the chunk, a ragged end, every mode;
+    # the diagonal modes at D = 16, 32, 64 run as one resident launch unless
+    # FLAG_MULTI_LAUNCH asks for the launch-per-round driver
     wl = _advancing_case(kind, D, 4, 2, 333, W, 600 + D + W)
     # Picard (A~ = I) is the small-step method: run on the Euler cell only.
     # On the plain tanh RNN and the GRU it passes through 1e7-1e30
     # transients, and which tail steps happen to meet tol is then decided by
     # the rounding of those transients
     for mode in (Q, N, J, pn.BANDED) + ((P,) if kind == pn.CELL_EULER_TANH else ()):
+        _parity(wl, mode, flags=flags)
+
+
+@pytest.mark.parametrize("kind, D, m, B, T, W", [
+    (pn.CELL_EULER_TANH, 32, 8, 40, 2000, 256),   # 640 chunks of 16 steps: runs on 32-step chunks
+    (pn.CELL_GRU, 64, 6, 8, 1200, 300),           # a window that is not a multiple of the chunk
+    (pn.CELL_TANH_RNN, 24, 5, 6, 900, 1000),      # a window longer than the horizon
+])
+def test_advancing_resident_matches_oracle(kind, D, m, B, T, W):
+    # the one-launch advancing window and the launch-per-round driver, each
+    # against the oracle's decisions (the two may round a decision that lies
+    # within the ambiguity band of tol differently)
+    wl = _advancing_case(kind, D, m, B, T, W, 660 + D + W)
+    for mode in ((P, Q, J) if kind == pn.CELL_EULER_TANH else (Q, J)):
         _parity(wl, mode)
+        _parity(wl, mode, flags=pn.FLAG_MULTI_LAUNCH)
+
+
+@pytest.mark.parametrize("flags", [0, pn.FLAG_MULTI_LAUNCH])
+def test_advancing_window_nonfinite_mid_horizon(flags):
+    # a NaN input at step 700 of one row: the check of the first window that
+    # reaches it reports NONFINITE, after the prefix before it was accepted
+    wl = _advancing_case(pn.CELL_EULER_TANH, 32, 4, 3, 1200, 128, 671)
+    wl["x"][1, 700, 2] = np.nan
+    for mode in (Q, P):
+        ref = _parity(wl, mode, flags=flags)
+        assert ref.status == oracle.NONFINITE and sum(ref.accepted) <= 700
 
 
 def test_advancing_window_carry_launch_path():
@@ -407,15 +436,18 @@ def test_advancing_window_exact_newton_takes_one_update_per_window():
     assert ref.iters == -(-T // W)
 
 
-def test_advancing_window_cap_fills_the_tail():
+@pytest.mark.parametrize("flags", [0, pn.FLAG_MULTI_LAUNCH])
+@pytest.mark.parametrize("cap", [0, 7])
+def test_advancing_window_cap_fills_the_tail(flags, cap):
     wl = _advancing_case(pn.CELL_EULER_TANH, 16, 3, 2, 500, 64, 630)
-    wl["max_iter"] = 7
-    gpu = run_gpu(wl, Q)
+    wl["max_iter"] = cap
+    gpu = run_gpu(wl, Q, flags=flags)
     ref = run_oracle(wl, Q)
-    assert gpu.status == ref.status == pn.NOT_CONVERGED and gpu.iters == ref.iters == 7
+    assert gpu.status == ref.status == pn.NOT_CONVERGED and gpu.iters == ref.iters == cap
+    assert gpu.accepted == ref.accepted
     assert np.all(np.isfinite(gpu.out_np))
     np.testing.assert_allclose(gpu.out_np, ref.s, rtol=0, atol=1e-4)
-    assert len(gpu.resid_hist) == 8
+    assert len(gpu.resid_hist) == cap + 1
     np.testing.assert_allclose(gpu.resid_hist, ref.hist[0], rtol=2e-2, atol=1e-6)
 
 
