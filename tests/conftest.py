@@ -16,8 +16,10 @@ def pytest_configure(config):
 
 def pytest_terminal_summary(terminalreporter, exitstatus, config):
     """List every parity case whose iteration count was accepted through the
-    one-off ambiguity band or the float32 count reference (none means every
-    count equalled the float64 oracle's)."""
+    one-off ambiguity band or the float32 count reference, and every
+    advancing-window case whose acceptance decisions differed from the float64
+    oracle's within the band (none means every count and decision equalled
+    the oracle's)."""
     mod = sys.modules.get("_parity")
     if mod is None:
         return
