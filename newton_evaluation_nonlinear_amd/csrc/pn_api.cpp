@@ -171,6 +171,9 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
         p.L = p.Lc = static_cast<int>(std::min<int64_t>(L, p.W));
         p.NC = static_cast<int>((p.W + p.L - 1) / p.L);
         p.nblocks = p.NC * p.B;
+        // the apply sweeps take their own check, so the carry launches need
+        // not, and the sweeps are enqueued ahead of the host's reads
+        if (!p.advancing && p.DP <= 32) p.fc = kFcCheck;
     } else {
         p.DP = std::max(4, next_pow2(p.D));
         const int Lmax = 64;
@@ -235,7 +238,7 @@ void layout(Plan& p, const Plan* other) {
     p.off_rpart = off; off = align_up(off + sizeof(uint32_t) * nparts);
     p.off_fpart = off; off = align_up(off + sizeof(uint32_t) * nparts);
     // chunk maps: two sets (iterations of either parity) for fc sweeps
-    const size_t nsets = (p.fc || p.adv_resident_ok || (other && other->fc)) ? 2 : 1;
+    const size_t nsets = ((p.fc & kFcCarry) || p.adv_resident_ok || (other && (other->fc & kFcCarry))) ? 2 : 1;
     p.off_aggA = off; off = align_up(off + sizeof(float) * nA * nsets);
     p.off_aggB = off; off = align_up(off + sizeof(float) * bnd * nsets);
     p.off_carry = off; off = align_up(off + sizeof(float) * bnd);
@@ -628,6 +631,12 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
     };
 
     configure(*pp);
+    // sweeps that take their own check leave the carry launches only the
+    // carries; a carry launch queued after the stop does nothing
+    if (pp->fc & kFcCheck) {
+        cy.do_check = 0;
+        cy.stop_on = ctrl;
+    }
     *sw = -1;
     // fc sweeps reduce r_0 into ctrl->rmax[0] and expect rmax[1] clear
     if (pp->fc & kFcCheck) PN_HIP(hipMemsetAsync(ctrl, 0, sizeof(Ctrl), c.st));
@@ -653,7 +662,10 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
     // Apply launch k (update k).  Sweeps that take their own check (fc) are
     // kept `ahead` launches in front of the check the host is reading: a
     // sweep after the stop finds the control word set and exits at once.
-    const int ahead = (pp->fc & kFcCheck) ? 2 : 0;
+    // (one when the check is published at the start of the sweep, as in the
+    // sweeps that keep their carry launches: the host reads it while the
+    // sweep runs)
+    const int ahead = (pp->fc & kFcCheck) ? ((pp->fc & kFcCarry) ? 2 : 1) : 0;
     std::vector<int> tslot;      // launch k -> its timing entry, or -1
     auto enqueue_apply = [&](int k) -> int {
         const int phase = k == 0 ? (recompute ? kFirstNS : kFirst)
@@ -661,6 +673,9 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
         if (recompute) grain(k >= 2, k == 2 ? pp->Lc / pp->L : 1);
         // timing covers the steady-state apply launches, including the
         // final ones that exit at once
+        if ((pp->fc & kFcCheck) && !(pp->fc & kFcCarry))
+            // the carries of iteration k's maps (a launch after the stop exits at once)
+            PN_HIP(pp->dense ? launch_dense_carry(cy, c.st) : launch_diag_carry(cy, c.st));
         const bool timed = phase == kSteady && c.tm->take();
         size_t e0 = 0, e1 = 0;
         if (timed) { int rc = request_timing(c, &e0, &e1); if (rc) return rc; }

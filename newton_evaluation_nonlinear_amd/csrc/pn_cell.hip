@@ -1475,6 +1475,7 @@ __device__ __forceinline__ void carry_chain(const CarryArgs& g, float* ys, float
 
 template <int DP>
 __global__ __launch_bounds__(64) void dense_carry_kernel(CarryArgs g) {
+    if (g.stop_on && g.stop_on->stop) return;     // queued ahead of a stop
     if (g.do_check && blockIdx.x == 0) run_check(g.chk);
     __shared__ __attribute__((aligned(16))) float ys[DP < 4 ? 4 : DP];
     const int b = blockIdx.x;
@@ -1530,6 +1531,7 @@ __device__ __forceinline__ float dpp_add(float v) {
 
 template <int DP>
 __global__ __launch_bounds__(DP * DP / 4) void dense_carry_wide(CarryArgs g) {
+    if (g.stop_on && g.stop_on->stop) return;     // queued ahead of a stop
     if (g.do_check && blockIdx.x == 0) run_check(g.chk);
     constexpr int TPR = DP / 4;              // threads per map row
     __shared__ __attribute__((aligned(16))) float ys[2][DP];

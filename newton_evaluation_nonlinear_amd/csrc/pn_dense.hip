@@ -264,6 +264,31 @@ template <int CELL, int DP, int PHASE, bool BANDED, bool SPLIT>
 __global__ __launch_bounds__(SPLIT ? 128 : 64) void dense_pass(CellArgs g) {
     if constexpr (PHASE != kPrologue && PHASE != kMaps) {   // apply launches enqueued ahead
         if (g.ctrl->stop) return;
+        if (g.fc & kFcCheck) {
+            // The check of iteration i, taken alike by every workgroup from
+            // the residual slots the sweep before filled; a stop writes
+            // nothing.  Workgroup (0, 0) clears the slot set of the sweep
+            // after next and publishes the check to the control word and
+            // the host.
+            const int ln = threadIdx.x & 63;
+            const uint32_t rv = ln < kRSlots ? g.ctrl->rmax[g.iter % 3][ln][0] : 0u;
+            const uint32_t r_i = wave_max_u32(rv);
+            CheckArgs chk{};
+            chk.iter = g.iter;
+            chk.max_iter = g.max_iter;
+            chk.tol = g.tol;
+            chk.ctrl = g.ctrl;
+            chk.host = g.host + g.iter % kHostRing;
+            chk.epoch = g.epoch;
+            const int st = check_status(r_i, chk);
+            if (blockIdx.x == 0 && blockIdx.y == 0) {
+                if (threadIdx.x < kRSlots)
+                    __hip_atomic_store(&g.ctrl->rmax[(g.iter + 2) % 3][threadIdx.x][0], 0u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                if (threadIdx.x == 0) publish_check(chk, r_i, st, 0xffffffffu);
+            }
+            if (st >= 0) return;
+        }
     }
     using Tl = MfmaTile<DP>;
     using acc_t = typename Tl::acc_t;
@@ -429,13 +454,47 @@ __global__ __launch_bounds__(SPLIT ? 128 : 64) void dense_pass(CellArgs g) {
         }
     }
 
+    // Staging registers: the x rows of a sub-chunk (m <= 16) and, in the
+    // steady sweeps, its rows of the old iterate, loaded while the chain of
+    // the sub-chunk before it runs, so that their memory latency is hidden.
+    constexpr int kXP = kSub * 16 / 64, kPP = kSub * DP / 64;
+    const bool xpre = m <= 16;
+    float xpf[kXP], ppf[kPP];
+    auto prefetch = [&](int k) {
+        const int j0 = k * kSub;
+        const int Sc = min(kSub, Lc - j0);
+        if (xpre) {
+#pragma unroll
+            for (int u = 0; u < kXP; ++u) {
+                const int e = u * 64 + lane;
+                xpf[u] = e < Sc * m ? xg[static_cast<int64_t>(j0) * m + e] : 0.0f;
+            }
+        }
+        if constexpr (PHASE == kSteady) {
+#pragma unroll
+            for (int u = 0; u < kPP; ++u) {
+                const int e = u * 64 + lane;
+                const int r = e / DP, q = e % DP;
+                ppf[u] = (r < Sc && q < D) ? sg[static_cast<int64_t>(j0 + r) * D + q] : 0.0f;
+            }
+        }
+    };
+
     // Sub-chunk k: stage its rows, evaluate the cell at the old iterate and
     // replay (apply launches), store, then evaluate at the new iterate:
     // residual, V and the coefficients of iteration i+1 (co_set(k)).
     auto process = [&](int k) {
         const int j0 = k * kSub;
         const int Sc = min(kSub, Lc - j0);
-        copy_to_lds<64>(X, xg + static_cast<int64_t>(j0) * m, Sc * m, lane);
+        if (xpre) {
+#pragma unroll
+            for (int u = 0; u < kXP; ++u) {
+                const int e = u * 64 + lane;
+                if (e < Sc * m) X[e] = xpf[u];
+            }
+        } else {
+            copy_to_lds<64>(X, xg + static_cast<int64_t>(j0) * m, Sc * m, lane);
+        }
         if constexpr (PHASE == kPrologue || PHASE == kFirst) {
             for (int e = lane; e < Sc * DP; e += 64) {
                 const int q = e % DP;
@@ -444,7 +503,11 @@ __global__ __launch_bounds__(SPLIT ? 128 : 64) void dense_pass(CellArgs g) {
         } else if constexpr (PHASE == kMaps) {
             stage_maps_rows<64>(P + DP, DP, sg + static_cast<int64_t>(j0) * D, D, Sc, t0 + j0, ff, fillrow, lane);
         } else {
-            copy_rows_to_lds<64>(P + DP, DP, sg + static_cast<int64_t>(j0) * D, D, Sc, D, lane);
+#pragma unroll
+            for (int u = 0; u < kPP; ++u) {
+                const int e = u * 64 + lane;
+                if (e / DP < Sc) P[DP + e] = ppf[u];
+            }
         }
         wave_sync();
         // input projection U x + b_ih for every row and gate (registers)
@@ -513,11 +576,13 @@ __global__ __launch_bounds__(SPLIT ? 128 : 64) void dense_pass(CellArgs g) {
         wave_sync();
     };
 
+    prefetch(0);
     process(0);
     for (int k = 0; k < nsub; ++k) {
         if constexpr (SPLIT) __syncthreads();   // coefficients of sub-chunk k are out
         const int Sc = min(kSub, Lc - k * kSub);
         const float* COk = co_set(k);
+        if (k + 1 < nsub) prefetch(k + 1);
         for (int j = 0; j < Sc; ++j) {
             acc_t C[NG];
             if constexpr (!SPLIT) products(C);
@@ -553,7 +618,16 @@ __global__ __launch_bounds__(SPLIT ? 128 : 64) void dense_pass(CellArgs g) {
     }
     if (h == 0 && live) g.aggB[ci * D + i] = bg;
     rb = wave_max_u32(rb);
-    if (lane == 0) g.rpart[ci] = rb;
+    if (lane == 0) {
+        if (g.fc & kFcCheck) {
+            // r_{i+1} (r_0 in the prologue) for the check the next sweep takes
+            const int set = PHASE == kPrologue ? 0 : (g.iter + 1) % 3;
+            __hip_atomic_fetch_max(&g.ctrl->rmax[set][ci % kRSlots][0], rb, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            g.rpart[ci] = rb;
+        }
+    }
     if (track) {
         fb = ~wave_max_u32(~fb);
         if (lane == 0) g.fpart[ci] = fb == 0xffffffffu ? fb : t0 + fb;

@@ -143,22 +143,29 @@ __device__ __forceinline__ int check_status(uint32_t m, const CheckArgs& c) {
 }
 
 // Publish a decision to the device control word and the pinned host record
-// (payload, then epoch, then iter).  One thread.
+// (payload, then epoch, then iter).  One thread.  The record's words are
+// written with system-scope stores, which go past the compute die's caches
+// to the host memory; waiting for each group of stores to complete before
+// the next is issued orders them for the host.  No cache-wide fence: the
+// workgroups still running beside this one keep their cached data.
 __device__ __forceinline__ void publish_check(const CheckArgs& c, uint32_t m, int st, uint32_t first) {
     const int stop = st >= 0 ? 1 : 0;
     c.ctrl->stop = stop;
     c.ctrl->status = st;
     c.ctrl->iter = c.iter;
     c.ctrl->r_bits = m;
-    c.host->r_bits = m;
-    c.host->first = first;
-    c.host->status = st;
-    c.host->stop = stop;
-    __threadfence_system();
+    __hip_atomic_store(&c.host->r_bits, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(&c.host->first, first, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(&c.host->status, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(&c.host->stop, stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __hip_atomic_store(&c.host->epoch, c.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __threadfence_system();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __hip_atomic_store(&c.host->iter, c.iter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __threadfence_system();
 }
 
 // With c.advancing the check only reduces (residual max and the first step

@@ -116,7 +116,9 @@ struct CellArgs {
     uint32_t* fpart;         // advancing window: per-block first step with r_t > tol
                              // (window-relative; 0xffffffff if none), or null
     float tol;
-    // fc (diagonal modes, at most kFcMaxChunks chunks per row), bits:
+    // fc (diagonal modes with at most kFcMaxChunks chunks per row: both bits;
+    // the matrix-core Newton and banded sweeps at D padded to 16 or 32:
+    // kFcCheck alone), bits:
     // kFcCarry: no carry launch; every apply sweep composes the carry of its
     //   chunk from the chunk maps, which for iteration k are at aggA/aggB +
     //   (k & 1) * mstride (a maps pass launched with iter k writes set k & 1);
@@ -146,6 +148,9 @@ struct CarryArgs {
     int32_t B, D, NC;
     int32_t do_check;
     CheckArgs chk;
+    // launches queued ahead of the check their sweep takes: with stop_on
+    // set, a launch that finds its stop word set does nothing (null: never)
+    const Ctrl* stop_on;
 };
 
 // kPrologue: iteration-0 chunk maps at s^(0) = s0 (implicit);  kFirst /
