@@ -194,12 +194,21 @@ enum { PN_WINDOW_CONSECUTIVE = 0, PN_WINDOW_ADVANCING = 1 };
  * the faster one for the shapes measured here. */
 enum { PN_FLAG_PERSISTENT = 1 };
 
-/* pn_opts.flags.  A solve of a matrix cell with D <= 8 whose windows hold at
- * most 1024 (D <= 4) or 512 (D <= 8) (b, t) pairs runs by default in one
- * launch of a single workgroup, every window, iteration and check included
- * (float storage, consecutive windows, no switching, chunk 0, max_iter <=
- * 16384).  PN_FLAG_MULTI_LAUNCH keeps such a solve on the launch-per-phase
- * driver instead. */
+/* pn_opts.flags.  By default the library runs some solves in one launch:
+ *  - a matrix cell with D <= 8 whose windows hold at most 1024 (D <= 4) or
+ *    512 (D <= 8) (b, t) pairs, in one workgroup, every window, iteration
+ *    and check included (float storage, consecutive windows, no switching,
+ *    chunk 0, max_iter <= 16384);
+ *  - a matrix cell in a diagonal mode (Jacobi, Picard, quasi-Newton) with D
+ *    padded to 16, 32 or 64, float storage and no switching, as one
+ *    cooperative launch of workgroups that each keep a chunk on chip, when
+ *    all chunks fit on the device at once: consecutive windows of at most
+ *    128 chunks (max_iter <= 16384), or the advancing window, whose
+ *    acceptance decisions and window moves are then taken on the device
+ *    (max_iter below ceil(T / W) * (W + 1) and below 65536, the capacity of
+ *    its residual history).
+ * PN_FLAG_MULTI_LAUNCH keeps such a solve on the launch-per-phase driver
+ * instead.  Results meet the same bar either way. */
 enum { PN_FLAG_MULTI_LAUNCH = 2 };
 
 /* Fill *o with the defaults: damping 1, chunk 0, window 0, bandwidth 1,
