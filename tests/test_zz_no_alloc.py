@@ -10,7 +10,7 @@ import torch
 
 import workloads
 import newton_evaluation_nonlinear_amd as pn
-from _parity import check_parity, run_gpu, run_oracle, to_dev
+from _parity import advancing, check_parity, check_parity_advancing, run_gpu, run_oracle, to_dev
 
 J, P, Q, N = pn.JACOBI, pn.PICARD, pn.QUASI_NEWTON, pn.NEWTON
 
@@ -18,7 +18,8 @@ J, P, Q, N = pn.JACOBI, pn.PICARD, pn.QUASI_NEWTON, pn.NEWTON
 def _run_noalloc(wl, mode):
     params, x, s0 = to_dev(wl)
     res = pn.eval(wl["cell"], params, x, s0, mode=mode, tol=wl["tol"], max_iter=wl["max_iter"],
-                  damping=wl["damping"], window=wl["window"], history=True, noalloc=True)
+                  damping=wl["damping"], window=wl["window"], history=True, noalloc=True,
+                  window_mode=pn.WINDOW_ADVANCING if advancing(wl) else pn.WINDOW_CONSECUTIVE)
     torch.cuda.synchronize()
     res.out_np = res.out.cpu().numpy()
     return res
@@ -45,6 +46,22 @@ def test_noalloc_matches_pn_eval_ex_on_two_calls_in_a_row(first, second, mode):
         assert a.resid_hist == b.resid_hist
         np.testing.assert_array_equal(a.out_np, b.out_np)
         check_parity(wl, mode, a, run_oracle(wl, mode), label=f"noalloc cfg{cfg}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mode", [P, N])
+def test_noalloc_advancing_window_on_two_calls_in_a_row(mode):
+    # the advancing window: one resident launch (Picard; its records come back
+    # from the static scratch after the launch) or a launch per round (Newton)
+    for B, T in ((4, 1500), (2, 600)):
+        wl = workloads.make(7, B=B, T=T)
+        print(f"[noalloc] cfg7 B={B} T={T} mode={mode}", flush=True)
+        a = _run_noalloc(wl, mode)
+        b = run_gpu(wl, mode)
+        assert a.status == b.status and a.iters == b.iters and a.accepted == b.accepted
+        assert a.resid_hist == b.resid_hist
+        np.testing.assert_array_equal(a.out_np, b.out_np)
+        check_parity_advancing(wl, mode, a, run_oracle(wl, mode), label=f"noalloc cfg7 B={B}")
 
 
 @pytest.mark.gpu
