@@ -1991,7 +1991,6 @@ __global__ __launch_bounds__(kThreads, 1) void cell_resident_adv(ResidentArgs a)
     float* X = CO + L * DP;                      // [L][xs]
     float* SCR = X + L * xs;                     // [2][kThreads] fold segments
     float* S0 = SCR + 2 * kThreads;              // [DP] accepted state s_{A-1}
-    float* FILL = S0 + DP;                       // [DP] start value of steps entering the window
     float* outb = a.out + static_cast<int64_t>(b) * T * D;
     const float* s0b = a.s0 + static_cast<int64_t>(b) * D;
     CellRegs<CELL, DP> cr;
@@ -2005,23 +2004,32 @@ __global__ __launch_bounds__(kThreads, 1) void cell_resident_adv(ResidentArgs a)
     auto stage = [&](int64_t A, int64_t E, int64_t Ev) -> int {
         const int64_t t0 = A + static_cast<int64_t>(c) * L;
         const int Lc = t0 < E ? static_cast<int>(E - t0 < L ? E - t0 : L) : 0;
-        if (tid < DP) {
-            float sv = 0.0f, fv = 0.0f;
-            if (tid < D) {
-                sv = A == 0 ? s0b[tid] : ld_dev(outb + (A - 1) * D + tid);
-                fv = Ev == 0 ? s0b[tid] : ld_dev(outb + (Ev - 1) * D + tid);
-            }
-            S0[tid] = sv;
-            FILL[tid] = fv;
-        }
+        if (tid < DP) S0[tid] = tid < D ? (A == 0 ? s0b[tid] : ld_dev(outb + (A - 1) * D + tid)) : 0.0f;
         if (Lc > 0) copy_rows_to_lds<kThreads>(X, xs, a.x + (static_cast<int64_t>(b) * T + t0) * m, m, Lc, m);
-        __syncthreads();
-        for (int e = tid; e < (Lc + 1) * PS; e += kThreads) {
-            const int r = e / PS, i = e - r * PS;
-            const int64_t t = t0 - 1 + r;
-            float v = 0.0f;
-            if (i < D) v = t < 0 ? s0b[i] : (t < Ev ? ld_dev(outb + t * D + i) : FILL[i]);
-            S[e] = v;
+        // every element one load from its own source (kStageKB loads in
+        // flight per thread before their LDS stores): row t of out below Ev,
+        // the fill row Ev - 1 (s0 if Ev = 0) from Ev on, s0 before step 0
+        constexpr int kStageKB = 8;
+        const int n = (Lc + 1) * PS;
+        for (int base = 0; base < n; base += kThreads * kStageKB) {
+            float v[kStageKB];
+#pragma unroll
+            for (int u = 0; u < kStageKB; ++u) {
+                const int e = base + u * kThreads + tid;
+                const int r = e / PS, i = e - r * PS;
+                const int64_t t = t0 - 1 + r;
+                const bool live = e < n && i < D;
+                const int ic = live ? i : 0;
+                const int64_t tr = t < Ev ? t : Ev - 1;   // the row it reads
+                const float* src = (tr < 0 || !live) ? s0b + ic : outb + tr * D + ic;
+                const float x = ld_dev(src);
+                v[u] = live ? x : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < kStageKB; ++u) {
+                const int e = base + u * kThreads + tid;
+                if (e < n) S[e] = v[u];
+            }
         }
         __syncthreads();
         return Lc;
@@ -2212,7 +2220,7 @@ __global__ __launch_bounds__(kThreads, 1) void cell_resident_adv(ResidentArgs a)
 
 size_t resident_adv_lds_bytes(int DP, int L, int m) {
     const size_t PS = DP + 4, xs = x_stride(m);
-    const size_t n = (L + 1) * PS + 2ull * L * DP + static_cast<size_t>(L) * xs + 2ull * kThreads + 2ull * DP;
+    const size_t n = (L + 1) * PS + 2ull * L * DP + static_cast<size_t>(L) * xs + 2ull * kThreads + DP;
     return sizeof(float) * n;
 }
 
