@@ -1205,9 +1205,11 @@ int solve_advancing_resident(SolveCtx& c, const float* x, const float* s0, float
     a.hist_cap = p.hist_cap;
     a.acc = reinterpret_cast<int32_t*>(inf.dev + (p.off_acc - p.off_sync));
     a.acc_cap = p.hist_cap;
-    // residual and first-step slots, arrival words and error flag start at zero
+    a.ready = reinterpret_cast<unsigned*>(ws + p.off_halo);   // the halo region, unused here
+    // residual and first-step slots, arrival words, ready words and error flag start at zero
     PN_HIP(hipMemsetAsync(ctrl, 0, sizeof(Ctrl), c.st));
     PN_HIP(hipMemsetAsync(a.bar, 0, sizeof(unsigned) * p.B * NC, c.st));
+    PN_HIP(hipMemsetAsync(a.ready, 0, sizeof(unsigned) * p.B * NC, c.st));
     const bool timed = c.tm->take();
     size_t e0 = 0, e1 = 0;
     if (timed) { rc = request_timing(c, &e0, &e1); if (rc) return rc; }

@@ -1967,10 +1967,11 @@ __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(Resid
 //           window moved, every workgroup stages its chunk of the new window
 //           from the iterate in `out` (steps from the old E on start from the
 //           old window's last state) and evaluates the cell there;
-//   update: the chunk map, a grid barrier, the carry folded from the maps of
-//           the chunks before it applied to the accepted state s_{A-1}, the
-//           replay with damping, and the evaluation at the new iterate,
-//           which is the next check; the chunk's rows go back to `out`.
+//   update: the chunk map, a wait for the maps of the chunks before it in
+//           its row, the carry folded from those maps applied to the
+//           accepted state s_{A-1}, the replay with damping, and the
+//           evaluation at the new iterate, which is the next check; the
+//           chunk's rows go back to `out`; a grid barrier ends the round.
 // Rows travel between workgroups only through `out`, with device-scope
 // loads and stores; the window never needs the host.
 template <int CELL, int DP>
@@ -1998,6 +1999,7 @@ __global__ __launch_bounds__(kThreads, 1) void cell_resident_adv(ResidentArgs a)
     unsigned epoch = 0;
     const bool rthr = tid < D;                   // replay / composition thread of channel tid
     float own_a = 1.0f, own_b = 0.0f;
+    __shared__ int row_ok;
 
     // the chunk of window [A, E) with the iterate's rows below Ev read from
     // out and the rest set to the fill value; returns the chunk's rows
@@ -2126,7 +2128,39 @@ __global__ __launch_bounds__(kThreads, 1) void cell_resident_adv(ResidentArgs a)
             st_dev(mA + static_cast<size_t>(c) * D + tid, Am);
             st_dev(mB + static_cast<size_t>(c) * D + tid, Bm);
         }
-        if (!resident_sync(a, epoch, nblocks)) return;
+        // The fold needs the maps of the chunks before this one in its row
+        // only: once its own map stores have completed, the chunk stores the
+        // update's tag (i + 1) into its ready word, and waits (bounded) for
+        // the ready words of its row's earlier chunks instead of a grid
+        // barrier.
+        {
+            const unsigned tag = static_cast<unsigned>(i + 1);
+            unsigned* rdy = a.ready + static_cast<size_t>(b) * a.NC;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0 && Lc > 0) __hip_atomic_store(rdy + c, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid < 64) {
+                int good = 1;
+                if (Lc > 0 && c > 0) {
+                    unsigned spins = 0;
+                    for (;;) {
+                        int done = 1;
+                        for (int k = tid; k < c; k += 64)
+                            done &= __hip_atomic_load(rdy + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= tag;
+                        if (__all(done)) break;
+                        __builtin_amdgcn_s_sleep(1);
+                        if (++spins > (1u << 22) || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                            if (tid == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            good = 0;
+                            break;
+                        }
+                    }
+                }
+                if (tid == 0) row_ok = good;
+            }
+            __syncthreads();
+            if (!row_ok) return;
+        }
         if (Lc > 0) {
             // the carry of chunk c: NS segments of the maps of the chunks before it
             {

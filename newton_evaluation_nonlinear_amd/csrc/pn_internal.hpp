@@ -271,6 +271,7 @@ struct ResidentArgs {
     int32_t hist_cap;
     int32_t* acc;            // advancing window: steps accepted at each check
     int32_t acc_cap;
+    unsigned* ready;         // advancing window: [B * NC] chunk-map ready words (zero at launch)
 };
 
 // cpw: chunks per workgroup (1, or 4 at D padded to 16); the grid is
