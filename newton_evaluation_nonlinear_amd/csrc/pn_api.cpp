@@ -90,6 +90,7 @@ struct Plan {
     size_t off_ctrl, off_rpart, off_fpart, off_aggA, off_aggB, off_carry, off_carry0, off_halo, off_w,
         total;
     size_t off_sync, off_winfo, off_hist, off_acc, off_info_end;
+    size_t off_lag;        // resident solver: residual words, ready words, window-state words
 };
 
 void layout(Plan& p, const Plan* other);
@@ -238,15 +239,23 @@ void layout(Plan& p, const Plan* other) {
     p.off_rpart = off; off = align_up(off + sizeof(uint32_t) * nparts);
     p.off_fpart = off; off = align_up(off + sizeof(uint32_t) * nparts);
     // chunk maps: two sets (iterations of either parity) for fc sweeps
-    const size_t nsets = ((p.fc & kFcCarry) || p.adv_resident_ok || (other && (other->fc & kFcCarry))) ? 2 : 1;
+    // chunk maps: three sets for the resident solver (by publication), two
+    // (by iteration parity) for sweeps that compose their own carries
+    const size_t nsets = p.resident_ok ? 3
+                         : ((p.fc & kFcCarry) || p.adv_resident_ok || (other && (other->fc & kFcCarry))) ? 2 : 1;
     p.off_aggA = off; off = align_up(off + sizeof(float) * nA * nsets);
     p.off_aggB = off; off = align_up(off + sizeof(float) * bnd * nsets);
     p.off_carry = off; off = align_up(off + sizeof(float) * bnd);
     p.off_carry0 = off;
     if (p.recompute || (other && other->recompute)) off = align_up(off + sizeof(float) * bnd);
-    p.off_halo = off; off = align_up(off + sizeof(float) * 2 * bnd);
+    p.off_halo = off; off = align_up(off + sizeof(float) * (p.resident_ok ? 3 : 2) * bnd);
     p.off_w = off;
     if (p.matrix_cell) off = align_up(off + sizeof(float) * prepared_total_floats(p.kind, p.DP, p.m));
+    p.off_lag = off;
+    if (p.resident_ok) {
+        const size_t chunks = static_cast<size_t>(p.B) * p.NC;
+        off = align_up(off + sizeof(unsigned long long) * 4 * chunks + sizeof(unsigned) * (chunks + p.B));
+    }
     p.off_sync = p.off_winfo = p.off_hist = p.off_acc = off;
     if (p.persist_ok || p.small || p.resident_ok || p.adv_resident_ok) {
         p.off_sync = off; off = align_up(off + 256);
@@ -1127,17 +1136,20 @@ int solve_resident(SolveCtx& c, const float* x, const float* s0, float* out, int
     a.halo = reinterpret_cast<float*>(ws + p.off_halo);
     a.s0n = reinterpret_cast<float*>(ws + p.off_carry);
     Ctrl* ctrl = reinterpret_cast<Ctrl*>(ws + p.off_ctrl);
-    a.rslot = &ctrl->rmax[0][0][0];
-    a.bar = reinterpret_cast<unsigned*>(ws + p.off_rpart);   // one arrival word per workgroup
     a.err = &ctrl->bar_err;
+    const size_t chunks = static_cast<size_t>(p.B) * p.NC;
+    a.rword = reinterpret_cast<unsigned long long*>(ws + p.off_lag);
+    a.ready = reinterpret_cast<unsigned*>(a.rword + 4 * chunks);
+    a.s0ready = a.ready + chunks;
     a.hist_len = reinterpret_cast<int32_t*>(inf.dev);
     a.win_iters = reinterpret_cast<int32_t*>(inf.dev + (p.off_winfo - p.off_sync));
     a.win_status = a.win_iters + p.nwin;
     a.hist = reinterpret_cast<float*>(inf.dev + (p.off_hist - p.off_sync));
     a.hist_cap = p.hist_cap;
-    // residual slots, arrival words and error flag start at zero
+    // error flag, residual words, ready words and window-state words start at zero
     PN_HIP(hipMemsetAsync(ctrl, 0, sizeof(Ctrl), c.st));
-    PN_HIP(hipMemsetAsync(a.bar, 0, sizeof(unsigned) * p.B * ((p.NC + cpw - 1) / cpw), c.st));
+    PN_HIP(hipMemsetAsync(a.rword, 0, sizeof(unsigned long long) * 4 * chunks + sizeof(unsigned) * (chunks + p.B),
+                          c.st));
     const bool timed = c.tm->take();
     size_t e0 = 0, e1 = 0;
     if (timed) { rc = request_timing(c, &e0, &e1); if (rc) return rc; }

@@ -1678,8 +1678,25 @@ __device__ __forceinline__ bool resident_sync(const ResidentArgs& a, unsigned& e
 // 2048 chunks over 512 workgroups).  Each chunk keeps its own LDS region; the
 // fold, the replay and the map composition of the CPW chunks run side by
 // side on disjoint thread groups, the evaluations one chunk after another.
-// The replay works in place on the chunk's rows: the old row is read before
-// the new one is written over it.
+//
+// No grid barrier per iteration.  A chunk's fold needs the maps (and the
+// halo) of the chunks before it in its batch row only: after its own map
+// stores have completed, each chunk stores the publication's tag into its
+// ready word, and a workgroup waits for the ready words of its row's earlier
+// chunks.  The stop decision needs every workgroup's residual, so it is taken
+// one iteration late: iteration i replays s^(i+1) into the chunk's second row
+// buffer and publishes its maps and r_{i+1} before it reads r_i, by then
+// (almost always) complete, from one (tag, residual) word per workgroup.
+// Each iteration first stores its rows of s^(i) to out (the last chunk of a
+// row also its last row to s0n), so a stop at i finds the result in place;
+// the work on s^(i+1) is dropped.
+// Tags count publications alike in every workgroup (the decisions are
+// alike), maps and halo rotate over three sets and the residual words over
+// four, which no workgroup can overrun: to publish tag t + 3 a workgroup has
+// seen every workgroup publish tag t + 1 (and t + 2 for the words), which
+// each does only after its fold of tag t.  At a window's end every
+// workgroup also waits for the iteration past the stop, before the next
+// window reuses the sets.
 template <int CELL, int DP, int CPW>
 __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(ResidentArgs a) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -1691,23 +1708,90 @@ __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(Resid
     const int xs = x_stride(m);
     const int bx = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int GX = gridDim.x;
-    const unsigned nblocks = gridDim.x * gridDim.y;
+    const int nblocks = gridDim.x * gridDim.y;
+    const int blk = b * GX + bx;
+    const bool lead = bx == 0 && b == 0;
     const int per_chunk = (L + 1) * PS + 2 * L * DP + L * xs;
     float* SCR = lds + CPW * per_chunk;          // [2][kThreads] fold segments
     float* S0 = SCR + 2 * kThreads;              // [DP] initial state of the window
     auto Sk = [&](int k) { return lds + k * per_chunk; };                 // [L+1][PS] rows t0-1 .. t1-1
     auto Vk = [&](int k) { return lds + k * per_chunk + (L + 1) * PS; };  // [L][DP]
-    auto COk = [&](int k) { return Vk(k) + L * DP; };                       // [L][DP]
-    auto Xk = [&](int k) { return COk(k) + L * DP; };                       // [L][xs]
+    auto COk = [&](int k) { return Vk(k) + L * DP; };                   // [L][DP]
+    auto Xk = [&](int k) { return COk(k) + L * DP; };                   // [L][xs]
+    __shared__ uint32_t chk_r;
+    __shared__ int sync_ok;
     CellRegs<CELL, DP> cr;
     cr.load(a.w, a.w, D, m);
-    const size_t HS = static_cast<size_t>(B) * a.NC * D;   // parity stride of maps and halo
-    unsigned epoch = 0;
-    int hist_pos = 0, q = 0;
+    const size_t HS = static_cast<size_t>(B) * a.NC * D;   // set stride of maps and halo
+    unsigned* rdy = a.ready + static_cast<size_t>(b) * a.NC;
+    unsigned tag = 0;                            // publications so far
+    int hist_pos = 0;
     // the thread's (chunk, channel) in the replay and the composition
     const int rk = tid / DP, ri = tid % DP;
     const bool rthr = rk < CPW && ri < D;
     float own_a = 1.0f, own_b = 0.0f;            // map of chunk (rk) of the current iteration, channel ri
+
+    // Bounded waits of wavefront 0; on a timeout (or another workgroup's) the
+    // error flag is set and the caller leaves.
+    auto spin_fail = [&](unsigned& spins) -> bool {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > (1u << 22) || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            if (tid == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return true;
+        }
+        return false;
+    };
+    // every workgroup's word of set t % 4 carries tag t: their residual maximum to chk_r
+    auto wait_all = [&](unsigned t) -> bool {
+        if (tid < 64) {
+            const unsigned long long* w = a.rword + static_cast<size_t>(t % 4) * nblocks;
+            unsigned spins = 0;
+            int good = 1;
+            uint32_t mx = 0;
+            for (;;) {
+                int done = 1;
+                mx = 0;
+                for (int k = tid; k < nblocks; k += 64) {
+                    const unsigned long long v = __hip_atomic_load(w + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    done &= static_cast<unsigned>(v >> 32) == t;
+                    mx = max(mx, static_cast<uint32_t>(v));
+                }
+                if (__all(done)) break;
+                if (spin_fail(spins)) {
+                    good = 0;
+                    break;
+                }
+            }
+            mx = wave_max_u32(mx);
+            if (tid == 0) {
+                chk_r = mx;
+                sync_ok = good;
+            }
+        }
+        __syncthreads();
+        return sync_ok != 0;
+    };
+    // the ready words of chunks [0, upto) of the row hold at least t
+    auto wait_row = [&](unsigned t, int upto) -> bool {
+        if (tid < 64) {
+            int good = 1;
+            unsigned spins = 0;
+            for (;;) {
+                int done = 1;
+                for (int k = tid; k < upto; k += 64)
+                    done &= __hip_atomic_load(rdy + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= t;
+                if (__all(done)) break;
+                if (spin_fail(spins)) {
+                    good = 0;
+                    break;
+                }
+            }
+            if (tid == 0) sync_ok = good;
+        }
+        __syncthreads();
+        return sync_ok != 0;
+    };
+
     for (int wi = 0; wi < a.nwin; ++wi) {
         const int64_t w0 = static_cast<int64_t>(wi) * a.W;
         const int Tw = static_cast<int>(a.T - w0 < a.W ? a.T - w0 : a.W);
@@ -1715,6 +1799,27 @@ __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(Resid
         auto chunk = [&](int k) { return bx + k * GX; };
         auto active = [&](int k) { return chunk(k) < NCw; };
         auto rows = [&](int k) { return active(k) ? min(L, Tw - chunk(k) * L) : 0; };
+        int upto = 0;                            // the fold waits for chunks [0, upto) of the row
+#pragma unroll
+        for (int k = 0; k < CPW; ++k)
+            if (active(k)) upto = chunk(k);
+        // the window's initial state: s0, or the last state of the row's previous window
+        if (wi > 0) {
+            if (tid < 64) {
+                int good = 1;
+                unsigned spins = 0;
+                while (!__all(__hip_atomic_load(a.s0ready + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+                              static_cast<unsigned>(wi))) {
+                    if (spin_fail(spins)) {
+                        good = 0;
+                        break;
+                    }
+                }
+                if (tid == 0) sync_ok = good;
+            }
+            __syncthreads();
+            if (!sync_ok) return;
+        }
         if (tid < DP)
             S0[tid] = tid < D ? (wi == 0 ? a.s0[static_cast<int64_t>(b) * D + tid] : ld_dev(a.s0n + b * D + tid)) : 0.0f;
         uint32_t rb = 0;
@@ -1743,58 +1848,69 @@ __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(Resid
             cr.template eval<false>(Sk(k), Vk(k), COk(k), rows(k), L, a.mode, Sk(k), rb, nullptr, a.tol);
         }
         __syncthreads();
-        if (rthr && active(rk)) {
-            const int Lc = rows(rk);
-            const float* V = Vk(rk);
-            const float* CO = COk(rk);
-            const float* S = Sk(rk);
-            float A = 1.0f, Bc = 0.0f;
-            if (a.mode == kJacobi) {
-                A = 0.0f;
-                Bc = V[(Lc - 1) * DP + ri];
-            } else {
-                for (int j = 0; j < Lc; ++j) {
-                    const float at = CO[j * DP + ri];
-                    Bc = at * Bc + (V[j * DP + ri] - at * S[j * PS + ri]);
-                    A = at * A;
+        // the chunk map of the iterate in the chunk's rows, composed and
+        // published with its last row (the next chunk's halo) under tag t
+        auto compose_publish = [&](unsigned t) {
+            if (rthr && active(rk)) {
+                const int Lc = rows(rk);
+                const float* V = Vk(rk);
+                const float* CO = COk(rk);
+                const float* S = Sk(rk);
+                float A = 1.0f, Bc = 0.0f;
+                if (a.mode == kJacobi) {
+                    A = 0.0f;
+                    Bc = V[(Lc - 1) * DP + ri];
+                } else {
+#pragma unroll 8
+                    for (int j = 0; j < Lc; ++j) {
+                        const float at = CO[j * DP + ri];
+                        Bc = at * Bc + (V[j * DP + ri] - at * S[j * PS + ri]);
+                        A = at * A;
+                    }
                 }
+                own_a = A;
+                own_b = Bc;
+                const size_t o = (t % 3) * HS + (static_cast<size_t>(b) * a.NC + chunk(rk)) * D + ri;
+                st_dev(a.mapA + o, A);
+                st_dev(a.mapB + o, Bc);
+                st_dev(a.halo + o, S[Lc * PS + ri]);
             }
-            own_a = A;
-            own_b = Bc;
-            const size_t ci = static_cast<size_t>(b) * a.NC + chunk(rk);
-            st_dev(a.mapA + ci * D + ri, A);
-            st_dev(a.mapB + ci * D + ri, Bc);
-        }
+        };
+        // once every memory operation of the workgroup has completed: the
+        // ready words of its chunks and its (tag, residual) word
+        auto post = [&](unsigned t, uint32_t rbv) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid < CPW && active(tid))
+                __hip_atomic_store(rdy + chunk(tid), t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid == 0)
+                __hip_atomic_store(a.rword + static_cast<size_t>(t % 4) * nblocks + blk,
+                                   (static_cast<unsigned long long>(t) << 32) | rbv, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        };
+        ++tag;
+        compose_publish(tag);
         rb = block_max_u32(rb);
-        if (tid == 0 && active(0))
-            __hip_atomic_fetch_max(a.rslot + ((q % 3) * kRSlots + (b * GX + bx) % kRSlots) * 64, rb,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (!resident_sync(a, epoch, nblocks)) return;
+        post(tag, rb);
         int K = 0, status = kStOk;
-        for (int i = 0;; ++i, ++q) {
-            // the check of iteration i, taken alike by every workgroup
-            const int lane = tid & 63;
-            uint32_t rv = lane < kRSlots ? __hip_atomic_load(a.rslot + ((q % 3) * kRSlots + lane) * 64,
-                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-            const uint32_t r_i = wave_max_u32(rv);
-            int st = -1;
-            if (r_i >= kNonFiniteBits) st = kStNonFinite;
-            else if (__uint_as_float(r_i) <= a.tol) st = kStOk;
-            else if (i >= a.max_iter) st = kStNotConverged;
-            if (bx == 0 && b == 0) {
-                if (tid == 0 && hist_pos < a.hist_cap) a.hist[hist_pos] = __uint_as_float(r_i);
-                if (tid < kRSlots)
-                    __hip_atomic_store(a.rslot + (((q + 2) % 3) * kRSlots + tid) * 64, 0u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = 0;; ++i) {
+            const unsigned tg = tag;             // tag of iteration i's maps and of r_i
+            const int sel = static_cast<int>(tg % 3);
+            // s^(i), the result should the check of iteration i stop: the
+            // chunks' rows to out, the row's last state to s0n
+#pragma unroll
+            for (int k = 0; k < CPW; ++k) {
+                if (!active(k)) continue;
+                const int c = chunk(k), Lc = rows(k);
+                const float* S = Sk(k);
+                float* o = a.out + (static_cast<int64_t>(b) * a.T + w0 + c * L) * D;
+                for (int e = tid; e < Lc * D; e += kThreads) {
+                    const int j = e / D, ii = e % D;
+                    o[e] = S[(j + 1) * PS + ii];
+                }
+                if (c + 1 == NCw && tid < D) st_dev(a.s0n + b * D + tid, S[Lc * PS + tid]);
             }
-            ++hist_pos;
-            if (st >= 0) {
-                K = i;
-                status = st;
-                ++q;
-                break;
-            }
-            const int par = i & 1;
+            if (!wait_row(tg, upto)) return;
             // the carries: per chunk, NS segments of the maps of the chunks
             // before it, each folded into one map, applied to s0 after the barrier
             {
@@ -1805,8 +1921,8 @@ __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(Resid
                 const int per = (cc + NS - 1) / NS;
                 const int k0 = min(cc, sg_ * per);
                 const int k1 = d < D ? min(cc, k0 + per) : k0;
-                const float* mA = a.mapA + par * HS + static_cast<size_t>(b) * a.NC * D;
-                const float* mB = a.mapB + par * HS + static_cast<size_t>(b) * a.NC * D;
+                const float* mA = a.mapA + sel * HS + static_cast<size_t>(b) * a.NC * D;
+                const float* mB = a.mapB + sel * HS + static_cast<size_t>(b) * a.NC * D;
                 constexpr int kRF = (kFcMaxChunks + NS - 1) / NS < 16 ? (kFcMaxChunks + NS - 1) / NS : 16;
                 float pa[kRF], pb[kRF];
 #pragma unroll
@@ -1835,7 +1951,7 @@ __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(Resid
             if (rthr && active(rk)) {
                 const int c = chunk(rk);
                 hrow = (c == 0 || i == 0) ? S0[ri]
-                                          : ld_dev(a.halo + par * HS + (static_cast<size_t>(b) * a.NC + c - 1) * D + ri);
+                                          : ld_dev(a.halo + sel * HS + (static_cast<size_t>(b) * a.NC + c - 1) * D + ri);
             }
             __syncthreads();
             // replay from the carry, damping, in place: rows t0-1 .. t1-1 of s^(i+1)
@@ -1902,57 +2018,44 @@ __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(Resid
                 cr.template eval<false>(Sk(k), Vk(k), COk(k), rows(k), L, a.mode, Sk(k), rbn, nullptr, a.tol);
             }
             __syncthreads();
-            if (rthr && active(rk)) {
-                const int Lc = rows(rk);
-                const float* V = Vk(rk);
-                const float* CO = COk(rk);
-                const float* S = Sk(rk);
-                float A = 1.0f, Bc = 0.0f;
-                if (a.mode == kJacobi) {
-                    A = 0.0f;
-                    Bc = V[(Lc - 1) * DP + ri];
-                } else {
-#pragma unroll 8
-                    for (int j = 0; j < Lc; ++j) {
-                        const float at = CO[j * DP + ri];
-                        Bc = at * Bc + (V[j * DP + ri] - at * S[j * PS + ri]);
-                        A = at * A;
-                    }
-                }
-                own_a = A;
-                own_b = Bc;
-                const size_t ci = static_cast<size_t>(b) * a.NC + chunk(rk);
-                st_dev(a.mapA + (par ^ 1) * HS + ci * D + ri, A);
-                st_dev(a.mapB + (par ^ 1) * HS + ci * D + ri, Bc);
-                st_dev(a.halo + (par ^ 1) * HS + ci * D + ri, S[Lc * PS + ri]);
-            }
+            ++tag;
+            compose_publish(tag);
             rbn = block_max_u32(rbn);
-            if (tid == 0 && active(0))
-                __hip_atomic_fetch_max(a.rslot + (((q + 1) % 3) * kRSlots + (b * GX + bx) % kRSlots) * 64, rbn,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (!resident_sync(a, epoch, nblocks)) return;
-        }
-        // the window's result: the chunks' rows of the last iterate, and the
-        // next window's initial state from the row's last chunk
-#pragma unroll
-        for (int k = 0; k < CPW; ++k) {
-            if (!active(k)) continue;
-            const int c = chunk(k), Lc = rows(k);
-            const float* S = Sk(k);
-            float* o = a.out + (static_cast<int64_t>(b) * a.T + w0 + c * L) * D;
-            for (int e = tid; e < Lc * D; e += kThreads) {
-                const int j = e / D, ii = e % D;
-                o[e] = S[(j + 1) * PS + ii];
+            post(tag, rbn);
+            // the check of iteration i (its residual words are in by now, as a rule)
+            if (!wait_all(tg)) return;
+            const uint32_t r_i = chk_r;
+            int st = -1;
+            if (r_i >= kNonFiniteBits) st = kStNonFinite;
+            else if (__uint_as_float(r_i) <= a.tol) st = kStOk;
+            else if (i >= a.max_iter) st = kStNotConverged;
+            if (lead && tid == 0 && hist_pos < a.hist_cap) a.hist[hist_pos] = __uint_as_float(r_i);
+            ++hist_pos;
+            if (st >= 0) {
+                K = i;
+                status = st;
+                break;
             }
-            if (c + 1 == NCw && tid < D) st_dev(a.s0n + b * D + tid, S[Lc * PS + tid]);
         }
-        if (bx == 0 && b == 0 && tid == 0) {
+        // every workgroup past the iteration after the stop before the sets
+        // are reused; out and s0n hold s^(K) since the start of iteration K
+        if (!wait_all(tag)) return;
+        bool last = false;
+#pragma unroll
+        for (int k = 0; k < CPW; ++k)
+            if (active(k) && chunk(k) + 1 == NCw) last = true;
+        if (lead && tid == 0) {
             a.win_iters[wi] = K;
             a.win_status[wi] = status;
             *a.hist_len = hist_pos;
         }
         if (status == kStNonFinite) break;
-        if (!resident_sync(a, epoch, nblocks)) return;
+        if (last) {
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        __syncthreads();
+        if (last && tid == 0)
+            __hip_atomic_store(a.s0ready + b, static_cast<unsigned>(wi + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -257,9 +257,9 @@ struct ResidentArgs {
     int64_t T;
     int32_t W, nwin, B, D, m, L, NC, mode, undamped, max_iter;
     float lam, tol;
-    float* mapA;             // [2][B][NC][D] chunk maps by iteration parity
-    float* mapB;
-    float* halo;             // [2][B][NC][D] last row of every chunk, by parity
+    float* mapA;             // [3][B][NC][D] chunk maps by publication (the
+    float* mapB;             //   advancing window: [2][B][NC][D] by parity)
+    float* halo;             // [3][B][NC][D] last row of every chunk, alike
     float* s0n;              // [B][D] initial state of the next window
     uint32_t* rslot;         // [3][kRSlots][64] residual maxima, one 256-byte line per slot
     unsigned* bar;           // [B * NC] grid barrier arrival words (zero at launch)
@@ -271,7 +271,9 @@ struct ResidentArgs {
     int32_t hist_cap;
     int32_t* acc;            // advancing window: steps accepted at each check
     int32_t acc_cap;
-    unsigned* ready;         // advancing window: [B * NC] chunk-map ready words (zero at launch)
+    unsigned* ready;         // [B * NC] chunk-map ready words (zero at launch)
+    unsigned long long* rword;  // consecutive windows: [4][workgroups] (tag << 32 | residual bits)
+    unsigned* s0ready;       // consecutive windows: [B] windows whose final state is in s0n
 };
 
 // cpw: chunks per workgroup (1, or 4 at D padded to 16); the grid is
