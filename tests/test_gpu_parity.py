@@ -713,6 +713,16 @@ def test_resident_solver_matches_oracle(kind, D, m, window):
     for mode in (Q, J):
         _parity(wl, mode)
         _parity(wl, mode, flags=pn.FLAG_MULTI_LAUNCH)
+        if window:
+            # 3 x 44 chunks fit on the device at once at every width here (the
+            # whole horizon's 3 x 94 do not at D padded to 32 or 64)
+            _assert_one_launch(wl, mode)
+
+
+def _assert_one_launch(wl, mode, **kw):
+    # the solve ran as one launch (no silent fall back to the launch-per-iteration driver)
+    g = run_gpu(wl, mode, profile=True, **kw)
+    assert g.profile["apply_launches"] == 1, g.profile
 
 
 @pytest.mark.parametrize("kind, window", [(pn.CELL_GRU, 0), (pn.CELL_TANH_RNN, 300), (pn.CELL_EULER_TANH, 0)])
@@ -728,6 +738,15 @@ def test_resident_solver_four_chunks_per_workgroup(kind, window):
               s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32))
     for mode in (Q, J):
         _parity(wl, mode)
+        _assert_one_launch(wl, mode)
+
+
+@pytest.mark.parametrize("cfg, mode, B, T", [(2, Q, None, None), (2, J, None, None), (5, Q, 4, 4096),
+                                             (7, P, 16, 2048), (7, Q, 16, 2048)])
+def test_workloads_run_as_one_launch(cfg, mode, B, T):
+    # the diagonal modes of workloads 2, 5 and 7 at their shapes: all chunks fit
+    # on the device at once, so each solve is one resident launch
+    _assert_one_launch(_case(cfg, B=B, T=T), mode)
 
 
 def test_resident_solver_outcomes():
