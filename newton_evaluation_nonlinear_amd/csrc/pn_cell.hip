@@ -1711,11 +1711,19 @@ __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(Resid
     const int nblocks = gridDim.x * gridDim.y;
     const int blk = b * GX + bx;
     const bool lead = bx == 0 && b == 0;
-    const int per_chunk = (L + 1) * PS + 2 * L * DP + L * xs;
+    // One chunk per workgroup: two row buffers, s^(i) kept in one while the
+    // replay writes s^(i+1) into the other.  Four: one buffer, replayed in
+    // place (two would not leave two workgroups room on a compute unit), and
+    // s^(i) stored to out at the start of each iteration instead.
+    constexpr bool DB = CPW == 1;
+    const int RB = (L + 1) * PS;                 // one row buffer
+    const int per_chunk = (DB ? 2 : 1) * RB + 2 * L * DP + L * xs;
     float* SCR = lds + CPW * per_chunk;          // [2][kThreads] fold segments
     float* S0 = SCR + 2 * kThreads;              // [DP] initial state of the window
-    auto Sk = [&](int k) { return lds + k * per_chunk; };                 // [L+1][PS] rows t0-1 .. t1-1
-    auto Vk = [&](int k) { return lds + k * per_chunk + (L + 1) * PS; };  // [L][DP]
+    int cur = 0;                                 // the row buffer holding s^(i) (DB)
+    auto Sk = [&](int k) { return lds + k * per_chunk + (DB ? cur * RB : 0); };         // [L+1][PS] rows t0-1 .. t1-1
+    auto Snx = [&](int k) { return lds + k * per_chunk + (DB ? (cur ^ 1) * RB : 0); };  // where the replay writes
+    auto Vk = [&](int k) { return lds + k * per_chunk + (DB ? 2 : 1) * RB; };            // [L][DP]
     auto COk = [&](int k) { return Vk(k) + L * DP; };                   // [L][DP]
     auto Xk = [&](int k) { return COk(k) + L * DP; };                   // [L][xs]
     __shared__ uint32_t chk_r;
@@ -1897,10 +1905,10 @@ __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(Resid
             const unsigned tg = tag;             // tag of iteration i's maps and of r_i
             const int sel = static_cast<int>(tg % 3);
             // s^(i), the result should the check of iteration i stop: the
-            // chunks' rows to out, the row's last state to s0n
+            // chunks' rows to out, the row's last state to s0n (one buffer)
 #pragma unroll
             for (int k = 0; k < CPW; ++k) {
-                if (!active(k)) continue;
+                if (DB || !active(k)) continue;
                 const int c = chunk(k), Lc = rows(k);
                 const float* S = Sk(k);
                 float* o = a.out + (static_cast<int64_t>(b) * a.T + w0 + c * L) * D;
@@ -1954,7 +1962,9 @@ __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(Resid
                                           : ld_dev(a.halo + sel * HS + (static_cast<size_t>(b) * a.NC + c - 1) * D + ri);
             }
             __syncthreads();
-            // replay from the carry, damping, in place: rows t0-1 .. t1-1 of s^(i+1)
+            // replay from the carry, damping: rows t0-1 .. t1-1 of s^(i+1) from
+            // So into Sn (the same rows with one buffer: each old row is read
+            // before the new one is written over it)
             const float lam = a.lam;
             const bool und = a.undamped != 0;
             if (rthr && active(rk)) {
@@ -1967,18 +1977,19 @@ __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(Resid
                     xv = SCR[rk * TG + sgi * DP + ri] * xv + SCR[kThreads + rk * TG + sgi * DP + ri];
                 const float c_first = xv;
                 const float c_next = own_a * xv + own_b;
-                float* S = Sk(rk);
+                const float* So = Sk(rk);
+                float* Sn = Snx(rk);
                 const float* V = Vk(rk);
                 const float* CO = COk(rk);
-                float pold = hrow;                   // old value of the row being replaced
+                float pold = hrow;                   // old value of the row before the current one
                 float shat = c_first;
-                S[ri] = und ? shat : pold + lam * (shat - pold);
+                Sn[ri] = und ? shat : pold + lam * (shat - pold);
                 const int nrep = has_next ? Lc - 1 : Lc;
                 if (a.mode == kJacobi) {
                     for (int j = 0; j < nrep; ++j) {
-                        const float so = S[(j + 1) * PS + ri];
+                        const float so = So[(j + 1) * PS + ri];
                         const float sh = V[j * DP + ri];
-                        S[(j + 1) * PS + ri] = und ? sh : so + lam * (sh - so);
+                        Sn[(j + 1) * PS + ri] = und ? sh : so + lam * (sh - so);
                     }
                 } else {
                     int j = 0;
@@ -1988,27 +1999,28 @@ __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(Resid
                         for (int u = 0; u < 8; ++u) {
                             v[u] = V[(j + u) * DP + ri];
                             co[u] = CO[(j + u) * DP + ri];
-                            po[u] = S[(j + u + 1) * PS + ri];
+                            po[u] = So[(j + u + 1) * PS + ri];
                         }
 #pragma unroll
                         for (int u = 0; u < 8; ++u) {
                             shat = v[u] + co[u] * (shat - pold);
                             pold = po[u];
-                            S[(j + u + 1) * PS + ri] = und ? shat : pold + lam * (shat - pold);
+                            Sn[(j + u + 1) * PS + ri] = und ? shat : pold + lam * (shat - pold);
                         }
                     }
                     for (; j < nrep; ++j) {
                         shat = V[j * DP + ri] + CO[j * DP + ri] * (shat - pold);
-                        pold = S[(j + 1) * PS + ri];
-                        S[(j + 1) * PS + ri] = und ? shat : pold + lam * (shat - pold);
+                        pold = So[(j + 1) * PS + ri];
+                        Sn[(j + 1) * PS + ri] = und ? shat : pold + lam * (shat - pold);
                     }
                 }
                 if (has_next) {
-                    const float so = S[Lc * PS + ri];
-                    S[Lc * PS + ri] = und ? c_next : so + lam * (c_next - so);
+                    const float so = So[Lc * PS + ri];
+                    Sn[Lc * PS + ri] = und ? c_next : so + lam * (c_next - so);
                 }
             }
             __syncthreads();
+            if constexpr (DB) cur ^= 1;          // s^(i+1) is the current buffer now
             // the maps of iteration i+1 at s^(i+1), and r_{i+1}
             uint32_t rbn = 0;
 #pragma unroll 1
@@ -2034,16 +2046,30 @@ __global__ __launch_bounds__(kThreads, CPW > 1 ? 2 : 1) void cell_resident(Resid
             if (st >= 0) {
                 K = i;
                 status = st;
+                if constexpr (DB) cur ^= 1;      // the result is s^(i)
                 break;
             }
         }
         // every workgroup past the iteration after the stop before the sets
-        // are reused; out and s0n hold s^(K) since the start of iteration K
+        // are reused; with one buffer out and s0n hold s^(K) since the start
+        // of iteration K, with two they are stored now
         if (!wait_all(tag)) return;
         bool last = false;
 #pragma unroll
-        for (int k = 0; k < CPW; ++k)
-            if (active(k) && chunk(k) + 1 == NCw) last = true;
+        for (int k = 0; k < CPW; ++k) {
+            if (!active(k)) continue;
+            const int c = chunk(k), Lc = rows(k);
+            if (c + 1 == NCw) last = true;
+            if constexpr (DB) {
+                const float* S = Sk(k);
+                float* o = a.out + (static_cast<int64_t>(b) * a.T + w0 + c * L) * D;
+                for (int e = tid; e < Lc * D; e += kThreads) {
+                    const int j = e / D, ii = e % D;
+                    o[e] = S[(j + 1) * PS + ii];
+                }
+                if (c + 1 == NCw && tid < D) st_dev(a.s0n + b * D + tid, S[Lc * PS + tid]);
+            }
+        }
         if (lead && tid == 0) {
             a.win_iters[wi] = K;
             a.win_status[wi] = status;
@@ -2421,7 +2447,7 @@ hipError_t launch_cell_resident_adv(int kind, int DP, const ResidentArgs& a, hip
 
 size_t resident_lds_bytes(int DP, int L, int m, int cpw) {
     const size_t PS = DP + 4, xs = x_stride(m);
-    const size_t per = (L + 1) * PS + 2ull * L * DP + static_cast<size_t>(L) * xs;
+    const size_t per = (cpw == 1 ? 2 : 1) * (L + 1) * PS + 2ull * L * DP + static_cast<size_t>(L) * xs;
     return sizeof(float) * (cpw * per + 2ull * kThreads + DP);
 }
 
