@@ -264,6 +264,22 @@ def test_matrix_core_one_wavefront_form(kind, D):
         _parity(wl, mode, chunk=48)
 
 
+@pytest.mark.parametrize("window", [0, 1000])
+@pytest.mark.parametrize("kind, D", [(pn.CELL_GRU, 16), (pn.CELL_TANH_RNN, 12), (pn.CELL_EULER_TANH, 16)])
+def test_matrix_core_one_wavefront_form_d16(kind, D, window):
+    # D padded to 16 with more chunks than SIMDs (64 x 23): one wavefront per
+    # chunk, the carries of 23 chunks per row.  With windows of 1000 steps the
+    # second window has 3 chunks per row and runs two wavefronts per chunk.
+    rng = np.random.default_rng(520 + D + kind)
+    m, B, T = 6, 64, 1100
+    params = workloads.lattice_cell_params(kind, D, m, rng)
+    wl = dict(cfg=0, cell=kind, D=D, m=m, B=B, T=T, tol=1e-6, damping=1.0, window=window,
+              max_iter=window or T, params=params, x=rng.standard_normal((B, T, m)).astype(np.float32),
+              s0=(0.2 * rng.standard_normal((B, D))).astype(np.float32), bandwidth=2)
+    for mode in (N, pn.BANDED):
+        _parity(wl, mode, chunk=48)
+
+
 @pytest.mark.parametrize("k", [1, 2, 3])
 @pytest.mark.parametrize("D", [5, 12, 20, 33, 64])
 @pytest.mark.parametrize("kind", [pn.CELL_TANH_RNN, pn.CELL_GRU])
