@@ -168,6 +168,12 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
         } else {
             while (L < 512 && static_cast<int64_t>(B) * ((p.W + 2 * L - 1) / (2 * L)) >= 2048) L *= 2;
             while (L > 16 && static_cast<int64_t>(B) * ((p.W + L - 1) / L) < 1024) L /= 2;
+            // the one-wavefront sweep at D padded to 16 holds four wavefronts
+            // per SIMD: halve the chunks once more while that still fits
+            // the 4096 wavefronts of one residency round
+            if (p.DP == 16 && L > 16 && static_cast<int64_t>(B) * ((p.W + L - 1) / L) > kSplitMax &&
+                static_cast<int64_t>(B) * ((p.W + L / 2 - 1) / (L / 2)) <= 4096)
+                L /= 2;
         }
         p.L = p.Lc = static_cast<int>(std::min<int64_t>(L, p.W));
         p.NC = static_cast<int>((p.W + p.L - 1) / p.L);

@@ -1598,8 +1598,150 @@ __global__ __launch_bounds__(DP * DP / 4) void dense_carry_wide(CarryArgs g) {
     }
 }
 
+// D padded to 16 with at most kScanMaxChunks chunks per row: the carries as
+// a two-level scan of the affine chunk maps (composing affine maps is
+// associative [PN §2.1]) on the 16x16x4 FP32 matrix cores.  One workgroup per
+// batch row, one wavefront per group of G <= kScanG consecutive chunks:
+//  1. every group but the last composes its maps into one affine map (P, q);
+//  2. wavefront 0 runs the group maps from s0: the carry entering each group;
+//  3. every group runs its own maps from its entering carry and stores its
+//     carries.
+// That is 2 G + NC / G dependent map steps instead of NC - 1 (G about
+// sqrt(NC / 2) minimises it).  A
+// map step is four chained MFMAs: the A operand is the map as loaded (lane
+// (i, h) holds M[i][4h .. 4h+3]), the B operand the running matrix or vector
+// in the accumulator layout (register r of lane (j, h) holds entry (4h + r,
+// j)), so each result is the next step's operand as it stands; a vector
+// rides in every column.  Rows and columns past D are zero.
+constexpr int kScanG = 8;
+constexpr int kScanMaxChunks = 16 * kScanG;
+
+// group size for NC chunks: the least G with 2 G^2 >= NC, at most kScanG
+__host__ __device__ __forceinline__ int scan_group(int NC) {
+    int G = 1;
+    while (G < kScanG && 2 * G * G < NC) ++G;
+    return G;
+}
+
+__device__ __forceinline__ v4f map_step16(const float4& A, const v4f& X, v4f C) {
+    C = __builtin_amdgcn_mfma_f32_16x16x4f32(A.x, X[0], C, 0, 0, 0);
+    C = __builtin_amdgcn_mfma_f32_16x16x4f32(A.y, X[1], C, 0, 0, 0);
+    C = __builtin_amdgcn_mfma_f32_16x16x4f32(A.z, X[2], C, 0, 0, 0);
+    C = __builtin_amdgcn_mfma_f32_16x16x4f32(A.w, X[3], C, 0, 0, 0);
+    return C;
+}
+
+__global__ __launch_bounds__(64 * (kScanMaxChunks / kScanG)) void dense_carry_scan16(CarryArgs g) {
+    if (g.stop_on && g.stop_on->stop) return;     // queued ahead of a stop
+    if (g.do_check && blockIdx.x == 0) run_check(g.chk);
+    __shared__ __attribute__((aligned(16))) float Pl[kScanMaxChunks / kScanG][256];   // group maps, row-major
+    __shared__ __attribute__((aligned(16))) float ql[kScanMaxChunks / kScanG][16];    // group offsets
+    __shared__ __attribute__((aligned(16))) float yl[kScanMaxChunks / kScanG][16];    // carries entering groups
+    const int D = g.D, NC = g.NC;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int i = lane & 15, h = lane >> 4;
+    const int G = scan_group(NC);
+    const int nw = static_cast<int>(blockDim.x >> 6);     // ceil(NC / G)
+    const size_t cb = static_cast<size_t>(blockIdx.x) * NC;
+    const int c0 = w * G;
+    const int nown = min(G, NC - c0);                     // carries of this group
+    const int nmap = w < nw - 1 ? G : nown - 1;           // maps it runs
+    const bool vec4 = (D & 3) == 0;
+    // maps c0 .. c0 + nmap - 1 (at most NC - 2) in the A layout, offsets in
+    // the accumulator layout.  Every load is unconditional (clamped chunk,
+    // row and column; unused values are replaced by zeros), so all of them
+    // are in flight at once.
+    float4 Ma[kScanG], ba[kScanG];
+    const float4 zero4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const int ir = min(i, D - 1);
+    if (vec4) {
+        const bool colok = 4 * h < D;
+        const int kc = colok ? 4 * h : 0;
+#pragma unroll
+        for (int u = 0; u < kScanG; ++u) {
+            const size_t c = cb + min(c0 + u, NC - 1);
+            const float4 mv = *reinterpret_cast<const float4*>(g.aggA + c * D * D + ir * D + kc);
+            const float4 bb = *reinterpret_cast<const float4*>(g.aggB + c * D + kc);
+            Ma[u] = (u < nmap && i < D && colok) ? mv : zero4;
+            ba[u] = (u < nmap && colok) ? bb : zero4;
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kScanG; ++u) {
+            const size_t c = cb + min(c0 + u, NC - 1);
+            float mv[4], bb[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int k = 4 * h + s, kk = min(k, D - 1);
+                const float m = g.aggA[c * D * D + ir * D + kk];
+                const float o = g.aggB[c * D + kk];
+                mv[s] = (u < nmap && i < D && k < D) ? m : 0.0f;
+                bb[s] = (u < nmap && k < D) ? o : 0.0f;
+            }
+            Ma[u] = make_float4(mv[0], mv[1], mv[2], mv[3]);
+            ba[u] = make_float4(bb[0], bb[1], bb[2], bb[3]);
+        }
+    }
+    auto bvec = [](const float4& v) {
+        v4f r;
+        r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
+        return r;
+    };
+    if (w < nw - 1) {
+        // 1. (P, q) <- (M_c P, M_c q + b_c) over the group's maps
+        v4f P, q = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) P[r] = 4 * h + r == i ? 1.0f : 0.0f;
+#pragma unroll
+        for (int u = 0; u < kScanG; ++u) {
+            if (u < G) {
+                P = map_step16(Ma[u], P, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                q = map_step16(Ma[u], q, bvec(ba[u]));
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Pl[w][(4 * h + r) * 16 + i] = P[r];
+        if (i == 0) *reinterpret_cast<float4*>(&ql[w][4 * h]) = make_float4(q[0], q[1], q[2], q[3]);
+    }
+    __syncthreads();
+    if (w == 0) {
+        // 2. the carry entering each group
+        const float* s0b = g.s0 + static_cast<int64_t>(blockIdx.x) * g.s0s;
+        v4f y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = 4 * h + r < D ? s0b[4 * h + r] : 0.0f;
+        for (int v = 0; v < nw; ++v) {
+            if (i == 0) *reinterpret_cast<float4*>(&yl[v][4 * h]) = make_float4(y[0], y[1], y[2], y[3]);
+            if (v == nw - 1) break;
+            const float4 A = *reinterpret_cast<const float4*>(&Pl[v][i * 16 + 4 * h]);
+            y = map_step16(A, y, bvec(*reinterpret_cast<const float4*>(&ql[v][4 * h])));
+        }
+    }
+    __syncthreads();
+    // 3. the group's carries
+    v4f y = bvec(*reinterpret_cast<const float4*>(&yl[w][4 * h]));
+#pragma unroll
+    for (int u = 0; u < kScanG; ++u) {
+        if (u < nown) {
+            if (i == 0) {
+                float* cr = g.carry + (cb + c0 + u) * D;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * h + r < D) cr[4 * h + r] = y[r];
+            }
+            if (u < nown - 1) y = map_step16(Ma[u], y, bvec(ba[u]));
+        }
+    }
+}
+
 hipError_t launch_dense_carry(const CarryArgs& a, hipStream_t st) {
     const int DP = a.D <= 4 ? 4 : a.D <= 8 ? 8 : a.D <= 16 ? 16 : a.D <= 32 ? 32 : 64;
+    if (DP == 16 && a.NC >= 1 && a.NC <= kScanMaxChunks) {
+        const int G = scan_group(a.NC);
+        const int nw = (a.NC + G - 1) / G;
+        dense_carry_scan16<<<a.B, 64 * nw, 0, st>>>(a);
+        return hipGetLastError();
+    }
     if (a.D % 4 == 0 && DP >= 16) {
         if (DP == 16) dense_carry_wide<16><<<a.B, 16 * 4, 0, st>>>(a);
         else if (DP == 32) dense_carry_wide<32><<<a.B, 32 * 8, 0, st>>>(a);

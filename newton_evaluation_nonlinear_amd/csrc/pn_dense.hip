@@ -260,8 +260,12 @@ __device__ __forceinline__ float cell_point(const float (&gv)[3], float xn, floa
 // latency chains of the two roles then overlap within one chunk, which pays
 // when there are too few chunks to fill the SIMDs with other chunks; with
 // many chunks one wavefront per chunk runs both roles (more chunks resident).
+// At D padded to 16 the one-wavefront form is held to 128 registers (no
+// spills), so four wavefronts share each SIMD and hide one another's
+// latencies: the planner then gives 4096 chunks where it can.
 template <int CELL, int DP, int PHASE, bool BANDED, bool SPLIT>
-__global__ __launch_bounds__(SPLIT ? 128 : 64) void dense_pass(CellArgs g) {
+__global__ __launch_bounds__(SPLIT ? 128 : 64)
+__attribute__((amdgpu_waves_per_eu((DP == 16 && !SPLIT) ? 4 : 1))) void dense_pass(CellArgs g) {
     if constexpr (PHASE != kPrologue && PHASE != kMaps) {   // apply launches enqueued ahead
         if (g.ctrl->stop) return;
         if (g.fc & kFcCheck) {
@@ -1040,7 +1044,6 @@ static hipError_t launch_dense_phase_s(int phase, const CellArgs& a, hipStream_t
 // Two wavefronts per chunk when the chunks alone (one wavefront each) would
 // leave SIMDs without a second chunk: at most one chunk per SIMD (the chip
 // has 1024).
-constexpr int kSplitMax = 1024;
 
 template <int CELL, int DP, bool BANDED>
 static hipError_t launch_dense_phase_b(int phase, const CellArgs& a, hipStream_t st) {

@@ -138,6 +138,8 @@ struct CellArgs {
 constexpr int kFcMaxChunks = 128;
 constexpr int kFcMaxBlocks = 16384;      // workgroups of one sweep (B x chunks)
 constexpr int kFcCarry = 1, kFcCheck = 2;
+// chunks (B x NC) up to which a matrix-core sweep runs two wavefronts per chunk
+constexpr int kSplitMax = 1024;
 
 struct CarryArgs {
     const float* aggA;

@@ -862,6 +862,47 @@ def test_nonfinite_input_is_reported_at_the_oracle_iteration():
     assert gpu.iters == ref.iters == 0
 
 
+def _with_param(wl, index, value):
+    out = dict(wl)
+    out["params"] = wl["params"].copy()
+    out["params"][index] = value
+    return out
+
+
+@pytest.mark.parametrize("small", [False, True])
+def test_nonfinite_and_infinite_parameters(small):
+    # Parameters that are NaN or infinite, on the matrix-core and resident
+    # paths (D = 32) and on the one-workgroup solver (D = 4).  A NaN bias
+    # makes the first residual NaN in every mode.  An infinite bias saturates
+    # its channel at tanh = 1 with a zero derivative: the solve stays finite
+    # and is held to the usual bar.  An infinite off-diagonal weight saturates
+    # its row too, but that row of the Newton Jacobian is 0 x inf = NaN, so
+    # Newton turns non-finite after its first update, at the oracle's update,
+    # while the diagonal modes (finite diagonal) and Jacobi converge.
+    wl = _small_case(pn.CELL_TANH_RNN, 4, 2, 100, 4242) if small else _case(4, B=2, T=300)
+    D, m = wl["D"], wl["m"]
+    # a nonzero initial state: inf x 0 in W s^(0) would be NaN at once
+    wl["s0"] = (0.3 * np.random.default_rng(4243).standard_normal((2, D))).astype(np.float32)
+    bias = D * D + D * m                     # params: W[D*D] | U[D*m] | b[D]
+    nan_b = _with_param(wl, bias + 1, np.nan)
+    for mode in (N, Q, J):
+        g = run_gpu(nan_b, mode)
+        r = run_oracle(nan_b, mode)
+        assert g.status == r.status == oracle.NONFINITE and g.iters == r.iters == 0
+    inf_b = _with_param(wl, bias + 2, np.inf)
+    for mode in (N, Q):
+        ref = _parity(inf_b, mode)
+        assert ref.status == oracle.OK and np.all(ref.s[:, :, 2] == 1.0)
+    inf_w = _with_param(wl, 2 * D + 3, np.inf)   # W[2][3]
+    g = run_gpu(inf_w, N)
+    r = run_oracle(inf_w, N)
+    assert r.status == oracle.NONFINITE and r.iters == 1
+    assert g.status == pn.NONFINITE and g.iters == r.iters
+    for mode in (Q, J):
+        ref = _parity(inf_w, mode)
+        assert ref.status == oracle.OK
+
+
 @pytest.mark.parametrize("chunk, T, window", [(0, 1500, 0), (16, 3000, 0), (16, 2100, 700), (0, 640, 100)])
 def test_fused_check_and_carry_launch_paths(chunk, T, window):
     # diagonal modes of a matrix cell: with at most 128 chunks per window

@@ -867,6 +867,36 @@ def test_residual_of_a_perturbed_trajectory():
     assert oracle.residual_inf(cell, x, s0, pert) == pytest.approx(0.125, abs=1e-15)
 
 
+def test_infinite_parameters_saturate_or_poison_the_newton_jacobian():
+    # IEEE arithmetic fixes the outcome: an infinite bias gives tanh = 1
+    # exactly with derivative 1 - 1 = 0, so every mode reaches the sequential
+    # trajectory; an infinite weight W[2][3] also gives |tanh| = 1 on channel
+    # 2, but the Newton Jacobian's entry (1 - 1) x inf is NaN and poisons the
+    # first update, while the diagonal Jacobian (1 - 1) x W[2][2] stays 0.
+    D, m, B, T = 4, 2, 2, 30
+    rng = np.random.default_rng(77)
+    params = _rnn_params(D, m, rng)
+    x = rng.standard_normal((B, T, m))
+    s0 = 0.3 * rng.standard_normal((B, D))
+    pb = params.copy()
+    pb[D * D + D * m + 1] = np.inf
+    cell = oracle.make_cell(oracle.CELL_TANH_RNN, pb, D, m)
+    seq = oracle.sequential(cell, x, s0)
+    assert np.all(seq[:, :, 1] == 1.0) and np.all(np.isfinite(seq))
+    for mode in (oracle.NEWTON, oracle.QUASI_NEWTON, oracle.JACOBI):
+        r = oracle.solve(oracle.CELL_TANH_RNN, pb, x, s0, mode, 1e-12, T)
+        assert r.status == oracle.OK and np.max(np.abs(r.s - seq)) <= 1e-12
+    pw = params.copy()
+    pw[2 * D + 3] = np.inf
+    with np.errstate(invalid="ignore"):
+        seq = oracle.sequential(oracle.make_cell(oracle.CELL_TANH_RNN, pw, D, m), x, s0)
+        assert np.all(np.abs(seq[:, :, 2]) == 1.0) and np.all(np.isfinite(seq))
+        rn = oracle.solve(oracle.CELL_TANH_RNN, pw, x, s0, oracle.NEWTON, 1e-12, T)
+        assert rn.status == oracle.NONFINITE and rn.iters == 1 and np.isfinite(rn.hist[0][0])
+        rq = oracle.solve(oracle.CELL_TANH_RNN, pw, x, s0, oracle.QUASI_NEWTON, 1e-12, T)
+    assert rq.status == oracle.OK and np.max(np.abs(rq.s - seq)) <= 1e-12
+
+
 def test_stop_rule_edges():
     wl = workloads.make(2, B=2, T=40)
     a = (wl["cell"], wl["params"], wl["x"], wl["s0"], oracle.QUASI_NEWTON)
