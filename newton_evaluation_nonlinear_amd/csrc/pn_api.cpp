@@ -144,8 +144,11 @@ int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int
             p.L = static_cast<int>(L);
             p.Lc = static_cast<int>(recompute ? std::min<int64_t>(2 * L, 1024) : L);
         }
-        p.L = static_cast<int>(std::min<int64_t>(p.L, p.W));
-        p.Lc = static_cast<int>(std::min<int64_t>(std::max(p.Lc, p.L), p.W));
+        // the sweeps address a chunk's rows with 32-bit buffer offsets (row
+        // index x row bytes): keep a chunk's rows within 2^30 bytes
+        const int64_t maxL = std::max<int64_t>(1, (int64_t{1} << 30) / (static_cast<int64_t>(D) * (half ? 2 : 4)));
+        p.L = static_cast<int>(std::min<int64_t>(std::min<int64_t>(p.L, p.W), maxL));
+        p.Lc = static_cast<int>(std::min<int64_t>(std::min<int64_t>(std::max(p.Lc, p.L), p.W), maxL));
         if (p.Lc % p.L != 0) p.Lc = p.L;    // steady chunks are whole multiples of the first ones
         p.NC = static_cast<int>((p.W + p.L - 1) / p.L);
         DiagArgs a{};

@@ -82,6 +82,34 @@ __device__ __forceinline__ float stored(float v) {
     return static_cast<float>(static_cast<S>(v));
 }
 
+// Rows of a [.., T, D] array inside one chunk, as seen by one wavefront:
+// buffer loads and stores whose base (row 0 at the wave's first channel) is
+// uniform over the wave, with the row offset a scalar operand and the lane's
+// byte offset the vector one, so addressing costs no vector instruction.
+// Offsets stay below 2^31 (the planner bounds chunk rows x row bytes); the
+// callers' row tests keep every access inside the chunk.
+template <typename V> struct Rows {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t lo;     // lane offset in bytes
+    int32_t rs;      // row stride in bytes
+    __device__ __forceinline__ Rows(const void* base, uint32_t lane_off, int32_t row_bytes)
+        : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), 0x7fffffff,
+                                                 0x00020000)),
+          lo(lane_off), rs(row_bytes) {}
+    __device__ __forceinline__ V ld(int r) const {
+        if constexpr (sizeof(V) == 4)
+            return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(rsrc, lo, r * rs, 0));
+        else
+            return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b16(rsrc, lo, r * rs, 0));
+    }
+    __device__ __forceinline__ void st(int r, const V& v) const {
+        if constexpr (sizeof(V) == 4)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsrc, lo, r * rs, 0);
+        else
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), rsrc, lo, r * rs, 0);
+    }
+};
+
 // TRACK: also reduce the first step whose residual exceeds tol (the
 // advancing window); compiled out otherwise.
 template <int MODE, int PHASE, typename S, int NCH, bool UND, bool TRACK = false>
@@ -101,6 +129,10 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
     // it every row-count test below, is uniform over the wave (scalar)
     const int c = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / cpb) + cl);
     const int d = (blockIdx.y * cpb + dl) * NCH;     // first channel of the group
+    // the wave's first channel (every lane is active here) and this lane's
+    // byte offset from it: lanes hold consecutive channel groups of one row
+    const int dw = __builtin_amdgcn_readfirstlane(d);
+    const uint32_t lo = static_cast<uint32_t>(d - dw) * static_cast<uint32_t>(sizeof(S));
     const int b = blockIdx.z;
     uint32_t rb = 0;
     uint32_t fb = 0xffffffffu;                       // first step over tol (TRACK)
@@ -117,6 +149,9 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
         }
         const V* xp = reinterpret_cast<const V*>(reinterpret_cast<const S*>(g.x) + b * g.xs +
                                                  static_cast<int64_t>(t0) * D + d);
+        // rows of x in this chunk: a wave-uniform base plus the lane's offset
+        const Rows<V> xr(reinterpret_cast<const S*>(g.x) + b * g.xs + static_cast<int64_t>(t0) * D + dw, lo,
+                         D * static_cast<int32_t>(sizeof(S)));
         const size_t ai = (static_cast<size_t>(b) * g.NC + c) * D + d;
         float A[NCH], Bc[NCH];
 #pragma unroll
@@ -126,17 +161,16 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
         }
         if constexpr (PHASE == kPrologue) {
             // Iteration 0: s^(0)_t = s0 for every t, so p_t = s0 throughout.
-            V xb[kUP];
+            // group(j): issue the loads of rows j+kUP.. into xn, then take
+            // rows j.. from xb.  FULL: both groups lie inside the chunk, so
+            // no row test is compiled in.
+            auto group = [&](auto full, int j, const V (&xb)[kUP], V (&xn)[kUP]) {
+                constexpr bool F = decltype(full)::value;
 #pragma unroll
-            for (int u = 0; u < kUP; ++u) xb[u] = u < n ? xp[u * DV] : V{};
-            for (int j = 0; j < n; j += kUP) {
-                const V* xq = xp + static_cast<int64_t>(j) * DV;   // row j of the chunk
-                V xn[kUP];
-#pragma unroll
-                for (int u = 0; u < kUP; ++u) xn[u] = (j + kUP + u < n) ? xq[(kUP + u) * DV] : V{};
+                for (int u = 0; u < kUP; ++u) xn[u] = (F || j + kUP + u < n) ? xr.ld(j + kUP + u) : V{};
 #pragma unroll
                 for (int u = 0; u < kUP; ++u) {
-                    if (j + u < n) {
+                    if (F || j + u < n) {
                         float xt[NCH];
                         unpack<S, NCH>(xb[u], xt);
 #pragma unroll
@@ -150,8 +184,20 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
                         }
                     }
                 }
+            };
+            V x0[kUP], x1[kUP];
 #pragma unroll
-                for (int u = 0; u < kUP; ++u) xb[u] = xn[u];
+            for (int u = 0; u < kUP; ++u) x0[u] = u < n ? xr.ld(u) : V{};
+            int j = 0;
+            // two groups per trip, their buffers alternating (no register copies)
+            for (; j + 3 * kUP <= n; j += 2 * kUP) {
+                group(std::true_type{}, j, x0, x1);
+                group(std::true_type{}, j + kUP, x1, x0);
+            }
+            for (; j < n; j += kUP) {
+                group(std::false_type{}, j, x0, x1);
+#pragma unroll
+                for (int u = 0; u < kUP; ++u) x0[u] = x1[u];
             }
         } else if constexpr (PHASE == kMaps) {
             // The iterate stored in s (the advancing window, after it slides):
@@ -216,7 +262,6 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
             // chunk of this launch)
             const size_t HS = static_cast<size_t>(g.hs);
             const size_t ri = (static_cast<size_t>(b) * g.NCr + static_cast<size_t>(c) * g.rf) * D + d;
-            V* sp = reinterpret_cast<V*>(reinterpret_cast<S*>(g.s) + b * g.ss + static_cast<int64_t>(t0) * D + d);
             const bool has_next = (c + 1 < g.NC);
             const float lam = g.lam;
             // p_old: s^(i) at t0-1 (halo of the previous chunk);  shat: s^ at t0-1;
@@ -240,25 +285,27 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
             // float passes that read only x prefetch as deep as the prologue
             // (binary16 sweeps are bound by their vector instructions)
             constexpr int U = (kReadS || !std::is_same<S, float>::value) ? kU : kUP;
-            V xb[U], sb[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                xb[u] = u < n ? xp[u * DV] : V{};
-                if constexpr (kReadS) sb[u] = u < n ? sp[u * DV] : V{};
-            }
-            for (int j = 0; j < n; j += U) {
-                const V* xq = xp + static_cast<int64_t>(j) * DV;   // row j of the chunk
-                V* sq = sp + static_cast<int64_t>(j) * DV;
-                V xn[U], sn_[U];
+            // rows of the iterate in this chunk (read in kSteady, written
+            // unless kFirstNS), addressed like xr
+            const Rows<V> sr(reinterpret_cast<const S*>(g.s) + b * g.ss + static_cast<int64_t>(t0) * D + dw, lo,
+                             xr.rs);
+            // group(j): issue the loads of rows j+U.. into xn/sn_, then take
+            // rows j.. from xb/sb.  FULL: both groups lie inside the chunk
+            // and hold neither its last step nor rows past it, so no row
+            // test is compiled in.
+            auto group = [&](auto full, int j, const V (&xb)[U], const V (&sb)[U], V (&xn)[U], V (&sn_)[U]) {
+                constexpr bool F = decltype(full)::value;
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const bool in = j + U + u < n;
-                    xn[u] = in ? xq[(U + u) * DV] : V{};
-                    if constexpr (kReadS) sn_[u] = in ? sq[(U + u) * DV] : V{};
+                    const bool in = F || j + U + u < n;
+                    xn[u] = in ? xr.ld(j + U + u) : V{};
+                    if constexpr (kReadS) sn_[u] = in ? sr.ld(j + U + u) : V{};
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    if (j + u < n) {
+                    if (F || j + u < n) {
+                        // the chunk's last step takes the value the scan hands to the next chunk
+                        const bool last = !F && j + u == n - 1 && has_next;
                         float xt[NCH], so[NCH], sn[NCH];
                         unpack<S, NCH>(xb[u], xt);
                         if constexpr (kFromS0) {
@@ -271,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
                                 const float v0 = tanh_f(a[k] * s0v[k] + xt[k]);
                                 const float a0 = mode_coef<MODE>(a[k] * (1.0f - v0 * v0));
                                 sh0[k] = v0 + a0 * (sh0[k] - s0v[k]);
-                                if (j + u == n - 1 && has_next) sh0[k] = sh0_end[k];
+                                if (last) sh0[k] = sh0_end[k];
                                 so[k] = stored<S>(UND ? sh0[k] : s0v[k] + lam * (sh0[k] - s0v[k]));
                             }
                         } else {
@@ -283,15 +330,14 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
                             const float v = tanh_f(a[k] * p_old[k] + xt[k]);
                             const float at = mode_coef<MODE>(a[k] * (1.0f - v * v));
                             shat[k] = v + at * (shat[k] - p_old[k]);
-                            // the chunk's last value is the one the scan hands to the next chunk
-                            if (j + u == n - 1 && has_next) shat[k] = shat_end[k];
+                            if (last) shat[k] = shat_end[k];
                             sn[k] = UND ? shat[k] : so[k] + lam * (shat[k] - so[k]);
                         }
                         if constexpr (PHASE == kFirstNS) {
 #pragma unroll
                             for (int k = 0; k < NCH; ++k) sn[k] = stored<S>(sn[k]);
                         } else {
-                            sq[u * DV] = pack<S, NCH>(sn);   // sn now holds the stored values
+                            sr.st(j + u, pack<S, NCH>(sn));   // sn now holds the stored values
                         }
 #pragma unroll
                         for (int k = 0; k < NCH; ++k) {
@@ -309,10 +355,27 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
                         }
                     }
                 }
+            };
+            V x0[U], s0b[U], x1[U], s1b[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                x0[u] = u < n ? xr.ld(u) : V{};
+                s0b[u] = s1b[u] = V{};
+                if constexpr (kReadS) s0b[u] = u < n ? sr.ld(u) : V{};
+            }
+            int j = 0;
+            // two groups per trip, their buffers alternating (no register
+            // copies); the rows they take end U rows before the chunk does
+            for (; j + 3 * U <= n; j += 2 * U) {
+                group(std::true_type{}, j, x0, s0b, x1, s1b);
+                group(std::true_type{}, j + U, x1, s1b, x0, s0b);
+            }
+            for (; j < n; j += U) {
+                group(std::false_type{}, j, x0, s0b, x1, s1b);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    xb[u] = xn[u];
-                    if constexpr (kReadS) sb[u] = sn_[u];
+                    x0[u] = x1[u];
+                    s0b[u] = s1b[u];
                 }
             }
 #pragma unroll
