@@ -202,7 +202,7 @@ def cpu_detail(cfg, mode, switch_mode=-1, switch_ratio=0.5, storage=None):
 
 
 CEILING_BYTES = 512 << 20      # per array: the headline's x (8 x 65536 x 256 floats)
-CEILING_PATTERNS = (("read", 0), ("write", 1), ("copy", 2), ("2r1w_flat", 3), ("2r1w_rows", 4))
+CEILING_PATTERNS = (("read", 0), ("write", 1), ("copy", 2), ("2r1w_flat", 3), ("2r1w_rows", 4), ("read_rows", 5))
 
 
 def ceilings(reps=10):

@@ -31,8 +31,12 @@ extern "C" {
  *  PNC_2R1W_ROWS  s = x + 0.5 s over [8, T, 256] float arrays in the access
  *                 order of the channel-wise apply kernel: one workgroup per
  *                 (batch row, 1024-step chunk), one channel per thread, rows
- *                 in order with 8-step register prefetch; T from n (3n). */
-enum { PNC_READ = 0, PNC_WRITE = 1, PNC_COPY = 2, PNC_2R1W = 3, PNC_2R1W_ROWS = 4 };
+ *                 in order with 8-step register prefetch; T from n (3n).
+ *  PNC_READ_ROWS  sum of x over [8, T, 256] in the access order of the
+ *                 channel-wise sweeps that read only x: one workgroup per
+ *                 (batch row, 512-step chunk), one channel per thread, 16
+ *                 rows in flight while the previous 16 are summed (n). */
+enum { PNC_READ = 0, PNC_WRITE = 1, PNC_COPY = 2, PNC_2R1W = 3, PNC_2R1W_ROWS = 4, PNC_READ_ROWS = 5 };
 
 /* Best and median rate in GB/s (1e9 bytes/s) of `reps` launches. */
 int pnc_hbm(int pattern, size_t bytes, int reps, double* best_gbs, double* median_gbs);

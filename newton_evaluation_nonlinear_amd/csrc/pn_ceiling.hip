@@ -12,6 +12,10 @@
 //                  apply kernel: [8, T, 256] float arrays, one workgroup per
 //                  (batch row, 1024-step chunk), one channel per thread, rows
 //                  walked in order with 8-step register prefetch      [3n]
+//   PNC_READ_ROWS  sum of x in the access order of the channel-wise sweeps
+//                  that read only x: [8, T, 256], one workgroup per (batch
+//                  row, 512-step chunk), one channel per thread, rows in
+//                  order, 16 rows in flight while the previous 16 are summed [n]
 // The MFMA loop runs independent chains of v_mfma_f32_32x32x2f32 on register
 // operands (4096 flops each) on every SIMD.
 
@@ -97,6 +101,36 @@ __global__ __launch_bounds__(kThreads) void k_2r1w_rows(const float* __restrict_
     for (; t < n; ++t) sp[static_cast<size_t>(t) * kRowsD] = xp[static_cast<size_t>(t) * kRowsD] + 0.5f * sp[static_cast<size_t>(t) * kRowsD];
 }
 
+constexpr int kReadL = 512, kReadPre = 16;
+
+__global__ __launch_bounds__(kThreads) void k_read_rows(const float* __restrict__ x, float* __restrict__ out, int T) {
+    const int c = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int t0 = c * kReadL;
+    const int n = min(kReadL, T - t0);
+    const float* xp = x + (static_cast<size_t>(b) * T + t0) * kRowsD + d;
+    float acc = 0.0f;
+    float xa[kReadPre], xb[kReadPre];
+#pragma unroll
+    for (int u = 0; u < kReadPre; ++u) xa[u] = u < n ? xp[static_cast<size_t>(u) * kRowsD] : 0.0f;
+    for (int t = 0; t < n; t += 2 * kReadPre) {
+#pragma unroll
+        for (int u = 0; u < kReadPre; ++u) {
+            const int r = t + kReadPre + u;
+            xb[u] = r < n ? xp[static_cast<size_t>(r) * kRowsD] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kReadPre; ++u) acc += xa[u];
+#pragma unroll
+        for (int u = 0; u < kReadPre; ++u) {
+            const int r = t + 2 * kReadPre + u;
+            xa[u] = r < n ? xp[static_cast<size_t>(r) * kRowsD] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kReadPre; ++u) acc += xb[u];
+    }
+    out[(static_cast<size_t>(b) * gridDim.x + c) * kThreads + d] = acc;
+}
+
 typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kMfmaChains = 4;
 
@@ -152,7 +186,7 @@ extern "C" {
 
 int pnc_hbm(int pattern, size_t bytes, int reps, double* best_gbs, double* median_gbs) {
     g_err.clear();
-    if (!best_gbs || !median_gbs || reps < 1 || pattern < PNC_READ || pattern > PNC_2R1W_ROWS) {
+    if (!best_gbs || !median_gbs || reps < 1 || pattern < PNC_READ || pattern > PNC_READ_ROWS) {
         g_err = "bad argument";
         return -1;
     }
@@ -161,7 +195,7 @@ int pnc_hbm(int pattern, size_t bytes, int reps, double* best_gbs, double* media
     PNC_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     size_t n4 = bytes / 16;
     int T = 0;
-    if (pattern == PNC_2R1W_ROWS) {
+    if (pattern == PNC_2R1W_ROWS || pattern == PNC_READ_ROWS) {
         T = static_cast<int>(bytes / (sizeof(float) * kRowsB * kRowsD));
         T = std::max(kRowsL, T / kRowsL * kRowsL);
         n4 = static_cast<size_t>(kRowsB) * T * kRowsD / 4;
@@ -171,9 +205,11 @@ int pnc_hbm(int pattern, size_t bytes, int reps, double* best_gbs, double* media
     PNC_HIP(hipStreamCreate(&st));
     float *x = nullptr, *y = nullptr, *out = nullptr;
     const int grid = cus * 8;
+    // one partial sum per thread of either reading kernel
+    const size_t nout = std::max<size_t>(static_cast<size_t>(grid), static_cast<size_t>(T / kReadL) * kRowsB) * kThreads;
     PNC_HIP(hipMalloc(&x, nbytes));
     PNC_HIP(hipMalloc(&y, nbytes));
-    PNC_HIP(hipMalloc(&out, sizeof(float) * grid * kThreads));
+    PNC_HIP(hipMalloc(&out, sizeof(float) * nout));
     PNC_HIP(hipMemsetAsync(x, 0, nbytes, st));
     PNC_HIP(hipMemsetAsync(y, 0, nbytes, st));
     std::vector<float> ms;
@@ -195,6 +231,10 @@ int pnc_hbm(int pattern, size_t bytes, int reps, double* best_gbs, double* media
         case PNC_2R1W:
             moved = 3.0 * nbytes;
             rc = timed(st, reps, [&] { k_2r1w<<<grid, kThreads, 0, st>>>(reinterpret_cast<const float4*>(x), reinterpret_cast<float4*>(y), n4); }, &ms);
+            break;
+        case PNC_READ_ROWS:
+            moved = nbytes;
+            rc = timed(st, reps, [&] { k_read_rows<<<dim3(T / kReadL, kRowsB), kThreads, 0, st>>>(x, out, T); }, &ms);
             break;
         default:
             moved = 3.0 * nbytes;
