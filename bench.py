@@ -351,8 +351,8 @@ def scan_bench(reps=20):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--mode", default=None)
     ap.add_argument("--chunk", type=int, default=0)
@@ -473,7 +473,11 @@ def main():
         # ALUs (FP32 vector and matrix peaks are both 157.3 TFLOP/s on MI355X)
         fine = smode if smode >= 0 else mode
         dense = fine == 3 or (fine == 4 and 0 < wl["bandwidth"] < wl["D"] - 1)
-        unit = "alu" if dense and src == KERNEL_SOURCES[wl["cell"]] else "mfma"
+        # at D padded to 64 a band of at most two diagonals each side extends
+        # the chunk map on the vector ALUs (the row chain of dense64_pass)
+        row_chain = (fine == 4 and 0 < wl["bandwidth"] <= 2 and wl["bandwidth"] < wl["D"] - 1 and
+                     32 < wl["D"] <= 64 and wl["cell"] in (1, 3))
+        unit = "alu" if dense and (src == KERNEL_SOURCES[wl["cell"]] or row_chain) else "mfma"
         roof = {"bound": unit, "achieved": tf, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": tf / FP32_PEAK_TFLOPS, "traffic": _traffic(name, src, bytes_per_launch)}
     else:

@@ -659,8 +659,27 @@ template <int CELL> struct D64Lds {
     }
 };
 
-template <int CELL, int PHASE, bool BANDED>
+//
+// The banded mode with half-bandwidth k <= RB (RB > 0) extends the chunk map
+// on the vector ALUs instead and uses the band [PN §2.2.2]: lane i holds row i
+// of M (64 registers, one per column), and row i of band_k(W) M is
+// sum_{|d| <= k} W[i][i+d] M[i+d][:], whose rows i +- d come from the lanes
+// d below and above through whole-wavefront DPP shifts by one lane (zero
+// beyond the ends).  Per time step that is (2k+1) multiply-adds and 2k lane
+// shifts per column, against 128 matrix-core steps of the dense product.
+
+// v of lane i - 1 into lane i (0 into lane 0); v of lane i + 1 into lane i
+// (0 into lane 63): wavefront shifts by one lane.  Every lane must be active.
+__device__ __forceinline__ float lane_from_below(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x138, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float lane_from_above(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x130, 0xf, 0xf, true));
+}
+
+template <int CELL, int PHASE, bool BANDED, int RB = 0>
 __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
+    static_assert(RB == 0 || BANDED, "the row chain is the banded mode's");
     static_assert(DTraits<CELL>::NG == 1, "single-gate cells only");
     if constexpr (PHASE != kPrologue && PHASE != kMaps) {
         if (g.ctrl->stop) return;
@@ -705,6 +724,13 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
                 wr[I][K][s] = w[k * DP + row];
                 wj[I][K][s] = (!BANDED || abs(k - row) <= g.band) ? wr[I][K][s] : 0.0f;
             }
+    // row chain: wl[RB + d] = W[lane][lane + d] inside the band and the live block
+    float wl[2 * RB + 1];
+#pragma unroll
+    for (int d = -RB; d <= RB; ++d) {
+        const int k = lane + d;
+        wl[RB + d] = (abs(d) <= g.band && lane < D && k >= 0 && k < D) ? w[k * DP + lane] : 0.0f;
+    }
     copy_to_lds<64>(UT, wUT, m * DP);
     const float bias2[2] = {wbi[r], wbi[32 + r]};
     float hs[2] = {0.0f, 0.0f};               // Euler step sizes of rows r, 32 + r
@@ -785,18 +811,45 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
         }
     };
     auto own = [&](const float (&x)[2]) { return h ? x[1] : x[0]; };
+    // Row-chain form of jac_apply (RB > 0): the band product of the lane's
+    // own row from its neighbours' entries through lane shifts, the partner
+    // row (l ^ 32) by one exchange; no LDS vector and no barrier.
+    auto jac_apply_row = [&](const float (&dd)[2], const float (&co)[2][NCO], float (&o)[2]) {
+        const float dl = own(dd);
+        float y = wl[RB] * dl, up = dl, dn = dl;
+#pragma unroll
+        for (int e = 1; e <= RB; ++e) {
+            up = lane_from_below(up);
+            dn = lane_from_above(dn);
+            y = fmaf(wl[RB - e], up, y);
+            y = fmaf(wl[RB + e], dn, y);
+        }
+        const float yo = __shfl_xor(y, 32, 64);
+        const float a[2] = {h ? yo : y, h ? y : yo};
+#pragma unroll
+        for (int I = 0; I < 2; ++I) {
+            if constexpr (CELL == kCellTanhRnnD) o[I] = co[I][0] * a[I];
+            else o[I] = co[I][0] * dd[I] + co[I][NCO - 1] * a[I];
+        }
+    };
 
-    // chunk map: identity on the live rows
+    // chunk map: identity on the live rows (row chain: row lane of M)
     v16f M[2][2];
+    float Mr[RB > 0 ? DP : 1];
+    if constexpr (RB > 0) {
 #pragma unroll
-    for (int K = 0; K < 2; ++K)
+        for (int col = 0; col < DP; ++col) Mr[col] = (col == lane && col < D) ? 1.0f : 0.0f;
+    } else {
 #pragma unroll
-        for (int J = 0; J < 2; ++J)
+        for (int K = 0; K < 2; ++K)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int row = 32 * K + Tl::krow(h, q), col = 32 * J + r;
-                M[K][J][q] = (row == col && col < D) ? 1.0f : 0.0f;
-            }
+            for (int J = 0; J < 2; ++J)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int row = 32 * K + Tl::krow(h, q), col = 32 * J + r;
+                    M[K][J][q] = (row == col && col < D) ? 1.0f : 0.0f;
+                }
+    }
     float bg[2] = {0.0f, 0.0f};
     uint32_t rb = 0;
     const bool track = g.fpart != nullptr;
@@ -871,15 +924,18 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
                 float dd[2];
                 dd[0] = live0 ? shat[0] - P[j * DP + r] : 0.0f;
                 dd[1] = live1 ? shat[1] - P[j * DP + 32 + r] : 0.0f;
-                YV[orow] = own(dd);
-                __syncthreads();
+                if constexpr (RB == 0) {
+                    YV[orow] = own(dd);
+                    __syncthreads();
+                }
                 float co[2][NCO];
 #pragma unroll
                 for (int I = 0; I < 2; ++I)
 #pragma unroll
                     for (int q = 0; q < NCO; ++q) co[I][q] = CO[(q * kSub + j) * DP + 32 * I + r];
                 float ad[2];
-                jac_apply(YV, dd, co, ad);
+                if constexpr (RB > 0) jac_apply_row(dd, co, ad);
+                else jac_apply(YV, dd, co, ad);
                 float sn[2];
 #pragma unroll
                 for (int I = 0; I < 2; ++I) {
@@ -890,8 +946,9 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
                     sn[I] = g.undamped ? shat[I] : so + g.lam * (shat[I] - so);
                 }
                 N[(j + 1) * DP + orow] = olive ? own(sn) : 0.0f;
-                __syncthreads();
+                if constexpr (RB == 0) __syncthreads();      // YV is rewritten next step
             }
+            if constexpr (RB > 0) __syncthreads();
             for (int e = lane; e < Sc * D; e += 64) {
                 const int j = e / D, q = e % D;
                 sg[static_cast<int64_t>(j0 + j) * D + q] = N[(j + 1) * DP + q];
@@ -927,23 +984,27 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
         // extend the chunk map over the sub-chunk
         for (int j = 0; j < Sc; ++j) {
             v16f C[2][2];
+            if constexpr (RB == 0) {
 #pragma unroll
-            for (int I = 0; I < 2; ++I)
+                for (int I = 0; I < 2; ++I)
 #pragma unroll
-                for (int J = 0; J < 2; ++J) {
+                    for (int J = 0; J < 2; ++J) {
 #pragma unroll
-                    for (int q = 0; q < 16; ++q) C[I][J][q] = 0.0f;
+                        for (int q = 0; q < 16; ++q) C[I][J][q] = 0.0f;
 #pragma unroll
-                    for (int K = 0; K < 2; ++K)
+                        for (int K = 0; K < 2; ++K)
 #pragma unroll
-                        for (int s = 0; s < 16; ++s) C[I][J] = Tl::step(wj[I][K][s], M[K][J][s], C[I][J]);
-                }
+                            for (int s = 0; s < 16; ++s) C[I][J] = Tl::step(wj[I][K][s], M[K][J][s], C[I][J]);
+                    }
+            }
             // offset: bg <- A_j (bg - p_j) + v_j  (p_j = N[j])
             float dbi[2];
             dbi[0] = live0 ? bg[0] - N[j * DP + r] : 0.0f;
             dbi[1] = live1 ? bg[1] - N[j * DP + 32 + r] : 0.0f;
-            YV[DP + orow] = own(dbi);
-            __syncthreads();
+            if constexpr (RB == 0) {
+                YV[DP + orow] = own(dbi);
+                __syncthreads();
+            }
             {
                 float co[2][NCO];
 #pragma unroll
@@ -951,13 +1012,34 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
 #pragma unroll
                     for (int q = 0; q < NCO; ++q) co[I][q] = CO[(q * kSub + j) * DP + 32 * I + r];
                 float ad[2];
-                jac_apply(YV + DP, dbi, co, ad);
+                if constexpr (RB > 0) jac_apply_row(dbi, co, ad);
+                else jac_apply(YV + DP, dbi, co, ad);
 #pragma unroll
                 for (int I = 0; I < 2; ++I) bg[I] = V[j * DP + 32 * I + r] + ad[I];
             }
+            if constexpr (RB > 0) {
+                // row lane of M <- row lane of A_j M, A_j = diag(c0) band(W)
+                // (tanh RNN) or diag(c0) + diag(c1) band(W) (Euler step)
+                const float c0 = CO[j * DP + lane];
+                const float c1 = CO[((NCO - 1) * kSub + j) * DP + lane];
+#pragma unroll
+                for (int col = 0; col < DP; ++col) {
+                    float t = wl[RB] * Mr[col];
+                    float up = Mr[col], dn = Mr[col];
+#pragma unroll
+                    for (int d = 1; d <= RB; ++d) {
+                        up = lane_from_below(up);     // M[lane - d][col]
+                        dn = lane_from_above(dn);     // M[lane + d][col]
+                        t = fmaf(wl[RB - d], up, t);
+                        t = fmaf(wl[RB + d], dn, t);
+                    }
+                    if constexpr (CELL == kCellTanhRnnD) Mr[col] = c0 * t;
+                    else Mr[col] = fmaf(c0, Mr[col], c1 * t);
+                }
+            }
             // row scalings of the accumulator rows 32 I + krow(h, q)
 #pragma unroll
-            for (int I = 0; I < 2; ++I) {
+            for (int I = 0; I < 2 && RB == 0; ++I) {
                 float rs[NCO][16];
 #pragma unroll
                 for (int q = 0; q < NCO; ++q)
@@ -977,7 +1059,7 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
                         else M[I][J][q] = rs[0][q] * M[I][J][q] + rs[NCO - 1][q] * C[I][J][q];
                     }
             }
-            __syncthreads();
+            if constexpr (RB == 0) __syncthreads();      // YV is rewritten next step
         }
         // carry the last rows into the next sub-chunk
         const float plast = P[Sc * DP + orow];
@@ -994,15 +1076,21 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
         if (olive) g.halo[((g.iter + 1) & 1) * HS + ci * D + orow] = N[orow];
     }
     float* aA = g.aggA + ci * D * D;
+    if constexpr (RB > 0) {
 #pragma unroll
-    for (int K = 0; K < 2; ++K)
+        for (int col = 0; col < DP; ++col)
+            if (lane < D && col < D) aA[lane * D + col] = Mr[col];
+    } else {
 #pragma unroll
-        for (int J = 0; J < 2; ++J)
+        for (int K = 0; K < 2; ++K)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int row = 32 * K + Tl::krow(h, q), col = 32 * J + r;
-                if (row < D && col < D) aA[row * D + col] = M[K][J][q];
-            }
+            for (int J = 0; J < 2; ++J)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int row = 32 * K + Tl::krow(h, q), col = 32 * J + r;
+                    if (row < D && col < D) aA[row * D + col] = M[K][J][q];
+                }
+    }
     if (olive) g.aggB[ci * D + orow] = own(bg);
     rb = wave_max_u32(rb);
     if (lane == 0) g.rpart[ci] = rb;
@@ -1012,21 +1100,26 @@ __global__ __launch_bounds__(64) void dense64_pass(CellArgs g) {
     }
 }
 
-template <int CELL, bool BANDED>
+template <int CELL, bool BANDED, int RB>
 static hipError_t launch_dense64_b(int phase, const CellArgs& a, hipStream_t st) {
     const size_t lds = D64Lds<CELL>::floats(a.m) * sizeof(float);
     const dim3 grid(a.NC, a.B);
-    if (phase == kPrologue) dense64_pass<CELL, kPrologue, BANDED><<<grid, 64, lds, st>>>(a);
-    else if (phase == kFirst) dense64_pass<CELL, kFirst, BANDED><<<grid, 64, lds, st>>>(a);
-    else if (phase == kMaps) dense64_pass<CELL, kMaps, BANDED><<<grid, 64, lds, st>>>(a);
-    else return launch_maybe_timed(dense64_pass<CELL, kSteady, BANDED>, grid, dim3(64), lds, st, a);
+    if (phase == kPrologue) dense64_pass<CELL, kPrologue, BANDED, RB><<<grid, 64, lds, st>>>(a);
+    else if (phase == kFirst) dense64_pass<CELL, kFirst, BANDED, RB><<<grid, 64, lds, st>>>(a);
+    else if (phase == kMaps) dense64_pass<CELL, kMaps, BANDED, RB><<<grid, 64, lds, st>>>(a);
+    else return launch_maybe_timed(dense64_pass<CELL, kSteady, BANDED, RB>, grid, dim3(64), lds, st, a);
     return hipGetLastError();
 }
 
+// band < D - 1 selects the masked Jacobian weights; a band of at most
+// kRowBand diagonals each side extends the chunk map on the vector ALUs.
+constexpr int kRowBand = 2;
+
 template <int CELL>
 static hipError_t launch_dense64(int phase, const CellArgs& a, hipStream_t st) {
-    return a.band < a.D - 1 ? launch_dense64_b<CELL, true>(phase, a, st)
-                            : launch_dense64_b<CELL, false>(phase, a, st);
+    if (a.band >= a.D - 1) return launch_dense64_b<CELL, false, 0>(phase, a, st);
+    return a.band <= kRowBand ? launch_dense64_b<CELL, true, kRowBand>(phase, a, st)
+                              : launch_dense64_b<CELL, true, 0>(phase, a, st);
 }
 
 template <int CELL, int DP, bool BANDED, bool SPLIT>
