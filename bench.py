@@ -231,6 +231,36 @@ def ceilings(reps=10):
     return out
 
 
+def sequential_gpu(params, x, s0, out_solve, solve_ms, reps=10):
+    """The plain time loop of the channel-wise cell on the same GPU and the
+    same inputs (libpn_ceiling.so, pnc_sequential_tanh: one thread per (b, d)
+    walking t in order): the GPU baseline of the parallel-in-time solve, with
+    its largest difference from the solve's trajectory."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "newton_evaluation_nonlinear_amd", "libpn_ceiling.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build with `python -m newton_evaluation_nonlinear_amd._build`")
+    L = ctypes.CDLL(path)
+    vp, dbl = ctypes.c_void_p, ctypes.c_double
+    L.pnc_sequential_tanh.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.POINTER(dbl), ctypes.POINTER(dbl)]
+    L.pnc_last_error.restype = ctypes.c_char_p
+    B, T, D = out_solve.shape
+    seq = torch.empty_like(out_solve)
+    torch.cuda.synchronize()
+    best, med = dbl(0.0), dbl(0.0)
+    if L.pnc_sequential_tanh(x.data_ptr(), params.data_ptr(), s0.data_ptr(), seq.data_ptr(), B, T, D, reps,
+                             ctypes.byref(best), ctypes.byref(med)) != 0:
+        raise SystemExit("sequential GPU loop failed: " + L.pnc_last_error().decode())
+    diff = float((seq - out_solve).abs().max())
+    return {"kernel": "time loop in order, one thread per (b, d) (pnc_sequential_tanh)",
+            "ms": med.value, "best_ms": best.value,
+            "state_updates_per_s": B * T * D / (med.value * 1e-3),
+            "solve_ms": solve_ms, "solve_speedup_over_loop": med.value / solve_ms,
+            "max_abs_diff_vs_solve": diff}
+
+
 COPY_PROBE_BYTES = 64 * 1024 * 1024 * 4   # read once and written once by the probe copy
 
 
@@ -518,6 +548,8 @@ def main():
             c = ceil["mfma_f32_tflops"]["median"]
             roof.update(measured_ceiling={"pattern": "mfma_f32", "value": c, "unit": "TFLOP/s"},
                         frac_of_measured_ceiling=roof["achieved"] / c)
+    if not args.no_ceiling and wl["cell"] == 0 and not half and not wmode and wl["window"] == 0:
+        line["sequential_gpu"] = sequential_gpu(params, x, s0, out, ms)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.config, mode, smode, args.switch_ratio,
                                             "f16" if half else None)

@@ -45,6 +45,17 @@ int pnc_hbm(int pattern, size_t bytes, int reps, double* best_gbs, double* media
  * v_mfma_f32_32x32x2f32 on register operands, two wavefronts per SIMD. */
 int pnc_mfma_f32(int reps, double* best_tflops, double* median_tflops);
 
+/* The plain time loop of the channel-wise cell on the GPU, the baseline a
+ * parallel-in-time solve has to beat: s_t = tanh(a[d] s_{t-1} + x[b,t,d])
+ * for t = 1..T from s_0 = s0[b,d], one thread per (b, d), in time order.
+ * x [B,T,D], a [D], s0 [B,D] and out [B,T,D] (receives s_1..s_T) are
+ * caller-owned float32 device arrays.  Runs one untimed and `reps` timed
+ * launches on a stream of its own; best and median milliseconds per launch.
+ * Returns 0, or -1 (bad argument: null pointer, a size below 1, B > 65535,
+ * reps < 1; or a HIP failure) with a message in pnc_last_error(). */
+int pnc_sequential_tanh(const float* x, const float* a, const float* s0, float* out, int B, int T, int D,
+                        int reps, double* best_ms, double* median_ms);
+
 /* Message of the last failure on this thread ("" if none). */
 const char* pnc_last_error(void);
 

@@ -18,6 +18,11 @@
 //                  order, 16 rows in flight while the previous 16 are summed [n]
 // The MFMA loop runs independent chains of v_mfma_f32_32x32x2f32 on register
 // operands (4096 flops each) on every SIMD.
+//
+// The sequential reference is the plain time loop of the channel-wise cell
+// s_t = tanh(a s_{t-1} + x_t): one thread per (batch row, channel) walks
+// t = 1..T in order, the loads 16 steps ahead of use.  It is the GPU baseline
+// that a parallel-in-time solve of the same recurrence has to beat.
 
 #include <hip/hip_runtime.h>
 
@@ -129,6 +134,42 @@ __global__ __launch_bounds__(kThreads) void k_read_rows(const float* __restrict_
         for (int u = 0; u < kReadPre; ++u) acc += xb[u];
     }
     out[(static_cast<size_t>(b) * gridDim.x + c) * kThreads + d] = acc;
+}
+
+// tanh(u) = 1 - 2 / (e^{2u} + 1), e^{2u} as exp2 of 2u log2(e)
+__device__ __forceinline__ float seq_tanh(float u) {
+    return 1.0f - 2.0f * __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(u * 2.88539008177792681472f) + 1.0f);
+}
+
+constexpr int kSeqPre = 16;
+
+__global__ __launch_bounds__(64) void k_seq_tanh(const float* __restrict__ x, const float* __restrict__ a,
+                                                 const float* __restrict__ s0, float* __restrict__ out, int T, int D) {
+    const int d = blockIdx.x * 64 + threadIdx.x, b = blockIdx.y;
+    if (d >= D) return;
+    const float ad = a[d];
+    float st = s0[static_cast<size_t>(b) * D + d];
+    const float* xp = x + static_cast<size_t>(b) * T * D + d;
+    float* op = out + static_cast<size_t>(b) * T * D + d;
+    float xa[kSeqPre], xb[kSeqPre];
+#pragma unroll
+    for (int u = 0; u < kSeqPre; ++u) xa[u] = u < T ? xp[static_cast<size_t>(u) * D] : 0.0f;
+    for (int t = 0; t < T; t += kSeqPre) {
+#pragma unroll
+        for (int u = 0; u < kSeqPre; ++u) {
+            const int r = t + kSeqPre + u;
+            xb[u] = r < T ? xp[static_cast<size_t>(r) * D] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kSeqPre; ++u) {
+            if (t + u < T) {
+                st = seq_tanh(ad * st + xa[u]);
+                op[static_cast<size_t>(t + u) * D] = st;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kSeqPre; ++u) xa[u] = xb[u];
+    }
 }
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -274,6 +315,28 @@ int pnc_mfma_f32(int reps, double* best_tflops, double* median_tflops) {
     if (rc != 0) return rc;
     const double flops = static_cast<double>(grid) * (kThreads / 64) * iters * kMfmaChains * 4096.0;
     best_median(ms, flops / 1e12, best_tflops, median_tflops);
+    return 0;
+}
+
+int pnc_sequential_tanh(const float* x, const float* a, const float* s0, float* out, int B, int T, int D, int reps,
+                        double* best_ms, double* median_ms) {
+    g_err.clear();
+    if (!x || !a || !s0 || !out || !best_ms || !median_ms || B < 1 || T < 1 || D < 1 || reps < 1 ||
+        B > 65535) {
+        g_err = "bad argument";
+        return -1;
+    }
+    hipStream_t st;
+    PNC_HIP(hipStreamCreate(&st));
+    std::vector<float> ms;
+    const dim3 grid((D + 63) / 64, B);
+    const int rc = timed(st, reps, [&] { k_seq_tanh<<<grid, 64, 0, st>>>(x, a, s0, out, T, D); }, &ms);
+    (void)hipStreamSynchronize(st);
+    (void)hipStreamDestroy(st);
+    if (rc != 0) return rc;
+    std::sort(ms.begin(), ms.end());
+    *best_ms = ms.front();
+    *median_ms = ms[ms.size() / 2];
     return 0;
 }
 

@@ -267,7 +267,7 @@ def test_ceiling_tool_exports_every_declared_symbol():
     text = open(os.path.join(ROOT, "include", "pn_ceiling.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(pnc_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["pnc_hbm", "pnc_last_error", "pnc_mfma_f32"]
+    assert names == ["pnc_hbm", "pnc_last_error", "pnc_mfma_f32", "pnc_sequential_tanh"]
     lib = ctypes.CDLL(os.path.join(ROOT, "newton_evaluation_nonlinear_amd", "libpn_ceiling.so"))
     for name in names:
         assert hasattr(lib, name), name
@@ -277,4 +277,9 @@ def test_ceiling_tool_exports_every_declared_symbol():
                             ctypes.POINTER(ctypes.c_double)]
     lib.pnc_last_error.restype = ctypes.c_char_p
     assert lib.pnc_hbm(9, 1 << 20, 1, ctypes.byref(d), ctypes.byref(d)) == -1
+    assert lib.pnc_last_error().decode() == "bad argument"
+    vp = ctypes.c_void_p
+    lib.pnc_sequential_tanh.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    assert lib.pnc_sequential_tanh(None, None, None, None, 1, 1, 1, 1, ctypes.byref(d), ctypes.byref(d)) == -1
     assert lib.pnc_last_error().decode() == "bad argument"

@@ -132,3 +132,33 @@ def test_binding_rejects_bad_arguments_before_any_launch():
         pn.eval(pn.CELL_DIAG_TANH, torch.full((D,), 0.5, device=dev), xd, s0, out=xd)
     assert e.value.code == pn.EINVAL and "overlaps x" in str(e.value)
     torch.cuda.synchronize()
+
+
+def test_sequential_gpu_loop_matches_the_oracle_time_loop():
+    # The GPU baseline the bench sets beside the solve (pnc_sequential_tanh in
+    # libpn_ceiling.so): the plain time loop of the channel-wise cell, against
+    # the oracle's float64 time loop; D = 70 leaves a ragged channel block and
+    # T = 1000 a ragged prefetch group.
+    import os
+    wl = workloads.make(3, B=2, T=1000)
+    wl["params"] = wl["params"][:70].copy()
+    wl["x"] = np.ascontiguousarray(wl["x"][:, :, :70])
+    wl["s0"] = (0.3 * np.random.default_rng(7).standard_normal((2, 70))).astype(np.float32)
+    B, T, D = 2, 1000, 70
+    dev = torch.device("cuda:0")
+    a, x, s0 = (torch.from_numpy(wl[k]).to(dev) for k in ("params", "x", "s0"))
+    out = torch.full((B, T, D), float("nan"), device=dev)
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(pn.__file__), "libpn_ceiling.so"))
+    vp, dbl = ctypes.c_void_p, ctypes.c_double
+    lib.pnc_sequential_tanh.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.POINTER(dbl), ctypes.POINTER(dbl)]
+    best, med = dbl(0.0), dbl(0.0)
+    print(f"[pnc_sequential_tanh] B={B} T={T} D={D}", flush=True)
+    assert lib.pnc_sequential_tanh(x.data_ptr(), a.data_ptr(), s0.data_ptr(), out.data_ptr(), B, T, D, 2,
+                                   ctypes.byref(best), ctypes.byref(med)) == 0
+    torch.cuda.synchronize()
+    cell = oracle.make_cell(oracle.CELL_DIAG_TANH, wl["params"].astype(np.float64), D, D)
+    ref = oracle.sequential(cell, wl["x"].astype(np.float64), wl["s0"].astype(np.float64))
+    err = float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref)))
+    assert err <= 1e-5, err
+    assert 0.0 < best.value <= med.value
