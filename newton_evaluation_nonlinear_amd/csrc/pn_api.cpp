@@ -81,19 +81,29 @@ struct Plan {
                            // when all B x NC chunks fit on the device at once
     bool adv_resident_ok;  // advancing window with a one-launch resident form
                            // (cell_resident_adv), used when its chunks fit at once
-    bool recompute;        // channel-wise cell, float storage: first update stores nothing,
-                           // the second recomputes s^(1) (kFirstNS, kSecondR)
+    bool recompute;        // channel-wise cell, float storage: the first kRecomputeDepth
+                           // updates store nothing, the next recomputes s^(1) .. s^(i)
+                           // (kFirstNS, kSecondNS, kThirdNS, kFourthR)
     int fc;                // matrix cell, diagonal mode, few chunks (CellArgs::fc): the apply
                            // sweeps compose their own carries (kFcCarry) and, with
                            // consecutive windows, take their own check (kFcCheck)
     int nblocks, nwin, hist_cap;
-    size_t off_ctrl, off_rpart, off_fpart, off_aggA, off_aggB, off_carry, off_carry0, off_halo, off_w,
+    size_t off_ctrl, off_rpart, off_fpart, off_aggA, off_aggB, off_carry, off_carryr, off_halo, off_w,
         total;
     size_t off_sync, off_winfo, off_hist, off_acc, off_info_end;
     size_t off_lag;        // resident solver: residual words, ready words, window-state words
 };
 
 void layout(Plan& p, const Plan* other);
+
+// The channel-wise cell with float storage: updates 1 .. kRecomputeDepth read
+// only x and store nothing, and update kRecomputeDepth + 1 recomputes the
+// iterates s^(1) .. s^(kRecomputeDepth) from the carries of their iterations
+// before its own replay; kNoStorePass[l] and kStorePass[l] are the passes of
+// update l + 1 that recompute l iterates.
+constexpr int kRecomputeDepth = 3;
+constexpr int kNoStorePass[3] = {kFirstNS, kSecondNS, kThirdNS};
+constexpr int kStorePass[4] = {kFirst, kSecondR, kThirdR, kFourthR};
 
 int make_plan(Plan& p, const pn_cell* cell, int64_t B, int64_t T, int64_t D, int32_t mode,
               const pn_opts* o, bool half = false) {
@@ -255,8 +265,8 @@ void layout(Plan& p, const Plan* other) {
     p.off_aggA = off; off = align_up(off + sizeof(float) * nA * nsets);
     p.off_aggB = off; off = align_up(off + sizeof(float) * bnd * nsets);
     p.off_carry = off; off = align_up(off + sizeof(float) * bnd);
-    p.off_carry0 = off;
-    if (p.recompute || (other && other->recompute)) off = align_up(off + sizeof(float) * bnd);
+    p.off_carryr = off;     // the carries of iterations 0 .. kRecomputeDepth - 1
+    if (p.recompute || (other && other->recompute)) off = align_up(off + sizeof(float) * bnd * kRecomputeDepth);
     p.off_halo = off; off = align_up(off + sizeof(float) * (p.resident_ok ? 3 : 2) * bnd);
     p.off_w = off;
     if (p.matrix_cell) off = align_up(off + sizeof(float) * prepared_total_floats(p.kind, p.DP, p.m));
@@ -590,14 +600,20 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
     float* aggA = reinterpret_cast<float*>(c.ws + pp->off_aggA);
     float* aggB = reinterpret_cast<float*>(c.ws + pp->off_aggB);
     float* carry = reinterpret_cast<float*>(c.ws + pp->off_carry);
-    float* carry0 = reinterpret_cast<float*>(c.ws + pp->off_carry0);
+    // carries of iterations 0 .. kRecomputeDepth - 1 (recomputing passes)
+    float* carryr[kRecomputeDepth];
+    for (int l = 0; l < kRecomputeDepth; ++l)
+        carryr[l] = reinterpret_cast<float*>(c.ws + pp->off_carryr) +
+                    static_cast<size_t>(l) * pp->B * pp->NC * pp->D;
     float* halo = reinterpret_cast<float*>(c.ws + pp->off_halo);
     const float* w = reinterpret_cast<const float*>(c.ws + pp->off_w);
     uint32_t* fpart = reinterpret_cast<uint32_t*>(c.ws + pp->off_fpart);
     float lam = c.lam;       // step damping of the updates still to be enqueued
-    // the first two updates of the channel-wise cell move less (kFirstNS,
-    // kSecondR): iteration 0's carries go to their own buffer
+    // the first kRecomputeDepth + 1 updates of the channel-wise cell move
+    // less: the carries of iterations 0 .. kRecomputeDepth - 1 go to buffers
+    // of their own
     const bool recompute = pp->recompute && !p2;
+    constexpr int RD = kRecomputeDepth;
 
     DiagArgs da{};
     CellArgs ca{};
@@ -614,7 +630,8 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
             da = DiagArgs{};
             da.a = c.params; da.x = x; da.xs = xs; da.s = s; da.ss = ss; da.s0 = s0; da.s0s = s0s;
             da.B = p.B; da.Tw = Tw; da.D = p.D; da.L = p.L; da.NC = NC; da.cpb = p.cpb;
-            da.aggA = aggA; da.aggB = aggB; da.carry = carry; da.carry0 = carry0; da.halo = halo;
+            da.aggA = aggA; da.aggB = aggB; da.carry = carry; da.halo = halo;
+            for (int l = 0; l < RD; ++l) da.carryr[l] = carryr[l];
             da.rpart = rpart;
             da.ctrl = ctrl; da.mode = p.mode; da.lam = lam; da.undamped = lam == 1.0f;
             da.half = p.hmode;
@@ -665,9 +682,9 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
     ca.epoch = epoch;
     for (int k = 0; k < kHostRing; ++k) ring[k].iter = -1;
     float r_prev = 0.0f;
-    // Chunking of the channel-wise launches with the recomputing pair: the
-    // prologue and updates 1 and 2 run on chunks of L, the later updates on
-    // chunks of Lc (a multiple of L); the first of them reads the carries
+    // Chunking of the channel-wise launches with the recomputing passes: the
+    // prologue and updates 1 to RD + 1 run on chunks of L, the later updates
+    // on chunks of Lc (a multiple of L); the first of them reads the carries
     // and the halo of the fine chunking at chunk c * Lc / L.
     const int NCf = (Tw + pp->L - 1) / pp->L;
     const int NCc = (Tw + pp->Lc - 1) / pp->Lc;
@@ -686,9 +703,13 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
     const int ahead = (pp->fc & kFcCheck) ? ((pp->fc & kFcCarry) ? 2 : 1) : 0;
     std::vector<int> tslot;      // launch k -> its timing entry, or -1
     auto enqueue_apply = [&](int k) -> int {
-        const int phase = k == 0 ? (recompute ? kFirstNS : kFirst)
-                                 : (recompute && k == 1 ? kSecondR : kSteady);
-        if (recompute) grain(k >= 2, k == 2 ? pp->Lc / pp->L : 1);
+        // recomputing: updates 1 .. RD store nothing, update RD + 1
+        // recomputes s^(1) .. s^(RD) and stores s^(RD + 1)
+        const int phase = !recompute ? (k == 0 ? kFirst : kSteady)
+                          : k < RD   ? kNoStorePass[k]
+                          : k == RD  ? kStorePass[RD]
+                                     : kSteady;
+        if (recompute) grain(k >= RD + 1, k == RD + 1 ? pp->Lc / pp->L : 1);
         // timing covers the steady-state apply launches, including the
         // final ones that exit at once
         if ((pp->fc & kFcCheck) && !(pp->fc & kFcCarry))
@@ -717,11 +738,11 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
         volatile HostRec* hr = ring + i % kHostRing;
         cy.chk.iter = i;
         cy.chk.host = c.res->host_dev + i % kHostRing;
-        cy.carry = (recompute && i == 0) ? carry0 : carry;
+        cy.carry = (recompute && i < RD) ? carryr[i] : carry;
         da.carry = cy.carry;
         if (recompute) {
             // the carry scans the maps of the launch before: apply(i-1), or the prologue
-            grain(i >= 3, 1);
+            grain(i >= RD + 2, 1);
             cy.NC = da.NC;
             cy.chk.nparts = diag_tanh_nblocks(da);
         }
@@ -751,12 +772,13 @@ int solve_window(SolveCtx& c, const float* x, int64_t xs, float* s, int64_t ss, 
         if (stop) {
             *K = i;
             *status = st;
-            if (recompute && i == 1) {
-                // the result is s^(1), which the first update did not store
+            if (recompute && i >= 1 && i <= RD) {
+                // the result is s^(i), which update i did not store: update i
+                // again, the form that stores (its iteration is i - 1)
                 grain(false, 1);
-                da.carry = carry0;
+                da.carry = carryr[i - 1];
                 da.force = 1;
-                PN_HIP(launch_pass(kFirst, 0));
+                PN_HIP(launch_pass(kStorePass[i - 1], i - 1));
                 da.force = 0;
             }
             break;

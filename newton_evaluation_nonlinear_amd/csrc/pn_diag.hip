@@ -110,6 +110,14 @@ template <typename V> struct Rows {
     }
 };
 
+// The damped update s + lam (shat - s) as stored (shat itself when
+// undamped): one expression for every pass, so that a recomputed iterate
+// equals the stored one bit for bit.
+template <typename S, bool UND>
+__device__ __forceinline__ float damp(float s, float shat, float lam) {
+    return stored<S>(UND ? shat : s + lam * (shat - s));
+}
+
 // TRACK: also reduce the first step whose residual exceeds tol (the
 // advancing window); compiled out otherwise.
 template <int MODE, int PHASE, typename S, int NCH, bool UND, bool TRACK = false>
@@ -118,9 +126,12 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
         if (g.ctrl->stop && !g.force) return;    // uniform over the grid: converged earlier
     }
     // which passes start from s0, read the stored iterate, recompute s^(1)
+    // (and s^(2)), store nothing
     constexpr bool kFromS0 = PHASE == kFirst || PHASE == kFirstNS;
     constexpr bool kReadS = PHASE == kSteady;
-    constexpr bool kRecompute = PHASE == kSecondR;
+    constexpr int NR = recompute_depth(PHASE);
+    constexpr bool kRecompute = NR > 0;
+    constexpr bool kNoStore = PHASE == kFirstNS || PHASE == kSecondNS || PHASE == kThirdNS;
     typedef typename Pack<S, NCH>::V V;
     const int cpb = g.cpb;                           // channel groups per block row
     const int dl = threadIdx.x % cpb;
@@ -267,20 +278,29 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
             // p_old: s^(i) at t0-1 (halo of the previous chunk);  shat: s^ at t0-1;
             // snp: s^(i+1) at t0-1, exactly as the previous chunk stores it.
             float p_old[NCH], shat[NCH], shat_end[NCH], snp[NCH];
-            // kSecondR: s^ of iteration 0 entering this chunk and the next one
-            float sh0[NCH], sh0_end[NCH];
+            // recomputing passes, level l < NR replays iteration l: sh[l] is
+            // its s^ entering this chunk (and sh_end[l] the next one), pr[l]
+            // holds s^(l)_{t-1} (level 0 has p = s0 throughout)
+            constexpr int NRA = NR > 0 ? NR : 1;
+            float sh[NRA][NCH], sh_end[NRA][NCH], pr[NRA][NCH];
 #pragma unroll
             for (int k = 0; k < NCH; ++k) {
-                p_old[k] = (kFromS0 || c == 0) ? s0v[k] : g.halo[(g.iter & 1) * HS + ri - D + k];
                 shat[k] = g.carry[ri + k];
                 shat_end[k] = has_next ? g.carry[ri + static_cast<size_t>(g.rf) * D + k] : 0.0f;
-                snp[k] = stored<S>(UND ? shat[k] : p_old[k] + lam * (shat[k] - p_old[k]));
-                if constexpr (kRecompute) {
-                    sh0[k] = g.carry0[ri + k];
-                    sh0_end[k] = has_next ? g.carry0[ri + static_cast<size_t>(g.rf) * D + k] : 0.0f;
-                } else {
-                    sh0[k] = sh0_end[k] = 0.0f;
+                float q = s0v[k];       // s^(l)_{t0-1}, from the carries as the previous chunk produced it
+#pragma unroll
+                for (int l = 0; l < NRA; ++l) {
+                    sh[l][k] = sh_end[l][k] = 0.0f;
+                    pr[l][k] = q;
+                    if (l < NR) {
+                        sh[l][k] = g.carryr[l][ri + k];
+                        sh_end[l][k] = has_next ? g.carryr[l][ri + static_cast<size_t>(g.rf) * D + k] : 0.0f;
+                        q = c == 0 ? s0v[k] : damp<S, UND>(q, sh[l][k], lam);
+                    }
                 }
+                if constexpr (kRecompute) p_old[k] = q;
+                else p_old[k] = (kFromS0 || c == 0) ? s0v[k] : g.halo[(g.iter & 1) * HS + ri - D + k];
+                snp[k] = damp<S, UND>(p_old[k], shat[k], lam);
             }
             // float passes that read only x prefetch as deep as the prologue
             // (binary16 sweeps are bound by their vector instructions)
@@ -312,14 +332,23 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
 #pragma unroll
                             for (int k = 0; k < NCH; ++k) so[k] = s0v[k];
                         } else if constexpr (kRecompute) {
-                            // s^(1)_t again: iteration 0's replay, p = s0 throughout
+                            // s^(1)_t .. s^(NR)_t again: iteration l's replay at
+                            // p = s^(l)_{t-1} (s0 for l = 0) gives s^(l+1)_t
 #pragma unroll
                             for (int k = 0; k < NCH; ++k) {
-                                const float v0 = tanh_f(a[k] * s0v[k] + xt[k]);
-                                const float a0 = mode_coef<MODE>(a[k] * (1.0f - v0 * v0));
-                                sh0[k] = v0 + a0 * (sh0[k] - s0v[k]);
-                                if (last) sh0[k] = sh0_end[k];
-                                so[k] = stored<S>(UND ? sh0[k] : s0v[k] + lam * (sh0[k] - s0v[k]));
+                                float cur = s0v[k];          // s^(l)_t
+#pragma unroll
+                                for (int l = 0; l < NR; ++l) {
+                                    const float p = l == 0 ? s0v[k] : pr[l][k];
+                                    const float vl = tanh_f(a[k] * p + xt[k]);
+                                    const float al = mode_coef<MODE>(a[k] * (1.0f - vl * vl));
+                                    sh[l][k] = vl + al * (sh[l][k] - p);
+                                    if (last) sh[l][k] = sh_end[l][k];
+                                    const float nxt = damp<S, UND>(cur, sh[l][k], lam);
+                                    pr[l][k] = cur;
+                                    cur = nxt;
+                                }
+                                so[k] = cur;
                             }
                         } else {
                             unpack<S, NCH>(sb[u], so);
@@ -331,9 +360,9 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
                             const float at = mode_coef<MODE>(a[k] * (1.0f - v * v));
                             shat[k] = v + at * (shat[k] - p_old[k]);
                             if (last) shat[k] = shat_end[k];
-                            sn[k] = UND ? shat[k] : so[k] + lam * (shat[k] - so[k]);
+                            sn[k] = damp<S, UND>(so[k], shat[k], lam);
                         }
-                        if constexpr (PHASE == kFirstNS) {
+                        if constexpr (kNoStore) {
 #pragma unroll
                             for (int k = 0; k < NCH; ++k) sn[k] = stored<S>(sn[k]);
                         } else {
@@ -423,6 +452,10 @@ static hipError_t launch_und(int phase, const DiagArgs& a, hipStream_t st) {
         else if (phase == kMaps) diag_tanh_pass<MODE, kMaps, S, NCH, UND, true><<<grid, kThreads, 0, st>>>(a);
         else if (phase == kFirstNS) diag_tanh_pass<MODE, kFirstNS, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
         else if (phase == kSecondR) diag_tanh_pass<MODE, kSecondR, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
+        else if (phase == kSecondNS) diag_tanh_pass<MODE, kSecondNS, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
+        else if (phase == kThirdR) diag_tanh_pass<MODE, kThirdR, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
+        else if (phase == kThirdNS) diag_tanh_pass<MODE, kThirdNS, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
+        else if (phase == kFourthR) diag_tanh_pass<MODE, kFourthR, S, NCH, UND><<<grid, kThreads, 0, st>>>(a);
         else return hipErrorInvalidValue;
     } else {
         return hipErrorInvalidValue;

@@ -73,7 +73,7 @@ struct DiagArgs {
     float* aggA;             // [B][NC][D]
     float* aggB;             // [B][NC][D]
     const float* carry;      // [B][NC][D]
-    const float* carry0;     // [B][NC][D] carries of iteration 0 (kSecondR)
+    const float* carryr[3];  // [B][NC][D] carries of iterations 0, 1, 2 (the recomputing passes)
     float* halo;             // [2][B][NC][D]
     uint32_t* rpart;         // one slot per workgroup
     const Ctrl* ctrl;
@@ -158,10 +158,19 @@ struct CarryArgs {
 // kPrologue: iteration-0 chunk maps at s^(0) = s0 (implicit);  kFirst /
 // kSteady: apply for i = 0 / i >= 1;  kMaps: chunk maps, residual and halo
 // of the iterate stored in s (the advancing window, after it slides).
-// Channel-wise cell only: kFirstNS is kFirst without the store of s^(1), and
-// kSecondR the apply for i = 1 that recomputes s^(1) from the carries of
-// iteration 0 instead of reading it (see pn_diag.hip).
-enum Phase { kPrologue = 0, kFirst = 1, kSteady = 2, kMaps = 3, kFirstNS = 4, kSecondR = 5 };
+// Channel-wise cell only, the recomputing passes: the apply for i = 1, 2, 3
+// that recomputes s^(1) .. s^(i) from the carries of iterations 0 .. i-1
+// instead of reading s^(i) (kSecondR, kThirdR, kFourthR), and the passes
+// that store nothing: kFirstNS (kFirst without the store of s^(1)), kSecondNS
+// and kThirdNS (see pn_diag.hip).
+enum Phase { kPrologue = 0, kFirst = 1, kSteady = 2, kMaps = 3, kFirstNS = 4, kSecondR = 5, kSecondNS = 6,
+             kThirdR = 7, kThirdNS = 8, kFourthR = 9 };
+
+// iterates a pass recomputes (0 for the passes that start from s0 or read s^(i))
+__host__ __device__ constexpr int recompute_depth(int phase) {
+    return phase == kSecondR || phase == kSecondNS ? 1 : phase == kThirdR || phase == kThirdNS ? 2
+                                                       : phase == kFourthR ? 3 : 0;
+}
 
 // Timing request for the next steady apply launch of this thread: the
 // launcher records these events around the kernel itself and clears them.

@@ -154,6 +154,30 @@ def test_diag_tanh_odd_width_and_damping():
     _parity(wl, J)
 
 
+@pytest.mark.parametrize("damping", [1.0, 0.7])
+def test_diag_tanh_every_stopping_point(damping):
+    # The channel-wise cell's first updates store nothing (updates 1 and 2)
+    # or recompute the earlier iterates from their carries (updates 2 and 3),
+    # and a stop right after update 1 or 2 stores the iterate by one more
+    # sweep.  Stop after each of updates 0..5 (tol 0, max_iter k) and compare
+    # the returned iterate with the oracle's s^(k).  D = 70 and T = 3000 give
+    # 16-step chunks with a ragged tail and steady chunks twice as long.
+    rng = np.random.default_rng(11)
+    D, B, T = 70, 2, 3000
+    wl = dict(cfg=0, cell=pn.CELL_DIAG_TANH, D=D, m=D, B=B, T=T, tol=1e-6, damping=damping, window=0,
+              max_iter=T, params=rng.uniform(-0.95, 0.95, D).astype(np.float32),
+              x=rng.standard_normal((B, T, D)).astype(np.float32),
+              s0=(0.3 * rng.standard_normal((B, D))).astype(np.float32))
+    for mode in (Q, J):
+        for mi in range(6):
+            gpu = run_gpu(wl, mode, max_iter=mi, tol=0.0)
+            ref = run_oracle(wl, mode, max_iter=mi, tol=0.0)
+            assert gpu.status == ref.status == oracle.NOT_CONVERGED, (mode, mi)
+            assert gpu.iters == ref.iters == mi, (mode, mi)
+            err = float(np.max(np.abs(gpu.out_np - ref.s)))
+            assert err <= 1e-4 * max(1.0, float(np.max(np.abs(ref.s)))), (mode, mi, err)
+
+
 @pytest.mark.parametrize("flags", [0, pn.FLAG_MULTI_LAUNCH])
 def test_cfg1_newton_full(flags):
     # one workgroup (default) and the launch-per-phase driver
