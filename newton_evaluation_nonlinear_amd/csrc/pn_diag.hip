@@ -12,13 +12,15 @@
 //            iterate: residual |s_t - f_t(s_{t-1})| and the chunk's next map.
 // The apply sweep therefore moves exactly x, s^(i) in and s^(i+1) out, and
 // the following carry only touches the chunk maps.
-// With float storage the first two updates move less: s^(0) = s0 is known
-// everywhere, so the first update (kFirstNS) stores no s^(1), and the second
-// (kSecondR) replays iteration 0 again from its carries, which yields s^(1)
-// bit for bit, before replaying iteration 1 and storing s^(2).  The second
-// update then reads x only (8 bytes per element instead of 12, and 4 instead
-// of 8 for the first) at the price of one more tanh per element; if the
-// loop stops right after the first update, a kFirst launch stores s^(1).
+// With float storage the first four updates move less: s^(0) = s0 is known
+// everywhere, and s^(l) follows bit for bit from x, s0 and the carries of
+// iterations 0 .. l-1 (replaying iteration l from its carry gives s^(l+1)).
+// So updates 1 .. 3 (kFirstNS, kSecondNS, kThirdNS) read only x and store
+// nothing, update l + 1 recomputing s^(1) .. s^(l) on the way (one more tanh
+// per element and level), and update 4 (kFourthR) recomputes s^(1) .. s^(3)
+// and stores s^(4): 4, 4, 4 and 8 bytes per element instead of 12.  If the
+// loop stops right after update l <= 3, the form of update l that stores
+// (kFirst, kSecondR, kThirdR) runs once more to write s^(l).
 //
 // Layout: lanes run along channels (row-contiguous in [B, T, D]); each thread
 // walks the L steps of its chunk serially, so loads are fully coalesced rows
@@ -125,8 +127,8 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
     if constexpr (PHASE != kPrologue && PHASE != kMaps) {
         if (g.ctrl->stop && !g.force) return;    // uniform over the grid: converged earlier
     }
-    // which passes start from s0, read the stored iterate, recompute s^(1)
-    // (and s^(2)), store nothing
+    // which passes start from s0, read the stored iterate, recompute
+    // s^(1) .. s^(NR), store nothing
     constexpr bool kFromS0 = PHASE == kFirst || PHASE == kFirstNS;
     constexpr bool kReadS = PHASE == kSteady;
     constexpr int NR = recompute_depth(PHASE);
