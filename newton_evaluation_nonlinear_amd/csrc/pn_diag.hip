@@ -499,7 +499,12 @@ constexpr int kChan = 64;         // channels per workgroup (one wave wide)
 constexpr int kPer = 16;          // chunks per segment held in registers
 
 __global__ __launch_bounds__(kSeg * kChan) void diag_carry_kernel(CarryArgs g) {
-    if (g.do_check && blockIdx.x == 0 && blockIdx.y == 0) run_check(g.chk);
+    // With the check, one more column of workgroups: its first one takes the
+    // check beside the carries instead of before a share of them.
+    if (g.do_check && blockIdx.x == gridDim.x - 1) {
+        if (blockIdx.y == 0) run_check(g.chk);
+        return;
+    }
     __shared__ float segA[kSeg][kChan];
     __shared__ float segB[kSeg][kChan];
     const int dl = threadIdx.x % kChan;
@@ -561,7 +566,7 @@ __global__ __launch_bounds__(kSeg * kChan) void diag_carry_kernel(CarryArgs g) {
 }
 
 hipError_t launch_diag_carry(const CarryArgs& a, hipStream_t st) {
-    const dim3 grid((a.D + kChan - 1) / kChan, a.B);
+    const dim3 grid((a.D + kChan - 1) / kChan + (a.do_check ? 1 : 0), a.B);
     diag_carry_kernel<<<grid, kSeg * kChan, 0, st>>>(a);
     return hipGetLastError();
 }
