@@ -90,6 +90,8 @@ __device__ __forceinline__ float stored(float v) {
 // byte offset the vector one, so addressing costs no vector instruction.
 // Offsets stay below 2^31 (the planner bounds chunk rows x row bytes); the
 // callers' row tests keep every access inside the chunk.
+// The resource is a raw buffer (stride 0) whose range (2^31 - 1 bytes) never
+// clips an access here; its last word is the gfx9 format word for 32-bit data.
 template <typename V> struct Rows {
     __amdgpu_buffer_rsrc_t rsrc;
     uint32_t lo;     // lane offset in bytes
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void diag_tanh_pass(DiagArgs g) {
             // (binary16 sweeps are bound by their vector instructions)
             constexpr int U = (kReadS || !std::is_same<S, float>::value) ? kU : kUP;
             // rows of the iterate in this chunk (read in kSteady, written
-            // unless kFirstNS), addressed like xr
+            // except by the passes that store nothing), addressed like xr
             const Rows<V> sr(reinterpret_cast<const S*>(g.s) + b * g.ss + static_cast<int64_t>(t0) * D + dw, lo,
                              xr.rs);
             // group(j): issue the loads of rows j+U.. into xn/sn_, then take
