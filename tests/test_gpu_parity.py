@@ -178,6 +178,24 @@ def test_diag_tanh_every_stopping_point(damping):
             assert err <= 1e-4 * max(1.0, float(np.max(np.abs(ref.s)))), (mode, mi, err)
 
 
+@pytest.mark.slow
+def test_diag_tanh_stopping_points_on_long_chunks():
+    # The same stopping points where the chunks are long enough for the
+    # sweeps' unguarded prefetch groups (B = 2, T = 32768, D = 256 plan
+    # 64-step chunks, 128-step steady ones): the recomputing passes, the
+    # stores after a stop at updates 1 .. 3 and the fourth update's own store
+    # run their whole-group loops; undamped and damped.
+    wl = _case(3, B=2, T=32768)
+    for damping, stops in ((1.0, (1, 2, 3, 4)), (0.7, (2, 3))):
+        for mi in stops:
+            gpu = run_gpu(wl, Q, max_iter=mi, tol=0.0, damping=damping)
+            ref = run_oracle(wl, Q, max_iter=mi, tol=0.0, damping=damping)
+            assert gpu.status == ref.status == oracle.NOT_CONVERGED, (damping, mi)
+            assert gpu.iters == ref.iters == mi, (damping, mi)
+            err = float(np.max(np.abs(gpu.out_np - ref.s)))
+            assert err <= 1e-4, (damping, mi, err)
+
+
 @pytest.mark.parametrize("flags", [0, pn.FLAG_MULTI_LAUNCH])
 def test_cfg1_newton_full(flags):
     # one workgroup (default) and the launch-per-phase driver
