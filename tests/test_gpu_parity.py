@@ -178,6 +178,30 @@ def test_diag_tanh_every_stopping_point(damping):
             assert err <= 1e-4 * max(1.0, float(np.max(np.abs(ref.s)))), (mode, mi, err)
 
 
+def test_diag_tanh_nonfinite_after_the_first_update():
+    # An infinite coefficient a_d with s0_d != 0 saturates tanh at +-1 with
+    # the derivative inf x 0 = NaN: the first update's replay turns that
+    # channel NaN, so the solve is non-finite at update 1 (the iterate the
+    # first update does not store is written by the pass that stores it).
+    rng = np.random.default_rng(17)
+    D, B, T = 70, 2, 600
+    a = rng.uniform(-0.9, 0.9, D).astype(np.float32)
+    a[9] = np.inf
+    wl = dict(cfg=0, cell=pn.CELL_DIAG_TANH, D=D, m=D, B=B, T=T, tol=1e-6, damping=1.0, window=0,
+              max_iter=T, params=a, x=rng.standard_normal((B, T, D)).astype(np.float32),
+              s0=(0.3 + 0.2 * rng.random((B, D))).astype(np.float32))
+    gpu = run_gpu(wl, Q)
+    ref = run_oracle(wl, Q)
+    assert ref.status == oracle.NONFINITE and ref.iters == 1
+    assert gpu.status == ref.status and gpu.iters == ref.iters, (gpu.status, gpu.iters)
+    fin = np.isfinite(ref.s)
+    assert np.array_equal(np.isfinite(gpu.out_np), fin)
+    assert float(np.max(np.abs(gpu.out_np[fin] - ref.s[fin]))) <= 1e-4
+    # Jacobi takes no derivative: the saturated channel is finite and the
+    # solve converges with the oracle's count
+    _parity(wl, J)
+
+
 @pytest.mark.slow
 def test_diag_tanh_stopping_points_on_long_chunks():
     # The same stopping points where the chunks are long enough for the
